@@ -1,0 +1,151 @@
+/*
+ * fhd.h -- C ABI of the gfx950 F^H D / Q library (libncmri_fhd.so).
+ *
+ * The operations (PMPP ch. 17 "Iterative MRI reconstruction"):
+ *
+ *   F^H D  (section 17.2, Fig. 17.3; section 17.3, Figs. 17.4-17.17)
+ *     FhD[b][n] = sum_{m<M} conj(phi[m]) * D[b][m]
+ *                          * exp(+i 2 pi (kx[m] x[n] + ky[m] y[n] + kz[m] z[n]))
+ *
+ *   Q      (section 17.2: computed once per trajectory, same core structure)
+ *     Q[n]      = sum_{m<M} |phi[m]|^2 * exp(+i 2 pi (kx[m] x[n] + ky[m] y[n] + kz[m] z[n]))
+ *
+ * k is in cycles per voxel and x, y, z in voxel units, so k.x is the phase in
+ * revolutions (Eq. 17.1 uses exp(i 2 pi k_j . r)).  The exponent sign and the
+ * complex multiply-accumulate follow the register-promoted kernel on the
+ * study-notes page for step 2 ("FHD Kernel memory bandwidth optimisation"):
+ * re += rMu cos - iMu sin, im += iMu cos + rMu sin, with Mu = conj(phi) D (the
+ * pages never print Mu; conj(phi) D makes the sum the conjugate transpose of
+ * F[m][n] = phi[m] exp(-i 2 pi k_m . x_n) applied to D).
+ *
+ * Work is split as the pages' loop fission does (section 17.3 step 1, Figs.
+ * 17.6/17.7): a per-sample kernel forms Mu and packs one k-space record per
+ * sample; then a gather kernel with one group of voxels per lane sums every
+ * sample (Figs. 17.9/17.10 gather after loop interchange).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
+ *     caller-owned, naturally aligned (float: 4 B, fhd_c32: 8 B).
+ *   - Complex data are interleaved (re, im) float32 pairs: fhd_c32.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     null stream) and the call returns without synchronising.  Inputs must
+ *     stay alive and unmodified until the stream has passed the work.
+ *   - The output is overwritten (not accumulated into).  M == 0 writes zeros;
+ *     N == 0 does nothing and returns FHD_OK.
+ *   - Argument errors are reported before anything is enqueued.  Kernel faults
+ *     surface at the caller's next synchronisation as a HIP error.
+ *   - No C++ exception crosses this interface.  Calls are re-entrant; the only
+ *     global state is a per-device property cache and the thread-local text
+ *     returned by fhd_last_error().
+ */
+#ifndef NCMRI_FHD_H
+#define NCMRI_FHD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One complex float32 sample, layout-compatible with torch.complex64. */
+typedef struct fhd_c32 {
+  float re, im;
+} fhd_c32;
+
+typedef enum fhd_status {
+  FHD_OK = 0,
+  FHD_ERR_INVALID_ARGUMENT = 1, /* null pointer with nonzero size, negative size,
+                                   batch < 1, unknown enum, overlapping output */
+  FHD_ERR_WORKSPACE = 2,        /* workspace too small / missing for split stages */
+  FHD_ERR_HIP = 3,              /* a HIP runtime call or launch failed */
+  FHD_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950 */
+  FHD_ERR_INTERNAL = 5          /* unexpected internal failure */
+} fhd_status;
+
+/* How sin/cos of the phase are evaluated (section 17.3 step 3, Fig. 17.17:
+ * hardware trigonometry trades a little accuracy for speed). */
+typedef enum fhd_trig {
+  FHD_TRIG_ACCURATE = 0, /* exact reduction of the phase in revolutions + library sincospi */
+  FHD_TRIG_HW = 1        /* fract() of the phase, then the v_sin_f32 / v_cos_f32 instructions */
+} fhd_trig;
+
+/* How the fp32 accumulators sum over the samples. */
+typedef enum fhd_sum {
+  FHD_SUM_BLOCKED = 0, /* per-tile partial sums folded into running totals */
+  FHD_SUM_KAHAN = 1,   /* as BLOCKED, with Kahan-compensated folding of the tiles */
+  FHD_SUM_PLAIN = 2    /* one running fp32 sum over all samples */
+} fhd_sum;
+
+/* Pipeline stages (the two loops produced by loop fission). */
+enum {
+  FHD_STAGE_MU = 1,     /* per-sample kernel: Mu (or |phi|^2) and sample records */
+  FHD_STAGE_GATHER = 2, /* per-voxel gather kernel */
+  FHD_STAGE_ALL = 3
+};
+
+/* Options; pass NULL for all defaults (accurate trig, blocked sum, automatic
+ * tuning, library-allocated workspace, both stages). */
+typedef struct fhd_opts {
+  int32_t trig;            /* fhd_trig, default FHD_TRIG_ACCURATE */
+  int32_t sum;             /* fhd_sum, default FHD_SUM_BLOCKED */
+  int32_t voxels_per_lane; /* 0 = automatic, else 1, 2, 4, 8 or 16 */
+  int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
+  int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL */
+  int32_t reserved;        /* must be 0 */
+  void* workspace;         /* device buffer, or NULL: the library then allocates it
+                              stream-ordered (hipMallocAsync/hipFreeAsync) for this
+                              call; running the stages in separate calls requires a
+                              caller workspace that persists between them */
+  size_t workspace_bytes;  /* size of `workspace` */
+} fhd_opts;
+
+/* Fills *opts with the defaults. */
+void fhd_default_opts(fhd_opts* opts);
+
+/* Workspace bytes fhd_compute (is_q = 0) or q_compute (is_q = 1) needs for
+ * these sizes and options (opts may be NULL).  Returns 0 on invalid arguments.
+ * The workspace holds one packed record per sample (and per batch group). */
+size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+                           const fhd_opts* opts);
+
+/*
+ * F^H D for `batch` data vectors sharing one trajectory.
+ *   kx, ky, kz : float[M]            k-space sample coordinates (cycles/voxel)
+ *   x, y, z    : float[N]            voxel coordinates (voxel units), any set;
+ *                                    regular grids run fastest
+ *   phi        : fhd_c32[M]          per-sample complex weight
+ *   D          : fhd_c32[batch][M]   scan data, vector-major
+ *   FhD        : fhd_c32[batch][N]   output, overwritten; must not overlap any input
+ * Returns FHD_OK or an error code (see fhd_last_error()).
+ */
+fhd_status fhd_compute(const float* kx, const float* ky, const float* kz,
+                       const float* x, const float* y, const float* z,
+                       const fhd_c32* phi, const fhd_c32* D, fhd_c32* FhD,
+                       int64_t M, int64_t N, int32_t batch,
+                       const fhd_opts* opts, void* stream);
+
+/*
+ * Q for one trajectory: as fhd_compute with the real weight |phi[m]|^2 in place
+ * of conj(phi[m]) D[m].   Q : fhd_c32[N] output, overwritten.
+ */
+fhd_status q_compute(const float* kx, const float* ky, const float* kz,
+                     const float* x, const float* y, const float* z,
+                     const fhd_c32* phi, fhd_c32* Q,
+                     int64_t M, int64_t N,
+                     const fhd_opts* opts, void* stream);
+
+/* Static text for a status code. */
+const char* fhd_status_string(fhd_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* fhd_last_error(void);
+
+/* Library version string. */
+const char* fhd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NCMRI_FHD_H */
