@@ -1,0 +1,24 @@
+"""gfx950 (MI355X) F^H D / Q for iterative non-Cartesian MRI reconstruction.
+
+Public entry points (thin wrappers over the C ABI in include/fhd.h):
+  fhd_compute(kx, ky, kz, x, y, z, phi, D, ...) -> complex64 [N] or [B, N]
+  q_compute(kx, ky, kz, x, y, z, phi, ...)      -> complex64 [N]
+  fhd_workspace_bytes(M, N, batch, is_q, ...)
+
+The HIP library is loaded on first use; a missing library raises instead of
+falling back to any CPU path.  ``inputs`` holds the seeded synthetic data
+generators (trajectories, voxel grids, phantom).
+"""
+from . import inputs  # noqa: F401
+
+__all__ = ["fhd_compute", "q_compute", "fhd_workspace_bytes", "inputs", "library_path"]
+
+
+def __getattr__(name):
+    if name in ("fhd_compute", "q_compute", "fhd_workspace_bytes"):
+        from . import fhd
+        return getattr(fhd, name)
+    if name == "library_path":
+        from . import _lib
+        return _lib.LIB_PATH
+    raise AttributeError(name)

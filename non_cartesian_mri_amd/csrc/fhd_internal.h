@@ -1,0 +1,65 @@
+// Internal interface between the C-ABI host code (fhd_api.hip) and the gfx950
+// kernels (fhd_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ncmri {
+
+constexpr int kWorkgroup = 256;   // lanes per workgroup (4 wave64)
+constexpr int kUnroll = 4;        // samples per unrolled step; records are padded to it
+
+enum Trig : int { kTrigAccurate = 0, kTrigHw = 1 };
+
+// Record layout of one k-space sample as the per-sample kernel packs it and
+// the gather kernel reads it (all dwords are float32):
+//   header  HW trig:       kx, ky, kz                       (3 dwords)
+//           accurate trig: khx, khy, khz, klx, kly, klz     (6 dwords)
+//           k = kh + kl exactly, kh a multiple of 2^-12 (see fhd_kernels.hip)
+//   then one weight set per (voxel offset j, vector b), set index s = j*BC + b:
+//     complex set: (fr + fi, fr, fi) where f = Mu_b * exp(i 2 pi k.d_j)
+//     real set (Q, j = 0 only): w = |phi|^2 (1 dword)
+//   padded with zeros to a multiple of 4 dwords.
+struct Layout {
+  int is_q;      // 0: F^H D (complex Mu), 1: Q (real |phi|^2)
+  int trig;      // Trig
+  int V;         // voxels per lane (group size)
+  int BC;        // data vectors per gather pass
+  int header;    // header dwords
+  int stride;    // dwords per record
+};
+
+inline constexpr int header_dwords(int trig) { return trig == kTrigHw ? 3 : 6; }
+
+inline constexpr int record_dwords(int is_q, int trig, int V, int BC) {
+  int w = is_q ? (1 + 3 * (V - 1)) : 3 * V * BC;
+  int d = header_dwords(trig) + w;
+  return (d + 3) / 4 * 4;
+}
+
+struct RecordArgs {
+  const float* kx; const float* ky; const float* kz;
+  const float* x; const float* y; const float* z;   // only x[0..V-1] etc. are read
+  const float2* phi;
+  const float2* D;       // first vector of this pass ([BC][M]); unused for Q
+  int64_t M;             // real samples
+  int64_t mpad;          // padded sample count (multiple of kUnroll)
+  float* rec;            // [mpad][stride]
+};
+
+struct GatherArgs {
+  const float* rec;      // [mpad][stride]
+  int64_t mpad;
+  int64_t tile;          // samples per summation tile (multiple of kUnroll)
+  const float* x; const float* y; const float* z;
+  int64_t N;
+  float2* out;           // first output vector of this pass ([BC][N])
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_records(const Layout& L, const RecordArgs& a, hipStream_t s);
+hipError_t launch_gather(const Layout& L, bool kahan, const GatherArgs& a, hipStream_t s);
+bool gather_supported(int is_q, int V, int BC);
+
+}  // namespace ncmri

@@ -1,0 +1,123 @@
+"""Python binding of the F^H D / Q library: argument marshalling only.
+
+torch provides device memory and the stream; every step of the computation
+runs in the HIP kernels behind the C ABI (include/fhd.h).  Names match the C
+entry points: fhd_compute, q_compute, fhd_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_TRIG = {"accurate": _lib.FHD_TRIG_ACCURATE, "hw": _lib.FHD_TRIG_HW}
+_SUM = {"blocked": _lib.FHD_SUM_BLOCKED, "kahan": _lib.FHD_SUM_KAHAN, "plain": _lib.FHD_SUM_PLAIN}
+_STAGES = {"all": _lib.FHD_STAGE_ALL, "mu": _lib.FHD_STAGE_MU, "gather": _lib.FHD_STAGE_GATHER}
+
+
+def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages="all",
+              workspace: torch.Tensor | None = None) -> _lib.FhdOpts:
+    o = _lib.FhdOpts()
+    _lib.load().fhd_default_opts(ctypes.byref(o))
+    o.trig = _TRIG[trig] if isinstance(trig, str) else int(trig)
+    o.sum = _SUM[sum] if isinstance(sum, str) else int(sum)
+    o.voxels_per_lane = int(voxels_per_lane)
+    o.tile = int(tile)
+    o.stages = _STAGES[stages] if isinstance(stages, str) else int(stages)
+    if workspace is not None:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    return o
+
+
+def fhd_workspace_bytes(M: int, N: int, batch: int = 1, is_q: bool = False, **opts) -> int:
+    o = make_opts(**opts)
+    return int(_lib.load().fhd_workspace_bytes(int(M), int(N), int(batch), int(bool(is_q)), ctypes.byref(o)))
+
+
+def _dev_f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 1:
+        raise TypeError(f"{name} must be a contiguous 1-D float32 tensor")
+    return t
+
+
+def _dev_c64(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.complex64 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous complex64 tensor")
+    return t
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
+                voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
+                stream=None) -> torch.Tensor:
+    """F^H D on the GPU.  D is complex64 [M] or [B, M]; returns complex64 [N] or [B, N].
+
+    The work is enqueued on `stream` (default: torch's current stream).
+    """
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    _dev_c64(D, "D")
+    M, N = kx.numel(), x.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == M) or not (y.numel() == z.numel() == N):
+        raise ValueError("inconsistent sizes")
+    squeeze = D.dim() == 1
+    D2 = D.reshape(1, -1) if squeeze else D
+    if D2.dim() != 2 or D2.shape[1] != M:
+        raise ValueError("D must be [M] or [B, M]")
+    B = D2.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.complex64, device=x.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != B * N:
+            raise ValueError("out must hold B*N complex values")
+    if workspace is None:
+        nbytes = fhd_workspace_bytes(M, N, B, False, trig=trig, sum=sum,
+                                     voxels_per_lane=voxels_per_lane, tile=tile)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace)
+    st = _lib.load().fhd_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
+                                 y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
+                                 out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
+    _lib.check(st)
+    return out.reshape(N) if squeeze else out.reshape(B, N)
+
+
+def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
+              voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
+              stream=None) -> torch.Tensor:
+    """Q on the GPU: complex64 [N]."""
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    M, N = kx.numel(), x.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == M) or not (y.numel() == z.numel() == N):
+        raise ValueError("inconsistent sizes")
+    if out is None:
+        out = torch.empty(N, dtype=torch.complex64, device=x.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != N:
+            raise ValueError("out must hold N complex values")
+    if workspace is None:
+        nbytes = fhd_workspace_bytes(M, N, 1, True, trig=trig, sum=sum,
+                                     voxels_per_lane=voxels_per_lane, tile=tile)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace)
+    st = _lib.load().q_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
+                               y.data_ptr(), z.data_ptr(), phi.data_ptr(), out.data_ptr(),
+                               M, N, ctypes.byref(o), _stream_ptr(stream))
+    _lib.check(st)
+    return out

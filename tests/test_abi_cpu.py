@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from non_cartesian_mri_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fhd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from non_cartesian_mri_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("sizeof",)))
+
+
+def test_header_declarations_match_binding():
+    assert sorted(_lib.EXPORTED) == _declared_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_opts_struct_layout(lib):
+    # 6 int32 + pointer + size_t on LP64
+    assert ctypes.sizeof(_lib.FhdOpts) == 40
+    o = _lib.FhdOpts()
+    o.trig = 77
+    lib.fhd_default_opts(ctypes.byref(o))
+    assert (o.trig, o.sum, o.voxels_per_lane, o.tile, o.stages, o.reserved) == (0, 0, 0, 0, 3, 0)
+    assert o.workspace is None and o.workspace_bytes == 0
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fhd_status_string(0) == b"FHD_OK"
+    assert lib.fhd_status_string(1) == b"FHD_ERR_INVALID_ARGUMENT"
+    assert lib.fhd_status_string(2) == b"FHD_ERR_WORKSPACE"
+    assert lib.fhd_status_string(99) == b"FHD_UNKNOWN_STATUS"
+    assert b"gfx950" in lib.fhd_version()
+
+
+def _opts(**kw):
+    o = _lib.FhdOpts()
+    _lib.load().fhd_default_opts(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+# Fake, never dereferenced device addresses: every case below must be rejected
+# by argument checks that run before any HIP call.
+A = 1 << 40
+
+
+def _fhd(lib, M=16, N=8, batch=1, opts=None, **ptrs):
+    p = dict(kx=A, ky=A + 0x1000, kz=A + 0x2000, x=A + 0x3000, y=A + 0x4000, z=A + 0x5000,
+             phi=A + 0x6000, D=A + 0x8000, out=A + 0x100000)
+    p.update(ptrs)
+    return lib.fhd_compute(p["kx"], p["ky"], p["kz"], p["x"], p["y"], p["z"], p["phi"], p["D"],
+                           p["out"], M, N, batch, None if opts is None else ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(M=-1), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(N=-5), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(batch=513), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(M=1 << 31), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(kx=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(D=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(x=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(out=A + 0x3000), _lib.FHD_ERR_INVALID_ARGUMENT),    # output aliases x
+    (dict(out=A + 0x8000 + 64), _lib.FHD_ERR_INVALID_ARGUMENT),  # output inside D
+])
+def test_fhd_argument_errors(lib, kw, err):
+    assert _fhd(lib, **kw) == err
+    assert lib.fhd_last_error() != b""
+
+
+@pytest.mark.parametrize("field,value", [
+    ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 32),
+    ("tile", -4), ("stages", 4), ("reserved", 1),
+])
+def test_bad_options(lib, field, value):
+    assert _fhd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_errors(lib):
+    need = lib.fhd_workspace_bytes(16, 8, 1, 0, None)
+    assert need > 0
+    small = _opts(workspace=A + 0x200000, workspace_bytes=need - 1)
+    assert _fhd(lib, opts=small) == _lib.FHD_ERR_WORKSPACE
+    # a single stage needs a caller workspace
+    assert _fhd(lib, opts=_opts(stages=_lib.FHD_STAGE_MU)) == _lib.FHD_ERR_WORKSPACE
+    # workspace overlapping an input or the output
+    assert _fhd(lib, opts=_opts(workspace=A + 0x6000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert _fhd(lib, opts=_opts(workspace=A + 0x100000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def test_empty_voxel_set_is_a_noop(lib):
+    # N == 0 returns before any device call
+    assert _fhd(lib, N=0, x=None, y=None, z=None, out=None) == _lib.FHD_OK
+    assert lib.q_compute(A, A + 0x1000, A + 0x2000, None, None, None, A + 0x6000, None, 16, 0,
+                         None, None) == _lib.FHD_OK
+
+
+def test_q_argument_errors(lib):
+    E = _lib.FHD_ERR_INVALID_ARGUMENT
+    assert lib.q_compute(None, A, A, A + 0x3000, A + 0x4000, A + 0x5000, A + 0x6000, A + 0x100000, 4, 4, None, None) == E
+    assert lib.q_compute(A, A, A, A + 0x3000, A + 0x4000, A + 0x5000, A + 0x6000, A + 0x3000, 4, 4, None, None) == E
+    assert lib.q_compute(A, A, A, A + 0x3000, A + 0x4000, A + 0x5000, A + 0x6000, A + 0x100000, -4, 4, None, None) == E
+
+
+def test_workspace_bytes(lib):
+    # records: mpad * stride dwords, 256-byte aligned per pass
+    def ws(M, N, batch=1, is_q=0, **kw):
+        return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
+    assert ws(-1, 4) == 0
+    assert ws(4, 4, batch=0) == 0
+    assert ws(0, 100) == 0
+    # HW trig, V=1, one vector: 3 header + 3 weights -> 8 dwords (padded to 4)
+    assert ws(1000, 1, trig=1, voxels_per_lane=1) == (1000 * 8 * 4 + 255) // 256 * 256
+    # accurate trig, V=8: 6 + 24 = 30 -> 32 dwords
+    assert ws(1001, 4096, voxels_per_lane=8) == (1004 * 32 * 4 + 255) // 256 * 256
+    # Q, HW, V=4: 3 + 1 + 9 = 13 -> 16 dwords
+    assert ws(8, 64, is_q=1, trig=1, voxels_per_lane=4) == 8 * 16 * 4 // 256 * 256 + 256 * (8 * 16 * 4 % 256 > 0)
+    # batch 5 = passes of 4 and 1 vectors, V forced to 1 (HW): strides 3+12->16 and 3+3->8
+    assert ws(100, 50, batch=5, trig=1) == (100 * 16 * 4 + 255) // 256 * 256 + (100 * 8 * 4 + 255) // 256 * 256

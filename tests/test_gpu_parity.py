@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the double-precision oracle.
+
+Small problems are compared exhaustively; they span several workgroups,
+several summation tiles and ragged tails in both the voxel and the sample
+dimension.  Every trig path, summation mode and voxel-group size is covered,
+for F^H D, batched F^H D and Q, on grid (factored phase) and non-grid (direct
+phase) voxel sets.
+"""
+import numpy as np
+import pytest
+import torch
+
+from non_cartesian_mri_amd import inputs
+from tests.gpu_util import TOL, assert_close, dev_problem, gpu_fhd, gpu_q, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+TRIGS = ["accurate", "hw"]
+SUMS = ["blocked", "kahan", "plain"]
+VS = [1, 2, 4, 8, 16]
+
+
+@pytest.fixture(scope="module")
+def small_grid(oracle_mod):
+    # 18^3 = 5832 voxels: not a multiple of 64*V; M = 1001 with 128-sample tiles
+    p = inputs.random_problem(201, M=1001, L=18)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
+    return p, dev_problem(p), ref, qref
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("sum_", SUMS)
+@pytest.mark.parametrize("V", VS)
+def test_fhd_small_grid(small_grid, trig, sum_, V):
+    p, d, ref, _ = small_grid
+    got = gpu_fhd(p, d, trig=trig, sum=sum_, voxels_per_lane=V, tile=128)
+    assert_close(got, ref, TOL[trig], f"fhd grid {trig}/{sum_}/V={V}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("sum_", SUMS)
+@pytest.mark.parametrize("V", VS)
+def test_q_small_grid(small_grid, trig, sum_, V):
+    p, d, _, qref = small_grid
+    got = gpu_q(p, d, trig=trig, sum=sum_, voxels_per_lane=V, tile=128)
+    assert_close(got, qref, TOL[trig], f"q grid {trig}/{sum_}/V={V}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("V", [1, 4, 8, 16])
+def test_irregular_voxels(oracle_mod, trig, V):
+    """Non-grid voxel centres: every wave takes the direct-phase path."""
+    p = inputs.random_problem(202, M=777, N=3001, L=40, coords="random")
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    assert_close(gpu_fhd(p, trig=trig, voxels_per_lane=V), ref, TOL[trig], f"fhd irregular {trig}/V={V}")
+    qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
+    assert_close(gpu_q(p, trig=trig, voxels_per_lane=V), qref, TOL[trig], f"q irregular {trig}/V={V}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_mixed_regular_and_irregular_waves(oracle_mod, trig):
+    """A grid with a few displaced voxels: only the waves holding them go direct."""
+    p = inputs.random_problem(203, M=600, L=24)
+    x = p.x.copy()
+    x[[100, 5000, 13823]] += np.float32(0.25)
+    p.x = x
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    assert_close(gpu_fhd(p, trig=trig, voxels_per_lane=8), ref, TOL[trig], f"fhd mixed {trig}")
+    qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
+    assert_close(gpu_q(p, trig=trig, voxels_per_lane=8), qref, TOL[trig], f"q mixed {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("B", [2, 3, 5, 16, 19])
+def test_batched(oracle_mod, trig, B):
+    p = inputs.random_problem(204, M=513, L=10, B=B)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    assert_close(gpu_fhd(p, trig=trig), ref, TOL[trig], f"fhd batched {trig}/B={B}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_batch_rows_equal_single_calls_bitwise(trig):
+    """Row b of a batched call equals a single call on D[b] (same per-sample arithmetic)."""
+    p = inputs.random_problem(205, M=300, L=8, B=16)
+    d = dev_problem(p)
+    full = gpu_fhd(p, d, trig=trig)
+    for b in (0, 7, 15):
+        q = inputs.Problem(p.name, "fhd", p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D[b:b + 1], p.seed)
+        one = gpu_fhd(q, trig=trig, voxels_per_lane=1)
+        assert np.array_equal(one[0], full[b])
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_deterministic(trig):
+    p = inputs.random_problem(206, M=2000, L=20)
+    d = dev_problem(p)
+    a = gpu_fhd(p, d, trig=trig)
+    b = gpu_fhd(p, d, trig=trig)
+    assert np.array_equal(a, b)
+    qa, qb = gpu_q(p, d, trig=trig), gpu_q(p, d, trig=trig)
+    assert np.array_equal(qa, qb)
+
+
+def test_split_stages_equal_one_call():
+    from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes
+    p = inputs.random_problem(207, M=999, L=12, B=3)
+    d = dev_problem(p)
+    nb = fhd_workspace_bytes(p.M, p.N, p.B)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"],
+                stages="mu", workspace=ws)
+    out = fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"],
+                      stages="gather", workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), gpu_fhd(p, d))
+
+
+def test_non_default_stream(oracle_mod):
+    p = inputs.random_problem(208, M=400, L=10)
+    d = dev_problem(p)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    from non_cartesian_mri_amd import fhd_compute
+    with torch.cuda.stream(s):
+        out = fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"])
+    s.synchronize()
+    assert_close(out.cpu().numpy().reshape(1, -1), ref, TOL["accurate"], "fhd side stream")
+
+
+# ------------------------------ edge cases ---------------------------------
+@pytest.mark.parametrize("trig", TRIGS)
+def test_empty_sample_set_gives_zeros(trig):
+    p = inputs.random_problem(209, M=0, L=6, B=2)
+    got = gpu_fhd(p, trig=trig)
+    assert got.shape == (2, 216) and np.all(got == 0)
+    assert np.all(gpu_q(p, trig=trig) == 0)
+
+
+def test_empty_voxel_set():
+    from non_cartesian_mri_amd import fhd_compute, q_compute
+    p = inputs.random_problem(210, M=50, L=4)
+    d = dev_problem(p)
+    e = torch.empty(0, dtype=torch.float32, device="cuda:0")
+    out = fhd_compute(d["kx"], d["ky"], d["kz"], e, e, e, d["phi"], d["D"])
+    assert out.numel() == 0
+    assert q_compute(d["kx"], d["ky"], d["kz"], e, e, e, d["phi"]).numel() == 0
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("N", [1, 3, 5, 17])
+def test_tiny_voxel_counts(oracle_mod, trig, N):
+    """N below the group size: the group size shrinks; lanes past N stay idle."""
+    p = inputs.random_problem(211, M=321, L=4, N=N)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    assert_close(gpu_fhd(p, trig=trig, voxels_per_lane=16), ref, TOL[trig], f"fhd N={N} {trig}")
+    qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
+    assert_close(gpu_q(p, trig=trig, voxels_per_lane=16), qref, TOL[trig], f"q N={N} {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_single_sample_at_k0(trig):
+    """M=1, k=0: every voxel gets Mu = conj(phi) D (to within fp32 rounding of the packing)."""
+    p = inputs.random_problem(212, M=1, L=8)
+    p.kx, p.ky, p.kz = (np.zeros(1, np.float32) for _ in range(3))
+    mu = np.conj(p.phi[0].astype(np.complex128)) * p.D[0, 0].astype(np.complex128)
+    for V in (1, 8):
+        got = gpu_fhd(p, trig=trig, voxels_per_lane=V)[0]
+        assert np.max(np.abs(got - mu)) <= 2.5e-7 * abs(mu)
+        assert np.all(got == got[0])
+    w = abs(complex(p.phi[0])) ** 2
+    gq = gpu_q(p, trig=trig)
+    assert np.max(np.abs(gq - w)) <= 1.5e-7 * w
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("axis,k,base", [(0, 0.25, 1j), (1, 0.5, -1.0), (2, -0.25, -1j)])
+def test_single_sample_plane_wave(trig, axis, k, base):
+    """One sample on an axis with k.x a multiple of a quarter turn: base**x."""
+    p = inputs.random_problem(213, M=1, L=8)
+    kv = [np.zeros(1, np.float32) for _ in range(3)]
+    kv[axis][0] = k
+    p.kx, p.ky, p.kz = kv
+    mu = np.conj(p.phi[0].astype(np.complex128)) * p.D[0, 0].astype(np.complex128)
+    coord = (p.x, p.y, p.z)[axis].astype(np.int64)
+    want = np.array([mu * base ** int(c) for c in coord])
+    for V in (1, 4, 16):
+        got = gpu_fhd(p, trig=trig, voxels_per_lane=V)[0]
+        assert np.max(np.abs(got - want)) <= 1e-6 * abs(mu), (V, np.max(np.abs(got - want)))
+
+
+@pytest.mark.parametrize("M", [3, 4, 5, 127, 128, 129, 4099])
+def test_sample_count_tails(oracle_mod, M):
+    """Sample counts around the unroll step and the tile size (tile=128)."""
+    p = inputs.random_problem(214, M=M, L=9)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    for trig in TRIGS:
+        assert_close(gpu_fhd(p, trig=trig, tile=128), ref, TOL[trig], f"fhd M={M} {trig}")
+
+
+def test_voxel_at_origin_sums_mu():
+    p = inputs.random_problem(215, M=5000, L=8)
+    got = gpu_fhd(p)[0]
+    o = np.nonzero((p.x == 0) & (p.y == 0) & (p.z == 0))[0][0]
+    want = np.sum(np.conj(p.phi.astype(np.complex128)) * p.D[0].astype(np.complex128))
+    assert abs(got[o] - want) <= 1e-5 * np.sqrt(np.sum(np.abs(p.phi.astype(np.complex128) * p.D[0]) ** 2))
+
+
+def test_permutation_invariance_within_tolerance():
+    p = inputs.random_problem(216, M=3000, L=12)
+    a = gpu_fhd(p)
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(p.M)
+    q = inputs.Problem(p.name, "fhd", p.kx[perm], p.ky[perm], p.kz[perm], p.x, p.y, p.z,
+                       p.phi[perm], p.D[:, perm], p.seed)
+    b = gpu_fhd(q)
+    assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(a)
