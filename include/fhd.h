@@ -66,7 +66,7 @@ typedef enum fhd_status {
 /* How sin/cos of the phase are evaluated (section 17.3 step 3, Fig. 17.17:
  * hardware trigonometry trades a little accuracy for speed). */
 typedef enum fhd_trig {
-  FHD_TRIG_ACCURATE = 0, /* exact reduction of the phase in revolutions + library sincospi */
+  FHD_TRIG_ACCURATE = 0, /* exact reduction of the phase in revolutions + polynomial sincos (<= 2 ulp) */
   FHD_TRIG_HW = 1        /* fract() of the phase, then the v_sin_f32 / v_cos_f32 instructions */
 } fhd_trig;
 

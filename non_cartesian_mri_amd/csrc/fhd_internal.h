@@ -8,7 +8,10 @@
 namespace ncmri {
 
 constexpr int kWorkgroup = 256;   // lanes per workgroup (4 wave64)
-constexpr int kUnroll = 4;        // samples per unrolled step; records are padded to it
+#ifndef NCMRI_UNROLL
+#define NCMRI_UNROLL 4
+#endif
+constexpr int kUnroll = NCMRI_UNROLL;  // samples per unrolled step; records are padded to it
 
 enum Trig : int { kTrigAccurate = 0, kTrigHw = 1 };
 
@@ -55,6 +58,7 @@ struct GatherArgs {
   const float* x; const float* y; const float* z;
   int64_t N;
   float2* out;           // first output vector of this pass ([BC][N])
+  int32_t stagger;       // samples between the starting points of successive waves (0: all start at 0)
 };
 
 // Launchers: return hipSuccess or the launch error.

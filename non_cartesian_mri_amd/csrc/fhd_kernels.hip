@@ -40,7 +40,8 @@
 //  * accurate: k is split as kh + kl with kh a multiple of 2^-12; for integer
 //    or half-integer coordinates of moderate size kh.x is exact in fp32, so
 //    its fractional part is exact and only the small kl.x term rounds; the
-//    reduced phase then goes through the library's sincospi.
+//    reduced phase then goes through sincos_turns (exact quarter-turn
+//    reduction and fitted polynomials, within 2 ulp).
 //
 // Summation: per-tile partial sums are folded into running totals (blocked);
 // optionally the fold is Kahan-compensated (the reduction article's
@@ -50,28 +51,62 @@
 namespace ncmri {
 namespace {
 
-__device__ __forceinline__ void phase_sincos_hw(const float* r, float x, float y, float z,
+// Keeps the compiler's scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <typename R>
+__device__ __forceinline__ void phase_sincos_hw(const R& r, float p0, float x, float y, float z,
                                                 float& c, float& s) {
-  float t = __builtin_fmaf(r[2], z, __builtin_fmaf(r[1], y, r[0] * x));
+  float t = __builtin_fmaf(r[2], z, __builtin_fmaf(r[1], y, p0));
   float f = __builtin_amdgcn_fractf(t);
   s = __builtin_amdgcn_sinf(f);
   c = __builtin_amdgcn_cosf(f);
 }
 
-__device__ __forceinline__ void phase_sincos_acc(const float* r, float x, float y, float z,
-                                                 float& c, float& s) {
-  float th = __builtin_fmaf(r[2], z, __builtin_fmaf(r[1], y, r[0] * x));
-  th = th - __builtin_rintf(th);
-  float tl = __builtin_fmaf(r[5], z, __builtin_fmaf(r[4], y, r[3] * x));
-  float u = th + tl;
-  sincospif(2.0f * u, &s, &c);
+// sin(2 pi u) and cos(2 pi u) for an angle u in turns (|u| < 2^22).
+// u is split exactly as u = q/4 + r with q = rint(4u) and |r| <= 1/8, then
+// sin(2 pi r) = r P(r^2) and cos(2 pi r) = 1 + r^2 Q(r^2), and the pair is
+// rotated by q quarter turns (swaps and sign flips, exact).  P and Q are our
+// own fits (weighted least squares on Chebyshev nodes, Lawson-reweighted
+// towards minimax, coefficients rounded to fp32); evaluated in fp32 Horner
+// form the results are within 1.7 ulp (sin) and 1.0 ulp (cos) of the true
+// values on the reduced range.
+__device__ __forceinline__ void sincos_turns(float u, float& s, float& c) {
+  const float q = __builtin_rintf(4.0f * u);
+  const float r = __builtin_fmaf(q, -0.25f, u);  // exact
+  const float r2 = r * r;
+  float p = __builtin_fmaf(-75.39374542236328f, r2, 81.59236145019531f);
+  p = __builtin_fmaf(p, r2, -41.3416633605957f);
+  p = __builtin_fmaf(p, r2, 6.2831854820251465f);
+  const float sp = p * r;
+  float k = __builtin_fmaf(59.245967864990234f, r2, -85.44374084472656f);
+  k = __builtin_fmaf(k, r2, 64.93932342529297f);
+  k = __builtin_fmaf(k, r2, -19.739208221435547f);
+  const float cp = __builtin_fmaf(k, r2, 1.0f);
+  const int qi = (int)q;
+  const bool odd = (qi & 1) != 0;
+  const float s1 = odd ? cp : sp;
+  const float c1 = odd ? sp : cp;
+  s = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, s1) ^ ((unsigned)(qi & 2) << 30));
+  c = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, c1) ^ ((unsigned)((qi + 1) & 2) << 30));
 }
 
-template <int TRIG>
-__device__ __forceinline__ void phase_sincos(const float* r, float x, float y, float z,
+template <typename R>
+__device__ __forceinline__ void phase_sincos_acc(const R& r, float p0, float x, float y, float z,
+                                                 float& c, float& s) {
+  float th = __builtin_fmaf(r[2], z, __builtin_fmaf(r[1], y, p0));
+  th = th - __builtin_rintf(th);
+  float tl = __builtin_fmaf(r[5], z, __builtin_fmaf(r[4], y, r[3] * x));
+  sincos_turns(th + tl, s, c);
+}
+
+// p0 must be r[0] * x (the first product of the phase); passing it in lets a
+// caller consume the record's first dword early.
+template <int TRIG, typename R>
+__device__ __forceinline__ void phase_sincos(const R& r, float p0, float x, float y, float z,
                                              float& c, float& s) {
-  if constexpr (TRIG == kTrigHw) phase_sincos_hw(r, x, y, z, c, s);
-  else phase_sincos_acc(r, x, y, z, c, s);
+  if constexpr (TRIG == kTrigHw) phase_sincos_hw(r, p0, x, y, z, c, s);
+  else phase_sincos_acc(r, p0, x, y, z, c, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -138,9 +173,67 @@ struct Gather {
   static constexpr int S = V * BC;                       // weight sets per record
   static constexpr int H = header_dwords(TRIG);
   static constexpr int STRIDE = record_dwords(QW ? 1 : 0, TRIG, V, BC);
+  // Double-buffer the records in SGPRs when two of them fit and a sample
+  // carries enough VALU work to cover the next record's load (measured: a
+  // gain for 24-32 dword records, a loss for shorter ones).
+  static constexpr bool PIPE = STRIDE >= 24 && 2 * STRIDE <= 64 && kUnroll % 2 == 0;
 
   // dword offset of set s inside a record
   static constexpr int set_off(int s) { return QW ? (s == 0 ? H : H + 1 + 3 * (s - 1)) : H + 3 * s; }
+
+  __device__ static __forceinline__ void load_record(float (&dst)[STRIDE], const float* src) {
+#pragma unroll
+    for (int i = 0; i < STRIDE; ++i) dst[i] = src[i];
+  }
+
+  // One sample for a regular wave: phase of the group's first voxel (p0 =
+  // r[0] * x0 already formed), then the three-FMA complex MAC for every set.
+  template <typename R>
+  __device__ static __forceinline__ void regular_step(const R& r, float p0, float x0, float y0,
+                                                      float z0, float (&A)[S], float (&Bq)[S],
+                                                      float (&Cr)[S]) {
+    float c, s;
+    phase_sincos<TRIG>(r, p0, x0, y0, z0, c, s);
+    const float cps = c + s, smc = s - c;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int o = set_off(q);
+      if (QW && q == 0) {
+        A[0] = __builtin_fmaf(r[o], c, A[0]);
+        Bq[0] = __builtin_fmaf(r[o], s, Bq[0]);
+      } else {
+        A[q] = __builtin_fmaf(r[o], c, A[q]);
+        Bq[q] = __builtin_fmaf(r[o + 2], cps, Bq[q]);
+        Cr[q] = __builtin_fmaf(r[o + 1], smc, Cr[q]);
+      }
+    }
+  }
+
+  // One sample for a wave whose voxels are not on the common offsets: every
+  // voxel's phase is evaluated; the sets of offset 0 carry Mu_b (or w).
+  __device__ static __forceinline__ void direct_step(const float* r, const float (&vx)[V],
+                                                     const float (&vy)[V], const float (&vz)[V],
+                                                     float (&A)[S], float (&Bq)[S], float (&Cr)[S]) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      float c, s;
+      phase_sincos<TRIG>(r, r[0] * vx[j], vx[j], vy[j], vz[j], c, s);
+      if constexpr (QW) {
+        A[j] = __builtin_fmaf(r[H], c, A[j]);
+        Bq[j] = __builtin_fmaf(r[H], s, Bq[j]);
+      } else {
+        const float cps = c + s, smc = s - c;
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+          const int q = j * BC + b;
+          const int o = set_off(b);
+          A[q] = __builtin_fmaf(r[o], c, A[q]);
+          Bq[q] = __builtin_fmaf(r[o + 2], cps, Bq[q]);
+          Cr[q] = __builtin_fmaf(r[o + 1], smc, Cr[q]);
+        }
+      }
+    }
+  }
 
   __device__ static void run(const GatherArgs& a) {
     const int64_t lane = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
@@ -171,94 +264,103 @@ struct Gather {
     const bool wave_regular = __all(reg);
 
     // real-form sets (Q weight w applied directly): re += w c, im += w s
-    auto real_form = [&](int s) -> bool { return QW && (s == 0 || !wave_regular); };
+    auto real_form = [&](int q) -> bool { return QW && (q == 0 || !wave_regular); };
 
     float A[S], Bq[S], Cr[S];          // tile partials
     float Tre[S], Tim[S];              // running totals
     float Kre[KAHAN ? S : 1], Kim[KAHAN ? S : 1];  // Kahan compensations
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      Tre[s] = 0.0f; Tim[s] = 0.0f;
-      if constexpr (KAHAN) { Kre[s] = 0.0f; Kim[s] = 0.0f; }
+    for (int q = 0; q < S; ++q) {
+      Tre[q] = 0.0f; Tim[q] = 0.0f;
+      if constexpr (KAHAN) { Kre[q] = 0.0f; Kim[q] = 0.0f; }
     }
 
     const float* __restrict__ rec = a.rec;
-    for (int64_t t0 = 0; t0 < a.mpad; t0 += a.tile) {
-      const int64_t t1 = (t0 + a.tile < a.mpad) ? t0 + a.tile : a.mpad;
-#pragma unroll
-      for (int s = 0; s < S; ++s) { A[s] = 0.0f; Bq[s] = 0.0f; Cr[s] = 0.0f; }
+    const int32_t mpad = (int32_t)a.mpad;
+    const int32_t tile = (int32_t)a.tile;
 
-      if (wave_regular) {
-        for (int64_t m = t0; m < t1; m += kUnroll) {
+    // Sums the samples [lo, hi) (both multiples of kUnroll) tile by tile.
+    auto run_range = [&](int32_t lo, int32_t hi) {
+      for (int32_t t0 = lo; t0 < hi; t0 += tile) {
+        const int32_t t1 = (hi - t0 > tile) ? t0 + tile : hi;
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const float* r = rec + (m + u) * STRIDE;
-            float c, s;
-            phase_sincos<TRIG>(r, vx[0], vy[0], vz[0], c, s);
-            const float cps = c + s, smc = s - c;
+        for (int q = 0; q < S; ++q) { A[q] = 0.0f; Bq[q] = 0.0f; Cr[q] = 0.0f; }
+        if (wave_regular) {
+          if constexpr (PIPE) {
+            // Ping-pong over two SGPR-resident records.  Scalar loads may
+            // return out of order, so a wait covers every load in flight: the
+            // current record's first dword is consumed (forcing its wait)
+            // before the next record's loads are issued, and the fences keep
+            // the scheduler from hoisting those loads above that first use.
+            // The next record's latency then overlaps one sample's VALU work.
+            float ra[STRIDE], rb[STRIDE];
+            const float* p = rec + (int64_t)t0 * STRIDE;
+            const float* pend = rec + (int64_t)t1 * STRIDE;
+            load_record(ra, p);
+            for (; p < pend; p += 2 * STRIDE) {
+              const float pa = ra[0] * vx[0];
+              sched_fence();
+              load_record(rb, p + STRIDE);
+              sched_fence();
+              regular_step(ra, pa, vx[0], vy[0], vz[0], A, Bq, Cr);
+              const float pb = rb[0] * vx[0];
+              sched_fence();
+              load_record(ra, (p + 2 * STRIDE < pend) ? p + 2 * STRIDE : p);
+              sched_fence();
+              regular_step(rb, pb, vx[0], vy[0], vz[0], A, Bq, Cr);
+            }
+          } else {
+            for (const float* p = rec + (int64_t)t0 * STRIDE, *pend = rec + (int64_t)t1 * STRIDE;
+                 p < pend; p += kUnroll * STRIDE) {
 #pragma unroll
-            for (int q = 0; q < S; ++q) {
-              const int o = set_off(q);
-              if (QW && q == 0) {
-                A[0] = __builtin_fmaf(r[o], c, A[0]);
-                Bq[0] = __builtin_fmaf(r[o], s, Bq[0]);
-              } else {
-                A[q] = __builtin_fmaf(r[o], c, A[q]);
-                Bq[q] = __builtin_fmaf(r[o + 2], cps, Bq[q]);
-                Cr[q] = __builtin_fmaf(r[o + 1], smc, Cr[q]);
+              for (int u = 0; u < kUnroll; ++u) {
+                const float* r = p + u * STRIDE;
+                regular_step(r, r[0] * vx[0], vx[0], vy[0], vz[0], A, Bq, Cr);
               }
             }
           }
-        }
-      } else {
-        // direct evaluation of every voxel's phase; sets (0, b) carry Mu_b
-        for (int64_t m = t0; m < t1; m += kUnroll) {
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u) {
-            const float* r = rec + (m + u) * STRIDE;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-              float c, s;
-              phase_sincos<TRIG>(r, vx[j], vy[j], vz[j], c, s);
-              if constexpr (QW) {
-                A[j] = __builtin_fmaf(r[H], c, A[j]);
-                Bq[j] = __builtin_fmaf(r[H], s, Bq[j]);
-              } else {
-                const float cps = c + s, smc = s - c;
-#pragma unroll
-                for (int b = 0; b < BC; ++b) {
-                  const int q = j * BC + b;
-                  const int o = set_off(b);
-                  A[q] = __builtin_fmaf(r[o], c, A[q]);
-                  Bq[q] = __builtin_fmaf(r[o + 2], cps, Bq[q]);
-                  Cr[q] = __builtin_fmaf(r[o + 1], smc, Cr[q]);
-                }
-              }
-            }
-          }
-        }
-      }
-      // fold the tile into the totals
-#pragma unroll
-      for (int q = 0; q < S; ++q) {
-        const bool rf = real_form(q);
-        const float dre = rf ? A[q] : A[q] - Bq[q];
-        const float dim = rf ? Bq[q] : A[q] + Cr[q];
-        if constexpr (KAHAN) {
-          const float yr = dre - Kre[q];
-          const float tr = Tre[q] + yr;
-          Kre[q] = (tr - Tre[q]) - yr;
-          Tre[q] = tr;
-          const float yi = dim - Kim[q];
-          const float ti = Tim[q] + yi;
-          Kim[q] = (ti - Tim[q]) - yi;
-          Tim[q] = ti;
         } else {
-          Tre[q] += dre;
-          Tim[q] += dim;
+          for (const float* p = rec + (int64_t)t0 * STRIDE, *pend = rec + (int64_t)t1 * STRIDE;
+               p < pend; p += kUnroll * STRIDE) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) direct_step(p + u * STRIDE, vx, vy, vz, A, Bq, Cr);
+          }
+        }
+        // fold the tile into the totals
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const bool rf = real_form(q);
+          const float dre = rf ? A[q] : A[q] - Bq[q];
+          const float dim = rf ? Bq[q] : A[q] + Cr[q];
+          if constexpr (KAHAN) {
+            const float yr = dre - Kre[q];
+            const float tr = Tre[q] + yr;
+            Kre[q] = (tr - Tre[q]) - yr;
+            Tre[q] = tr;
+            const float yi = dim - Kim[q];
+            const float ti = Tim[q] + yi;
+            Kim[q] = (ti - Tim[q]) - yi;
+            Tim[q] = ti;
+          } else {
+            Tre[q] += dre;
+            Tim[q] += dim;
+          }
         }
       }
+    };
+
+    // Waves walk the samples from different starting points (the sum does not
+    // depend on the order) so that the waves sharing a scalar cache are not
+    // all waiting on the same record line at the same time.
+    int32_t start = 0;
+    if (a.stagger > 0 && mpad > 0) {
+      const uint32_t wave = __builtin_amdgcn_readfirstlane((uint32_t)(lane >> 6));
+      const int64_t off = (int64_t)((wave * 7u) & 15u) * a.stagger;
+      start = (int32_t)((off % mpad) / kUnroll * kUnroll);
     }
+    run_range(start, mpad);
+    run_range(0, start);
+
     // write-out: out[b][n0 + j]
 #pragma unroll
     for (int j = 0; j < V; ++j) {
