@@ -22,11 +22,11 @@ METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roof
 FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
 FLOP_PER_PAIR = {"fhd": 14, "q": 10}   # phase 5 + reduction 1 + complex MAC 8 (Q: real MAC 4)
 WORKLOADS = {
-    "c3_spiral": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
-    "c2_radial": "FhD 64^3 voxels x 65,536 radial samples",
-    "c4_q": "Q on 128^3 voxels (step 0.5) x 1,048,576 uniform samples",
-    "c5_batched": "FhD x16 vectors, 96^3 voxels x 500,001 radial samples",
-    "c1_tiny": "FhD 32^3 voxels x 2048 uniform samples",
+    "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
+    "fhd_64cube_65536_radial": "FhD 64^3 voxels x 65,536 radial samples",
+    "q_128cube_halfstep_1048576_uniform": "Q on 128^3 voxels (step 0.5) x 1,048,576 uniform samples",
+    "fhd16_96cube_500001_radial": "FhD x16 vectors, 96^3 voxels x 500,001 radial samples",
+    "fhd_32cube_2048_uniform": "FhD 32^3 voxels x 2048 uniform samples",
 }
 
 
@@ -35,14 +35,29 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c3_spiral", choices=sorted(WORKLOADS))
-    ap.add_argument("--trig", default="accurate", choices=["accurate", "hw"])
+    ap.add_argument("--config", default="fhd_128cube_262144_spirals", choices=sorted(WORKLOADS))
+    ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU-oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
+                         "five times (reference reading for the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain copy kernel of known size, for scaling FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}}))
 
 
 def cpu_baseline(p, target_s: float) -> dict:
@@ -87,6 +102,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     dev = torch.device("cuda:0")
     p = inputs.make_config(args.config)
     t = {k: torch.from_numpy(np.ascontiguousarray(getattr(p, k))).to(dev)

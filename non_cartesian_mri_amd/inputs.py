@@ -222,26 +222,26 @@ class Problem:
 
 
 CONFIGS = {
-    "c1_tiny": "FhD 32^3 voxels, M=2048 uniform-random k, complex N(0,1) phi and D",
-    "c2_radial": "FhD 64^3 voxels, M=65,536 on 256 Fibonacci spokes x 256 points",
-    "c3_spiral": "FhD 128^3 voxels, M=262,144 on 64 kz planes x 4096-point spirals",
-    "c4_q": "Q on a 2x-oversampled 128^3 grid (step 0.5), M=1,048,576 uniform-random k",
-    "c4_q_wide": "Q on a 128^3 grid with step 1 (coords -64..63), M=1,048,576 uniform-random k",
-    "c5_batched": "FhD x16 D vectors, 96^3 voxels, M=500,001 radial (odd tail)",
-    "c5_phantom": "FhD of the analytic ellipsoid phantom, 96^3 voxels, M=500,001 radial, phi=|k|^2",
+    "fhd_32cube_2048_uniform": "FhD 32^3 voxels, M=2048 uniform-random k, complex N(0,1) phi and D",
+    "fhd_64cube_65536_radial": "FhD 64^3 voxels, M=65,536 on 256 Fibonacci spokes x 256 points",
+    "fhd_128cube_262144_spirals": "FhD 128^3 voxels, M=262,144 on 64 kz planes x 4096-point spirals",
+    "q_128cube_halfstep_1048576_uniform": "Q on a 2x-oversampled 128^3 grid (step 0.5), M=1,048,576 uniform-random k",
+    "q_128cube_unitstep_1048576_uniform": "Q on a 128^3 grid with step 1 (coords -64..63), M=1,048,576 uniform-random k",
+    "fhd16_96cube_500001_radial": "FhD x16 D vectors, 96^3 voxels, M=500,001 radial (odd tail)",
+    "phantom_96cube_500001_radial": "FhD of the analytic ellipsoid phantom, 96^3 voxels, M=500,001 radial, phi=|k|^2",
 }
 
 
 def make_config(name: str) -> Problem:
     """Build one of the named workloads (see CONFIGS)."""
-    if name == "c1_tiny":
+    if name == "fhd_32cube_2048_uniform":
         rng = _rng(101)
         kx, ky, kz = uniform_k(2048, rng)
         x, y, z = voxel_grid(32)
         phi = complex_normal(rng, 2048)
         D = complex_normal(rng, 2048)[None, :]
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 101, 32)
-    if name == "c2_radial":
+    if name == "fhd_64cube_65536_radial":
         rng = _rng(102)
         kx, ky, kz = radial_k(256, 256)
         x, y, z = voxel_grid(64)
@@ -249,7 +249,7 @@ def make_config(name: str) -> Problem:
         phi = complex_normal(rng, M)
         D = complex_normal(rng, M)[None, :]
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 102, 64)
-    if name == "c3_spiral":
+    if name == "fhd_128cube_262144_spirals":
         rng = _rng(103)
         kx, ky, kz = stack_of_spirals_k(64, 4096, 64)
         x, y, z = voxel_grid(128)
@@ -257,14 +257,14 @@ def make_config(name: str) -> Problem:
         phi = complex_normal(rng, M)
         D = complex_normal(rng, M)[None, :]
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 103, 128)
-    if name in ("c4_q", "c4_q_wide"):
+    if name in ("q_128cube_halfstep_1048576_uniform", "q_128cube_unitstep_1048576_uniform"):
         rng = _rng(104)
         kx, ky, kz = uniform_k(1 << 20, rng)
-        x, y, z = voxel_grid(128, 0.5 if name == "c4_q" else 1.0)
+        x, y, z = voxel_grid(128, 0.5 if name == "q_128cube_halfstep_1048576_uniform" else 1.0)
         phi = complex_normal(rng, 1 << 20)
         return Problem(name, "q", kx, ky, kz, x, y, z, phi, None, 104, 128,
-                       extra={"step": 0.5 if name == "c4_q" else 1.0})
-    if name == "c5_batched":
+                       extra={"step": 0.5 if name == "q_128cube_halfstep_1048576_uniform" else 1.0})
+    if name == "fhd16_96cube_500001_radial":
         rng = _rng(105)
         kx, ky, kz = radial_k(1954, 256, 500_001)
         x, y, z = voxel_grid(96)
@@ -272,7 +272,7 @@ def make_config(name: str) -> Problem:
         phi = complex_normal(rng, M)
         D = np.stack([complex_normal(rng, M) for _ in range(16)])
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 105, 96)
-    if name == "c5_phantom":
+    if name == "phantom_96cube_500001_radial":
         kx, ky, kz = radial_k(1954, 256, 500_001)
         x, y, z = voxel_grid(96)
         k2 = (kx.astype(np.float64) ** 2 + ky.astype(np.float64) ** 2

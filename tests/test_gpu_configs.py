@@ -18,7 +18,7 @@ from tests.gpu_util import TOL, assert_close, dev_problem, gpu_fhd, gpu_q, requi
 pytestmark = pytest.mark.gpu
 
 TRIGS = ["accurate", "hw"]
-SUBSET = {"c2_radial": 16384, "c3_spiral": 4096, "c4_q": 4096, "c4_q_wide": 2048, "c5_batched": 2048}
+SUBSET = {"fhd_64cube_65536_radial": 16384, "fhd_128cube_262144_spirals": 4096, "q_128cube_halfstep_1048576_uniform": 4096, "q_128cube_unitstep_1048576_uniform": 2048, "fhd16_96cube_500001_radial": 2048}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,7 +32,7 @@ _cache = {}
 def _problem_and_ref(name, oracle_mod):
     if name not in _cache:
         p = inputs.make_config(name)
-        idx = None if name == "c1_tiny" else inputs.subset_indices(p.N, SUBSET[name], p.seed)
+        idx = None if name == "fhd_32cube_2048_uniform" else inputs.subset_indices(p.N, SUBSET[name], p.seed)
         if p.kind == "q":
             ref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, idx=idx)
         else:
@@ -43,7 +43,7 @@ def _problem_and_ref(name, oracle_mod):
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-@pytest.mark.parametrize("name", ["c1_tiny", "c2_radial", "c3_spiral", "c5_batched"])
+@pytest.mark.parametrize("name", ["fhd_32cube_2048_uniform", "fhd_64cube_65536_radial", "fhd_128cube_262144_spirals", "fhd16_96cube_500001_radial"])
 def test_fhd_config(oracle_mod, name, trig):
     p, idx, ref, d = _problem_and_ref(name, oracle_mod)
     print(f"[gpu] {name} trig={trig} N={p.N} M={p.M} B={p.B}", flush=True)
@@ -54,7 +54,7 @@ def test_fhd_config(oracle_mod, name, trig):
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-@pytest.mark.parametrize("name", ["c4_q", "c4_q_wide"])
+@pytest.mark.parametrize("name", ["q_128cube_halfstep_1048576_uniform", "q_128cube_unitstep_1048576_uniform"])
 def test_q_config(oracle_mod, name, trig):
     p, idx, ref, d = _problem_and_ref(name, oracle_mod)
     print(f"[gpu] {name} trig={trig} N={p.N} M={p.M}", flush=True)
@@ -79,7 +79,7 @@ def test_q_config(oracle_mod, name, trig):
 def test_phantom_round_trip_psnr(oracle_mod):
     """Ellipsoid phantom -> analytic k-space on the radial trajectory -> F^H D with
     density weights |k|^2: PSNR of the GPU image may drop at most 0.1 dB from the oracle's."""
-    p = inputs.make_config("c5_phantom")
+    p = inputs.make_config("phantom_96cube_500001_radial")
     sl = p.extra["slices"]
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D, idx=sl)[0]
     print(f"[oracle] phantom slices ({sl.size} voxels): {oracle_mod.last.seconds:.1f}s", flush=True)
