@@ -21,6 +21,16 @@ import numpy as np
 METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roofline"
 FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
 FLOP_PER_PAIR = {"fhd": 14, "q": 10}   # phase 5 + reduction 1 + complex MAC 8 (Q: real MAC 4)
+# HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
+# Valid only for the kernel source they were taken on (sha256 prefix) and the
+# same launch configuration; otherwise the benchmark reports null.
+TRAFFIC = {
+    ("fhd_128cube_262144_spirals", "hw", "blocked", 16): {
+        "kernel_sha256": "73120cd474cdf845",
+        "fetch_bytes": 438359 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
+        "profile": "profiles/gather_128cubed_x_262144_hw_counters.md"},
+}
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
     "fhd_64cube_65536_radial": "FhD 64^3 voxels x 65,536 radial samples",
@@ -45,6 +55,8 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
                          "five times (reference reading for the HBM byte counters) and exit")
+    ap.add_argument("--issue-rates", action="store_true",
+                    help="run the gfx950 issue-rate microbenchmark (FMA, v_sin, mixed issue, trig error) and exit")
     return ap.parse_args()
 
 
@@ -84,6 +96,24 @@ def cpu_baseline(p, target_s: float) -> dict:
                       f"workload ({pairs:.3e} pairs, {t:.1f} s wall)"}
 
 
+def kernel_source_sha() -> str:
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc",
+                        "fhd_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(config: str, trig: str, summ: str, voxels_per_lane: int, gather_ms: float):
+    """Counter-derived HBM traffic (GB/s over the launch) or None if not measured for this kernel."""
+    t = TRAFFIC.get((config, trig, summ, voxels_per_lane))
+    if t is None or t["kernel_sha256"] != kernel_source_sha():
+        return None, None
+    total = t["fetch_bytes"] + t["write_bytes"]
+    return total / (gather_ms * 1e-3) / 1e9, {"bytes_per_launch": total, "fetch_bytes": t["fetch_bytes"],
+                                               "write_bytes": t["write_bytes"], "profile": t["profile"]}
+
+
 def oracle_threads_hint() -> int:
     try:
         return int(os.environ.get("OMP_NUM_THREADS", "")) or os.cpu_count() or 1
@@ -93,6 +123,13 @@ def oracle_threads_hint() -> int:
 
 def main():
     args = parse()
+    if args.issue_rates:
+        import subprocess
+        from non_cartesian_mri_amd.build import ISSUE_RATES
+        if not os.path.exists(ISSUE_RATES):
+            print(f"{ISSUE_RATES} is not built (python -m non_cartesian_mri_amd.build)", file=sys.stderr)
+            sys.exit(1)
+        sys.exit(subprocess.run([ISSUE_RATES]).returncode)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the F^H D path here is a single-GPU build "
               "(voxel sharding across GPUs is a design note only); use --gpus 1", file=sys.stderr)
@@ -149,6 +186,9 @@ def main():
     # launches per gather stage: one per batch pass
     g_avg = float(gather_ms.mean())
     achieved = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
+    from non_cartesian_mri_amd.fhd import resolved_voxels_per_lane
+    vpl = resolved_voxels_per_lane(p.M, p.N, p.B, is_q, **opts)
+    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, vpl, g_avg)
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -164,7 +204,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "voxels": p.N,
                    "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": args.sum,
-                   "voxels_per_lane": args.voxels_per_lane or "auto", "tile": args.tile or "auto",
+                   "voxels_per_lane": vpl, "tile": args.tile or "auto",
                    "parallelism": "single GPU, data-parallel over voxels"},
         "timing_ms": {"step_event_median": round(float(np.median(step_ms)), 4),
                       "gather_event_mean": round(g_avg, 4),
@@ -172,7 +212,9 @@ def main():
                       "mu_event_mean": round(float(mu_ms.mean()), 4)},
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": None if traffic is None else round(traffic, 3),
+                     "traffic_unit": "GB/s (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE / launch time)",
+                     "traffic_detail": traffic_detail,
                      "kernel": "gather_kernel (one launch per step)",
                      "flop_per_pair": FLOP_PER_PAIR[p.kind]},
     }

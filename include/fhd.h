@@ -135,6 +135,22 @@ fhd_status q_compute(const float* kx, const float* ky, const float* kz,
                      int64_t M, int64_t N,
                      const fhd_opts* opts, void* stream);
 
+/* The launch plan the library derives from sizes and options. */
+typedef struct fhd_plan_info {
+  int32_t voxels_per_lane;  /* voxels owned by one lane (group size) */
+  int32_t tile;             /* samples per summation tile */
+  int32_t passes;           /* gather launches (batch groups of 16, 8, 4, 2, 1 vectors) */
+  int32_t record_dwords;    /* dwords per sample record of the first pass */
+  int64_t padded_samples;   /* M rounded up to the record padding */
+  size_t workspace_bytes;   /* = fhd_workspace_bytes(...) */
+} fhd_plan_info;
+
+/* Fills *info with the plan for these sizes and options (opts may be NULL);
+ * returns FHD_ERR_INVALID_ARGUMENT (and leaves *info untouched) for the same
+ * argument errors fhd_compute / q_compute report.  No device call. */
+fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+                             const fhd_opts* opts, fhd_plan_info* info);
+
 /* Static text for a status code. */
 const char* fhd_status_string(fhd_status s);
 

@@ -11,11 +11,12 @@ generators (trajectories, voxel grids, phantom).
 """
 from . import inputs  # noqa: F401
 
-__all__ = ["fhd_compute", "q_compute", "fhd_workspace_bytes", "inputs", "library_path"]
+__all__ = ["fhd_compute", "q_compute", "fhd_workspace_bytes", "fhd_describe_plan", "inputs",
+           "library_path"]
 
 
 def __getattr__(name):
-    if name in ("fhd_compute", "q_compute", "fhd_workspace_bytes"):
+    if name in ("fhd_compute", "q_compute", "fhd_workspace_bytes", "fhd_describe_plan"):
         from . import fhd
         return getattr(fhd, name)
     if name == "library_path":

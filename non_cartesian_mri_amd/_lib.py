@@ -31,7 +31,7 @@ FHD_STAGE_ALL = 3
 
 # every symbol the header declares
 EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "q_compute",
-            "fhd_status_string", "fhd_last_error", "fhd_version")
+            "fhd_describe_plan", "fhd_status_string", "fhd_last_error", "fhd_version")
 
 
 class FhdOpts(ctypes.Structure):
@@ -43,6 +43,17 @@ class FhdOpts(ctypes.Structure):
         ("stages", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class FhdPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("voxels_per_lane", ctypes.c_int32),
+        ("tile", ctypes.c_int32),
+        ("passes", ctypes.c_int32),
+        ("record_dwords", ctypes.c_int32),
+        ("padded_samples", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -75,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.fhd_compute.restype = ctypes.c_int
     lib.q_compute.argtypes = [P, P, P, P, P, P, P, P, i64, i64, ctypes.POINTER(FhdOpts), P]
     lib.q_compute.restype = ctypes.c_int
+    lib.fhd_describe_plan.argtypes = [i64, i64, i32, i32, ctypes.POINTER(FhdOpts), ctypes.POINTER(FhdPlanInfo)]
+    lib.fhd_describe_plan.restype = ctypes.c_int
     lib.fhd_status_string.argtypes = [ctypes.c_int]
     lib.fhd_status_string.restype = ctypes.c_char_p
     lib.fhd_last_error.argtypes = []

@@ -62,5 +62,20 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+ISSUE_RATES = os.path.join(PKG, "issue_rates")
+
+
+def build_issue_rates() -> str:
+    """Compile the standalone issue-rate microbenchmark (csrc/issue_rates.hip)."""
+    tmp = ISSUE_RATES + f".tmp{os.getpid()}"
+    cmd = [_hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, "issue_rates.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for issue_rates.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ISSUE_RATES)
+    return ISSUE_RATES
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    print(build_issue_rates())

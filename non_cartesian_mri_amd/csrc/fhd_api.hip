@@ -231,6 +231,26 @@ NCMRI_API size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_
   }
 }
 
+NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+                                       const fhd_opts* opts, fhd_plan_info* info) {
+  try {
+    g_err[0] = '\0';
+    if (!info) return fail(FHD_ERR_INVALID_ARGUMENT, "info is NULL");
+    Plan p;
+    fhd_status st = make_plan(p, is_q ? 1 : 0, M, N, batch, opts);
+    if (st != FHD_OK) return st;
+    info->voxels_per_lane = p.V;
+    info->tile = (int32_t)p.tile;
+    info->passes = p.npass;
+    info->record_dwords = p.npass > 0 ? ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]) : 0;
+    info->padded_samples = p.mpad;
+    info->workspace_bytes = p.ws_bytes;
+    return FHD_OK;
+  } catch (...) {
+    return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
 NCMRI_API fhd_status fhd_compute(const float* kx, const float* ky, const float* kz, const float* x,
                                  const float* y, const float* z, const fhd_c32* phi,
                                  const fhd_c32* D, fhd_c32* FhD, int64_t M, int64_t N,

@@ -1,0 +1,147 @@
+// Issue-rate microbenchmarks for gfx950 that back the gather kernel's cost
+// model: FP32 FMA throughput, v_sin_f32 throughput, whether transcendentals
+// share the VALU issue port with FMAs (mixed loops), the shader clock, and
+// the absolute error of v_sin_f32/v_cos_f32 and of sincospif over one turn.
+// Standalone program: built by non_cartesian_mri_amd/build.py
+// (build_issue_rates) and run by `python bench.py --issue-rates`.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cmath>
+#include <vector>
+#include <cstdlib>
+
+#define CK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e), __LINE__); exit(1);} } while(0)
+
+template <int K>
+__global__ void __launch_bounds__(256) k_fma(float* out, int iters, float a, float b) {
+  float acc[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) acc[j] = threadIdx.x * 1e-3f + j;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) acc[j] = __builtin_fmaf(acc[j], a, b);
+  }
+  float s = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) s += acc[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// T chains of sin; K independent fma chains per iteration.
+template <int T, int K>
+__global__ void __launch_bounds__(256) k_mix(float* out, int iters, float a, float b) {
+  float u[T];
+  float acc[K > 0 ? K : 1];
+#pragma unroll
+  for (int j = 0; j < T; ++j) u[j] = threadIdx.x * 1e-4f + j * 0.01f;
+#pragma unroll
+  for (int j = 0; j < (K > 0 ? K : 1); ++j) acc[j] = threadIdx.x * 1e-3f + j;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < T; ++j) u[j] = __builtin_amdgcn_sinf(u[j]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) acc[j] = __builtin_fmaf(acc[j], a, b);
+  }
+  float s = 0;
+#pragma unroll
+  for (int j = 0; j < T; ++j) s += u[j];
+#pragma unroll
+  for (int j = 0; j < K; ++j) s += acc[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ void k_clock(long long* out, int iters, float a, float b, float* sink) {
+  long long c0 = clock64();
+  long long w0 = wall_clock64();
+  float x = threadIdx.x;
+  for (int i = 0; i < iters; ++i) x = __builtin_fmaf(x, a, b);
+  long long c1 = clock64();
+  long long w1 = wall_clock64();
+  if (threadIdx.x == 0) { out[0] = c1 - c0; out[1] = w1 - w0; }
+  sink[threadIdx.x] = x;
+}
+
+__global__ void k_trig_acc(const float* r, float* s_hw, float* c_hw, float* s_pi, float* c_pi, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float x = r[i];
+  s_hw[i] = __builtin_amdgcn_sinf(x);
+  c_hw[i] = __builtin_amdgcn_cosf(x);
+  float s, c;
+  sincospif(2.0f * x, &s, &c);
+  s_pi[i] = s; c_pi[i] = c;
+}
+
+template <typename F>
+double time_it(F f, int reps) {
+  hipEvent_t e0, e1; CK(hipEventCreate(&e0)); CK(hipEventCreate(&e1));
+  f(); CK(hipDeviceSynchronize());
+  CK(hipEventRecord(e0));
+  for (int r = 0; r < reps; ++r) f();
+  CK(hipEventRecord(e1)); CK(hipEventSynchronize(e1));
+  float ms; CK(hipEventElapsedTime(&ms, e0, e1));
+  return ms / reps * 1e-3;
+}
+
+int main() {
+  hipDeviceProp_t p; CK(hipGetDeviceProperties(&p, 0));
+  printf("device %s arch %s CUs %d clock %d kHz\n", p.name, p.gcnArchName, p.multiProcessorCount, p.clockRate);
+  const int CU = p.multiProcessorCount;
+  float* out; CK(hipMalloc(&out, 64 << 20));
+  long long* clk; CK(hipMalloc(&clk, 64));
+  // clock estimate
+  {
+    int iters = 1 << 22;
+    hipLaunchKernelGGL(k_clock, dim3(1), dim3(64), 0, 0, clk, iters, 0.999f, 0.001f, out);
+    CK(hipDeviceSynchronize());
+    long long h[2]; CK(hipMemcpy(h, clk, 16, hipMemcpyDeviceToHost));
+    printf("clock: %lld shader cycles in %lld wall ticks (100MHz) -> %.3f GHz, cycles/dep-fma %.2f\n", h[0], h[1], h[0] / (h[1] * 10.0), (double)h[0] / iters);
+  }
+  const int waves_per_simd = 8;
+  const int blocks = CU * 4 * waves_per_simd / 4;  // 256 threads = 4 waves per block
+  const int iters = 4096;
+  double threads = (double)blocks * 256;
+  {
+    double t = time_it([&] { hipLaunchKernelGGL(k_fma<16>, dim3(blocks), dim3(256), 0, 0, out, iters, 0.999f, 0.001f); }, 10);
+    double fl = threads * iters * 16 * 2;
+    printf("MB-FMA: %.2f TFLOP/s (%.3f ms)\n", fl / t * 1e-12, t * 1e3);
+  }
+  {
+    double t = time_it([&] { hipLaunchKernelGGL((k_mix<8, 0>), dim3(blocks), dim3(256), 0, 0, out, iters, 0.999f, 0.001f); }, 10);
+    double tr = threads * iters * 8;
+    printf("MB-TRANS: %.3f Tsin/s = %.2f per clk per CU at 2.4GHz (%.3f ms)\n", tr / t * 1e-12, tr / t / (CU * 2.4e9), t * 1e3);
+  }
+#define MIX(T, K) { double t = time_it([&] { hipLaunchKernelGGL((k_mix<T, K>), dim3(blocks), dim3(256), 0, 0, out, iters, 0.999f, 0.001f); }, 10); \
+    double wi = (double)blocks * 4 * iters; /* wave-iterations */ \
+    double slots = t * CU * 2.4e9 / wi; /* cycles per wave-iteration per CU */ \
+    printf("MB-MIX T=%d K=%2d: %.3f ms, CU-cycles per wave-iter %.2f (x4 SIMD = %.2f SIMD-cycles)\n", T, K, t * 1e3, slots, slots * 4); }
+  MIX(2, 0) MIX(2, 2) MIX(2, 4) MIX(2, 6) MIX(2, 8) MIX(2, 12) MIX(2, 16) MIX(2, 24)
+  MIX(4, 0) MIX(4, 8) MIX(4, 16)
+  // accuracy of builtins on r in [0,1)
+  {
+    const int n = 1 << 24;
+    std::vector<float> r(n);
+    for (int i = 0; i < n; ++i) r[i] = (float)((double)i / n) ;
+    float *dr, *a, *b, *c, *d;
+    CK(hipMalloc(&dr, n * 4)); CK(hipMalloc(&a, n * 4)); CK(hipMalloc(&b, n * 4)); CK(hipMalloc(&c, n * 4)); CK(hipMalloc(&d, n * 4));
+    CK(hipMemcpy(dr, r.data(), n * 4, hipMemcpyHostToDevice));
+    hipLaunchKernelGGL(k_trig_acc, dim3(n / 256), dim3(256), 0, 0, dr, a, b, c, d, n);
+    CK(hipDeviceSynchronize());
+    std::vector<float> sh(n), ch(n), sp(n), cp(n);
+    CK(hipMemcpy(sh.data(), a, n * 4, hipMemcpyDeviceToHost)); CK(hipMemcpy(ch.data(), b, n * 4, hipMemcpyDeviceToHost));
+    CK(hipMemcpy(sp.data(), c, n * 4, hipMemcpyDeviceToHost)); CK(hipMemcpy(cp.data(), d, n * 4, hipMemcpyDeviceToHost));
+    double mh = 0, mp = 0, rh = 0, rp = 0;
+    for (int i = 0; i < n; ++i) {
+      double th = 2 * M_PI * (double)r[i];
+      double es = sin(th), ec = cos(th);
+      double e1 = fmax(fabs(sh[i] - es), fabs(ch[i] - ec));
+      double e2 = fmax(fabs(sp[i] - es), fabs(cp[i] - ec));
+      mh = fmax(mh, e1); mp = fmax(mp, e2);
+      rh += (sh[i] - es) * (sh[i] - es) + (ch[i] - ec) * (ch[i] - ec);
+      rp += (sp[i] - es) * (sp[i] - es) + (cp[i] - ec) * (cp[i] - ec);
+    }
+    printf("trig accuracy over 2^24 pts in [0,1) rev: HW max abs %.3e rms %.3e | sincospif max abs %.3e rms %.3e\n", mh, sqrt(rh / (2.0 * n)), mp, sqrt(rp / (2.0 * n)));
+  }
+  printf("done\n");
+  return 0;
+}

@@ -37,6 +37,19 @@ def fhd_workspace_bytes(M: int, N: int, batch: int = 1, is_q: bool = False, **op
     return int(_lib.load().fhd_workspace_bytes(int(M), int(N), int(batch), int(bool(is_q)), ctypes.byref(o)))
 
 
+def fhd_describe_plan(M: int, N: int, batch: int = 1, is_q: bool = False, **opts) -> dict:
+    """The launch plan (group size, tile, passes, record size, workspace) for these sizes."""
+    o = make_opts(**opts)
+    info = _lib.FhdPlanInfo()
+    _lib.check(_lib.load().fhd_describe_plan(int(M), int(N), int(batch), int(bool(is_q)),
+                                             ctypes.byref(o), ctypes.byref(info)))
+    return {k: getattr(info, k) for k, _ in _lib.FhdPlanInfo._fields_}
+
+
+def resolved_voxels_per_lane(M: int, N: int, batch: int = 1, is_q: bool = False, **opts) -> int:
+    return fhd_describe_plan(M, N, batch, is_q, **opts)["voxels_per_lane"]
+
+
 def _dev_f32(t: torch.Tensor, name: str) -> torch.Tensor:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")

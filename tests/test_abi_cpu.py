@@ -142,3 +142,23 @@ def test_workspace_bytes(lib):
     assert ws(8, 64, is_q=1, trig=1, voxels_per_lane=4) == 8 * 16 * 4 // 256 * 256 + 256 * (8 * 16 * 4 % 256 > 0)
     # batch 5 = passes of 4 and 1 vectors, V forced to 1 (HW): strides 3+12->16 and 3+3->8
     assert ws(100, 50, batch=5, trig=1) == (100 * 16 * 4 + 255) // 256 * 256 + (100 * 8 * 4 + 255) // 256 * 256
+
+
+def test_describe_plan(lib):
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan
+    # the 128^3 benchmark shape: 16 voxels per lane on the HW path, 8 on the accurate one
+    hw = fhd_describe_plan(262144, 128 ** 3, trig="hw")
+    acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
+    assert hw["voxels_per_lane"] == 16 and acc["voxels_per_lane"] == 8
+    assert hw["record_dwords"] == 52 and acc["record_dwords"] == 32
+    assert hw["workspace_bytes"] == lib.fhd_workspace_bytes(262144, 128 ** 3, 1, 0, ctypes.byref(_opts(trig=1)))
+    assert hw["padded_samples"] == 262144 and hw["passes"] == 1
+    # tiny N shrinks the group; batches force one voxel per lane and split into passes
+    assert fhd_describe_plan(1000, 5, trig="hw")["voxels_per_lane"] == 1
+    assert fhd_describe_plan(1000, 5, trig="hw", voxels_per_lane=16)["voxels_per_lane"] == 4
+    b = fhd_describe_plan(500001, 96 ** 3, batch=19)
+    assert b["voxels_per_lane"] == 1 and b["passes"] == 3 and b["padded_samples"] == 500004
+    assert fhd_describe_plan(1000, 100, sum="plain")["tile"] == 1000
+    info = _lib.FhdPlanInfo()
+    assert lib.fhd_describe_plan(-1, 4, 1, 0, None, ctypes.byref(info)) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert lib.fhd_describe_plan(4, 4, 1, 0, None, None) == _lib.FHD_ERR_INVALID_ARGUMENT
