@@ -27,9 +27,13 @@ FLOP_PER_PAIR = {"fhd": 14, "q": 10}   # phase 5 + reduction 1 + complex MAC 8 (
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", 16): {
-        "kernel_sha256": "73120cd474cdf845",
-        "fetch_bytes": 438359 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
-        "profile": "profiles/gather_128cubed_x_262144_hw_counters.md"},
+        "kernel_sha256": "f6072e9b1ffa6677",
+        "fetch_bytes": 438354 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
+        "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals", "accurate", "blocked", 16): {
+        "kernel_sha256": "f6072e9b1ffa6677",
+        "fetch_bytes": 471127 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
+        "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
 }
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",

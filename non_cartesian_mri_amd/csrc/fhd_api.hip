@@ -61,7 +61,6 @@ struct Plan {
   int V;
   int stages;
   int64_t M, N, mpad, tile;
-  int32_t stagger;
   int batch;
   int npass;           // gather passes (batch groups)
   int bc[40];          // vectors per pass (<= 31 + 4 for batch <= 512)
@@ -70,20 +69,16 @@ struct Plan {
 };
 
 // Voxel-group size when the caller leaves it to the library (measured on
-// MI355X at 128^3 x 262,144): the HW-trig gather is fastest with 16 voxels
-// per lane, the accurate one with 8 (its longer per-sample trig pushes 16 into
-// register spills).  Smaller N shrinks the group so that at least ~2 waves per
-// SIMD remain (256 CUs x 4 SIMDs x 2 waves x 64 lanes).
+// MI355X at 128^3 x 262,144 and Q at 128^3 x 2^20: 16 voxels per lane is
+// fastest for both trig paths).  Smaller N shrinks the group so that at least
+// ~2 waves per SIMD remain (256 CUs x 4 SIMDs x 2 waves x 64 lanes).
 int auto_voxels_per_lane(int64_t N, int trig) {
+  (void)trig;
   const int64_t lanes_wanted = 256LL * 4 * 2 * 64;
-  int v = trig == FHD_TRIG_HW ? 16 : 8;
+  int v = 16;
   while (v > 1 && (N + v - 1) / v < lanes_wanted) v /= 2;
   return v;
 }
-
-// Spacing (in samples) between the starting points of successive waves; a
-// small gain for 8-voxel groups, a loss for 16 (measured).
-int32_t auto_stagger(int V) { return V <= 8 ? 128 : 0; }
 
 fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
   fhd_opts d;
@@ -129,7 +124,6 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     while (t * t < p.mpad && t < 8192) t *= 2;
     p.tile = t;
   }
-  p.stagger = auto_stagger(p.V);
   p.ws_bytes = 0;
   for (int i = 0; i < p.npass; ++i) {
     int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);
@@ -196,7 +190,7 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
       if (e != hipSuccess) result = fail(FHD_ERR_HIP, "records kernel launch: %s", hipGetErrorString(e));
     }
     if (result == FHD_OK && (p.stages & FHD_STAGE_GATHER)) {
-      ncmri::GatherArgs ga{rec, p.mpad, p.tile, x, y, z, N, (float2*)(out + (int64_t)b0 * N), p.stagger};
+      ncmri::GatherArgs ga{rec, p.mpad, p.tile, x, y, z, N, (float2*)(out + (int64_t)b0 * N)};
       hipError_t e = ncmri::launch_gather(L, p.sum == FHD_SUM_KAHAN, ga, s);
       if (e != hipSuccess) result = fail(FHD_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
     }

@@ -58,7 +58,6 @@ struct GatherArgs {
   const float* x; const float* y; const float* z;
   int64_t N;
   float2* out;           // first output vector of this pass ([BC][N])
-  int32_t stagger;       // samples between the starting points of successive waves (0: all start at 0)
 };
 
 // Launchers: return hipSuccess or the launch error.

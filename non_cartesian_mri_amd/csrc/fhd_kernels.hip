@@ -349,17 +349,7 @@ struct Gather {
       }
     };
 
-    // Waves walk the samples from different starting points (the sum does not
-    // depend on the order) so that the waves sharing a scalar cache are not
-    // all waiting on the same record line at the same time.
-    int32_t start = 0;
-    if (a.stagger > 0 && mpad > 0) {
-      const uint32_t wave = __builtin_amdgcn_readfirstlane((uint32_t)(lane >> 6));
-      const int64_t off = (int64_t)((wave * 7u) & 15u) * a.stagger;
-      start = (int32_t)((off % mpad) / kUnroll * kUnroll);
-    }
-    run_range(start, mpad);
-    run_range(0, start);
+    run_range(0, mpad);
 
     // write-out: out[b][n0 + j]
 #pragma unroll

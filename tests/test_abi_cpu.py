@@ -146,11 +146,11 @@ def test_workspace_bytes(lib):
 
 def test_describe_plan(lib):
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
-    # the 128^3 benchmark shape: 16 voxels per lane on the HW path, 8 on the accurate one
+    # the 128^3 benchmark shape: 16 voxels per lane on both trig paths
     hw = fhd_describe_plan(262144, 128 ** 3, trig="hw")
     acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
-    assert hw["voxels_per_lane"] == 16 and acc["voxels_per_lane"] == 8
-    assert hw["record_dwords"] == 52 and acc["record_dwords"] == 32
+    assert hw["voxels_per_lane"] == 16 and acc["voxels_per_lane"] == 16
+    assert hw["record_dwords"] == 52 and acc["record_dwords"] == 56
     assert hw["workspace_bytes"] == lib.fhd_workspace_bytes(262144, 128 ** 3, 1, 0, ctypes.byref(_opts(trig=1)))
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1
     # tiny N shrinks the group; batches force one voxel per lane and split into passes
