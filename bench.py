@@ -27,12 +27,12 @@ FLOP_PER_PAIR = {"fhd": 14, "q": 10}   # phase 5 + reduction 1 + complex MAC 8 (
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", 16): {
-        "kernel_sha256": "f6072e9b1ffa6677",
-        "fetch_bytes": 438354 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
+        "kernel_sha256": "9c3822754b2dc6cb",
+        "fetch_bytes": 984615 * 1024 * 2.0, "write_bytes": 262149 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", 16): {
-        "kernel_sha256": "f6072e9b1ffa6677",
-        "fetch_bytes": 471127 * 1024 * 2.0, "write_bytes": 16384 * 1024 * 1.0,
+        "kernel_sha256": "9c3822754b2dc6cb",
+        "fetch_bytes": 1046113 * 1024 * 2.0, "write_bytes": 262148 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
 }
 WORKLOADS = {
@@ -168,30 +168,34 @@ def main():
     for _ in range(args.warmup):
         stage("mu")
         stage("gather")
+        stage("reduce")
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
+    for e0, e1, e2, e3 in ev:
         e0.record(stream)
         stage("mu")
         e1.record(stream)
         stage("gather")
         e2.record(stream)
+        stage("reduce")
+        e3.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(c) for a, b, c in ev])
-    gather_ms = np.array([b.elapsed_time(c) for a, b, c in ev])
-    mu_ms = np.array([a.elapsed_time(b) for a, b, c in ev])
+    step_ms = np.array([a.elapsed_time(d) for a, b, c, d in ev])
+    gather_ms = np.array([b.elapsed_time(c) for a, b, c, d in ev])
+    mu_ms = np.array([a.elapsed_time(b) for a, b, c, d in ev])
+    reduce_ms = np.array([c.elapsed_time(d) for a, b, c, d in ev])
     ms_per_step = wall * 1e3 / args.steps
     pairs = p.N * p.M * p.B
     value = pairs / (ms_per_step * 1e-3) / 1e9
     # launches per gather stage: one per batch pass
     g_avg = float(gather_ms.mean())
     achieved = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
-    from non_cartesian_mri_amd.fhd import resolved_voxels_per_lane
-    vpl = resolved_voxels_per_lane(p.M, p.N, p.B, is_q, **opts)
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan
+    plan = fhd_describe_plan(p.M, p.N, p.B, is_q, **opts)
+    vpl = plan["voxels_per_lane"]
     traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, vpl, g_avg)
     res = {
         "metric": METRIC,
@@ -208,18 +212,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "voxels": p.N,
                    "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": args.sum,
-                   "voxels_per_lane": vpl, "tile": args.tile or "auto",
+                   "voxels_per_lane": vpl, "tile": plan["tile"],
+                   "sample_splits": plan["sample_splits"], "gather_launches": plan["passes"],
                    "parallelism": "single GPU, data-parallel over voxels"},
         "timing_ms": {"step_event_median": round(float(np.median(step_ms)), 4),
                       "gather_event_mean": round(g_avg, 4),
                       "gather_event_min": round(float(gather_ms.min()), 4),
-                      "mu_event_mean": round(float(mu_ms.mean()), 4)},
+                      "mu_event_mean": round(float(mu_ms.mean()), 4),
+                      "reduce_event_mean": round(float(reduce_ms.mean()), 4)},
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic, 3),
                      "traffic_unit": "GB/s (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE / launch time)",
                      "traffic_detail": traffic_detail,
-                     "kernel": "gather_kernel (one launch per step)",
+                     "kernel": "gather_kernel (its launches in one step, timed alone; the per-sample "
+                               "and reduce kernels are outside this interval)",
                      "flop_per_pair": FLOP_PER_PAIR[p.kind]},
     }
     if args.cpu_seconds > 0:

@@ -77,22 +77,29 @@ typedef enum fhd_sum {
   FHD_SUM_PLAIN = 2    /* one running fp32 sum over all samples */
 } fhd_sum;
 
-/* Pipeline stages (the two loops produced by loop fission). */
+/* Pipeline stages: the two loops produced by loop fission, plus the
+ * reduction of the sample-split rows' partial sums. */
 enum {
   FHD_STAGE_MU = 1,     /* per-sample kernel: Mu (or |phi|^2) and sample records */
-  FHD_STAGE_GATHER = 2, /* per-voxel gather kernel */
-  FHD_STAGE_ALL = 3
+  FHD_STAGE_GATHER = 2, /* per-voxel gather kernel (one launch row per sample split) */
+  FHD_STAGE_REDUCE = 4, /* adds the rows' partial sums into the output (no-op with one row) */
+  FHD_STAGE_ALL = 7
 };
 
 /* Options; pass NULL for all defaults (accurate trig, blocked sum, automatic
- * tuning, library-allocated workspace, both stages). */
+ * tuning, library-allocated workspace, both stages).  Start from
+ * fhd_default_opts() so that fields added later keep their defaults. */
 typedef struct fhd_opts {
   int32_t trig;            /* fhd_trig, default FHD_TRIG_ACCURATE */
   int32_t sum;             /* fhd_sum, default FHD_SUM_BLOCKED */
   int32_t voxels_per_lane; /* 0 = automatic, else 1, 2, 4, 8 or 16 */
   int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
-  int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL */
-  int32_t reserved;        /* must be 0 */
+  int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL.  Stages run in
+                              separate calls must use the same sizes, options and
+                              workspace, in the order MU, GATHER, REDUCE */
+  int32_t sample_splits;   /* 0 = automatic; else 1..1024 launch rows that each sum a
+                              contiguous share of the samples (partial sums, then a
+                              fixed-order reduction); FHD_SUM_PLAIN always uses 1 */
   void* workspace;         /* device buffer, or NULL: the library then allocates it
                               stream-ordered (hipMallocAsync/hipFreeAsync) for this
                               call; running the stages in separate calls requires a
@@ -105,7 +112,8 @@ void fhd_default_opts(fhd_opts* opts);
 
 /* Workspace bytes fhd_compute (is_q = 0) or q_compute (is_q = 1) needs for
  * these sizes and options (opts may be NULL).  Returns 0 on invalid arguments.
- * The workspace holds one packed record per sample (and per batch group). */
+ * The workspace holds one packed record per sample (and per batch group) and,
+ * when the samples are split across launch rows, the rows' partial sums. */
 size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t is_q,
                            const fhd_opts* opts);
 
@@ -143,6 +151,8 @@ typedef struct fhd_plan_info {
   int32_t record_dwords;    /* dwords per sample record of the first pass */
   int64_t padded_samples;   /* M rounded up to the record padding */
   size_t workspace_bytes;   /* = fhd_workspace_bytes(...) */
+  int32_t sample_splits;    /* launch rows splitting the samples (1: no reduction step) */
+  int32_t reserved;         /* 0 */
 } fhd_plan_info;
 
 /* Fills *info with the plan for these sizes and options (opts may be NULL);

@@ -27,7 +27,8 @@ FHD_SUM_PLAIN = 2
 # stages
 FHD_STAGE_MU = 1
 FHD_STAGE_GATHER = 2
-FHD_STAGE_ALL = 3
+FHD_STAGE_REDUCE = 4
+FHD_STAGE_ALL = 7
 
 # every symbol the header declares
 EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "q_compute",
@@ -41,7 +42,7 @@ class FhdOpts(ctypes.Structure):
         ("voxels_per_lane", ctypes.c_int32),
         ("tile", ctypes.c_int32),
         ("stages", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("sample_splits", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -55,6 +56,8 @@ class FhdPlanInfo(ctypes.Structure):
         ("record_dwords", ctypes.c_int32),
         ("padded_samples", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
+        ("sample_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -61,6 +61,9 @@ struct Plan {
   int V;
   int stages;
   int64_t M, N, mpad, tile;
+  int32_t splits;      // launch rows splitting the samples (partial sums + reduce when > 1)
+  int64_t m_split;     // samples per row
+  size_t partial_bytes;
   int batch;
   int npass;           // gather passes (batch groups)
   int bc[40];          // vectors per pass (<= 31 + 4 for batch <= 512)
@@ -68,16 +71,62 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// Voxel-group size when the caller leaves it to the library (measured on
-// MI355X at 128^3 x 262,144 and Q at 128^3 x 2^20: 16 voxels per lane is
-// fastest for both trig paths).  Smaller N shrinks the group so that at least
-// ~2 waves per SIMD remain (256 CUs x 4 SIMDs x 2 waves x 64 lanes).
-int auto_voxels_per_lane(int64_t N, int trig) {
-  (void)trig;
-  const int64_t lanes_wanted = 256LL * 4 * 2 * 64;
-  int v = 16;
-  while (v > 1 && (N + v - 1) / v < lanes_wanted) v /= 2;
-  return v;
+// Launch-shape choices when the caller leaves them to the library; all
+// measured on MI355X (256 CUs x 4 SIMDs).  Waves of one gather launch all do
+// the same work, so the total wave count should be a whole number of
+// "rounds" of resident waves: 3 per SIMD for the 16-voxel kernels (129-170
+// VGPRs), 4 for smaller ones -- hence multiples of 1024 x lcm(3, 4) = 12288.
+constexpr int64_t kSimds = 256LL * 4;
+constexpr int64_t kWaveQuantum = kSimds * 12;
+constexpr int64_t kMinSplitSamples = 256;  // samples per launch row at least
+constexpr int32_t kMaxSplits = 1024;
+
+int64_t waves_for(int64_t N, int V) { return ((N + V - 1) / V + 63) / 64; }
+
+int32_t max_splits(int64_t mpad) {
+  int64_t cap = mpad / kMinSplitSamples;
+  if (cap > kMaxSplits) cap = kMaxSplits;
+  return (int32_t)(cap < 1 ? 1 : cap);
+}
+
+// Voxel group: 16 voxels per lane (fastest for both trig paths at 128^3),
+// unless even the most sample splits cannot give every SIMD 3 waves; then the
+// largest group that can (or 1).
+int auto_voxels_per_lane(int64_t N, int64_t mpad) {
+  const int64_t smax = max_splits(mpad);
+  for (int v = 16; v > 1; v /= 2)
+    if (waves_for(N, v) * smax >= 3 * kSimds) return v;
+  return 1;
+}
+
+// Sample splits.  Rows that start at different points of the record stream
+// keep the waves of a CU from all waiting on the same scalar-cache line, and
+// extra rows fill the GPU when the voxel set is small.  Measured on MI355X:
+// gains saturate around 16K samples per row (128^3 x 262,144: 62.9 ms with 1
+// row, 54.5-54.9 ms with 12-96; Q 128^3 x 2^20: 282 ms -> 215 ms at 48 rows).
+// So: enough rows for a whole quantum of waves when the voxels alone do not
+// give one, and at most kSplitSamples samples per row, within a 2 GiB cap on
+// the rows' partial sums.
+constexpr int64_t kSplitSamples = 16384;
+constexpr int64_t kMaxPartialBytes = 2LL << 30;
+
+int32_t auto_splits(int64_t N, int V, int BC, int64_t mpad) {
+  const int64_t waves = waves_for(N, V);
+  if (waves <= 0 || mpad <= 0) return 1;
+  const int32_t smax = max_splits(mpad);
+  int64_t s_fill = 1;
+  if (waves < kWaveQuantum) {
+    s_fill = (kWaveQuantum + waves - 1) / waves;
+    for (int32_t s = 1; s <= smax; ++s)
+      if ((waves * s) % kWaveQuantum == 0) { s_fill = s; break; }
+  }
+  int64_t s = (mpad + kSplitSamples - 1) / kSplitSamples;
+  if (s < s_fill) s = s_fill;
+  const int64_t row_bytes = (int64_t)BC * N * (int64_t)sizeof(fhd_c32);
+  const int64_t s_mem = row_bytes > 0 ? kMaxPartialBytes / row_bytes : s;
+  if (s > s_mem) s = s_mem;
+  if (s > smax) s = smax;
+  return (int32_t)(s < 1 ? 1 : s);
 }
 
 fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
@@ -92,7 +141,10 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   if (o->sum != FHD_SUM_BLOCKED && o->sum != FHD_SUM_KAHAN && o->sum != FHD_SUM_PLAIN) return fail(FHD_ERR_INVALID_ARGUMENT, "unknown sum %d", o->sum);
   if (o->tile < 0) return fail(FHD_ERR_INVALID_ARGUMENT, "tile must be >= 0");
   if (o->stages < 0 || o->stages > FHD_STAGE_ALL) return fail(FHD_ERR_INVALID_ARGUMENT, "unknown stages mask %d", o->stages);
-  if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  if ((o->stages & FHD_STAGE_MU) && (o->stages & FHD_STAGE_REDUCE) && !(o->stages & FHD_STAGE_GATHER))
+    return fail(FHD_ERR_INVALID_ARGUMENT, "stages mask %d skips the gather between mu and reduce", o->stages);
+  if (o->sample_splits < 0 || o->sample_splits > kMaxSplits)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "sample_splits must be in [0, %d] (got %d)", kMaxSplits, o->sample_splits);
   int V = o->voxels_per_lane;
   if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16) return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8 or 16 (got %d)", V);
   p.is_q = is_q;
@@ -111,7 +163,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
   } else if (V == 0) {
-    V = auto_voxels_per_lane(N, o->trig);
+    V = auto_voxels_per_lane(N, p.mpad);
   }
   while (V > 1 && V > N) V /= 2;  // the first group must be complete
   p.V = V;
@@ -124,6 +176,18 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     while (t * t < p.mpad && t < 8192) t *= 2;
     p.tile = t;
   }
+  // sample splits: one launch row per split, partial sums reduced afterwards
+  int32_t splits = o->sample_splits;
+  if (o->sum == FHD_SUM_PLAIN) splits = 1;  // a single running sum by definition
+  else if (splits == 0) splits = auto_splits(N, V, p.bc[0], p.mpad);
+  if (p.mpad == 0) splits = 1;
+  p.m_split = p.mpad;
+  if (splits > 1) {
+    p.m_split = (p.mpad + splits - 1) / splits;
+    p.m_split = (p.m_split + ncmri::kUnroll - 1) / ncmri::kUnroll * ncmri::kUnroll;
+    splits = (int32_t)((p.mpad + p.m_split - 1) / p.m_split);  // no empty rows
+  }
+  p.splits = splits;
   p.ws_bytes = 0;
   for (int i = 0; i < p.npass; ++i) {
     int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);
@@ -131,6 +195,9 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     p.ws_bytes += (p.pass_bytes[i] + 255) / 256 * 256;
     if (!ncmri::gather_supported(is_q, p.V, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no kernel for V=%d BC=%d", p.V, p.bc[i]);
   }
+  // one partial-sum buffer, reused by every pass (passes run in stream order)
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
+  p.ws_bytes += (p.partial_bytes + 255) / 256 * 256;
   return FHD_OK;
 }
 
@@ -163,8 +230,12 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
     for (const Range& r : ins)
       if (overlaps(wr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "workspace overlaps an input array");
   } else if (p.stages != FHD_STAGE_ALL && p.ws_bytes > 0) {
-    return fail(FHD_ERR_WORKSPACE, "running one stage alone needs a caller workspace");
+    return fail(FHD_ERR_WORKSPACE, "running stages separately needs a caller workspace");
   }
+  if (p.npass > 1 && p.splits > 1 &&
+      ((p.stages & FHD_STAGE_GATHER) != 0) != ((p.stages & FHD_STAGE_REDUCE) != 0))
+    return fail(FHD_ERR_INVALID_ARGUMENT,
+                "batch passes share the partial-sum buffer: run GATHER and REDUCE in the same call");
   if (N == 0) return FHD_OK;
   st = check_device();
   if (st != FHD_OK) return st;
@@ -178,6 +249,12 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   }
   fhd_status result = FHD_OK;
   char* base = (char*)ws;
+  float2* partial = nullptr;
+  if (p.partial_bytes > 0) {
+    size_t recs = 0;
+    for (int i = 0; i < p.npass; ++i) recs += (p.pass_bytes[i] + 255) / 256 * 256;
+    partial = (float2*)(base + recs);
+  }
   int b0 = 0;
   for (int i = 0; i < p.npass && result == FHD_OK; ++i) {
     ncmri::Layout L{is_q, p.trig, p.V, p.bc[i], ncmri::header_dwords(p.trig),
@@ -189,10 +266,15 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
       hipError_t e = ncmri::launch_records(L, ra, s);
       if (e != hipSuccess) result = fail(FHD_ERR_HIP, "records kernel launch: %s", hipGetErrorString(e));
     }
-    if (result == FHD_OK && (p.stages & FHD_STAGE_GATHER)) {
-      ncmri::GatherArgs ga{rec, p.mpad, p.tile, x, y, z, N, (float2*)(out + (int64_t)b0 * N)};
-      hipError_t e = ncmri::launch_gather(L, p.sum == FHD_SUM_KAHAN, ga, s);
-      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "gather kernel launch: %s", hipGetErrorString(e));
+    if (result == FHD_OK && (p.stages & (FHD_STAGE_GATHER | FHD_STAGE_REDUCE))) {
+      ncmri::GatherArgs ga{rec, p.mpad, p.tile, x, y, z, N, (float2*)(out + (int64_t)b0 * N),
+                           p.m_split, p.splits > 1 ? partial : nullptr};
+      const bool kahan = p.sum == FHD_SUM_KAHAN;
+      hipError_t e = hipSuccess;
+      if (p.stages & FHD_STAGE_GATHER) e = ncmri::launch_gather(L, kahan, p.splits, ga, s);
+      if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE))
+        e = ncmri::launch_reduce(p.bc[i], kahan, p.splits, ga, s);
+      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "gather/reduce kernel launch: %s", hipGetErrorString(e));
     }
     base += (p.pass_bytes[i] + 255) / 256 * 256;
     b0 += p.bc[i];
@@ -239,6 +321,8 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->record_dwords = p.npass > 0 ? ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]) : 0;
     info->padded_samples = p.mpad;
     info->workspace_bytes = p.ws_bytes;
+    info->sample_splits = p.splits;
+    info->reserved = 0;
     return FHD_OK;
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");

@@ -58,11 +58,17 @@ struct GatherArgs {
   const float* x; const float* y; const float* z;
   int64_t N;
   float2* out;           // first output vector of this pass ([BC][N])
+  int64_t m_split;       // samples per launch row (gridDim.y rows split the samples)
+  float2* partial;       // [rows][BC][N] partial sums when rows > 1, else nullptr
 };
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_records(const Layout& L, const RecordArgs& a, hipStream_t s);
-hipError_t launch_gather(const Layout& L, bool kahan, const GatherArgs& a, hipStream_t s);
+// With splits > 1 the gather writes the rows' partial sums to a.partial and
+// launch_reduce adds them into a.out (a no-op for splits == 1).
+hipError_t launch_gather(const Layout& L, bool kahan, int32_t splits, const GatherArgs& a,
+                         hipStream_t s);
+hipError_t launch_reduce(int BC, bool kahan, int32_t splits, const GatherArgs& a, hipStream_t s);
 bool gather_supported(int is_q, int V, int BC);
 
 }  // namespace ncmri

@@ -177,6 +177,10 @@ struct Gather {
   // carries enough VALU work to cover the next record's load (measured: a
   // gain for 24-32 dword records, a loss for shorter ones).
   static constexpr bool PIPE = STRIDE >= 24 && 2 * STRIDE <= 64 && kUnroll % 2 == 0;
+  // Samples per step of the plain regular loop (kUnroll must be a multiple).
+  // Measured on MI355X for 52-56 dword records: 4 is fastest for F^H D and
+  // the batched passes; Q spills scalar registers at 4 and runs best at 2.
+  static constexpr int RU = (STRIDE > 40 && QW) ? 2 : kUnroll;
 
   // dword offset of set s inside a record
   static constexpr int set_off(int s) { return QW ? (s == 0 ? H : H + 1 + 3 * (s - 1)) : H + 3 * s; }
@@ -235,6 +239,93 @@ struct Gather {
     }
   }
 
+  // Folds one tile's partial sums into the running totals (optionally
+  // Kahan-compensated).  rf_all: every set is in real form (Q, direct path).
+  __device__ static __forceinline__ void fold(bool direct, float (&A)[S], float (&Bq)[S],
+                                              float (&Cr)[S], float (&Tre)[S], float (&Tim)[S],
+                                              float (&Kre)[KAHAN ? S : 1],
+                                              float (&Kim)[KAHAN ? S : 1]) {
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      // real-form sets (Q weight w applied directly): re += w c, im += w s
+      const bool rf = QW && (q == 0 || direct);
+      const float dre = rf ? A[q] : A[q] - Bq[q];
+      const float dim = rf ? Bq[q] : A[q] + Cr[q];
+      if constexpr (KAHAN) {
+        const float yr = dre - Kre[q];
+        const float tr = Tre[q] + yr;
+        Kre[q] = (tr - Tre[q]) - yr;
+        Tre[q] = tr;
+        const float yi = dim - Kim[q];
+        const float ti = Tim[q] + yi;
+        Kim[q] = (ti - Tim[q]) - yi;
+        Tim[q] = ti;
+      } else {
+        Tre[q] += dre;
+        Tim[q] += dim;
+      }
+    }
+  }
+
+  // Sums the samples [lo, hi) (both multiples of kUnroll) tile by tile into
+  // the totals.  The regular (factored) and direct forms are separate
+  // instantiations so that the regular loop keeps only the group's first
+  // voxel in registers.
+  template <bool REG>
+  __device__ static __forceinline__ void sum_range(const float* __restrict__ rec, int32_t lo,
+                                                   int32_t hi, int32_t tile,
+                                                   const float (&vx)[V], const float (&vy)[V],
+                                                   const float (&vz)[V], float (&Tre)[S],
+                                                   float (&Tim)[S], float (&Kre)[KAHAN ? S : 1],
+                                                   float (&Kim)[KAHAN ? S : 1]) {
+    float A[S], Bq[S], Cr[S];  // tile partials
+    for (int32_t t0 = lo; t0 < hi; t0 += tile) {
+      const int32_t t1 = (hi - t0 > tile) ? t0 + tile : hi;
+#pragma unroll
+      for (int q = 0; q < S; ++q) { A[q] = 0.0f; Bq[q] = 0.0f; Cr[q] = 0.0f; }
+      const float* p = rec + (int64_t)t0 * STRIDE;
+      const float* pend = rec + (int64_t)t1 * STRIDE;
+      if constexpr (REG && PIPE) {
+        // Ping-pong over two SGPR-resident records.  Scalar loads may return
+        // out of order, so a wait covers every load in flight: the current
+        // record's first dword is consumed (forcing its wait) before the next
+        // record's loads are issued, and the fences keep the scheduler from
+        // hoisting those loads above that first use.  The next record's
+        // latency then overlaps one sample's VALU work.
+        const float x0 = vx[0], y0 = vy[0], z0 = vz[0];
+        float ra[STRIDE], rb[STRIDE];
+        load_record(ra, p);
+        for (; p < pend; p += 2 * STRIDE) {
+          const float pa = ra[0] * x0;
+          sched_fence();
+          load_record(rb, p + STRIDE);
+          sched_fence();
+          regular_step(ra, pa, x0, y0, z0, A, Bq, Cr);
+          const float pb = rb[0] * x0;
+          sched_fence();
+          load_record(ra, (p + 2 * STRIDE < pend) ? p + 2 * STRIDE : p);
+          sched_fence();
+          regular_step(rb, pb, x0, y0, z0, A, Bq, Cr);
+        }
+      } else if constexpr (REG) {
+        const float x0 = vx[0], y0 = vy[0], z0 = vz[0];
+        for (; p < pend; p += RU * STRIDE) {
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            const float* r = p + u * STRIDE;
+            regular_step(r, r[0] * x0, x0, y0, z0, A, Bq, Cr);
+          }
+        }
+      } else {
+        for (; p < pend; p += kUnroll * STRIDE) {
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) direct_step(p + u * STRIDE, vx, vy, vz, A, Bq, Cr);
+        }
+      }
+      fold(!REG, A, Bq, Cr, Tre, Tim, Kre, Kim);
+    }
+  }
+
   __device__ static void run(const GatherArgs& a) {
     const int64_t lane = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
     const int64_t n0 = lane * V;
@@ -263,11 +354,7 @@ struct Gather {
     }
     const bool wave_regular = __all(reg);
 
-    // real-form sets (Q weight w applied directly): re += w c, im += w s
-    auto real_form = [&](int q) -> bool { return QW && (q == 0 || !wave_regular); };
-
-    float A[S], Bq[S], Cr[S];          // tile partials
-    float Tre[S], Tim[S];              // running totals
+    float Tre[S], Tim[S];                          // running totals
     float Kre[KAHAN ? S : 1], Kim[KAHAN ? S : 1];  // Kahan compensations
 #pragma unroll
     for (int q = 0; q < S; ++q) {
@@ -275,83 +362,20 @@ struct Gather {
       if constexpr (KAHAN) { Kre[q] = 0.0f; Kim[q] = 0.0f; }
     }
 
-    const float* __restrict__ rec = a.rec;
+    // This launch row's share of the samples (the sample dimension is split
+    // across gridDim.y rows; the rows' partial sums are added by reduce_kernel).
+    const int32_t split = (int32_t)blockIdx.y;
     const int32_t mpad = (int32_t)a.mpad;
-    const int32_t tile = (int32_t)a.tile;
+    const int64_t lo64 = (int64_t)split * a.m_split;
+    const int32_t lo = (int32_t)(lo64 < mpad ? lo64 : mpad);
+    const int32_t hi = (int32_t)(lo64 + a.m_split < mpad ? lo64 + a.m_split : mpad);
+    if (wave_regular)
+      sum_range<true>(a.rec, lo, hi, (int32_t)a.tile, vx, vy, vz, Tre, Tim, Kre, Kim);
+    else
+      sum_range<false>(a.rec, lo, hi, (int32_t)a.tile, vx, vy, vz, Tre, Tim, Kre, Kim);
 
-    // Sums the samples [lo, hi) (both multiples of kUnroll) tile by tile.
-    auto run_range = [&](int32_t lo, int32_t hi) {
-      for (int32_t t0 = lo; t0 < hi; t0 += tile) {
-        const int32_t t1 = (hi - t0 > tile) ? t0 + tile : hi;
-#pragma unroll
-        for (int q = 0; q < S; ++q) { A[q] = 0.0f; Bq[q] = 0.0f; Cr[q] = 0.0f; }
-        if (wave_regular) {
-          if constexpr (PIPE) {
-            // Ping-pong over two SGPR-resident records.  Scalar loads may
-            // return out of order, so a wait covers every load in flight: the
-            // current record's first dword is consumed (forcing its wait)
-            // before the next record's loads are issued, and the fences keep
-            // the scheduler from hoisting those loads above that first use.
-            // The next record's latency then overlaps one sample's VALU work.
-            float ra[STRIDE], rb[STRIDE];
-            const float* p = rec + (int64_t)t0 * STRIDE;
-            const float* pend = rec + (int64_t)t1 * STRIDE;
-            load_record(ra, p);
-            for (; p < pend; p += 2 * STRIDE) {
-              const float pa = ra[0] * vx[0];
-              sched_fence();
-              load_record(rb, p + STRIDE);
-              sched_fence();
-              regular_step(ra, pa, vx[0], vy[0], vz[0], A, Bq, Cr);
-              const float pb = rb[0] * vx[0];
-              sched_fence();
-              load_record(ra, (p + 2 * STRIDE < pend) ? p + 2 * STRIDE : p);
-              sched_fence();
-              regular_step(rb, pb, vx[0], vy[0], vz[0], A, Bq, Cr);
-            }
-          } else {
-            for (const float* p = rec + (int64_t)t0 * STRIDE, *pend = rec + (int64_t)t1 * STRIDE;
-                 p < pend; p += kUnroll * STRIDE) {
-#pragma unroll
-              for (int u = 0; u < kUnroll; ++u) {
-                const float* r = p + u * STRIDE;
-                regular_step(r, r[0] * vx[0], vx[0], vy[0], vz[0], A, Bq, Cr);
-              }
-            }
-          }
-        } else {
-          for (const float* p = rec + (int64_t)t0 * STRIDE, *pend = rec + (int64_t)t1 * STRIDE;
-               p < pend; p += kUnroll * STRIDE) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) direct_step(p + u * STRIDE, vx, vy, vz, A, Bq, Cr);
-          }
-        }
-        // fold the tile into the totals
-#pragma unroll
-        for (int q = 0; q < S; ++q) {
-          const bool rf = real_form(q);
-          const float dre = rf ? A[q] : A[q] - Bq[q];
-          const float dim = rf ? Bq[q] : A[q] + Cr[q];
-          if constexpr (KAHAN) {
-            const float yr = dre - Kre[q];
-            const float tr = Tre[q] + yr;
-            Kre[q] = (tr - Tre[q]) - yr;
-            Tre[q] = tr;
-            const float yi = dim - Kim[q];
-            const float ti = Tim[q] + yi;
-            Kim[q] = (ti - Tim[q]) - yi;
-            Tim[q] = ti;
-          } else {
-            Tre[q] += dre;
-            Tim[q] += dim;
-          }
-        }
-      }
-    };
-
-    run_range(0, mpad);
-
-    // write-out: out[b][n0 + j]
+    // write-out: out[b][n0 + j], or this row's partial sums
+    float2* dst = a.partial ? a.partial + (int64_t)split * BC * a.N : a.out;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int64_t n = n0 + j;
@@ -359,12 +383,37 @@ struct Gather {
 #pragma unroll
         for (int b = 0; b < BC; ++b) {
           const int q = j * BC + b;
-          a.out[(int64_t)b * a.N + n] = make_float2(Tre[q], Tim[q]);
+          dst[(int64_t)b * a.N + n] = make_float2(Tre[q], Tim[q]);
         }
       }
     }
   }
 };
+
+// Adds the partial sums of the sample splits in split order (fixed, so the
+// result is deterministic): out[i] = sum_p partial[p][i], i < count.
+__global__ void __launch_bounds__(kWorkgroup)
+reduce_kernel(const float2* __restrict__ partial, float2* __restrict__ out, int64_t count,
+              int32_t splits, int32_t kahan) {
+  const int64_t i = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  if (i >= count) return;
+  float re = 0.0f, im = 0.0f, cr = 0.0f, ci = 0.0f;
+  for (int32_t p = 0; p < splits; ++p) {
+    const float2 v = partial[(int64_t)p * count + i];
+    if (kahan) {
+      const float yr = v.x - cr, tr = re + yr;
+      cr = (tr - re) - yr;
+      re = tr;
+      const float yi = v.y - ci, ti = im + yi;
+      ci = (ti - im) - yi;
+      im = ti;
+    } else {
+      re += v.x;
+      im += v.y;
+    }
+  }
+  out[i] = make_float2(re, im);
+}
 
 template <int V, int BC, bool QW, int TRIG, bool KAHAN>
 __global__ void __launch_bounds__(kWorkgroup) gather_kernel(GatherArgs a) {
@@ -427,13 +476,23 @@ hipError_t launch_records(const Layout& L, const RecordArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Layout& L, bool kahan, const GatherArgs& a, hipStream_t s) {
+hipError_t launch_gather(const Layout& L, bool kahan, int32_t splits, const GatherArgs& a,
+                         hipStream_t s) {
   GatherFn fn = select(L, kahan);
-  if (!fn) return hipErrorInvalidValue;
+  if (!fn || splits < 1 || (splits > 1) != (a.partial != nullptr)) return hipErrorInvalidValue;
   if (a.N <= 0) return hipSuccess;
   const int64_t lanes = (a.N + L.V - 1) / L.V;
   const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(int BC, bool kahan, int32_t splits, const GatherArgs& a, hipStream_t s) {
+  if (splits < 2 || !a.partial || a.N <= 0) return hipSuccess;
+  const int64_t count = (int64_t)BC * a.N;
+  const int64_t rblocks = (count + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)rblocks), dim3(kWorkgroup), 0, s, a.partial,
+                     a.out, count, splits, kahan ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def test_opts_struct_layout(lib):
     o = _lib.FhdOpts()
     o.trig = 77
     lib.fhd_default_opts(ctypes.byref(o))
-    assert (o.trig, o.sum, o.voxels_per_lane, o.tile, o.stages, o.reserved) == (0, 0, 0, 0, 3, 0)
+    assert (o.trig, o.sum, o.voxels_per_lane, o.tile, o.stages, o.sample_splits) == (0, 0, 0, 0, 7, 0)
     assert o.workspace is None and o.workspace_bytes == 0
 
 
@@ -93,9 +93,21 @@ def test_fhd_argument_errors(lib, kw, err):
     assert lib.fhd_last_error() != b""
 
 
+def test_stage_combinations(lib):
+    big = _opts(workspace=A + 0x10000000, workspace_bytes=1 << 30)
+    # mu + reduce without the gather between them
+    big.stages = _lib.FHD_STAGE_MU | _lib.FHD_STAGE_REDUCE
+    assert _fhd(lib, opts=big) == _lib.FHD_ERR_INVALID_ARGUMENT
+    # batch of 5 = two passes sharing one partial buffer: gather and reduce must run together
+    for st in (_lib.FHD_STAGE_GATHER, _lib.FHD_STAGE_REDUCE, _lib.FHD_STAGE_MU | _lib.FHD_STAGE_GATHER):
+        o = _opts(workspace=A + 0x10000000, workspace_bytes=1 << 30, stages=st, sample_splits=2)
+        assert _fhd(lib, M=4096, batch=5, opts=o) == _lib.FHD_ERR_INVALID_ARGUMENT
+        assert b"same call" in lib.fhd_last_error()
+
+
 @pytest.mark.parametrize("field,value", [
     ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 32),
-    ("tile", -4), ("stages", 4), ("reserved", 1),
+    ("tile", -4), ("stages", 8), ("sample_splits", -1), ("sample_splits", 1025),
 ])
 def test_bad_options(lib, field, value):
     assert _fhd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
@@ -108,6 +120,7 @@ def test_workspace_errors(lib):
     assert _fhd(lib, opts=small) == _lib.FHD_ERR_WORKSPACE
     # a single stage needs a caller workspace
     assert _fhd(lib, opts=_opts(stages=_lib.FHD_STAGE_MU)) == _lib.FHD_ERR_WORKSPACE
+    assert _fhd(lib, opts=_opts(stages=_lib.FHD_STAGE_REDUCE)) == _lib.FHD_ERR_WORKSPACE
     # workspace overlapping an input or the output
     assert _fhd(lib, opts=_opts(workspace=A + 0x6000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert _fhd(lib, opts=_opts(workspace=A + 0x100000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
@@ -130,6 +143,7 @@ def test_q_argument_errors(lib):
 def test_workspace_bytes(lib):
     # records: mpad * stride dwords, 256-byte aligned per pass
     def ws(M, N, batch=1, is_q=0, **kw):
+        kw.setdefault("sample_splits", 1)
         return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
     assert ws(-1, 4) == 0
     assert ws(4, 4, batch=0) == 0
@@ -142,6 +156,9 @@ def test_workspace_bytes(lib):
     assert ws(8, 64, is_q=1, trig=1, voxels_per_lane=4) == 8 * 16 * 4 // 256 * 256 + 256 * (8 * 16 * 4 % 256 > 0)
     # batch 5 = passes of 4 and 1 vectors, V forced to 1 (HW): strides 3+12->16 and 3+3->8
     assert ws(100, 50, batch=5, trig=1) == (100 * 16 * 4 + 255) // 256 * 256 + (100 * 8 * 4 + 255) // 256 * 256
+    # 3 sample splits add one [3][4][50] complex partial buffer shared by the passes
+    assert ws(1000, 50, batch=5, trig=1, sample_splits=3) == ((1000 * 16 * 4 + 255) // 256 * 256 + (1000 * 8 * 4 + 255) // 256 * 256
+                                                             + (3 * 4 * 50 * 8 + 255) // 256 * 256)
 
 
 def test_describe_plan(lib):
@@ -153,12 +170,39 @@ def test_describe_plan(lib):
     assert hw["record_dwords"] == 52 and acc["record_dwords"] == 56
     assert hw["workspace_bytes"] == lib.fhd_workspace_bytes(262144, 128 ** 3, 1, 0, ctypes.byref(_opts(trig=1)))
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1
+    # 262,144 samples -> 16 rows of 16384 samples
+    assert hw["sample_splits"] == 16
+    assert hw["workspace_bytes"] == 262144 * 52 * 4 + 16 * 128 ** 3 * 8
+    # small voxel sets are filled by splitting the samples (>= 256 samples per split)
+    assert fhd_describe_plan(65536, 64 ** 3, trig="hw")["sample_splits"] == 48
+    tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
+    assert tiny["voxels_per_lane"] == 1 and tiny["sample_splits"] == 8
+    assert fhd_describe_plan(1000, 5, trig="hw")["sample_splits"] == 3
+    # batched: 31 rows of 16384 samples wanted, partial sums capped at 2 GiB -> 18
+    assert fhd_describe_plan(500001, 96 ** 3, batch=16)["sample_splits"] == 18
+    # short sample lists with plenty of voxels: one row
+    assert fhd_describe_plan(4096, 256 ** 3)["sample_splits"] == 1
+    # explicit and plain-sum choices
+    assert fhd_describe_plan(262144, 128 ** 3, sample_splits=5)["sample_splits"] == 5
+    assert fhd_describe_plan(262144, 128 ** 3, sum="plain")["sample_splits"] == 1
+    assert fhd_describe_plan(10, 4096, sample_splits=7)["sample_splits"] == 3  # no empty rows (12 padded samples)
+    assert fhd_describe_plan(0, 4096)["sample_splits"] == 1
     # tiny N shrinks the group; batches force one voxel per lane and split into passes
-    assert fhd_describe_plan(1000, 5, trig="hw")["voxels_per_lane"] == 1
-    assert fhd_describe_plan(1000, 5, trig="hw", voxels_per_lane=16)["voxels_per_lane"] == 4
+    assert fhd_describe_plan(1000, 5, trig="hw")["voxels_per_lane"] == 1  # cannot fill the GPU anyway
+    assert fhd_describe_plan(1000, 5, trig="hw", voxels_per_lane=1)["voxels_per_lane"] == 1
     b = fhd_describe_plan(500001, 96 ** 3, batch=19)
     assert b["voxels_per_lane"] == 1 and b["passes"] == 3 and b["padded_samples"] == 500004
     assert fhd_describe_plan(1000, 100, sum="plain")["tile"] == 1000
     info = _lib.FhdPlanInfo()
     assert lib.fhd_describe_plan(-1, 4, 1, 0, None, ctypes.byref(info)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert lib.fhd_describe_plan(4, 4, 1, 0, None, None) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def test_describe_plan_zero_sizes(lib):
+    """Empty voxel or sample sets plan one row and no partial buffer (no division by zero)."""
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan
+    for M, N in ((100, 0), (0, 0), (0, 100)):
+        for is_q in (False, True):
+            r = fhd_describe_plan(M, N, is_q=is_q, trig="hw")
+            assert r["sample_splits"] == 1
+    assert fhd_describe_plan(100, 0)["workspace_bytes"] == (100 * 12 * 4 + 255) // 256 * 256

@@ -108,18 +108,22 @@ def test_deterministic(trig):
     assert np.array_equal(qa, qb)
 
 
-def test_split_stages_equal_one_call():
+@pytest.mark.parametrize("B,splits", [(1, 3), (3, 1), (3, 2)])
+def test_split_stages_equal_one_call(B, splits):
+    """mu / gather / reduce in separate calls give the one-call result bitwise
+    (multi-pass batches with sample splits run gather and reduce together)."""
     from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes
-    p = inputs.random_problem(207, M=999, L=12, B=3)
+    p = inputs.random_problem(207, M=999, L=12, B=B)
     d = dev_problem(p)
-    nb = fhd_workspace_bytes(p.M, p.N, p.B)
+    nb = fhd_workspace_bytes(p.M, p.N, p.B, sample_splits=splits)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
-    fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"],
-                stages="mu", workspace=ws)
-    out = fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"],
-                      stages="gather", workspace=ws)
+    args = (d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"])
+    out = torch.empty((p.B, p.N), dtype=torch.complex64, device="cuda:0")
+    steps = ["mu", "gather", "reduce"] if (B == 1 or splits == 1) else ["mu", "gather+reduce"]
+    for st in steps:
+        fhd_compute(*args, stages=st, workspace=ws, out=out, sample_splits=splits)
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy(), gpu_fhd(p, d))
+    assert np.array_equal(out.cpu().numpy(), gpu_fhd(p, d, sample_splits=splits))
 
 
 def test_non_default_stream(oracle_mod):
@@ -221,3 +225,27 @@ def test_permutation_invariance_within_tolerance():
                        p.phi[perm], p.D[:, perm], p.seed)
     b = gpu_fhd(q)
     assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(a)
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("sum_", ["blocked", "kahan"])
+@pytest.mark.parametrize("V", [1, 16])
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_sample_splits(small_grid, trig, sum_, V, splits):
+    """Samples split across launch rows (partial sums + fixed-order reduction);
+    1001 samples pad to 1004, so 5 rows get 204, 204, 204, 204 and 188."""
+    p, d, ref, qref = small_grid
+    got = gpu_fhd(p, d, trig=trig, sum=sum_, voxels_per_lane=V, tile=64, sample_splits=splits)
+    assert_close(got, ref, TOL[trig], f"fhd splits={splits} {trig}/{sum_}/V={V}")
+    gq = gpu_q(p, d, trig=trig, sum=sum_, voxels_per_lane=V, tile=64, sample_splits=splits)
+    assert_close(gq, qref, TOL[trig], f"q splits={splits} {trig}/{sum_}/V={V}")
+    again = gpu_fhd(p, d, trig=trig, sum=sum_, voxels_per_lane=V, tile=64, sample_splits=splits)
+    assert np.array_equal(got, again)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_batched_sample_splits(oracle_mod, splits):
+    """Batch passes of 16 and 2 vectors share one partial-sum buffer."""
+    p = inputs.random_problem(217, M=900, L=9, B=18)
+    ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
+    assert_close(gpu_fhd(p, trig="hw", sample_splits=splits), ref, TOL["hw"], f"batched splits={splits}")
