@@ -1,12 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark: F^H D voxel-sample pairs/s at 128^3 voxels x 262,144 samples on one MI355X.
 
-One step = one pass of the whole hot path (per-sample Mu/record kernel + gather
-kernel) over the 128^3 stack-of-spirals workload, inputs resident in HBM.
-Prints one JSON line.  The gather kernel (the dominant kernel) is also timed
-on its own with HIP events on the stream it is launched on; its algorithmic
-FLOP rate is reported against the MI355X FP32 vector peak.  The CPU oracle is
-timed on a bounded voxel sample of the same workload (rank 0, one GPU only).
+One step = one pass of the whole hot path (per-sample Mu/record kernel, gather
+kernel, reduction of the sample-split rows) over the 128^3 stack-of-spirals
+workload, inputs resident in HBM.  Prints one JSON line.  The gather stage (the
+dominant kernel) is also timed on its own with HIP events on the stream it is
+launched on.  Its roofline: for the matrix-core engine, one complex
+multiply-accumulate (8 FLOP) per voxel-sample pair against the MI355X FP32
+matrix peak; for the VALU engine, the direct formulation's 14 FLOP per pair
+against the FP32 vector peak.  The CPU oracle is timed on a bounded voxel
+sample of the same workload (rank 0, one GPU only).
 """
 from __future__ import annotations
 
@@ -19,19 +22,28 @@ import time
 import numpy as np
 
 METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roofline"
-FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
-FLOP_PER_PAIR = {"fhd": 14, "q": 10}   # phase 5 + reduction 1 + complex MAC 8 (Q: real MAC 4)
+FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 peak (vector, and dense matrix)
+# Direct formulation per voxel-sample pair: phase 5 + reduction 1 + complex MAC 8
+# (Q: real MAC 4), plus two transcendentals.
+FLOP_PER_PAIR = {"fhd": 14, "q": 10}
+# Factored formulation on the matrix cores: one complex MAC = 4 real MACs per
+# pair (the group phase and its sine are shared by 32 voxel columns).
+MFMA_FLOP_PER_PAIR = 8
 # HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Valid only for the kernel source they were taken on (sha256 prefix) and the
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
-    ("fhd_128cube_262144_spirals", "hw", "blocked", 16): {
-        "kernel_sha256": "9c3822754b2dc6cb",
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma"): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "2a3b0da1e02cb7f0",
+        "fetch_bytes": 1225644 * 1024 * 2.0, "write_bytes": 262144 * 1024 * 1.0,
+        "profile": "profiles/mfma_gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "valu"): {
+        "source": "fhd_kernels.hip", "kernel_sha256": "9c3822754b2dc6cb",
         "fetch_bytes": 984615 * 1024 * 2.0, "write_bytes": 262149 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals", "accurate", "blocked", 16): {
-        "kernel_sha256": "9c3822754b2dc6cb",
+    ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu"): {
+        "source": "fhd_kernels.hip", "kernel_sha256": "9c3822754b2dc6cb",
         "fetch_bytes": 1046113 * 1024 * 2.0, "write_bytes": 262148 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
 }
@@ -52,6 +64,7 @@ def parse():
     ap.add_argument("--config", default="fhd_128cube_262144_spirals", choices=sorted(WORKLOADS))
     ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
+    ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -100,18 +113,17 @@ def cpu_baseline(p, target_s: float) -> dict:
                       f"workload ({pairs:.3e} pairs, {t:.1f} s wall)"}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(name: str) -> str:
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc",
-                        "fhd_kernels.hip")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc", name)
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(config: str, trig: str, summ: str, voxels_per_lane: int, gather_ms: float):
+def traffic_for(config: str, trig: str, summ: str, engine: str, gather_ms: float):
     """Counter-derived HBM traffic (GB/s over the launch) or None if not measured for this kernel."""
-    t = TRAFFIC.get((config, trig, summ, voxels_per_lane))
-    if t is None or t["kernel_sha256"] != kernel_source_sha():
+    t = TRAFFIC.get((config, trig, summ, engine))
+    if t is None or t["kernel_sha256"] != kernel_source_sha(t["source"]):
         return None, None
     total = t["fetch_bytes"] + t["write_bytes"]
     return total / (gather_ms * 1e-3) / 1e9, {"bytes_per_launch": total, "fetch_bytes": t["fetch_bytes"],
@@ -152,7 +164,8 @@ def main():
          for k in ("kx", "ky", "kz", "x", "y", "z", "phi")}
     D = None if p.D is None else torch.from_numpy(np.ascontiguousarray(p.D)).to(dev)
     is_q = p.kind == "q"
-    opts = dict(trig=args.trig, sum=args.sum, voxels_per_lane=args.voxels_per_lane, tile=args.tile)
+    opts = dict(trig=args.trig, sum=args.sum, voxels_per_lane=args.voxels_per_lane, tile=args.tile,
+                engine=args.engine)
     ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, is_q, **opts)), dtype=torch.uint8, device=dev)
     out = torch.empty((p.B, p.N), dtype=torch.complex64, device=dev)
 
@@ -190,13 +203,22 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     pairs = p.N * p.M * p.B
     value = pairs / (ms_per_step * 1e-3) / 1e9
-    # launches per gather stage: one per batch pass
     g_avg = float(gather_ms.mean())
-    achieved = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
+    direct_tflops = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
     plan = fhd_describe_plan(p.M, p.N, p.B, is_q, **opts)
-    vpl = plan["voxels_per_lane"]
-    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, vpl, g_avg)
+    engine = {1: "valu", 2: "mfma"}[plan["engine"]]
+    if engine == "mfma":
+        achieved, bound = MFMA_FLOP_PER_PAIR * pairs / (g_avg * 1e-3) / 1e12, "mfma"
+        kernel = ("mfma_gather_kernel: its launch rows in one step, timed alone with the (empty on a "
+                  "grid) mfma_direct_kernel; records and reduction kernels are outside the interval")
+        per_pair = MFMA_FLOP_PER_PAIR
+    else:
+        achieved, bound = direct_tflops, "alu"
+        kernel = ("gather_kernel: its launches in one step, timed alone; the per-sample and reduce "
+                  "kernels are outside this interval")
+        per_pair = FLOP_PER_PAIR[p.kind]
+    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, engine, g_avg)
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -212,7 +234,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "name": args.config, "voxels": p.N,
                    "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": args.sum,
-                   "voxels_per_lane": vpl, "tile": plan["tile"],
+                   "engine": engine, "group_voxels": plan["voxels_per_lane"], "tile": plan["tile"],
                    "sample_splits": plan["sample_splits"], "gather_launches": plan["passes"],
                    "parallelism": "single GPU, data-parallel over voxels"},
         "timing_ms": {"step_event_median": round(float(np.median(step_ms)), 4),
@@ -220,14 +242,13 @@ def main():
                       "gather_event_min": round(float(gather_ms.min()), 4),
                       "mu_event_mean": round(float(mu_ms.mean()), 4),
                       "reduce_event_mean": round(float(reduce_ms.mean()), 4)},
-        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic, 3),
                      "traffic_unit": "GB/s (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE / launch time)",
                      "traffic_detail": traffic_detail,
-                     "kernel": "gather_kernel (its launches in one step, timed alone; the per-sample "
-                               "and reduce kernels are outside this interval)",
-                     "flop_per_pair": FLOP_PER_PAIR[p.kind]},
+                     "kernel": kernel, "flop_per_pair": per_pair,
+                     "direct_formulation_tflops": round(direct_tflops, 3)},
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)

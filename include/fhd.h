@@ -20,8 +20,9 @@
  *
  * Work is split as the pages' loop fission does (section 17.3 step 1, Figs.
  * 17.6/17.7): a per-sample kernel forms Mu and packs one k-space record per
- * sample; then a gather kernel with one group of voxels per lane sums every
- * sample (Figs. 17.9/17.10 gather after loop interchange).
+ * sample; then a gather kernel over groups of voxels sums every sample (Figs.
+ * 17.9/17.10 gather after loop interchange), on the vector ALU or, for voxel
+ * groups on a common grid, as a matrix-core product (fhd_engine).
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
@@ -77,6 +78,17 @@ typedef enum fhd_sum {
   FHD_SUM_PLAIN = 2    /* one running fp32 sum over all samples */
 } fhd_sum;
 
+/* Which kernels evaluate the gather.  Both compute the same sums (only the
+ * fp32 rounding differs) and share records, sample splits and reduction. */
+typedef enum fhd_engine {
+  FHD_ENGINE_AUTO = 0, /* MFMA, except with FHD_SUM_KAHAN or an explicit voxels_per_lane */
+  FHD_ENGINE_VALU = 1, /* vector-ALU kernels: a lane owns voxels_per_lane voxels, three-FMA
+                          complex multiply-accumulate per voxel and sample */
+  FHD_ENGINE_MFMA = 2  /* matrix-core kernels: groups of 32 / batch-group voxels, the
+                          per-sample sum as a 32x2 by 2x32 v_mfma_f32_32x32x2_f32 product
+                          (blocked or plain summation only) */
+} fhd_engine;
+
 /* Pipeline stages: the two loops produced by loop fission, plus the
  * reduction of the sample-split rows' partial sums. */
 enum {
@@ -87,12 +99,13 @@ enum {
 };
 
 /* Options; pass NULL for all defaults (accurate trig, blocked sum, automatic
- * tuning, library-allocated workspace, both stages).  Start from
+ * engine and tuning, library-allocated workspace, all stages).  Start from
  * fhd_default_opts() so that fields added later keep their defaults. */
 typedef struct fhd_opts {
   int32_t trig;            /* fhd_trig, default FHD_TRIG_ACCURATE */
   int32_t sum;             /* fhd_sum, default FHD_SUM_BLOCKED */
-  int32_t voxels_per_lane; /* 0 = automatic, else 1, 2, 4, 8 or 16 */
+  int32_t voxels_per_lane; /* VALU engine group size: 0 = automatic, else 1, 2, 4, 8 or 16;
+                              must be 0 with FHD_ENGINE_MFMA */
   int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
   int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL.  Stages run in
                               separate calls must use the same sizes, options and
@@ -100,7 +113,9 @@ typedef struct fhd_opts {
   int32_t sample_splits;   /* 0 = automatic; else 1..1024 launch rows that each sum a
                               contiguous share of the samples (partial sums, then a
                               fixed-order reduction); FHD_SUM_PLAIN always uses 1 */
-  void* workspace;         /* device buffer, or NULL: the library then allocates it
+  int32_t engine;          /* fhd_engine, default FHD_ENGINE_AUTO */
+  int32_t reserved;        /* must be 0 */
+  void* workspace;         /* device buffer (16-byte aligned), or NULL: the library then allocates it
                               stream-ordered (hipMallocAsync/hipFreeAsync) for this
                               call; running the stages in separate calls requires a
                               caller workspace that persists between them */
@@ -145,14 +160,15 @@ fhd_status q_compute(const float* kx, const float* ky, const float* kz,
 
 /* The launch plan the library derives from sizes and options. */
 typedef struct fhd_plan_info {
-  int32_t voxels_per_lane;  /* voxels owned by one lane (group size) */
+  int32_t voxels_per_lane;  /* voxel group size of the first pass (VALU: voxels owned by one
+                               lane; MFMA: voxels sharing one group phase) */
   int32_t tile;             /* samples per summation tile */
   int32_t passes;           /* gather launches (batch groups of 16, 8, 4, 2, 1 vectors) */
   int32_t record_dwords;    /* dwords per sample record of the first pass */
   int64_t padded_samples;   /* M rounded up to the record padding */
   size_t workspace_bytes;   /* = fhd_workspace_bytes(...) */
   int32_t sample_splits;    /* launch rows splitting the samples (1: no reduction step) */
-  int32_t reserved;         /* 0 */
+  int32_t engine;           /* FHD_ENGINE_VALU or FHD_ENGINE_MFMA */
 } fhd_plan_info;
 
 /* Fills *info with the plan for these sizes and options (opts may be NULL);

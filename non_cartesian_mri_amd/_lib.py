@@ -25,6 +25,10 @@ FHD_SUM_BLOCKED = 0
 FHD_SUM_KAHAN = 1
 FHD_SUM_PLAIN = 2
 # stages
+FHD_ENGINE_AUTO = 0
+FHD_ENGINE_VALU = 1
+FHD_ENGINE_MFMA = 2
+
 FHD_STAGE_MU = 1
 FHD_STAGE_GATHER = 2
 FHD_STAGE_REDUCE = 4
@@ -43,6 +47,8 @@ class FhdOpts(ctypes.Structure):
         ("tile", ctypes.c_int32),
         ("stages", ctypes.c_int32),
         ("sample_splits", ctypes.c_int32),
+        ("engine", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -57,7 +63,7 @@ class FhdPlanInfo(ctypes.Structure):
         ("padded_samples", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
         ("sample_splits", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("engine", ctypes.c_int32),
     ]
 
 

@@ -58,7 +58,8 @@ struct Plan {
   int is_q;
   int trig;
   int sum;
-  int V;
+  int engine;          // FHD_ENGINE_VALU or FHD_ENGINE_MFMA
+  int V;               // group size of the first pass
   int stages;
   int64_t M, N, mpad, tile;
   int32_t splits;      // launch rows splitting the samples (partial sums + reduce when > 1)
@@ -68,6 +69,7 @@ struct Plan {
   int npass;           // gather passes (batch groups)
   int bc[40];          // vectors per pass (<= 31 + 4 for batch <= 512)
   size_t pass_bytes[40];
+  size_t hdr_bytes;    // MFMA: header part of each pass's records (256-aligned)
   size_t ws_bytes;
 };
 
@@ -80,6 +82,8 @@ constexpr int64_t kSimds = 256LL * 4;
 constexpr int64_t kWaveQuantum = kSimds * 12;
 constexpr int64_t kMinSplitSamples = 256;  // samples per launch row at least
 constexpr int32_t kMaxSplits = 1024;
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 int64_t waves_for(int64_t N, int V) { return ((N + V - 1) / V + 63) / 64; }
 
@@ -99,6 +103,12 @@ int auto_voxels_per_lane(int64_t N, int64_t mpad) {
   return 1;
 }
 
+// The MFMA gather runs 4 waves per SIMD (<= 128 VGPRs, 34 KB of LDS per
+// 4-wave workgroup), one wave per 32 voxel groups.
+constexpr int64_t kMfmaWaveQuantum = kSimds * 4;
+
+int64_t mfma_waves(int64_t N, int V) { return ((N + V - 1) / V + 31) / 32; }
+
 // Sample splits.  Rows that start at different points of the record stream
 // keep the waves of a CU from all waiting on the same scalar-cache line, and
 // extra rows fill the GPU when the voxel set is small.  Measured on MI355X:
@@ -110,15 +120,14 @@ int auto_voxels_per_lane(int64_t N, int64_t mpad) {
 constexpr int64_t kSplitSamples = 16384;
 constexpr int64_t kMaxPartialBytes = 2LL << 30;
 
-int32_t auto_splits(int64_t N, int V, int BC, int64_t mpad) {
-  const int64_t waves = waves_for(N, V);
+int32_t auto_splits(int64_t waves, int64_t quantum, int64_t N, int BC, int64_t mpad) {
   if (waves <= 0 || mpad <= 0) return 1;
   const int32_t smax = max_splits(mpad);
   int64_t s_fill = 1;
-  if (waves < kWaveQuantum) {
-    s_fill = (kWaveQuantum + waves - 1) / waves;
+  if (waves < quantum) {
+    s_fill = (quantum + waves - 1) / waves;
     for (int32_t s = 1; s <= smax; ++s)
-      if ((waves * s) % kWaveQuantum == 0) { s_fill = s; break; }
+      if ((waves * s) % quantum == 0) { s_fill = s; break; }
   }
   int64_t s = (mpad + kSplitSamples - 1) / kSplitSamples;
   if (s < s_fill) s = s_fill;
@@ -147,6 +156,19 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     return fail(FHD_ERR_INVALID_ARGUMENT, "sample_splits must be in [0, %d] (got %d)", kMaxSplits, o->sample_splits);
   int V = o->voxels_per_lane;
   if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16) return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8 or 16 (got %d)", V);
+  if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
+  if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
+  int engine = o->engine;
+  if (engine == FHD_ENGINE_AUTO)
+    engine = (o->sum == FHD_SUM_KAHAN || V != 0) ? FHD_ENGINE_VALU : FHD_ENGINE_MFMA;
+  if (engine == FHD_ENGINE_MFMA && o->sum == FHD_SUM_KAHAN)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the MFMA engine sums blocked or plain, not Kahan");
+  if (engine == FHD_ENGINE_MFMA && V != 0)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane applies to the VALU engine only");
+  const bool mfma = engine == FHD_ENGINE_MFMA;
+  const int64_t pad = mfma ? ncmri::kMfmaChunk : ncmri::kUnroll;
+  p.engine = engine;
   p.is_q = is_q;
   p.trig = o->trig;
   p.sum = o->sum;
@@ -154,23 +176,26 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   p.M = M;
   p.N = N;
   p.batch = is_q ? 1 : batch;
-  p.mpad = (M + ncmri::kUnroll - 1) / ncmri::kUnroll * ncmri::kUnroll;
+  p.mpad = (M + pad - 1) / pad * pad;
   // batch groups: 16, 8, 4, 2, 1 vectors per gather pass
   p.npass = 0;
   int left = p.batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  if (p.batch > 1) {
+  if (mfma) {
+    V = ncmri::kMfmaColumns / p.bc[0];  // columns of a group: voxels x vectors
+  } else if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
   } else if (V == 0) {
     V = auto_voxels_per_lane(N, p.mpad);
   }
-  while (V > 1 && V > N) V /= 2;  // the first group must be complete
+  if (!mfma)
+    while (V > 1 && V > N) V /= 2;  // the first group must be complete
   p.V = V;
   if (o->sum == FHD_SUM_PLAIN) {
-    p.tile = p.mpad > 0 ? p.mpad : ncmri::kUnroll;
+    p.tile = p.mpad > 0 ? p.mpad : pad;
   } else if (o->tile > 0) {
-    p.tile = ((int64_t)o->tile + ncmri::kUnroll - 1) / ncmri::kUnroll * ncmri::kUnroll;
+    p.tile = ((int64_t)o->tile + pad - 1) / pad * pad;
   } else {
     int64_t t = 64;
     while (t * t < p.mpad && t < 8192) t *= 2;
@@ -179,25 +204,33 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   // sample splits: one launch row per split, partial sums reduced afterwards
   int32_t splits = o->sample_splits;
   if (o->sum == FHD_SUM_PLAIN) splits = 1;  // a single running sum by definition
-  else if (splits == 0) splits = auto_splits(N, V, p.bc[0], p.mpad);
+  else if (splits == 0)
+    splits = mfma ? auto_splits(mfma_waves(N, V), kMfmaWaveQuantum, N, p.bc[0], p.mpad)
+                  : auto_splits(waves_for(N, V), kWaveQuantum, N, p.bc[0], p.mpad);
   if (p.mpad == 0) splits = 1;
   p.m_split = p.mpad;
   if (splits > 1) {
     p.m_split = (p.mpad + splits - 1) / splits;
-    p.m_split = (p.m_split + ncmri::kUnroll - 1) / ncmri::kUnroll * ncmri::kUnroll;
+    p.m_split = (p.m_split + pad - 1) / pad * pad;
     splits = (int32_t)((p.mpad + p.m_split - 1) / p.m_split);  // no empty rows
   }
   p.splits = splits;
   p.ws_bytes = 0;
+  p.hdr_bytes = mfma ? align256((size_t)p.mpad * ncmri::mfma_header_floats(p.trig) * sizeof(float)) : 0;
   for (int i = 0; i < p.npass; ++i) {
-    int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);
-    p.pass_bytes[i] = (size_t)p.mpad * (size_t)stride * sizeof(float);
-    p.ws_bytes += (p.pass_bytes[i] + 255) / 256 * 256;
-    if (!ncmri::gather_supported(is_q, p.V, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no kernel for V=%d BC=%d", p.V, p.bc[i]);
+    if (mfma) {
+      if (!ncmri::mfma_supported(p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for BC=%d", p.bc[i]);
+      p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * ncmri::kMfmaTiles * 64 * sizeof(float);
+    } else {
+      if (!ncmri::gather_supported(is_q, p.V, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no kernel for V=%d BC=%d", p.V, p.bc[i]);
+      int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);
+      p.pass_bytes[i] = (size_t)p.mpad * (size_t)stride * sizeof(float);
+    }
+    p.ws_bytes += align256(p.pass_bytes[i]);
   }
   // one partial-sum buffer, reused by every pass (passes run in stream order)
   p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
-  p.ws_bytes += (p.partial_bytes + 255) / 256 * 256;
+  p.ws_bytes += align256(p.partial_bytes);
   return FHD_OK;
 }
 
@@ -223,6 +256,8 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   for (const Range& r : ins)
     if (overlaps(outr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "output overlaps an input array");
   if (ws) {
+    if ((uintptr_t)ws % 16 != 0)
+      return fail(FHD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (ws_given < p.ws_bytes)
       return fail(FHD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_given, p.ws_bytes);
     Range wr{ws, ws_given};
@@ -252,32 +287,55 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   float2* partial = nullptr;
   if (p.partial_bytes > 0) {
     size_t recs = 0;
-    for (int i = 0; i < p.npass; ++i) recs += (p.pass_bytes[i] + 255) / 256 * 256;
+    for (int i = 0; i < p.npass; ++i) recs += align256(p.pass_bytes[i]);
     partial = (float2*)(base + recs);
   }
   int b0 = 0;
+  const bool kahan = p.sum == FHD_SUM_KAHAN;
   for (int i = 0; i < p.npass && result == FHD_OK; ++i) {
-    ncmri::Layout L{is_q, p.trig, p.V, p.bc[i], ncmri::header_dwords(p.trig),
-                    ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i])};
-    float* rec = (float*)base;
-    if (p.stages & FHD_STAGE_MU) {
-      ncmri::RecordArgs ra{kx, ky, kz, x, y, z, (const float2*)phi,
-                           is_q ? nullptr : (const float2*)(D + (int64_t)b0 * M), M, p.mpad, rec};
-      hipError_t e = ncmri::launch_records(L, ra, s);
-      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "records kernel launch: %s", hipGetErrorString(e));
+    const int bc = p.bc[i];
+    const fhd_c32* Dp = is_q ? nullptr : D + (int64_t)b0 * M;
+    float2* outp = (float2*)(out + (int64_t)b0 * N);
+    // the reduction only needs the output, partial buffer and sizes
+    ncmri::GatherArgs ga{nullptr, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+                         p.splits > 1 ? partial : nullptr};
+    hipError_t e = hipSuccess;
+    const char* what = "records";
+    if (p.engine == FHD_ENGINE_MFMA) {
+      float* hdr = (float*)base;
+      float* wb = (float*)(base + p.hdr_bytes);
+      if (p.stages & FHD_STAGE_MU) {
+        ncmri::MfmaRecordArgs ra{kx, ky, kz, x, y, z, (const float2*)phi, (const float2*)Dp,
+                                 M, N, p.mpad, hdr, wb};
+        e = ncmri::launch_mfma_records(is_q, p.trig, bc, ra, s);
+      }
+      if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
+        what = "gather";
+        ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+                           p.splits > 1 ? partial : nullptr};
+        e = ncmri::launch_mfma_gather(p.trig, bc, p.splits, ma, s);
+      }
+    } else {
+      ncmri::Layout L{is_q, p.trig, p.V, bc, ncmri::header_dwords(p.trig),
+                      ncmri::record_dwords(is_q, p.trig, p.V, bc)};
+      float* rec = (float*)base;
+      ga.rec = rec;
+      if (p.stages & FHD_STAGE_MU) {
+        ncmri::RecordArgs ra{kx, ky, kz, x, y, z, (const float2*)phi, (const float2*)Dp, M, p.mpad, rec};
+        e = ncmri::launch_records(L, ra, s);
+      }
+      if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
+        what = "gather";
+        e = ncmri::launch_gather(L, kahan, p.splits, ga, s);
+      }
     }
-    if (result == FHD_OK && (p.stages & (FHD_STAGE_GATHER | FHD_STAGE_REDUCE))) {
-      ncmri::GatherArgs ga{rec, p.mpad, p.tile, x, y, z, N, (float2*)(out + (int64_t)b0 * N),
-                           p.m_split, p.splits > 1 ? partial : nullptr};
-      const bool kahan = p.sum == FHD_SUM_KAHAN;
-      hipError_t e = hipSuccess;
-      if (p.stages & FHD_STAGE_GATHER) e = ncmri::launch_gather(L, kahan, p.splits, ga, s);
-      if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE))
-        e = ncmri::launch_reduce(p.bc[i], kahan, p.splits, ga, s);
-      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "gather/reduce kernel launch: %s", hipGetErrorString(e));
+    if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE)) {
+      what = "reduce";
+      e = ncmri::launch_reduce(bc, kahan, p.splits, ga, s);
     }
-    base += (p.pass_bytes[i] + 255) / 256 * 256;
-    b0 += p.bc[i];
+    if (e != hipSuccess) result = fail(FHD_ERR_HIP, "%s kernel launch: %s", what, hipGetErrorString(e));
+    base += align256(p.pass_bytes[i]);
+    b0 += bc;
   }
   if (own) {
     hipError_t e = hipFreeAsync(ws, s);
@@ -294,6 +352,7 @@ NCMRI_API void fhd_default_opts(fhd_opts* o) {
   o->trig = FHD_TRIG_ACCURATE;
   o->sum = FHD_SUM_BLOCKED;
   o->stages = FHD_STAGE_ALL;
+  o->engine = FHD_ENGINE_AUTO;
 }
 
 NCMRI_API size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t is_q,
@@ -318,11 +377,13 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->voxels_per_lane = p.V;
     info->tile = (int32_t)p.tile;
     info->passes = p.npass;
-    info->record_dwords = p.npass > 0 ? ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]) : 0;
+    info->record_dwords = p.npass == 0 ? 0
+                          : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig)
+                                                         : ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]);
     info->padded_samples = p.mpad;
     info->workspace_bytes = p.ws_bytes;
     info->sample_splits = p.splits;
-    info->reserved = 0;
+    info->engine = p.engine;
     return FHD_OK;
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");

@@ -71,4 +71,50 @@ hipError_t launch_gather(const Layout& L, bool kahan, int32_t splits, const Gath
 hipError_t launch_reduce(int BC, bool kahan, int32_t splits, const GatherArgs& a, hipStream_t s);
 bool gather_supported(int is_q, int V, int BC);
 
+// ---------------------------------------------------------------------------
+// Matrix-core (MFMA) engine.  Each wave owns 32 voxel groups of V voxels
+// (V x BC = kMfmaColumns); per sample it evaluates one phase per group and
+// multiplies the 32 x 2 matrix (cos, sin of the group phases) by kMfmaTiles
+// 2 x 32 factor matrices with v_mfma_f32_32x32x2_f32.
+constexpr int kMfmaChunk = 32;   // samples per LDS chunk; records are padded to it
+constexpr int kMfmaTiles = 2;    // 32-column MFMA tiles per group phase
+constexpr int kMfmaColumns = 16 * kMfmaTiles;  // complex columns = voxels per group x vectors
+
+inline constexpr int mfma_header_floats(int trig) { return trig == kTrigHw ? 4 : 8; }
+// dwords of one sample's records (header + factor tiles)
+inline constexpr int mfma_record_dwords(int trig) { return mfma_header_floats(trig) + 64 * kMfmaTiles; }
+
+// Records of one sample m for the MFMA engine (all float32):
+//   header hdr[m][]  HW trig:       kx, ky, kz, 0
+//                    accurate trig: khx, khy, khz, 0, klx, kly, klz, 0
+//   factors wb[m][t][64], tile t: complex column cc = 16 t + c (c < 16) holds
+//     f = Mu_b exp(i 2 pi k.d_j) with b = cc / V, j = cc % V (V = kMfmaColumns / BC),
+//     stored as the two rows of the MFMA B operand: [2c] = fr, [2c+1] = fi,
+//     [32+2c] = -fi, [33+2c] = fr.
+struct MfmaRecordArgs {
+  const float* kx; const float* ky; const float* kz;
+  const float* x; const float* y; const float* z;  // x[0..min(V,N)-1] etc. are read
+  const float2* phi;
+  const float2* D;       // first vector of this pass ([BC][M]); unused for Q
+  int64_t M, N, mpad;    // mpad: multiple of kMfmaChunk
+  float* hdr;            // [mpad][mfma_header_floats]
+  float* wb;             // [mpad][kMfmaTiles][64]
+};
+
+struct MfmaArgs {
+  const float* hdr;
+  const float* wb;
+  int64_t mpad;
+  int64_t tile;          // samples per summation tile (multiple of kMfmaChunk)
+  const float* x; const float* y; const float* z;
+  int64_t N;
+  float2* out;           // first output vector of this pass ([BC][N])
+  int64_t m_split;       // samples per launch row (multiple of kMfmaChunk)
+  float2* partial;       // [rows][BC][N] when rows > 1, else nullptr
+};
+
+hipError_t launch_mfma_records(int is_q, int trig, int BC, const MfmaRecordArgs& a, hipStream_t s);
+hipError_t launch_mfma_gather(int trig, int BC, int32_t splits, const MfmaArgs& a, hipStream_t s);
+bool mfma_supported(int BC);
+
 }  // namespace ncmri

@@ -1,0 +1,471 @@
+// gfx950 matrix-core engine for F^H D and Q (PMPP ch. 17 "Iterative MRI
+// reconstruction").
+//
+// The pages' gather (section 17.3, Figs. 17.9-17.11) evaluates, for every
+// voxel and sample, one phase, its sine and cosine, and a complex
+// multiply-accumulate.  Phase factoring turns most of that into a dense
+// product.  Split the voxels into groups of V that sit at common offsets d_j
+// from their group's first voxel x_g (on a Cartesian grid: V consecutive
+// voxels of one row).  Then
+//
+//   out[b][x_g + d_j] = sum_m  exp(i 2 pi k_m.x_g) * f_m[j][b],
+//   f_m[j][b]         = Mu_b[m] exp(i 2 pi k_m.d_j)   (Mu = conj(phi) D, or |phi|^2 for Q)
+//
+// i.e. for 32 groups and 32 complex columns (j, b) the sum over samples is the
+// real matrix product
+//
+//   [Re | Im] (32 x 64) += sum_m  E_m (32 x 2) * W_m (2 x 64),
+//   E_m[g] = (cos, sin)(2 pi k_m.x_g),   W_m = [ fr  fi ; -fi  fr ] per column,
+//
+// which v_mfma_f32_32x32x2_f32 computes (K = 2) one sample at a time: one
+// phase, one sine per lane and two MFMAs per sample for 32 x 32 voxel
+// columns.  The factor matrices W_m do not depend on the voxel; the records
+// kernel forms them once per sample, in double, rounded once to fp32, already
+// laid out as the MFMA B operand.
+//
+// Operand layouts of v_mfma_f32_32x32x2_f32 (wave64), checked on gfx950:
+//   A[i][k] = lane 32 k + i,  B[k][j] = lane 32 k + j,
+//   D[i][j] = register (i / 8) * 4 + i % 4 of lane 32 * ((i / 4) % 2) + j.
+// So lanes 0-31 supply cos of group i = lane and lanes 32-63 sin of group
+// i = lane - 32: every lane evaluates one sine, the cosine lanes with a
+// quarter turn added to the phase.
+//
+// Data flow.  The 4 waves of a workgroup walk the same samples, so each
+// 32-sample chunk of records is copied from memory once per workgroup into LDS
+// and read from there by every wave -- the role the pages give constant memory
+// (Figs. 17.12/17.13).  The copy uses gfx950's LDS DMA (global_load_lds_dwordx4:
+// lane i's 16 bytes land at the LDS base + 16 i, no VGPRs involved), double
+// buffered in two separate LDS arrays: the next chunk's copy is in flight
+// while the current one is consumed, with one wait and workgroup barrier per
+// chunk.  The header (k) is read as an LDS broadcast.
+//
+// Waves whose voxels are not on the common offsets (any non-grid coordinate
+// set) only help stage the chunks; a second kernel (mfma_direct_kernel)
+// evaluates every voxel phase of those waves directly on the vector ALU from
+// the same records (the offset-0 columns hold Mu_b), and exits at once for
+// the other waves.  Both kernels take the same decision per wave.
+//
+// Summation is blocked as in the VALU engine: tile partial sums in the MFMA
+// accumulators, folded into running totals at tile ends.
+#include "fhd_internal.h"
+#include "fhd_trig.h"
+
+namespace ncmri {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes at
+// src (its own address) go to lds + 16 i (lds is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const float4* src, float4* lds) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds, 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Records: one lane per (padded sample, complex column).
+__global__ void __launch_bounds__(kWorkgroup)
+mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int BC) {
+  const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  const int64_t m = idx / kMfmaColumns;
+  const int cc = (int)(idx - m * kMfmaColumns);
+  if (m >= a.mpad) return;
+  const int HF = mfma_header_floats(trig);
+  const int V = kMfmaColumns / BC;
+  float* h = a.hdr + m * HF;
+  float* w = a.wb + (m * kMfmaTiles + cc / 16) * 64;
+  const int c = cc % 16;
+  if (m >= a.M) {  // padding sample: contributes exactly zero
+    if (cc == 0)
+      for (int i = 0; i < HF; ++i) h[i] = 0.0f;
+    w[2 * c] = 0.0f; w[2 * c + 1] = 0.0f; w[32 + 2 * c] = 0.0f; w[33 + 2 * c] = 0.0f;
+    return;
+  }
+  const float kx = a.kx[m], ky = a.ky[m], kz = a.kz[m];
+  if (cc == 0) {
+    if (trig == kTrigHw) {
+      h[0] = kx; h[1] = ky; h[2] = kz; h[3] = 0.0f;
+    } else {
+      // kh = nearest multiple of 2^-12 (exact scaling by powers of two), kl = k - kh (exact)
+      const float khx = __builtin_rintf(kx * 4096.0f) * (1.0f / 4096.0f);
+      const float khy = __builtin_rintf(ky * 4096.0f) * (1.0f / 4096.0f);
+      const float khz = __builtin_rintf(kz * 4096.0f) * (1.0f / 4096.0f);
+      h[0] = khx; h[1] = khy; h[2] = khz; h[3] = 0.0f;
+      h[4] = kx - khx; h[5] = ky - khy; h[6] = kz - khz; h[7] = 0.0f;
+    }
+  }
+  const int b = cc / V, j = cc % V;
+  // phase factor of offset j relative to the group's first voxel (columns of
+  // offsets beyond a voxel set smaller than one group are never written out)
+  double cj = 1.0, sj = 0.0;
+  if (j > 0 && j < a.N) {
+    const double p = (double)kx * ((double)a.x[j] - (double)a.x[0]) +
+                     (double)ky * ((double)a.y[j] - (double)a.y[0]) +
+                     (double)kz * ((double)a.z[j] - (double)a.z[0]);
+    sincospi(2.0 * p, &sj, &cj);
+  }
+  const double pr = a.phi[m].x, pim = a.phi[m].y;
+  double mr, mi;
+  if (is_q) {
+    mr = pr * pr + pim * pim;
+    mi = 0.0;
+  } else {
+    const float2 d = a.D[(int64_t)b * a.M + m];
+    mr = pr * d.x + pim * d.y;  // Mu = conj(phi) * D
+    mi = pr * d.y - pim * d.x;
+  }
+  const float fr = (float)(mr * cj - mi * sj), fi = (float)(mr * sj + mi * cj);
+  w[2 * c] = fr; w[2 * c + 1] = fi; w[32 + 2 * c] = -fi; w[33 + 2 * c] = fr;
+}
+
+// ---------------------------------------------------------------------------
+// Wave w of either gather kernel owns the voxel groups 32 w .. 32 w + 31 of V
+// voxels each, i.e. voxels [32 V w, 32 V (w + 1)).  The wave is "regular" when
+// every group's voxels sit at the offsets of the first group (exact double
+// comparison of the coordinate differences); lanes l and l + 32 share group
+// l % 32 and split its voxels.  Returns the wave-uniform vote.
+template <int V>
+__device__ __forceinline__ bool wave_regular(const float* __restrict__ x, const float* __restrict__ y,
+                                             const float* __restrict__ z, int64_t N, int64_t n0,
+                                             int lane, float gx, float gy, float gz) {
+  bool reg = true;
+  const double bx = x[0], by = y[0], bz = z[0];
+  const int j0 = lane < 32 ? 1 : V / 2, j1 = lane < 32 ? V / 2 : V;
+  for (int j = j0; j < j1; ++j) {
+    const int64_t n = n0 + j;
+    if (n < N)
+      reg = reg && ((double)x[n] - (double)gx == (double)x[j] - bx) &&
+            ((double)y[n] - (double)gy == (double)y[j] - by) &&
+            ((double)z[n] - (double)gz == (double)z[j] - bz);
+  }
+  return __all(reg);
+}
+
+// Samples [lo, hi) of launch row `row`.
+__device__ __forceinline__ void row_range(int64_t m_split, int64_t mpad, int32_t row, int64_t& lo,
+                                          int64_t& hi) {
+  const int64_t lo64 = (int64_t)row * m_split;
+  lo = lo64 < mpad ? lo64 : mpad;
+  hi = lo64 + m_split < mpad ? lo64 + m_split : mpad;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core gather (regular waves).
+template <int BC, int TRIG>
+struct MfmaGather {
+  static constexpr int T = kMfmaTiles;
+  static constexpr int V = kMfmaColumns / BC;          // voxels per group
+  static constexpr int HF = mfma_header_floats(TRIG);  // header floats per sample
+  static constexpr int C = kMfmaChunk;
+  static constexpr int U = 4;                          // samples per unrolled step
+  static constexpr int NW = kWorkgroup / 64;           // waves per workgroup
+  static constexpr int NB = C * T * 16 / 64;           // 1 KiB factor blocks per chunk
+  static constexpr int NH = C * HF / 4;                // header float4s per chunk
+  static_assert(V >= 2 && V * BC == kMfmaColumns, "group shape");
+  static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
+  static_assert(C % U == 0, "unroll");
+
+  // Phase of the lane's group in revolutions, plus a quarter turn on the
+  // cosine lanes (q = 0.25), and its sine: the lane's A-operand entry.
+  __device__ static __forceinline__ float group_entry(const float* hs, float gx, float gy, float gz,
+                                                      float q) {
+    if constexpr (TRIG == kTrigHw) {
+      const float t = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, __builtin_fmaf(hs[0], gx, q)));
+      return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(t));
+    } else {
+      // kh.x (plus the quarter turn) is exact for integer or half-integer
+      // coordinates of moderate size, so its fractional part is exact.
+      float th = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, __builtin_fmaf(hs[0], gx, q)));
+      th = th - __builtin_rintf(th);
+      const float tl = __builtin_fmaf(hs[6], gz, __builtin_fmaf(hs[5], gy, hs[4] * gx));
+      float s, c;
+      sincos_turns(th + tl, s, c);
+      return s;
+    }
+  }
+
+  // One chunk for a wave on the common offsets.
+  __device__ static __forceinline__ void regular_chunk(const float* __restrict__ hb,
+                                                       const float* __restrict__ wb, int lane,
+                                                       float gx, float gy, float gz, float q,
+                                                       f32x16 (&acc)[T]) {
+    for (int s0 = 0; s0 < C; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        float bv[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) bv[t] = wb[(s * T + t) * 64 + lane];
+        const float a = group_entry(hb + s * HF, gx, gy, gz, q);
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[t], acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // Starts the copy of the chunk at sample c into (lb, lh): wave w copies the
+  // factor blocks w, w + NW, ... and wave 0 the header.
+  __device__ static __forceinline__ void stage(const MfmaArgs& a, int64_t c, int wave_in_wg,
+                                               int lane, float4* lb, float4* lh) {
+    const float4* wb4 = reinterpret_cast<const float4*>(a.wb) + c * (T * 16);
+#pragma unroll
+    for (int i = 0; i < NB / NW; ++i) {
+      const int blk = i * NW + wave_in_wg;
+      lds_dma16(wb4 + blk * 64 + lane, lb + blk * 64);
+    }
+    if (wave_in_wg == 0 && lane < NH)
+      lds_dma16(reinterpret_cast<const float4*>(a.hdr) + c * (HF / 4) + lane, lh);
+  }
+
+  // Chunk copies complete (this wave's) and visible to the workgroup.
+  __device__ static __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  __device__ static void run(const MfmaArgs& a) {
+    __shared__ float4 sb0[C * T * 16], sb1[C * T * 16];
+    __shared__ float4 sh0[NH], sh1[NH];
+    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int64_t wave = (int64_t)blockIdx.x * NW + wig;
+    const int64_t vbase = wave * 32 * V;   // first voxel of the wave
+    const int64_t n0 = vbase + (int64_t)(lane & 31) * V;  // first voxel of the lane's group
+    const bool gin = n0 < a.N;
+    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
+    const float q = lane < 32 ? 0.25f : 0.0f;
+    const bool regular = wave_regular<V>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
+    const int32_t row = (int32_t)blockIdx.y;
+    int64_t lo, hi;
+    row_range(a.m_split, a.mpad, row, lo, hi);
+
+    // Chunks alternate between the two buffers; tiles (a whole number of
+    // chunks, counted from lo) fold into the totals.
+    const int64_t nch = (hi - lo) / C;
+    const int64_t cpt = a.tile / C;
+    if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
+    publish();
+    f32x16 acc[T], tot[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) { acc[t] = f32x16{}; tot[t] = f32x16{}; }
+    for (int64_t ch = 0; ch < nch; ch += 2) {
+      if (ch + 1 < nch) stage(a, lo + (ch + 1) * C, wig, lane, sb1, sh1);
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
+                      gx, gy, gz, q, acc);
+      if ((ch + 1) % cpt == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+      }
+      publish();
+      if (ch + 1 >= nch) break;
+      if (ch + 2 < nch) stage(a, lo + (ch + 2) * C, wig, lane, sb0, sh0);
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
+                      gx, gy, gz, q, acc);
+      if ((ch + 2) % cpt == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+      }
+      publish();
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) tot[t] += acc[t];  // the last (partial) tile
+
+    // write-out: out[b][n], or this row's partial sums (irregular waves are
+    // written by mfma_direct_kernel)
+    if (!regular) return;
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+    float* df = reinterpret_cast<float*>(dst);
+    const int c = lane & 31;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int cc = 16 * t + c / 2;
+      const int b = cc / V, j = cc % V;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+        const int64_t n = vbase + (int64_t)i * V + j;
+        if (n < a.N) df[2 * ((int64_t)b * a.N + n) + (c & 1)] = tot[t][v];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Direct gather for the irregular waves (one launch row; all samples).  Lane
+// l of wave w owns voxels 32 V w + l + 64 i, i < V / 2, and evaluates each
+// voxel's phase; records are read with wave-uniform scalar loads.  With
+// sample splits the totals go to partial row 0 and the other rows get zeros,
+// so the fixed-order reduction returns them unchanged.
+template <int BC, int TRIG>
+struct MfmaDirect {
+  static constexpr int T = kMfmaTiles;
+  static constexpr int V = kMfmaColumns / BC;
+  static constexpr int HF = mfma_header_floats(TRIG);
+  static constexpr int ND = V / 2;
+
+  // sin and cos of one voxel's phase (direct path).
+  __device__ static __forceinline__ void voxel_sincos(const float* hs, float x, float y, float z,
+                                                      float& c, float& s) {
+    if constexpr (TRIG == kTrigHw) {
+      const float t = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
+      const float f = __builtin_amdgcn_fractf(t);
+      s = __builtin_amdgcn_sinf(f);
+      c = __builtin_amdgcn_cosf(f);
+    } else {
+      float th = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
+      th = th - __builtin_rintf(th);
+      const float tl = __builtin_fmaf(hs[6], z, __builtin_fmaf(hs[5], y, hs[4] * x));
+      sincos_turns(th + tl, s, c);
+    }
+  }
+
+  __device__ static void run(const MfmaArgs& a, int32_t splits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
+    const int64_t vbase = wave * 32 * V;
+    if (vbase >= a.N) return;
+    const int64_t n0 = vbase + (int64_t)(lane & 31) * V;
+    const bool gin = n0 < a.N;
+    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
+    if (wave_regular<V>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz)) return;
+
+    float vx[ND], vy[ND], vz[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int64_t n = vbase + lane + 64 * i;
+      const bool ok = n < a.N;
+      vx[i] = ok ? a.x[n] : 0.0f;
+      vy[i] = ok ? a.y[n] : 0.0f;
+      vz[i] = ok ? a.z[n] : 0.0f;
+    }
+    float tre[ND][BC], tim[ND][BC];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int b = 0; b < BC; ++b) { tre[i][b] = 0.0f; tim[i][b] = 0.0f; }
+    for (int64_t t0 = 0; t0 < a.mpad; t0 += a.tile) {
+      const int64_t t1 = (a.mpad - t0 > a.tile) ? t0 + a.tile : a.mpad;
+      float are[ND][BC], aim[ND][BC];
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int b = 0; b < BC; ++b) { are[i][b] = 0.0f; aim[i][b] = 0.0f; }
+      for (int64_t m = t0; m < t1; ++m) {
+        const float* hs = a.hdr + m * HF;
+        const float* wm = a.wb + m * (T * 64);
+        float mr[BC], mi[BC];
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+          // Mu_b is the offset-0 column of vector b
+          const int cc = b * V;
+          mr[b] = wm[(cc / 16) * 64 + 2 * (cc % 16)];
+          mi[b] = wm[(cc / 16) * 64 + 2 * (cc % 16) + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          float c, sn;
+          voxel_sincos(hs, vx[i], vy[i], vz[i], c, sn);
+#pragma unroll
+          for (int b = 0; b < BC; ++b) {
+            are[i][b] = __builtin_fmaf(mr[b], c, __builtin_fmaf(-mi[b], sn, are[i][b]));
+            aim[i][b] = __builtin_fmaf(mi[b], c, __builtin_fmaf(mr[b], sn, aim[i][b]));
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int b = 0; b < BC; ++b) { tre[i][b] += are[i][b]; tim[i][b] += aim[i][b]; }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int64_t n = vbase + lane + 64 * i;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int b = 0; b < BC; ++b) {
+        if (a.partial) {
+          for (int32_t r = 0; r < splits; ++r)
+            a.partial[((int64_t)r * BC + b) * a.N + n] =
+                r == 0 ? make_float2(tre[i][b], tim[i][b]) : make_float2(0.0f, 0.0f);
+        } else {
+          a.out[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
+        }
+      }
+    }
+  }
+};
+
+// 4 waves per SIMD: the kernels fit in 128 VGPRs (HW trig without spills).
+template <int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(4)))
+mfma_gather_kernel(MfmaArgs a) {
+  MfmaGather<BC, TRIG>::run(a);
+}
+
+template <int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int32_t splits) {
+  MfmaDirect<BC, TRIG>::run(a, splits);
+}
+
+using MfmaFn = void (*)(MfmaArgs);
+using DirectFn = void (*)(MfmaArgs, int32_t);
+
+struct MfmaPair {
+  MfmaFn gather;
+  DirectFn direct;
+};
+
+template <int BC>
+MfmaPair pick_mfma(int trig) {
+  if (trig == kTrigHw) return {mfma_gather_kernel<BC, kTrigHw>, mfma_direct_kernel<BC, kTrigHw>};
+  return {mfma_gather_kernel<BC, kTrigAccurate>, mfma_direct_kernel<BC, kTrigAccurate>};
+}
+
+MfmaPair select_mfma(int trig, int BC) {
+  switch (BC) {
+    case 1: return pick_mfma<1>(trig);
+    case 2: return pick_mfma<2>(trig);
+    case 4: return pick_mfma<4>(trig);
+    case 8: return pick_mfma<8>(trig);
+    case 16: return pick_mfma<16>(trig);
+    default: return {nullptr, nullptr};
+  }
+}
+
+}  // namespace
+
+bool mfma_supported(int BC) { return select_mfma(kTrigHw, BC).gather != nullptr; }
+
+hipError_t launch_mfma_records(int is_q, int trig, int BC, const MfmaRecordArgs& a, hipStream_t s) {
+  if (a.mpad <= 0) return hipSuccess;
+  if (!mfma_supported(BC) || a.mpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  const int64_t lanes = a.mpad * kMfmaColumns;
+  const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(mfma_records_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, is_q,
+                     trig, BC);
+  return hipGetLastError();
+}
+
+// Launches the matrix-core kernel (regular waves, one launch row per sample
+// split) and the direct kernel (irregular waves, one row).
+hipError_t launch_mfma_gather(int trig, int BC, int32_t splits, const MfmaArgs& a, hipStream_t s) {
+  MfmaPair fn = select_mfma(trig, BC);
+  if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr)) return hipErrorInvalidValue;
+  if (a.mpad % kMfmaChunk != 0 || a.m_split % kMfmaChunk != 0 || a.tile % kMfmaChunk != 0 ||
+      a.tile <= 0)
+    return hipErrorInvalidValue;
+  if (a.N <= 0) return hipSuccess;
+  const int V = kMfmaColumns / BC;
+  const int64_t groups = (a.N + V - 1) / V;
+  const int64_t waves = (groups + 31) / 32;
+  const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  hipLaunchKernelGGL(fn.gather, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn.direct, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, splits);
+  return hipGetLastError();
+}
+
+}  // namespace ncmri

@@ -14,13 +14,14 @@ from . import _lib
 
 _TRIG = {"accurate": _lib.FHD_TRIG_ACCURATE, "hw": _lib.FHD_TRIG_HW}
 _SUM = {"blocked": _lib.FHD_SUM_BLOCKED, "kahan": _lib.FHD_SUM_KAHAN, "plain": _lib.FHD_SUM_PLAIN}
+_ENGINE = {"auto": _lib.FHD_ENGINE_AUTO, "valu": _lib.FHD_ENGINE_VALU, "mfma": _lib.FHD_ENGINE_MFMA}
 _STAGES = {"all": _lib.FHD_STAGE_ALL, "mu": _lib.FHD_STAGE_MU, "gather": _lib.FHD_STAGE_GATHER,
            "reduce": _lib.FHD_STAGE_REDUCE,
            "gather+reduce": _lib.FHD_STAGE_GATHER | _lib.FHD_STAGE_REDUCE}
 
 
 def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages="all",
-              workspace: torch.Tensor | None = None, sample_splits=0) -> _lib.FhdOpts:
+              workspace: torch.Tensor | None = None, sample_splits=0, engine="auto") -> _lib.FhdOpts:
     o = _lib.FhdOpts()
     _lib.load().fhd_default_opts(ctypes.byref(o))
     o.trig = _TRIG[trig] if isinstance(trig, str) else int(trig)
@@ -29,6 +30,7 @@ def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages=
     o.tile = int(tile)
     o.stages = _STAGES[stages] if isinstance(stages, str) else int(stages)
     o.sample_splits = int(sample_splits)
+    o.engine = _ENGINE[engine] if isinstance(engine, str) else int(engine)
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -76,7 +78,7 @@ def _stream_ptr(stream) -> int:
 
 def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
                 voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
-                stream=None, sample_splits=0) -> torch.Tensor:
+                stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
     """F^H D on the GPU.  D is complex64 [M] or [B, M]; returns complex64 [N] or [B, N].
 
     The work is enqueued on `stream` (default: torch's current stream).
@@ -102,9 +104,9 @@ def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
     if workspace is None:
         nbytes = fhd_workspace_bytes(M, N, B, False, trig=trig, sum=sum,
                                      voxels_per_lane=voxels_per_lane, tile=tile,
-                                     sample_splits=sample_splits)
+                                     sample_splits=sample_splits, engine=engine)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
     st = _lib.load().fhd_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                  y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
                                  out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
@@ -114,7 +116,7 @@ def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
 
 def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
               voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
-              stream=None, sample_splits=0) -> torch.Tensor:
+              stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
     """Q on the GPU: complex64 [N]."""
     for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
         _dev_f32(t, n)
@@ -131,9 +133,9 @@ def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
     if workspace is None:
         nbytes = fhd_workspace_bytes(M, N, 1, True, trig=trig, sum=sum,
                                      voxels_per_lane=voxels_per_lane, tile=tile,
-                                     sample_splits=sample_splits)
+                                     sample_splits=sample_splits, engine=engine)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
     st = _lib.load().q_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                y.data_ptr(), z.data_ptr(), phi.data_ptr(), out.data_ptr(),
                                M, N, ctypes.byref(o), _stream_ptr(stream))

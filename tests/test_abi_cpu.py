@@ -37,13 +37,17 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_opts_struct_layout(lib):
-    # 6 int32 + pointer + size_t on LP64
-    assert ctypes.sizeof(_lib.FhdOpts) == 40
+    # 8 int32 + pointer + size_t on LP64
+    assert ctypes.sizeof(_lib.FhdOpts) == 48
+    assert _lib.FhdOpts.workspace.offset == 32
     o = _lib.FhdOpts()
     o.trig = 77
+    o.engine = 5
     lib.fhd_default_opts(ctypes.byref(o))
     assert (o.trig, o.sum, o.voxels_per_lane, o.tile, o.stages, o.sample_splits) == (0, 0, 0, 0, 7, 0)
+    assert (o.engine, o.reserved) == (_lib.FHD_ENGINE_AUTO, 0)
     assert o.workspace is None and o.workspace_bytes == 0
+    assert ctypes.sizeof(_lib.FhdPlanInfo) == 40
 
 
 def test_status_strings_and_version(lib):
@@ -108,9 +112,19 @@ def test_stage_combinations(lib):
 @pytest.mark.parametrize("field,value", [
     ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 32),
     ("tile", -4), ("stages", 8), ("sample_splits", -1), ("sample_splits", 1025),
+    ("engine", 3), ("engine", -1), ("reserved", 1),
 ])
 def test_bad_options(lib, field, value):
     assert _fhd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def test_engine_option_conflicts(lib):
+    E = _lib.FHD_ERR_INVALID_ARGUMENT
+    # the matrix-core engine sums blocked or plain, and its group size is fixed
+    assert _fhd(lib, opts=_opts(engine=_lib.FHD_ENGINE_MFMA, sum=_lib.FHD_SUM_KAHAN)) == E
+    assert b"Kahan" in lib.fhd_last_error()
+    assert _fhd(lib, opts=_opts(engine=_lib.FHD_ENGINE_MFMA, voxels_per_lane=4)) == E
+    assert b"VALU" in lib.fhd_last_error()
 
 
 def test_workspace_errors(lib):
@@ -121,6 +135,9 @@ def test_workspace_errors(lib):
     # a single stage needs a caller workspace
     assert _fhd(lib, opts=_opts(stages=_lib.FHD_STAGE_MU)) == _lib.FHD_ERR_WORKSPACE
     assert _fhd(lib, opts=_opts(stages=_lib.FHD_STAGE_REDUCE)) == _lib.FHD_ERR_WORKSPACE
+    # misaligned workspace (records are read as 16-byte vectors)
+    assert _fhd(lib, opts=_opts(workspace=A + 0x200008, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.fhd_last_error()
     # workspace overlapping an input or the output
     assert _fhd(lib, opts=_opts(workspace=A + 0x6000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert _fhd(lib, opts=_opts(workspace=A + 0x100000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
@@ -144,6 +161,7 @@ def test_workspace_bytes(lib):
     # records: mpad * stride dwords, 256-byte aligned per pass
     def ws(M, N, batch=1, is_q=0, **kw):
         kw.setdefault("sample_splits", 1)
+        kw.setdefault("engine", _lib.FHD_ENGINE_VALU)
         return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
     assert ws(-1, 4) == 0
     assert ws(4, 4, batch=0) == 0
@@ -161,14 +179,42 @@ def test_workspace_bytes(lib):
                                                              + (3 * 4 * 50 * 8 + 255) // 256 * 256)
 
 
-def test_describe_plan(lib):
-    from non_cartesian_mri_amd.fhd import fhd_describe_plan
+def test_workspace_bytes_mfma(lib):
+    # per pass: header [mpad][4 or 8] floats (256-aligned) + factors [mpad][2][64] floats,
+    # mpad = M rounded up to the 32-sample chunk
+    def ws(M, N, batch=1, is_q=0, **kw):
+        kw.setdefault("sample_splits", 1)
+        kw.setdefault("engine", _lib.FHD_ENGINE_MFMA)
+        return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
+    a256 = lambda b: (b + 255) // 256 * 256
+    assert ws(1000, 4096, trig=1) == a256(1024 * 16) + 1024 * 512
+    assert ws(1000, 4096) == a256(1024 * 32) + 1024 * 512            # accurate: 8 header floats
+    assert ws(1000, 4096, is_q=1, trig=1) == a256(1024 * 16) + 1024 * 512
+    assert ws(33, 4096, trig=1) == a256(64 * 16) + 64 * 512
+    # batch 5: passes of 4 and 1 vectors, same record size; 3 splits add [3][4][N] partials
+    one = a256(1024 * 16) + 1024 * 512
+    assert ws(1000, 50, batch=5, trig=1) == 2 * one
+    assert ws(1000, 50, batch=5, trig=1, sample_splits=3) == 2 * one + a256(3 * 4 * 50 * 8)
+    # the default engine is the matrix-core one
+    assert lib.fhd_workspace_bytes(1000, 4096, 1, 0, ctypes.byref(_opts(trig=1, sample_splits=1))) == ws(1000, 4096, trig=1)
+    assert lib.fhd_workspace_bytes(1000, 4096, 1, 0, ctypes.byref(_opts(trig=1, sample_splits=1, sum=1))) == \
+        ws(1000, 4096, trig=1, engine=_lib.FHD_ENGINE_VALU, sum=1)
+
+
+def test_describe_plan_valu(lib):
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan as plan
+
+    def fhd_describe_plan(*a, **kw):
+        kw.setdefault("engine", "valu")
+        r = plan(*a, **kw)
+        assert r["engine"] == _lib.FHD_ENGINE_VALU
+        return r
     # the 128^3 benchmark shape: 16 voxels per lane on both trig paths
     hw = fhd_describe_plan(262144, 128 ** 3, trig="hw")
     acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
     assert hw["voxels_per_lane"] == 16 and acc["voxels_per_lane"] == 16
     assert hw["record_dwords"] == 52 and acc["record_dwords"] == 56
-    assert hw["workspace_bytes"] == lib.fhd_workspace_bytes(262144, 128 ** 3, 1, 0, ctypes.byref(_opts(trig=1)))
+    assert hw["workspace_bytes"] == lib.fhd_workspace_bytes(262144, 128 ** 3, 1, 0, ctypes.byref(_opts(trig=1, engine=1)))
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1
     # 262,144 samples -> 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
@@ -198,6 +244,41 @@ def test_describe_plan(lib):
     assert lib.fhd_describe_plan(4, 4, 1, 0, None, None) == _lib.FHD_ERR_INVALID_ARGUMENT
 
 
+def test_describe_plan_mfma(lib):
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan
+    # the 128^3 benchmark shape: groups of 32 voxels, 2 x 64-float factor tiles per sample
+    hw = fhd_describe_plan(262144, 128 ** 3, trig="hw")
+    acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
+    assert hw["engine"] == acc["engine"] == _lib.FHD_ENGINE_MFMA
+    assert hw["voxels_per_lane"] == 32 and acc["voxels_per_lane"] == 32
+    assert hw["record_dwords"] == 4 + 128 and acc["record_dwords"] == 8 + 128
+    assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 512
+    # 2048 waves of 32 groups; 16 rows of 16384 samples
+    assert hw["sample_splits"] == 16
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 512 + 16 * 128 ** 3 * 8
+    # 64^3: 256 waves x 16 rows fill 4 waves per SIMD; 32^3 x 2048: at most 8 rows of 256
+    assert fhd_describe_plan(65536, 64 ** 3, trig="hw")["sample_splits"] == 16
+    tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
+    assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 8 and tiny["tile"] == 64
+    # fewer voxels than one group: still one wave; samples padded to the 32-sample chunk
+    small = fhd_describe_plan(1000, 5, trig="hw")
+    assert small["padded_samples"] == 1024 and small["sample_splits"] == 4
+    # batched: group size 32 / vectors; the partial buffer cap gives 18 rows
+    b16 = fhd_describe_plan(500001, 96 ** 3, batch=16)
+    assert b16["voxels_per_lane"] == 2 and b16["sample_splits"] == 18 and b16["padded_samples"] == 500032
+    b19 = fhd_describe_plan(500001, 96 ** 3, batch=19)
+    assert b19["passes"] == 3 and b19["voxels_per_lane"] == 2
+    q = fhd_describe_plan(1048576, 128 ** 3, is_q=True, trig="hw")
+    assert q["voxels_per_lane"] == 32 and q["sample_splits"] == 64
+    assert fhd_describe_plan(4096, 256 ** 3)["sample_splits"] == 1
+    assert fhd_describe_plan(10, 4096, sample_splits=7)["sample_splits"] == 1  # 32 padded samples
+    assert fhd_describe_plan(1000, 100, sum="plain")["tile"] == 1024
+    assert fhd_describe_plan(262144, 128 ** 3, tile=100)["tile"] == 128      # multiple of 32
+    # Kahan or an explicit group size select the VALU engine
+    assert fhd_describe_plan(262144, 128 ** 3, sum="kahan")["engine"] == _lib.FHD_ENGINE_VALU
+    assert fhd_describe_plan(262144, 128 ** 3, voxels_per_lane=8)["engine"] == _lib.FHD_ENGINE_VALU
+
+
 def test_describe_plan_zero_sizes(lib):
     """Empty voxel or sample sets plan one row and no partial buffer (no division by zero)."""
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
@@ -205,4 +286,5 @@ def test_describe_plan_zero_sizes(lib):
         for is_q in (False, True):
             r = fhd_describe_plan(M, N, is_q=is_q, trig="hw")
             assert r["sample_splits"] == 1
-    assert fhd_describe_plan(100, 0)["workspace_bytes"] == (100 * 12 * 4 + 255) // 256 * 256
+    assert fhd_describe_plan(100, 0, engine="valu")["workspace_bytes"] == (100 * 12 * 4 + 255) // 256 * 256
+    assert fhd_describe_plan(100, 0)["workspace_bytes"] == 128 * 32 + 128 * 512

@@ -42,23 +42,28 @@ def _problem_and_ref(name, oracle_mod):
     return _cache[name]
 
 
+ENGINES = ["auto", "valu"]   # auto = the matrix-core engine for these options
+
+
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("name", ["fhd_32cube_2048_uniform", "fhd_64cube_65536_radial", "fhd_128cube_262144_spirals", "fhd16_96cube_500001_radial"])
-def test_fhd_config(oracle_mod, name, trig):
+def test_fhd_config(oracle_mod, name, trig, engine):
     p, idx, ref, d = _problem_and_ref(name, oracle_mod)
-    print(f"[gpu] {name} trig={trig} N={p.N} M={p.M} B={p.B}", flush=True)
-    got = gpu_fhd(p, d, trig=trig)
+    print(f"[gpu] {name} trig={trig} engine={engine} N={p.N} M={p.M} B={p.B}", flush=True)
+    got = gpu_fhd(p, d, trig=trig, engine=engine)
     if idx is not None:
         got = got[:, idx]
-    assert_close(got, ref, TOL[trig], f"{name} {trig}")
+    assert_close(got, ref, TOL[trig], f"{name} {trig} {engine}")
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("name", ["q_128cube_halfstep_1048576_uniform", "q_128cube_unitstep_1048576_uniform"])
-def test_q_config(oracle_mod, name, trig):
+def test_q_config(oracle_mod, name, trig, engine):
     p, idx, ref, d = _problem_and_ref(name, oracle_mod)
-    print(f"[gpu] {name} trig={trig} N={p.N} M={p.M}", flush=True)
-    got = gpu_q(p, d, trig=trig)
+    print(f"[gpu] {name} trig={trig} engine={engine} N={p.N} M={p.M}", flush=True)
+    got = gpu_q(p, d, trig=trig, engine=engine)
     assert_close(got[idx], ref, TOL[trig], f"{name} {trig}")
     # closed forms at full size
     w = np.abs(p.phi.astype(np.complex128)) ** 2
@@ -87,10 +92,11 @@ def test_phantom_round_trip_psnr(oracle_mod):
     alpha = oracle_mod.ls_scale(I0, ref)
     ps_ref = oracle_mod.psnr_db(I0, ref, alpha)
     d = dev_problem(p)
-    for trig in TRIGS:
-        got = gpu_fhd(p, d, trig=trig)[0, sl]
-        ps = oracle_mod.psnr_db(I0, got, alpha)
-        print(f"[psnr] oracle {ps_ref:.3f} dB, gpu {trig} {ps:.3f} dB", flush=True)
-        assert math.isfinite(ps_ref) and ps_ref > 5.0
-        assert ps_ref - ps <= 0.1
-        assert_close(got, ref, TOL[trig], f"phantom {trig}")
+    for engine in ENGINES:
+        for trig in TRIGS:
+            got = gpu_fhd(p, d, trig=trig, engine=engine)[0, sl]
+            ps = oracle_mod.psnr_db(I0, got, alpha)
+            print(f"[psnr] oracle {ps_ref:.3f} dB, gpu {trig}/{engine} {ps:.3f} dB", flush=True)
+            assert math.isfinite(ps_ref) and ps_ref > 5.0
+            assert ps_ref - ps <= 0.1
+            assert_close(got, ref, TOL[trig], f"phantom {trig} {engine}")
