@@ -84,9 +84,11 @@ typedef enum fhd_engine {
   FHD_ENGINE_AUTO = 0, /* MFMA, except with FHD_SUM_KAHAN or an explicit voxels_per_lane */
   FHD_ENGINE_VALU = 1, /* vector-ALU kernels: a lane owns voxels_per_lane voxels, three-FMA
                           complex multiply-accumulate per voxel and sample */
-  FHD_ENGINE_MFMA = 2  /* matrix-core kernels: groups of 32 / batch-group voxels, the
-                          per-sample sum as a 32x2 by 2x32 v_mfma_f32_32x32x2_f32 product
-                          (blocked or plain summation only) */
+  FHD_ENGINE_MFMA = 2  /* matrix-core kernels: groups of consecutive voxels share one
+                          phase per sample; the per-sample sum is a 32x2 by 2x32
+                          v_mfma_f32_32x32x2_f32 product per factor tile (blocked or
+                          plain summation only).  Groups that do not tile the grid rows
+                          (x fastest) fall back to a direct evaluation, correct but slow */
 } fhd_engine;
 
 /* Pipeline stages: the two loops produced by loop fission, plus the
@@ -104,8 +106,11 @@ enum {
 typedef struct fhd_opts {
   int32_t trig;            /* fhd_trig, default FHD_TRIG_ACCURATE */
   int32_t sum;             /* fhd_sum, default FHD_SUM_BLOCKED */
-  int32_t voxels_per_lane; /* VALU engine group size: 0 = automatic, else 1, 2, 4, 8 or 16;
-                              must be 0 with FHD_ENGINE_MFMA */
+  int32_t voxels_per_lane; /* group size; 0 = automatic.  VALU engine: 1, 2, 4, 8 or 16
+                              voxels per lane.  MFMA engine: 32 or 64 voxels sharing one
+                              group phase in single-vector passes (2 or 4 factor tiles;
+                              batched passes keep the tiles, groups of 16 x tiles / vectors).
+                              With FHD_ENGINE_AUTO, 1-16 select VALU and 32 or 64 MFMA */
   int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
   int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL.  Stages run in
                               separate calls must use the same sizes, options and

@@ -59,6 +59,7 @@ struct Plan {
   int trig;
   int sum;
   int engine;          // FHD_ENGINE_VALU or FHD_ENGINE_MFMA
+  int tiles;           // MFMA: 32-column factor tiles per group phase (2 or 4)
   int V;               // group size of the first pass
   int stages;
   int64_t M, N, mpad, tile;
@@ -103,11 +104,32 @@ int auto_voxels_per_lane(int64_t N, int64_t mpad) {
   return 1;
 }
 
-// The MFMA gather runs 4 waves per SIMD (<= 128 VGPRs, 34 KB of LDS per
-// 4-wave workgroup), one wave per 32 voxel groups.
-constexpr int64_t kMfmaWaveQuantum = kSimds * 4;
+// The MFMA gather runs one wave per 32 voxel groups, 4 waves per SIMD with
+// two factor tiles and 2 with four.
+int64_t mfma_wave_quantum(int T) { return kSimds * (T == 2 ? 4 : 2); }
 
 int64_t mfma_waves(int64_t N, int V) { return ((N + V - 1) / V + 31) / 32; }
+
+// Edge L of a cubic voxel count N = L^3, else 0.
+int64_t cube_edge(int64_t N) {
+  if (N <= 0) return 0;
+  int64_t L = (int64_t)std::llround(std::cbrt((double)N));
+  for (int64_t c = L > 1 ? L - 1 : 1; c <= L + 1; ++c)
+    if (c * c * c == N) return c;
+  return 0;
+}
+
+// Factor tiles per group phase.  Groups of 16 T / BC consecutive voxels only
+// take the factored path when they tile the grid rows (x fastest); four tiles
+// halve the phase and sine work per MFMA but double the group length, so
+// they are chosen when N is a cube whose edge every pass's group divides.
+int auto_mfma_tiles(int64_t N, const int* bc, int npass) {
+  const int64_t L = cube_edge(N);
+  if (L == 0) return 2;
+  for (int i = 0; i < npass; ++i)
+    if (L % (64 / bc[i]) != 0) return 2;
+  return 4;
+}
 
 // Sample splits.  Rows that start at different points of the record stream
 // keep the waves of a CU from all waiting on the same scalar-cache line, and
@@ -155,17 +177,20 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   if (o->sample_splits < 0 || o->sample_splits > kMaxSplits)
     return fail(FHD_ERR_INVALID_ARGUMENT, "sample_splits must be in [0, %d] (got %d)", kMaxSplits, o->sample_splits);
   int V = o->voxels_per_lane;
-  if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16) return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8 or 16 (got %d)", V);
+  if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16 && V != 32 && V != 64)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8, 16, 32 or 64 (got %d)", V);
   if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA)
     return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
   if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
   int engine = o->engine;
   if (engine == FHD_ENGINE_AUTO)
-    engine = (o->sum == FHD_SUM_KAHAN || V != 0) ? FHD_ENGINE_VALU : FHD_ENGINE_MFMA;
+    engine = (o->sum == FHD_SUM_KAHAN || (V != 0 && V <= 16)) ? FHD_ENGINE_VALU : FHD_ENGINE_MFMA;
   if (engine == FHD_ENGINE_MFMA && o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the MFMA engine sums blocked or plain, not Kahan");
-  if (engine == FHD_ENGINE_MFMA && V != 0)
-    return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane applies to the VALU engine only");
+  if (engine == FHD_ENGINE_MFMA && V != 0 && V < 32)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32 or 64 voxels (got %d)", V);
+  if (engine == FHD_ENGINE_VALU && V > 16)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "VALU group sizes are 1 to 16 voxels (got %d)", V);
   const bool mfma = engine == FHD_ENGINE_MFMA;
   const int64_t pad = mfma ? ncmri::kMfmaChunk : ncmri::kUnroll;
   p.engine = engine;
@@ -182,8 +207,10 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   int left = p.batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
+  p.tiles = 0;
   if (mfma) {
-    V = ncmri::kMfmaColumns / p.bc[0];  // columns of a group: voxels x vectors
+    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass);
+    V = 16 * p.tiles / p.bc[0];  // columns of a group: voxels x vectors
   } else if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
   } else if (V == 0) {
@@ -205,7 +232,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   int32_t splits = o->sample_splits;
   if (o->sum == FHD_SUM_PLAIN) splits = 1;  // a single running sum by definition
   else if (splits == 0)
-    splits = mfma ? auto_splits(mfma_waves(N, V), kMfmaWaveQuantum, N, p.bc[0], p.mpad)
+    splits = mfma ? auto_splits(mfma_waves(N, V), mfma_wave_quantum(p.tiles), N, p.bc[0], p.mpad)
                   : auto_splits(waves_for(N, V), kWaveQuantum, N, p.bc[0], p.mpad);
   if (p.mpad == 0) splits = 1;
   p.m_split = p.mpad;
@@ -219,8 +246,8 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   p.hdr_bytes = mfma ? align256((size_t)p.mpad * ncmri::mfma_header_floats(p.trig) * sizeof(float)) : 0;
   for (int i = 0; i < p.npass; ++i) {
     if (mfma) {
-      if (!ncmri::mfma_supported(p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for BC=%d", p.bc[i]);
-      p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * ncmri::kMfmaTiles * 64 * sizeof(float);
+      if (!ncmri::mfma_supported(p.tiles, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for T=%d BC=%d", p.tiles, p.bc[i]);
+      p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * p.tiles * 64 * sizeof(float);
     } else {
       if (!ncmri::gather_supported(is_q, p.V, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no kernel for V=%d BC=%d", p.V, p.bc[i]);
       int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);
@@ -307,13 +334,13 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
       if (p.stages & FHD_STAGE_MU) {
         ncmri::MfmaRecordArgs ra{kx, ky, kz, x, y, z, (const float2*)phi, (const float2*)Dp,
                                  M, N, p.mpad, hdr, wb};
-        e = ncmri::launch_mfma_records(is_q, p.trig, bc, ra, s);
+        e = ncmri::launch_mfma_records(is_q, p.trig, p.tiles, bc, ra, s);
       }
       if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
         what = "gather";
         ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
                            p.splits > 1 ? partial : nullptr};
-        e = ncmri::launch_mfma_gather(p.trig, bc, p.splits, ma, s);
+        e = ncmri::launch_mfma_gather(p.trig, p.tiles, bc, p.splits, ma, s);
       }
     } else {
       ncmri::Layout L{is_q, p.trig, p.V, bc, ncmri::header_dwords(p.trig),
@@ -378,7 +405,7 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->tile = (int32_t)p.tile;
     info->passes = p.npass;
     info->record_dwords = p.npass == 0 ? 0
-                          : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig)
+                          : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig, p.tiles)
                                                          : ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]);
     info->padded_samples = p.mpad;
     info->workspace_bytes = p.ws_bytes;

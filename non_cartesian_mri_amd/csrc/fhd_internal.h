@@ -73,22 +73,20 @@ bool gather_supported(int is_q, int V, int BC);
 
 // ---------------------------------------------------------------------------
 // Matrix-core (MFMA) engine.  Each wave owns 32 voxel groups of V voxels
-// (V x BC = kMfmaColumns); per sample it evaluates one phase per group and
-// multiplies the 32 x 2 matrix (cos, sin of the group phases) by kMfmaTiles
+// (V x BC = 16 T complex columns); per sample it evaluates one phase per
+// group and multiplies the 32 x 2 matrix (cos, sin of the group phases) by T
 // 2 x 32 factor matrices with v_mfma_f32_32x32x2_f32.
 constexpr int kMfmaChunk = 32;   // samples per LDS chunk; records are padded to it
-constexpr int kMfmaTiles = 2;    // 32-column MFMA tiles per group phase
-constexpr int kMfmaColumns = 16 * kMfmaTiles;  // complex columns = voxels per group x vectors
 
 inline constexpr int mfma_header_floats(int trig) { return trig == kTrigHw ? 4 : 8; }
-// dwords of one sample's records (header + factor tiles)
-inline constexpr int mfma_record_dwords(int trig) { return mfma_header_floats(trig) + 64 * kMfmaTiles; }
+// dwords of one sample's records (header + T factor tiles)
+inline constexpr int mfma_record_dwords(int trig, int T) { return mfma_header_floats(trig) + 64 * T; }
 
 // Records of one sample m for the MFMA engine (all float32):
 //   header hdr[m][]  HW trig:       kx, ky, kz, 0
 //                    accurate trig: khx, khy, khz, 0, klx, kly, klz, 0
-//   factors wb[m][t][64], tile t: complex column cc = 16 t + c (c < 16) holds
-//     f = Mu_b exp(i 2 pi k.d_j) with b = cc / V, j = cc % V (V = kMfmaColumns / BC),
+//   factors wb[m][t][64], tile t < T: complex column cc = 16 t + c (c < 16) holds
+//     f = Mu_b exp(i 2 pi k.d_j) with b = cc / V, j = cc % V (V = 16 T / BC),
 //     stored as the two rows of the MFMA B operand: [2c] = fr, [2c+1] = fi,
 //     [32+2c] = -fi, [33+2c] = fr.
 struct MfmaRecordArgs {
@@ -98,7 +96,7 @@ struct MfmaRecordArgs {
   const float2* D;       // first vector of this pass ([BC][M]); unused for Q
   int64_t M, N, mpad;    // mpad: multiple of kMfmaChunk
   float* hdr;            // [mpad][mfma_header_floats]
-  float* wb;             // [mpad][kMfmaTiles][64]
+  float* wb;             // [mpad][T][64]
 };
 
 struct MfmaArgs {
@@ -113,8 +111,11 @@ struct MfmaArgs {
   float2* partial;       // [rows][BC][N] when rows > 1, else nullptr
 };
 
-hipError_t launch_mfma_records(int is_q, int trig, int BC, const MfmaRecordArgs& a, hipStream_t s);
-hipError_t launch_mfma_gather(int trig, int BC, int32_t splits, const MfmaArgs& a, hipStream_t s);
-bool mfma_supported(int BC);
+// T: 32-column factor tiles per group phase (2 or 4); BC: vectors of the pass.
+hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
+                               hipStream_t s);
+hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,
+                              hipStream_t s);
+bool mfma_supported(int T, int BC);
 
 }  // namespace ncmri

@@ -18,10 +18,11 @@
 //   E_m[g] = (cos, sin)(2 pi k_m.x_g),   W_m = [ fr  fi ; -fi  fr ] per column,
 //
 // which v_mfma_f32_32x32x2_f32 computes (K = 2) one sample at a time: one
-// phase, one sine per lane and two MFMAs per sample for 32 x 32 voxel
-// columns.  The factor matrices W_m do not depend on the voxel; the records
-// kernel forms them once per sample, in double, rounded once to fp32, already
-// laid out as the MFMA B operand.
+// phase and one sine per lane and T MFMAs per sample for 32 groups x 16 T
+// complex columns (T = 2 or 4 tiles of 32 real columns).  The factor matrices
+// W_m do not depend on the voxel; the records kernel forms them once per
+// sample, in double, rounded once to fp32, already laid out as the MFMA B
+// operand.
 //
 // Operand layouts of v_mfma_f32_32x32x2_f32 (wave64), checked on gfx950:
 //   A[i][k] = lane 32 k + i,  B[k][j] = lane 32 k + j,
@@ -33,8 +34,8 @@
 // Data flow.  The 4 waves of a workgroup walk the same samples, so each
 // 32-sample chunk of records is copied from memory once per workgroup into LDS
 // and read from there by every wave -- the role the pages give constant memory
-// (Figs. 17.12/17.13).  The copy uses gfx950's LDS DMA (global_load_lds_dwordx4:
-// lane i's 16 bytes land at the LDS base + 16 i, no VGPRs involved), double
+// (Figs. 17.12/17.13).  The copy uses gfx950's LDS DMA (buffer_load_dwordx4 ...
+// lds: lane i's 16 bytes land at the LDS base + 16 i, no VGPRs involved), double
 // buffered in two separate LDS arrays: the next chunk's copy is in flight
 // while the current one is consumed, with one wait and workgroup barrier per
 // chunk.  The header (k) is read as an LDS broadcast.
@@ -54,27 +55,38 @@ namespace ncmri {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(1))) void* global_void_ptr;
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes at
-// src (its own address) go to lds + 16 i (lds is wave-uniform).
-__device__ __forceinline__ void lds_dma16(const float4* src, float4* lds) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds, 16, 0, 0);
+// Keeps the compiler's scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Raw buffer resource over [base, base + bytes) (stride 0; the third config
+// dword of gfx9-family targets).  Loads outside the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// LDS DMA, 16 bytes per lane: the bytes at offset voff (per lane) of the
+// buffer land at lds + 16 i for lane i (lds is wave-uniform).  The buffer
+// (MUBUF) form is used rather than global_load_lds: it counts only in vmcnt,
+// so the compiler keeps exact lgkmcnt waits for the LDS reads that follow.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, float4* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 16, voff, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
 // Records: one lane per (padded sample, complex column).
 __global__ void __launch_bounds__(kWorkgroup)
-mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int BC) {
+mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
+  const int cols = 16 * T;
   const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
-  const int64_t m = idx / kMfmaColumns;
-  const int cc = (int)(idx - m * kMfmaColumns);
+  const int64_t m = idx / cols;
+  const int cc = (int)(idx - m * cols);
   if (m >= a.mpad) return;
   const int HF = mfma_header_floats(trig);
-  const int V = kMfmaColumns / BC;
+  const int V = cols / BC;
   float* h = a.hdr + m * HF;
-  float* w = a.wb + (m * kMfmaTiles + cc / 16) * 64;
+  float* w = a.wb + (m * T + cc / 16) * 64;
   const int c = cc % 16;
   if (m >= a.M) {  // padding sample: contributes exactly zero
     if (cc == 0)
@@ -152,24 +164,23 @@ __device__ __forceinline__ void row_range(int64_t m_split, int64_t mpad, int32_t
 
 // ---------------------------------------------------------------------------
 // Matrix-core gather (regular waves).
-template <int BC, int TRIG>
+template <int T, int BC, int TRIG>
 struct MfmaGather {
-  static constexpr int T = kMfmaTiles;
-  static constexpr int V = kMfmaColumns / BC;          // voxels per group
+  static constexpr int V = 16 * T / BC;                // voxels per group
   static constexpr int HF = mfma_header_floats(TRIG);  // header floats per sample
   static constexpr int C = kMfmaChunk;
-  static constexpr int U = 4;                          // samples per unrolled step
   static constexpr int NW = kWorkgroup / 64;           // waves per workgroup
   static constexpr int NB = C * T * 16 / 64;           // 1 KiB factor blocks per chunk
   static constexpr int NH = C * HF / 4;                // header float4s per chunk
-  static_assert(V >= 2 && V * BC == kMfmaColumns, "group shape");
+  static_assert(V >= 2 && V * BC == 16 * T, "group shape");
   static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
-  static_assert(C % U == 0, "unroll");
+
+  static constexpr int HK = TRIG == kTrigHw ? 3 : 7;  // header floats a sample's phase reads
 
   // Phase of the lane's group in revolutions, plus a quarter turn on the
   // cosine lanes (q = 0.25), and its sine: the lane's A-operand entry.
-  __device__ static __forceinline__ float group_entry(const float* hs, float gx, float gy, float gz,
-                                                      float q) {
+  __device__ static __forceinline__ float group_entry(const float (&hs)[HK], float gx, float gy,
+                                                      float gz, float q) {
     if constexpr (TRIG == kTrigHw) {
       const float t = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, __builtin_fmaf(hs[0], gx, q)));
       return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(t));
@@ -185,21 +196,40 @@ struct MfmaGather {
     }
   }
 
-  // One chunk for a wave on the common offsets.
+  // Header and B-operand entries of sample s of the chunk in LDS.
+  __device__ static __forceinline__ void load_sample(const float* __restrict__ hb,
+                                                     const float* __restrict__ wb, int s, int lane,
+                                                     float (&hs)[HK], float (&bv)[T]) {
+#pragma unroll
+    for (int i = 0; i < HK; ++i) hs[i] = hb[s * HF + i];
+#pragma unroll
+    for (int t = 0; t < T; ++t) bv[t] = wb[(s * T + t) * 64 + lane];
+  }
+
+  // One chunk for a wave on the common offsets, software-pipelined by one
+  // sample: the next sample's LDS reads are issued before this sample's phase
+  // and MFMAs (the fences keep the scheduler from sinking them), so their
+  // latency is covered.
   __device__ static __forceinline__ void regular_chunk(const float* __restrict__ hb,
                                                        const float* __restrict__ wb, int lane,
                                                        float gx, float gy, float gz, float q,
                                                        f32x16 (&acc)[T]) {
-    for (int s0 = 0; s0 < C; s0 += U) {
+    float hc[HK], bc[T];
+    load_sample(hb, wb, 0, lane, hc, bc);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u;
-        float bv[T];
+    for (int s = 0; s < C; ++s) {
+      float hn[HK], bn[T];
+      if (s + 1 < C) load_sample(hb, wb, s + 1, lane, hn, bn);
+      sched_fence();
+      const float a = group_entry(hc, gx, gy, gz, q);
 #pragma unroll
-        for (int t = 0; t < T; ++t) bv[t] = wb[(s * T + t) * 64 + lane];
-        const float a = group_entry(hb + s * HF, gx, gy, gz, q);
+      for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bc[t], acc[t], 0, 0, 0);
+      sched_fence();
+      if (s + 1 < C) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[t], acc[t], 0, 0, 0);
+        for (int i = 0; i < HK; ++i) hc[i] = hn[i];
+#pragma unroll
+        for (int t = 0; t < T; ++t) bc[t] = bn[t];
       }
     }
   }
@@ -208,14 +238,15 @@ struct MfmaGather {
   // factor blocks w, w + NW, ... and wave 0 the header.
   __device__ static __forceinline__ void stage(const MfmaArgs& a, int64_t c, int wave_in_wg,
                                                int lane, float4* lb, float4* lh) {
-    const float4* wb4 = reinterpret_cast<const float4*>(a.wb) + c * (T * 16);
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(reinterpret_cast<const float4*>(a.wb) + c * (T * 16), NB * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NB / NW; ++i) {
       const int blk = i * NW + wave_in_wg;
-      lds_dma16(wb4 + blk * 64 + lane, lb + blk * 64);
+      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
     }
     if (wave_in_wg == 0 && lane < NH)
-      lds_dma16(reinterpret_cast<const float4*>(a.hdr) + c * (HF / 4) + lane, lh);
+      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.hdr) + c * (HF / 4), NH * 16), lane * 16, lh);
   }
 
   // Chunk copies complete (this wave's) and visible to the workgroup.
@@ -241,31 +272,34 @@ struct MfmaGather {
 
     // Chunks alternate between the two buffers; tiles (a whole number of
     // chunks, counted from lo) fold into the totals.
-    const int64_t nch = (hi - lo) / C;
-    const int64_t cpt = a.tile / C;
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    const int32_t cpt = (int32_t)(a.tile / C);
     if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
     publish();
     f32x16 acc[T], tot[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) { acc[t] = f32x16{}; tot[t] = f32x16{}; }
-    for (int64_t ch = 0; ch < nch; ch += 2) {
-      if (ch + 1 < nch) stage(a, lo + (ch + 1) * C, wig, lane, sb1, sh1);
+    int32_t left = cpt;  // chunks left in the current tile
+    for (int32_t ch = 0; ch < nch; ch += 2) {
+      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
                       gx, gy, gz, q, acc);
-      if ((ch + 1) % cpt == 0) {
+      if (--left == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        left = cpt;
       }
       publish();
       if (ch + 1 >= nch) break;
-      if (ch + 2 < nch) stage(a, lo + (ch + 2) * C, wig, lane, sb0, sh0);
+      if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
                       gx, gy, gz, q, acc);
-      if ((ch + 2) % cpt == 0) {
+      if (--left == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        left = cpt;
       }
       publish();
     }
@@ -298,10 +332,9 @@ struct MfmaGather {
 // voxel's phase; records are read with wave-uniform scalar loads.  With
 // sample splits the totals go to partial row 0 and the other rows get zeros,
 // so the fixed-order reduction returns them unchanged.
-template <int BC, int TRIG>
+template <int T, int BC, int TRIG>
 struct MfmaDirect {
-  static constexpr int T = kMfmaTiles;
-  static constexpr int V = kMfmaColumns / BC;
+  static constexpr int V = 16 * T / BC;
   static constexpr int HF = mfma_header_floats(TRIG);
   static constexpr int ND = V / 2;
 
@@ -397,16 +430,21 @@ struct MfmaDirect {
   }
 };
 
-// 4 waves per SIMD: the kernels fit in 128 VGPRs (HW trig without spills).
-template <int BC, int TRIG>
-__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(4)))
+// Resident waves per SIMD the gather is compiled for: 4 with two factor
+// tiles (<= 128 VGPRs; 34 KB of LDS per 4-wave workgroup), 2 with four tiles
+// (64 accumulators + 64 running totals; 66 KB of LDS per workgroup).
+template <int T>
+constexpr int mfma_waves_per_simd() { return T == 2 ? 4 : 2; }
+
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_simd<T>())))
 mfma_gather_kernel(MfmaArgs a) {
-  MfmaGather<BC, TRIG>::run(a);
+  MfmaGather<T, BC, TRIG>::run(a);
 }
 
-template <int BC, int TRIG>
+template <int T, int BC, int TRIG>
 __global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int32_t splits) {
-  MfmaDirect<BC, TRIG>::run(a, splits);
+  MfmaDirect<T, BC, TRIG>::run(a, splits);
 }
 
 using MfmaFn = void (*)(MfmaArgs);
@@ -417,47 +455,56 @@ struct MfmaPair {
   DirectFn direct;
 };
 
-template <int BC>
+template <int T, int BC>
 MfmaPair pick_mfma(int trig) {
-  if (trig == kTrigHw) return {mfma_gather_kernel<BC, kTrigHw>, mfma_direct_kernel<BC, kTrigHw>};
-  return {mfma_gather_kernel<BC, kTrigAccurate>, mfma_direct_kernel<BC, kTrigAccurate>};
+  if (trig == kTrigHw) return {mfma_gather_kernel<T, BC, kTrigHw>, mfma_direct_kernel<T, BC, kTrigHw>};
+  return {mfma_gather_kernel<T, BC, kTrigAccurate>, mfma_direct_kernel<T, BC, kTrigAccurate>};
 }
 
-MfmaPair select_mfma(int trig, int BC) {
+template <int T>
+MfmaPair select_bc(int trig, int BC) {
   switch (BC) {
-    case 1: return pick_mfma<1>(trig);
-    case 2: return pick_mfma<2>(trig);
-    case 4: return pick_mfma<4>(trig);
-    case 8: return pick_mfma<8>(trig);
-    case 16: return pick_mfma<16>(trig);
+    case 1: return pick_mfma<T, 1>(trig);
+    case 2: return pick_mfma<T, 2>(trig);
+    case 4: return pick_mfma<T, 4>(trig);
+    case 8: return pick_mfma<T, 8>(trig);
+    case 16: return pick_mfma<T, 16>(trig);
     default: return {nullptr, nullptr};
   }
 }
 
+MfmaPair select_mfma(int trig, int T, int BC) {
+  if (T == 2) return select_bc<2>(trig, BC);
+  if (T == 4) return select_bc<4>(trig, BC);
+  return {nullptr, nullptr};
+}
+
 }  // namespace
 
-bool mfma_supported(int BC) { return select_mfma(kTrigHw, BC).gather != nullptr; }
+bool mfma_supported(int T, int BC) { return select_mfma(kTrigHw, T, BC).gather != nullptr; }
 
-hipError_t launch_mfma_records(int is_q, int trig, int BC, const MfmaRecordArgs& a, hipStream_t s) {
+hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
+                               hipStream_t s) {
   if (a.mpad <= 0) return hipSuccess;
-  if (!mfma_supported(BC) || a.mpad % kMfmaChunk != 0) return hipErrorInvalidValue;
-  const int64_t lanes = a.mpad * kMfmaColumns;
+  if (!mfma_supported(T, BC) || a.mpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  const int64_t lanes = a.mpad * 16 * T;
   const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
   hipLaunchKernelGGL(mfma_records_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, is_q,
-                     trig, BC);
+                     trig, T, BC);
   return hipGetLastError();
 }
 
 // Launches the matrix-core kernel (regular waves, one launch row per sample
 // split) and the direct kernel (irregular waves, one row).
-hipError_t launch_mfma_gather(int trig, int BC, int32_t splits, const MfmaArgs& a, hipStream_t s) {
-  MfmaPair fn = select_mfma(trig, BC);
+hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,
+                              hipStream_t s) {
+  MfmaPair fn = select_mfma(trig, T, BC);
   if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr)) return hipErrorInvalidValue;
   if (a.mpad % kMfmaChunk != 0 || a.m_split % kMfmaChunk != 0 || a.tile % kMfmaChunk != 0 ||
       a.tile <= 0)
     return hipErrorInvalidValue;
   if (a.N <= 0) return hipSuccess;
-  const int V = kMfmaColumns / BC;
+  const int V = 16 * T / BC;
   const int64_t groups = (a.N + V - 1) / V;
   const int64_t waves = (groups + 31) / 32;
   const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);

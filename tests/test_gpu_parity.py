@@ -266,86 +266,98 @@ def mfma_grid(oracle_mod):
     return p, dev_problem(p), ref, qref
 
 
+# MFMA group sizes of single-vector passes: 2 and 4 factor tiles
+GROUPS = [32, 64]
+
+
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("sum_", ["blocked", "plain"])
 @pytest.mark.parametrize("splits", [0, 1, 3])
-def test_mfma_grid(mfma_grid, trig, sum_, splits):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_grid(mfma_grid, trig, sum_, splits, G):
     p, d, ref, qref = mfma_grid
-    opts = dict(trig=trig, sum=sum_, tile=128, sample_splits=splits, engine="mfma")
-    assert_close(gpu_fhd(p, d, **opts), ref, TOL[trig], f"mfma fhd {trig}/{sum_}/splits={splits}")
-    assert_close(gpu_q(p, d, **opts), qref, TOL[trig], f"mfma q {trig}/{sum_}/splits={splits}")
+    opts = dict(trig=trig, sum=sum_, tile=128, sample_splits=splits, engine="mfma", voxels_per_lane=G)
+    assert_close(gpu_fhd(p, d, **opts), ref, TOL[trig], f"mfma fhd {trig}/{sum_}/splits={splits}/G={G}")
+    assert_close(gpu_q(p, d, **opts), qref, TOL[trig], f"mfma q {trig}/{sum_}/splits={splits}/G={G}")
 
 
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("B", [2, 4, 8, 16, 19])
-def test_mfma_batched_grid(oracle_mod, trig, B):
-    """Batch passes of 16/8/4/2/1 vectors: groups of 2/4/8/16/32 voxels, all on
-    the 16-voxel rows except the 32-voxel groups (two rows each)."""
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_batched_grid(oracle_mod, trig, B, G):
+    """Batch passes of 16/8/4/2/1 vectors: groups of G/16 ... G voxels, each a
+    whole number of the 16-voxel rows or a divisor of them."""
     p = inputs.random_problem(302, M=700, L=16, B=B)
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
-    assert_close(gpu_fhd(p, trig=trig, engine="mfma", tile=96), ref, TOL[trig], f"mfma batched {trig}/B={B}")
+    assert_close(gpu_fhd(p, trig=trig, engine="mfma", tile=96, voxels_per_lane=G), ref, TOL[trig],
+                 f"mfma batched {trig}/B={B}/G={G}")
 
 
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("splits", [1, 4])
-def test_mfma_irregular_voxels(oracle_mod, trig, splits):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_irregular_voxels(oracle_mod, trig, splits, G):
     """Non-grid voxel centres: every wave runs the direct kernel (partial row 0
     carries its totals, the other rows zeros)."""
     p = inputs.random_problem(303, M=777, N=3001, L=40, coords="random", B=3)
+    opts = dict(trig=trig, engine="mfma", sample_splits=splits, voxels_per_lane=G)
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
-    assert_close(gpu_fhd(p, trig=trig, engine="mfma", sample_splits=splits), ref, TOL[trig],
-                 f"mfma fhd irregular {trig}/splits={splits}")
+    assert_close(gpu_fhd(p, **opts), ref, TOL[trig], f"mfma fhd irregular {trig}/splits={splits}/G={G}")
     qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
-    assert_close(gpu_q(p, trig=trig, engine="mfma", sample_splits=splits), qref, TOL[trig],
-                 f"mfma q irregular {trig}/splits={splits}")
+    assert_close(gpu_q(p, **opts), qref, TOL[trig], f"mfma q irregular {trig}/splits={splits}/G={G}")
 
 
 @pytest.mark.parametrize("trig", TRIGS)
 @pytest.mark.parametrize("splits", [1, 3])
-def test_mfma_mixed_regular_and_irregular_waves(oracle_mod, trig, splits):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_mixed_regular_and_irregular_waves(oracle_mod, trig, splits, G):
     """A 32^3 grid with displaced voxels in three waves: those go direct, the
     others through the matrix cores, and both write the same partial rows."""
     p = inputs.random_problem(304, M=600, L=32)
     x = p.x.copy()
     x[[100, 5000, 32767]] += np.float32(0.25)
     p.x = x
+    opts = dict(trig=trig, engine="mfma", sample_splits=splits, voxels_per_lane=G)
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
-    assert_close(gpu_fhd(p, trig=trig, engine="mfma", sample_splits=splits), ref, TOL[trig],
-                 f"mfma fhd mixed {trig}/splits={splits}")
+    assert_close(gpu_fhd(p, **opts), ref, TOL[trig], f"mfma fhd mixed {trig}/splits={splits}/G={G}")
     qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
-    assert_close(gpu_q(p, trig=trig, engine="mfma", sample_splits=splits), qref, TOL[trig],
-                 f"mfma q mixed {trig}/splits={splits}")
+    assert_close(gpu_q(p, **opts), qref, TOL[trig], f"mfma q mixed {trig}/splits={splits}/G={G}")
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-@pytest.mark.parametrize("N", [1, 3, 31, 33, 1000])
-def test_mfma_tiny_and_ragged_voxel_counts(oracle_mod, trig, N):
+@pytest.mark.parametrize("N", [1, 3, 31, 33, 65, 1000])
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_tiny_and_ragged_voxel_counts(oracle_mod, trig, N, G):
     """Fewer voxels than one group (unused columns are never written) and
     partial groups and waves."""
     p = inputs.random_problem(305, M=321, L=16, N=N)
+    opts = dict(trig=trig, engine="mfma", voxels_per_lane=G)
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
-    assert_close(gpu_fhd(p, trig=trig, engine="mfma"), ref, TOL[trig], f"mfma fhd N={N} {trig}")
+    assert_close(gpu_fhd(p, **opts), ref, TOL[trig], f"mfma fhd N={N} {trig}/G={G}")
     qref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi)
-    assert_close(gpu_q(p, trig=trig, engine="mfma"), qref, TOL[trig], f"mfma q N={N} {trig}")
+    assert_close(gpu_q(p, **opts), qref, TOL[trig], f"mfma q N={N} {trig}/G={G}")
 
 
 @pytest.mark.parametrize("M", [1, 31, 32, 33, 63, 65, 4099])
-def test_mfma_sample_count_tails(oracle_mod, M):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_sample_count_tails(oracle_mod, M, G):
     """Sample counts around the 32-sample chunk and the 64-sample tile."""
     p = inputs.random_problem(306, M=M, L=8)
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D)
     for trig in TRIGS:
-        assert_close(gpu_fhd(p, trig=trig, engine="mfma", tile=64), ref, TOL[trig], f"mfma fhd M={M} {trig}")
+        assert_close(gpu_fhd(p, trig=trig, engine="mfma", tile=64, voxels_per_lane=G), ref, TOL[trig],
+                     f"mfma fhd M={M} {trig}/G={G}")
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-def test_mfma_plane_waves_and_k0(trig):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_plane_waves_and_k0(trig, G):
     """One sample at k = 0 gives Mu everywhere; on an axis at a quarter-turn k
     the result is Mu * base**x (factored path on the 16^3 grid)."""
     p = inputs.random_problem(307, M=1, L=16)
     mu = np.conj(p.phi[0].astype(np.complex128)) * p.D[0, 0].astype(np.complex128)
     p.kx, p.ky, p.kz = (np.zeros(1, np.float32) for _ in range(3))
-    got = gpu_fhd(p, trig=trig, engine="mfma")[0]
+    got = gpu_fhd(p, trig=trig, engine="mfma", voxels_per_lane=G)[0]
     assert np.max(np.abs(got - mu)) <= 2.5e-7 * abs(mu)
     assert np.all(got == got[0])
     for axis, k, base in ((0, 0.25, 1j), (1, 0.5, -1.0), (2, -0.25, -1j)):
@@ -354,15 +366,16 @@ def test_mfma_plane_waves_and_k0(trig):
         p.kx, p.ky, p.kz = kv
         coord = (p.x, p.y, p.z)[axis].astype(np.int64)
         want = np.array([mu * base ** int(c) for c in coord])
-        got = gpu_fhd(p, trig=trig, engine="mfma")[0]
+        got = gpu_fhd(p, trig=trig, engine="mfma", voxels_per_lane=G)[0]
         assert np.max(np.abs(got - want)) <= 1e-6 * abs(mu), (axis, np.max(np.abs(got - want)))
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-def test_mfma_deterministic_and_engines_agree(trig):
+@pytest.mark.parametrize("G", GROUPS)
+def test_mfma_deterministic_and_engines_agree(trig, G):
     p = inputs.random_problem(308, M=2000, L=32, B=2)
     d = dev_problem(p)
-    a = gpu_fhd(p, d, trig=trig, engine="mfma")
-    assert np.array_equal(a, gpu_fhd(p, d, trig=trig, engine="mfma"))
+    a = gpu_fhd(p, d, trig=trig, engine="mfma", voxels_per_lane=G)
+    assert np.array_equal(a, gpu_fhd(p, d, trig=trig, engine="mfma", voxels_per_lane=G))
     v = gpu_fhd(p, d, trig=trig, engine="valu")
     assert np.linalg.norm(a - v) <= TOL[trig] * np.linalg.norm(v)
