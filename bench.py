@@ -34,17 +34,21 @@ MFMA_FLOP_PER_PAIR = 8
 # Valid only for the kernel source they were taken on (sha256 prefix) and the
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
-    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma"): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "2a3b0da1e02cb7f0",
-        "fetch_bytes": 1225644 * 1024 * 2.0, "write_bytes": 262144 * 1024 * 1.0,
-        "profile": "profiles/mfma_gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals", "hw", "blocked", "valu"): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "9c3822754b2dc6cb",
-        "fetch_bytes": 984615 * 1024 * 2.0, "write_bytes": 262149 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 64): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "9682d3868a393b3f",
+        "fetch_bytes": 1249852.1 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu"): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "9c3822754b2dc6cb",
-        "fetch_bytes": 1046113 * 1024 * 2.0, "write_bytes": 262148 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 64): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "9682d3868a393b3f",
+        "fetch_bytes": 1266050.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
+        "source": "fhd_kernels.hip", "kernel_sha256": "df6c84219fd9d20b",
+        "fetch_bytes": 981274.6 * 1024 * 2.0, "write_bytes": 262148.3 * 1024 * 1.0,
+        "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu", 16): {
+        "source": "fhd_kernels.hip", "kernel_sha256": "df6c84219fd9d20b",
+        "fetch_bytes": 1047039.9 * 1024 * 2.0, "write_bytes": 262147.8 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
 }
 WORKLOADS = {
@@ -120,9 +124,9 @@ def kernel_source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(config: str, trig: str, summ: str, engine: str, gather_ms: float):
+def traffic_for(config: str, trig: str, summ: str, engine: str, group: int, gather_ms: float):
     """Counter-derived HBM traffic (GB/s over the launch) or None if not measured for this kernel."""
-    t = TRAFFIC.get((config, trig, summ, engine))
+    t = TRAFFIC.get((config, trig, summ, engine, group))
     if t is None or t["kernel_sha256"] != kernel_source_sha(t["source"]):
         return None, None
     total = t["fetch_bytes"] + t["write_bytes"]
@@ -218,7 +222,8 @@ def main():
         kernel = ("gather_kernel: its launches in one step, timed alone; the per-sample and reduce "
                   "kernels are outside this interval")
         per_pair = FLOP_PER_PAIR[p.kind]
-    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, engine, g_avg)
+    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, engine,
+                                          plan["voxels_per_lane"], g_avg)
     res = {
         "metric": METRIC,
         "value": round(value, 3),
