@@ -8,6 +8,8 @@ by the phantom round trip.  It never imports or calls the HIP library.
 Function map to the pages (PMPP ch. 17 "Iterative MRI reconstruction"):
   fhd()       -- F^H D, section 17.2 (Fig. 17.3) and section 17.3 (Figs. 17.4/17.6)
   q()         -- Q, section 17.2 (same core computation with |phi|^2 weights)
+  forward()   -- F rho, the forward model whose conjugate transpose fhd() applies
+                 (section 17.2; the "inverse process" of section 17.3 step 3)
   psnr_db()   -- PSNR = 20 log10(max(I0) / sqrt(MSE)), section 17.3 step 3 (Fig. 17.18)
   ls_scale()  -- least-squares intensity scale; the pages leave the scaling of
                  the reconstructed image open, so it is fitted (see the header
@@ -52,6 +54,8 @@ def _load():
         lib.oracle_fhd.restype = ctypes.c_int
         lib.oracle_q.argtypes = [P, P, P, P, P, P, P, i64, i64, P, i64, P, P]
         lib.oracle_q.restype = ctypes.c_int
+        lib.oracle_forward.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i32, P, i64, P, P]
+        lib.oracle_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -144,6 +148,39 @@ def q(kx, ky, kz, x, y, z, phi, idx=None) -> np.ndarray:
     if rc != 0:
         raise RuntimeError(f"oracle_q failed with code {rc}")
     return out[:, 0] + 1j * out[:, 1]
+
+
+def forward(kx, ky, kz, x, y, z, phi, rho, idx=None) -> np.ndarray:
+    """F rho in double: complex128 [B, nidx] over samples (rho may be [N] or [B, N])."""
+    kx, ky, kz, x, y, z = (_f32(a) for a in (kx, ky, kz, x, y, z))
+    phi = _c64(phi)
+    rho = _c64(rho)
+    if rho.ndim == 1:
+        rho = rho[None, :]
+    B, N = rho.shape
+    M = kx.shape[0]
+    if not (ky.shape == kz.shape == phi.shape == (M,)):
+        raise ValueError("k and phi must have M samples")
+    if not (x.shape == y.shape == z.shape == (N,)):
+        raise ValueError("x, y, z and rho must have N voxels")
+    if idx is None:
+        nidx, idx_arr = M, None
+    else:
+        idx_arr = np.ascontiguousarray(idx, dtype=np.int64)
+        if idx_arr.size and (idx_arr.min() < 0 or idx_arr.max() >= M):
+            raise IndexError("sample subset out of range")
+        nidx = idx_arr.shape[0]
+    out = np.zeros((B, nidx, 2), np.float64)
+    th = ctypes.c_int32(0)
+    t0 = time.perf_counter()
+    rc = _load().oracle_forward(_ptr(kx), _ptr(ky), _ptr(kz), _ptr(x), _ptr(y), _ptr(z),
+                                _ptr(phi), _ptr(rho), M, N, B, _ptr(idx_arr), nidx,
+                                _ptr(out), ctypes.byref(th))
+    last.seconds = time.perf_counter() - t0
+    last.threads = th.value
+    if rc != 0:
+        raise RuntimeError(f"oracle_forward failed with code {rc}")
+    return out[..., 0] + 1j * out[..., 1]
 
 
 def rel_l2(test, ref) -> float:

@@ -23,6 +23,12 @@
  * equal to the conjugate transpose of F[m][n] = phi_m exp(-i 2 pi k_m . x_n)
  * applied to D).  Q uses the real weight |phi_m|^2 in place of Mu.
  *
+ * The forward model F itself (section 17.2: F models the imaging physics
+ * relating the image to the scan data; section 17.3 step 3 synthesises scan
+ * data from an image by this "inverse process"):
+ *
+ *   D[b][m]   = phi[m] * sum_n rho[b][n] exp(-i 2 pi (kx[m]x[n]+ky[m]y[n]+kz[m]z[n]))
+ *
  *   FhD[b][n] = sum_m conj(phi[m]) D[b][m] exp(+i 2 pi (kx[m]x[n]+ky[m]y[n]+kz[m]z[n]))
  *   Q[n]      = sum_m |phi[m]|^2          exp(+i 2 pi (kx[m]x[n]+ky[m]y[n]+kz[m]z[n]))
  *
@@ -135,5 +141,46 @@ int oracle_q(const float* kx, const float* ky, const float* kz,
     out[2 * i + 1] = im;
   }
   free(w);
+  return 0;
+}
+
+/*
+ * oracle_forward: out[(b*nidx + i)*2 + {0,1}] = D[b][m] = (F rho_b)[m] with
+ * m = idx[i] (or m = i if idx is NULL, then nidx must equal M), for the
+ * forward model F[m][n] = phi_m exp(-i 2 pi k_m . x_n) applied to the images
+ * rho[b][n] (complex, vector-major).  For every sample the voxel sum runs in
+ * order n = 0..N-1 in double, then the sum is multiplied by phi_m.  Same
+ * return codes as oracle_fhd.
+ */
+int oracle_forward(const float* kx, const float* ky, const float* kz,
+                   const float* x, const float* y, const float* z,
+                   const float* phi, const float* rho,
+                   int64_t M, int64_t N, int32_t B,
+                   const int64_t* idx, int64_t nidx,
+                   double* out, int32_t* threads) {
+  if (M < 0 || N < 0 || B < 1 || nidx < 0) return -1;
+  if (!idx && nidx != M) return -1;
+  if (threads) *threads = threads_used();
+  if (nidx == 0) return 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nidx; ++i) {
+    int64_t m = idx ? idx[i] : i;
+    double km[3] = {kx[m], ky[m], kz[m]};
+    double pr = phi[2 * m], pi = phi[2 * m + 1];
+    for (int32_t b = 0; b < B; ++b) {
+      double re = 0.0, im = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        double arg = 2.0 * M_PI * (km[0] * (double)x[n] + km[1] * (double)y[n] + km[2] * (double)z[n]);
+        double c = cos(arg), s = sin(arg);
+        double rr = rho[2 * ((int64_t)b * N + n)], ri = rho[2 * ((int64_t)b * N + n) + 1];
+        /* rho * exp(-i arg) = (rr + i ri)(c - i s) */
+        re += rr * c + ri * s;
+        im += ri * c - rr * s;
+      }
+      /* phi * sum */
+      out[2 * ((int64_t)b * nidx + i)] = pr * re - pi * im;
+      out[2 * ((int64_t)b * nidx + i) + 1] = pr * im + pi * re;
+    }
+  }
   return 0;
 }
