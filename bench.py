@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward"],
+                    help="fhd: F^H D (or Q for a Q workload); forward: F rho of a seeded image "
+                         "on the same trajectory and voxels")
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -93,15 +96,19 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}}))
 
 
-def cpu_baseline(p, target_s: float) -> dict:
-    """Time the oracle as it stands on a seeded voxel sample of the same workload."""
+def cpu_baseline(p, target_s: float, rho=None) -> dict:
+    """Time the oracle as it stands on a seeded voxel (or, for the forward
+    operator, sample) subset of the same workload."""
     import oracle
     from non_cartesian_mri_amd import inputs
     oracle.build(force=False)
+    total = p.M if rho is not None else p.N
 
-    def run(nvox):
-        idx = inputs.subset_indices(p.N, nvox, p.seed)
-        if p.kind == "q":
+    def run(count):
+        idx = inputs.subset_indices(total, count, p.seed)
+        if rho is not None:
+            oracle.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho, idx=idx)
+        elif p.kind == "q":
             oracle.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, idx=idx)
         else:
             oracle.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D, idx=idx)
@@ -109,12 +116,13 @@ def cpu_baseline(p, target_s: float) -> dict:
 
     probe = 64 * max(1, oracle_threads_hint())
     t, _ = run(probe)
-    nvox = int(min(p.N, max(probe, probe * target_s / max(t, 1e-6))))
-    t, threads = run(nvox)
-    pairs = nvox * p.M * p.B
+    count = int(min(total, max(probe, probe * target_s / max(t, 1e-6))))
+    t, threads = run(count)
+    pairs = count * (p.N if rho is not None else p.M) * p.B
+    what = (f"{count} seeded samples x all {p.N} voxels" if rho is not None
+            else f"{count} seeded voxels x all {p.M} samples")
     return {"value": pairs / t / 1e9, "unit": "Gpair/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nvox} seeded voxels x all {p.M} samples x {p.B} vector(s) of the same "
-                      f"workload ({pairs:.3e} pairs, {t:.1f} s wall)"}
+            "sample": f"{what} x {p.B} vector(s) of the same workload ({pairs:.3e} pairs, {t:.1f} s wall)"}
 
 
 def kernel_source_sha(name: str) -> str:
@@ -155,7 +163,7 @@ def main():
               "(voxel sharding across GPUs is a design note only); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
-    from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes, inputs, q_compute
+    from non_cartesian_mri_amd import fhd_compute, fhd_forward, fhd_workspace_bytes, inputs, q_compute
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -168,13 +176,26 @@ def main():
          for k in ("kx", "ky", "kz", "x", "y", "z", "phi")}
     D = None if p.D is None else torch.from_numpy(np.ascontiguousarray(p.D)).to(dev)
     is_q = p.kind == "q"
+    forward = args.op == "forward"
+    if forward and is_q:
+        print("--op forward needs an F^H D workload (the image replaces the data vectors)", file=sys.stderr)
+        sys.exit(2)
     opts = dict(trig=args.trig, sum=args.sum, voxels_per_lane=args.voxels_per_lane, tile=args.tile,
                 engine=args.engine)
-    ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, is_q, **opts)), dtype=torch.uint8, device=dev)
-    out = torch.empty((p.B, p.N), dtype=torch.complex64, device=dev)
+    op = "forward" if forward else ("q" if is_q else "fhd")
+    ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, op=op, **opts)), dtype=torch.uint8, device=dev)
+    if forward:
+        rng = np.random.Generator(np.random.PCG64(p.seed + 2000))
+        rho = torch.from_numpy(np.stack([inputs.complex_normal(rng, p.N) for _ in range(p.B)])).to(dev)
+        out = torch.empty((p.B, p.M), dtype=torch.complex64, device=dev)
+    else:
+        out = torch.empty((p.B, p.N), dtype=torch.complex64, device=dev)
 
     def stage(which):
-        if is_q:
+        if forward:
+            fhd_forward(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], rho,
+                        stages=which, workspace=ws, out=out, **opts)
+        elif is_q:
             q_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], stages=which,
                       workspace=ws, out=out.view(-1), **opts)
         else:
@@ -210,9 +231,14 @@ def main():
     g_avg = float(gather_ms.mean())
     direct_tflops = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
-    plan = fhd_describe_plan(p.M, p.N, p.B, is_q, **opts)
+    plan = fhd_describe_plan(p.M, p.N, p.B, op=op, **opts)
     engine = {1: "valu", 2: "mfma"}[plan["engine"]]
-    if engine == "mfma":
+    if forward:
+        achieved, bound = MFMA_FLOP_PER_PAIR * pairs / (g_avg * 1e-3) / 1e12, "mfma"
+        kernel = ("fwd_gather_kernel: its launch rows in one step, timed alone; the image packing, "
+                  "row reduction and (on a grid, empty) direct kernels are outside the interval")
+        per_pair = MFMA_FLOP_PER_PAIR
+    elif engine == "mfma":
         achieved, bound = MFMA_FLOP_PER_PAIR * pairs / (g_avg * 1e-3) / 1e12, "mfma"
         kernel = ("mfma_gather_kernel: its launch rows in one step, timed alone with the (empty on a "
                   "grid) mfma_direct_kernel; records and reduction kernels are outside the interval")
@@ -222,10 +248,10 @@ def main():
         kernel = ("gather_kernel: its launches in one step, timed alone; the per-sample and reduce "
                   "kernels are outside this interval")
         per_pair = FLOP_PER_PAIR[p.kind]
-    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, engine,
-                                          plan["voxels_per_lane"], g_avg)
+    traffic, traffic_detail = traffic_for(args.config + ("/forward" if forward else ""), args.trig,
+                                          args.sum, engine, plan["voxels_per_lane"], g_avg)
     res = {
-        "metric": METRIC,
+        "metric": METRIC if not forward else METRIC.replace("FhD", "Forward-operator F rho"),
         "value": round(value, 3),
         "unit": "Gpair/s",
         "n_gpus": 1,
@@ -237,7 +263,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "name": args.config, "voxels": p.N,
+        "config": {"workload": WORKLOADS[args.config] + ("; forward operator F rho of a seeded "
+                                                          "complex N(0,1) image" if forward else ""),
+                   "op": op, "name": args.config, "voxels": p.N,
                    "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": args.sum,
                    "engine": engine, "group_voxels": plan["voxels_per_lane"], "tile": plan["tile"],
                    "sample_splits": plan["sample_splits"], "gather_launches": plan["passes"],
@@ -256,7 +284,7 @@ def main():
                      "direct_formulation_tflops": round(direct_tflops, 3)},
     }
     if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, rho.cpu().numpy() if forward else None)
     print(json.dumps(res), flush=True)
 
 

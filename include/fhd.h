@@ -10,6 +10,10 @@
  *   Q      (section 17.2: computed once per trajectory, same core structure)
  *     Q[n]      = sum_{m<M} |phi[m]|^2 * exp(+i 2 pi (kx[m] x[n] + ky[m] y[n] + kz[m] z[n]))
  *
+ *   F rho  (section 17.2: F models the imaging physics; section 17.3 step 3
+ *           synthesises scan data from an image, the "inverse process")
+ *     D[b][m]   = phi[m] * sum_{n<N} rho[b][n] * exp(-i 2 pi (kx[m] x[n] + ky[m] y[n] + kz[m] z[n]))
+ *
  * k is in cycles per voxel and x, y, z in voxel units, so k.x is the phase in
  * revolutions (Eq. 17.1 uses exp(i 2 pi k_j . r)).  The exponent sign and the
  * complex multiply-accumulate follow the register-promoted kernel on the
@@ -91,6 +95,13 @@ typedef enum fhd_engine {
                           (x fastest) fall back to a direct evaluation, correct but slow */
 } fhd_engine;
 
+/* Operation codes of fhd_workspace_bytes and fhd_describe_plan. */
+typedef enum fhd_op {
+  FHD_OP_FHD = 0,     /* fhd_compute */
+  FHD_OP_Q = 1,       /* q_compute */
+  FHD_OP_FORWARD = 2  /* fhd_forward */
+} fhd_op;
+
 /* Pipeline stages: the two loops produced by loop fission, plus the
  * reduction of the sample-split rows' partial sums. */
 enum {
@@ -130,11 +141,13 @@ typedef struct fhd_opts {
 /* Fills *opts with the defaults. */
 void fhd_default_opts(fhd_opts* opts);
 
-/* Workspace bytes fhd_compute (is_q = 0) or q_compute (is_q = 1) needs for
- * these sizes and options (opts may be NULL).  Returns 0 on invalid arguments.
- * The workspace holds one packed record per sample (and per batch group) and,
- * when the samples are split across launch rows, the rows' partial sums. */
-size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+/* Workspace bytes the operation `op` (fhd_op: fhd_compute, q_compute or
+ * fhd_forward) needs for these sizes and options (opts may be NULL).  Returns
+ * 0 on invalid arguments.  The workspace holds the packed records (one per
+ * sample and batch group for F^H D and Q, one per voxel group for the forward
+ * operator) and, when the work is split across launch rows, the rows'
+ * partial sums. */
+size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t op,
                            const fhd_opts* opts);
 
 /*
@@ -163,23 +176,47 @@ fhd_status q_compute(const float* kx, const float* ky, const float* kz,
                      int64_t M, int64_t N,
                      const fhd_opts* opts, void* stream);
 
+/*
+ * The forward model F applied to `batch` images on one trajectory:
+ *   kx, ky, kz : float[M]            k-space sample coordinates (cycles/voxel)
+ *   x, y, z    : float[N]            voxel coordinates (voxel units); groups of
+ *                                    consecutive voxels on a common grid run on
+ *                                    the matrix cores, others are evaluated directly
+ *   phi        : fhd_c32[M]          per-sample complex weight
+ *   rho        : fhd_c32[batch][N]   images, vector-major
+ *   D          : fhd_c32[batch][M]   output scan data, overwritten; must not
+ *                                    overlap any input
+ * D[b][m] = phi[m] sum_n rho[b][n] exp(-i 2 pi k_m . x_n), so that
+ * <F rho, d> = <rho, F^H d> with fhd_compute.  Runs on the matrix-core engine
+ * only (FHD_ENGINE_VALU and FHD_SUM_KAHAN are rejected); voxels_per_lane may
+ * be 0, 32 or 64; sample_splits here splits the voxel groups across launch
+ * rows.  N == 0 writes zeros; M == 0 does nothing.  Returns FHD_OK or an error
+ * code as fhd_compute does.
+ */
+fhd_status fhd_forward(const float* kx, const float* ky, const float* kz,
+                       const float* x, const float* y, const float* z,
+                       const fhd_c32* phi, const fhd_c32* rho, fhd_c32* D,
+                       int64_t M, int64_t N, int32_t batch,
+                       const fhd_opts* opts, void* stream);
+
 /* The launch plan the library derives from sizes and options. */
 typedef struct fhd_plan_info {
   int32_t voxels_per_lane;  /* voxel group size of the first pass (VALU: voxels owned by one
                                lane; MFMA: voxels sharing one group phase) */
   int32_t tile;             /* samples per summation tile */
   int32_t passes;           /* gather launches (batch groups of 16, 8, 4, 2, 1 vectors) */
-  int32_t record_dwords;    /* dwords per sample record of the first pass */
-  int64_t padded_samples;   /* M rounded up to the record padding */
+  int32_t record_dwords;    /* dwords per record of the first pass (forward: per voxel group) */
+  int64_t padded_samples;   /* M rounded up to the record padding (forward: M) */
   size_t workspace_bytes;   /* = fhd_workspace_bytes(...) */
-  int32_t sample_splits;    /* launch rows splitting the samples (1: no reduction step) */
+  int32_t sample_splits;    /* launch rows splitting the samples (forward: the voxel
+                               groups); 1: no reduction step */
   int32_t engine;           /* FHD_ENGINE_VALU or FHD_ENGINE_MFMA */
 } fhd_plan_info;
 
 /* Fills *info with the plan for these sizes and options (opts may be NULL);
  * returns FHD_ERR_INVALID_ARGUMENT (and leaves *info untouched) for the same
  * argument errors fhd_compute / q_compute report.  No device call. */
-fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t op,
                              const fhd_opts* opts, fhd_plan_info* info);
 
 /* Static text for a status code. */

@@ -3,7 +3,8 @@
 Public entry points (thin wrappers over the C ABI in include/fhd.h):
   fhd_compute(kx, ky, kz, x, y, z, phi, D, ...) -> complex64 [N] or [B, N]
   q_compute(kx, ky, kz, x, y, z, phi, ...)      -> complex64 [N]
-  fhd_workspace_bytes(M, N, batch, is_q, ...)
+  fhd_forward(kx, ky, kz, x, y, z, phi, rho, ...) -> complex64 [M] or [B, M]
+  fhd_workspace_bytes(M, N, batch, is_q, ..., op=...), fhd_describe_plan(...)
 
 The HIP library is loaded on first use; a missing library raises instead of
 falling back to any CPU path.  ``inputs`` holds the seeded synthetic data
@@ -11,12 +12,12 @@ generators (trajectories, voxel grids, phantom).
 """
 from . import inputs  # noqa: F401
 
-__all__ = ["fhd_compute", "q_compute", "fhd_workspace_bytes", "fhd_describe_plan", "inputs",
-           "library_path"]
+__all__ = ["fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan",
+           "inputs", "library_path"]
 
 
 def __getattr__(name):
-    if name in ("fhd_compute", "q_compute", "fhd_workspace_bytes", "fhd_describe_plan"):
+    if name in ("fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan"):
         from . import fhd
         return getattr(fhd, name)
     if name == "library_path":

@@ -25,6 +25,10 @@ FHD_SUM_BLOCKED = 0
 FHD_SUM_KAHAN = 1
 FHD_SUM_PLAIN = 2
 # stages
+FHD_OP_FHD = 0
+FHD_OP_Q = 1
+FHD_OP_FORWARD = 2
+
 FHD_ENGINE_AUTO = 0
 FHD_ENGINE_VALU = 1
 FHD_ENGINE_MFMA = 2
@@ -36,7 +40,7 @@ FHD_STAGE_ALL = 7
 
 # every symbol the header declares
 EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "q_compute",
-            "fhd_describe_plan", "fhd_status_string", "fhd_last_error", "fhd_version")
+            "fhd_forward", "fhd_describe_plan", "fhd_status_string", "fhd_last_error", "fhd_version")
 
 
 class FhdOpts(ctypes.Structure):
@@ -95,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.fhd_compute.restype = ctypes.c_int
     lib.q_compute.argtypes = [P, P, P, P, P, P, P, P, i64, i64, ctypes.POINTER(FhdOpts), P]
     lib.q_compute.restype = ctypes.c_int
+    lib.fhd_forward.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, ctypes.POINTER(FhdOpts), P]
+    lib.fhd_forward.restype = ctypes.c_int
     lib.fhd_describe_plan.argtypes = [i64, i64, i32, i32, ctypes.POINTER(FhdOpts), ctypes.POINTER(FhdPlanInfo)]
     lib.fhd_describe_plan.restype = ctypes.c_int
     lib.fhd_status_string.argtypes = [ctypes.c_int]

@@ -55,6 +55,7 @@ bool overlaps(Range a, Range b) {
 }
 
 struct Plan {
+  int op;              // fhd_op
   int is_q;
   int trig;
   int sum;
@@ -71,6 +72,8 @@ struct Plan {
   int bc[40];          // vectors per pass (<= 31 + 4 for batch <= 512)
   size_t pass_bytes[40];
   size_t hdr_bytes;    // MFMA: header part of each pass's records (256-aligned)
+  int64_t gpad[40];    // forward: padded group count of each pass
+  int64_t g_split[40]; // forward: groups per launch row of each pass
   size_t ws_bytes;
 };
 
@@ -160,10 +163,8 @@ int32_t auto_splits(int64_t waves, int64_t quantum, int64_t N, int BC, int64_t m
   return (int32_t)(s < 1 ? 1 : s);
 }
 
-fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
-  fhd_opts d;
-  fhd_default_opts(&d);
-  if (!o) o = &d;
+// Checks shared by every operation's plan.
+fhd_status validate(int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
   if (M < 0 || N < 0) return fail(FHD_ERR_INVALID_ARGUMENT, "negative size (M=%lld, N=%lld)", (long long)M, (long long)N);
   if (M > 0x7fffffffLL || N > 0x7fffffffLL) return fail(FHD_ERR_INVALID_ARGUMENT, "M and N must be < 2^31");
   if (batch < 1) return fail(FHD_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);
@@ -176,12 +177,22 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     return fail(FHD_ERR_INVALID_ARGUMENT, "stages mask %d skips the gather between mu and reduce", o->stages);
   if (o->sample_splits < 0 || o->sample_splits > kMaxSplits)
     return fail(FHD_ERR_INVALID_ARGUMENT, "sample_splits must be in [0, %d] (got %d)", kMaxSplits, o->sample_splits);
-  int V = o->voxels_per_lane;
+  const int V = o->voxels_per_lane;
   if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16 && V != 32 && V != 64)
     return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8, 16, 32 or 64 (got %d)", V);
   if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA)
     return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
   if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
+  return FHD_OK;
+}
+
+fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
+  fhd_opts d;
+  fhd_default_opts(&d);
+  if (!o) o = &d;
+  fhd_status vst = validate(M, N, batch, o);
+  if (vst != FHD_OK) return vst;
+  int V = o->voxels_per_lane;
   int engine = o->engine;
   if (engine == FHD_ENGINE_AUTO)
     engine = (o->sum == FHD_SUM_KAHAN || (V != 0 && V <= 16)) ? FHD_ENGINE_VALU : FHD_ENGINE_MFMA;
@@ -194,6 +205,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   const bool mfma = engine == FHD_ENGINE_MFMA;
   const int64_t pad = mfma ? ncmri::kMfmaChunk : ncmri::kUnroll;
   p.engine = engine;
+  p.op = is_q ? FHD_OP_Q : FHD_OP_FHD;
   p.is_q = is_q;
   p.trig = o->trig;
   p.sum = o->sum;
@@ -259,6 +271,220 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
   p.ws_bytes += align256(p.partial_bytes);
   return FHD_OK;
+}
+
+// Forward operator: matrix-core engine only; waves own 32 samples and the
+// launch rows split the voxel groups.
+int64_t fwd_gpad(int64_t N, int T, int BC) {
+  const int V = 16 * T / BC;
+  const int64_t G = (N + V - 1) / V;
+  return (G + ncmri::kMfmaChunk - 1) / ncmri::kMfmaChunk * ncmri::kMfmaChunk;
+}
+
+fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
+  fhd_opts d;
+  fhd_default_opts(&d);
+  if (!o) o = &d;
+  fhd_status vst = validate(M, N, batch, o);
+  if (vst != FHD_OK) return vst;
+  const int V = o->voxels_per_lane;
+  if (o->engine == FHD_ENGINE_VALU)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only");
+  if (o->sum == FHD_SUM_KAHAN)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator sums blocked or plain, not Kahan");
+  if (V != 0 && V < 32)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32 or 64 voxels (got %d)", V);
+  const int64_t C = ncmri::kMfmaChunk;
+  p.op = FHD_OP_FORWARD;
+  p.is_q = 0;
+  p.engine = FHD_ENGINE_MFMA;
+  p.trig = o->trig;
+  p.sum = o->sum;
+  p.stages = o->stages == 0 ? FHD_STAGE_ALL : o->stages;
+  p.M = M;
+  p.N = N;
+  p.batch = batch;
+  p.mpad = M;
+  p.npass = 0;
+  int left = batch;
+  for (int g = 16; g >= 1; g /= 2)
+    while (left >= g) { p.bc[p.npass++] = g; left -= g; }
+  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass);
+  p.V = 16 * p.tiles / p.bc[0];
+  int64_t gmax = 0, gmin = -1;
+  for (int i = 0; i < p.npass; ++i) {
+    if (!ncmri::mfma_supported(p.tiles, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for T=%d BC=%d", p.tiles, p.bc[i]);
+    p.gpad[i] = fwd_gpad(N, p.tiles, p.bc[i]);
+    if (p.gpad[i] > gmax) gmax = p.gpad[i];
+    if (gmin < 0 || p.gpad[i] < gmin) gmin = p.gpad[i];
+  }
+  // summation tile in groups
+  if (o->sum == FHD_SUM_PLAIN) {
+    p.tile = gmax > 0 ? gmax : C;
+  } else if (o->tile > 0) {
+    p.tile = ((int64_t)o->tile + C - 1) / C * C;
+  } else {
+    int64_t t = 64;
+    while (t * t < gmax && t < 8192) t *= 2;
+    p.tile = t;
+  }
+  // launch rows over the groups: enough for whole rounds of resident waves
+  // when the samples alone give fewer; at least 256 groups per row
+  int32_t splits = o->sample_splits;
+  const int64_t waves = (M + 31) / 32;
+  if (o->sum == FHD_SUM_PLAIN) {
+    splits = 1;
+  } else if (splits == 0) {
+    const int64_t quantum = mfma_wave_quantum(p.tiles);
+    int64_t smax = gmin / 256;
+    if (smax > kMaxSplits) smax = kMaxSplits;
+    if (smax < 1) smax = 1;
+    int64_t s = 1;
+    if (waves > 0 && waves < quantum) {
+      s = (quantum + waves - 1) / waves;
+      for (int64_t c = 1; c <= smax; ++c)
+        if ((waves * c) % quantum == 0) { s = c; break; }
+    }
+    const int64_t row_bytes = (int64_t)p.bc[0] * M * (int64_t)sizeof(fhd_c32);
+    if (row_bytes > 0 && s > kMaxPartialBytes / row_bytes) s = kMaxPartialBytes / row_bytes;
+    if (s > smax) s = smax;
+    splits = (int32_t)(s < 1 ? 1 : s);
+  }
+  if (gmax == 0 || M == 0) splits = 1;
+  p.splits = splits;
+  for (int i = 0; i < p.npass; ++i) {
+    int64_t gs = (p.gpad[i] + splits - 1) / splits;
+    gs = (gs + C - 1) / C * C;
+    p.g_split[i] = gs > 0 ? gs : C;
+  }
+  p.m_split = 0;
+  p.hdr_bytes = 0;
+  p.ws_bytes = 0;
+  for (int i = 0; i < p.npass; ++i) {
+    // header [gpad][4], image [gpad][T][64], list of flagged groups [1 + gpad] int32
+    p.pass_bytes[i] = p.gpad[i] == 0 ? 0
+                      : align256((size_t)p.gpad[i] * 4 * sizeof(float)) +
+                            align256((size_t)p.gpad[i] * p.tiles * 64 * sizeof(float)) +
+                            (size_t)(p.gpad[i] + 1) * sizeof(int32_t);
+    p.ws_bytes += align256(p.pass_bytes[i]);
+  }
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)M * sizeof(fhd_c32) : 0;
+  p.ws_bytes += align256(p.partial_bytes);
+  return FHD_OK;
+}
+
+fhd_status make_any_plan(Plan& p, int op, int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
+  if (op == FHD_OP_FORWARD) return make_fwd_plan(p, M, N, batch, o);
+  if (op == FHD_OP_FHD || op == FHD_OP_Q) return make_plan(p, op == FHD_OP_Q ? 1 : 0, M, N, batch, o);
+  return fail(FHD_ERR_INVALID_ARGUMENT, "unknown operation %d", op);
+}
+
+// Workspace handling shared by the operations: the caller's buffer (checked)
+// or a stream-ordered allocation.
+struct Workspace {
+  void* ptr = nullptr;
+  bool own = false;
+};
+
+fhd_status acquire_workspace(const Plan& p, const fhd_opts* opts, const Range* ins, int nins,
+                             Range outr, hipStream_t s, Workspace& w) {
+  void* ws = opts ? opts->workspace : nullptr;
+  const size_t ws_given = opts ? opts->workspace_bytes : 0;
+  if (ws) {
+    if ((uintptr_t)ws % 16 != 0)
+      return fail(FHD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (ws_given < p.ws_bytes)
+      return fail(FHD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_given, p.ws_bytes);
+    Range wr{ws, ws_given};
+    if (overlaps(wr, outr)) return fail(FHD_ERR_INVALID_ARGUMENT, "workspace overlaps the output");
+    for (int i = 0; i < nins; ++i)
+      if (overlaps(wr, ins[i])) return fail(FHD_ERR_INVALID_ARGUMENT, "workspace overlaps an input array");
+  } else if (p.stages != FHD_STAGE_ALL && p.ws_bytes > 0) {
+    return fail(FHD_ERR_WORKSPACE, "running stages separately needs a caller workspace");
+  }
+  if (p.npass > 1 && p.splits > 1 &&
+      ((p.stages & FHD_STAGE_GATHER) != 0) != ((p.stages & FHD_STAGE_REDUCE) != 0))
+    return fail(FHD_ERR_INVALID_ARGUMENT,
+                "batch passes share the partial-sum buffer: run GATHER and REDUCE in the same call");
+  w.ptr = ws;
+  w.own = false;
+  return FHD_OK;
+}
+
+fhd_status run_forward(const float* kx, const float* ky, const float* kz, const float* x,
+                       const float* y, const float* z, const fhd_c32* phi, const fhd_c32* rho,
+                       fhd_c32* out, int64_t M, int64_t N, int32_t batch, const fhd_opts* opts,
+                       void* stream) {
+  g_err[0] = '\0';
+  Plan p;
+  fhd_status st = make_fwd_plan(p, M, N, batch, opts);
+  if (st != FHD_OK) return st;
+  const size_t fm = (size_t)M * sizeof(float), cm = (size_t)M * sizeof(fhd_c32);
+  const size_t fn = (size_t)N * sizeof(float), cn = (size_t)N * sizeof(fhd_c32);
+  const size_t outb = (size_t)M * (size_t)batch * sizeof(fhd_c32);
+  if (M > 0 && (!kx || !ky || !kz || !phi || !out))
+    return fail(FHD_ERR_INVALID_ARGUMENT, "null sample or output array with M=%lld", (long long)M);
+  if (N > 0 && (!x || !y || !z || !rho))
+    return fail(FHD_ERR_INVALID_ARGUMENT, "null voxel or image array with N=%lld", (long long)N);
+  Range outr{out, outb};
+  Range ins[] = {{kx, fm}, {ky, fm}, {kz, fm}, {x, fn}, {y, fn}, {z, fn}, {phi, cm},
+                 {rho, cn * (size_t)batch}};
+  for (const Range& r : ins)
+    if (overlaps(outr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "output overlaps an input array");
+  hipStream_t s = (hipStream_t)stream;
+  Workspace w;
+  st = acquire_workspace(p, opts, ins, 8, outr, s, w);
+  if (st != FHD_OK) return st;
+  if (M == 0) return FHD_OK;
+  st = check_device();
+  if (st != FHD_OK) return st;
+  if (!w.ptr && p.ws_bytes > 0) {
+    hipError_t e = hipMallocAsync(&w.ptr, p.ws_bytes, s);
+    if (e != hipSuccess) return fail(FHD_ERR_HIP, "hipMallocAsync(%zu): %s", p.ws_bytes, hipGetErrorString(e));
+    w.own = true;
+  }
+  fhd_status result = FHD_OK;
+  char* base = (char*)w.ptr;
+  float2* partial = nullptr;
+  if (p.partial_bytes > 0) {
+    size_t recs = 0;
+    for (int i = 0; i < p.npass; ++i) recs += align256(p.pass_bytes[i]);
+    partial = (float2*)(base + recs);
+  }
+  int b0 = 0;
+  for (int i = 0; i < p.npass && result == FHD_OK; ++i) {
+    const int bc = p.bc[i];
+    const size_t hb = align256((size_t)p.gpad[i] * 4 * sizeof(float));
+    const size_t ib = align256((size_t)p.gpad[i] * p.tiles * 64 * sizeof(float));
+    ncmri::FwdArgs fa{kx, ky, kz, x, y, z, (const float2*)phi,
+                      (const float2*)(rho ? rho + (int64_t)b0 * N : nullptr), M, N, p.gpad[i], p.tile,
+                      p.g_split[i], (float*)base, (float*)(base + hb),
+                      p.gpad[i] > 0 ? (int32_t*)(base + hb + ib) : nullptr,
+                      (float2*)(out + (int64_t)b0 * M), p.splits > 1 ? partial : nullptr};
+    hipError_t e = hipSuccess;
+    const char* what = "pack";
+    if (p.stages & FHD_STAGE_MU) e = ncmri::launch_fwd_pack(p.tiles, bc, fa, s);
+    if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
+      what = "gather";
+      e = ncmri::launch_fwd_gather(p.trig, p.tiles, bc, p.splits, fa, s);
+    }
+    if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE)) {
+      what = "reduce";
+      // the rows' partial sums -> output ([BC][M] values), then the groups
+      // off the common offsets are added
+      ncmri::GatherArgs ga{nullptr, 0, p.tile, x, y, z, M, fa.out, 0, fa.partial};
+      e = ncmri::launch_reduce(bc, false, p.splits, ga, s);
+      if (e == hipSuccess) e = ncmri::launch_fwd_direct(p.trig, p.tiles, bc, fa, s);
+    }
+    if (e != hipSuccess) result = fail(FHD_ERR_HIP, "forward %s kernel launch: %s", what, hipGetErrorString(e));
+    base += align256(p.pass_bytes[i]);
+    b0 += bc;
+  }
+  if (w.own) {
+    hipError_t e = hipFreeAsync(w.ptr, s);
+    if (e != hipSuccess && result == FHD_OK) result = fail(FHD_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e));
+  }
+  return result;
 }
 
 fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, const float* x,
@@ -382,29 +608,30 @@ NCMRI_API void fhd_default_opts(fhd_opts* o) {
   o->engine = FHD_ENGINE_AUTO;
 }
 
-NCMRI_API size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+NCMRI_API size_t fhd_workspace_bytes(int64_t M, int64_t N, int32_t batch, int32_t op,
                                      const fhd_opts* opts) {
   try {
     Plan p;
-    if (make_plan(p, is_q ? 1 : 0, M, N, batch, opts) != FHD_OK) return 0;
+    if (make_any_plan(p, op, M, N, batch, opts) != FHD_OK) return 0;
     return p.ws_bytes;
   } catch (...) {
     return 0;
   }
 }
 
-NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t is_q,
+NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int32_t op,
                                        const fhd_opts* opts, fhd_plan_info* info) {
   try {
     g_err[0] = '\0';
     if (!info) return fail(FHD_ERR_INVALID_ARGUMENT, "info is NULL");
     Plan p;
-    fhd_status st = make_plan(p, is_q ? 1 : 0, M, N, batch, opts);
+    fhd_status st = make_any_plan(p, op, M, N, batch, opts);
     if (st != FHD_OK) return st;
     info->voxels_per_lane = p.V;
     info->tile = (int32_t)p.tile;
     info->passes = p.npass;
     info->record_dwords = p.npass == 0 ? 0
+                          : p.op == FHD_OP_FORWARD ? 4 + 64 * p.tiles
                           : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig, p.tiles)
                                                          : ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]);
     info->padded_samples = p.mpad;
@@ -423,6 +650,17 @@ NCMRI_API fhd_status fhd_compute(const float* kx, const float* ky, const float* 
                                  int32_t batch, const fhd_opts* opts, void* stream) {
   try {
     return run(0, kx, ky, kz, x, y, z, phi, D, FhD, M, N, batch, opts, stream);
+  } catch (...) {
+    return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+NCMRI_API fhd_status fhd_forward(const float* kx, const float* ky, const float* kz, const float* x,
+                                 const float* y, const float* z, const fhd_c32* phi,
+                                 const fhd_c32* rho, fhd_c32* D, int64_t M, int64_t N,
+                                 int32_t batch, const fhd_opts* opts, void* stream) {
+  try {
+    return run_forward(kx, ky, kz, x, y, z, phi, rho, D, M, N, batch, opts, stream);
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
   }

@@ -1,0 +1,434 @@
+// gfx950 matrix-core forward operator (PMPP ch. 17 "Iterative MRI
+// reconstruction", section 17.2: F models the imaging physics, F[m][n] =
+// phi_m exp(-i 2 pi k_m . x_n), the matrix whose conjugate transpose the F^H D
+// kernels apply; section 17.3 step 3 synthesises scan data from an image):
+//
+//   D[b][m] = phi_m sum_n rho_b[n] exp(-i 2 pi k_m . x_n)
+//
+// The adjoint engine with the roles of samples and voxels swapped.  With the
+// voxels in groups of V at the first group's offsets d_j (x_n = x_g + d_j),
+//
+//   D[b][m] = phi_m sum_j exp(-i 2 pi k_m . d_j) G[m][j][b],
+//   G[m][j][b] = sum_g exp(-i 2 pi k_m . x_g) rho_b[x_g + d_j],
+//
+// and for 32 samples and 16 T complex columns (j, b) the sum over groups is
+// the real matrix product [Re | Im] (32 x 32T) += sum_g E_g (32 x 2) W_g (2 x 32T)
+// with E_g[m] = (cos, sin)(2 pi k_m . x_g) and W_g = [rr ri; ri -rr] per
+// column, i.e. (c - i s)(rr + i ri): one v_mfma_f32_32x32x2_f32 per tile and
+// group.  Each wave owns 32 samples (sample m in lanes m and m + 32: cosine and
+// sine, the cosine with a quarter turn added to the phase); the packed image
+// is streamed through LDS in 32-group chunks by LDS DMA, shared by the 4
+// waves of a workgroup, exactly as the adjoint streams its sample records.
+// After the last group the wave writes G to LDS and lanes 0-31 contract their
+// sample's row with exp(-i 2 pi k_m . d_j) and multiply by phi_m.
+//
+// Groups whose voxels are not on the first group's offsets are packed as
+// zeros and flagged; one workgroup then lists them in increasing order
+// (fwd_list_kernel) and fwd_direct_kernel adds their voxels per sample on the
+// VALU after the launch rows have been reduced (it returns at once when the
+// list is empty, as on a grid).
+#include "fhd_internal.h"
+#include "fhd_mfma_common.h"
+#include "fhd_trig.h"
+
+namespace ncmri {
+namespace {
+
+// Group g of V voxels (first voxel n0 = g V) is on the common offsets when
+// every voxel n0 + j < N satisfies x[n0 + j] - x[n0] == x[j] - x[0] (exact,
+// in double; likewise y, z).
+__device__ bool group_regular(const float* __restrict__ x, const float* __restrict__ y,
+                              const float* __restrict__ z, int64_t N, int64_t n0, int V) {
+  const double bx = x[0], by = y[0], bz = z[0];
+  const double gx = x[n0], gy = y[n0], gz = z[n0];
+  for (int j = 1; j < V; ++j) {
+    const int64_t n = n0 + j;
+    if (n >= N) break;
+    if (!((double)x[n] - gx == (double)x[j] - bx && (double)y[n] - gy == (double)y[j] - by &&
+          (double)z[n] - gz == (double)z[j] - bz))
+      return false;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Packing: one lane per (padded group, complex column).
+__global__ void __launch_bounds__(kWorkgroup) fwd_pack_kernel(FwdArgs a, int T, int BC) {
+  const int cols = 16 * T;
+  const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  const int64_t g = idx / cols;
+  const int cc = (int)(idx - g * cols);
+  if (g >= a.gpad) return;
+  const int V = cols / BC;
+  const int64_t n0 = g * V;
+  const bool inside = n0 < a.N;
+  const bool reg = inside ? group_regular(a.x, a.y, a.z, a.N, n0, V) : true;
+  if (cc == 0) {
+    float* h = a.ghdr + g * 4;
+    h[0] = inside ? a.x[n0] : 0.0f;
+    h[1] = inside ? a.y[n0] : 0.0f;
+    h[2] = inside ? a.z[n0] : 0.0f;
+    h[3] = reg ? 0.0f : 1.0f;
+  }
+  const int b = cc / V, j = cc % V;
+  const int64_t n = n0 + j;
+  const float2 r = (inside && reg && n < a.N) ? a.rho[(int64_t)b * a.N + n] : make_float2(0.0f, 0.0f);
+  float* w = a.gwb + (g * T + cc / 16) * 64;
+  const int c = cc % 16;
+  w[2 * c] = r.x; w[2 * c + 1] = r.y; w[32 + 2 * c] = r.y; w[33 + 2 * c] = -r.x;
+}
+
+// Lists the flagged groups: each of the workgroup's lanes counts the flags of
+// a contiguous range of groups, an exclusive scan of the counts in LDS gives
+// each range's place, and the ranges write their group indices in order.
+// glist[0] = count, glist[1 + i] = i-th flagged group.
+__global__ void __launch_bounds__(kWorkgroup) fwd_list_kernel(FwdArgs a, int V) {
+  __shared__ int32_t cnt[kWorkgroup];
+  const int tid = threadIdx.x;
+  const int64_t G = (a.N + V - 1) / V;
+  const int64_t per = (G + kWorkgroup - 1) / kWorkgroup;
+  const int64_t g0 = tid * per < G ? tid * per : G;
+  const int64_t g1 = g0 + per < G ? g0 + per : G;
+  int32_t c = 0;
+  for (int64_t g = g0; g < g1; ++g) c += a.ghdr[g * 4 + 3] != 0.0f ? 1 : 0;
+  cnt[tid] = c;
+  __syncthreads();
+  // exclusive prefix sum (Hillis-Steele on the inclusive sums, then shift)
+  for (int off = 1; off < kWorkgroup; off *= 2) {
+    const int32_t v = tid >= off ? cnt[tid - off] : 0;
+    __syncthreads();
+    cnt[tid] += v;
+    __syncthreads();
+  }
+  int32_t pos = cnt[tid] - c;
+  if (tid == kWorkgroup - 1) a.glist[0] = cnt[tid];
+  for (int64_t g = g0; g < g1; ++g)
+    if (a.ghdr[g * 4 + 3] != 0.0f) a.glist[1 + pos++] = (int32_t)g;
+}
+
+// Per-lane sample wave-vector: k (HW) or its exact split k = kh + kl, kh a
+// multiple of 2^-12 (accurate), as the adjoint's records kernel forms it.
+template <int TRIG>
+struct SampleK {
+  static constexpr int NK = TRIG == kTrigHw ? 3 : 6;
+  float v[NK];
+  __device__ void load(const FwdArgs& a, int64_t m, bool valid) {
+    const float kx = valid ? a.kx[m] : 0.0f, ky = valid ? a.ky[m] : 0.0f, kz = valid ? a.kz[m] : 0.0f;
+    if constexpr (TRIG == kTrigHw) {
+      v[0] = kx; v[1] = ky; v[2] = kz;
+    } else {
+      v[0] = __builtin_rintf(kx * 4096.0f) * (1.0f / 4096.0f);
+      v[1] = __builtin_rintf(ky * 4096.0f) * (1.0f / 4096.0f);
+      v[2] = __builtin_rintf(kz * 4096.0f) * (1.0f / 4096.0f);
+      v[3] = kx - v[0]; v[4] = ky - v[1]; v[5] = kz - v[2];
+    }
+  }
+  // sin(2 pi (k . p + q)); the accurate path reduces kh . p exactly first.
+  __device__ __forceinline__ float sin_phase(float px, float py, float pz, float q) const {
+    if constexpr (TRIG == kTrigHw) {
+      const float t = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, __builtin_fmaf(v[0], px, q)));
+      return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(t));
+    } else {
+      float th = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, __builtin_fmaf(v[0], px, q)));
+      th = th - __builtin_rintf(th);
+      const float tl = __builtin_fmaf(v[5], pz, __builtin_fmaf(v[4], py, v[3] * px));
+      float s, c;
+      sincos_turns(th + tl, s, c);
+      return s;
+    }
+  }
+  // cos and sin of 2 pi k . p.
+  __device__ __forceinline__ void sincos_phase(float px, float py, float pz, float& c, float& s) const {
+    if constexpr (TRIG == kTrigHw) {
+      const float t = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, v[0] * px));
+      const float f = __builtin_amdgcn_fractf(t);
+      s = __builtin_amdgcn_sinf(f);
+      c = __builtin_amdgcn_cosf(f);
+    } else {
+      float th = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, v[0] * px));
+      th = th - __builtin_rintf(th);
+      const float tl = __builtin_fmaf(v[5], pz, __builtin_fmaf(v[4], py, v[3] * px));
+      sincos_turns(th + tl, s, c);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Matrix-core gather over the regular groups.
+template <int T, int BC, int TRIG>
+struct FwdGather {
+  static constexpr int V = 16 * T / BC;
+  static constexpr int C = kMfmaChunk;
+  static constexpr int NW = kWorkgroup / 64;
+  static constexpr int NB = C * T * 16 / 64;  // 1 KiB image blocks per chunk
+  static constexpr int NH = C;                // header float4s per chunk (one per group)
+  static_assert(V >= 1 && V * BC == 16 * T, "group shape");
+  static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
+
+  __device__ static __forceinline__ void stage(const FwdArgs& a, int64_t g, int wig, int lane,
+                                               float4* lb, float4* lh) {
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + g * (T * 16), NB * 64 * 16);
+#pragma unroll
+    for (int i = 0; i < NB / NW; ++i) {
+      const int blk = i * NW + wig;
+      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
+    }
+    if (wig == 0 && lane < NH)
+      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.ghdr) + g, NH * 16), lane * 16, lh);
+  }
+
+  __device__ static __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // One chunk of 32 groups, pipelined by one group like the adjoint's loop.
+  __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb,
+                                               int lane, const SampleK<TRIG>& k, float q,
+                                               f32x16 (&acc)[T]) {
+    float hc[3], bc[T];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) hc[i] = hb[i];
+#pragma unroll
+    for (int t = 0; t < T; ++t) bc[t] = wb[t * 64 + lane];
+#pragma unroll
+    for (int s = 0; s < C; ++s) {
+      float hn[3], bn[T];
+      if (s + 1 < C) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hn[i] = hb[(s + 1) * 4 + i];
+#pragma unroll
+        for (int t = 0; t < T; ++t) bn[t] = wb[((s + 1) * T + t) * 64 + lane];
+      }
+      sched_fence();
+      const float e = k.sin_phase(hc[0], hc[1], hc[2], q);
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(e, bc[t], acc[t], 0, 0, 0);
+      sched_fence();
+      if (s + 1 < C) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hc[i] = hn[i];
+#pragma unroll
+        for (int t = 0; t < T; ++t) bc[t] = bn[t];
+      }
+    }
+  }
+
+  __device__ static void run(const FwdArgs& a) {
+    __shared__ float4 sb0[C * T * 16], sb1[C * T * 16];
+    __shared__ float4 sh0[NH], sh1[NH];
+    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int64_t wave = (int64_t)blockIdx.x * NW + wig;
+    const int64_t m = wave * 32 + (lane & 31);   // this lane's sample
+    const bool valid = m < a.M;
+    SampleK<TRIG> k;
+    k.load(a, m, valid);
+    const float q = lane < 32 ? 0.25f : 0.0f;
+
+    // this launch row's groups
+    const int32_t row = (int32_t)blockIdx.y;
+    const int64_t lo64 = (int64_t)row * a.g_split;
+    const int64_t lo = lo64 < a.gpad ? lo64 : a.gpad;
+    const int64_t hi = lo64 + a.g_split < a.gpad ? lo64 + a.g_split : a.gpad;
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    const int32_t cpt = (int32_t)(a.tile / C);
+    if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
+    publish();
+    f32x16 acc[T], tot[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) { acc[t] = f32x16{}; tot[t] = f32x16{}; }
+    int32_t left = cpt;
+    for (int32_t ch = 0; ch < nch; ch += 2) {
+      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, q, acc);
+      if (--left == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        left = cpt;
+      }
+      publish();
+      if (ch + 1 >= nch) break;
+      if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+      chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, q, acc);
+      if (--left == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        left = cpt;
+      }
+      publish();
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) tot[t] += acc[t];
+
+    // Finish.  Every wave has passed the last barrier, so the staging buffers
+    // are free: each wave stores its 32 x 32T block of G there (waves 0, 1 in
+    // sb0, waves 2, 3 in sb1; 4 T KiB each) ...
+    float* gl = reinterpret_cast<float*>(wig < 2 ? sb0 : sb1) + (wig & 1) * (32 * 32 * T);
+    const int c = lane & 31;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+        gl[i * (32 * T) + 32 * t + c] = tot[t][v];
+      }
+    __syncthreads();
+    // ... and lane i < 32 contracts row i (its sample) with exp(-i 2 pi k . d_j)
+    // over the offsets j, then multiplies by phi_m.
+    if (lane >= 32 || !valid) return;
+    const float* gr = gl + lane * (32 * T);
+    float dre[BC], dim[BC];
+#pragma unroll
+    for (int b = 0; b < BC; ++b) { dre[b] = 0.0f; dim[b] = 0.0f; }
+    const bool any_voxel = a.N > 0;
+    const float x0 = any_voxel ? a.x[0] : 0.0f, y0 = any_voxel ? a.y[0] : 0.0f, z0 = any_voxel ? a.z[0] : 0.0f;
+    for (int j = 0; j < V && j < a.N; ++j) {
+      float cj = 1.0f, sj = 0.0f;
+      if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
+#pragma unroll
+      for (int b = 0; b < BC; ++b) {
+        const int cc = b * V + j;
+        const float gre = gr[2 * cc], gim = gr[2 * cc + 1];
+        // (cj - i sj)(gre + i gim)
+        dre[b] = __builtin_fmaf(cj, gre, __builtin_fmaf(sj, gim, dre[b]));
+        dim[b] = __builtin_fmaf(cj, gim, __builtin_fmaf(-sj, gre, dim[b]));
+      }
+    }
+    const float2 ph = a.phi[m];
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.M : a.out;
+#pragma unroll
+    for (int b = 0; b < BC; ++b)
+      dst[(int64_t)b * a.M + m] = make_float2(ph.x * dre[b] - ph.y * dim[b], ph.x * dim[b] + ph.y * dre[b]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Direct evaluation of the listed groups: one lane per sample, the groups in
+// increasing order (indices and voxels read as wave-uniform scalars); the sum
+// is blocked by `tile` listed groups and added into the (already reduced)
+// output.
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) fwd_direct_kernel(FwdArgs a) {
+  constexpr int V = 16 * T / BC;
+  const int32_t count = a.glist[0];
+  if (count == 0) return;
+  const int64_t m = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  const bool valid = m < a.M;
+  SampleK<TRIG> k;
+  k.load(a, m, valid);
+  float tre[BC], tim[BC], are[BC], aim[BC];
+#pragma unroll
+  for (int b = 0; b < BC; ++b) { tre[b] = 0.0f; tim[b] = 0.0f; are[b] = 0.0f; aim[b] = 0.0f; }
+  int64_t left = a.tile;
+  for (int32_t i = 0; i < count; ++i) {
+    const int64_t g = a.glist[1 + i];
+    for (int j = 0; j < V; ++j) {
+      const int64_t n = g * V + j;
+      if (n >= a.N) break;
+      float c, s;
+      k.sincos_phase(a.x[n], a.y[n], a.z[n], c, s);
+#pragma unroll
+      for (int b = 0; b < BC; ++b) {
+        const float2 r = a.rho[(int64_t)b * a.N + n];
+        // (rr + i ri)(c - i s)
+        are[b] = __builtin_fmaf(r.x, c, __builtin_fmaf(r.y, s, are[b]));
+        aim[b] = __builtin_fmaf(r.y, c, __builtin_fmaf(-r.x, s, aim[b]));
+      }
+    }
+    if (--left == 0) {
+#pragma unroll
+      for (int b = 0; b < BC; ++b) { tre[b] += are[b]; tim[b] += aim[b]; are[b] = 0.0f; aim[b] = 0.0f; }
+      left = a.tile;
+    }
+  }
+  if (!valid) return;
+  const float2 ph = a.phi[m];
+#pragma unroll
+  for (int b = 0; b < BC; ++b) {
+    const float re = tre[b] + are[b], im = tim[b] + aim[b];
+    float2* o = a.out + (int64_t)b * a.M + m;
+    const float2 prev = *o;
+    *o = make_float2(prev.x + (ph.x * re - ph.y * im), prev.y + (ph.x * im + ph.y * re));
+  }
+}
+
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(T == 2 ? 4 : 2)))
+fwd_gather_kernel(FwdArgs a) {
+  FwdGather<T, BC, TRIG>::run(a);
+}
+
+using FwdFn = void (*)(FwdArgs);
+
+template <int T, int BC>
+void pick(int trig, FwdFn& gather, FwdFn& direct) {
+  if (trig == kTrigHw) {
+    gather = fwd_gather_kernel<T, BC, kTrigHw>;
+    direct = fwd_direct_kernel<T, BC, kTrigHw>;
+  } else {
+    gather = fwd_gather_kernel<T, BC, kTrigAccurate>;
+    direct = fwd_direct_kernel<T, BC, kTrigAccurate>;
+  }
+}
+
+template <int T>
+bool select_bc(int trig, int BC, FwdFn& gather, FwdFn& direct) {
+  switch (BC) {
+    case 1: pick<T, 1>(trig, gather, direct); return true;
+    case 2: pick<T, 2>(trig, gather, direct); return true;
+    case 4: pick<T, 4>(trig, gather, direct); return true;
+    case 8: pick<T, 8>(trig, gather, direct); return true;
+    case 16: pick<T, 16>(trig, gather, direct); return true;
+    default: return false;
+  }
+}
+
+bool select_fwd(int trig, int T, int BC, FwdFn& gather, FwdFn& direct) {
+  if (T == 2) return select_bc<2>(trig, BC, gather, direct);
+  if (T == 4) return select_bc<4>(trig, BC, gather, direct);
+  return false;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_pack(int T, int BC, const FwdArgs& a, hipStream_t s) {
+  FwdFn g, d;
+  if (!select_fwd(kTrigHw, T, BC, g, d) || a.gpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  if (a.gpad <= 0) return hipSuccess;
+  if (!a.glist) return hipErrorInvalidValue;
+  const int64_t lanes = a.gpad * 16 * T;
+  const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(fwd_pack_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, T, BC);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_list_kernel, dim3(1), dim3(kWorkgroup), 0, s, a, 16 * T / BC);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdArgs& a,
+                             hipStream_t s) {
+  FwdFn g, d;
+  if (!select_fwd(trig, T, BC, g, d) || splits < 1 || (splits > 1) != (a.partial != nullptr))
+    return hipErrorInvalidValue;
+  if (a.gpad % kMfmaChunk != 0 || a.g_split % kMfmaChunk != 0 || a.tile % kMfmaChunk != 0 ||
+      a.tile <= 0)
+    return hipErrorInvalidValue;
+  if (a.M <= 0) return hipSuccess;
+  const int64_t waves = (a.M + 31) / 32;
+  const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStream_t s) {
+  FwdFn g, d;
+  if (!select_fwd(trig, T, BC, g, d) || a.tile <= 0) return hipErrorInvalidValue;
+  if (a.M <= 0 || a.N <= 0 || a.gpad <= 0) return hipSuccess;
+  if (!a.glist) return hipErrorInvalidValue;
+  const int64_t blocks = (a.M + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(d, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ncmri

@@ -111,6 +111,39 @@ struct MfmaArgs {
   float2* partial;       // [rows][BC][N] when rows > 1, else nullptr
 };
 
+// ---------------------------------------------------------------------------
+// Forward operator D[b][m] = phi_m sum_n rho_b[n] exp(-i 2 pi k_m . x_n) on the
+// matrix cores: waves own 32 samples, the K dimension runs over voxel groups.
+// Packed image of one pass (groups g < gpad, gpad a multiple of kMfmaChunk):
+//   header ghdr[g][4]: x, y, z of the group's first voxel, and 1.0 when the
+//     group is not on the first group's offsets (0.0 otherwise);
+//   image  gwb[g][T][64]: complex column cc = 16 t + c holds rho_b[g V + j]
+//     (b = cc / V, j = cc % V; zero past N and in irregular groups) as the
+//     MFMA B operand rows [2c] = re, [2c+1] = im, [32+2c] = im, [33+2c] = -re.
+struct FwdArgs {
+  const float* kx; const float* ky; const float* kz;
+  const float* x; const float* y; const float* z;
+  const float2* phi;
+  const float2* rho;     // first image of this pass ([BC][N])
+  int64_t M, N;
+  int64_t gpad;          // padded group count
+  int64_t tile;          // groups per summation tile (multiple of kMfmaChunk)
+  int64_t g_split;       // groups per launch row (multiple of kMfmaChunk)
+  float* ghdr;           // [gpad][4]
+  float* gwb;            // [gpad][T][64]
+  int32_t* glist;        // [1 + groups]: count of groups off the common offsets, then their
+                         // indices in increasing order
+  float2* out;           // first output vector of this pass ([BC][M])
+  float2* partial;       // [rows][BC][M] when rows > 1, else nullptr
+};
+
+// Packs the image (and lists the groups off the common offsets).
+hipError_t launch_fwd_pack(int T, int BC, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdArgs& a,
+                             hipStream_t s);
+// Adds the groups off the common offsets into a.out (after the rows' reduction).
+hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStream_t s);
+
 // T: 32-column factor tiles per group phase (2 or 4); BC: vectors of the pass.
 hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
                                hipStream_t s);

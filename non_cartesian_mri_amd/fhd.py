@@ -37,16 +37,27 @@ def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages=
     return o
 
 
-def fhd_workspace_bytes(M: int, N: int, batch: int = 1, is_q: bool = False, **opts) -> int:
+_OPS = {"fhd": _lib.FHD_OP_FHD, "q": _lib.FHD_OP_Q, "forward": _lib.FHD_OP_FORWARD}
+
+
+def _op_code(is_q, op) -> int:
+    if op is None:
+        return _lib.FHD_OP_Q if is_q else _lib.FHD_OP_FHD
+    return _OPS[op] if isinstance(op, str) else int(op)
+
+
+def fhd_workspace_bytes(M: int, N: int, batch: int = 1, is_q: bool = False, op=None, **opts) -> int:
+    """Workspace bytes of fhd_compute (default), q_compute (is_q) or op="forward"."""
     o = make_opts(**opts)
-    return int(_lib.load().fhd_workspace_bytes(int(M), int(N), int(batch), int(bool(is_q)), ctypes.byref(o)))
+    return int(_lib.load().fhd_workspace_bytes(int(M), int(N), int(batch), _op_code(is_q, op),
+                                               ctypes.byref(o)))
 
 
-def fhd_describe_plan(M: int, N: int, batch: int = 1, is_q: bool = False, **opts) -> dict:
+def fhd_describe_plan(M: int, N: int, batch: int = 1, is_q: bool = False, op=None, **opts) -> dict:
     """The launch plan (group size, tile, passes, record size, workspace) for these sizes."""
     o = make_opts(**opts)
     info = _lib.FhdPlanInfo()
-    _lib.check(_lib.load().fhd_describe_plan(int(M), int(N), int(batch), int(bool(is_q)),
+    _lib.check(_lib.load().fhd_describe_plan(int(M), int(N), int(batch), _op_code(is_q, op),
                                              ctypes.byref(o), ctypes.byref(info)))
     return {k: getattr(info, k) for k, _ in _lib.FhdPlanInfo._fields_}
 
@@ -141,3 +152,42 @@ def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
                                M, N, ctypes.byref(o), _stream_ptr(stream))
     _lib.check(st)
     return out
+
+
+def fhd_forward(kx, ky, kz, x, y, z, phi, rho, *, trig="accurate", sum="blocked",
+                voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
+                stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
+    """F rho on the GPU: rho complex64 [N] or [B, N]; returns complex64 [M] or [B, M].
+
+    D[b][m] = phi[m] sum_n rho[b][n] exp(-i 2 pi k_m . x_n), the adjoint of
+    fhd_compute.  The work is enqueued on `stream` (default: torch's current stream).
+    """
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    _dev_c64(rho, "rho")
+    M, N = kx.numel(), x.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == M) or not (y.numel() == z.numel() == N):
+        raise ValueError("inconsistent sizes")
+    squeeze = rho.dim() == 1
+    R2 = rho.reshape(1, -1) if squeeze else rho
+    if R2.dim() != 2 or R2.shape[1] != N:
+        raise ValueError("rho must be [N] or [B, N]")
+    B = R2.shape[0]
+    if out is None:
+        out = torch.empty((B, M), dtype=torch.complex64, device=kx.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != B * M:
+            raise ValueError("out must hold B*M complex values")
+    if workspace is None:
+        nbytes = fhd_workspace_bytes(M, N, B, op="forward", trig=trig, sum=sum,
+                                     voxels_per_lane=voxels_per_lane, tile=tile,
+                                     sample_splits=sample_splits, engine=engine)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kx.device)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
+    st = _lib.load().fhd_forward(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
+                                 y.data_ptr(), z.data_ptr(), phi.data_ptr(), R2.data_ptr(),
+                                 out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
+    _lib.check(st)
+    return out.reshape(M) if squeeze else out.reshape(B, M)

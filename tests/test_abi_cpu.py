@@ -301,3 +301,65 @@ def test_describe_plan_zero_sizes(lib):
             assert r["sample_splits"] == 1
     assert fhd_describe_plan(100, 0, engine="valu")["workspace_bytes"] == (100 * 12 * 4 + 255) // 256 * 256
     assert fhd_describe_plan(100, 0)["workspace_bytes"] == 128 * 32 + 128 * 512
+
+
+# ----------------------------- forward operator -----------------------------
+def _fwd(lib, M=16, N=8, batch=1, opts=None, **ptrs):
+    p = dict(kx=A, ky=A + 0x1000, kz=A + 0x2000, x=A + 0x3000, y=A + 0x4000, z=A + 0x5000,
+             phi=A + 0x6000, rho=A + 0x8000, out=A + 0x100000)
+    p.update(ptrs)
+    return lib.fhd_forward(p["kx"], p["ky"], p["kz"], p["x"], p["y"], p["z"], p["phi"], p["rho"],
+                           p["out"], M, N, batch, None if opts is None else ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-1), dict(batch=0), dict(kx=None), dict(phi=None), dict(out=None),
+    dict(x=None), dict(rho=None), dict(out=A + 0x8000 + 8),      # output inside rho
+    dict(out=A + 0x1000),                                         # output aliases ky
+])
+def test_forward_argument_errors(lib, kw):
+    assert _fwd(lib, **kw) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert lib.fhd_last_error() != b""
+
+
+@pytest.mark.parametrize("field,value,text", [
+    ("engine", _lib.FHD_ENGINE_VALU, b"MFMA engine only"),
+    ("sum", _lib.FHD_SUM_KAHAN, b"not Kahan"),
+    ("voxels_per_lane", 8, b"group sizes"),
+])
+def test_forward_option_errors(lib, field, value, text):
+    assert _fwd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert text in lib.fhd_last_error()
+
+
+def test_forward_empty_sample_set_is_a_noop(lib):
+    assert _fwd(lib, M=0, kx=None, ky=None, kz=None, phi=None, out=None) == _lib.FHD_OK
+
+
+def test_forward_plan(lib):
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan, fhd_workspace_bytes
+    a256 = lambda b: (b + 255) // 256 * 256
+    # 128^3: four tiles, groups of 64 voxels -> 32,768 groups; 8192 waves of 32 samples fill the GPU
+    p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
+    assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 64
+    assert p["record_dwords"] == 4 + 256 and p["padded_samples"] == 262144
+    assert p["sample_splits"] == 1 and p["tile"] == 256
+    pas = lambda g, T: a256(a256(g * 16) + a256(g * 256 * T) + 4 * (g + 1))
+    assert p["workspace_bytes"] == pas(32768, 4)
+    assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw") == p["workspace_bytes"]
+    # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 256 groups each)
+    s = fhd_describe_plan(2048, 32 ** 3, op="forward", trig="hw")
+    assert s["voxels_per_lane"] == 32 and s["sample_splits"] == 4 and s["tile"] == 64
+    assert s["workspace_bytes"] == pas(1024, 2) + a256(4 * 2048 * 8)
+    # batch 3 on 64^3: passes of 2 and 1 images, groups of 32 and 64 voxels
+    b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1)
+    assert b["passes"] == 2 and b["voxels_per_lane"] == 32
+    assert b["workspace_bytes"] == pas(8192, 4) + pas(4096, 4)
+    # explicit group size, plain sum (one row, one tile)
+    g = fhd_describe_plan(1000, 128 ** 3, op="forward", voxels_per_lane=32, sum="plain")
+    assert g["voxels_per_lane"] == 32 and g["sample_splits"] == 1 and g["tile"] == 65536
+    # no voxels: nothing to pack
+    assert fhd_describe_plan(1000, 0, op="forward")["workspace_bytes"] == 0
+    info = _lib.FhdPlanInfo()
+    assert lib.fhd_describe_plan(10, 10, 1, 3, None, ctypes.byref(info)) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert b"operation" in lib.fhd_last_error()
