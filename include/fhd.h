@@ -22,6 +22,10 @@
  * pages never print Mu; conj(phi) D makes the sum the conjugate transpose of
  * F[m][n] = phi[m] exp(-i 2 pi k_m . x_n) applied to D).
  *
+ * The reconstruction entry points (fhd_toeplitz_kernel, fhd_normal_apply,
+ * fhd_cg_solve) solve for the image with these operators; they are declared
+ * below with their own conventions.
+ *
  * Work is split as the pages' loop fission does (section 17.3 step 1, Figs.
  * 17.6/17.7): a per-sample kernel forms Mu and packs one k-space record per
  * sample; then a gather kernel over groups of voxels sums every sample (Figs.
@@ -198,6 +202,71 @@ fhd_status fhd_forward(const float* kx, const float* ky, const float* kz,
                        const fhd_c32* phi, const fhd_c32* rho, fhd_c32* D,
                        int64_t M, int64_t N, int32_t batch,
                        const fhd_opts* opts, void* stream);
+
+/*
+ * Iterative reconstruction (section 17.2, Fig. 17.3): conjugate gradient on
+ *
+ *   (F^H F + lambda W^H W) rho = F^H D
+ *
+ * for an image on a unit voxel grid: nx x ny x nz voxels, x fastest, voxel
+ * (ix, iy, iz) at coordinates (ix - nx/2, iy - ny/2, iz - nz/2) (any shift of
+ * the grid gives the same operator).  F^H F is applied through Q, which is
+ * computed once per trajectory (section 17.2): its entry for voxels n, n' is
+ * Q at x_n - x_n', so F^H F is a convolution with Q on the grid of coordinate
+ * differences and runs as FFTs of twice the grid size per axis.  W is the
+ * first difference between face neighbours (a stand-in for the pages'
+ * anatomical prior), so W^H W p at a voxel is the sum of p[n] - p[n'] over its
+ * up to 6 neighbours.  All arrays are device arrays, complex images are
+ * fhd_c32[nz][ny][nx]; 8 nx ny nz must be below 2^31.
+ */
+
+/* Bytes of the Toeplitz spectrum Qhat: 8 nx ny nz fhd_c32 (0 if a size < 1). */
+size_t fhd_toeplitz_bytes(int32_t nx, int32_t ny, int32_t nz);
+
+/*
+ * Qhat = FFT(Q on the (2nz, 2ny, 2nx) grid of coordinate differences, index i
+ * along an axis of n voxels standing for difference i if i < n, i - 2n else)
+ * / (8 nx ny nz).  Q is computed by the q_compute path (opts as for q_compute,
+ * without workspace or stages: the call allocates its scratch with
+ * hipMallocAsync on `stream`).  Qhat is overwritten; it must not overlap the
+ * inputs.  M == 0 gives Qhat = 0.
+ */
+fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const float* kz,
+                               const fhd_c32* phi, int64_t M,
+                               int32_t nx, int32_t ny, int32_t nz,
+                               fhd_c32* Qhat, const fhd_opts* opts, void* stream);
+
+/* Workspace bytes of fhd_normal_apply / fhd_cg_solve (0 if a size < 1):
+ * two padded grids, three images and the dot-product partial sums. */
+size_t fhd_cg_workspace_bytes(int32_t nx, int32_t ny, int32_t nz);
+
+/*
+ * Ap = F^H F p + lambda W^H W p with Qhat from fhd_toeplitz_kernel.
+ *   p, Ap     : fhd_c32[nz][ny][nx]; Ap is overwritten and must not overlap p
+ *   lambda    : >= 0
+ *   workspace : >= fhd_cg_workspace_bytes() bytes, 16-byte aligned, caller-owned
+ */
+fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+                            float lambda, const fhd_c32* p, fhd_c32* Ap,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * `iters` conjugate-gradient iterations from the start image in x (updated in
+ * place): r = b - A x, p = r; then alpha = <r,r>/<p,Ap>, x += alpha p,
+ * r -= alpha Ap, beta = <r',r'>/<r,r>, p = r' + beta p, with A the operator of
+ * fhd_normal_apply.  Dot products are summed in double in a fixed order (the
+ * result does not depend on scheduling); alpha and beta stay on the device,
+ * so the call enqueues every iteration without synchronising.
+ *   b     : fhd_c32[nz][ny][nx] right-hand side (F^H D)
+ *   x     : fhd_c32[nz][ny][nx] start image in, solution out
+ *   resid : NULL or a DEVICE double[iters + 1] receiving <r, r> before the
+ *           first and after each iteration
+ * A zero <p, Ap> or <r, r> sets the step to 0 (x then stays put).
+ */
+fhd_status fhd_cg_solve(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+                        float lambda, const fhd_c32* b, fhd_c32* x, int32_t iters,
+                        double* resid, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* The launch plan the library derives from sizes and options. */
 typedef struct fhd_plan_info {

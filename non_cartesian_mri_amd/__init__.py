@@ -5,6 +5,9 @@ Public entry points (thin wrappers over the C ABI in include/fhd.h):
   q_compute(kx, ky, kz, x, y, z, phi, ...)      -> complex64 [N]
   fhd_forward(kx, ky, kz, x, y, z, phi, rho, ...) -> complex64 [M] or [B, M]
   fhd_workspace_bytes(M, N, batch, is_q, ..., op=...), fhd_describe_plan(...)
+  fhd_toeplitz_kernel(kx, ky, kz, phi, (nz, ny, nx), ...) -> complex64 [2nz, 2ny, 2nx]
+  fhd_normal_apply(Qhat, p, lam, ...)           -> F^H F p + lam W^H W p
+  fhd_cg_solve(Qhat, b, iters, lam, ...)        -> conjugate-gradient image
 
 The HIP library is loaded on first use; a missing library raises instead of
 falling back to any CPU path.  ``inputs`` holds the seeded synthetic data
@@ -13,11 +16,12 @@ generators (trajectories, voxel grids, phantom).
 from . import inputs  # noqa: F401
 
 __all__ = ["fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan",
-           "inputs", "library_path"]
+           "fhd_toeplitz_kernel", "fhd_normal_apply", "fhd_cg_solve", "fhd_toeplitz_bytes",
+           "fhd_cg_workspace_bytes", "inputs", "library_path"]
 
 
 def __getattr__(name):
-    if name in ("fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan"):
+    if name in __all__ and name not in ("inputs", "library_path"):
         from . import fhd
         return getattr(fhd, name)
     if name == "library_path":

@@ -2,7 +2,8 @@
 
 torch provides device memory and the stream; every step of the computation
 runs in the HIP kernels behind the C ABI (include/fhd.h).  Names match the C
-entry points: fhd_compute, q_compute, fhd_workspace_bytes.
+entry points: fhd_compute, q_compute, fhd_forward, fhd_workspace_bytes, and the
+reconstruction calls fhd_toeplitz_kernel, fhd_normal_apply, fhd_cg_solve.
 """
 from __future__ import annotations
 
@@ -191,3 +192,104 @@ def fhd_forward(kx, ky, kz, x, y, z, phi, rho, *, trig="accurate", sum="blocked"
                                  out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
     _lib.check(st)
     return out.reshape(M) if squeeze else out.reshape(B, M)
+
+
+def fhd_toeplitz_bytes(nx: int, ny: int, nz: int) -> int:
+    return int(_lib.load().fhd_toeplitz_bytes(int(nx), int(ny), int(nz)))
+
+
+def fhd_cg_workspace_bytes(nx: int, ny: int, nz: int) -> int:
+    return int(_lib.load().fhd_cg_workspace_bytes(int(nx), int(ny), int(nz)))
+
+
+def _grid(shape) -> tuple[int, int, int]:
+    nz, ny, nx = (int(v) for v in shape)
+    return nx, ny, nz
+
+
+def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked",
+                        voxels_per_lane=0, tile=0, sample_splits=0, engine="auto",
+                        out=None, stream=None) -> torch.Tensor:
+    """Qhat for an image grid of `shape` = (nz, ny, nx): complex64 [2nz, 2ny, 2nx].
+
+    The FFT of Q on the grid of coordinate differences, scaled by 1/(8 nx ny nz),
+    so that fhd_normal_apply applies F^H F as a convolution.
+    """
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    M = kx.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == M):
+        raise ValueError("inconsistent sizes")
+    nx, ny, nz = _grid(shape)
+    if out is None:
+        out = torch.empty((2 * nz, 2 * ny, 2 * nx), dtype=torch.complex64, device=kx.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != 8 * nx * ny * nz:
+            raise ValueError("out must hold 8 nx ny nz complex values")
+    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine)
+    st = _lib.load().fhd_toeplitz_kernel(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), phi.data_ptr(),
+                                         M, nx, ny, nz, out.data_ptr(), ctypes.byref(o),
+                                         _stream_ptr(stream))
+    _lib.check(st)
+    return out
+
+
+def _cg_workspace(workspace, nx, ny, nz, device):
+    if workspace is None:
+        nbytes = fhd_cg_workspace_bytes(nx, ny, nz)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fhd_normal_apply(Qhat, p, lam=0.0, *, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """F^H F p + lam W^H W p for an image p of shape (nz, ny, nx) (complex64)."""
+    _dev_c64(Qhat, "Qhat")
+    _dev_c64(p, "p")
+    if p.dim() != 3:
+        raise ValueError("p must be [nz, ny, nx]")
+    nx, ny, nz = _grid(p.shape)
+    if Qhat.numel() != 8 * nx * ny * nz:
+        raise ValueError("Qhat does not match the image grid")
+    if out is None:
+        out = torch.empty_like(p)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != p.numel():
+            raise ValueError("out must match p")
+    workspace, nbytes = _cg_workspace(workspace, nx, ny, nz, p.device)
+    st = _lib.load().fhd_normal_apply(Qhat.data_ptr(), nx, ny, nz, float(lam), p.data_ptr(),
+                                      out.data_ptr(), workspace.data_ptr(), nbytes, _stream_ptr(stream))
+    _lib.check(st)
+    return out
+
+
+def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, resid=False, workspace=None,
+                 stream=None):
+    """`iters` CG iterations on (F^H F + lam W^H W) x = b, b of shape (nz, ny, nx).
+
+    Starts from x0 (default zeros; never modified).  Returns x, or (x, r) with r
+    the float64 device tensor of <r, r> before and after each iteration.
+    """
+    _dev_c64(Qhat, "Qhat")
+    _dev_c64(b, "b")
+    if b.dim() != 3:
+        raise ValueError("b must be [nz, ny, nx]")
+    nx, ny, nz = _grid(b.shape)
+    if Qhat.numel() != 8 * nx * ny * nz:
+        raise ValueError("Qhat does not match the image grid")
+    if x0 is None:
+        x = torch.zeros_like(b)
+    else:
+        _dev_c64(x0, "x0")
+        if x0.shape != b.shape:
+            raise ValueError("x0 must match b")
+        x = x0.clone()
+    r = torch.empty(int(iters) + 1, dtype=torch.float64, device=b.device) if resid else None
+    workspace, nbytes = _cg_workspace(workspace, nx, ny, nz, b.device)
+    st = _lib.load().fhd_cg_solve(Qhat.data_ptr(), nx, ny, nz, float(lam), b.data_ptr(), x.data_ptr(),
+                                  int(iters), r.data_ptr() if r is not None else None,
+                                  workspace.data_ptr(), nbytes, _stream_ptr(stream))
+    _lib.check(st)
+    return (x, r) if resid else x

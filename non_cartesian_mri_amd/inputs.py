@@ -123,6 +123,12 @@ PHANTOM = (
 )
 
 
+def scaled_phantom(f: float, phantom=PHANTOM):
+    """The phantom with centres and semi-axes multiplied by f (for smaller grids)."""
+    return tuple((tuple(f * c for c in centre), tuple(f * a for a in axes), psi, rho)
+                 for centre, axes, psi, rho in phantom)
+
+
 def _rot_z(deg: float) -> np.ndarray:
     a = math.radians(deg)
     c, s = math.cos(a), math.sin(a)

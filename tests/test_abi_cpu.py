@@ -363,3 +363,83 @@ def test_forward_plan(lib):
     info = _lib.FhdPlanInfo()
     assert lib.fhd_describe_plan(10, 10, 1, 3, None, ctypes.byref(info)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert b"operation" in lib.fhd_last_error()
+
+
+# --- reconstruction entry points (Toeplitz kernel, normal operator, CG) ---
+
+def test_reconstruction_sizes(lib):
+    a256 = lambda b: (b + 255) // 256 * 256
+    assert lib.fhd_toeplitz_bytes(4, 5, 6) == 8 * 120 * 8
+    assert lib.fhd_toeplitz_bytes(0, 5, 6) == 0
+    n = 4 * 5 * 6
+    assert lib.fhd_cg_workspace_bytes(4, 5, 6) == 2 * a256(64 * n) + 3 * a256(8 * n) + a256(8 * 1024) + a256(64)
+    assert lib.fhd_cg_workspace_bytes(4, -1, 6) == 0
+
+
+def _toe(lib, M=16, nx=4, ny=4, nz=4, opts=None, **ptrs):
+    p = dict(kx=A, ky=A + 0x1000, kz=A + 0x2000, phi=A + 0x6000, out=A + 0x100000)
+    p.update(ptrs)
+    return lib.fhd_toeplitz_kernel(p["kx"], p["ky"], p["kz"], p["phi"], M, nx, ny, nz, p["out"],
+                                   None if opts is None else ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(nx=0), dict(nz=-3), dict(nx=1024, ny=1024, nz=256),   # 8 n >= 2^31
+    dict(kx=None), dict(phi=None), dict(out=None),
+    dict(out=A + 0x6000 + 8),                                              # Qhat overlaps phi
+    dict(opts=_opts(workspace=A + 0x200000, workspace_bytes=1 << 20)),     # no workspace here
+    dict(opts=_opts(stages=_lib.FHD_STAGE_MU)),
+])
+def test_toeplitz_argument_errors(lib, kw):
+    assert _toe(lib, **kw) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert lib.fhd_last_error() != b""
+
+
+CG_WS = A + 0x10000000
+
+
+def _normal(lib, nx=4, ny=4, nz=4, lam=0.5, ws_bytes=None, **ptrs):
+    p = dict(Q=A, p=A + 0x100000, Ap=A + 0x200000, ws=CG_WS)
+    p.update(ptrs)
+    nb = lib.fhd_cg_workspace_bytes(nx, ny, nz) if ws_bytes is None else ws_bytes
+    return lib.fhd_normal_apply(p["Q"], nx, ny, nz, lam, p["p"], p["Ap"], p["ws"], nb, None)
+
+
+def _cg(lib, nx=4, ny=4, nz=4, lam=0.5, iters=3, ws_bytes=None, **ptrs):
+    p = dict(Q=A, b=A + 0x100000, x=A + 0x200000, r=A + 0x300000, ws=CG_WS)
+    p.update(ptrs)
+    nb = lib.fhd_cg_workspace_bytes(nx, ny, nz) if ws_bytes is None else ws_bytes
+    return lib.fhd_cg_solve(p["Q"], nx, ny, nz, lam, p["b"], p["x"], iters, p["r"], p["ws"], nb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nx=0), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(Q=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(p=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(lam=-1.0), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(lam=float("nan")), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), _lib.FHD_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), _lib.FHD_ERR_WORKSPACE),
+    (dict(ws=CG_WS + 8), _lib.FHD_ERR_INVALID_ARGUMENT),                 # misaligned
+    (dict(Ap=A + 0x100000 + 64), _lib.FHD_ERR_INVALID_ARGUMENT),         # Ap overlaps p
+    (dict(ws=A + 0x200000 - 256), _lib.FHD_ERR_INVALID_ARGUMENT),        # workspace overlaps Ap
+])
+def test_normal_apply_argument_errors(lib, kw, status):
+    assert _normal(lib, **kw) == status
+    assert lib.fhd_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ny=0), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(b=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(x=None), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(iters=-1), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(lam=-0.5), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=8), _lib.FHD_ERR_WORKSPACE),
+    (dict(x=A + 0x100000), _lib.FHD_ERR_INVALID_ARGUMENT),               # x aliases b
+    (dict(r=A + 0x200000 + 8), _lib.FHD_ERR_INVALID_ARGUMENT),           # resid inside x
+    (dict(x=A + 8), _lib.FHD_ERR_INVALID_ARGUMENT),                      # x inside Qhat
+])
+def test_cg_argument_errors(lib, kw, status):
+    assert _cg(lib, **kw) == status
+    assert lib.fhd_last_error() != b""
