@@ -23,6 +23,7 @@ import numpy as np
 
 METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roofline"
 FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 peak (vector, and dense matrix)
+HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # Direct formulation per voxel-sample pair: phase 5 + reduction 1 + complex MAC 8
 # (Q: real MAC 4), plus two transcendentals.
 FLOP_PER_PAIR = {"fhd": 14, "q": 10}
@@ -31,17 +32,26 @@ FLOP_PER_PAIR = {"fhd": 14, "q": 10}
 MFMA_FLOP_PER_PAIR = 8
 # HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
-# Valid only for the kernel source they were taken on (sha256 prefix) and the
+# Valid only for the kernel source (with the headers it includes) they were
+# taken on (sha256 prefix) and the
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9682d3868a393b3f",
-        "fetch_bytes": 1249852.1 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "1e10da7d1f5b160c",
+        "fetch_bytes": 1249867.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9682d3868a393b3f",
-        "fetch_bytes": 1266050.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "1e10da7d1f5b160c",
+        "fetch_bytes": 1266063.9 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
+        "source": "fhd_forward.hip", "kernel_sha256": "cb960d29d5811644",
+        "fetch_bytes": 1005902.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 64): {
+        "source": "fhd_forward.hip", "kernel_sha256": "cb960d29d5811644",
+        "fetch_bytes": 1049517.4 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "df6c84219fd9d20b",
         "fetch_bytes": 981274.6 * 1024 * 2.0, "write_bytes": 262148.3 * 1024 * 1.0,
@@ -69,9 +79,13 @@ def parse():
     ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--op", default="fhd", choices=["fhd", "forward"],
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "cg"],
                     help="fhd: F^H D (or Q for a Q workload); forward: F rho of a seeded image "
-                         "on the same trajectory and voxels")
+                         "on the same trajectory and voxels; cg: conjugate-gradient reconstruction "
+                         "(Toeplitz F^H F through Q) on the workload's voxel grid")
+    ap.add_argument("--cg-iters", type=int, default=10, help="CG iterations per step (--op cg)")
+    ap.add_argument("--cg-lambda", type=float, default=0.0,
+                    help="regulariser weight relative to sum |phi|^2 / 6 (--op cg)")
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -125,11 +139,137 @@ def cpu_baseline(p, target_s: float, rho=None) -> dict:
             "sample": f"{what} x {p.B} vector(s) of the same workload ({pairs:.3e} pairs, {t:.1f} s wall)"}
 
 
+def cpu_baseline_cg(p, target_s: float, lam: float) -> dict:
+    """Time the oracle's CG iteration (Toeplitz product by the plain double sum
+    over voxel pairs) on a small cubic grid with the same trajectory, grown
+    until one iteration takes about target_s / 3."""
+    import oracle
+    from oracle import recon
+    oracle.build(force=False)
+    rng = np.random.Generator(np.random.PCG64(p.seed + 3000))
+    best = None
+    for L in (4, 6, 8, 10, 12, 14, 16):
+        t0 = time.perf_counter()
+        qd = recon.q_differences(p.kx, p.ky, p.kz, p.phi, L, L, L)
+        tq = time.perf_counter() - t0
+        b = rng.standard_normal(L ** 3) + 1j * rng.standard_normal(L ** 3)
+        t0 = time.perf_counter()
+        recon.cg(lambda v: recon.toeplitz_apply(qd, v, L, L, L) + lam * recon.laplacian(v, L, L, L),
+                 b, np.zeros(L ** 3), 2)
+        ti = (time.perf_counter() - t0) / 3.0        # initial residual + 2 iterations: 3 operator calls
+        best = (L, ti, tq)
+        if tq + 3 * ti > target_s / 3:
+            break
+    L, ti, tq = best
+    return {"value": 1.0 / ti, "unit": "iter/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle CG iterations on a {L}^3 grid with all {p.M} samples of the same trajectory "
+                      f"(Q at the {(2 * L - 1) ** 3} coordinate differences in {tq:.1f} s with "
+                      f"{oracle.last.threads} threads, then {ti * 1e3:.1f} ms per iteration, single thread); "
+                      f"the GPU figure is at the full grid"}
+
+
+def bench_cg(args, p, t, D, dev) -> dict:
+    """One step = --cg-iters CG iterations from a zero image on b = F^H D, with Qhat
+    computed once per trajectory beforehand (timed separately)."""
+    import torch
+    from non_cartesian_mri_amd import (fhd_cg_solve, fhd_cg_workspace_bytes, fhd_compute,
+                                       fhd_normal_apply, fhd_toeplitz_kernel)
+    L = p.L
+    if p.N != L ** 3 or p.extra.get("step", 1.0) != 1.0 or p.B != 1:
+        print("--op cg needs a single-vector workload on a unit-step cubic grid", file=sys.stderr)
+        sys.exit(2)
+    stream = torch.cuda.current_stream()
+    opts = dict(trig=args.trig, sum=args.sum, voxels_per_lane=args.voxels_per_lane, tile=args.tile,
+                engine=args.engine)
+    lam = args.cg_lambda * float(np.sum(np.abs(p.phi.astype(np.complex128)) ** 2)) / 6.0
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record(stream)
+    b = fhd_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], D[0], **opts).reshape(L, L, L)
+    e[1].record(stream)
+    Qhat = fhd_toeplitz_kernel(t["kx"], t["ky"], t["kz"], t["phi"], (L, L, L), **opts)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    fhd_ms, toe_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    ws = torch.empty(fhd_cg_workspace_bytes(L, L, L), dtype=torch.uint8, device=dev)
+    x = torch.zeros_like(b)
+    r = torch.empty(args.cg_iters + 1, dtype=torch.float64, device=dev)
+
+    def step():
+        x.zero_()
+        fhd_cg_solve(Qhat, b, args.cg_iters, lam, out=x, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, c in ev:
+        a.record(stream)
+        step()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(c) for a, c in ev])
+    # the normal operator alone (pad, FFT, spectral product, inverse FFT, crop + regulariser)
+    Ap = torch.empty_like(b)
+    nev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(20)]
+    for a, c in nev:
+        a.record(stream)
+        fhd_normal_apply(Qhat, x, lam, out=Ap, workspace=ws)
+        c.record(stream)
+    torch.cuda.synchronize()
+    op_ms = float(np.mean([a.elapsed_time(c) for a, c in nev]))
+    _, rr = fhd_cg_solve(Qhat, b, args.cg_iters, lam, workspace=ws, resid=True)
+    rr = rr.cpu().numpy()
+    n = L ** 3
+    # HBM bytes the FFT route cannot avoid per operator application: read p and
+    # Qhat, write Ap, and one read + write of the 8n-point grid per transform
+    op_bytes = 8 * n + 64 * n + 8 * n + 2 * 2 * 64 * n
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = op_bytes / (op_ms * 1e-3) / 1e9
+    res = {
+        "metric": f"CG iterations/s, (F^H F + lambda W^H W) x = F^H D with Toeplitz F^H F through Q, {L}^3 grid",
+        "value": round(args.cg_iters / (ms_per_step * 1e-3), 3),
+        "unit": "iter/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config] + f"; CG on the {L}^3 grid, {args.cg_iters} "
+                               f"iterations per step from a zero image",
+                   "op": "cg", "name": args.config, "grid": [L, L, L], "samples": p.M,
+                   "iterations_per_step": args.cg_iters, "lambda_rel": args.cg_lambda, "trig": args.trig,
+                   "parallelism": "single GPU"},
+        "timing_ms": {"step_event_median": round(float(np.median(step_ms)), 4),
+                      "normal_operator_event_mean": round(op_ms, 4),
+                      "fhd_setup": round(fhd_ms, 3), "toeplitz_setup": round(toe_ms, 3)},
+        "residual": {"first": float(rr[0]), "last": float(rr[-1])},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "the normal operator (pad, hipFFT forward, spectral product, hipFFT inverse, "
+                               "crop + regulariser) timed as one unit",
+                     "algorithmic_bytes": op_bytes},
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_cg(p, args.cpu_seconds, lam)
+    return res
+
+
 def kernel_source_sha(name: str) -> str:
+    """sha256 prefix of a kernel source together with the library headers it includes."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc")
+    h = hashlib.sha256()
+    with open(os.path.join(csrc, name), "rb") as f:
+        text = f.read()
+    h.update(text)
+    for inc in sorted(set(re.findall(rb'#include "([^"]+)"', text))):
+        path = os.path.join(csrc, inc.decode())
+        if os.path.exists(path):
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(config: str, trig: str, summ: str, engine: str, group: int, gather_ms: float):
@@ -176,6 +316,9 @@ def main():
          for k in ("kx", "ky", "kz", "x", "y", "z", "phi")}
     D = None if p.D is None else torch.from_numpy(np.ascontiguousarray(p.D)).to(dev)
     is_q = p.kind == "q"
+    if args.op == "cg":
+        print(json.dumps(bench_cg(args, p, t, D, dev)), flush=True)
+        return
     forward = args.op == "forward"
     if forward and is_q:
         print("--op forward needs an F^H D workload (the image replaces the data vectors)", file=sys.stderr)

@@ -265,12 +265,14 @@ def fhd_normal_apply(Qhat, p, lam=0.0, *, out=None, workspace=None, stream=None)
     return out
 
 
-def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, resid=False, workspace=None,
+def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, out=None, resid=False, workspace=None,
                  stream=None):
     """`iters` CG iterations on (F^H F + lam W^H W) x = b, b of shape (nz, ny, nx).
 
-    Starts from x0 (default zeros; never modified).  Returns x, or (x, r) with r
-    the float64 device tensor of <r, r> before and after each iteration.
+    Starts from x0 (default zeros; never modified), or, when `out` is given,
+    from the image in `out`, which is then updated in place.  Returns x, or
+    (x, r) with r the float64 device tensor of <r, r> before and after each
+    iteration.
     """
     _dev_c64(Qhat, "Qhat")
     _dev_c64(b, "b")
@@ -279,7 +281,14 @@ def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, resid=False, workspace=Non
     nx, ny, nz = _grid(b.shape)
     if Qhat.numel() != 8 * nx * ny * nz:
         raise ValueError("Qhat does not match the image grid")
-    if x0 is None:
+    if out is not None:
+        if x0 is not None:
+            raise ValueError("give x0 or out, not both")
+        _dev_c64(out, "out")
+        if out.shape != b.shape:
+            raise ValueError("out must match b")
+        x = out
+    elif x0 is None:
         x = torch.zeros_like(b)
     else:
         _dev_c64(x0, "x0")
