@@ -212,41 +212,45 @@ fhd_status fhd_forward(const float* kx, const float* ky, const float* kz,
  * (ix, iy, iz) at coordinates (ix - nx/2, iy - ny/2, iz - nz/2) (any shift of
  * the grid gives the same operator).  F^H F is applied through Q, which is
  * computed once per trajectory (section 17.2): its entry for voxels n, n' is
- * Q at x_n - x_n', so F^H F is a convolution with Q on the grid of coordinate
- * differences and runs as FFTs of twice the grid size per axis.  W is the
- * first difference between face neighbours (a stand-in for the pages'
- * anatomical prior), so W^H W p at a voxel is the sum of p[n] - p[n'] over its
- * up to 6 neighbours.  All arrays are device arrays, complex images are
- * fhd_c32[nz][ny][nx]; 8 nx ny nz must be below 2^31.
+ * Q at x_n - x_n', so F^H F is a convolution with Q over the coordinate
+ * differences, run as a cyclic convolution on a padded grid of
+ * px x py x pz points, p_a = the smallest power of two >= 2 n_a (transforms by
+ * the library's own FFT kernels).  W is the first difference between face
+ * neighbours (a stand-in for the pages' anatomical prior), so W^H W p at a
+ * voxel is the sum of p[n] - p[n'] over its up to 6 neighbours.  All arrays
+ * are device arrays; complex images are fhd_c32[nz][ny][nx].  Grids: 1 to 512
+ * voxels per axis and 8 nx ny nz < 2^31.
  */
 
-/* Bytes of the Toeplitz spectrum Qhat: 8 nx ny nz fhd_c32 (0 if a size < 1). */
+/* Bytes of the Toeplitz spectrum Qhat: px py pz floats (0 for an invalid grid). */
 size_t fhd_toeplitz_bytes(int32_t nx, int32_t ny, int32_t nz);
 
 /*
- * Qhat = FFT(Q on the (2nz, 2ny, 2nx) grid of coordinate differences, index i
- * along an axis of n voxels standing for difference i if i < n, i - 2n else)
- * / (8 nx ny nz).  Q is computed by the q_compute path (opts as for q_compute,
- * without workspace or stages: the call allocates its scratch with
- * hipMallocAsync on `stream`).  Qhat is overwritten; it must not overlap the
- * inputs.  M == 0 gives Qhat = 0.
+ * Qhat = DFT(Q embedded in the padded grid) / (px py pz), real: float[pz][py][px].
+ * Q at difference d sits at d mod p per axis for |d| < n, zero elsewhere; as
+ * Q(-d) = conj(Q(d)) the spectrum is real and only its real part is kept.  Q
+ * is computed by the q_compute path on the (2nz, 2ny, 2nx) grid of
+ * differences (opts as for q_compute, without workspace or stages: the call
+ * allocates its scratch with hipMallocAsync on `stream`).  Qhat is
+ * overwritten; it must not overlap the inputs.  M == 0 gives Qhat = 0.
  */
 fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const float* kz,
                                const fhd_c32* phi, int64_t M,
                                int32_t nx, int32_t ny, int32_t nz,
-                               fhd_c32* Qhat, const fhd_opts* opts, void* stream);
+                               float* Qhat, const fhd_opts* opts, void* stream);
 
-/* Workspace bytes of fhd_normal_apply / fhd_cg_solve (0 if a size < 1):
- * two padded grids, three images and the dot-product partial sums. */
+/* Workspace bytes of fhd_normal_apply / fhd_cg_solve (0 for an invalid grid):
+ * the nz x py x px working grid of the transforms, three images and the
+ * dot-product partial sums. */
 size_t fhd_cg_workspace_bytes(int32_t nx, int32_t ny, int32_t nz);
 
 /*
  * Ap = F^H F p + lambda W^H W p with Qhat from fhd_toeplitz_kernel.
  *   p, Ap     : fhd_c32[nz][ny][nx]; Ap is overwritten and must not overlap p
- *   lambda    : >= 0
+ *   lambda    : finite, >= 0
  *   workspace : >= fhd_cg_workspace_bytes() bytes, 16-byte aligned, caller-owned
  */
-fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+fhd_status fhd_normal_apply(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
                             float lambda, const fhd_c32* p, fhd_c32* Ap,
                             void* workspace, size_t workspace_bytes, void* stream);
 
@@ -263,7 +267,7 @@ fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t
  *           first and after each iteration
  * A zero <p, Ap> or <r, r> sets the step to 0 (x then stays put).
  */
-fhd_status fhd_cg_solve(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
                         float lambda, const fhd_c32* b, fhd_c32* x, int32_t iters,
                         double* resid, void* workspace, size_t workspace_bytes,
                         void* stream);

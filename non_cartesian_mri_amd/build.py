@@ -15,8 +15,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libncmri_fhd.so")
 SOURCES = ["fhd_kernels.hip", "fhd_mfma.hip", "fhd_forward.hip", "fhd_cg.hip", "fhd_api.hip"]
-# hipFFT carries the FFTs of the Toeplitz normal operator
-LINK_LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipfft"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -56,7 +54,7 @@ def build_library(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK_LIBS, "-o", tmp]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

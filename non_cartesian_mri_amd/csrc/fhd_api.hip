@@ -671,36 +671,46 @@ NCMRI_API fhd_status fhd_forward(const float* kx, const float* ky, const float* 
 // Reconstruction: Toeplitz kernel, normal operator, conjugate gradient.
 namespace {
 
+bool grid_ok(int32_t nx, int32_t ny, int32_t nz) {
+  if (nx < 1 || ny < 1 || nz < 1) return false;
+  if (nx > ncmri::kToeplitzMaxLen / 2 || ny > ncmri::kToeplitzMaxLen / 2 || nz > ncmri::kToeplitzMaxLen / 2)
+    return false;
+  const ncmri::ToeplitzDims d = ncmri::toeplitz_dims(nx, ny, nz);
+  return (int64_t)8 * d.voxels() <= 0x7fffffffLL && d.spectrum() <= 0x7fffffffLL;
+}
+
 fhd_status check_grid(int32_t nx, int32_t ny, int32_t nz) {
-  if (nx < 1 || ny < 1 || nz < 1) return fail(FHD_ERR_INVALID_ARGUMENT, "grid sizes must be >= 1 (got %d x %d x %d)", nx, ny, nz);
-  const int64_t n2 = (int64_t)8 * nx * ny * nz;
-  if (n2 > 0x7fffffffLL) return fail(FHD_ERR_INVALID_ARGUMENT, "8 nx ny nz must be < 2^31");
+  if (nx < 1 || ny < 1 || nz < 1)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "grid sizes must be >= 1 (got %d x %d x %d)", nx, ny, nz);
+  if (!grid_ok(nx, ny, nz))
+    return fail(FHD_ERR_INVALID_ARGUMENT, "grid %d x %d x %d too large: at most %d voxels per axis and "
+                "8 nx ny nz < 2^31", nx, ny, nz, ncmri::kToeplitzMaxLen / 2);
   return FHD_OK;
 }
 
-fhd_status check_cg_ws(int64_t n, void* ws, size_t bytes) {
+fhd_status check_cg_ws(const ncmri::ToeplitzDims& d, void* ws, size_t bytes) {
   if (!ws) return fail(FHD_ERR_WORKSPACE, "a workspace of fhd_cg_workspace_bytes() bytes is required");
   if ((uintptr_t)ws % 16 != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  if (bytes < ncmri::cg_workspace_bytes(n))
-    return fail(FHD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, ncmri::cg_workspace_bytes(n));
+  const size_t need = ncmri::cg_workspace_bytes(d);
+  if (bytes < need) return fail(FHD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, need);
   return FHD_OK;
 }
 
 }  // namespace
 
 NCMRI_API size_t fhd_toeplitz_bytes(int32_t nx, int32_t ny, int32_t nz) {
-  if (nx < 1 || ny < 1 || nz < 1) return 0;
-  return (size_t)8 * nx * ny * nz * sizeof(fhd_c32);
+  if (!grid_ok(nx, ny, nz)) return 0;
+  return (size_t)ncmri::toeplitz_dims(nx, ny, nz).spectrum() * sizeof(float);
 }
 
 NCMRI_API size_t fhd_cg_workspace_bytes(int32_t nx, int32_t ny, int32_t nz) {
-  if (nx < 1 || ny < 1 || nz < 1) return 0;
-  return ncmri::cg_workspace_bytes((int64_t)nx * ny * nz);
+  if (!grid_ok(nx, ny, nz)) return 0;
+  return ncmri::cg_workspace_bytes(ncmri::toeplitz_dims(nx, ny, nz));
 }
 
 NCMRI_API fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const float* kz,
                                          const fhd_c32* phi, int64_t M, int32_t nx, int32_t ny,
-                                         int32_t nz, fhd_c32* Qhat, const fhd_opts* opts,
+                                         int32_t nz, float* Qhat, const fhd_opts* opts,
                                          void* stream) {
   try {
     g_err[0] = '\0';
@@ -708,37 +718,39 @@ NCMRI_API fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const
     if (st != FHD_OK) return st;
     if (M < 0 || M > 0x7fffffffLL) return fail(FHD_ERR_INVALID_ARGUMENT, "M must be in [0, 2^31)");
     if (!Qhat) return fail(FHD_ERR_INVALID_ARGUMENT, "Qhat is NULL");
-    if (M > 0 && (!kx || !ky || !kz || !phi)) return fail(FHD_ERR_INVALID_ARGUMENT, "null sample array with M=%lld", (long long)M);
+    if (M > 0 && (!kx || !ky || !kz || !phi))
+      return fail(FHD_ERR_INVALID_ARGUMENT, "null sample array with M=%lld", (long long)M);
     if (opts && (opts->workspace || (opts->stages != 0 && opts->stages != FHD_STAGE_ALL)))
       return fail(FHD_ERR_INVALID_ARGUMENT, "fhd_toeplitz_kernel allocates its own scratch; pass no workspace or stages");
-    const int64_t n2 = (int64_t)8 * nx * ny * nz;
+    const ncmri::ToeplitzDims d = ncmri::toeplitz_dims(nx, ny, nz);
+    const int64_t n2 = 8 * d.voxels();
     const size_t fm = (size_t)M * sizeof(float), cm = (size_t)M * sizeof(fhd_c32);
-    Range outr{Qhat, (size_t)n2 * sizeof(fhd_c32)};
+    Range outr{Qhat, (size_t)d.spectrum() * sizeof(float)};
     Range ins[] = {{kx, fm}, {ky, fm}, {kz, fm}, {phi, cm}};
     for (const Range& r : ins)
       if (overlaps(outr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "Qhat overlaps an input array");
     st = check_device();
     if (st != FHD_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    // Q on the difference grid (circular order), through the library's Q path
-    float* coords = nullptr;
-    hipError_t e = hipMallocAsync((void**)&coords, (size_t)3 * n2 * sizeof(float), s);
+    // scratch: difference-grid coordinates, Q on that grid, the padded grid
+    const size_t coord_bytes = align256((size_t)3 * n2 * sizeof(float));
+    const size_t q_bytes = align256((size_t)n2 * sizeof(fhd_c32));
+    char* scratch = nullptr;
+    hipError_t e = hipMallocAsync((void**)&scratch, coord_bytes + q_bytes + ncmri::toeplitz_scratch_bytes(d), s);
     if (e != hipSuccess) return fail(FHD_ERR_HIP, "hipMallocAsync: %s", hipGetErrorString(e));
+    float* coords = (float*)scratch;
+    fhd_c32* Q2 = (fhd_c32*)(scratch + coord_bytes);
+    float2* G = (float2*)(scratch + coord_bytes + q_bytes);
     fhd_status result = FHD_OK;
     e = ncmri::launch_diff_grid(nx, ny, nz, coords, coords + n2, coords + 2 * n2, s);
     if (e != hipSuccess) result = fail(FHD_ERR_HIP, "difference grid kernel: %s", hipGetErrorString(e));
+    if (result == FHD_OK)   // Q on the difference grid through the library's Q path
+      result = run(1, kx, ky, kz, coords, coords + n2, coords + 2 * n2, phi, nullptr, Q2, M, n2, 1, opts, stream);
     if (result == FHD_OK) {
-      result = run(1, kx, ky, kz, coords, coords + n2, coords + 2 * n2, phi, nullptr, Qhat, M, n2, 1, opts, stream);
+      if (const char* fe = ncmri::toeplitz_spectrum(d, (const float2*)Q2, G, Qhat, s))
+        result = fail(FHD_ERR_HIP, "spectrum of Q: %s", fe);
     }
-    if (result == FHD_OK) {
-      if (const char* fe = ncmri::fft3(nx, ny, nz, (float2*)Qhat, (float2*)Qhat, true, s))
-        result = fail(FHD_ERR_HIP, "FFT of Q: %s", fe);
-    }
-    if (result == FHD_OK) {
-      e = ncmri::launch_scale((float2*)Qhat, n2, (float)(1.0 / (double)n2), s);
-      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "scale kernel: %s", hipGetErrorString(e));
-    }
-    e = hipFreeAsync(coords, s);
+    e = hipFreeAsync(scratch, s);
     if (e != hipSuccess && result == FHD_OK) result = fail(FHD_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e));
     return result;
   } catch (...) {
@@ -746,7 +758,7 @@ NCMRI_API fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const
   }
 }
 
-NCMRI_API fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+NCMRI_API fhd_status fhd_normal_apply(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
                                       float lambda, const fhd_c32* p, fhd_c32* Ap, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   try {
@@ -754,18 +766,19 @@ NCMRI_API fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t n
     fhd_status st = check_grid(nx, ny, nz);
     if (st != FHD_OK) return st;
     if (!Qhat || !p || !Ap) return fail(FHD_ERR_INVALID_ARGUMENT, "null array");
-    if (!(lambda >= 0.0f)) return fail(FHD_ERR_INVALID_ARGUMENT, "lambda must be >= 0");
-    const int64_t n = (int64_t)nx * ny * nz;
-    st = check_cg_ws(n, workspace, workspace_bytes);
+    if (!(lambda >= 0.0f) || !(lambda < INFINITY)) return fail(FHD_ERR_INVALID_ARGUMENT, "lambda must be finite and >= 0");
+    const ncmri::ToeplitzDims d = ncmri::toeplitz_dims(nx, ny, nz);
+    const size_t nb = (size_t)d.voxels() * 8;
+    st = check_cg_ws(d, workspace, workspace_bytes);
     if (st != FHD_OK) return st;
-    Range ar{Ap, (size_t)n * 8}, pr{p, (size_t)n * 8}, qr{Qhat, (size_t)8 * n * 8}, wr{workspace, workspace_bytes};
+    Range ar{Ap, nb}, pr{p, nb}, qr{Qhat, (size_t)d.spectrum() * sizeof(float)}, wr{workspace, workspace_bytes};
     if (overlaps(ar, pr) || overlaps(ar, qr) || overlaps(wr, ar) || overlaps(wr, pr) || overlaps(wr, qr))
       return fail(FHD_ERR_INVALID_ARGUMENT, "overlapping arrays");
     st = check_device();
     if (st != FHD_OK) return st;
-    ncmri::CgWorkspace w = ncmri::cg_workspace(workspace, n);
-    if (const char* e = ncmri::normal_apply((const float2*)Qhat, nx, ny, nz, lambda, (const float2*)p,
-                                            (float2*)Ap, w.P, w.X, nullptr, (hipStream_t)stream))
+    ncmri::CgWorkspace w = ncmri::cg_workspace(workspace, d);
+    if (const char* e = ncmri::normal_apply(d, Qhat, lambda, (const float2*)p, (float2*)Ap, w.T, nullptr,
+                                            (hipStream_t)stream))
       return fail(FHD_ERR_HIP, "normal operator: %s", e);
     return FHD_OK;
   } catch (...) {
@@ -773,7 +786,7 @@ NCMRI_API fhd_status fhd_normal_apply(const fhd_c32* Qhat, int32_t nx, int32_t n
   }
 }
 
-NCMRI_API fhd_status fhd_cg_solve(const fhd_c32* Qhat, int32_t nx, int32_t ny, int32_t nz,
+NCMRI_API fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
                                   float lambda, const fhd_c32* b, fhd_c32* x, int32_t iters,
                                   double* resid, void* workspace, size_t workspace_bytes,
                                   void* stream) {
@@ -782,21 +795,22 @@ NCMRI_API fhd_status fhd_cg_solve(const fhd_c32* Qhat, int32_t nx, int32_t ny, i
     fhd_status st = check_grid(nx, ny, nz);
     if (st != FHD_OK) return st;
     if (!Qhat || !b || !x) return fail(FHD_ERR_INVALID_ARGUMENT, "null array");
-    if (!(lambda >= 0.0f)) return fail(FHD_ERR_INVALID_ARGUMENT, "lambda must be >= 0");
+    if (!(lambda >= 0.0f) || !(lambda < INFINITY)) return fail(FHD_ERR_INVALID_ARGUMENT, "lambda must be finite and >= 0");
     if (iters < 0) return fail(FHD_ERR_INVALID_ARGUMENT, "iters must be >= 0");
-    const int64_t n = (int64_t)nx * ny * nz;
-    st = check_cg_ws(n, workspace, workspace_bytes);
+    const ncmri::ToeplitzDims d = ncmri::toeplitz_dims(nx, ny, nz);
+    const size_t nb = (size_t)d.voxels() * 8;
+    st = check_cg_ws(d, workspace, workspace_bytes);
     if (st != FHD_OK) return st;
-    Range xr{x, (size_t)n * 8}, br{b, (size_t)n * 8}, qr{Qhat, (size_t)8 * n * 8}, wr{workspace, workspace_bytes},
+    Range xr{x, nb}, br{b, nb}, qr{Qhat, (size_t)d.spectrum() * sizeof(float)}, wr{workspace, workspace_bytes},
         rr{resid, resid ? (size_t)(iters + 1) * sizeof(double) : 0};
     if (overlaps(xr, br) || overlaps(xr, qr) || overlaps(wr, xr) || overlaps(wr, br) || overlaps(wr, qr) ||
         overlaps(rr, xr) || overlaps(rr, br) || overlaps(rr, qr) || overlaps(rr, wr))
       return fail(FHD_ERR_INVALID_ARGUMENT, "overlapping arrays");
     st = check_device();
     if (st != FHD_OK) return st;
-    ncmri::CgWorkspace w = ncmri::cg_workspace(workspace, n);
-    if (const char* e = ncmri::cg_run((const float2*)Qhat, nx, ny, nz, lambda, (const float2*)b, (float2*)x,
-                                      iters, resid, w, (hipStream_t)stream))
+    ncmri::CgWorkspace w = ncmri::cg_workspace(workspace, d);
+    if (const char* e = ncmri::cg_run(d, Qhat, lambda, (const float2*)b, (float2*)x, iters, resid, w,
+                                      (hipStream_t)stream))
       return fail(FHD_ERR_HIP, "conjugate gradient: %s", e);
     return FHD_OK;
   } catch (...) {

@@ -1,5 +1,5 @@
 // Internal interface of the reconstruction module (fhd_cg.hip): Toeplitz
-// F^H F through the FFT of Q on the grid of coordinate differences, the
+// F^H F through the FFT of Q on a padded grid of coordinate differences, the
 // regulariser, and conjugate gradient.  Not installed; not part of the ABI.
 #pragma once
 
@@ -9,46 +9,68 @@
 
 namespace ncmri {
 
-// Device buffers of one CG solve / normal-operator application on an
-// nx x ny x nz grid (n = nx ny nz voxels).
+// FFT length along an axis of n voxels: the smallest power of two >= 2n
+// (a cyclic convolution of that length holds every difference in (-n, n)).
+inline int toeplitz_len(int n) {
+  int p = 2;
+  while (p < 2 * n) p *= 2;
+  return p;
+}
+constexpr int kToeplitzMaxLen = 1024;   // longest transform the line FFTs take
+
+struct ToeplitzDims {
+  int nx, ny, nz;   // image grid
+  int px, py, pz;   // transform lengths
+  int64_t voxels() const { return (int64_t)nx * ny * nz; }
+  int64_t spectrum() const { return (int64_t)px * py * pz; }
+  int64_t lines() const { return (int64_t)nz * py * px; }   // the working grid: nz planes of py x px
+};
+inline ToeplitzDims toeplitz_dims(int nx, int ny, int nz) {
+  return ToeplitzDims{nx, ny, nz, toeplitz_len(nx), toeplitz_len(ny), toeplitz_len(nz)};
+}
+
+// Device buffers of one CG solve / normal-operator application.
 struct CgWorkspace {
-  float2* P;        // [8n] padded grid
-  float2* X;        // [8n] its spectrum
+  float2* T;        // [nz][py][px] working grid of the transforms
   float2* r;        // [n] residual
   float2* p;        // [n] search direction
   float2* Ap;       // [n] operator applied to p
-  double* partial;  // [1024] stage-1 sums of the dot products
+  double* partial;  // [kCgPartials] stage-1 sums of the dot products
   double* state;    // [8] <r,r>, <p,Ap>, alpha, beta
 };
 
 constexpr int kCgPartials = 1024;
 
-// Bytes of a CgWorkspace for an nx x ny x nz grid and the layout within it.
 inline size_t cg_align(size_t b) { return (b + 255) / 256 * 256; }
-inline size_t cg_workspace_bytes(int64_t n) {
-  return 2 * cg_align((size_t)(8 * n) * 8) + 3 * cg_align((size_t)n * 8) +
+inline size_t cg_workspace_bytes(const ToeplitzDims& d) {
+  return cg_align((size_t)d.lines() * 8) + 3 * cg_align((size_t)d.voxels() * 8) +
          cg_align(kCgPartials * sizeof(double)) + cg_align(8 * sizeof(double));
 }
-inline CgWorkspace cg_workspace(void* base, int64_t n) {
+inline CgWorkspace cg_workspace(void* base, const ToeplitzDims& d) {
   char* c = (char*)base;
   CgWorkspace w;
-  w.P = (float2*)c;  c += cg_align((size_t)(8 * n) * 8);
-  w.X = (float2*)c;  c += cg_align((size_t)(8 * n) * 8);
-  w.r = (float2*)c;  c += cg_align((size_t)n * 8);
-  w.p = (float2*)c;  c += cg_align((size_t)n * 8);
-  w.Ap = (float2*)c; c += cg_align((size_t)n * 8);
+  w.T = (float2*)c;  c += cg_align((size_t)d.lines() * 8);
+  w.r = (float2*)c;  c += cg_align((size_t)d.voxels() * 8);
+  w.p = (float2*)c;  c += cg_align((size_t)d.voxels() * 8);
+  w.Ap = (float2*)c; c += cg_align((size_t)d.voxels() * 8);
   w.partial = (double*)c; c += cg_align(kCgPartials * sizeof(double));
   w.state = (double*)c;
   return w;
 }
 
+// Scratch of toeplitz_spectrum: the padded complex grid [pz][py][px].
+inline size_t toeplitz_scratch_bytes(const ToeplitzDims& d) { return (size_t)d.spectrum() * 8; }
+
 // Each returns nullptr on success, else a static description of the failure.
-const char* fft3(int nx, int ny, int nz, float2* in, float2* out, bool forward, hipStream_t s);
-const char* normal_apply(const float2* Qhat, int nx, int ny, int nz, float lambda, const float2* p,
-                         float2* Ap, float2* P, float2* X, double* partial, hipStream_t s);
-const char* cg_run(const float2* Qhat, int nx, int ny, int nz, float lambda, const float2* b,
-                   float2* x, int iters, double* resid, const CgWorkspace& w, hipStream_t s);
+// Q2 holds Q on the (2nz, 2ny, 2nx) circular difference grid (index i < n is
+// difference i, i >= n is i - 2n); Qhat (real, [pz][py][px]) receives the
+// spectrum of its embedding in the padded grid, divided by px py pz.
+const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G, float* Qhat,
+                              hipStream_t s);
+const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p,
+                         float2* Ap, float2* T, double* partial, hipStream_t s);
+const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* b, float2* x,
+                   int iters, double* resid, const CgWorkspace& w, hipStream_t s);
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s);
-hipError_t launch_scale(float2* v, int64_t n, float f, hipStream_t s);
 
 }  // namespace ncmri

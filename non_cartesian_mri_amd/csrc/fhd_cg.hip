@@ -5,35 +5,41 @@
 //
 // with F^H F applied through Q (computed once per trajectory).  On a grid with
 // unit steps, (F^H F p)[n] = sum_n' Q(x_n - x_n') p[n'] is a convolution with
-// Q at the coordinate differences d in (-n, n) per axis; embedded circularly
-// in a grid of twice the size it is a cyclic convolution, so
+// Q at the coordinate differences d in (-n, n) per axis.  Embedded in a grid
+// of P >= 2n points per axis (Q at d placed at d mod P, zeros elsewhere) it is
+// a cyclic convolution, so
 //
-//   F^H F p = crop( IFFT( Qhat * FFT( zero-pad(p) ) ) ),
-//   Qhat    = FFT( Q on the 2n grid of differences, circular order ) / (8 nx ny nz).
+//   F^H F p = crop( IDFT( Qhat * DFT( zero-pad(p) ) ) ),
+//   Qhat    = DFT( embedded Q ) / (Px Py Pz).
 //
-// Q comes from the library's own Q path (q_compute on the difference grid:
-// the matrix-core engine, since the circular grid's rows still hold whole
-// voxel groups); the FFTs are hipFFT library calls; the padding, spectral
-// product, crop, regulariser and every CG step are the kernels below.  W is
-// the first-difference stand-in for the pages' anatomical prior: W^H W p is
-// the 6-neighbour graph Laplacian.  CG's scalars (<r,r>, <p,Ap>, alpha, beta)
-// stay in device memory, so an iteration needs no host synchronisation; dot
-// products are accumulated in double with a fixed-order two-stage reduction,
-// so results are deterministic.
+// Q(-d) = conj(Q(d)), so the embedded grid is Hermitian and Qhat is real; the
+// entry at d = -n, never used by the product, is left zero to keep it so.
+//
+// The transforms are the library's own line FFTs (fhd_fft.h), one kernel per
+// axis, and the product skips what the padding makes trivial:
+//   x pass   rows (z < nz, y < ny) of p, zero-extended to Px       -> T
+//   y pass   columns (z < nz, kx) of T, zero-extended to Py         -> T
+//   z pass   columns (ky, kx): nz points zero-extended to Pz, DFT, times Qhat,
+//            inverse DFT, first nz points kept                      -> T
+//   y pass   inverse, first ny points kept                          -> T
+//   x pass   inverse, first nx points kept, plus lambda W^H W p and the
+//            partial sums of <p, Ap>                                -> Ap
+// T holds nz planes of Py x Px points; nothing else is stored between passes.
+// W is the first-difference stand-in for the pages' anatomical prior: W^H W p
+// is the 6-neighbour graph Laplacian.  CG's scalars (<r,r>, <p,Ap>, alpha,
+// beta) stay in device memory, so an iteration needs no host synchronisation;
+// dot products are accumulated in double with a fixed-order two-stage
+// reduction, so results are deterministic.
 #include "fhd.h"
 #include "fhd_cg.h"
-
-#include <hipfft/hipfft.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
+#include "fhd_fft.h"
 
 namespace ncmri {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBlocks = kCgPartials;  // grid of every reduction stage 1 (fixed: deterministic sums)
+static_assert(kThreads == fft::kThreads, "one block size");
 
 // Circular coordinates of the difference grid: index i < n is d = i, i >= n is d = i - 2n.
 __global__ void __launch_bounds__(kThreads)
@@ -49,31 +55,93 @@ diff_grid_kernel(int nx, int ny, int nz, float* x, float* y, float* z) {
   }
 }
 
-__global__ void __launch_bounds__(kThreads) scale_kernel(float2* v, int64_t n, float s) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const float2 a = v[i];
-    v[i] = make_float2(a.x * s, a.y * s);
+// Index in the circular 2n grid of the difference held at padded index a
+// (a < n: d = a; a > P - n: d = a - P), or -1 where the padded grid is zero.
+__device__ __forceinline__ int embed_src(int a, int n, int P) {
+  return a < n ? a : (a > P - n ? a - P + 2 * n : -1);
+}
+
+__global__ void __launch_bounds__(kThreads)
+embed_kernel(const float2* __restrict__ Q2, float2* __restrict__ G, int nx, int ny, int nz, int px, int py,
+             int pz) {
+  const int64_t total = (int64_t)px * py * pz;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int a1 = (int)(i % px);
+    const int a2 = (int)((i / px) % py);
+    const int a3 = (int)(i / ((int64_t)px * py));
+    const int s1 = embed_src(a1, nx, px), s2 = embed_src(a2, ny, py), s3 = embed_src(a3, nz, pz);
+    G[i] = (s1 >= 0 && s2 >= 0 && s3 >= 0) ? Q2[((int64_t)s3 * 2 * ny + s2) * 2 * nx + s1]
+                                            : make_float2(0.0f, 0.0f);
   }
 }
 
-// P (2nz x 2ny x 2nx) = p in the low corner, zeros elsewhere.
 __global__ void __launch_bounds__(kThreads)
-pad_kernel(const float2* __restrict__ p, float2* __restrict__ P, int nx, int ny, int nz) {
-  const int64_t n2 = (int64_t)8 * nx * ny * nz;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n2; i += (int64_t)gridDim.x * kThreads) {
-    const int ix = (int)(i % (2 * nx));
-    const int iy = (int)((i / (2 * nx)) % (2 * ny));
-    const int iz = (int)(i / ((int64_t)4 * nx * ny));
-    P[i] = (ix < nx && iy < ny && iz < nz) ? p[((int64_t)iz * ny + iy) * nx + ix] : make_float2(0.0f, 0.0f);
-  }
+real_scale_kernel(const float2* __restrict__ G, float* __restrict__ Qhat, int64_t n, float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    Qhat[i] = G[i].x * scale;
 }
 
-// X *= Qhat (complex).
-__global__ void __launch_bounds__(kThreads)
-spectral_kernel(float2* __restrict__ X, const float2* __restrict__ Qhat, int64_t n2) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n2; i += (int64_t)gridDim.x * kThreads) {
-    const float2 a = X[i], q = Qhat[i];
-    X[i] = make_float2(a.x * q.x - a.y * q.y, a.x * q.y + a.y * q.x);
+// One axis of transforms over a batch of lines.  Line c sits at outer index
+// o = c / inner and inner index w = c % inner; its point i is at
+// o * os + w * ws + i * es of the array.
+struct LinePass {
+  const float2* in;
+  float2* out;
+  const float* q;  // spectral pass: the real spectrum at q[c + i * q_es]
+  int count;       // lines
+  int inner;
+  int64_t in_os, in_ws, in_es;
+  int64_t out_os, out_ws, out_es;
+  int64_t q_es;
+  int nin;         // points read per line (the rest are zero)
+  int nout;        // points written per line (the first nout)
+};
+
+enum { kFwd = 0, kInv = 1, kFwdQInv = 2 };
+
+template <int N, bool ROW, int MODE>
+__global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
+  using L = fft::Lds<N, ROW>;
+  __shared__ float2 buf[L::kSize];
+  __shared__ float2 tw[N];
+  fft::fill_twiddles<N>(tw);
+  const int c0 = blockIdx.x * L::kLines;
+  float qv[fft::kPerThread];
+#pragma unroll
+  for (int k = 0; k < fft::kPerThread; ++k) {
+    int l, i;
+    L::element(threadIdx.x + k * fft::kThreads, l, i);
+    const int c = c0 + l;
+    float2 v = make_float2(0.0f, 0.0f);
+    if (c < a.count && i < a.nin) {
+      const int o = c / a.inner, w = c - o * a.inner;
+      v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
+    }
+    buf[L::addr(l, i)] = v;
+    if constexpr (MODE == kFwdQInv) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
+  }
+  __syncthreads();
+  fft::transform<N, ROW, MODE == kInv>(buf, tw);
+  if constexpr (MODE == kFwdQInv) {
+#pragma unroll
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      int l, i;
+      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      const float2 v = buf[L::addr(l, i)];
+      buf[L::addr(l, i)] = make_float2(v.x * qv[k], v.y * qv[k]);
+    }
+    __syncthreads();
+    fft::transform<N, ROW, true>(buf, tw);
+  }
+#pragma unroll
+  for (int k = 0; k < fft::kPerThread; ++k) {
+    int l, i;
+    L::element(threadIdx.x + k * fft::kThreads, l, i);
+    const int c = c0 + l;
+    if (c < a.count && i < a.nout) {
+      const int o = c / a.inner, w = c - o * a.inner;
+      a.out[o * a.out_os + w * a.out_ws + i * a.out_es] = buf[L::addr(l, i)];
+    }
   }
 }
 
@@ -90,33 +158,66 @@ __device__ double block_sum(double v, double* sh) {
   return r;
 }
 
-// Ap = crop(P) + lambda (W^H W p); partial[block] = sum Re(conj(p) Ap).
-__global__ void __launch_bounds__(kThreads)
-crop_kernel(const float2* __restrict__ P, const float2* __restrict__ p, float2* __restrict__ Ap,
+// Last pass of the normal operator: inverse transforms of the rows (z < nz,
+// y < ny) of T, the first nx points of each, plus lambda (W^H W p); writes Ap
+// and partial[block] = sum Re(conj(p) Ap) over the block's rows.  Launched on
+// kBlocks blocks that stride over the row groups in a fixed order.
+template <int N>
+__global__ void __launch_bounds__(fft::kThreads)
+crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, float2* __restrict__ Ap,
             int nx, int ny, int nz, float lambda, double* __restrict__ partial) {
+  using L = fft::Lds<N, true>;
+  __shared__ float2 buf[L::kSize];
+  __shared__ float2 tw[N];
   __shared__ double sh[kThreads];
-  const int64_t n = (int64_t)nx * ny * nz;
+  fft::fill_twiddles<N>(tw);
+  const int count = ny * nz;
+  const int groups = (count + L::kLines - 1) / L::kLines;
+  const int64_t plane = (int64_t)nx * ny;
   double acc = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const int ix = (int)(i % nx);
-    const int iy = (int)((i / nx) % ny);
-    const int iz = (int)(i / ((int64_t)nx * ny));
-    float2 v = P[((int64_t)iz * 2 * ny + iy) * 2 * nx + ix];
-    const float2 c = p[i];
-    if (lambda != 0.0f) {
-      float lr = 0.0f, li = 0.0f;
-      // sum over the existing neighbours of p[i] - p[neighbour]
-      if (ix > 0) { const float2 q = p[i - 1]; lr += c.x - q.x; li += c.y - q.y; }
-      if (ix + 1 < nx) { const float2 q = p[i + 1]; lr += c.x - q.x; li += c.y - q.y; }
-      if (iy > 0) { const float2 q = p[i - nx]; lr += c.x - q.x; li += c.y - q.y; }
-      if (iy + 1 < ny) { const float2 q = p[i + nx]; lr += c.x - q.x; li += c.y - q.y; }
-      if (iz > 0) { const float2 q = p[i - (int64_t)nx * ny]; lr += c.x - q.x; li += c.y - q.y; }
-      if (iz + 1 < nz) { const float2 q = p[i + (int64_t)nx * ny]; lr += c.x - q.x; li += c.y - q.y; }
-      v.x = __builtin_fmaf(lambda, lr, v.x);
-      v.y = __builtin_fmaf(lambda, li, v.y);
+  for (int g = blockIdx.x; g < groups; g += gridDim.x) {
+    const int c0 = g * L::kLines;
+#pragma unroll
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      int l, i;
+      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      const int c = c0 + l;
+      float2 v = make_float2(0.0f, 0.0f);
+      if (c < count) {
+        const int z = c / ny, y = c - z * ny;
+        v = T[((int64_t)z * py + y) * N + i];
+      }
+      buf[L::addr(l, i)] = v;
     }
-    Ap[i] = v;
-    acc += (double)c.x * v.x + (double)c.y * v.y;
+    __syncthreads();
+    fft::transform<N, true, true>(buf, tw);
+#pragma unroll
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      int l, i;
+      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      const int c = c0 + l;
+      if (c < count && i < nx) {
+        const int z = c / ny, y = c - z * ny;
+        const int64_t vox = (int64_t)c * nx + i;
+        float2 v = buf[L::addr(l, i)];
+        const float2 cv = p[vox];
+        if (lambda != 0.0f) {
+          float lr = 0.0f, li = 0.0f;
+          // sum over the existing neighbours of p[vox] - p[neighbour]
+          if (i > 0) { const float2 q = p[vox - 1]; lr += cv.x - q.x; li += cv.y - q.y; }
+          if (i + 1 < nx) { const float2 q = p[vox + 1]; lr += cv.x - q.x; li += cv.y - q.y; }
+          if (y > 0) { const float2 q = p[vox - nx]; lr += cv.x - q.x; li += cv.y - q.y; }
+          if (y + 1 < ny) { const float2 q = p[vox + nx]; lr += cv.x - q.x; li += cv.y - q.y; }
+          if (z > 0) { const float2 q = p[vox - plane]; lr += cv.x - q.x; li += cv.y - q.y; }
+          if (z + 1 < nz) { const float2 q = p[vox + plane]; lr += cv.x - q.x; li += cv.y - q.y; }
+          v.x = __builtin_fmaf(lambda, lr, v.x);
+          v.y = __builtin_fmaf(lambda, li, v.y);
+        }
+        Ap[vox] = v;
+        acc += (double)cv.x * v.x + (double)cv.y * v.y;
+      }
+    }
+    __syncthreads();
   }
   const double s = block_sum(acc, sh);
   if (threadIdx.x == 0 && partial) partial[blockIdx.x] = s;
@@ -203,47 +304,76 @@ int blocks_for(int64_t n) {
   return (int)(b < kBlocks ? (b > 0 ? b : 1) : kBlocks);
 }
 
-// hipFFT plans for (2nz, 2ny, 2nx) C2C, one per device, stream and size, kept
-// until the process ends (plan creation is expensive).  A plan's work area is
-// used by every transform run with it, so plans are not shared across streams:
-// work on different streams may overlap, work on one stream is ordered.
-std::mutex g_plan_mu;
-std::map<std::tuple<int, hipStream_t, int, int, int>, hipfftHandle> g_plans;
+template <int N, bool ROW, int MODE>
+hipError_t launch_lines_n(const LinePass& a, hipStream_t s) {
+  constexpr int lines = fft::Lds<N, ROW>::kLines;
+  const int grid = (a.count + lines - 1) / lines;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE>), dim3(grid), dim3(fft::kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
-const char* fft_name(hipfftResult r) {
-  switch (r) {
-    case HIPFFT_SUCCESS: return "HIPFFT_SUCCESS";
-    case HIPFFT_ALLOC_FAILED: return "HIPFFT_ALLOC_FAILED";
-    case HIPFFT_INVALID_VALUE: return "HIPFFT_INVALID_VALUE";
-    case HIPFFT_INVALID_SIZE: return "HIPFFT_INVALID_SIZE";
-    case HIPFFT_EXEC_FAILED: return "HIPFFT_EXEC_FAILED";
-    default: return "hipFFT error";
+template <bool ROW, int MODE>
+hipError_t launch_lines(int N, const LinePass& a, hipStream_t s) {
+  switch (N) {
+    case 2: return launch_lines_n<2, ROW, MODE>(a, s);
+    case 4: return launch_lines_n<4, ROW, MODE>(a, s);
+    case 8: return launch_lines_n<8, ROW, MODE>(a, s);
+    case 16: return launch_lines_n<16, ROW, MODE>(a, s);
+    case 32: return launch_lines_n<32, ROW, MODE>(a, s);
+    case 64: return launch_lines_n<64, ROW, MODE>(a, s);
+    case 128: return launch_lines_n<128, ROW, MODE>(a, s);
+    case 256: return launch_lines_n<256, ROW, MODE>(a, s);
+    case 512: return launch_lines_n<512, ROW, MODE>(a, s);
+    case 1024: return launch_lines_n<1024, ROW, MODE>(a, s);
+    default: return hipErrorInvalidValue;
   }
+}
+
+template <int N>
+hipError_t launch_crop_n(const ToeplitzDims& d, const float2* T, const float2* p, float2* Ap, float lambda,
+                         double* partial, hipStream_t s) {
+  hipLaunchKernelGGL(crop_kernel<N>, dim3(kBlocks), dim3(fft::kThreads), 0, s, T, d.py, p, Ap, d.nx, d.ny, d.nz,
+                     lambda, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_crop(const ToeplitzDims& d, const float2* T, const float2* p, float2* Ap, float lambda,
+                       double* partial, hipStream_t s) {
+  switch (d.px) {
+    case 2: return launch_crop_n<2>(d, T, p, Ap, lambda, partial, s);
+    case 4: return launch_crop_n<4>(d, T, p, Ap, lambda, partial, s);
+    case 8: return launch_crop_n<8>(d, T, p, Ap, lambda, partial, s);
+    case 16: return launch_crop_n<16>(d, T, p, Ap, lambda, partial, s);
+    case 32: return launch_crop_n<32>(d, T, p, Ap, lambda, partial, s);
+    case 64: return launch_crop_n<64>(d, T, p, Ap, lambda, partial, s);
+    case 128: return launch_crop_n<128>(d, T, p, Ap, lambda, partial, s);
+    case 256: return launch_crop_n<256>(d, T, p, Ap, lambda, partial, s);
+    case 512: return launch_crop_n<512>(d, T, p, Ap, lambda, partial, s);
+    case 1024: return launch_crop_n<1024>(d, T, p, Ap, lambda, partial, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// A pass whose input and output share one layout.
+LinePass pass(const float2* in, float2* out, int64_t count, int64_t inner, int64_t os, int64_t ws, int64_t es,
+              int nin, int nout) {
+  LinePass a{};
+  a.in = in;
+  a.out = out;
+  a.q = nullptr;
+  a.count = (int)count;
+  a.inner = (int)inner;
+  a.in_os = a.out_os = os;
+  a.in_ws = a.out_ws = ws;
+  a.in_es = a.out_es = es;
+  a.q_es = 0;
+  a.nin = nin;
+  a.nout = nout;
+  return a;
 }
 
 }  // namespace
-
-// Runs one C2C transform of the (2nz, 2ny, 2nx) grid on `stream`.
-const char* fft3(int nx, int ny, int nz, float2* in, float2* out, bool forward, hipStream_t stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
-  std::lock_guard<std::mutex> lk(g_plan_mu);
-  auto key = std::make_tuple(dev, stream, nx, ny, nz);
-  auto it = g_plans.find(key);
-  hipfftHandle plan;
-  if (it == g_plans.end()) {
-    hipfftResult r = hipfftPlan3d(&plan, 2 * nz, 2 * ny, 2 * nx, HIPFFT_C2C);
-    if (r != HIPFFT_SUCCESS) return fft_name(r);
-    g_plans[key] = plan;
-  } else {
-    plan = it->second;
-  }
-  hipfftResult r = hipfftSetStream(plan, stream);
-  if (r != HIPFFT_SUCCESS) return fft_name(r);
-  r = hipfftExecC2C(plan, reinterpret_cast<hipfftComplex*>(in), reinterpret_cast<hipfftComplex*>(out),
-                    forward ? HIPFFT_FORWARD : HIPFFT_BACKWARD);
-  return r == HIPFFT_SUCCESS ? nullptr : fft_name(r);
-}
 
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s) {
   const int64_t n2 = (int64_t)8 * nx * ny * nz;
@@ -251,36 +381,64 @@ hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z
   return hipGetLastError();
 }
 
-hipError_t launch_scale(float2* v, int64_t n, float f, hipStream_t s) {
-  hipLaunchKernelGGL(scale_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, v, n, f);
-  return hipGetLastError();
-}
-
-// Ap = F^H F p + lambda W^H W p (and the <p, Ap> partials when `partial`).
-const char* normal_apply(const float2* Qhat, int nx, int ny, int nz, float lambda, const float2* p,
-                         float2* Ap, float2* P, float2* X, double* partial, hipStream_t s) {
-  const int64_t n = (int64_t)nx * ny * nz, n2 = 8 * n;
-  hipLaunchKernelGGL(pad_kernel, dim3(blocks_for(n2)), dim3(kThreads), 0, s, p, P, nx, ny, nz);
-  if (hipGetLastError() != hipSuccess) return "pad kernel launch failed";
-  if (const char* e = fft3(nx, ny, nz, P, X, true, s)) return e;
-  hipLaunchKernelGGL(spectral_kernel, dim3(blocks_for(n2)), dim3(kThreads), 0, s, X, Qhat, n2);
-  if (hipGetLastError() != hipSuccess) return "spectral kernel launch failed";
-  if (const char* e = fft3(nx, ny, nz, X, P, false, s)) return e;
-  hipLaunchKernelGGL(crop_kernel, dim3(kBlocks), dim3(kThreads), 0, s, P, p, Ap, nx, ny, nz, lambda, partial);
-  if (hipGetLastError() != hipSuccess) return "crop kernel launch failed";
+const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G, float* Qhat, hipStream_t s) {
+  const int64_t total = d.spectrum();
+  const int64_t plane = (int64_t)d.px * d.py;
+  hipLaunchKernelGGL(embed_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, Q2, G, d.nx, d.ny, d.nz, d.px,
+                     d.py, d.pz);
+  if (hipGetLastError() != hipSuccess) return "embed kernel launch failed";
+  // x: rows (kz, ky); y: columns (kz, kx); z: columns (ky, kx) -- all in place, full length
+  if (launch_lines<true, kFwd>(d.px, pass(G, G, (int64_t)d.pz * d.py, 1, d.px, 0, 1, d.px, d.px), s) != hipSuccess)
+    return "x transform launch failed";
+  if (launch_lines<false, kFwd>(d.py, pass(G, G, (int64_t)d.pz * d.px, d.px, plane, 1, d.px, d.py, d.py), s) !=
+      hipSuccess)
+    return "y transform launch failed";
+  if (launch_lines<false, kFwd>(d.pz, pass(G, G, plane, 1, 1, 0, plane, d.pz, d.pz), s) != hipSuccess)
+    return "z transform launch failed";
+  hipLaunchKernelGGL(real_scale_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, G, Qhat, total,
+                     (float)(1.0 / (double)total));
+  if (hipGetLastError() != hipSuccess) return "spectrum scale kernel launch failed";
   return nullptr;
 }
 
-const char* cg_run(const float2* Qhat, int nx, int ny, int nz, float lambda, const float2* b,
-                   float2* x, int iters, double* resid, const CgWorkspace& w, hipStream_t s) {
-  const int64_t n = (int64_t)nx * ny * nz;
+// Ap = F^H F p + lambda W^H W p (and the <p, Ap> partials when `partial`).
+const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p, float2* Ap,
+                         float2* T, double* partial, hipStream_t s) {
+  const int64_t plane = (int64_t)d.px * d.py;
+  // x: rows (z < nz, y < ny) of p -> rows of T
+  LinePass a = pass(p, T, (int64_t)d.nz * d.ny, d.ny, 0, 0, 1, d.nx, d.px);
+  a.in_os = (int64_t)d.nx * d.ny;
+  a.in_ws = d.nx;
+  a.out_os = plane;
+  a.out_ws = d.px;
+  if (launch_lines<true, kFwd>(d.px, a, s) != hipSuccess) return "x transform launch failed";
+  // y: columns (z < nz, kx), ny points in, py out
+  if (launch_lines<false, kFwd>(d.py, pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.ny, d.py), s) !=
+      hipSuccess)
+    return "y transform launch failed";
+  // z: columns (ky, kx): nz points, spectral product, nz points back
+  LinePass zq = pass(T, T, plane, 1, 1, 0, plane, d.nz, d.nz);
+  zq.q = Qhat;
+  zq.q_es = plane;
+  if (launch_lines<false, kFwdQInv>(d.pz, zq, s) != hipSuccess) return "z transform launch failed";
+  // y inverse: py points in, ny out
+  if (launch_lines<false, kInv>(d.py, pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.py, d.ny), s) !=
+      hipSuccess)
+    return "y inverse transform launch failed";
+  if (launch_crop(d, T, p, Ap, lambda, partial, s) != hipSuccess) return "x inverse transform launch failed";
+  return nullptr;
+}
+
+const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* b, float2* x, int iters,
+                   double* resid, const CgWorkspace& w, hipStream_t s) {
+  const int64_t n = d.voxels();
   // r = b - A x, p = r, <r, r>
-  if (const char* e = normal_apply(Qhat, nx, ny, nz, lambda, x, w.Ap, w.P, w.X, nullptr, s)) return e;
+  if (const char* e = normal_apply(d, Qhat, lambda, x, w.Ap, w.T, nullptr, s)) return e;
   hipLaunchKernelGGL(residual_kernel, dim3(kBlocks), dim3(kThreads), 0, s, b, w.Ap, w.r, w.p, n, w.partial);
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 0, resid);
   if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
   for (int it = 0; it < iters; ++it) {
-    if (const char* e = normal_apply(Qhat, nx, ny, nz, lambda, w.p, w.Ap, w.P, w.X, w.partial, s)) return e;
+    if (const char* e = normal_apply(d, Qhat, lambda, w.p, w.Ap, w.T, w.partial, s)) return e;
     hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 1, nullptr);
     hipLaunchKernelGGL(step_kernel, dim3(kBlocks), dim3(kThreads), 0, s, x, w.r, w.p, w.Ap, n, w.state, w.partial);
     hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 2,

@@ -207,13 +207,25 @@ def _grid(shape) -> tuple[int, int, int]:
     return nx, ny, nz
 
 
+def toeplitz_lengths(shape) -> tuple[int, int, int]:
+    """Transform lengths (pz, py, px) of an image grid (nz, ny, nx): powers of two >= 2n."""
+    out = []
+    for n in shape:
+        p = 2
+        while p < 2 * int(n):
+            p *= 2
+        out.append(p)
+    return tuple(out)
+
+
 def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked",
                         voxels_per_lane=0, tile=0, sample_splits=0, engine="auto",
                         out=None, stream=None) -> torch.Tensor:
-    """Qhat for an image grid of `shape` = (nz, ny, nx): complex64 [2nz, 2ny, 2nx].
+    """Qhat for an image grid of `shape` = (nz, ny, nx): float32 [pz, py, px].
 
-    The FFT of Q on the grid of coordinate differences, scaled by 1/(8 nx ny nz),
-    so that fhd_normal_apply applies F^H F as a convolution.
+    The (real) DFT of Q embedded in the padded grid of coordinate differences,
+    divided by px py pz, so that fhd_normal_apply applies F^H F as a cyclic
+    convolution.
     """
     for n, t in (("kx", kx), ("ky", ky), ("kz", kz)):
         _dev_f32(t, n)
@@ -222,18 +234,30 @@ def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked
     if not (ky.numel() == kz.numel() == phi.numel() == M):
         raise ValueError("inconsistent sizes")
     nx, ny, nz = _grid(shape)
+    plen = toeplitz_lengths((nz, ny, nx))
     if out is None:
-        out = torch.empty((2 * nz, 2 * ny, 2 * nx), dtype=torch.complex64, device=kx.device)
+        out = torch.empty(plen, dtype=torch.float32, device=kx.device)
     else:
-        _dev_c64(out, "out")
-        if out.numel() != 8 * nx * ny * nz:
-            raise ValueError("out must hold 8 nx ny nz complex values")
+        if not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.float32 \
+                or not out.is_contiguous():
+            raise TypeError("out must be a contiguous float32 CUDA tensor")
+        if out.numel() != plen[0] * plen[1] * plen[2]:
+            raise ValueError("out must hold pz * py * px floats")
     o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine)
     st = _lib.load().fhd_toeplitz_kernel(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), phi.data_ptr(),
                                          M, nx, ny, nz, out.data_ptr(), ctypes.byref(o),
                                          _stream_ptr(stream))
     _lib.check(st)
     return out
+
+
+def _check_qhat(Qhat, nx, ny, nz):
+    if not isinstance(Qhat, torch.Tensor) or not Qhat.is_cuda or Qhat.dtype != torch.float32 \
+            or not Qhat.is_contiguous():
+        raise TypeError("Qhat must be the contiguous float32 CUDA tensor of fhd_toeplitz_kernel")
+    pz, py, px = toeplitz_lengths((nz, ny, nx))
+    if Qhat.numel() != pz * py * px:
+        raise ValueError("Qhat does not match the image grid")
 
 
 def _cg_workspace(workspace, nx, ny, nz, device):
@@ -245,13 +269,11 @@ def _cg_workspace(workspace, nx, ny, nz, device):
 
 def fhd_normal_apply(Qhat, p, lam=0.0, *, out=None, workspace=None, stream=None) -> torch.Tensor:
     """F^H F p + lam W^H W p for an image p of shape (nz, ny, nx) (complex64)."""
-    _dev_c64(Qhat, "Qhat")
     _dev_c64(p, "p")
     if p.dim() != 3:
         raise ValueError("p must be [nz, ny, nx]")
     nx, ny, nz = _grid(p.shape)
-    if Qhat.numel() != 8 * nx * ny * nz:
-        raise ValueError("Qhat does not match the image grid")
+    _check_qhat(Qhat, nx, ny, nz)
     if out is None:
         out = torch.empty_like(p)
     else:
@@ -274,13 +296,11 @@ def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, out=None, resid=False, wor
     (x, r) with r the float64 device tensor of <r, r> before and after each
     iteration.
     """
-    _dev_c64(Qhat, "Qhat")
     _dev_c64(b, "b")
     if b.dim() != 3:
         raise ValueError("b must be [nz, ny, nx]")
     nx, ny, nz = _grid(b.shape)
-    if Qhat.numel() != 8 * nx * ny * nz:
-        raise ValueError("Qhat does not match the image grid")
+    _check_qhat(Qhat, nx, ny, nz)
     if out is not None:
         if x0 is not None:
             raise ValueError("give x0 or out, not both")

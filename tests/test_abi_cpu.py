@@ -369,11 +369,17 @@ def test_forward_plan(lib):
 
 def test_reconstruction_sizes(lib):
     a256 = lambda b: (b + 255) // 256 * 256
-    assert lib.fhd_toeplitz_bytes(4, 5, 6) == 8 * 120 * 8
+    # transform lengths: smallest powers of two >= 2n -> 8, 16, 16
+    assert lib.fhd_toeplitz_bytes(4, 5, 6) == 8 * 16 * 16 * 4
     assert lib.fhd_toeplitz_bytes(0, 5, 6) == 0
+    assert lib.fhd_toeplitz_bytes(513, 2, 2) == 0            # at most 512 voxels per axis
+    assert lib.fhd_toeplitz_bytes(512, 512, 512) == 1024 ** 3 * 4
     n = 4 * 5 * 6
-    assert lib.fhd_cg_workspace_bytes(4, 5, 6) == 2 * a256(64 * n) + 3 * a256(8 * n) + a256(8 * 1024) + a256(64)
+    # working grid nz x py x px, three images, 1024 partial sums, CG state
+    assert lib.fhd_cg_workspace_bytes(4, 5, 6) == (a256(6 * 16 * 8 * 8) + 3 * a256(8 * n) + a256(8 * 1024)
+                                                    + a256(64))
     assert lib.fhd_cg_workspace_bytes(4, -1, 6) == 0
+    assert lib.fhd_cg_workspace_bytes(1, 1, 1) == a256(2 * 2 * 8) + 3 * 256 + 8192 + 256
 
 
 def _toe(lib, M=16, nx=4, ny=4, nz=4, opts=None, **ptrs):
@@ -384,7 +390,7 @@ def _toe(lib, M=16, nx=4, ny=4, nz=4, opts=None, **ptrs):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(M=-1), dict(nx=0), dict(nz=-3), dict(nx=1024, ny=1024, nz=256),   # 8 n >= 2^31
+    dict(M=-1), dict(nx=0), dict(nz=-3), dict(nx=513), dict(ny=1024),    # at most 512 per axis
     dict(kx=None), dict(phi=None), dict(out=None),
     dict(out=A + 0x6000 + 8),                                              # Qhat overlaps phi
     dict(opts=_opts(workspace=A + 0x200000, workspace_bytes=1 << 20)),     # no workspace here
@@ -414,6 +420,8 @@ def _cg(lib, nx=4, ny=4, nz=4, lam=0.5, iters=3, ws_bytes=None, **ptrs):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(nx=0), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(nz=600), _lib.FHD_ERR_INVALID_ARGUMENT),
+    (dict(lam=float("inf")), _lib.FHD_ERR_INVALID_ARGUMENT),
     (dict(Q=None), _lib.FHD_ERR_INVALID_ARGUMENT),
     (dict(p=None), _lib.FHD_ERR_INVALID_ARGUMENT),
     (dict(lam=-1.0), _lib.FHD_ERR_INVALID_ARGUMENT),

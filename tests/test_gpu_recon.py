@@ -2,11 +2,11 @@
 fhd_cg_solve, through the C ABI) against the double-precision oracle
 (oracle/recon.py), plus properties that hold at any size.
 
-  - the normal operator F^H F p + lam W^H W p, with F^H F through the FFT of
-    Q on the grid of differences, against the oracle's plain double sum over
-    all voxel pairs (cubic grids take the matrix-core Q path with whole voxel
-    groups per row; a non-cubic grid's rows split groups, so its Q runs on
-    the direct kernel);
+  - the normal operator F^H F p + lam W^H W p, with F^H F a cyclic
+    convolution with Q on a padded grid (the library's own FFT kernels),
+    against the oracle's plain double sum over all voxel pairs (cubic grids
+    take the matrix-core Q path with whole voxel groups per row; a non-cubic
+    grid's rows split groups, so its Q runs on the direct kernel);
   - conjugate-gradient iterates and residual history against the oracle's CG
     driven by the same oracle operator;
   - at 128^3 with 262,144 spiral samples, the Toeplitz product against the
@@ -17,8 +17,8 @@ fhd_cg_solve, through the C ABI) against the double-precision oracle
 
 Tolerances (relative L2 against the oracle):
   Toeplitz product: Q's own bar (1e-5 accurate / 2e-3 hw) plus the float32
-  FFT round trip on the 2n grid, whose relative error grows like
-  eps_f32 * log2(8 nx ny nz) (about 1e-6 at these sizes): 3e-5 / 2e-3.
+  FFT round trip on the padded grid, whose relative error grows like
+  eps_f32 * log2(px py pz) (about 1e-6 at these sizes): 3e-5 / 2e-3.
   CG iterates: the operator's error is carried through k iterations and
   grows at most about linearly with k at these well-conditioned sizes:
   k * 3e-5 / k * 2e-3.
@@ -82,7 +82,9 @@ class _OracleOp:
         return out
 
 
-GRIDS = [(16, 16, 16), (12, 10, 7)]
+# (transform lengths): 32^3 (exactly 2n); 32 x 32 x 16 (padded beyond 2n);
+# 2 x 16 x 32 with a single-voxel axis
+GRIDS = [(16, 16, 16), (12, 10, 7), (9, 5, 1)]
 
 
 @pytest.fixture(scope="module")
