@@ -91,6 +91,9 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m non_cartesian_mri_amd.build` "
             "(or __graft_entry__.build()); there is no CPU fallback")
+    # torch's HIP runtime is loaded first, so the library binds to that same
+    # runtime (by soname) instead of bringing in a second copy from the system
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     lib.fhd_default_opts.argtypes = [ctypes.POINTER(FhdOpts)]

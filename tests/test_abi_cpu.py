@@ -393,10 +393,15 @@ def _toe(lib, M=16, nx=4, ny=4, nz=4, opts=None, **ptrs):
     dict(M=-1), dict(nx=0), dict(nz=-3), dict(nx=513), dict(ny=1024),    # at most 512 per axis
     dict(kx=None), dict(phi=None), dict(out=None),
     dict(out=A + 0x6000 + 8),                                              # Qhat overlaps phi
-    dict(opts=_opts(workspace=A + 0x200000, workspace_bytes=1 << 20)),     # no workspace here
-    dict(opts=_opts(stages=_lib.FHD_STAGE_MU)),
+    dict(opts=dict(workspace=A + 0x200000, workspace_bytes=1 << 20)),      # no workspace here
+    dict(opts=dict(stages=_lib.FHD_STAGE_MU)),
 ])
 def test_toeplitz_argument_errors(lib, kw):
+    # option structs are built here, not at collection: loading the library
+    # must not happen before a test runs
+    kw = dict(kw)
+    if "opts" in kw:
+        kw["opts"] = _opts(**kw["opts"])
     assert _toe(lib, **kw) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert lib.fhd_last_error() != b""
 
