@@ -11,6 +11,9 @@ Function map to the pages (PMPP ch. 17 "Iterative MRI reconstruction"):
   forward()   -- F rho, the forward model whose conjugate transpose fhd() applies
                  (section 17.2; the "inverse process" of section 17.3 step 3)
   psnr_db()   -- PSNR = 20 log10(max(I0) / sqrt(MSE)), section 17.3 step 3 (Fig. 17.18)
+Submodules: recon (Toeplitz F^H F, regulariser, CG; section 17.2) and
+gridding (trilinear gridding onto the k-lattice + lattice inverse DFT, the
+baseline of section 17.1 / Fig. 17.19).
   ls_scale()  -- least-squares intensity scale; the pages leave the scaling of
                  the reconstructed image open, so it is fitted (see the header
                  of psnr_db).
