@@ -68,6 +68,20 @@ def lattice_image(G: np.ndarray) -> np.ndarray:
     return np.einsum("jyx,zj->zyx", t, E[2])
 
 
+def lattice_image_at(G: np.ndarray, idx) -> np.ndarray:
+    """The same sum as lattice_image at the voxels idx only (flat indices, x fastest)."""
+    nz, ny, nx = G.shape
+    idx = np.asarray(idx, np.int64)
+    ix, iy, iz = idx % nx, (idx // nx) % ny, idx // (nx * ny)
+    ex = np.exp(2j * math.pi * np.outer(positions(nx)[ix], lattice(nx)))   # [count, nx]
+    ey = np.exp(2j * math.pi * np.outer(positions(ny)[iy], lattice(ny)))
+    ez = np.exp(2j * math.pi * np.outer(positions(nz)[iz], lattice(nz)))
+    out = np.empty(idx.size, np.complex128)
+    for t in range(idx.size):
+        out[t] = np.einsum("zyx,x,y,z->", G, ex[t], ey[t], ez[t])
+    return out
+
+
 def gridding(kx, ky, kz, phi, D, nx: int, ny: int, nz: int) -> np.ndarray:
     """Gridded image, complex128 [nz * ny * nx] (x fastest)."""
     return lattice_image(grid_samples(kx, ky, kz, phi, D, nx, ny, nz)).ravel()

@@ -7,6 +7,7 @@
                   (sum G = sum Mu); a sample on a lattice point lands there only
   lattice_image   a single lattice value -> the plane wave exp(i 2 pi kappa.x);
                   pure-Python triple-loop brute force on tiny grids
+  lattice_image_at  equals lattice_image at the chosen voxels
   gridding        on a Cartesian trajectory (every sample on a lattice point)
                   it equals F^H D from the pinned oracle exactly (rounding)
 Status: all pinned.
@@ -46,8 +47,8 @@ def test_trilinear_weights_by_hand():
 
 def test_wrap_at_the_lattice_edge():
     n = 8
-    # u = n - 0.25 in x: 0.75 of the weight to cell n-1... no: floor(7.75) = 7, frac 0.75 ->
-    # 0.25 to cell 7 and 0.75 to cell 8 = cell 0 (periodic)
+    # u = 7.75 in x: floor 7, fraction 0.75 -> 0.25 to cell 7 and 0.75 to
+    # cell 8, which is cell 0 (periodic)
     kx = np.array([(7.75 - 4) / 8], np.float32)
     zero = np.array([0.0], np.float32)
     g = G_.grid_samples(kx, zero, zero, np.ones(1, np.complex64), np.ones(1, np.complex64), n, n, n)
@@ -117,3 +118,11 @@ def test_cartesian_trajectory_equals_fhd(oracle_mod):
     ref = oracle_mod.fhd(kx, ky, kz, x, y, z, phi, D[None, :])[0]
     got = G_.gridding(kx, ky, kz, phi, D, nx, ny, nz)
     assert np.max(np.abs(got - ref)) <= 1e-11 * np.max(np.abs(ref))
+
+
+def test_lattice_image_at_matches_the_full_sum():
+    rng = _rng(44)
+    g = rng.standard_normal((4, 8, 2)) + 1j * rng.standard_normal((4, 8, 2))
+    full = G_.lattice_image(g).ravel()
+    idx = np.array([0, 5, 17, 63, 40])
+    assert np.max(np.abs(G_.lattice_image_at(g, idx) - full[idx])) <= 1e-12 * np.max(np.abs(full))
