@@ -79,10 +79,11 @@ def parse():
     ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
     ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "cg"],
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "cg", "gridding"],
                     help="fhd: F^H D (or Q for a Q workload); forward: F rho of a seeded image "
                          "on the same trajectory and voxels; cg: conjugate-gradient reconstruction "
-                         "(Toeplitz F^H F through Q) on the workload's voxel grid")
+                         "(Toeplitz F^H F through Q) on the workload's voxel grid; gridding: the "
+                         "trilinear gridding + inverse FFT baseline image on that grid")
     ap.add_argument("--cg-iters", type=int, default=10, help="CG iterations per step (--op cg)")
     ap.add_argument("--cg-lambda", type=float, default=0.0,
                     help="regulariser weight relative to sum |phi|^2 / 6 (--op cg)")
@@ -267,6 +268,84 @@ def bench_cg(args, p, t, D, dev) -> dict:
     return res
 
 
+def cpu_baseline_gridding(p, target_s: float) -> dict:
+    """Time the gridding oracle as it stands (all samples gridded, the image at
+    a seeded voxel sample), grown until it takes about target_s."""
+    from oracle import gridding as G_
+    from non_cartesian_mri_amd import inputs
+    L = p.L
+    t0 = time.perf_counter()
+    G = G_.grid_samples(p.kx, p.ky, p.kz, p.phi, p.D[0], L, L, L)
+    tg = time.perf_counter() - t0
+    count = 8
+    while True:
+        idx = inputs.subset_indices(L ** 3, count, p.seed)
+        t0 = time.perf_counter()
+        G_.lattice_image_at(G, idx)
+        ti = time.perf_counter() - t0
+        if ti > target_s / 4 or count >= L ** 3:
+            break
+        count *= 4
+    per_image = tg + ti * (L ** 3 / count)
+    return {"value": 1.0 / per_image, "unit": "images/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle gridding of all {p.M} samples ({tg:.2f} s) and the lattice sum at {count} seeded "
+                      f"voxels of {L ** 3} ({ti:.2f} s), scaled to the whole image; single thread"}
+
+
+def bench_gridding(args, p, t, D, dev) -> dict:
+    """One step = one gridding reconstruction (zero, scatter, three inverse FFT passes, sign)."""
+    import torch
+    from non_cartesian_mri_amd import fhd_gridding
+    L = p.L
+    if p.N != L ** 3 or p.extra.get("step", 1.0) != 1.0 or p.B != 1 or (L & (L - 1)) != 0:
+        print("--op gridding needs a single-vector workload on a unit-step cubic power-of-two grid", file=sys.stderr)
+        sys.exit(2)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((L, L, L), dtype=torch.complex64, device=dev)
+
+    def step():
+        fhd_gridding(t["kx"], t["ky"], t["kz"], t["phi"], D[0], (L, L, L), out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, c in ev:
+        a.record(stream)
+        step()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = float(np.median([a.elapsed_time(c) for a, c in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    n = L ** 3
+    # bytes one reconstruction must move: the samples (k 12 B, phi 8 B, D 8 B)
+    # once, the image written by the scatter, then read and written by each of
+    # three FFT passes and the sign pass
+    alg = p.M * 28 + 8 * n + 4 * 16 * n
+    achieved = alg / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": f"gridding/iFFT reconstructions/s, {L}^3 grid",
+        "value": round(1e3 / ms_per_step, 3), "unit": "images/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config] + f"; trilinear gridding onto the {L}^3 k-lattice, "
+                               "inverse FFT", "op": "gridding", "name": args.config, "grid": [L, L, L],
+                   "samples": p.M, "parallelism": "single GPU"},
+        "timing_ms": {"step_event_median": round(step_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "the whole reconstruction timed as one unit (zero, scatter, three FFT passes, sign)",
+                     "algorithmic_bytes": alg},
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_gridding(p, args.cpu_seconds)
+    return res
+
+
 def kernel_source_sha(name: str) -> str:
     """sha256 prefix of a kernel source together with the library headers it includes."""
     import hashlib
@@ -330,6 +409,9 @@ def main():
     is_q = p.kind == "q"
     if args.op == "cg":
         print(json.dumps(bench_cg(args, p, t, D, dev)), flush=True)
+        return
+    if args.op == "gridding":
+        print(json.dumps(bench_gridding(args, p, t, D, dev)), flush=True)
         return
     forward = args.op == "forward"
     if forward and is_q:

@@ -272,6 +272,24 @@ fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
                         double* resid, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Gridding reconstruction, the baseline of section 17.1 (Fig. 17.1B) that the
+ * pages compare with the iterative image (section 17.3 step 3, Fig. 17.19):
+ * each sample's conj(phi[m]) D[m] is spread with trilinear weights onto the 8
+ * nearest points of the image's k-lattice kappa_j = (j - n/2)/n per axis
+ * (periodic: neighbours past the edge wrap), and
+ *   image[iz][iy][ix] = sum_j G[j] exp(+i 2 pi kappa_j . x_i),  x_i = i - n/2,
+ * by the library's FFT kernels.  On a Cartesian trajectory (every sample on a
+ * lattice point) this equals fhd_compute on the grid x_i.
+ *   nx, ny, nz : powers of two in [2, 1024]
+ *   image      : fhd_c32[nz][ny][nx], overwritten; must not overlap the inputs
+ * Deposits are float atomics: the result is not bitwise reproducible (the
+ * rounding depends on the order in which samples land).  No workspace.
+ */
+fhd_status fhd_gridding(const float* kx, const float* ky, const float* kz,
+                        const fhd_c32* phi, const fhd_c32* D, int64_t M,
+                        int32_t nx, int32_t ny, int32_t nz, fhd_c32* image, void* stream);
+
 /* The launch plan the library derives from sizes and options. */
 typedef struct fhd_plan_info {
   int32_t voxels_per_lane;  /* voxel group size of the first pass (VALU: voxels owned by one

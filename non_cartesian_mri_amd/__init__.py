@@ -8,6 +8,7 @@ Public entry points (thin wrappers over the C ABI in include/fhd.h):
   fhd_toeplitz_kernel(kx, ky, kz, phi, (nz, ny, nx), ...) -> complex64 [2nz, 2ny, 2nx]
   fhd_normal_apply(Qhat, p, lam, ...)           -> F^H F p + lam W^H W p
   fhd_cg_solve(Qhat, b, iters, lam, ...)        -> conjugate-gradient image
+  fhd_gridding(kx, ky, kz, phi, D, (nz, ny, nx)) -> gridding/iFFT baseline image
 
 The HIP library is loaded on first use; a missing library raises instead of
 falling back to any CPU path.  ``inputs`` holds the seeded synthetic data
@@ -17,7 +18,7 @@ from . import inputs  # noqa: F401
 
 __all__ = ["fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan",
            "fhd_toeplitz_kernel", "fhd_normal_apply", "fhd_cg_solve", "fhd_toeplitz_bytes",
-           "fhd_cg_workspace_bytes", "inputs", "library_path"]
+           "fhd_cg_workspace_bytes", "fhd_gridding", "inputs", "library_path"]
 
 
 def __getattr__(name):

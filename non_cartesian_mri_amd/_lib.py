@@ -41,7 +41,7 @@ FHD_STAGE_ALL = 7
 # every symbol the header declares
 EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "q_compute",
             "fhd_forward", "fhd_toeplitz_bytes", "fhd_toeplitz_kernel", "fhd_cg_workspace_bytes",
-            "fhd_normal_apply", "fhd_cg_solve", "fhd_describe_plan", "fhd_status_string",
+            "fhd_normal_apply", "fhd_cg_solve", "fhd_gridding", "fhd_describe_plan", "fhd_status_string",
             "fhd_last_error", "fhd_version")
 
 
@@ -116,6 +116,8 @@ def load() -> ctypes.CDLL:
     lib.fhd_normal_apply.restype = ctypes.c_int
     lib.fhd_cg_solve.argtypes = [P, i32, i32, i32, ctypes.c_float, P, P, i32, P, P, sz, P]
     lib.fhd_cg_solve.restype = ctypes.c_int
+    lib.fhd_gridding.argtypes = [P, P, P, P, P, i64, i32, i32, i32, P, P]
+    lib.fhd_gridding.restype = ctypes.c_int
     lib.fhd_describe_plan.argtypes = [i64, i64, i32, i32, ctypes.POINTER(FhdOpts), ctypes.POINTER(FhdPlanInfo)]
     lib.fhd_describe_plan.restype = ctypes.c_int
     lib.fhd_status_string.argtypes = [ctypes.c_int]

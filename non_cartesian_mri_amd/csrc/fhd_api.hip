@@ -818,6 +818,37 @@ NCMRI_API fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int
   }
 }
 
+NCMRI_API fhd_status fhd_gridding(const float* kx, const float* ky, const float* kz, const fhd_c32* phi,
+                                  const fhd_c32* D, int64_t M, int32_t nx, int32_t ny, int32_t nz,
+                                  fhd_c32* image, void* stream) {
+  try {
+    g_err[0] = '\0';
+    auto pow2 = [](int32_t n) { return n >= 2 && n <= ncmri::kToeplitzMaxLen && (n & (n - 1)) == 0; };
+    if (!pow2(nx) || !pow2(ny) || !pow2(nz))
+      return fail(FHD_ERR_INVALID_ARGUMENT, "gridding needs powers of two in [2, %d] per axis (got %d x %d x %d)",
+                  ncmri::kToeplitzMaxLen, nx, ny, nz);
+    const int64_t n = (int64_t)nx * ny * nz;
+    if (n > 0x7fffffffLL) return fail(FHD_ERR_INVALID_ARGUMENT, "nx ny nz must be < 2^31");
+    if (M < 0 || M > 0x7fffffffLL) return fail(FHD_ERR_INVALID_ARGUMENT, "M must be in [0, 2^31)");
+    if (!image) return fail(FHD_ERR_INVALID_ARGUMENT, "image is NULL");
+    if (M > 0 && (!kx || !ky || !kz || !phi || !D))
+      return fail(FHD_ERR_INVALID_ARGUMENT, "null sample array with M=%lld", (long long)M);
+    const size_t fm = (size_t)M * sizeof(float), cm = (size_t)M * sizeof(fhd_c32);
+    Range outr{image, (size_t)n * sizeof(fhd_c32)};
+    Range ins[] = {{kx, fm}, {ky, fm}, {kz, fm}, {phi, cm}, {D, cm}};
+    for (const Range& r : ins)
+      if (overlaps(outr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "image overlaps an input array");
+    fhd_status st = check_device();
+    if (st != FHD_OK) return st;
+    if (const char* e = ncmri::gridding_run(kx, ky, kz, (const float2*)phi, (const float2*)D, M, nx, ny, nz,
+                                            (float2*)image, (hipStream_t)stream))
+      return fail(FHD_ERR_HIP, "gridding: %s", e);
+    return FHD_OK;
+  } catch (...) {
+    return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
 NCMRI_API fhd_status q_compute(const float* kx, const float* ky, const float* kz, const float* x,
                                const float* y, const float* z, const fhd_c32* phi, fhd_c32* Q,
                                int64_t M, int64_t N, const fhd_opts* opts, void* stream) {

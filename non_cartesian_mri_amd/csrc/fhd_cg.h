@@ -73,4 +73,10 @@ const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const
                    int iters, double* resid, const CgWorkspace& w, hipStream_t s);
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s);
 
+// Gridding reconstruction (fhd_grid.hip): image (complex [nz][ny][nx], each
+// axis a power of two in [2, kToeplitzMaxLen]) = the centred lattice inverse
+// DFT of the trilinearly gridded conj(phi) D.
+const char* gridding_run(const float* kx, const float* ky, const float* kz, const float2* phi, const float2* D,
+                         int64_t M, int nx, int ny, int nz, float2* image, hipStream_t s);
+
 }  // namespace ncmri

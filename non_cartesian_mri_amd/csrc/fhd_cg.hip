@@ -33,6 +33,7 @@
 #include "fhd.h"
 #include "fhd_cg.h"
 #include "fhd_fft.h"
+#include "fhd_lines.h"
 
 namespace ncmri {
 namespace {
@@ -79,70 +80,6 @@ __global__ void __launch_bounds__(kThreads)
 real_scale_kernel(const float2* __restrict__ G, float* __restrict__ Qhat, int64_t n, float scale) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
     Qhat[i] = G[i].x * scale;
-}
-
-// One axis of transforms over a batch of lines.  Line c sits at outer index
-// o = c / inner and inner index w = c % inner; its point i is at
-// o * os + w * ws + i * es of the array.
-struct LinePass {
-  const float2* in;
-  float2* out;
-  const float* q;  // spectral pass: the real spectrum at q[c + i * q_es]
-  int count;       // lines
-  int inner;
-  int64_t in_os, in_ws, in_es;
-  int64_t out_os, out_ws, out_es;
-  int64_t q_es;
-  int nin;         // points read per line (the rest are zero)
-  int nout;        // points written per line (the first nout)
-};
-
-enum { kFwd = 0, kInv = 1, kFwdQInv = 2 };
-
-template <int N, bool ROW, int MODE>
-__global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
-  using L = fft::Lds<N, ROW>;
-  __shared__ float2 buf[L::kSize];
-  __shared__ float2 tw[N];
-  fft::fill_twiddles<N>(tw);
-  const int c0 = blockIdx.x * L::kLines;
-  float qv[fft::kPerThread];
-#pragma unroll
-  for (int k = 0; k < fft::kPerThread; ++k) {
-    int l, i;
-    L::element(threadIdx.x + k * fft::kThreads, l, i);
-    const int c = c0 + l;
-    float2 v = make_float2(0.0f, 0.0f);
-    if (c < a.count && i < a.nin) {
-      const int o = c / a.inner, w = c - o * a.inner;
-      v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
-    }
-    buf[L::addr(l, i)] = v;
-    if constexpr (MODE == kFwdQInv) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
-  }
-  __syncthreads();
-  fft::transform<N, ROW, MODE == kInv>(buf, tw);
-  if constexpr (MODE == kFwdQInv) {
-#pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * fft::kThreads, l, i);
-      const float2 v = buf[L::addr(l, i)];
-      buf[L::addr(l, i)] = make_float2(v.x * qv[k], v.y * qv[k]);
-    }
-    __syncthreads();
-    fft::transform<N, ROW, true>(buf, tw);
-  }
-#pragma unroll
-  for (int k = 0; k < fft::kPerThread; ++k) {
-    int l, i;
-    L::element(threadIdx.x + k * fft::kThreads, l, i);
-    const int c = c0 + l;
-    if (c < a.count && i < a.nout) {
-      const int o = c / a.inner, w = c - o * a.inner;
-      a.out[o * a.out_os + w * a.out_ws + i * a.out_es] = buf[L::addr(l, i)];
-    }
-  }
 }
 
 // Block sum of a double in LDS (fixed tree: deterministic).
@@ -304,32 +241,6 @@ int blocks_for(int64_t n) {
   return (int)(b < kBlocks ? (b > 0 ? b : 1) : kBlocks);
 }
 
-template <int N, bool ROW, int MODE>
-hipError_t launch_lines_n(const LinePass& a, hipStream_t s) {
-  constexpr int lines = fft::Lds<N, ROW>::kLines;
-  const int grid = (a.count + lines - 1) / lines;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE>), dim3(grid), dim3(fft::kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-template <bool ROW, int MODE>
-hipError_t launch_lines(int N, const LinePass& a, hipStream_t s) {
-  switch (N) {
-    case 2: return launch_lines_n<2, ROW, MODE>(a, s);
-    case 4: return launch_lines_n<4, ROW, MODE>(a, s);
-    case 8: return launch_lines_n<8, ROW, MODE>(a, s);
-    case 16: return launch_lines_n<16, ROW, MODE>(a, s);
-    case 32: return launch_lines_n<32, ROW, MODE>(a, s);
-    case 64: return launch_lines_n<64, ROW, MODE>(a, s);
-    case 128: return launch_lines_n<128, ROW, MODE>(a, s);
-    case 256: return launch_lines_n<256, ROW, MODE>(a, s);
-    case 512: return launch_lines_n<512, ROW, MODE>(a, s);
-    case 1024: return launch_lines_n<1024, ROW, MODE>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 template <int N>
 hipError_t launch_crop_n(const ToeplitzDims& d, const float2* T, const float2* p, float2* Ap, float lambda,
                          double* partial, hipStream_t s) {
@@ -355,24 +266,6 @@ hipError_t launch_crop(const ToeplitzDims& d, const float2* T, const float2* p, 
   }
 }
 
-// A pass whose input and output share one layout.
-LinePass pass(const float2* in, float2* out, int64_t count, int64_t inner, int64_t os, int64_t ws, int64_t es,
-              int nin, int nout) {
-  LinePass a{};
-  a.in = in;
-  a.out = out;
-  a.q = nullptr;
-  a.count = (int)count;
-  a.inner = (int)inner;
-  a.in_os = a.out_os = os;
-  a.in_ws = a.out_ws = ws;
-  a.in_es = a.out_es = es;
-  a.q_es = 0;
-  a.nin = nin;
-  a.nout = nout;
-  return a;
-}
-
 }  // namespace
 
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s) {
@@ -388,12 +281,12 @@ const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G
                      d.py, d.pz);
   if (hipGetLastError() != hipSuccess) return "embed kernel launch failed";
   // x: rows (kz, ky); y: columns (kz, kx); z: columns (ky, kx) -- all in place, full length
-  if (launch_lines<true, kFwd>(d.px, pass(G, G, (int64_t)d.pz * d.py, 1, d.px, 0, 1, d.px, d.px), s) != hipSuccess)
+  if (launch_lines(true, kLineFwd, d.px, line_pass(G, G, (int64_t)d.pz * d.py, 1, d.px, 0, 1, d.px, d.px), s) != hipSuccess)
     return "x transform launch failed";
-  if (launch_lines<false, kFwd>(d.py, pass(G, G, (int64_t)d.pz * d.px, d.px, plane, 1, d.px, d.py, d.py), s) !=
+  if (launch_lines(false, kLineFwd, d.py, line_pass(G, G, (int64_t)d.pz * d.px, d.px, plane, 1, d.px, d.py, d.py), s) !=
       hipSuccess)
     return "y transform launch failed";
-  if (launch_lines<false, kFwd>(d.pz, pass(G, G, plane, 1, 1, 0, plane, d.pz, d.pz), s) != hipSuccess)
+  if (launch_lines(false, kLineFwd, d.pz, line_pass(G, G, plane, 1, 1, 0, plane, d.pz, d.pz), s) != hipSuccess)
     return "z transform launch failed";
   hipLaunchKernelGGL(real_scale_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, G, Qhat, total,
                      (float)(1.0 / (double)total));
@@ -406,23 +299,23 @@ const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda,
                          float2* T, double* partial, hipStream_t s) {
   const int64_t plane = (int64_t)d.px * d.py;
   // x: rows (z < nz, y < ny) of p -> rows of T
-  LinePass a = pass(p, T, (int64_t)d.nz * d.ny, d.ny, 0, 0, 1, d.nx, d.px);
+  LinePass a = line_pass(p, T, (int64_t)d.nz * d.ny, d.ny, 0, 0, 1, d.nx, d.px);
   a.in_os = (int64_t)d.nx * d.ny;
   a.in_ws = d.nx;
   a.out_os = plane;
   a.out_ws = d.px;
-  if (launch_lines<true, kFwd>(d.px, a, s) != hipSuccess) return "x transform launch failed";
+  if (launch_lines(true, kLineFwd, d.px, a, s) != hipSuccess) return "x transform launch failed";
   // y: columns (z < nz, kx), ny points in, py out
-  if (launch_lines<false, kFwd>(d.py, pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.ny, d.py), s) !=
+  if (launch_lines(false, kLineFwd, d.py, line_pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.ny, d.py), s) !=
       hipSuccess)
     return "y transform launch failed";
   // z: columns (ky, kx): nz points, spectral product, nz points back
-  LinePass zq = pass(T, T, plane, 1, 1, 0, plane, d.nz, d.nz);
+  LinePass zq = line_pass(T, T, plane, 1, 1, 0, plane, d.nz, d.nz);
   zq.q = Qhat;
   zq.q_es = plane;
-  if (launch_lines<false, kFwdQInv>(d.pz, zq, s) != hipSuccess) return "z transform launch failed";
+  if (launch_lines(false, kLineFwdQInv, d.pz, zq, s) != hipSuccess) return "z transform launch failed";
   // y inverse: py points in, ny out
-  if (launch_lines<false, kInv>(d.py, pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.py, d.ny), s) !=
+  if (launch_lines(false, kLineInv, d.py, line_pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.py, d.ny), s) !=
       hipSuccess)
     return "y inverse transform launch failed";
   if (launch_crop(d, T, p, Ap, lambda, partial, s) != hipSuccess) return "x inverse transform launch failed";

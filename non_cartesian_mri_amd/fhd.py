@@ -322,3 +322,26 @@ def fhd_cg_solve(Qhat, b, iters, lam=0.0, *, x0=None, out=None, resid=False, wor
                                   workspace.data_ptr(), nbytes, _stream_ptr(stream))
     _lib.check(st)
     return (x, r) if resid else x
+
+
+def fhd_gridding(kx, ky, kz, phi, D, shape, *, out=None, stream=None) -> torch.Tensor:
+    """Gridding reconstruction on a grid of `shape` = (nz, ny, nx) (powers of two):
+    complex64 [nz, ny, nx] at voxel coordinates i - n/2 per axis."""
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    _dev_c64(D, "D")
+    M = kx.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == D.numel() == M):
+        raise ValueError("inconsistent sizes")
+    nx, ny, nz = _grid(shape)
+    if out is None:
+        out = torch.empty((nz, ny, nx), dtype=torch.complex64, device=kx.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != nx * ny * nz:
+            raise ValueError("out must hold nx ny nz complex values")
+    st = _lib.load().fhd_gridding(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), phi.data_ptr(), D.data_ptr(), M,
+                                  nx, ny, nz, out.data_ptr(), _stream_ptr(stream))
+    _lib.check(st)
+    return out

@@ -456,3 +456,19 @@ def test_normal_apply_argument_errors(lib, kw, status):
 def test_cg_argument_errors(lib, kw, status):
     assert _cg(lib, **kw) == status
     assert lib.fhd_last_error() != b""
+
+
+def _grid(lib, M=16, nx=8, ny=8, nz=8, **ptrs):
+    p = dict(kx=A, ky=A + 0x1000, kz=A + 0x2000, phi=A + 0x6000, D=A + 0x8000, out=A + 0x100000)
+    p.update(ptrs)
+    return lib.fhd_gridding(p["kx"], p["ky"], p["kz"], p["phi"], p["D"], M, nx, ny, nz, p["out"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(nx=6), dict(ny=1), dict(nz=2048), dict(nx=0), dict(M=-1),
+    dict(kx=None), dict(D=None), dict(out=None),
+    dict(out=A + 0x8000 + 64),                       # image overlaps D
+])
+def test_gridding_argument_errors(lib, kw):
+    assert _grid(lib, **kw) == _lib.FHD_ERR_INVALID_ARGUMENT
+    assert lib.fhd_last_error() != b""
