@@ -64,6 +64,7 @@ TRAFFIC = {
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
     "fhd_64cube_65536_radial": "FhD 64^3 voxels x 65,536 radial samples",
+    "fhd_512cube_262144_spirals": "FhD 512^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
     "q_128cube_halfstep_1048576_uniform": "Q on 128^3 voxels (step 0.5) x 1,048,576 uniform samples",
     "fhd16_96cube_500001_radial": "FhD x16 vectors, 96^3 voxels x 500,001 radial samples",
     "fhd_32cube_2048_uniform": "FhD 32^3 voxels x 2048 uniform samples",

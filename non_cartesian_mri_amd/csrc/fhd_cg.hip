@@ -117,7 +117,7 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
 #pragma unroll
     for (int k = 0; k < fft::kPerThread; ++k) {
       int l, i;
-      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      L::element(threadIdx.x + k * L::kThreads, l, i);
       const int c = c0 + l;
       float2 v = make_float2(0.0f, 0.0f);
       if (c < count) {
@@ -131,7 +131,7 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
 #pragma unroll
     for (int k = 0; k < fft::kPerThread; ++k) {
       int l, i;
-      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      L::element(threadIdx.x + k * L::kThreads, l, i);
       const int c = c0 + l;
       if (c < count && i < nx) {
         const int z = c / ny, y = c - z * ny;

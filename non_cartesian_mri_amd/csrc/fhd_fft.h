@@ -1,11 +1,12 @@
 // Batched power-of-two FFTs of lines held in LDS (gfx950), for the Toeplitz
-// normal operator of the reconstruction module.
+// normal operator and the gridding reconstruction.
 //
-// A workgroup of 256 threads transforms kElems / N lines of N points (N = 2^p,
-// 2 <= N <= 1024) held in LDS.  The transform is the self-sorting (Stockham)
-// formulation: stage s with radix R combines R sub-transforms of length Ns
-// (the product of the earlier radices) into transforms of length Ns R; the
-// butterfly j reads its R inputs at j + r N/R, multiplies input r by
+// A workgroup transforms lines of N points (N = 2^p, 2 <= N <= 1024) held in
+// LDS; every thread holds 16 complex values per stage, so the register
+// footprint does not depend on N.  The transform is the self-sorting
+// (Stockham) formulation: stage s with radix R combines R sub-transforms of
+// length Ns (the product of the earlier radices) into transforms of length
+// Ns R; the butterfly j reads its R inputs at j + r N/R, multiplies input r by
 // w_N^(r (j mod Ns) N / (Ns R)), takes an R-point DFT in registers and writes
 // output r to (j div Ns) Ns R + (j mod Ns) + r Ns.  Radices: 2, 4 or 8 first
 // (N's bits mod 4), then 16s, so N = 256 takes two stages through LDS.  The
@@ -13,15 +14,17 @@
 // sixteenth-turn twiddles as constants.  w_N^t = e^(-2 pi i t / N) comes from a
 // per-workgroup table computed with the library's own sincos in turns.
 //
-// Every thread holds 16 complex values per stage (kElems = 16 x 256), so the
-// register footprint does not depend on N.  Two LDS layouts:
+// Two LDS layouts:
 //   row    -- line l, point i at l * pitch + swizzle(i): lines that are
-//             contiguous in memory (x axis); the XOR swizzle within 16-point
-//             chunks and the 16-point pad keep the stage reads and writes
-//             of a half-wave on distinct banks for N = 256.
+//             contiguous in memory (x axis); 4096 values per workgroup (256
+//             threads); the XOR swizzle within 16-point chunks and the
+//             16-point pad keep the stage reads and writes of a half-wave on
+//             distinct banks for N = 256.
 //   column -- point i of line l at i * (lines + 1) + l: lines that are
-//             adjacent columns in memory (y, z axes), loaded 16 or more
-//             columns wide.
+//             adjacent columns in memory (y, z axes), at least 16 columns
+//             (128 bytes) per workgroup so that every row of the tile is one
+//             full cache line: 4096 values (256 threads) up to N = 256, 16 N
+//             values (N threads) beyond.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,15 +34,16 @@
 namespace ncmri {
 namespace fft {
 
-constexpr int kThreads = 256;
-constexpr int kElems = 4096;   // complex values per workgroup
-constexpr int kPerThread = kElems / kThreads;
+constexpr int kThreads = 256;   // threads of a 4096-value workgroup
+constexpr int kPerThread = 16;  // complex values per thread and stage
 constexpr int kMaxLen = 1024;
 
 __host__ __device__ constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
 template <int N, bool ROW>
 struct Lds {
+  static constexpr int kElems = ROW ? 4096 : (16 * N > 4096 ? 16 * N : 4096);  // values per workgroup
+  static constexpr int kThreads = kElems / kPerThread;
   static constexpr int kLines = kElems / N;
   static constexpr int kRowPitch = N >= 32 ? N + 16 : N;
   static constexpr int kColPitch = kLines + 1;
@@ -116,12 +120,12 @@ template <int N, int R, int NS, bool ROW, bool INV>
 __device__ __forceinline__ void stage(float2* buf, const float2* tw) {
   using L = Lds<N, ROW>;
   constexpr int kBf = N / R;                              // butterflies per line
-  constexpr int kPer = L::kLines * kBf / kThreads;        // butterflies per thread (16 / R)
+  constexpr int kPer = L::kLines * kBf / L::kThreads;     // butterflies per thread (16 / R)
   static_assert(kPer * R == kPerThread, "16 values per thread");
   float2 v[kPer][R];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int b = threadIdx.x + k * kThreads;
+    const int b = threadIdx.x + k * L::kThreads;
     const int l = ROW ? b / kBf : b % L::kLines;
     const int j = ROW ? b % kBf : b / L::kLines;
 #pragma unroll
@@ -138,7 +142,7 @@ __device__ __forceinline__ void stage(float2* buf, const float2* tw) {
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int b = threadIdx.x + k * kThreads;
+    const int b = threadIdx.x + k * L::kThreads;
     const int l = ROW ? b / kBf : b % L::kLines;
     const int j = ROW ? b % kBf : b / L::kLines;
     dft<R, INV>(v[k]);
@@ -166,7 +170,7 @@ __device__ __forceinline__ void transform(float2* buf, const float2* tw) {
 // tw[t] = e^(-2 pi i t / N), t < N.
 template <int N>
 __device__ __forceinline__ void fill_twiddles(float2* tw) {
-  for (int t = threadIdx.x; t < N; t += kThreads) {
+  for (int t = threadIdx.x; t < N; t += blockDim.x) {
     float s, c;
     sincos_turns((float)t * (1.0f / (float)N), s, c);
     tw[t] = make_float2(c, -s);

@@ -1,5 +1,5 @@
 // Batched line transforms over one axis of a 3-D array (see fhd_lines.h).
-// A workgroup loads kElems / N lines (zero-extending past nin points), runs
+// A workgroup loads Lds<N, ROW>::kLines lines (zero-extending past nin points), runs
 // the LDS transform of fhd_fft.h (optionally forward, times a real spectrum,
 // inverse) and stores the first nout points of each line.
 #include "fhd_fft.h"
@@ -9,17 +9,18 @@ namespace ncmri {
 namespace {
 
 template <int N, bool ROW, int MODE>
-__global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
+__global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(LinePass a) {
   using L = fft::Lds<N, ROW>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
   fft::fill_twiddles<N>(tw);
   const int c0 = blockIdx.x * L::kLines;
+  constexpr bool kPrefetchQ = L::kThreads <= 512;
   float qv[fft::kPerThread];
 #pragma unroll
   for (int k = 0; k < fft::kPerThread; ++k) {
     int l, i;
-    L::element(threadIdx.x + k * fft::kThreads, l, i);
+    L::element(threadIdx.x + k * L::kThreads, l, i);
     const int c = c0 + l;
     float2 v = make_float2(0.0f, 0.0f);
     if (c < a.count && i < a.nin) {
@@ -27,7 +28,9 @@ __global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
       v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
     }
     buf[L::addr(l, i)] = v;
-    if constexpr (MODE == kLineFwdQInv) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
+    // the spectrum is read before the transform where registers allow (it
+    // then arrives while the transform runs); the 1024-thread tiles read it after
+    if constexpr (MODE == kLineFwdQInv && kPrefetchQ) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
   }
   __syncthreads();
   fft::transform<N, ROW, MODE == kLineInv>(buf, tw);
@@ -35,9 +38,16 @@ __global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
 #pragma unroll
     for (int k = 0; k < fft::kPerThread; ++k) {
       int l, i;
-      L::element(threadIdx.x + k * fft::kThreads, l, i);
+      L::element(threadIdx.x + k * L::kThreads, l, i);
+      float q;
+      if constexpr (kPrefetchQ) {
+        q = qv[k];
+      } else {
+        const int c = c0 + l;
+        q = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
+      }
       const float2 v = buf[L::addr(l, i)];
-      buf[L::addr(l, i)] = make_float2(v.x * qv[k], v.y * qv[k]);
+      buf[L::addr(l, i)] = make_float2(v.x * q, v.y * q);
     }
     __syncthreads();
     fft::transform<N, ROW, true>(buf, tw);
@@ -45,7 +55,7 @@ __global__ void __launch_bounds__(fft::kThreads) line_fft_kernel(LinePass a) {
 #pragma unroll
   for (int k = 0; k < fft::kPerThread; ++k) {
     int l, i;
-    L::element(threadIdx.x + k * fft::kThreads, l, i);
+    L::element(threadIdx.x + k * L::kThreads, l, i);
     const int c = c0 + l;
     if (c < a.count && i < a.nout) {
       const int o = c / a.inner, w = c - o * a.inner;
@@ -59,7 +69,7 @@ hipError_t launch_lines_n(const LinePass& a, hipStream_t s) {
   constexpr int lines = fft::Lds<N, ROW>::kLines;
   const int grid = (a.count + lines - 1) / lines;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE>), dim3(grid), dim3(fft::kThreads), 0, s, a);
+  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE>), dim3(grid), dim3(fft::Lds<N, ROW>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -40,10 +40,10 @@ def _rng(seed: int) -> np.random.Generator:
 
 def voxel_grid(L: int, step: float = 1.0) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Cartesian voxel centres of an L^3 grid, x fastest, c_i = (i - L/2)*step."""
-    c = (np.arange(L, dtype=np.float64) - L // 2) * step
-    z, y, x = np.meshgrid(c, c, c, indexing="ij")
-    return (x.ravel().astype(np.float32), y.ravel().astype(np.float32),
-            z.ravel().astype(np.float32))
+    c = ((np.arange(L, dtype=np.float64) - L // 2) * step).astype(np.float32)
+    shape = (L, L, L)
+    return (np.broadcast_to(c[None, None, :], shape).ravel(), np.broadcast_to(c[None, :, None], shape).ravel(),
+            np.broadcast_to(c[:, None, None], shape).ravel())
 
 
 def uniform_k(M: int, rng: np.random.Generator) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -231,6 +231,7 @@ CONFIGS = {
     "fhd_32cube_2048_uniform": "FhD 32^3 voxels, M=2048 uniform-random k, complex N(0,1) phi and D",
     "fhd_64cube_65536_radial": "FhD 64^3 voxels, M=65,536 on 256 Fibonacci spokes x 256 points",
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels, M=262,144 on 64 kz planes x 4096-point spirals",
+    "fhd_512cube_262144_spirals": "FhD 512^3 voxels (N beyond 128^3), the same 262,144-sample spiral stack",
     "q_128cube_halfstep_1048576_uniform": "Q on a 2x-oversampled 128^3 grid (step 0.5), M=1,048,576 uniform-random k",
     "q_128cube_unitstep_1048576_uniform": "Q on a 128^3 grid with step 1 (coords -64..63), M=1,048,576 uniform-random k",
     "fhd16_96cube_500001_radial": "FhD x16 D vectors, 96^3 voxels, M=500,001 radial (odd tail)",
@@ -263,6 +264,14 @@ def make_config(name: str) -> Problem:
         phi = complex_normal(rng, M)
         D = complex_normal(rng, M)[None, :]
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 103, 128)
+    if name == "fhd_512cube_262144_spirals":
+        rng = _rng(106)
+        kx, ky, kz = stack_of_spirals_k(64, 4096, 64)
+        x, y, z = voxel_grid(512)
+        M = kx.shape[0]
+        phi = complex_normal(rng, M)
+        D = complex_normal(rng, M)[None, :]
+        return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 106, 512)
     if name in ("q_128cube_halfstep_1048576_uniform", "q_128cube_unitstep_1048576_uniform"):
         rng = _rng(104)
         kx, ky, kz = uniform_k(1 << 20, rng)

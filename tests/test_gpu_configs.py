@@ -18,7 +18,7 @@ from tests.gpu_util import TOL, assert_close, dev_problem, gpu_fhd, gpu_q, requi
 pytestmark = pytest.mark.gpu
 
 TRIGS = ["accurate", "hw"]
-SUBSET = {"fhd_64cube_65536_radial": 16384, "fhd_128cube_262144_spirals": 4096, "q_128cube_halfstep_1048576_uniform": 4096, "q_128cube_unitstep_1048576_uniform": 2048, "fhd16_96cube_500001_radial": 2048}
+SUBSET = {"fhd_512cube_262144_spirals": 1024, "fhd_64cube_65536_radial": 16384, "fhd_128cube_262144_spirals": 4096, "q_128cube_halfstep_1048576_uniform": 4096, "q_128cube_unitstep_1048576_uniform": 2048, "fhd16_96cube_500001_radial": 2048}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,7 +47,8 @@ ENGINES = ["auto", "valu"]   # auto = the matrix-core engine for these options
 
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("trig", TRIGS)
-@pytest.mark.parametrize("name", ["fhd_32cube_2048_uniform", "fhd_64cube_65536_radial", "fhd_128cube_262144_spirals", "fhd16_96cube_500001_radial"])
+@pytest.mark.parametrize("name", ["fhd_32cube_2048_uniform", "fhd_64cube_65536_radial", "fhd_128cube_262144_spirals",
+                                  "fhd16_96cube_500001_radial", "fhd_512cube_262144_spirals"])
 def test_fhd_config(oracle_mod, name, trig, engine):
     p, idx, ref, d = _problem_and_ref(name, oracle_mod)
     print(f"[gpu] {name} trig={trig} engine={engine} N={p.N} M={p.M} B={p.B}", flush=True)

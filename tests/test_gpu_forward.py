@@ -215,3 +215,15 @@ def test_forward_full_size_sampled(oracle_mod, trig):
     print(f"[oracle] forward 128^3 x 256 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
     got = gpu_forward(p, rho, trig=trig)
     assert_close(got[:, idx], ref, TOL[trig], f"forward 128^3 {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_forward_512cubed_sampled(oracle_mod, trig):
+    """512^3 voxels (134M) x 262,144 spiral samples: 16 seeded samples against the oracle."""
+    p = inputs.make_config("fhd_512cube_262144_spirals")
+    rho = _images(424, 1, p.N)
+    idx = inputs.subset_indices(p.M, 16, p.seed)
+    ref = oracle_mod.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho, idx=idx)
+    print(f"[oracle] forward 512^3 x 16 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
+    got = gpu_forward(p, rho, trig=trig)
+    assert_close(got[:, idx], ref, TOL[trig], f"forward 512^3 {trig}")

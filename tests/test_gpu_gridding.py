@@ -134,3 +134,17 @@ def test_iterative_beats_gridding_on_the_phantom():
     p_cg = oracle.psnr_db(ideal, img.cpu().numpy().ravel())
     print(f"[recon] phantom 32^3: gridding PSNR {p_grid:.2f} dB, CG(12) PSNR {p_cg:.2f} dB", flush=True)
     assert p_cg >= p_grid + 1.0
+
+
+def test_gridding_512cubed_sampled():
+    """512^3 grid, 262,144 spiral samples: 8 seeded voxels against the oracle."""
+    from oracle import gridding as G_
+    p = inputs.make_config("fhd_512cube_262144_spirals")
+    D = p.D[0]
+    got = _gpu_grid(p.kx, p.ky, p.kz, p.phi, D, (512, 512, 512)).ravel()
+    idx = inputs.subset_indices(512 ** 3, 8, 807)
+    G = G_.grid_samples(p.kx, p.ky, p.kz, p.phi, D, 512, 512, 512)
+    ref = G_.lattice_image_at(G, idx)
+    rel = _rel(got[idx], ref)
+    print(f"[parity] gridding 512^3 x 262144, 8 voxels: rel_l2={rel:.3e}", flush=True)
+    assert rel <= TOL
