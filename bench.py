@@ -95,6 +95,11 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
                          "five times (reference reading for the HBM byte counters) and exit")
+    ap.add_argument("--tune", action="store_true",
+                    help="instead of the benchmark, sweep group size x sample rows x tile for --config, "
+                         "time the Pareto front of the static model and print one JSON line")
+    ap.add_argument("--exhaustive", action="store_true", help="with --tune: time every candidate")
+    ap.add_argument("--tune-engines", default="mfma", help="with --tune: comma-separated engines (mfma,valu)")
     ap.add_argument("--issue-rates", action="store_true",
                     help="run the gfx950 issue-rate microbenchmark (FMA, v_sin, mixed issue, trig error) and exit")
     return ap.parse_args()
@@ -408,6 +413,14 @@ def main():
          for k in ("kx", "ky", "kz", "x", "y", "z", "phi")}
     D = None if p.D is None else torch.from_numpy(np.ascontiguousarray(p.D)).to(dev)
     is_q = p.kind == "q"
+    if args.tune:
+        from non_cartesian_mri_amd import tune
+        t0 = time.perf_counter()
+        res = tune.sweep(t, D, trig=args.trig, sum=args.sum, engines=tuple(args.tune_engines.split(",")),
+                         exhaustive=args.exhaustive, grid_edge=p.L if p.N == p.L ** 3 else None)
+        res.update(config=args.config, trig=args.trig, engines=args.tune_engines, seconds=time.perf_counter() - t0)
+        print(json.dumps(res), flush=True)
+        return
     if args.op == "cg":
         print(json.dumps(bench_cg(args, p, t, D, dev)), flush=True)
         return
