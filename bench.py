@@ -53,12 +53,12 @@ TRAFFIC = {
         "fetch_bytes": 1049517.4 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "df6c84219fd9d20b",
-        "fetch_bytes": 981274.6 * 1024 * 2.0, "write_bytes": 262148.3 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
+        "fetch_bytes": 984501.3 * 1024 * 2.0, "write_bytes": 262145.5 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "df6c84219fd9d20b",
-        "fetch_bytes": 1047039.9 * 1024 * 2.0, "write_bytes": 262147.8 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
+        "fetch_bytes": 1047793.4 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
 }
 WORKLOADS = {
