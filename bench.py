@@ -37,12 +37,12 @@ MFMA_FLOP_PER_PAIR = 8
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "1e10da7d1f5b160c",
-        "fetch_bytes": 1249867.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "042fb11bb0a12168",
+        "fetch_bytes": 1249578.1 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "1e10da7d1f5b160c",
-        "fetch_bytes": 1266063.9 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "042fb11bb0a12168",
+        "fetch_bytes": 1266158.3 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
         "source": "fhd_forward.hip", "kernel_sha256": "cb960d29d5811644",

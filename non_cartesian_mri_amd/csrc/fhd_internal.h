@@ -85,10 +85,11 @@ inline constexpr int mfma_record_dwords(int trig, int T) { return mfma_header_fl
 // Records of one sample m for the MFMA engine (all float32):
 //   header hdr[m][]  HW trig:       kx, ky, kz, 0
 //                    accurate trig: khx, khy, khz, 0, klx, kly, klz, 0
-//   factors wb[m][t][64], tile t < T: complex column cc = 16 t + c (c < 16) holds
+//   factors wb[m][64][T], tile t < T: complex column cc = 16 t + c (c < 16) holds
 //     f = Mu_b exp(i 2 pi k.d_j) with b = cc / V, j = cc % V (V = 16 T / BC),
-//     stored as the two rows of the MFMA B operand: [2c] = fr, [2c+1] = fi,
-//     [32+2c] = -fi, [33+2c] = fr.
+//     stored as the two rows of the MFMA B operand of tile t, entry p at
+//     [p][t]: p = 2c -> fr, 2c+1 -> fi, 32+2c -> -fi, 33+2c -> fr (entry p
+//     is supplied by lane p, so a lane's T entries are contiguous).
 struct MfmaRecordArgs {
   const float* kx; const float* ky; const float* kz;
   const float* x; const float* y; const float* z;  // x[0..min(V,N)-1] etc. are read
@@ -96,7 +97,7 @@ struct MfmaRecordArgs {
   const float2* D;       // first vector of this pass ([BC][M]); unused for Q
   int64_t M, N, mpad;    // mpad: multiple of kMfmaChunk
   float* hdr;            // [mpad][mfma_header_floats]
-  float* wb;             // [mpad][T][64]
+  float* wb;             // [mpad][64][T]
 };
 
 struct MfmaArgs {
