@@ -45,12 +45,12 @@ TRAFFIC = {
         "fetch_bytes": 1266158.3 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "cb960d29d5811644",
-        "fetch_bytes": 1005902.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "9f0c83307b628d98",
+        "fetch_bytes": 1005913.5 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "cb960d29d5811644",
-        "fetch_bytes": 1049517.4 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "9f0c83307b628d98",
+        "fetch_bytes": 977914.5 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",

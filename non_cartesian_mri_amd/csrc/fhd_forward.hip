@@ -183,7 +183,9 @@ struct FwdGather {
     __syncthreads();
   }
 
-  // One chunk of 32 groups, pipelined by one group like the adjoint's loop.
+  // One chunk of 32 groups, pipelined by one group like the adjoint's loop
+  // (and, on the accurate path, with the next group's A entry computed right
+  // after this group's MFMAs, as the adjoint does).
   __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb,
                                                int lane, const SampleK<TRIG>& k, float q,
                                                f32x16 (&acc)[T]) {
@@ -192,6 +194,8 @@ struct FwdGather {
     for (int i = 0; i < 3; ++i) hc[i] = hb[i];
 #pragma unroll
     for (int t = 0; t < T; ++t) bc[t] = wb[t * 64 + lane];
+    float e = 0.0f;
+    if constexpr (TRIG != kTrigHw) e = k.sin_phase(hc[0], hc[1], hc[2], q);
 #pragma unroll
     for (int s = 0; s < C; ++s) {
       float hn[3], bn[T];
@@ -202,16 +206,18 @@ struct FwdGather {
         for (int t = 0; t < T; ++t) bn[t] = wb[((s + 1) * T + t) * 64 + lane];
       }
       sched_fence();
-      const float e = k.sin_phase(hc[0], hc[1], hc[2], q);
+      if constexpr (TRIG == kTrigHw) e = k.sin_phase(hc[0], hc[1], hc[2], q);
 #pragma unroll
       for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(e, bc[t], acc[t], 0, 0, 0);
       sched_fence();
       if (s + 1 < C) {
+        if constexpr (TRIG != kTrigHw) e = k.sin_phase(hn[0], hn[1], hn[2], q);
 #pragma unroll
         for (int i = 0; i < 3; ++i) hc[i] = hn[i];
 #pragma unroll
         for (int t = 0; t < T; ++t) bc[t] = bn[t];
       }
+      sched_fence();
     }
   }
 
