@@ -114,27 +114,53 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
   double acc = 0.0;
   for (int g = blockIdx.x; g < groups; g += gridDim.x) {
     const int c0 = g * L::kLines;
+    if constexpr (L::kThreadLine) {
+      // one line per thread (see fhd_fft.h): its row of T located once
+      int l0, i0;
+      L::element(threadIdx.x, l0, i0);
+      const int c = c0 + l0;
+      const int z = c / ny, y = c - z * ny;
+      const float2* tp = T + ((int64_t)z * py + y) * N + i0;
 #pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * L::kThreads, l, i);
-      const int c = c0 + l;
-      float2 v = make_float2(0.0f, 0.0f);
-      if (c < count) {
-        const int z = c / ny, y = c - z * ny;
-        v = T[((int64_t)z * py + y) * N + i];
+      for (int k = 0; k < fft::kPerThread; ++k)
+        buf[L::addr(l0, i0 + k * L::kPointStep)] = c < count ? tp[k * L::kPointStep] : make_float2(0.0f, 0.0f);
+    } else {
+#pragma unroll
+      for (int k = 0; k < fft::kPerThread; ++k) {
+        int l, i;
+        L::element(threadIdx.x + k * L::kThreads, l, i);
+        const int c = c0 + l;
+        float2 v = make_float2(0.0f, 0.0f);
+        if (c < count) {
+          const int z = c / ny, y = c - z * ny;
+          v = T[((int64_t)z * py + y) * N + i];
+        }
+        buf[L::addr(l, i)] = v;
       }
-      buf[L::addr(l, i)] = v;
     }
     __syncthreads();
     fft::transform<N, true, true>(buf, tw);
+    int zl = 0, yl = 0;
+    if constexpr (L::kThreadLine) {
+      int l0, i0;
+      L::element(threadIdx.x, l0, i0);
+      zl = (c0 + l0) / ny;
+      yl = c0 + l0 - zl * ny;
+    }
 #pragma unroll
     for (int k = 0; k < fft::kPerThread; ++k) {
       int l, i;
       L::element(threadIdx.x + k * L::kThreads, l, i);
       const int c = c0 + l;
       if (c < count && i < nx) {
-        const int z = c / ny, y = c - z * ny;
+        int z, y;
+        if constexpr (L::kThreadLine) {
+          z = zl;
+          y = yl;
+        } else {
+          z = c / ny;
+          y = c - z * ny;
+        }
         const int64_t vox = (int64_t)c * nx + i;
         float2 v = buf[L::addr(l, i)];
         const float2 cv = p[vox];

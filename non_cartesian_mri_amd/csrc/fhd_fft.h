@@ -55,10 +55,21 @@ struct Lds {
       return i * kColPitch + l;
     }
   }
+  // Threads of a row tile of N >= 256 points each keep one line (N / 16
+  // threads per line, 16 points each); a column tile's threads keep one line
+  // when the thread count is a multiple of the line count.
+  static constexpr bool kThreadLine = ROW ? N >= 256 : kThreads % kLines == 0;
+  static constexpr int kPointStep = ROW ? N / 16 : kThreads / kLines;  // for kThreadLine
   // element e of the workgroup's kElems in load/store order: consecutive
-  // threads take consecutive points of a line (row) or consecutive lines (column)
+  // threads take consecutive points of a line (row) or consecutive lines
+  // (column); element t + k kThreads of thread t is point i0 + k kPointStep
+  // of the thread's line when kThreadLine
   __device__ static __forceinline__ void element(int e, int& l, int& i) {
-    if constexpr (ROW) {
+    if constexpr (ROW && N >= 256) {
+      const int t = e % kThreads, k = e / kThreads;
+      l = t / (N / 16);
+      i = t % (N / 16) + k * (N / 16);
+    } else if constexpr (ROW) {
       l = e / N;
       i = e % N;
     } else {

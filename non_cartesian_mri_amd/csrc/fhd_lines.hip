@@ -15,22 +15,46 @@ __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(
   __shared__ float2 tw[N];
   fft::fill_twiddles<N>(tw);
   const int c0 = blockIdx.x * L::kLines;
-  constexpr bool kPrefetchQ = L::kThreads <= 512;
   float qv[fft::kPerThread];
+  // the spectrum is read before the transform where registers allow (it
+  // then arrives while the transform runs); the 1024-thread tiles read it after
+  constexpr bool kPrefetchQ = L::kThreads <= 512;
+  if constexpr (L::kThreadLine) {
+    // one line per thread: its address and bounds once, then a running pointer
+    int l0, i0;
+    L::element(threadIdx.x, l0, i0);
+    constexpr int di = L::kPointStep;
+    const int c = c0 + l0;
+    const bool ok = c < a.count;
+    const int o = c / a.inner, w = c - o * a.inner;
+    const float2* p = a.in + (o * a.in_os + w * a.in_ws + i0 * a.in_es);
+    const int64_t st = (int64_t)di * a.in_es;
+    const float* qp = a.q + (c + (int64_t)i0 * a.q_es);
+    const int64_t qst = (int64_t)di * a.q_es;
 #pragma unroll
-  for (int k = 0; k < fft::kPerThread; ++k) {
-    int l, i;
-    L::element(threadIdx.x + k * L::kThreads, l, i);
-    const int c = c0 + l;
-    float2 v = make_float2(0.0f, 0.0f);
-    if (c < a.count && i < a.nin) {
-      const int o = c / a.inner, w = c - o * a.inner;
-      v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      const int i = i0 + k * di;
+      buf[L::addr(l0, i)] = (ok && i < a.nin) ? *p : make_float2(0.0f, 0.0f);
+      p += st;
+      if constexpr (MODE == kLineFwdQInv && kPrefetchQ) {
+        qv[k] = ok ? *qp : 0.0f;
+        qp += qst;
+      }
     }
-    buf[L::addr(l, i)] = v;
-    // the spectrum is read before the transform where registers allow (it
-    // then arrives while the transform runs); the 1024-thread tiles read it after
-    if constexpr (MODE == kLineFwdQInv && kPrefetchQ) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
+  } else {
+#pragma unroll
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      int l, i;
+      L::element(threadIdx.x + k * L::kThreads, l, i);
+      const int c = c0 + l;
+      float2 v = make_float2(0.0f, 0.0f);
+      if (c < a.count && i < a.nin) {
+        const int o = c / a.inner, w = c - o * a.inner;
+        v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
+      }
+      buf[L::addr(l, i)] = v;
+      if constexpr (MODE == kLineFwdQInv && kPrefetchQ) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
+    }
   }
   __syncthreads();
   fft::transform<N, ROW, MODE == kLineInv>(buf, tw);
@@ -52,14 +76,32 @@ __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(
     __syncthreads();
     fft::transform<N, ROW, true>(buf, tw);
   }
-#pragma unroll
-  for (int k = 0; k < fft::kPerThread; ++k) {
-    int l, i;
-    L::element(threadIdx.x + k * L::kThreads, l, i);
-    const int c = c0 + l;
-    if (c < a.count && i < a.nout) {
+  if constexpr (L::kThreadLine) {
+    int l0, i0;
+    L::element(threadIdx.x, l0, i0);
+    constexpr int di = L::kPointStep;
+    const int c = c0 + l0;
+    if (c < a.count) {
       const int o = c / a.inner, w = c - o * a.inner;
-      a.out[o * a.out_os + w * a.out_ws + i * a.out_es] = buf[L::addr(l, i)];
+      float2* p = a.out + (o * a.out_os + w * a.out_ws + i0 * a.out_es);
+      const int64_t st = (int64_t)di * a.out_es;
+#pragma unroll
+      for (int k = 0; k < fft::kPerThread; ++k) {
+        const int i = i0 + k * di;
+        if (i < a.nout) *p = buf[L::addr(l0, i)];
+        p += st;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < fft::kPerThread; ++k) {
+      int l, i;
+      L::element(threadIdx.x + k * L::kThreads, l, i);
+      const int c = c0 + l;
+      if (c < a.count && i < a.nout) {
+        const int o = c / a.inner, w = c - o * a.inner;
+        a.out[o * a.out_os + w * a.out_ws + i * a.out_es] = buf[L::addr(l, i)];
+      }
     }
   }
 }
