@@ -95,6 +95,21 @@ __device__ double block_sum(double v, double* sh) {
   return r;
 }
 
+// Rows (z < nz, y < ny) of T, the first stage's inputs of the last pass.
+struct TRows {
+  const float2* T;
+  int c0, count, ny, py, px;
+  template <int R, int STEP>
+  __device__ __forceinline__ void get(int l, int j, float2* w) const {
+    const int c = c0 + l;
+    const bool ok = c < count;
+    const int z = c / ny, y = c - z * ny;
+    const float2* t = T + (((int64_t)z * py + y) * px + j);
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = ok ? t[r * STEP] : make_float2(0.0f, 0.0f);
+  }
+};
+
 // Last pass of the normal operator: inverse transforms of the rows (z < nz,
 // y < ny) of T, the first nx points of each, plus lambda (W^H W p); writes Ap
 // and partial[block] = sum Re(conj(p) Ap) over the block's rows.  Launched on
@@ -104,6 +119,7 @@ __global__ void __launch_bounds__(fft::kThreads)
 crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, float2* __restrict__ Ap,
             int nx, int ny, int nz, float lambda, double* __restrict__ partial) {
   using L = fft::Lds<N, true>;
+  using S = fft::Sched<N>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
   __shared__ double sh[kThreads];
@@ -111,58 +127,26 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
   const int count = ny * nz;
   const int groups = (count + L::kLines - 1) / L::kLines;
   const int64_t plane = (int64_t)nx * ny;
+  constexpr int RL = S::last(false), kStep = N / RL;
   double acc = 0.0;
   for (int g = blockIdx.x; g < groups; g += gridDim.x) {
     const int c0 = g * L::kLines;
-    if constexpr (L::kThreadLine) {
-      // one line per thread (see fhd_fft.h): its row of T located once
-      int l0, i0;
-      L::element(threadIdx.x, l0, i0);
-      const int c = c0 + l0;
-      const int z = c / ny, y = c - z * ny;
-      const float2* tp = T + ((int64_t)z * py + y) * N + i0;
+    float2 v[fft::kPerThread];
+    fft::transform<N, true, true, false>(TRows{T, c0, count, ny, py, N}, buf, tw, v);
+    // the last stage's outputs: point j + r kStep of line c0 + l
 #pragma unroll
-      for (int k = 0; k < fft::kPerThread; ++k)
-        buf[L::addr(l0, i0 + k * L::kPointStep)] = c < count ? tp[k * L::kPointStep] : make_float2(0.0f, 0.0f);
-    } else {
-#pragma unroll
-      for (int k = 0; k < fft::kPerThread; ++k) {
-        int l, i;
-        L::element(threadIdx.x + k * L::kThreads, l, i);
-        const int c = c0 + l;
-        float2 v = make_float2(0.0f, 0.0f);
-        if (c < count) {
-          const int z = c / ny, y = c - z * ny;
-          v = T[((int64_t)z * py + y) * N + i];
-        }
-        buf[L::addr(l, i)] = v;
-      }
-    }
-    __syncthreads();
-    fft::transform<N, true, true>(buf, tw);
-    int zl = 0, yl = 0;
-    if constexpr (L::kThreadLine) {
-      int l0, i0;
-      L::element(threadIdx.x, l0, i0);
-      zl = (c0 + l0) / ny;
-      yl = c0 + l0 - zl * ny;
-    }
-#pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * L::kThreads, l, i);
+    for (int k = 0; k < fft::kPerThread / RL; ++k) {
+      int l, j;
+      fft::locate<N, RL, true>(k, l, j);
       const int c = c0 + l;
-      if (c < count && i < nx) {
-        int z, y;
-        if constexpr (L::kThreadLine) {
-          z = zl;
-          y = yl;
-        } else {
-          z = c / ny;
-          y = c - z * ny;
-        }
+      if (c >= count) continue;
+      const int z = c / ny, y = c - z * ny;
+#pragma unroll
+      for (int r = 0; r < RL; ++r) {
+        const int i = j + r * kStep;
+        if (i >= nx) continue;
         const int64_t vox = (int64_t)c * nx + i;
-        float2 v = buf[L::addr(l, i)];
+        float2 a = v[k * RL + r];
         const float2 cv = p[vox];
         if (lambda != 0.0f) {
           float lr = 0.0f, li = 0.0f;
@@ -173,14 +157,13 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
           if (y + 1 < ny) { const float2 q = p[vox + nx]; lr += cv.x - q.x; li += cv.y - q.y; }
           if (z > 0) { const float2 q = p[vox - plane]; lr += cv.x - q.x; li += cv.y - q.y; }
           if (z + 1 < nz) { const float2 q = p[vox + plane]; lr += cv.x - q.x; li += cv.y - q.y; }
-          v.x = __builtin_fmaf(lambda, lr, v.x);
-          v.y = __builtin_fmaf(lambda, li, v.y);
+          a.x = __builtin_fmaf(lambda, lr, a.x);
+          a.y = __builtin_fmaf(lambda, li, a.y);
         }
-        Ap[vox] = v;
-        acc += (double)cv.x * v.x + (double)cv.y * v.y;
+        Ap[vox] = a;
+        acc += (double)cv.x * a.x + (double)cv.y * a.y;
       }
     }
-    __syncthreads();
   }
   const double s = block_sum(acc, sh);
   if (threadIdx.x == 0 && partial) partial[blockIdx.x] = s;

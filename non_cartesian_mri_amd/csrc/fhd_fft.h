@@ -1,20 +1,35 @@
-// Batched power-of-two FFTs of lines held in LDS (gfx950), for the Toeplitz
-// normal operator and the gridding reconstruction.
+// Batched power-of-two FFTs of lines (gfx950), for the Toeplitz normal
+// operator and the gridding reconstruction.
 //
-// A workgroup transforms lines of N points (N = 2^p, 2 <= N <= 1024) held in
-// LDS; every thread holds 16 complex values per stage, so the register
-// footprint does not depend on N.  The transform is the self-sorting
-// (Stockham) formulation: stage s with radix R combines R sub-transforms of
-// length Ns (the product of the earlier radices) into transforms of length
-// Ns R; the butterfly j reads its R inputs at j + r N/R, multiplies input r by
-// w_N^(r (j mod Ns) N / (Ns R)), takes an R-point DFT in registers and writes
-// output r to (j div Ns) Ns R + (j mod Ns) + r Ns.  Radices: 2, 4 or 8 first
-// (N's bits mod 4), then 16s, so N = 256 takes two stages through LDS.  The
-// R-point DFTs are radix-2 decimation in frequency in registers with the
-// sixteenth-turn twiddles as constants.  w_N^t = e^(-2 pi i t / N) comes from a
-// per-workgroup table computed with the library's own sincos in turns.
+// A workgroup transforms Lds<N, ROW>::kLines lines of N points (N = 2^p,
+// 2 <= N <= 1024); every thread holds 16 complex values per stage, so the
+// register footprint does not depend on N.  The transform is the
+// self-sorting (Stockham) formulation: stage s with radix R combines R
+// sub-transforms of length Ns (the product of the earlier radices) into
+// transforms of length Ns R; butterfly j reads its R inputs at j + r N/R,
+// multiplies input r by w_N^(r (j mod Ns) N / (Ns R)), takes an R-point DFT in
+// registers and writes output r to (j div Ns) Ns R + (j mod Ns) + r Ns.
+// Radices: 16s and, when p is not a multiple of 4, one stage of 2, 4 or 8,
+// either first (ascending order) or last (descending order); N = 256 takes
+// two stages.  The R-point DFTs are radix-2 decimation in frequency in
+// registers with the sixteenth-turn twiddles as constants; w_N^t =
+// e^(-2 pi i t / N) comes from a per-workgroup table computed with the
+// library's own sincos in turns.
 //
-// Two LDS layouts:
+// Only the exchanges between stages go through LDS.  The first stage takes
+// its inputs from the caller (global memory: butterfly j's inputs j + r N/R
+// are points of one line, and consecutive threads take consecutive lines in a
+// column tile or consecutive points in a row tile, so the reads coalesce), and
+// the last stage hands its outputs to the caller at their final positions:
+// the last stage has Ns R = N, so butterfly j writes points j + r N/R, the
+// same positions it would read.  The first stage of a transform in the
+// descending order reads exactly the points that the last stage of one in
+// the ascending order wrote from the same butterflies (both radix 16, or
+// both the single stage when N <= 16), so a forward transform, a pointwise
+// product and an inverse transform chain in registers with no LDS exchange
+// in between.
+//
+// Two LDS layouts for the exchanges:
 //   row    -- line l, point i at l * pitch + swizzle(i): lines that are
 //             contiguous in memory (x axis); 4096 values per workgroup (256
 //             threads); the XOR swizzle within 16-point chunks and the
@@ -55,29 +70,44 @@ struct Lds {
       return i * kColPitch + l;
     }
   }
-  // Threads of a row tile of N >= 256 points each keep one line (N / 16
-  // threads per line, 16 points each); a column tile's threads keep one line
-  // when the thread count is a multiple of the line count.
-  static constexpr bool kThreadLine = ROW ? N >= 256 : kThreads % kLines == 0;
-  static constexpr int kPointStep = ROW ? N / 16 : kThreads / kLines;  // for kThreadLine
-  // element e of the workgroup's kElems in load/store order: consecutive
-  // threads take consecutive points of a line (row) or consecutive lines
-  // (column); element t + k kThreads of thread t is point i0 + k kPointStep
-  // of the thread's line when kThreadLine
-  __device__ static __forceinline__ void element(int e, int& l, int& i) {
-    if constexpr (ROW && N >= 256) {
-      const int t = e % kThreads, k = e / kThreads;
-      l = t / (N / 16);
-      i = t % (N / 16) + k * (N / 16);
-    } else if constexpr (ROW) {
-      l = e / N;
-      i = e % N;
-    } else {
-      l = e % kLines;
-      i = e / kLines;
-    }
-  }
 };
+
+// Radix schedule of an N-point transform.
+template <int N>
+struct Sched {
+  static_assert(N >= 2 && N <= kMaxLen && (N & (N - 1)) == 0, "power of two in [2, 1024]");
+  static constexpr int kP = ilog2(N);
+  static constexpr int kRem = kP % 4;
+  static constexpr int kStages = (kP + 3) / 4;
+  // DESC: the short stage (radix 2^(p mod 4)) last instead of first
+  static constexpr int radix(int s, bool desc) {
+    return kRem == 0 ? 16 : (s == (desc ? kStages - 1 : 0) ? (1 << kRem) : 16);
+  }
+  static constexpr int ns(int s, bool desc) {
+    int n = 1;
+    for (int i = 0; i < s; ++i) n *= radix(i, desc);
+    return n;
+  }
+  static constexpr int first(bool desc) { return radix(0, desc); }
+  static constexpr int last(bool desc) { return radix(kStages - 1, desc); }
+};
+
+// Butterfly k (< 16 / R) of this thread in a radix-R stage: line l of the
+// workgroup and butterfly j < N / R of that line.  Column tiles give
+// consecutive threads consecutive lines, row tiles consecutive butterflies.
+template <int N, int R, bool ROW>
+__device__ __forceinline__ void locate(int k, int& l, int& j) {
+  using L = Lds<N, ROW>;
+  constexpr unsigned kBf = N / R;
+  const unsigned b = threadIdx.x + (unsigned)(k * L::kThreads);
+  if constexpr (ROW) {
+    l = (int)(b / kBf);
+    j = (int)(b % kBf);
+  } else {
+    l = (int)(b % (unsigned)L::kLines);
+    j = (int)(b / (unsigned)L::kLines);
+  }
+}
 
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
@@ -126,19 +156,23 @@ __device__ __forceinline__ void dft(float2* v) {
   for (int i = 0; i < R; ++i) v[i] = o[i];
 }
 
-// One radix-R stage over all lines of the workgroup (in place, two barriers).
-template <int N, int R, int NS, bool ROW, bool INV>
-__device__ __forceinline__ void stage(float2* buf, const float2* tw) {
-  using L = Lds<N, ROW>;
-  constexpr int kBf = N / R;                              // butterflies per line
-  constexpr int kPer = L::kLines * kBf / L::kThreads;     // butterflies per thread (16 / R)
-  static_assert(kPer * R == kPerThread, "16 values per thread");
-  float2 v[kPer][R];
+// The R-point DFTs of a thread's 16 / R butterflies; butterfly k's values
+// are v[k R .. k R + R).
+template <int R, bool INV>
+__device__ __forceinline__ void dft_all(float2* v) {
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int b = threadIdx.x + k * L::kThreads;
-    const int l = ROW ? b / kBf : b % L::kLines;
-    const int j = ROW ? b % kBf : b / L::kLines;
+  for (int k = 0; k < kPerThread / R; ++k) dft<R, INV>(v + k * R);
+}
+
+// Stage inputs from LDS, twiddled.
+template <int N, int R, int NS, bool ROW, bool INV>
+__device__ __forceinline__ void read_stage(const float2* buf, const float2* tw, float2* v) {
+  using L = Lds<N, ROW>;
+  constexpr int kBf = N / R;
+#pragma unroll
+  for (int k = 0; k < kPerThread / R; ++k) {
+    int l, j;
+    locate<N, R, ROW>(k, l, j);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float2 a = buf[L::addr(l, j + r * kBf)];
@@ -147,35 +181,78 @@ __device__ __forceinline__ void stage(float2* buf, const float2* tw) {
         if (INV) w.y = -w.y;
         a = cmul(a, w);
       }
-      v[k][r] = a;
+      v[k * R + r] = a;
     }
   }
-  __syncthreads();
+}
+
+// Stage outputs to LDS.
+template <int N, int R, int NS, bool ROW>
+__device__ __forceinline__ void write_stage(float2* buf, const float2* v) {
+  using L = Lds<N, ROW>;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int b = threadIdx.x + k * L::kThreads;
-    const int l = ROW ? b / kBf : b % L::kLines;
-    const int j = ROW ? b % kBf : b / L::kLines;
-    dft<R, INV>(v[k]);
+  for (int k = 0; k < kPerThread / R; ++k) {
+    int l, j;
+    locate<N, R, ROW>(k, l, j);
     const int d = (j / NS) * NS * R + (j % NS);
 #pragma unroll
-    for (int r = 0; r < R; ++r) buf[L::addr(l, d + r * NS)] = v[k][r];
+    for (int r = 0; r < R; ++r) buf[L::addr(l, d + r * NS)] = v[k * R + r];
   }
-  __syncthreads();
+}
+
+// Stages S .. last through LDS.  On entry v holds the outputs of stage S - 1
+// (after its DFTs), on exit those of the last stage.  Starts with a barrier,
+// so the buffer may still be read by earlier code, and ends without one.
+template <int N, bool ROW, bool INV, bool DESC, int S = 1>
+__device__ __forceinline__ void through_lds(float2* buf, const float2* tw, float2* v) {
+  using Sc = Sched<N>;
+  if constexpr (S < Sc::kStages) {
+    constexpr int Rp = Sc::radix(S - 1, DESC), NSp = Sc::ns(S - 1, DESC);
+    constexpr int R = Sc::radix(S, DESC), NS = Sc::ns(S, DESC);
+    __syncthreads();
+    write_stage<N, Rp, NSp, ROW>(buf, v);
+    __syncthreads();
+    read_stage<N, R, NS, ROW, INV>(buf, tw, v);
+    dft_all<R, INV>(v);
+    through_lds<N, ROW, INV, DESC, S + 1>(buf, tw, v);
+  }
+}
+
+// The first stage (no twiddles: Ns = 1) with inputs from the caller:
+// load.template get<R, STEP>(l, j, w) fills w[r] with point j + r STEP of line l.
+template <int N, bool ROW, bool INV, bool DESC, class Load>
+__device__ __forceinline__ void first_stage(const Load& load, float2* v) {
+  constexpr int R = Sched<N>::first(DESC);
+#pragma unroll
+  for (int k = 0; k < kPerThread / R; ++k) {
+    int l, j;
+    locate<N, R, ROW>(k, l, j);
+    load.template get<R, N / R>(l, j, v + k * R);
+  }
+  dft_all<R, INV>(v);
 }
 
 // Unnormalised DFT (forward: e^(-2 pi i jk/N); inverse: e^(+2 pi i jk/N)) of
-// every line in LDS.  Expects a barrier between the last writes to buf / tw
-// and the call; ends with a barrier.
-template <int N, bool ROW, bool INV>
-__device__ __forceinline__ void transform(float2* buf, const float2* tw) {
-  static_assert(N >= 2 && N <= kMaxLen && (N & (N - 1)) == 0, "power of two in [2, 1024]");
-  constexpr int p = ilog2(N);
-  constexpr int rem = p % 4;
-  constexpr int ns1 = rem != 0 ? (1 << rem) : 1;
-  if constexpr (rem != 0) stage<N, (1 << rem), 1, ROW, INV>(buf, tw);
-  if constexpr (p >= 4) stage<N, 16, ns1, ROW, INV>(buf, tw);
-  if constexpr (p >= 8) stage<N, 16, ns1 * 16, ROW, INV>(buf, tw);
+// the workgroup's lines: inputs from `load` (as in first_stage), outputs of
+// the last stage left in v (see last_stage).  The twiddle table may be
+// filled just before the call: the barriers of the LDS exchanges order it.
+template <int N, bool ROW, bool INV, bool DESC, class Load>
+__device__ __forceinline__ void transform(const Load& load, float2* buf, const float2* tw, float2* v) {
+  first_stage<N, ROW, INV, DESC>(load, v);
+  through_lds<N, ROW, INV, DESC>(buf, tw, v);
+}
+
+// The last stage's outputs to the caller: store.template put<R, STEP>(l, j, w)
+// takes w[r] as point j + r STEP of line l.
+template <int N, bool ROW, bool DESC, class Store>
+__device__ __forceinline__ void last_stage(const Store& store, const float2* v) {
+  constexpr int R = Sched<N>::last(DESC);
+#pragma unroll
+  for (int k = 0; k < kPerThread / R; ++k) {
+    int l, j;
+    locate<N, R, ROW>(k, l, j);
+    store.template put<R, N / R>(l, j, v + k * R);
+  }
 }
 
 // tw[t] = e^(-2 pi i t / N), t < N.

@@ -1,108 +1,106 @@
 // Batched line transforms over one axis of a 3-D array (see fhd_lines.h).
-// A workgroup loads Lds<N, ROW>::kLines lines (zero-extending past nin points), runs
-// the LDS transform of fhd_fft.h (optionally forward, times a real spectrum,
-// inverse) and stores the first nout points of each line.
+// A workgroup takes Lds<N, ROW>::kLines lines (zero-extending past nin
+// points) straight from global memory into the first stage of the
+// transforms of fhd_fft.h (forward, inverse, or forward then the product
+// with a real spectrum then inverse, chained in registers) and stores the
+// first nout points of each line from the last stage.
 #include "fhd_fft.h"
 #include "fhd_lines.h"
 
 namespace ncmri {
 namespace {
 
+// Offset of line c: outer index o = c / inner, inner index w = c mod inner.
+__device__ __forceinline__ int64_t line_offset(int c, int inner, int64_t os, int64_t ws) {
+  const int o = c / inner, w = c - o * inner;
+  return o * os + w * ws;
+}
+
+// Inputs of the first stage: point i of line c0 + l, zero past nin points
+// or past the last line.
+struct LineLoad {
+  const float2* in;
+  int c0, count, inner, nin;
+  int64_t os, ws, es;
+  template <int R, int STEP>
+  __device__ __forceinline__ void get(int l, int j, float2* w) const {
+    const int c = c0 + l;
+    const bool ok = c < count;
+    const float2* p = in + (line_offset(ok ? c : 0, inner, os, ws) + j * es);
+    const int64_t st = (int64_t)STEP * es;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w[r] = (ok && j + r * STEP < nin) ? *p : make_float2(0.0f, 0.0f);
+      p += st;
+    }
+  }
+};
+
+// Outputs of the last stage: the first nout points of each existing line.
+struct LineStore {
+  float2* out;
+  int c0, count, inner, nout;
+  int64_t os, ws, es;
+  template <int R, int STEP>
+  __device__ __forceinline__ void put(int l, int j, const float2* w) const {
+    const int c = c0 + l;
+    if (c >= count) return;
+    float2* p = out + (line_offset(c, inner, os, ws) + j * es);
+    const int64_t st = (int64_t)STEP * es;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (j + r * STEP < nout) *p = w[r];
+      p += st;
+    }
+  }
+};
+
 template <int N, bool ROW, int MODE>
 __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(LinePass a) {
   using L = fft::Lds<N, ROW>;
+  using S = fft::Sched<N>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
   fft::fill_twiddles<N>(tw);
   const int c0 = blockIdx.x * L::kLines;
-  float qv[fft::kPerThread];
-  // the spectrum is read before the transform where registers allow (it
-  // then arrives while the transform runs); the 1024-thread tiles read it after
-  constexpr bool kPrefetchQ = L::kThreads <= 512;
-  if constexpr (L::kThreadLine) {
-    // one line per thread: its address and bounds once, then a running pointer
-    int l0, i0;
-    L::element(threadIdx.x, l0, i0);
-    constexpr int di = L::kPointStep;
-    const int c = c0 + l0;
-    const bool ok = c < a.count;
-    const int o = c / a.inner, w = c - o * a.inner;
-    const float2* p = a.in + (o * a.in_os + w * a.in_ws + i0 * a.in_es);
-    const int64_t st = (int64_t)di * a.in_es;
-    const float* qp = a.q + (c + (int64_t)i0 * a.q_es);
-    const int64_t qst = (int64_t)di * a.q_es;
-#pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      const int i = i0 + k * di;
-      buf[L::addr(l0, i)] = (ok && i < a.nin) ? *p : make_float2(0.0f, 0.0f);
-      p += st;
-      if constexpr (MODE == kLineFwdQInv && kPrefetchQ) {
-        qv[k] = ok ? *qp : 0.0f;
-        qp += qst;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * L::kThreads, l, i);
-      const int c = c0 + l;
-      float2 v = make_float2(0.0f, 0.0f);
-      if (c < a.count && i < a.nin) {
-        const int o = c / a.inner, w = c - o * a.inner;
-        v = a.in[o * a.in_os + w * a.in_ws + i * a.in_es];
-      }
-      buf[L::addr(l, i)] = v;
-      if constexpr (MODE == kLineFwdQInv && kPrefetchQ) qv[k] = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
-    }
-  }
-  __syncthreads();
-  fft::transform<N, ROW, MODE == kLineInv>(buf, tw);
+  const LineLoad load{a.in, c0, a.count, a.inner, a.nin, a.in_os, a.in_ws, a.in_es};
+  const LineStore store{a.out, c0, a.count, a.inner, a.nout, a.out_os, a.out_ws, a.out_es};
+  float2 v[fft::kPerThread];
   if constexpr (MODE == kLineFwdQInv) {
+    static_assert(!ROW, "the spectral product runs on column tiles");
+    // The spectrum at the points of the forward transform's last stage; read
+    // before the transform where registers allow (it then arrives while the
+    // transform runs), after it for the 1024-thread tiles.
+    constexpr int RL = S::last(false), kStep = N / RL;
+    static_assert(RL == S::first(true), "the inverse's first stage takes the forward's last outputs");
+    float qv[fft::kPerThread];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * L::kThreads, l, i);
-      float q;
-      if constexpr (kPrefetchQ) {
-        q = qv[k];
-      } else {
+      for (int k = 0; k < fft::kPerThread / RL; ++k) {
+        int l, j;
+        fft::locate<N, RL, false>(k, l, j);
         const int c = c0 + l;
-        q = c < a.count ? a.q[c + i * a.q_es] : 0.0f;
-      }
-      const float2 v = buf[L::addr(l, i)];
-      buf[L::addr(l, i)] = make_float2(v.x * q, v.y * q);
-    }
-    __syncthreads();
-    fft::transform<N, ROW, true>(buf, tw);
-  }
-  if constexpr (L::kThreadLine) {
-    int l0, i0;
-    L::element(threadIdx.x, l0, i0);
-    constexpr int di = L::kPointStep;
-    const int c = c0 + l0;
-    if (c < a.count) {
-      const int o = c / a.inner, w = c - o * a.inner;
-      float2* p = a.out + (o * a.out_os + w * a.out_ws + i0 * a.out_es);
-      const int64_t st = (int64_t)di * a.out_es;
+        const float* qp = a.q + (c + (int64_t)j * a.q_es);
+        const int64_t qst = (int64_t)kStep * a.q_es;
 #pragma unroll
-      for (int k = 0; k < fft::kPerThread; ++k) {
-        const int i = i0 + k * di;
-        if (i < a.nout) *p = buf[L::addr(l0, i)];
-        p += st;
+        for (int r = 0; r < RL; ++r) {
+          qv[k * RL + r] = c < a.count ? *qp : 0.0f;
+          qp += qst;
+        }
       }
-    }
+    };
+    constexpr bool kPrefetchQ = L::kThreads <= 512;
+    if constexpr (kPrefetchQ) load_q();
+    fft::transform<N, false, false, false>(load, buf, tw, v);
+    if constexpr (!kPrefetchQ) load_q();
+#pragma unroll
+    for (int i = 0; i < fft::kPerThread; ++i) v[i] = make_float2(v[i].x * qv[i], v[i].y * qv[i]);
+    fft::dft_all<S::first(true), true>(v);
+    fft::through_lds<N, false, true, true>(buf, tw, v);
+    fft::last_stage<N, false, true>(store, v);
   } else {
-#pragma unroll
-    for (int k = 0; k < fft::kPerThread; ++k) {
-      int l, i;
-      L::element(threadIdx.x + k * L::kThreads, l, i);
-      const int c = c0 + l;
-      if (c < a.count && i < a.nout) {
-        const int o = c / a.inner, w = c - o * a.inner;
-        a.out[o * a.out_os + w * a.out_ws + i * a.out_es] = buf[L::addr(l, i)];
-      }
-    }
+    fft::transform<N, ROW, MODE == kLineInv, false>(load, buf, tw, v);
+    fft::last_stage<N, ROW, false>(store, v);
   }
 }
 
