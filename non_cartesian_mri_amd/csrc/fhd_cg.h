@@ -35,8 +35,9 @@ struct CgWorkspace {
   float2* r;        // [n] residual
   float2* p;        // [n] search direction
   float2* Ap;       // [n] operator applied to p
-  double* partial;  // [kCgPartials] stage-1 sums of the dot products
-  double* state;    // [8] <r,r>, <p,Ap>, alpha, beta
+  double* partial;  // [kCgPartials] stage-1 sums of <p, Ap> (and of the initial <r, r>)
+  double* partial2; // [kCgPartials] stage-1 sums of <r, r> in the iterations
+  double* state;    // [8] <r,r> (two slots), <p,Ap>, alpha, beta
 };
 
 constexpr int kCgPartials = 1024;
@@ -44,7 +45,7 @@ constexpr int kCgPartials = 1024;
 inline size_t cg_align(size_t b) { return (b + 255) / 256 * 256; }
 inline size_t cg_workspace_bytes(const ToeplitzDims& d) {
   return cg_align((size_t)d.lines() * 8) + 3 * cg_align((size_t)d.voxels() * 8) +
-         cg_align(kCgPartials * sizeof(double)) + cg_align(8 * sizeof(double));
+         2 * cg_align(kCgPartials * sizeof(double)) + cg_align(8 * sizeof(double));
 }
 inline CgWorkspace cg_workspace(void* base, const ToeplitzDims& d) {
   char* c = (char*)base;
@@ -54,6 +55,7 @@ inline CgWorkspace cg_workspace(void* base, const ToeplitzDims& d) {
   w.p = (float2*)c;  c += cg_align((size_t)d.voxels() * 8);
   w.Ap = (float2*)c; c += cg_align((size_t)d.voxels() * 8);
   w.partial = (double*)c; c += cg_align(kCgPartials * sizeof(double));
+  w.partial2 = (double*)c; c += cg_align(kCgPartials * sizeof(double));
   w.state = (double*)c;
   return w;
 }

@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBlocks = kCgPartials;  // grid of every reduction stage 1 (fixed: deterministic sums)
+static_assert(kBlocks % 64 == 0, "whole waves of partial sums");
 static_assert(kThreads == fft::kThreads, "one block size");
 
 // Circular coordinates of the difference grid: index i < n is d = i, i >= n is d = i - 2n.
@@ -99,14 +100,14 @@ __device__ double block_sum(double v, double* sh) {
 struct TRows {
   const float2* T;
   int c0, count, ny, py, px;
-  template <int R, int STEP>
+  template <int RN, int STEP>
   __device__ __forceinline__ void get(int l, int j, float2* w) const {
     const int c = c0 + l;
     const bool ok = c < count;
     const int z = c / ny, y = c - z * ny;
     const float2* t = T + (((int64_t)z * py + y) * px + j);
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = ok ? t[r * STEP] : make_float2(0.0f, 0.0f);
+    for (int r = 0; r < RN; ++r) w[r] = ok ? t[r * STEP] : make_float2(0.0f, 0.0f);
   }
 };
 
@@ -127,12 +128,13 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
   const int count = ny * nz;
   const int groups = (count + L::kLines - 1) / L::kLines;
   const int64_t plane = (int64_t)nx * ny;
+  // nx <= N / 2: only outputs r < RL / 2 of each last-stage butterfly are kept
   constexpr int RL = S::last(false), kStep = N / RL;
   double acc = 0.0;
   for (int g = blockIdx.x; g < groups; g += gridDim.x) {
     const int c0 = g * L::kLines;
     float2 v[fft::kPerThread];
-    fft::transform<N, true, true, false>(TRows{T, c0, count, ny, py, N}, buf, tw, v);
+    fft::transform<N, true, true, false, false>(TRows{T, c0, count, ny, py, N}, buf, tw, v);
     // the last stage's outputs: point j + r kStep of line c0 + l
 #pragma unroll
     for (int k = 0; k < fft::kPerThread / RL; ++k) {
@@ -142,7 +144,7 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
       if (c >= count) continue;
       const int z = c / ny, y = c - z * ny;
 #pragma unroll
-      for (int r = 0; r < RL; ++r) {
+      for (int r = 0; r < RL / 2; ++r) {
         const int i = j + r * kStep;
         if (i >= nx) continue;
         const int64_t vox = (int64_t)c * nx + i;
@@ -169,30 +171,33 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
   if (threadIdx.x == 0 && partial) partial[blockIdx.x] = s;
 }
 
-// Sums kBlocks partials in fixed order into a CG state slot, then derives:
-//   what 0: state[RS] = sum (and resid[0])                        -- initial <r, r>
-//   what 1: state[PAP] = sum, state[ALPHA] = state[RS] / sum      -- after A p
-//   what 2: state[BETA] = sum / state[RS], state[RS] = sum (and resid[it])
-enum { RS = 0, PAP = 1, ALPHA = 2, BETA = 3 };
-__global__ void __launch_bounds__(kThreads)
-finalize_kernel(const double* __restrict__ partial, double* __restrict__ state, int what,
-                double* __restrict__ resid) {
-  __shared__ double sh[kThreads];
+// CG state slots.  <r, r> alternates between two slots by iteration, so the
+// blocks of the direction update can read the old value while one of them
+// stores the new one.
+enum { RS0 = 0, RS1 = 1, PAP = 2, ALPHA = 3, BETA = 4 };
+
+// Sum of partial[0 .. kBlocks) in a fixed order, formed by every wave on its
+// own (no barrier): lane i adds partial[i + 64 k] for k = 0, 1, ..., then an
+// xor butterfly over the lanes.  Floating-point addition is commutative, so
+// both partners of each butterfly step get the same value: every lane of
+// every wave ends with the same bits.
+__device__ __forceinline__ double sum_partials(const double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < kBlocks; i += kThreads) acc += partial[i];
-  const double s = block_sum(acc, sh);
+#pragma unroll
+  for (int i = 0; i < kBlocks; i += 64) acc += partial[i + lane];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  return acc;
+}
+
+// The initial <r, r>: state[RS0] (and resid[0]).
+__global__ void __launch_bounds__(kThreads)
+initial_rs_kernel(const double* __restrict__ partial, double* __restrict__ state, double* __restrict__ resid) {
+  const double s = sum_partials(partial);
   if (threadIdx.x != 0) return;
-  if (what == 0) {
-    state[RS] = s;
-    if (resid) resid[0] = s;
-  } else if (what == 1) {
-    state[PAP] = s;
-    state[ALPHA] = s != 0.0 ? state[RS] / s : 0.0;
-  } else {
-    state[BETA] = state[RS] != 0.0 ? s / state[RS] : 0.0;
-    state[RS] = s;
-    if (resid) *resid = s;
-  }
+  state[RS0] = s;
+  if (resid) resid[0] = s;
 }
 
 // r = b - Ax, p = r; partial = sum |r|^2.
@@ -211,17 +216,31 @@ residual_kernel(const float2* __restrict__ b, const float2* __restrict__ Ax, flo
   if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
-// x += alpha p, r -= alpha Ap; partial = sum |r|^2.
+// alpha = <r, r> / <p, Ap> (every wave sums the <p, Ap> partials itself, while
+// its first elements load); x += alpha p, r -= alpha Ap; rr_partial = sum |r|^2.
 __global__ void __launch_bounds__(kThreads)
 step_kernel(float2* __restrict__ x, float2* __restrict__ r, const float2* __restrict__ pv,
-            const float2* __restrict__ Ap, int64_t n, const double* __restrict__ state,
-            double* __restrict__ partial) {
+            const float2* __restrict__ Ap, int64_t n, double* __restrict__ state, int slot,
+            const double* __restrict__ pap_partial, double* __restrict__ rr_partial) {
   __shared__ double sh[kThreads];
-  const float alpha = (float)state[ALPHA];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float2 p{}, a{}, xv{}, rv{};
+  if (i < n) {
+    p = pv[i];
+    a = Ap[i];
+    xv = x[i];
+    rv = r[i];
+  }
+  const double pap = sum_partials(pap_partial);
+  const double alpha_d = pap != 0.0 ? state[RS0 + slot] / pap : 0.0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    state[PAP] = pap;
+    state[ALPHA] = alpha_d;
+  }
+  const float alpha = (float)alpha_d;
   double acc = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const float2 p = pv[i], a = Ap[i];
-    float2 xv = x[i], rv = r[i];
+  while (i < n) {
     xv.x = __builtin_fmaf(alpha, p.x, xv.x);
     xv.y = __builtin_fmaf(alpha, p.y, xv.y);
     rv.x = __builtin_fmaf(-alpha, a.x, rv.x);
@@ -229,19 +248,47 @@ step_kernel(float2* __restrict__ x, float2* __restrict__ r, const float2* __rest
     x[i] = xv;
     r[i] = rv;
     acc += (double)rv.x * rv.x + (double)rv.y * rv.y;
+    i += stride;
+    if (i < n) {
+      p = pv[i];
+      a = Ap[i];
+      xv = x[i];
+      rv = r[i];
+    }
   }
   const double s = block_sum(acc, sh);
-  if (threadIdx.x == 0) partial[blockIdx.x] = s;
+  if (threadIdx.x == 0) rr_partial[blockIdx.x] = s;
 }
 
-// p = r + beta p.
+// beta = <r, r>_new / <r, r>_old (every wave sums the partials itself, while
+// its first elements load); p = r + beta p; the new <r, r> goes to the other
+// slot (and to *resid).
 __global__ void __launch_bounds__(kThreads)
-direction_kernel(const float2* __restrict__ r, float2* __restrict__ pv, int64_t n,
-                 const double* __restrict__ state) {
-  const float beta = (float)state[BETA];
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const float2 rv = r[i], p = pv[i];
+direction_kernel(const float2* __restrict__ r, float2* __restrict__ pv, int64_t n, double* __restrict__ state,
+                 int slot, const double* __restrict__ rr_partial, double* __restrict__ resid) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float2 rv{}, p{};
+  if (i < n) {
+    rv = r[i];
+    p = pv[i];
+  }
+  const double rs_new = sum_partials(rr_partial);
+  const double rs = state[RS0 + slot];
+  const double beta_d = rs != 0.0 ? rs_new / rs : 0.0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    state[BETA] = beta_d;
+    state[RS0 + (slot ^ 1)] = rs_new;
+    if (resid) *resid = rs_new;
+  }
+  const float beta = (float)beta_d;
+  while (i < n) {
     pv[i] = make_float2(__builtin_fmaf(beta, p.x, rv.x), __builtin_fmaf(beta, p.y, rv.y));
+    i += stride;
+    if (i < n) {
+      rv = r[i];
+      p = pv[i];
+    }
   }
 }
 
@@ -260,6 +307,7 @@ hipError_t launch_crop_n(const ToeplitzDims& d, const float2* T, const float2* p
 
 hipError_t launch_crop(const ToeplitzDims& d, const float2* T, const float2* p, float2* Ap, float lambda,
                        double* partial, hipStream_t s) {
+  if (2 * d.nx > d.px) return hipErrorInvalidValue;   // the kernel keeps the first half of each row only
   switch (d.px) {
     case 2: return launch_crop_n<2>(d, T, p, Ap, lambda, partial, s);
     case 4: return launch_crop_n<4>(d, T, p, Ap, lambda, partial, s);
@@ -337,15 +385,15 @@ const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const
   // r = b - A x, p = r, <r, r>
   if (const char* e = normal_apply(d, Qhat, lambda, x, w.Ap, w.T, nullptr, s)) return e;
   hipLaunchKernelGGL(residual_kernel, dim3(kBlocks), dim3(kThreads), 0, s, b, w.Ap, w.r, w.p, n, w.partial);
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 0, resid);
+  hipLaunchKernelGGL(initial_rs_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, resid);
   if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
   for (int it = 0; it < iters; ++it) {
+    const int slot = it & 1;
     if (const char* e = normal_apply(d, Qhat, lambda, w.p, w.Ap, w.T, w.partial, s)) return e;
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 1, nullptr);
-    hipLaunchKernelGGL(step_kernel, dim3(kBlocks), dim3(kThreads), 0, s, x, w.r, w.p, w.Ap, n, w.state, w.partial);
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kThreads), 0, s, w.partial, w.state, 2,
-                       resid ? resid + it + 1 : nullptr);
-    hipLaunchKernelGGL(direction_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, w.r, w.p, n, w.state);
+    hipLaunchKernelGGL(step_kernel, dim3(kBlocks), dim3(kThreads), 0, s, x, w.r, w.p, w.Ap, n, w.state, slot,
+                       w.partial, w.partial2);
+    hipLaunchKernelGGL(direction_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, w.r, w.p, n, w.state, slot,
+                       w.partial2, resid ? resid + it + 1 : nullptr);
     if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
   }
   return nullptr;

@@ -135,7 +135,9 @@ __host__ __device__ constexpr int bitrev(int i, int bits) {
 }
 
 // In-register R-point DFT (R = 2, 4, 8, 16), natural order in and out.
-template <int R, bool INV>
+// HALF_IN: inputs R/2 .. R-1 are zero (not read), which turns the first
+// butterfly level into copies and rotations.
+template <int R, bool INV, bool HALF_IN = false>
 __device__ __forceinline__ void dft(float2* v) {
 #pragma unroll
   for (int half = R / 2; half >= 1; half /= 2) {
@@ -143,9 +145,13 @@ __device__ __forceinline__ void dft(float2* v) {
     for (int start = 0; start < R; start += 2 * half) {
 #pragma unroll
       for (int k = 0; k < half; ++k) {
-        const float2 a = v[start + k], b = v[start + k + half];
-        v[start + k] = cadd(a, b);
-        v[start + k + half] = rot16<INV>(csub(a, b), k * (16 / (2 * half)));
+        if (HALF_IN && half == R / 2) {
+          v[start + k + half] = rot16<INV>(v[start + k], k * (16 / (2 * half)));
+        } else {
+          const float2 a = v[start + k], b = v[start + k + half];
+          v[start + k] = cadd(a, b);
+          v[start + k + half] = rot16<INV>(csub(a, b), k * (16 / (2 * half)));
+        }
       }
     }
   }
@@ -158,10 +164,10 @@ __device__ __forceinline__ void dft(float2* v) {
 
 // The R-point DFTs of a thread's 16 / R butterflies; butterfly k's values
 // are v[k R .. k R + R).
-template <int R, bool INV>
+template <int R, bool INV, bool HALF_IN = false>
 __device__ __forceinline__ void dft_all(float2* v) {
 #pragma unroll
-  for (int k = 0; k < kPerThread / R; ++k) dft<R, INV>(v + k * R);
+  for (int k = 0; k < kPerThread / R; ++k) dft<R, INV, HALF_IN>(v + k * R);
 }
 
 // Stage inputs from LDS, twiddled.
@@ -219,39 +225,45 @@ __device__ __forceinline__ void through_lds(float2* buf, const float2* tw, float
 }
 
 // The first stage (no twiddles: Ns = 1) with inputs from the caller:
-// load.template get<R, STEP>(l, j, w) fills w[r] with point j + r STEP of line l.
-template <int N, bool ROW, bool INV, bool DESC, class Load>
+// load.template get<RN, STEP>(l, j, w) fills w[r], r < RN, with point
+// j + r STEP of line l.  HALF_IN: the points from N/2 on are zero, which are
+// inputs r >= R/2 of every butterfly (j < N/R), so only RN = R/2 are read.
+template <int N, bool ROW, bool INV, bool DESC, bool HALF_IN, class Load>
 __device__ __forceinline__ void first_stage(const Load& load, float2* v) {
   constexpr int R = Sched<N>::first(DESC);
+  constexpr int RN = HALF_IN ? R / 2 : R;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
     locate<N, R, ROW>(k, l, j);
-    load.template get<R, N / R>(l, j, v + k * R);
+    load.template get<RN, N / R>(l, j, v + k * R);
   }
-  dft_all<R, INV>(v);
+  dft_all<R, INV, HALF_IN>(v);
 }
 
 // Unnormalised DFT (forward: e^(-2 pi i jk/N); inverse: e^(+2 pi i jk/N)) of
 // the workgroup's lines: inputs from `load` (as in first_stage), outputs of
 // the last stage left in v (see last_stage).  The twiddle table may be
 // filled just before the call: the barriers of the LDS exchanges order it.
-template <int N, bool ROW, bool INV, bool DESC, class Load>
+template <int N, bool ROW, bool INV, bool DESC, bool HALF_IN, class Load>
 __device__ __forceinline__ void transform(const Load& load, float2* buf, const float2* tw, float2* v) {
-  first_stage<N, ROW, INV, DESC>(load, v);
+  first_stage<N, ROW, INV, DESC, HALF_IN>(load, v);
   through_lds<N, ROW, INV, DESC>(buf, tw, v);
 }
 
-// The last stage's outputs to the caller: store.template put<R, STEP>(l, j, w)
-// takes w[r] as point j + r STEP of line l.
-template <int N, bool ROW, bool DESC, class Store>
+// The last stage's outputs to the caller: store.template put<RN, STEP>(l, j, w)
+// takes w[r], r < RN, as point j + r STEP of line l.  HALF_OUT: only the
+// points below N/2 are wanted, outputs r < R/2 of every butterfly (the
+// computation of the others is then dead code).
+template <int N, bool ROW, bool DESC, bool HALF_OUT, class Store>
 __device__ __forceinline__ void last_stage(const Store& store, const float2* v) {
   constexpr int R = Sched<N>::last(DESC);
+  constexpr int RN = HALF_OUT ? R / 2 : R;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
     locate<N, R, ROW>(k, l, j);
-    store.template put<R, N / R>(l, j, v + k * R);
+    store.template put<RN, N / R>(l, j, v + k * R);
   }
 }
 

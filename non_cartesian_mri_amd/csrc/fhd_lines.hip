@@ -3,7 +3,10 @@
 // points) straight from global memory into the first stage of the
 // transforms of fhd_fft.h (forward, inverse, or forward then the product
 // with a real spectrum then inverse, chained in registers) and stores the
-// first nout points of each line from the last stage.
+// first nout points of each line from the last stage.  Where nin <= N/2 (a
+// zero-padded line) or nout <= N/2 (a cropped one) the launch takes a
+// variant that neither reads the known zeros nor computes the discarded
+// half.
 #include "fhd_fft.h"
 #include "fhd_lines.h"
 
@@ -22,14 +25,14 @@ struct LineLoad {
   const float2* in;
   int c0, count, inner, nin;
   int64_t os, ws, es;
-  template <int R, int STEP>
+  template <int RN, int STEP>
   __device__ __forceinline__ void get(int l, int j, float2* w) const {
     const int c = c0 + l;
     const bool ok = c < count;
     const float2* p = in + (line_offset(ok ? c : 0, inner, os, ws) + j * es);
     const int64_t st = (int64_t)STEP * es;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RN; ++r) {
       w[r] = (ok && j + r * STEP < nin) ? *p : make_float2(0.0f, 0.0f);
       p += st;
     }
@@ -41,28 +44,40 @@ struct LineStore {
   float2* out;
   int c0, count, inner, nout;
   int64_t os, ws, es;
-  template <int R, int STEP>
+  template <int RN, int STEP>
   __device__ __forceinline__ void put(int l, int j, const float2* w) const {
     const int c = c0 + l;
     if (c >= count) return;
     float2* p = out + (line_offset(c, inner, os, ws) + j * es);
     const int64_t st = (int64_t)STEP * es;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RN; ++r) {
       if (j + r * STEP < nout) *p = w[r];
       p += st;
     }
   }
 };
 
-template <int N, bool ROW, int MODE>
+// PRUNE: bit 0 -- nin <= N/2, bit 1 -- nout <= N/2.
+enum { kPruneIn = 1, kPruneOut = 2 };
+
+// Tile of block b in the spectral-product pass.  Workgroups go to the 8 XCDs
+// in turn (block b to XCD b mod 8), each with its own L2; tiles 2k and 2k+1
+// read the two halves of the same 128-byte lines of the real spectrum (16
+// floats per row each), so they are given blocks 16m + i and 16m + i + 8,
+// which share an XCD.  The grid is a multiple of 16 blocks.
+__device__ __forceinline__ int paired_tile(int b) { return (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1); }
+
+template <int N, bool ROW, int MODE, int PRUNE>
 __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(LinePass a) {
+  constexpr bool kHalfIn = (PRUNE & kPruneIn) != 0, kHalfOut = (PRUNE & kPruneOut) != 0;
   using L = fft::Lds<N, ROW>;
   using S = fft::Sched<N>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
   fft::fill_twiddles<N>(tw);
-  const int c0 = blockIdx.x * L::kLines;
+  const int tile = MODE == kLineFwdQInv ? paired_tile(blockIdx.x) : (int)blockIdx.x;
+  const int c0 = tile * L::kLines;   // past the last line (padding blocks): nothing read or written
   const LineLoad load{a.in, c0, a.count, a.inner, a.nin, a.in_os, a.in_ws, a.in_es};
   const LineStore store{a.out, c0, a.count, a.inner, a.nout, a.out_os, a.out_ws, a.out_es};
   float2 v[fft::kPerThread];
@@ -91,26 +106,44 @@ __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(
     };
     constexpr bool kPrefetchQ = L::kThreads <= 512;
     if constexpr (kPrefetchQ) load_q();
-    fft::transform<N, false, false, false>(load, buf, tw, v);
+    fft::transform<N, false, false, false, kHalfIn>(load, buf, tw, v);
     if constexpr (!kPrefetchQ) load_q();
 #pragma unroll
     for (int i = 0; i < fft::kPerThread; ++i) v[i] = make_float2(v[i].x * qv[i], v[i].y * qv[i]);
     fft::dft_all<S::first(true), true>(v);
     fft::through_lds<N, false, true, true>(buf, tw, v);
-    fft::last_stage<N, false, true>(store, v);
+    fft::last_stage<N, false, true, kHalfOut>(store, v);
   } else {
-    fft::transform<N, ROW, MODE == kLineInv, false>(load, buf, tw, v);
-    fft::last_stage<N, ROW, false>(store, v);
+    fft::transform<N, ROW, MODE == kLineInv, false, kHalfIn>(load, buf, tw, v);
+    fft::last_stage<N, ROW, false, kHalfOut>(store, v);
   }
 }
 
+template <int N, bool ROW, int MODE, int PRUNE>
+hipError_t launch_grid(const LinePass& a, hipStream_t s) {
+  constexpr int lines = fft::Lds<N, ROW>::kLines;
+  int grid = (a.count + lines - 1) / lines;
+  if (grid == 0) return hipSuccess;
+  if (MODE == kLineFwdQInv) grid = (grid + 15) / 16 * 16;   // whole groups for paired_tile
+  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE, PRUNE>), dim3(grid), dim3(fft::Lds<N, ROW>::kThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+// The pruned variants that the passes use: a forward transform of a
+// zero-padded line, an inverse whose output is cropped, and the spectral
+// product with both; every mode also has the full one.
 template <int N, bool ROW, int MODE>
 hipError_t launch_lines_n(const LinePass& a, hipStream_t s) {
-  constexpr int lines = fft::Lds<N, ROW>::kLines;
-  const int grid = (a.count + lines - 1) / lines;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE>), dim3(grid), dim3(fft::Lds<N, ROW>::kThreads), 0, s, a);
-  return hipGetLastError();
+  const bool half_in = a.nin <= N / 2, half_out = a.nout <= N / 2;
+  if constexpr (MODE == kLineFwd) {
+    if (half_in) return launch_grid<N, ROW, MODE, kPruneIn>(a, s);
+  } else if constexpr (MODE == kLineInv) {
+    if (half_out) return launch_grid<N, ROW, MODE, kPruneOut>(a, s);
+  } else {
+    if (half_in && half_out) return launch_grid<N, ROW, MODE, kPruneIn | kPruneOut>(a, s);
+  }
+  return launch_grid<N, ROW, MODE, 0>(a, s);
 }
 
 template <bool ROW, int MODE>
