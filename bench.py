@@ -60,6 +60,11 @@ TRAFFIC = {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
         "fetch_bytes": 1047793.4 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    # the normal operator's five kernels, per application (128^3, lambda = 0)
+    ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "04e2d8eb52c8303e",
+        "fetch_bytes": 147708.4 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
+        "profile": "profiles/cg_normal_operator_128cubed_kernel_stats.md"},
 }
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
@@ -269,6 +274,13 @@ def bench_cg(args, p, t, D, dev) -> dict:
                                "spectral product, inverse y, inverse x with the regulariser and <p, Ap>",
                      "algorithmic_bytes": op_bytes},
     }
+    if args.cg_lambda == 0.0:
+        # the operator does not depend on the trig path (it only reads Qhat)
+        traffic, detail = traffic_for(args.config + "/cg", "hw", "blocked", "mfma", 64, op_ms)
+        if traffic is not None:
+            res["roofline"]["traffic"] = round(traffic, 3)
+            res["roofline"]["traffic_unit"] = "GB/s (HBM bytes per application from FETCH_SIZE/WRITE_SIZE / time)"
+            res["roofline"]["traffic_detail"] = detail
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline_cg(p, args.cpu_seconds, lam)
     return res
@@ -352,20 +364,22 @@ def bench_gridding(args, p, t, D, dev) -> dict:
     return res
 
 
-def kernel_source_sha(name: str) -> str:
-    """sha256 prefix of a kernel source together with the library headers it includes."""
+def kernel_source_sha(name) -> str:
+    """sha256 prefix of a kernel source (or a list of them, in order) together
+    with the library headers each includes."""
     import hashlib
     import re
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc")
     h = hashlib.sha256()
-    with open(os.path.join(csrc, name), "rb") as f:
-        text = f.read()
-    h.update(text)
-    for inc in sorted(set(re.findall(rb'#include "([^"]+)"', text))):
-        path = os.path.join(csrc, inc.decode())
-        if os.path.exists(path):
-            with open(path, "rb") as f:
-                h.update(f.read())
+    for one in ([name] if isinstance(name, str) else name):
+        with open(os.path.join(csrc, one), "rb") as f:
+            text = f.read()
+        h.update(text)
+        for inc in sorted(set(re.findall(rb'#include "([^"]+)"', text))):
+            path = os.path.join(csrc, inc.decode())
+            if os.path.exists(path):
+                with open(path, "rb") as f:
+                    h.update(f.read())
     return h.hexdigest()[:16]
 
 
