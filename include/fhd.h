@@ -283,8 +283,10 @@ fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
  * lattice point) this equals fhd_compute on the grid x_i.
  *   nx, ny, nz : powers of two in [2, 1024]
  *   image      : fhd_c32[nz][ny][nx], overwritten; must not overlap the inputs
- * Deposits are float atomics: the result is not bitwise reproducible (the
- * rounding depends on the order in which samples land).  No workspace.
+ * The deposits are sorted by lattice plane (two entries of 20 bytes per
+ * sample, in scratch the call allocates and frees stream-ordered) and summed
+ * per tile of a plane with LDS atomics: the result is not bitwise
+ * reproducible (the rounding depends on the order in which entries land).
  */
 fhd_status fhd_gridding(const float* kx, const float* ky, const float* kz,
                         const fhd_c32* phi, const fhd_c32* D, int64_t M,

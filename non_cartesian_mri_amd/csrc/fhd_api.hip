@@ -840,10 +840,18 @@ NCMRI_API fhd_status fhd_gridding(const float* kx, const float* ky, const float*
       if (overlaps(outr, r)) return fail(FHD_ERR_INVALID_ARGUMENT, "image overlaps an input array");
     fhd_status st = check_device();
     if (st != FHD_OK) return st;
-    if (const char* e = ncmri::gridding_run(kx, ky, kz, (const float2*)phi, (const float2*)D, M, nx, ny, nz,
-                                            (float2*)image, (hipStream_t)stream))
-      return fail(FHD_ERR_HIP, "gridding: %s", e);
-    return FHD_OK;
+    hipStream_t s = (hipStream_t)stream;
+    void* scratch = nullptr;
+    const size_t sb = ncmri::gridding_scratch_bytes(M, nz);
+    hipError_t e = hipMallocAsync(&scratch, sb, s);
+    if (e != hipSuccess) return fail(FHD_ERR_HIP, "hipMallocAsync(%zu): %s", sb, hipGetErrorString(e));
+    fhd_status result = FHD_OK;
+    if (const char* m = ncmri::gridding_run(kx, ky, kz, (const float2*)phi, (const float2*)D, M, nx, ny, nz,
+                                            (float2*)image, scratch, s))
+      result = fail(FHD_ERR_HIP, "gridding: %s", m);
+    e = hipFreeAsync(scratch, s);
+    if (e != hipSuccess && result == FHD_OK) result = fail(FHD_ERR_HIP, "hipFreeAsync: %s", hipGetErrorString(e));
+    return result;
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
   }

@@ -77,8 +77,11 @@ hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z
 
 // Gridding reconstruction (fhd_grid.hip): image (complex [nz][ny][nx], each
 // axis a power of two in [2, kToeplitzMaxLen]) = the centred lattice inverse
-// DFT of the trilinearly gridded conj(phi) D.
+// DFT of the trilinearly gridded conj(phi) D.  scratch: gridding_scratch_bytes
+// (the sorted deposit entries, two per sample, and the per-plane counts),
+// 16-byte aligned.
+size_t gridding_scratch_bytes(int64_t M, int nz);
 const char* gridding_run(const float* kx, const float* ky, const float* kz, const float2* phi, const float2* D,
-                         int64_t M, int nx, int ny, int nz, float2* image, hipStream_t s);
+                         int64_t M, int nx, int ny, int nz, float2* image, void* scratch, hipStream_t s);
 
 }  // namespace ncmri

@@ -8,16 +8,29 @@
 // is periodic with period 1 (voxel coordinates are integers), so neighbours
 // wrap.  The image at voxel coordinates x_i = i - n/2 is then
 //
-//   image[i] = sum_j G[j] exp(+i 2 pi kappa_j . x_i)
-//            = s (-1)^(ix+iy+iz) IDFT( (-1)^(jx+jy+jz) G )[i],   s = prod_axes i^n,
+//   image[i] = sum_j G[j] exp(+i 2 pi kappa_j . x_i).
 //
-// an unnormalised inverse DFT of the sign-alternated lattice (the centring of
-// both index sets), run as three passes of the library's line FFTs in place
-// in the output.  Deposits are float atomics, so the rounding of a lattice
-// value depends on the order in which samples land (results are not
-// bitwise reproducible); the lattice position and weights are computed in
-// double from the float32 k, so every sample lands in the cells its exact
-// coordinate selects.
+// Per axis, (j - n/2)(i - n/2) = j i - (n/2)(i + j) + n^2/4, so the sum is
+// i^n (-1)^i IDFT((-1)^j G)[i], and multiplying an inverse DFT's output by
+// (-1)^i is the same as rolling its input by n/2; i^n (-1)^(n/2) = 1 for every
+// power of two n >= 2.  Hence
+//
+//   image = IDFT(L),   L[j'] = (-1)^(j'x + j'y + j'z) G[j' - n/2 (mod n, per axis)],
+//
+// an unnormalised inverse DFT of the rolled, sign-alternated lattice, run as
+// three passes of the library's line FFTs in place in the output.
+//
+// The spreading uses no global atomics (scattered float atomics run at a
+// fraction of the rate of scattered stores).  A counting sort lists every
+// (sample, z plane) deposit under its lattice plane: a sample lands on planes
+// jz and jz + 1 (mod nz), so it makes two entries, each holding the sample's
+// x / y cell, x / y fractions and Mu times its z weight.  Then one workgroup
+// per tile of TY rows of a plane (TY nx <= 4096 cells, 32 KB of LDS) adds the
+// entries of its plane that touch its rows into the tile with LDS atomics and
+// writes the tile once, rolled and sign-alternated into L.  The lattice cell and fractions come
+// from the float32 k in double, so every sample lands in the cells its exact
+// coordinate selects; the sums in LDS depend on the order in which the
+// entries land (results are not bitwise reproducible).
 #include "fhd.h"
 #include "fhd_cg.h"
 #include "fhd_lines.h"
@@ -26,12 +39,10 @@ namespace ncmri {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 4096;
-
-__global__ void __launch_bounds__(kThreads) zero_kernel(float2* __restrict__ a, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
-    a[i] = make_float2(0.0f, 0.0f);
-}
+constexpr int kBinSamples = 512;             // samples per binning block (2 per thread)
+constexpr int kPerThread = kBinSamples / kThreads;
+constexpr int kTileCells = 4096;             // lattice cells of a deposit tile
+constexpr int kMaxPlanes = kToeplitzMaxLen;  // nz <= 1024: one LDS counter per plane
 
 // Cell and fraction of coordinate k on an n-point lattice: u = k n + n/2,
 // cell = floor(u) mod n, fraction = u - floor(u).
@@ -43,76 +54,227 @@ __device__ __forceinline__ void lattice_cell(float k, int n, int& j, double& f) 
   j = (int)(c < 0 ? c + n : c);
 }
 
+__device__ __forceinline__ int z_cell(float k, int nz) {
+  int j;
+  double f;
+  lattice_cell(k, nz, j, f);
+  return j;
+}
+
+__global__ void __launch_bounds__(kThreads) clear_counts(unsigned* __restrict__ count, int nz) {
+  for (int b = threadIdx.x; b < nz; b += kThreads) count[b] = 0u;
+}
+
+// Entries per plane: an LDS histogram per block of kBinSamples samples, then
+// one global atomic per plane the block touches.
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const float* __restrict__ kz,
-               const float2* __restrict__ phi, const float2* __restrict__ D, int64_t M, int nx, int ny, int nz,
-               float2* __restrict__ G) {
-  float* g = reinterpret_cast<float*>(G);
-  for (int64_t m = (int64_t)blockIdx.x * kThreads + threadIdx.x; m < M; m += (int64_t)gridDim.x * kThreads) {
+count_kernel(const float* __restrict__ kz, int64_t M, int nz, unsigned* __restrict__ count) {
+  __shared__ unsigned hist[kMaxPlanes];
+  for (int b = threadIdx.x; b < nz; b += kThreads) hist[b] = 0u;
+  __syncthreads();
+  const int64_t m0 = (int64_t)blockIdx.x * kBinSamples;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int64_t m = m0 + k * kThreads + threadIdx.x;
+    if (m < M) {
+      const int jz = z_cell(kz[m], nz);
+      atomicAdd(&hist[jz], 1u);
+      atomicAdd(&hist[jz + 1 == nz ? 0 : jz + 1], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nz; b += kThreads)
+    if (hist[b]) atomicAdd(&count[b], hist[b]);
+}
+
+// start[b] = cursor[b] = sum of count[b'] over b' < b (one block; nz <= 1024).
+__global__ void __launch_bounds__(kThreads)
+scan_kernel(const unsigned* __restrict__ count, unsigned* __restrict__ start, unsigned* __restrict__ cursor,
+            int nz) {
+  __shared__ unsigned part[kThreads];
+  constexpr int kPer = kMaxPlanes / kThreads;   // planes per thread
+  unsigned v[kPer], run = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = threadIdx.x * kPer + i;
+    v[i] = b < nz ? count[b] : 0u;
+    run += v[i];
+  }
+  part[threadIdx.x] = run;
+  __syncthreads();
+  // inclusive scan of the per-thread totals (Hillis-Steele)
+  for (int d = 1; d < kThreads; d *= 2) {
+    const unsigned add = (int)threadIdx.x >= d ? part[threadIdx.x - d] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  unsigned base = part[threadIdx.x] - run;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = threadIdx.x * kPer + i;
+    if (b < nz) {
+      start[b] = base;
+      cursor[b] = base;
+    }
+    base += v[i];
+  }
+}
+
+// The entries: each block ranks its samples per plane in LDS, reserves one
+// range per plane with a global atomic, and writes (cell, fractions, value).
+// cell = jx | jy << 16; val = (fx, fy, Re, Im of Mu times the z weight).
+__global__ void __launch_bounds__(kThreads)
+fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const float* __restrict__ kz,
+            const float2* __restrict__ phi, const float2* __restrict__ D, int64_t M, int nx, int ny, int nz,
+            unsigned* __restrict__ cursor, unsigned* __restrict__ cell, float4* __restrict__ val) {
+  __shared__ unsigned hist[kMaxPlanes];
+  __shared__ unsigned base[kMaxPlanes];
+  for (int b = threadIdx.x; b < nz; b += kThreads) hist[b] = 0u;
+  __syncthreads();
+  const int64_t m0 = (int64_t)blockIdx.x * kBinSamples;
+  int jz[kPerThread];
+  unsigned r0[kPerThread], r1[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int64_t m = m0 + k * kThreads + threadIdx.x;
+    jz[k] = 0;
+    r0[k] = r1[k] = 0u;
+    if (m < M) {
+      jz[k] = z_cell(kz[m], nz);
+      r0[k] = atomicAdd(&hist[jz[k]], 1u);
+      r1[k] = atomicAdd(&hist[jz[k] + 1 == nz ? 0 : jz[k] + 1], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nz; b += kThreads)
+    if (hist[b]) base[b] = atomicAdd(&cursor[b], hist[b]);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int64_t m = m0 + k * kThreads + threadIdx.x;
+    if (m >= M) continue;
     const float2 p = phi[m], d = D[m];
     // conj(phi) D
     const float mr = __builtin_fmaf(p.x, d.x, p.y * d.y);
     const float mi = __builtin_fmaf(p.x, d.y, -(p.y * d.x));
-    int jx, jy, jz;
+    int jx, jy, jzz;
     double fx, fy, fz;
     lattice_cell(kx[m], nx, jx, fx);
     lattice_cell(ky[m], ny, jy, fy);
-    lattice_cell(kz[m], nz, jz, fz);
-#pragma unroll
-    for (int dz = 0; dz < 2; ++dz) {
-      const int cz = jz + dz == nz ? 0 : jz + dz;
-      const double wz = dz ? fz : 1.0 - fz;
-#pragma unroll
-      for (int dy = 0; dy < 2; ++dy) {
-        const int cy = jy + dy == ny ? 0 : jy + dy;
-        const double wy = dy ? fy : 1.0 - fy;
-#pragma unroll
-        for (int dx = 0; dx < 2; ++dx) {
-          const int cx = jx + dx == nx ? 0 : jx + dx;
-          const double wx = dx ? fx : 1.0 - fx;
-          float w = (float)(wx * wy * wz);
-          if ((cx + cy + cz) & 1) w = -w;
-          const int64_t idx = ((int64_t)cz * ny + cy) * nx + cx;
-          unsafeAtomicAdd(g + 2 * idx, w * mr);
-          unsafeAtomicAdd(g + 2 * idx + 1, w * mi);
-        }
-      }
-    }
+    lattice_cell(kz[m], nz, jzz, fz);
+    const unsigned c = (unsigned)jx | ((unsigned)jy << 16);
+    const float w0 = (float)(1.0 - fz), w1 = (float)fz;
+    const unsigned e0 = base[jz[k]] + r0[k];
+    const unsigned e1 = base[jz[k] + 1 == nz ? 0 : jz[k] + 1] + r1[k];
+    cell[e0] = c;
+    val[e0] = make_float4((float)fx, (float)fy, w0 * mr, w0 * mi);
+    cell[e1] = c;
+    val[e1] = make_float4((float)fx, (float)fy, w1 * mr, w1 * mi);
   }
 }
 
-// image[i] *= s (-1)^(ix+iy+iz)
-__global__ void __launch_bounds__(kThreads)
-sign_kernel(float2* __restrict__ a, int nx, int ny, int nz, float s) {
-  const int64_t n = (int64_t)nx * ny * nz;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const int ix = (int)(i % nx), iy = (int)((i / nx) % ny), iz = (int)(i / ((int64_t)nx * ny));
-    const float f = ((ix + iy + iz) & 1) ? -s : s;
-    const float2 v = a[i];
-    a[i] = make_float2(v.x * f, v.y * f);
+// One tile: rows [row0, row0 + TY) of plane z.  The plane's entries that touch
+// those rows go into LDS with LDS atomics; the tile is then written once into
+// L: cell (x, y, z) to ((x, y, z) + n/2 mod n), times (-1) to the sum of the
+// new coordinates.
+constexpr int kDepositThreads = 1024;
+
+__device__ __forceinline__ void deposit_entry(float* t, unsigned c, const float4& f, int nx, int ny, int ty,
+                                              int row0) {
+  const int jx = (int)(c & 0xffffu), jy = (int)(c >> 16);
+  const int ra = jy - row0, rb = (jy + 1 == ny ? 0 : jy + 1) - row0;
+  const int xb = jx + 1 == nx ? 0 : jx + 1;
+  const float wx0 = 1.0f - f.x, wx1 = f.x;
+  if ((unsigned)ra < (unsigned)ty) {
+    const float wy = 1.0f - f.y;
+    const float a = wx0 * wy, b = wx1 * wy;
+    atomicAdd(&t[2 * (ra * nx + jx)], a * f.z);
+    atomicAdd(&t[2 * (ra * nx + jx) + 1], a * f.w);
+    atomicAdd(&t[2 * (ra * nx + xb)], b * f.z);
+    atomicAdd(&t[2 * (ra * nx + xb) + 1], b * f.w);
+  }
+  if ((unsigned)rb < (unsigned)ty) {
+    const float wy = f.y;
+    const float a = wx0 * wy, b = wx1 * wy;
+    atomicAdd(&t[2 * (rb * nx + jx)], a * f.z);
+    atomicAdd(&t[2 * (rb * nx + jx) + 1], a * f.w);
+    atomicAdd(&t[2 * (rb * nx + xb)], b * f.z);
+    atomicAdd(&t[2 * (rb * nx + xb) + 1], b * f.w);
   }
 }
 
-int blocks(int64_t n) {
-  const int64_t b = (n + kThreads - 1) / kThreads;
-  return (int)(b < kMaxBlocks ? (b > 0 ? b : 1) : kMaxBlocks);
+__global__ void __launch_bounds__(kDepositThreads)
+deposit_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ count,
+               const unsigned* __restrict__ cell, const float4* __restrict__ val, int nx, int lx, int ny, int nz,
+               int ty, float2* __restrict__ L) {
+  __shared__ float2 tile[kTileCells];
+  // plane = block mod nz, tile = block div nz: blocks go to the 8 XCDs in
+  // turn, so every XCD gets every tile index (the middle rows of a plane
+  // usually hold most of the samples)
+  const int z = (int)(blockIdx.x % (unsigned)nz), row0 = (int)(blockIdx.x / (unsigned)nz) * ty;
+  const int cells = ty * nx;
+  for (int i = threadIdx.x; i < cells; i += kDepositThreads) tile[i] = make_float2(0.0f, 0.0f);
+  __syncthreads();
+  float* t = reinterpret_cast<float*>(tile);
+  const unsigned e0 = start[z], e1 = e0 + count[z];
+  // two entries per thread and trip, so two loads are in flight
+  unsigned e = e0 + threadIdx.x;
+  for (; (int64_t)e + kDepositThreads < (int64_t)e1; e += 2 * kDepositThreads) {
+    const unsigned ca = cell[e], cb = cell[e + kDepositThreads];
+    const float4 fa = val[e], fb = val[e + kDepositThreads];
+    deposit_entry(t, ca, fa, nx, ny, ty, row0);
+    deposit_entry(t, cb, fb, nx, ny, ty, row0);
+  }
+  if (e < e1) deposit_entry(t, cell[e], val[e], nx, ny, ty, row0);
+  __syncthreads();
+  const int zr = (z + nz / 2) & (nz - 1);
+  for (int i = threadIdx.x; i < cells; i += kDepositThreads) {
+    const int y = i >> lx, x = i & (nx - 1);
+    const int yr = (row0 + y + ny / 2) & (ny - 1), xr = (x + nx / 2) & (nx - 1);
+    const float2 v = tile[i];
+    L[((int64_t)zr * ny + yr) * nx + xr] = ((xr + yr + zr) & 1) ? make_float2(-v.x, -v.y) : v;
+  }
 }
-
-// i^n for a power of two n >= 2: -1 for n = 2, +1 otherwise
-float quarter_power(int n) { return n % 4 == 0 ? 1.0f : -1.0f; }
 
 }  // namespace
 
+size_t gridding_scratch_bytes(int64_t M, int nz) {
+  const size_t entries = 2 * (size_t)M;
+  return entries * sizeof(float4) + cg_align(entries * sizeof(unsigned)) + 3 * cg_align((size_t)nz * sizeof(unsigned));
+}
+
 const char* gridding_run(const float* kx, const float* ky, const float* kz, const float2* phi, const float2* D,
-                         int64_t M, int nx, int ny, int nz, float2* image, hipStream_t s) {
-  const int64_t n = (int64_t)nx * ny * nz;
-  hipLaunchKernelGGL(zero_kernel, dim3(blocks(n)), dim3(kThreads), 0, s, image, n);
-  if (hipGetLastError() != hipSuccess) return "zero kernel launch failed";
+                         int64_t M, int nx, int ny, int nz, float2* image, void* scratch, hipStream_t s) {
+  if (nx > 0xffff || ny > 0xffff || nz > kMaxPlanes || M < 0 || 2 * M > (int64_t)0xffffffffLL)
+    return "gridding sizes out of range";
+  const size_t entries = 2 * (size_t)M;
+  char* c = (char*)scratch;
+  float4* val = (float4*)c;            c += entries * sizeof(float4);
+  unsigned* cell = (unsigned*)c;       c += cg_align(entries * sizeof(unsigned));
+  unsigned* count = (unsigned*)c;      c += cg_align((size_t)nz * sizeof(unsigned));
+  unsigned* start = (unsigned*)c;      c += cg_align((size_t)nz * sizeof(unsigned));
+  unsigned* cursor = (unsigned*)c;
+  hipLaunchKernelGGL(clear_counts, dim3(1), dim3(kThreads), 0, s, count, nz);
+  if (hipGetLastError() != hipSuccess) return "clear kernel launch failed";
+  const int64_t bins = (M + kBinSamples - 1) / kBinSamples;
   if (M > 0) {
-    hipLaunchKernelGGL(scatter_kernel, dim3(blocks(M)), dim3(kThreads), 0, s, kx, ky, kz, phi, D, M, nx, ny, nz,
-                       image);
-    if (hipGetLastError() != hipSuccess) return "scatter kernel launch failed";
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)bins), dim3(kThreads), 0, s, kz, M, nz, count);
+    if (hipGetLastError() != hipSuccess) return "count kernel launch failed";
   }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, count, start, cursor, nz);
+  if (hipGetLastError() != hipSuccess) return "scan kernel launch failed";
+  if (M > 0) {
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)bins), dim3(kThreads), 0, s, kx, ky, kz, phi, D, M, nx, ny, nz,
+                       cursor, cell, val);
+    if (hipGetLastError() != hipSuccess) return "fill kernel launch failed";
+  }
+  const int ty = ny < kTileCells / nx ? ny : kTileCells / nx;   // powers of two: ty divides ny
+  int lx = 0;
+  while ((1 << lx) < nx) ++lx;
+  hipLaunchKernelGGL(deposit_kernel, dim3((unsigned)((int64_t)nz * (ny / ty))), dim3(kDepositThreads), 0, s, start,
+                     count, cell, val, nx, lx, ny, nz, ty, image);
+  if (hipGetLastError() != hipSuccess) return "deposit kernel launch failed";
   const int64_t plane = (int64_t)nx * ny;
   if (launch_lines(true, kLineInv, nx, line_pass(image, image, (int64_t)nz * ny, 1, nx, 0, 1, nx, nx), s) !=
       hipSuccess)
@@ -122,9 +284,6 @@ const char* gridding_run(const float* kx, const float* ky, const float* kz, cons
     return "y transform launch failed";
   if (launch_lines(false, kLineInv, nz, line_pass(image, image, plane, 1, 1, 0, plane, nz, nz), s) != hipSuccess)
     return "z transform launch failed";
-  const float sg = quarter_power(nx) * quarter_power(ny) * quarter_power(nz);
-  hipLaunchKernelGGL(sign_kernel, dim3(blocks(n)), dim3(kThreads), 0, s, image, nx, ny, nz, sg);
-  if (hipGetLastError() != hipSuccess) return "sign kernel launch failed";
   return nullptr;
 }
 
