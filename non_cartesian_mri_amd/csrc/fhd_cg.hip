@@ -119,7 +119,7 @@ template <int N>
 __global__ void __launch_bounds__(fft::kThreads)
 crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, float2* __restrict__ Ap,
             int nx, int ny, int nz, float lambda, double* __restrict__ partial) {
-  using L = fft::Lds<N, true>;
+  using L = fft::Lds<N, fft::kRows>;
   using S = fft::Sched<N>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
@@ -134,12 +134,12 @@ crop_kernel(const float2* __restrict__ T, int py, const float2* __restrict__ p, 
   for (int g = blockIdx.x; g < groups; g += gridDim.x) {
     const int c0 = g * L::kLines;
     float2 v[fft::kPerThread];
-    fft::transform<N, true, true, false, false>(TRows{T, c0, count, ny, py, N}, buf, tw, v);
+    fft::transform<N, fft::kRows, true, false, false>(TRows{T, c0, count, ny, py, N}, buf, tw, v);
     // the last stage's outputs: point j + r kStep of line c0 + l
 #pragma unroll
     for (int k = 0; k < fft::kPerThread / RL; ++k) {
       int l, j;
-      fft::locate<N, RL, true>(k, l, j);
+      fft::locate<N, RL, fft::kRows>(k, l, j);
       const int c = c0 + l;
       if (c >= count) continue;
       const int z = c / ny, y = c - z * ny;

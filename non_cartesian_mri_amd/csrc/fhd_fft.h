@@ -1,7 +1,7 @@
 // Batched power-of-two FFTs of lines (gfx950), for the Toeplitz normal
 // operator and the gridding reconstruction.
 //
-// A workgroup transforms Lds<N, ROW>::kLines lines of N points (N = 2^p,
+// A workgroup transforms Lds<N, LAY>::kLines lines of N points (N = 2^p,
 // 2 <= N <= 1024); every thread holds 16 complex values per stage, so the
 // register footprint does not depend on N.  The transform is the
 // self-sorting (Stockham) formulation: stage s with radix R combines R
@@ -39,7 +39,12 @@
 //             adjacent columns in memory (y, z axes), at least 16 columns
 //             (128 bytes) per workgroup so that every row of the tile is one
 //             full cache line: 4096 values (256 threads) up to N = 256, 16 N
-//             values (N threads) beyond.
+//             values (N threads) beyond;
+//   narrow column -- 8 columns (64-byte rows, 8 N values, N / 2 threads) and
+//             no pad, for N = 1024: 64 KB, so that two workgroups fit a CU's
+//             LDS (the fused spectral-product pass, where overlapping one
+//             workgroup's loads with another's transforms pays more than
+//             full-line rows).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,13 +60,18 @@ constexpr int kMaxLen = 1024;
 
 __host__ __device__ constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
-template <int N, bool ROW>
+// LDS layouts (template parameter LAY of the helpers below)
+enum Layout { kRows = 0, kCols = 1, kColsNarrow = 2 };
+
+template <int N, int LAY>
 struct Lds {
-  static constexpr int kElems = ROW ? 4096 : (16 * N > 4096 ? 16 * N : 4096);  // values per workgroup
+  static constexpr bool ROW = LAY == kRows;
+  static constexpr int kColLines = LAY == kColsNarrow ? 8 : (N > 256 ? 16 : 4096 / N);
+  static constexpr int kElems = ROW ? 4096 : kColLines * N;  // values per workgroup
   static constexpr int kThreads = kElems / kPerThread;
   static constexpr int kLines = kElems / N;
   static constexpr int kRowPitch = N >= 32 ? N + 16 : N;
-  static constexpr int kColPitch = kLines + 1;
+  static constexpr int kColPitch = LAY == kColsNarrow ? kLines : kLines + 1;
   static constexpr int kSize = ROW ? kLines * kRowPitch : N * kColPitch;
   __device__ static __forceinline__ int addr(int l, int i) {
     if constexpr (ROW) {
@@ -95,12 +105,12 @@ struct Sched {
 // Butterfly k (< 16 / R) of this thread in a radix-R stage: line l of the
 // workgroup and butterfly j < N / R of that line.  Column tiles give
 // consecutive threads consecutive lines, row tiles consecutive butterflies.
-template <int N, int R, bool ROW>
+template <int N, int R, int LAY>
 __device__ __forceinline__ void locate(int k, int& l, int& j) {
-  using L = Lds<N, ROW>;
+  using L = Lds<N, LAY>;
   constexpr unsigned kBf = N / R;
   const unsigned b = threadIdx.x + (unsigned)(k * L::kThreads);
-  if constexpr (ROW) {
+  if constexpr (L::ROW) {
     l = (int)(b / kBf);
     j = (int)(b % kBf);
   } else {
@@ -171,14 +181,14 @@ __device__ __forceinline__ void dft_all(float2* v) {
 }
 
 // Stage inputs from LDS, twiddled.
-template <int N, int R, int NS, bool ROW, bool INV>
+template <int N, int R, int NS, int LAY, bool INV>
 __device__ __forceinline__ void read_stage(const float2* buf, const float2* tw, float2* v) {
-  using L = Lds<N, ROW>;
+  using L = Lds<N, LAY>;
   constexpr int kBf = N / R;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
-    locate<N, R, ROW>(k, l, j);
+    locate<N, R, LAY>(k, l, j);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float2 a = buf[L::addr(l, j + r * kBf)];
@@ -193,13 +203,13 @@ __device__ __forceinline__ void read_stage(const float2* buf, const float2* tw, 
 }
 
 // Stage outputs to LDS.
-template <int N, int R, int NS, bool ROW>
+template <int N, int R, int NS, int LAY>
 __device__ __forceinline__ void write_stage(float2* buf, const float2* v) {
-  using L = Lds<N, ROW>;
+  using L = Lds<N, LAY>;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
-    locate<N, R, ROW>(k, l, j);
+    locate<N, R, LAY>(k, l, j);
     const int d = (j / NS) * NS * R + (j % NS);
 #pragma unroll
     for (int r = 0; r < R; ++r) buf[L::addr(l, d + r * NS)] = v[k * R + r];
@@ -209,18 +219,18 @@ __device__ __forceinline__ void write_stage(float2* buf, const float2* v) {
 // Stages S .. last through LDS.  On entry v holds the outputs of stage S - 1
 // (after its DFTs), on exit those of the last stage.  Starts with a barrier,
 // so the buffer may still be read by earlier code, and ends without one.
-template <int N, bool ROW, bool INV, bool DESC, int S = 1>
+template <int N, int LAY, bool INV, bool DESC, int S = 1>
 __device__ __forceinline__ void through_lds(float2* buf, const float2* tw, float2* v) {
   using Sc = Sched<N>;
   if constexpr (S < Sc::kStages) {
     constexpr int Rp = Sc::radix(S - 1, DESC), NSp = Sc::ns(S - 1, DESC);
     constexpr int R = Sc::radix(S, DESC), NS = Sc::ns(S, DESC);
     __syncthreads();
-    write_stage<N, Rp, NSp, ROW>(buf, v);
+    write_stage<N, Rp, NSp, LAY>(buf, v);
     __syncthreads();
-    read_stage<N, R, NS, ROW, INV>(buf, tw, v);
+    read_stage<N, R, NS, LAY, INV>(buf, tw, v);
     dft_all<R, INV>(v);
-    through_lds<N, ROW, INV, DESC, S + 1>(buf, tw, v);
+    through_lds<N, LAY, INV, DESC, S + 1>(buf, tw, v);
   }
 }
 
@@ -228,14 +238,14 @@ __device__ __forceinline__ void through_lds(float2* buf, const float2* tw, float
 // load.template get<RN, STEP>(l, j, w) fills w[r], r < RN, with point
 // j + r STEP of line l.  HALF_IN: the points from N/2 on are zero, which are
 // inputs r >= R/2 of every butterfly (j < N/R), so only RN = R/2 are read.
-template <int N, bool ROW, bool INV, bool DESC, bool HALF_IN, class Load>
+template <int N, int LAY, bool INV, bool DESC, bool HALF_IN, class Load>
 __device__ __forceinline__ void first_stage(const Load& load, float2* v) {
   constexpr int R = Sched<N>::first(DESC);
   constexpr int RN = HALF_IN ? R / 2 : R;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
-    locate<N, R, ROW>(k, l, j);
+    locate<N, R, LAY>(k, l, j);
     load.template get<RN, N / R>(l, j, v + k * R);
   }
   dft_all<R, INV, HALF_IN>(v);
@@ -245,24 +255,24 @@ __device__ __forceinline__ void first_stage(const Load& load, float2* v) {
 // the workgroup's lines: inputs from `load` (as in first_stage), outputs of
 // the last stage left in v (see last_stage).  The twiddle table may be
 // filled just before the call: the barriers of the LDS exchanges order it.
-template <int N, bool ROW, bool INV, bool DESC, bool HALF_IN, class Load>
+template <int N, int LAY, bool INV, bool DESC, bool HALF_IN, class Load>
 __device__ __forceinline__ void transform(const Load& load, float2* buf, const float2* tw, float2* v) {
-  first_stage<N, ROW, INV, DESC, HALF_IN>(load, v);
-  through_lds<N, ROW, INV, DESC>(buf, tw, v);
+  first_stage<N, LAY, INV, DESC, HALF_IN>(load, v);
+  through_lds<N, LAY, INV, DESC>(buf, tw, v);
 }
 
 // The last stage's outputs to the caller: store.template put<RN, STEP>(l, j, w)
 // takes w[r], r < RN, as point j + r STEP of line l.  HALF_OUT: only the
 // points below N/2 are wanted, outputs r < R/2 of every butterfly (the
 // computation of the others is then dead code).
-template <int N, bool ROW, bool DESC, bool HALF_OUT, class Store>
+template <int N, int LAY, bool DESC, bool HALF_OUT, class Store>
 __device__ __forceinline__ void last_stage(const Store& store, const float2* v) {
   constexpr int R = Sched<N>::last(DESC);
   constexpr int RN = HALF_OUT ? R / 2 : R;
 #pragma unroll
   for (int k = 0; k < kPerThread / R; ++k) {
     int l, j;
-    locate<N, R, ROW>(k, l, j);
+    locate<N, R, LAY>(k, l, j);
     store.template put<RN, N / R>(l, j, v + k * R);
   }
 }

@@ -1,5 +1,5 @@
 // Batched line transforms over one axis of a 3-D array (see fhd_lines.h).
-// A workgroup takes Lds<N, ROW>::kLines lines (zero-extending past nin
+// A workgroup takes Lds<N, LAY>::kLines lines (zero-extending past nin
 // points) straight from global memory into the first stage of the
 // transforms of fhd_fft.h (forward, inverse, or forward then the product
 // with a real spectrum then inverse, chained in registers) and stores the
@@ -61,22 +61,51 @@ struct LineStore {
 // PRUNE: bit 0 -- nin <= N/2, bit 1 -- nout <= N/2.
 enum { kPruneIn = 1, kPruneOut = 2 };
 
-// Tile of block b in the spectral-product pass.  Workgroups go to the 8 XCDs
-// in turn (block b to XCD b mod 8), each with its own L2; tiles 2k and 2k+1
-// read the two halves of the same 128-byte lines of the real spectrum (16
-// floats per row each), so they are given blocks 16m + i and 16m + i + 8,
-// which share an XCD.  The grid is a multiple of 16 blocks.
-__device__ __forceinline__ int paired_tile(int b) { return (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1); }
+// Tile of block b when G consecutive column tiles share 128-byte lines (G = 2:
+// 64-byte rows of complex values or of 16 spectrum floats; G = 4: 32-byte
+// rows of 8 spectrum floats).  Workgroups go to the 8 XCDs in turn (block b
+// to XCD b mod 8), each with its own L2, so tiles Gk .. Gk + G - 1 are given
+// blocks 8Gm + i + 8q (q < G), which share an XCD.  The grid is a multiple of
+// 8G blocks.
+template <int G>
+__device__ __forceinline__ int grouped_tile(int b) {
+  if constexpr (G == 1) {
+    return b;
+  } else {
+    return (b / (8 * G)) * (8 * G) + (b % 8) * G + (b / 8) % G;
+  }
+}
+
+// LDS layout of a pass: rows, or column tiles (narrow ones for the 1024-point
+// spectral product, see fhd_fft.h).
+template <int N, bool ROW, int MODE>
+constexpr int layout() {
+  return ROW ? fft::kRows : (MODE == kLineFwdQInv && N >= 1024 ? fft::kColsNarrow : fft::kCols);
+}
+
+// Tiles per line-sharing group: complex rows need 16 columns per 128-byte
+// line, spectrum rows (the product pass) 32.
+template <int N, bool ROW, int MODE>
+constexpr int tile_group() {
+  if constexpr (ROW) {
+    return 1;
+  } else {
+    constexpr int lines = fft::Lds<N, layout<N, ROW, MODE>()>::kLines;
+    constexpr int per = MODE == kLineFwdQInv ? 32 : 16;
+    return lines >= per ? 1 : per / lines;
+  }
+}
 
 template <int N, bool ROW, int MODE, int PRUNE>
-__global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(LinePass a) {
+__global__ void __launch_bounds__((fft::Lds<N, layout<N, ROW, MODE>()>::kThreads)) line_fft_kernel(LinePass a) {
   constexpr bool kHalfIn = (PRUNE & kPruneIn) != 0, kHalfOut = (PRUNE & kPruneOut) != 0;
-  using L = fft::Lds<N, ROW>;
+  constexpr int LAY = layout<N, ROW, MODE>();
+  using L = fft::Lds<N, LAY>;
   using S = fft::Sched<N>;
   __shared__ float2 buf[L::kSize];
   __shared__ float2 tw[N];
   fft::fill_twiddles<N>(tw);
-  const int tile = MODE == kLineFwdQInv ? paired_tile(blockIdx.x) : (int)blockIdx.x;
+  const int tile = grouped_tile<tile_group<N, ROW, MODE>()>((int)blockIdx.x);
   const int c0 = tile * L::kLines;   // past the last line (padding blocks): nothing read or written
   const LineLoad load{a.in, c0, a.count, a.inner, a.nin, a.in_os, a.in_ws, a.in_es};
   const LineStore store{a.out, c0, a.count, a.inner, a.nout, a.out_os, a.out_ws, a.out_es};
@@ -93,7 +122,7 @@ __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(
 #pragma unroll
       for (int k = 0; k < fft::kPerThread / RL; ++k) {
         int l, j;
-        fft::locate<N, RL, false>(k, l, j);
+        fft::locate<N, RL, LAY>(k, l, j);
         const int c = c0 + l;
         const float* qp = a.q + (c + (int64_t)j * a.q_es);
         const int64_t qst = (int64_t)kStep * a.q_es;
@@ -106,27 +135,28 @@ __global__ void __launch_bounds__((fft::Lds<N, ROW>::kThreads)) line_fft_kernel(
     };
     constexpr bool kPrefetchQ = L::kThreads <= 512;
     if constexpr (kPrefetchQ) load_q();
-    fft::transform<N, false, false, false, kHalfIn>(load, buf, tw, v);
+    fft::transform<N, LAY, false, false, kHalfIn>(load, buf, tw, v);
     if constexpr (!kPrefetchQ) load_q();
 #pragma unroll
     for (int i = 0; i < fft::kPerThread; ++i) v[i] = make_float2(v[i].x * qv[i], v[i].y * qv[i]);
     fft::dft_all<S::first(true), true>(v);
-    fft::through_lds<N, false, true, true>(buf, tw, v);
-    fft::last_stage<N, false, true, kHalfOut>(store, v);
+    fft::through_lds<N, LAY, true, true>(buf, tw, v);
+    fft::last_stage<N, LAY, true, kHalfOut>(store, v);
   } else {
-    fft::transform<N, ROW, MODE == kLineInv, false, kHalfIn>(load, buf, tw, v);
-    fft::last_stage<N, ROW, false, kHalfOut>(store, v);
+    fft::transform<N, LAY, MODE == kLineInv, false, kHalfIn>(load, buf, tw, v);
+    fft::last_stage<N, LAY, false, kHalfOut>(store, v);
   }
 }
 
 template <int N, bool ROW, int MODE, int PRUNE>
 hipError_t launch_grid(const LinePass& a, hipStream_t s) {
-  constexpr int lines = fft::Lds<N, ROW>::kLines;
+  using L = fft::Lds<N, layout<N, ROW, MODE>()>;
+  constexpr int lines = L::kLines;
   int grid = (a.count + lines - 1) / lines;
   if (grid == 0) return hipSuccess;
-  if (MODE == kLineFwdQInv) grid = (grid + 15) / 16 * 16;   // whole groups for paired_tile
-  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE, PRUNE>), dim3(grid), dim3(fft::Lds<N, ROW>::kThreads), 0, s,
-                     a);
+  constexpr int kGroup = 8 * tile_group<N, ROW, MODE>();
+  grid = (grid + kGroup - 1) / kGroup * kGroup;   // whole groups for grouped_tile
+  hipLaunchKernelGGL((line_fft_kernel<N, ROW, MODE, PRUNE>), dim3(grid), dim3(L::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
