@@ -260,19 +260,55 @@ step_kernel(float2* __restrict__ x, float2* __restrict__ r, const float2* __rest
   if (threadIdx.x == 0) rr_partial[blockIdx.x] = s;
 }
 
-// beta = <r, r>_new / <r, r>_old (every wave sums the partials itself, while
-// its first elements load); p = r + beta p; the new <r, r> goes to the other
-// slot (and to *resid).
-__global__ void __launch_bounds__(kThreads)
-direction_kernel(const float2* __restrict__ r, float2* __restrict__ pv, int64_t n, double* __restrict__ state,
-                 int slot, const double* __restrict__ rr_partial, double* __restrict__ resid) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  float2 rv{}, p{};
-  if (i < n) {
-    rv = r[i];
-    p = pv[i];
+// Sum of the partials into *out (the <r, r> after the last iteration).
+__global__ void __launch_bounds__(kThreads) store_sum_kernel(const double* __restrict__ partial, double* __restrict__ out) {
+  const double s = sum_partials(partial);
+  if (threadIdx.x == 0) *out = s;
+}
+
+// Rows (z < nz, y < ny) of the new direction p = r + beta p as the first
+// stage's inputs of the x transform: each point is read, updated, written
+// back to p and handed to the transform exactly once.
+struct DirRows {
+  const float2* r;
+  float2* p;
+  float beta;
+  int c0, count, nx;
+  template <int RN, int STEP>
+  __device__ __forceinline__ void get(int l, int j, float2* w) const {
+    const int c = c0 + l;
+    const bool ok = c < count;
+    const int64_t base = (int64_t)(ok ? c : 0) * nx;
+#pragma unroll
+    for (int q = 0; q < RN; ++q) {
+      const int i = j + q * STEP;
+      float2 v = make_float2(0.0f, 0.0f);
+      if (ok && i < nx) {
+        const float2 rv = r[base + i], pv = p[base + i];
+        v = make_float2(__builtin_fmaf(beta, pv.x, rv.x), __builtin_fmaf(beta, pv.y, rv.y));
+        p[base + i] = v;
+      }
+      w[q] = v;
+    }
   }
+};
+
+// First pass of a CG iteration after the first: beta = <r, r>_new / <r, r>_old
+// from the step's partials (every wave sums them itself, as in
+// step_kernel), p = r + beta p on the rows (z < nz, y < ny), and the
+// zero-extended forward transforms of those rows -> rows of T.  The new
+// <r, r> goes to the other state slot (and to *resid).  Launched on
+// ceil(nz ny / lines) blocks.
+template <int N>
+__global__ void __launch_bounds__(fft::kThreads)
+direction_x_kernel(const float2* __restrict__ r, float2* __restrict__ pv, float2* __restrict__ T, int nx, int ny,
+                   int nz, int py, double* __restrict__ state, int slot, const double* __restrict__ rr_partial,
+                   double* __restrict__ resid) {
+  using L = fft::Lds<N, fft::kRows>;
+  using S = fft::Sched<N>;
+  __shared__ float2 buf[L::kSize];
+  __shared__ float2 tw[N];
+  fft::fill_twiddles<N>(tw);
   const double rs_new = sum_partials(rr_partial);
   const double rs = state[RS0 + slot];
   const double beta_d = rs != 0.0 ? rs_new / rs : 0.0;
@@ -281,14 +317,22 @@ direction_kernel(const float2* __restrict__ r, float2* __restrict__ pv, int64_t 
     state[RS0 + (slot ^ 1)] = rs_new;
     if (resid) *resid = rs_new;
   }
-  const float beta = (float)beta_d;
-  while (i < n) {
-    pv[i] = make_float2(__builtin_fmaf(beta, p.x, rv.x), __builtin_fmaf(beta, p.y, rv.y));
-    i += stride;
-    if (i < n) {
-      rv = r[i];
-      p = pv[i];
-    }
+  const int count = ny * nz;
+  const int c0 = blockIdx.x * L::kLines;
+  float2 v[fft::kPerThread];
+  // nx <= N / 2: the inputs from N/2 on are zero
+  fft::transform<N, fft::kRows, false, false, true>(DirRows{r, pv, (float)beta_d, c0, count, nx}, buf, tw, v);
+  constexpr int RL = S::last(false), kStep = N / RL;
+#pragma unroll
+  for (int k = 0; k < fft::kPerThread / RL; ++k) {
+    int l, j;
+    fft::locate<N, RL, fft::kRows>(k, l, j);
+    const int c = c0 + l;
+    if (c >= count) continue;
+    const int z = c / ny, y = c - z * ny;
+    float2* t = T + (((int64_t)z * py + y) * N + j);
+#pragma unroll
+    for (int q = 0; q < RL; ++q) t[q * kStep] = v[k * RL + q];
   }
 }
 
@@ -303,6 +347,34 @@ hipError_t launch_crop_n(const ToeplitzDims& d, const float2* T, const float2* p
   hipLaunchKernelGGL(crop_kernel<N>, dim3(kBlocks), dim3(fft::kThreads), 0, s, T, d.py, p, Ap, d.nx, d.ny, d.nz,
                      lambda, partial);
   return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_direction_x_n(const ToeplitzDims& d, const float2* r, float2* p, float2* T, double* state, int slot,
+                                const double* rr_partial, double* resid, hipStream_t s) {
+  constexpr int lines = fft::Lds<N, fft::kRows>::kLines;
+  const int64_t count = (int64_t)d.ny * d.nz;
+  hipLaunchKernelGGL(direction_x_kernel<N>, dim3((unsigned)((count + lines - 1) / lines)), dim3(fft::kThreads), 0, s,
+                     r, p, T, d.nx, d.ny, d.nz, d.py, state, slot, rr_partial, resid);
+  return hipGetLastError();
+}
+
+hipError_t launch_direction_x(const ToeplitzDims& d, const float2* r, float2* p, float2* T, double* state, int slot,
+                              const double* rr_partial, double* resid, hipStream_t s) {
+  if (2 * d.nx > d.px) return hipErrorInvalidValue;   // the transform reads the first half of each row only
+  switch (d.px) {
+    case 2: return launch_direction_x_n<2>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 4: return launch_direction_x_n<4>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 8: return launch_direction_x_n<8>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 16: return launch_direction_x_n<16>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 32: return launch_direction_x_n<32>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 64: return launch_direction_x_n<64>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 128: return launch_direction_x_n<128>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 256: return launch_direction_x_n<256>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 512: return launch_direction_x_n<512>(d, r, p, T, state, slot, rr_partial, resid, s);
+    case 1024: return launch_direction_x_n<1024>(d, r, p, T, state, slot, rr_partial, resid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_crop(const ToeplitzDims& d, const float2* T, const float2* p, float2* Ap, float lambda,
@@ -352,16 +424,12 @@ const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G
 }
 
 // Ap = F^H F p + lambda W^H W p (and the <p, Ap> partials when `partial`).
-const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p, float2* Ap,
-                         float2* T, double* partial, hipStream_t s) {
+namespace {
+
+// Passes 2 to 5 of the normal operator, after the x transform of p is in T.
+const char* normal_apply_rest(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p, float2* Ap,
+                              float2* T, double* partial, hipStream_t s) {
   const int64_t plane = (int64_t)d.px * d.py;
-  // x: rows (z < nz, y < ny) of p -> rows of T
-  LinePass a = line_pass(p, T, (int64_t)d.nz * d.ny, d.ny, 0, 0, 1, d.nx, d.px);
-  a.in_os = (int64_t)d.nx * d.ny;
-  a.in_ws = d.nx;
-  a.out_os = plane;
-  a.out_ws = d.px;
-  if (launch_lines(true, kLineFwd, d.px, a, s) != hipSuccess) return "x transform launch failed";
   // y: columns (z < nz, kx), ny points in, py out
   if (launch_lines(false, kLineFwd, d.py, line_pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.ny, d.py), s) !=
       hipSuccess)
@@ -379,6 +447,20 @@ const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda,
   return nullptr;
 }
 
+}  // namespace
+
+const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p, float2* Ap,
+                         float2* T, double* partial, hipStream_t s) {
+  // x: rows (z < nz, y < ny) of p -> rows of T
+  LinePass a = line_pass(p, T, (int64_t)d.nz * d.ny, d.ny, 0, 0, 1, d.nx, d.px);
+  a.in_os = (int64_t)d.nx * d.ny;
+  a.in_ws = d.nx;
+  a.out_os = (int64_t)d.px * d.py;
+  a.out_ws = d.px;
+  if (launch_lines(true, kLineFwd, d.px, a, s) != hipSuccess) return "x transform launch failed";
+  return normal_apply_rest(d, Qhat, lambda, p, Ap, T, partial, s);
+}
+
 const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* b, float2* x, int iters,
                    double* resid, const CgWorkspace& w, hipStream_t s) {
   const int64_t n = d.voxels();
@@ -389,11 +471,22 @@ const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const
   if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
   for (int it = 0; it < iters; ++it) {
     const int slot = it & 1;
-    if (const char* e = normal_apply(d, Qhat, lambda, w.p, w.Ap, w.T, w.partial, s)) return e;
+    if (it == 0) {
+      if (const char* e = normal_apply(d, Qhat, lambda, w.p, w.Ap, w.T, w.partial, s)) return e;
+    } else {
+      // p = r + beta p of the previous step, fused with the x transform of p
+      if (launch_direction_x(d, w.r, w.p, w.T, w.state, slot ^ 1, w.partial2, resid ? resid + it : nullptr, s) !=
+          hipSuccess)
+        return "CG direction launch failed";
+      if (const char* e = normal_apply_rest(d, Qhat, lambda, w.p, w.Ap, w.T, w.partial, s)) return e;
+    }
     hipLaunchKernelGGL(step_kernel, dim3(kBlocks), dim3(kThreads), 0, s, x, w.r, w.p, w.Ap, n, w.state, slot,
                        w.partial, w.partial2);
-    hipLaunchKernelGGL(direction_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, w.r, w.p, n, w.state, slot,
-                       w.partial2, resid ? resid + it + 1 : nullptr);
+    if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
+  }
+  // <r, r> after the last step (its direction update is never needed)
+  if (iters > 0 && resid) {
+    hipLaunchKernelGGL(store_sum_kernel, dim3(1), dim3(kThreads), 0, s, w.partial2, resid + iters);
     if (hipGetLastError() != hipSuccess) return "CG kernel launch failed";
   }
   return nullptr;

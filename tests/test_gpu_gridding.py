@@ -6,10 +6,16 @@ Sizes span several line groups per FFT pass, samples outside [-0.5, 0.5)
 262,144 spiral samples the image is compared at sampled voxels.  On a
 Cartesian trajectory the gridded image equals fhd_compute's.
 
-Tolerance (relative L2): the deposits are float32 atomics, each lattice
-value the sum of up to a few hundred terms (relative rounding ~ 6e-8 per
-term, growing with the square root of the count), then three float32 FFT
-passes (~ eps_f32 log2 n): 1e-5.
+The deposits are sorted by lattice plane and summed per tile of a plane
+(TY rows with TY nx <= 4096 cells) in LDS; the cases include planes of one
+tile and of several (samples whose two rows fall in different tiles, and
+rows that wrap from the last tile to the first), 4-row tiles (nx = 1024), and
+many samples in one lattice cell (same-address LDS atomics).
+
+Tolerance (relative L2): each lattice value is a float32 sum of up to a few
+hundred terms in an order that depends on scheduling (relative rounding
+~ 6e-8 per term, growing with the square root of the count), then three
+float32 FFT passes (~ eps_f32 log2 n): 1e-5.
 """
 import numpy as np
 import pytest
@@ -51,6 +57,8 @@ def _gpu_grid(kx, ky, kz, phi, D, shape):
     ((2, 2, 2), 50, 0.5),
     ((16, 32, 64), 5000, 0.5),
     ((8, 8, 8), 3000, 0.8),          # samples past the lattice edge wrap
+    ((4, 64, 128), 6000, 0.8),       # 2 tiles of 32 rows per plane; rows wrap across tiles
+    ((2, 16, 1024), 4000, 0.5),      # 4 tiles of 4 rows per plane
 ])
 def test_gridding_matches_oracle(shape, M, kmax):
     from oracle import gridding as G_
@@ -63,6 +71,26 @@ def test_gridding_matches_oracle(shape, M, kmax):
     got = _gpu_grid(k[0], k[1], k[2], phi, D, shape)
     rel = _rel(got, ref)
     print(f"[parity] gridding {shape} M={M} kmax={kmax}: rel_l2={rel:.3e}", flush=True)
+    assert rel <= TOL
+
+
+def test_gridding_many_samples_in_one_cell():
+    """4096 samples inside one lattice cell (and a few on its edges): every
+    deposit of a wave lands on the same 8 lattice points."""
+    from oracle import gridding as G_
+    rng = np.random.Generator(np.random.PCG64(807))
+    M = 4096
+    nz, ny, nx = 8, 64, 64
+    k = np.empty((3, M), np.float32)
+    for a, n in enumerate((nx, ny, nz)):
+        k[a] = ((5 + rng.random(M)) / n - 0.5).astype(np.float32)   # inside cell 5 + n/2 of each axis
+    k[:, :8] = np.float32(5.0 / 8 - 0.5)                            # on a lattice point of z; x, y edges
+    phi = inputs.complex_normal(rng, M)
+    D = inputs.complex_normal(rng, M)
+    ref = G_.gridding(k[0], k[1], k[2], phi, D, nx, ny, nz)
+    got = _gpu_grid(k[0], k[1], k[2], phi, D, (nz, ny, nx))
+    rel = _rel(got, ref)
+    print(f"[parity] gridding, {M} samples in one cell: rel_l2={rel:.3e}", flush=True)
     assert rel <= TOL
 
 
