@@ -44,7 +44,9 @@
 //             no pad, for N = 1024: 64 KB, so that two workgroups fit a CU's
 //             LDS (the fused spectral-product pass, where overlapping one
 //             workgroup's loads with another's transforms pays more than
-//             full-line rows).
+//             full-line rows).  A one-point pad (72 KB + the 8 KB twiddles,
+//             exactly 80 KB) measured slower: 5.84 against 5.69 ms for the
+//             512^3 pass.
 #pragma once
 
 #include <hip/hip_runtime.h>
