@@ -285,8 +285,10 @@ fhd_status fhd_cg_solve(const float* Qhat, int32_t nx, int32_t ny, int32_t nz,
  *   image      : fhd_c32[nz][ny][nx], overwritten; must not overlap the inputs
  * The deposits are sorted by lattice plane (two entries of 20 bytes per
  * sample, in scratch the call allocates and frees stream-ordered) and summed
- * per tile of a plane with LDS atomics: the result is not bitwise
- * reproducible (the rounding depends on the order in which entries land).
+ * per tile of a plane in 64-bit fixed point (scaled by a power of two from M
+ * and the largest |Re|, |Im| of conj(phi) D, so that no sum can overflow):
+ * the result is bitwise reproducible, whatever the order of the samples.
+ * NaN or infinite inputs give an undefined image.
  */
 fhd_status fhd_gridding(const float* kx, const float* ky, const float* kz,
                         const fhd_c32* phi, const fhd_c32* D, int64_t M,

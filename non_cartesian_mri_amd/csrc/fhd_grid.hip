@@ -25,12 +25,18 @@
 // (sample, z plane) deposit under its lattice plane: a sample lands on planes
 // jz and jz + 1 (mod nz), so it makes two entries, each holding the sample's
 // x / y cell, x / y fractions and Mu times its z weight.  Then one workgroup
-// per tile of TY rows of a plane (TY nx <= 4096 cells, 32 KB of LDS) adds the
-// entries of its plane that touch its rows into the tile with LDS atomics and
-// writes the tile once, rolled and sign-alternated into L.  The lattice cell and fractions come
-// from the float32 k in double, so every sample lands in the cells its exact
-// coordinate selects; the sums in LDS depend on the order in which the
-// entries land (results are not bitwise reproducible).
+// per tile of TY rows of a plane (TY nx <= 4096 cells) adds the entries of its
+// plane that touch its rows into the tile and writes the tile once, rolled and
+// sign-alternated into L.  The tile sums are 64-bit fixed point with LDS
+// integer atomics (on this GPU an LDS float atomic add runs at about a ninth
+// of the rate of an integer one): with c the largest |Re| or |Im| of any Mu,
+// no cell receives more than M contributions of size <= c, so terms scaled by
+// 2^s with M c 2^s < 2^61 cannot overflow, and each term is the double
+// product rounded to an integer (relative rounding ~1e-16 for the largest
+// terms, far below float32's).  Integer sums do not depend on the order in
+// which entries land, so the lattice, and the image, are bitwise
+// reproducible.  The lattice cell and fractions come from the float32 k in
+// double, so every sample lands in the cells its exact coordinate selects.
 #include "fhd.h"
 #include "fhd_cg.h"
 #include "fhd_lines.h"
@@ -43,6 +49,7 @@ constexpr int kBinSamples = 512;             // samples per binning block (2 per
 constexpr int kPerThread = kBinSamples / kThreads;
 constexpr int kTileCells = 4096;             // lattice cells of a deposit tile
 constexpr int kMaxPlanes = kToeplitzMaxLen;  // nz <= 1024: one LDS counter per plane
+constexpr int kMaxSlots = 64;                // the largest |Mu| component, spread over 64 words
 
 // Cell and fraction of coordinate k on an n-point lattice: u = k n + n/2,
 // cell = floor(u) mod n, fraction = u - floor(u).
@@ -61,8 +68,10 @@ __device__ __forceinline__ int z_cell(float k, int nz) {
   return j;
 }
 
-__global__ void __launch_bounds__(kThreads) clear_counts(unsigned* __restrict__ count, int nz) {
+__global__ void __launch_bounds__(kThreads) clear_counts(unsigned* __restrict__ count, int nz,
+                                                         unsigned* __restrict__ maxbits) {
   for (int b = threadIdx.x; b < nz; b += kThreads) count[b] = 0u;
+  if (threadIdx.x < kMaxSlots) maxbits[threadIdx.x] = 0u;
 }
 
 // Entries per plane: an LDS histogram per block of kBinSamples samples, then
@@ -123,13 +132,19 @@ scan_kernel(const unsigned* __restrict__ count, unsigned* __restrict__ start, un
 
 // The entries: each block ranks its samples per plane in LDS, reserves one
 // range per plane with a global atomic, and writes (cell, fractions, value).
-// cell = jx | jy << 16; val = (fx, fy, Re, Im of Mu times the z weight).
+// cell = jx | jy << 16; val = (fx, fy, Re, Im of Mu times the z weight).  The
+// largest |Re Mu|, |Im Mu| goes to maxbits[block mod 64] (as float bits:
+// non-negative floats order like their bit patterns, so an integer max is
+// exact and independent of order; 64 words keep the atomics of different
+// blocks off one address).
 __global__ void __launch_bounds__(kThreads)
 fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const float* __restrict__ kz,
             const float2* __restrict__ phi, const float2* __restrict__ D, int64_t M, int nx, int ny, int nz,
-            unsigned* __restrict__ cursor, unsigned* __restrict__ cell, float4* __restrict__ val) {
+            unsigned* __restrict__ cursor, unsigned* __restrict__ cell, float4* __restrict__ val,
+            unsigned* __restrict__ maxbits) {
   __shared__ unsigned hist[kMaxPlanes];
   __shared__ unsigned base[kMaxPlanes];
+  __shared__ unsigned wmax[kThreads / 64];
   for (int b = threadIdx.x; b < nz; b += kThreads) hist[b] = 0u;
   __syncthreads();
   const int64_t m0 = (int64_t)blockIdx.x * kBinSamples;
@@ -150,6 +165,7 @@ fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const fl
   for (int b = threadIdx.x; b < nz; b += kThreads)
     if (hist[b]) base[b] = atomicAdd(&cursor[b], hist[b]);
   __syncthreads();
+  unsigned tmax = 0u;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int64_t m = m0 + k * kThreads + threadIdx.x;
@@ -158,6 +174,8 @@ fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const fl
     // conj(phi) D
     const float mr = __builtin_fmaf(p.x, d.x, p.y * d.y);
     const float mi = __builtin_fmaf(p.x, d.y, -(p.y * d.x));
+    const unsigned bits = __float_as_uint(__builtin_fmaxf(__builtin_fabsf(mr), __builtin_fabsf(mi)));
+    tmax = bits > tmax ? bits : tmax;
     int jx, jy, jzz;
     double fx, fy, fz;
     lattice_cell(kx[m], nx, jx, fx);
@@ -172,67 +190,90 @@ fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const fl
     cell[e1] = c;
     val[e1] = make_float4((float)fx, (float)fy, w1 * mr, w1 * mi);
   }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned o = __shfl_xor(tmax, m, 64);
+    tmax = o > tmax ? o : tmax;
+  }
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = tmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned b = 0u;
+    for (int w = 0; w < kThreads / 64; ++w) b = wmax[w] > b ? wmax[w] : b;
+    if (b) atomicMax(&maxbits[blockIdx.x % kMaxSlots], b);
+  }
 }
 
 // One tile: rows [row0, row0 + TY) of plane z.  The plane's entries that touch
-// those rows go into LDS with LDS atomics; the tile is then written once into
-// L: cell (x, y, z) to ((x, y, z) + n/2 mod n), times (-1) to the sum of the
-// new coordinates.
+// those rows go into the tile as 64-bit fixed-point sums (LDS integer
+// atomics); the tile is then written once into L: cell (x, y, z) to
+// ((x, y, z) + n/2 mod n), times (-1) to the sum of the new coordinates.
 constexpr int kDepositThreads = 1024;
 
-__device__ __forceinline__ void deposit_entry(float* t, unsigned c, const float4& f, int nx, int ny, int ty,
-                                              int row0) {
+__device__ __forceinline__ void add_fixed(unsigned long long* t, int i, double re, double im) {
+  atomicAdd(&t[2 * i], (unsigned long long)(long long)__builtin_rint(re));
+  atomicAdd(&t[2 * i + 1], (unsigned long long)(long long)__builtin_rint(im));
+}
+
+// f = (fx, fy, Re, Im of the value); scale = 2^s.
+__device__ __forceinline__ void deposit_entry(unsigned long long* t, unsigned c, const float4& f, int nx, int ny,
+                                              int ty, int row0, double scale) {
   const int jx = (int)(c & 0xffffu), jy = (int)(c >> 16);
   const int ra = jy - row0, rb = (jy + 1 == ny ? 0 : jy + 1) - row0;
   const int xb = jx + 1 == nx ? 0 : jx + 1;
-  const float wx0 = 1.0f - f.x, wx1 = f.x;
+  const double vr = (double)f.z * scale, vi = (double)f.w * scale;
+  const double wx1 = (double)f.x, wx0 = 1.0 - wx1, wy1 = (double)f.y, wy0 = 1.0 - wy1;
   if ((unsigned)ra < (unsigned)ty) {
-    const float wy = 1.0f - f.y;
-    const float a = wx0 * wy, b = wx1 * wy;
-    atomicAdd(&t[2 * (ra * nx + jx)], a * f.z);
-    atomicAdd(&t[2 * (ra * nx + jx) + 1], a * f.w);
-    atomicAdd(&t[2 * (ra * nx + xb)], b * f.z);
-    atomicAdd(&t[2 * (ra * nx + xb) + 1], b * f.w);
+    const double a = wx0 * wy0, b = wx1 * wy0;
+    add_fixed(t, ra * nx + jx, vr * a, vi * a);
+    add_fixed(t, ra * nx + xb, vr * b, vi * b);
   }
   if ((unsigned)rb < (unsigned)ty) {
-    const float wy = f.y;
-    const float a = wx0 * wy, b = wx1 * wy;
-    atomicAdd(&t[2 * (rb * nx + jx)], a * f.z);
-    atomicAdd(&t[2 * (rb * nx + jx) + 1], a * f.w);
-    atomicAdd(&t[2 * (rb * nx + xb)], b * f.z);
-    atomicAdd(&t[2 * (rb * nx + xb) + 1], b * f.w);
+    const double a = wx0 * wy1, b = wx1 * wy1;
+    add_fixed(t, rb * nx + jx, vr * a, vi * a);
+    add_fixed(t, rb * nx + xb, vr * b, vi * b);
   }
 }
 
 __global__ void __launch_bounds__(kDepositThreads)
 deposit_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ count,
-               const unsigned* __restrict__ cell, const float4* __restrict__ val, int nx, int lx, int ny, int nz,
-               int ty, float2* __restrict__ L) {
-  __shared__ float2 tile[kTileCells];
+               const unsigned* __restrict__ cell, const float4* __restrict__ val, const unsigned* __restrict__ maxbits,
+               int64_t M, int nx, int lx, int ny, int nz, int ty, float2* __restrict__ L) {
+  __shared__ unsigned long long tile[2 * kTileCells];   // 64 KB: (Re, Im) per cell
   // plane = block mod nz, tile = block div nz: blocks go to the 8 XCDs in
   // turn, so every XCD gets every tile index (the middle rows of a plane
   // usually hold most of the samples)
   const int z = (int)(blockIdx.x % (unsigned)nz), row0 = (int)(blockIdx.x / (unsigned)nz) * ty;
   const int cells = ty * nx;
-  for (int i = threadIdx.x; i < cells; i += kDepositThreads) tile[i] = make_float2(0.0f, 0.0f);
+  for (int i = threadIdx.x; i < 2 * cells; i += kDepositThreads) tile[i] = 0ull;
+  // scale 2^s with M c 2^s < 2^61 (c: the largest |Re|, |Im| of any value)
+  unsigned cb = maxbits[threadIdx.x & (kMaxSlots - 1)];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned o = __shfl_xor(cb, m, 64);
+    cb = o > cb ? o : cb;
+  }
+  const float cmax = __uint_as_float(cb);
+  const int e = cmax > 0.0f ? ilogb((double)M * (double)cmax) + 1 : 0;
+  const double scale = ldexp(1.0, 61 - e), unscale = ldexp(1.0, e - 61);
   __syncthreads();
-  float* t = reinterpret_cast<float*>(tile);
   const unsigned e0 = start[z], e1 = e0 + count[z];
   // two entries per thread and trip, so two loads are in flight
-  unsigned e = e0 + threadIdx.x;
-  for (; (int64_t)e + kDepositThreads < (int64_t)e1; e += 2 * kDepositThreads) {
-    const unsigned ca = cell[e], cb = cell[e + kDepositThreads];
-    const float4 fa = val[e], fb = val[e + kDepositThreads];
-    deposit_entry(t, ca, fa, nx, ny, ty, row0);
-    deposit_entry(t, cb, fb, nx, ny, ty, row0);
+  unsigned i = e0 + threadIdx.x;
+  for (; (int64_t)i + kDepositThreads < (int64_t)e1; i += 2 * kDepositThreads) {
+    const unsigned ca = cell[i], cb = cell[i + kDepositThreads];
+    const float4 fa = val[i], fb = val[i + kDepositThreads];
+    deposit_entry(tile, ca, fa, nx, ny, ty, row0, scale);
+    deposit_entry(tile, cb, fb, nx, ny, ty, row0, scale);
   }
-  if (e < e1) deposit_entry(t, cell[e], val[e], nx, ny, ty, row0);
+  if (i < e1) deposit_entry(tile, cell[i], val[i], nx, ny, ty, row0, scale);
   __syncthreads();
   const int zr = (z + nz / 2) & (nz - 1);
-  for (int i = threadIdx.x; i < cells; i += kDepositThreads) {
-    const int y = i >> lx, x = i & (nx - 1);
+  for (int k = threadIdx.x; k < cells; k += kDepositThreads) {
+    const int y = k >> lx, x = k & (nx - 1);
     const int yr = (row0 + y + ny / 2) & (ny - 1), xr = (x + nx / 2) & (nx - 1);
-    const float2 v = tile[i];
+    const double re = (double)(long long)tile[2 * k] * unscale, im = (double)(long long)tile[2 * k + 1] * unscale;
+    const float2 v = make_float2((float)re, (float)im);
     L[((int64_t)zr * ny + yr) * nx + xr] = ((xr + yr + zr) & 1) ? make_float2(-v.x, -v.y) : v;
   }
 }
@@ -241,7 +282,8 @@ deposit_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ 
 
 size_t gridding_scratch_bytes(int64_t M, int nz) {
   const size_t entries = 2 * (size_t)M;
-  return entries * sizeof(float4) + cg_align(entries * sizeof(unsigned)) + 3 * cg_align((size_t)nz * sizeof(unsigned));
+  return entries * sizeof(float4) + cg_align(entries * sizeof(unsigned)) + 3 * cg_align((size_t)nz * sizeof(unsigned)) +
+         cg_align(kMaxSlots * sizeof(unsigned));
 }
 
 const char* gridding_run(const float* kx, const float* ky, const float* kz, const float2* phi, const float2* D,
@@ -254,8 +296,9 @@ const char* gridding_run(const float* kx, const float* ky, const float* kz, cons
   unsigned* cell = (unsigned*)c;       c += cg_align(entries * sizeof(unsigned));
   unsigned* count = (unsigned*)c;      c += cg_align((size_t)nz * sizeof(unsigned));
   unsigned* start = (unsigned*)c;      c += cg_align((size_t)nz * sizeof(unsigned));
-  unsigned* cursor = (unsigned*)c;
-  hipLaunchKernelGGL(clear_counts, dim3(1), dim3(kThreads), 0, s, count, nz);
+  unsigned* cursor = (unsigned*)c;    c += cg_align((size_t)nz * sizeof(unsigned));
+  unsigned* maxbits = (unsigned*)c;
+  hipLaunchKernelGGL(clear_counts, dim3(1), dim3(kThreads), 0, s, count, nz, maxbits);
   if (hipGetLastError() != hipSuccess) return "clear kernel launch failed";
   const int64_t bins = (M + kBinSamples - 1) / kBinSamples;
   if (M > 0) {
@@ -266,14 +309,14 @@ const char* gridding_run(const float* kx, const float* ky, const float* kz, cons
   if (hipGetLastError() != hipSuccess) return "scan kernel launch failed";
   if (M > 0) {
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)bins), dim3(kThreads), 0, s, kx, ky, kz, phi, D, M, nx, ny, nz,
-                       cursor, cell, val);
+                       cursor, cell, val, maxbits);
     if (hipGetLastError() != hipSuccess) return "fill kernel launch failed";
   }
   const int ty = ny < kTileCells / nx ? ny : kTileCells / nx;   // powers of two: ty divides ny
   int lx = 0;
   while ((1 << lx) < nx) ++lx;
   hipLaunchKernelGGL(deposit_kernel, dim3((unsigned)((int64_t)nz * (ny / ty))), dim3(kDepositThreads), 0, s, start,
-                     count, cell, val, nx, lx, ny, nz, ty, image);
+                     count, cell, val, maxbits, M, nx, lx, ny, nz, ty, image);
   if (hipGetLastError() != hipSuccess) return "deposit kernel launch failed";
   const int64_t plane = (int64_t)nx * ny;
   if (launch_lines(true, kLineInv, nx, line_pass(image, image, (int64_t)nz * ny, 1, nx, 0, 1, nx, nx), s) !=

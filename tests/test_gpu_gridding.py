@@ -12,10 +12,10 @@ tile and of several (samples whose two rows fall in different tiles, and
 rows that wrap from the last tile to the first), 4-row tiles (nx = 1024), and
 many samples in one lattice cell (same-address LDS atomics).
 
-Tolerance (relative L2): each lattice value is a float32 sum of up to a few
-hundred terms in an order that depends on scheduling (relative rounding
-~ 6e-8 per term, growing with the square root of the count), then three
-float32 FFT passes (~ eps_f32 log2 n): 1e-5.
+Tolerance (relative L2): each lattice value is a 64-bit fixed-point sum of
+terms rounded from double products (exact and independent of order, so the
+image is bitwise reproducible, which one test checks), converted to float32
+(~ 6e-8), then three float32 FFT passes (~ eps_f32 log2 n): 1e-5.
 """
 import numpy as np
 import pytest
@@ -92,6 +92,23 @@ def test_gridding_many_samples_in_one_cell():
     rel = _rel(got, ref)
     print(f"[parity] gridding, {M} samples in one cell: rel_l2={rel:.3e}", flush=True)
     assert rel <= TOL
+
+
+def test_gridding_is_bitwise_reproducible():
+    """The lattice sums are integers: two runs (and a run on a permuted
+    trajectory, whose entries land in another order) give the same bits."""
+    rng = np.random.Generator(np.random.PCG64(808))
+    M = 20000
+    k = (rng.random((3, M)) - 0.5).astype(np.float32)
+    phi = inputs.complex_normal(rng, M)
+    D = inputs.complex_normal(rng, M)
+    shape = (16, 64, 64)
+    a = _gpu_grid(k[0], k[1], k[2], phi, D, shape)
+    b = _gpu_grid(k[0], k[1], k[2], phi, D, shape)
+    perm = rng.permutation(M)
+    c = _gpu_grid(k[0][perm], k[1][perm], k[2][perm], phi[perm], D[perm], shape)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
 def test_gridding_empty_trajectory_writes_zeros():
