@@ -260,7 +260,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   for (int i = 0; i < p.npass; ++i) {
     if (mfma) {
       if (!ncmri::mfma_supported(p.tiles, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for T=%d BC=%d", p.tiles, p.bc[i]);
-      p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * p.tiles * 64 * sizeof(float);
+      p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * ncmri::mfma_factor_floats(p.tiles) * sizeof(float);
     } else {
       if (!ncmri::gather_supported(is_q, p.V, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no kernel for V=%d BC=%d", p.V, p.bc[i]);
       int stride = ncmri::record_dwords(is_q, p.trig, p.V, p.bc[i]);

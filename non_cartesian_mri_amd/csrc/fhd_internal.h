@@ -73,23 +73,28 @@ bool gather_supported(int is_q, int V, int BC);
 
 // ---------------------------------------------------------------------------
 // Matrix-core (MFMA) engine.  Each wave owns 32 voxel groups of V voxels
-// (V x BC = 16 T complex columns); per sample it evaluates one phase per
-// group and multiplies the 32 x 2 matrix (cos, sin of the group phases) by T
-// 2 x 32 factor matrices with v_mfma_f32_32x32x2_f32.
+// (V x BC = 16 T complex columns, i.e. T / 2 tiles of 32); per pair of
+// samples it evaluates one phase per group and lane and accumulates three
+// real products per tile (the three-multiplication complex product) with
+// v_mfma_f32_32x32x2_f32, the K dimension running over the two samples.
 constexpr int kMfmaChunk = 32;   // samples per LDS chunk; records are padded to it
 
 inline constexpr int mfma_header_floats(int trig) { return trig == kTrigHw ? 4 : 8; }
-// dwords of one sample's records (header + T factor tiles)
-inline constexpr int mfma_record_dwords(int trig, int T) { return mfma_header_floats(trig) + 64 * T; }
+// factor floats per sample: 3 values per complex column
+inline constexpr int mfma_factor_floats(int T) { return 48 * T; }
+// dwords of one sample's records (header + factors)
+inline constexpr int mfma_record_dwords(int trig, int T) { return mfma_header_floats(trig) + mfma_factor_floats(T); }
 
 // Records of one sample m for the MFMA engine (all float32):
 //   header hdr[m][]  HW trig:       kx, ky, kz, 0
 //                    accurate trig: khx, khy, khz, 0, klx, kly, klz, 0
-//   factors wb[m][64][T], tile t < T: complex column cc = 16 t + c (c < 16) holds
-//     f = Mu_b exp(i 2 pi k.d_j) with b = cc / V, j = cc % V (V = 16 T / BC),
-//     stored as the two rows of the MFMA B operand of tile t, entry p at
-//     [p][t]: p = 2c -> fr, 2c+1 -> fi, 32+2c -> -fi, 33+2c -> fr (entry p
-//     is supplied by lane p, so a lane's T entries are contiguous).
+//   factors, per pair of samples h = m / 2 (P = T / 2 tiles of 32 complex
+//     columns; complex column cc = 32 t + c holds f = Mu_b exp(i 2 pi k.d_j)
+//     with b = cc / V, j = cc % V, V = 16 T / BC), 192 P floats per pair:
+//       wb[h][p][2 P]   : [t] = fr, [P + t] = fi
+//       wb[h][128 P + p P + t] : fr + fi (rounded once)
+//     where p = 32 (m % 2) + c is the lane that supplies the entry as the
+//     MFMA B operand (row k = m % 2, column c).
 struct MfmaRecordArgs {
   const float* kx; const float* ky; const float* kz;
   const float* x; const float* y; const float* z;  // x[0..min(V,N)-1] etc. are read
@@ -97,7 +102,7 @@ struct MfmaRecordArgs {
   const float2* D;       // first vector of this pass ([BC][M]); unused for Q
   int64_t M, N, mpad;    // mpad: multiple of kMfmaChunk
   float* hdr;            // [mpad][mfma_header_floats]
-  float* wb;             // [mpad][64][T]
+  float* wb;             // [mpad / 2][192 P] (P = T / 2)
 };
 
 struct MfmaArgs {
@@ -145,7 +150,8 @@ hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdA
 // Adds the groups off the common offsets into a.out (after the rows' reduction).
 hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStream_t s);
 
-// T: 32-column factor tiles per group phase (2 or 4); BC: vectors of the pass.
+// T: units of 16 complex columns per group phase (2 or 4; T / 2 tiles of 32
+// complex columns); BC: vectors of the pass.
 hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
                                hipStream_t s);
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,

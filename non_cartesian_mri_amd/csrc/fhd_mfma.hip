@@ -8,28 +8,32 @@
 // from their group's first voxel x_g (on a Cartesian grid: V consecutive
 // voxels of one row).  Then
 //
-//   out[b][x_g + d_j] = sum_m  exp(i 2 pi k_m.x_g) * f_m[j][b],
-//   f_m[j][b]         = Mu_b[m] exp(i 2 pi k_m.d_j)   (Mu = conj(phi) D, or |phi|^2 for Q)
+//   out[b][x_g + d_j] = sum_m  (c + i s)_m[g] * (fr + i fi)_m[j][b],
+//   (c, s)_m[g] = (cos, sin)(2 pi k_m.x_g),
+//   f_m[j][b]   = Mu_b[m] exp(i 2 pi k_m.d_j)   (Mu = conj(phi) D, or |phi|^2 for Q)
 //
-// i.e. for 32 groups and 32 complex columns (j, b) the sum over samples is the
-// real matrix product
+// a complex matrix product (groups x samples) * (samples x columns).  It is
+// computed with three real products instead of four (the three-multiplication
+// form of a complex product, usually credited to Gauss):
 //
-//   [Re | Im] (32 x 64) += sum_m  E_m (32 x 2) * W_m (2 x 64),
-//   E_m[g] = (cos, sin)(2 pi k_m.x_g),   W_m = [ fr  fi ; -fi  fr ] per column,
+//   P1 = sum (c + s) fr,   P2 = sum (c - s) fi,   P3 = sum s (fr + fi),
+//   Re = P1 - P3,          Im = P2 + P3.
 //
-// which v_mfma_f32_32x32x2_f32 computes (K = 2) one sample at a time: one
-// phase and one sine per lane and T MFMAs per sample for 32 groups x 16 T
-// complex columns (T = 2 or 4 tiles of 32 real columns).  The factor matrices
-// W_m do not depend on the voxel; the records kernel forms them once per
-// sample, in double, rounded once to fp32, already laid out as the MFMA B
-// operands, a lane's T entries side by side (one LDS read per sample).
+// This variant keeps a sample at k = 0 exact: with s = 0 the products are
+// c fr, c fi and 0.  Each real product over 32 groups, 32 columns and two
+// samples is one v_mfma_f32_32x32x2_f32 (K = 2 = the samples of a pair), so a
+// pair of samples costs 3 MFMAs per tile of 32 complex columns where the
+// four-product form needs 4, and each lane evaluates one phase (3 FMAs), its
+// sine and its cosine per pair of samples.  The factor values (fr, fi,
+// fr + fi) do not depend on the voxel; the records kernel forms them once
+// per sample, in double, rounded once to fp32, already laid out as the MFMA B
+// operands.
 //
 // Operand layouts of v_mfma_f32_32x32x2_f32 (wave64), checked on gfx950:
 //   A[i][k] = lane 32 k + i,  B[k][j] = lane 32 k + j,
 //   D[i][j] = register (i / 8) * 4 + i % 4 of lane 32 * ((i / 4) % 2) + j.
-// So lanes 0-31 supply cos of group i = lane and lanes 32-63 sin of group
-// i = lane - 32: every lane evaluates one sine, the cosine lanes with a
-// quarter turn added to the phase.
+// So lane l supplies group i = l % 32 at sample 2 h + l / 32 of pair h, and
+// the B entry of column j at that sample.
 //
 // Data flow.  The 4 waves of a workgroup walk the same samples, so each
 // 32-sample chunk of records is copied from memory once per workgroup into LDS
@@ -38,16 +42,16 @@
 // lds: lane i's 16 bytes land at the LDS base + 16 i, no VGPRs involved), double
 // buffered in two separate LDS arrays: the next chunk's copy is in flight
 // while the current one is consumed, with one wait and workgroup barrier per
-// chunk.  The header (k) is read as an LDS broadcast.
+// chunk.  The headers (k) are read from LDS, two addresses per wave.
 //
 // Waves whose voxels are not on the common offsets (any non-grid coordinate
 // set) only help stage the chunks; a second kernel (mfma_direct_kernel)
 // evaluates every voxel phase of those waves directly on the vector ALU from
-// the same records (the offset-0 columns hold Mu_b), and exits at once for
-// the other waves.  Both kernels take the same decision per wave.
+// the same records (the offset-0 columns hold fr, fi = Mu_b), and exits at once
+// for the other waves.  Both kernels take the same decision per wave.
 //
 // Summation is blocked as in the VALU engine: tile partial sums in the MFMA
-// accumulators, folded into running totals at tile ends.
+// accumulators, folded (as Re, Im) into running totals at tile ends.
 #include "fhd_internal.h"
 #include "fhd_trig.h"
 #include "fhd_mfma_common.h"
@@ -60,6 +64,7 @@ namespace {
 __global__ void __launch_bounds__(kWorkgroup)
 mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   const int cols = 16 * T;
+  const int P = T / 2;
   const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
   const int64_t m = idx / cols;
   const int cc = (int)(idx - m * cols);
@@ -67,14 +72,15 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   const int HF = mfma_header_floats(trig);
   const int V = cols / BC;
   float* h = a.hdr + m * HF;
-  // B-operand entry p (= the lane that supplies it) of tile t sits at p T + t:
-  // each lane's T entries of a sample are contiguous
-  float* w = a.wb + m * T * 64 + cc / 16;
-  const int c = cc % 16;
+  // entry of column c = cc % 32 of tile t = cc / 32 at row m % 2
+  const int t = cc / 32, lp = 32 * (int)(m & 1) + cc % 32;
+  float* pair = a.wb + (m >> 1) * (192 * P);
+  float* wr = pair + lp * (2 * P) + t;            // fr; fi at + P
+  float* ws = pair + 128 * P + lp * P + t;        // fr + fi
   if (m >= a.M) {  // padding sample: contributes exactly zero
     if (cc == 0)
       for (int i = 0; i < HF; ++i) h[i] = 0.0f;
-    w[(2 * c) * T] = 0.0f; w[(2 * c + 1) * T] = 0.0f; w[(32 + 2 * c) * T] = 0.0f; w[(33 + 2 * c) * T] = 0.0f;
+    wr[0] = 0.0f; wr[P] = 0.0f; ws[0] = 0.0f;
     return;
   }
   const float kx = a.kx[m], ky = a.ky[m], kz = a.kz[m];
@@ -110,8 +116,8 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
     mr = pr * d.x + pim * d.y;  // Mu = conj(phi) * D
     mi = pr * d.y - pim * d.x;
   }
-  const float fr = (float)(mr * cj - mi * sj), fi = (float)(mr * sj + mi * cj);
-  w[(2 * c) * T] = fr; w[(2 * c + 1) * T] = fi; w[(32 + 2 * c) * T] = -fi; w[(33 + 2 * c) * T] = fr;
+  const double fr = mr * cj - mi * sj, fi = mr * sj + mi * cj;
+  wr[0] = (float)fr; wr[P] = (float)fi; ws[0] = (float)(fr + fi);
 }
 
 // ---------------------------------------------------------------------------
@@ -150,100 +156,118 @@ __device__ __forceinline__ void row_range(int64_t m_split, int64_t mpad, int32_t
 template <int T, int BC, int TRIG>
 struct MfmaGather {
   static constexpr int V = 16 * T / BC;                // voxels per group
+  static constexpr int P = T / 2;                      // tiles of 32 complex columns
   static constexpr int HF = mfma_header_floats(TRIG);  // header floats per sample
   static constexpr int C = kMfmaChunk;
   static constexpr int NW = kWorkgroup / 64;           // waves per workgroup
-  static constexpr int NB = C * T * 16 / 64;           // 1 KiB factor blocks per chunk
+  static constexpr int PF = 192 * P;                   // factor floats per pair of samples
+  static constexpr int NB = C / 2 * PF * 4 / 1024;     // 1 KiB factor blocks per chunk
   static constexpr int NH = C * HF / 4;                // header float4s per chunk
-  static_assert(V >= 2 && V * BC == 16 * T, "group shape");
+  static_assert(P >= 1 && V >= 2 && V * BC == 16 * T, "group shape");
   static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
 
   static constexpr int HK = TRIG == kTrigHw ? 3 : 7;  // header floats a sample's phase reads
 
-  // Phase of the lane's group in revolutions, plus a quarter turn on the
-  // cosine lanes (q = 0.25), and its sine: the lane's A-operand entry.
-  __device__ static __forceinline__ float group_entry(const float (&hs)[HK], float gx, float gy,
-                                                      float gz, float q) {
+  // A-operand entries of the lane's group at its sample: (c + s, c - s, s) of
+  // the group phase.
+  __device__ static __forceinline__ void group_entries(const float (&hs)[HK], float gx, float gy,
+                                                       float gz, float (&av)[3]) {
+    float s, c;
     if constexpr (TRIG == kTrigHw) {
-      const float t = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, __builtin_fmaf(hs[0], gx, q)));
-      return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(t));
+      const float t = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, hs[0] * gx));
+      const float f = __builtin_amdgcn_fractf(t);
+      s = __builtin_amdgcn_sinf(f);
+      c = __builtin_amdgcn_cosf(f);
     } else {
-      // kh.x (plus the quarter turn) is exact for integer or half-integer
-      // coordinates of moderate size, so its fractional part is exact.
-      float th = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, __builtin_fmaf(hs[0], gx, q)));
+      // kh.x is exact for integer or half-integer coordinates of moderate
+      // size, so its fractional part is exact.
+      float th = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, hs[0] * gx));
       th = th - __builtin_rintf(th);
       const float tl = __builtin_fmaf(hs[6], gz, __builtin_fmaf(hs[5], gy, hs[4] * gx));
-      float s, c;
       sincos_turns(th + tl, s, c);
-      return s;
+    }
+    av[0] = c + s;
+    av[1] = c - s;
+    av[2] = s;
+  }
+
+  // Header of the lane's sample and its B-operand entries of pair h of the
+  // chunk in LDS: fr (P), fi (P) in one read, fr + fi (P) in another.
+  __device__ static __forceinline__ void load_pair(const float* __restrict__ hb,
+                                                   const float* __restrict__ wb, int h, int lane,
+                                                   float (&hs)[HK], float (&bv)[3 * P]) {
+    const float* hp = hb + (2 * h + (lane >> 5)) * HF;
+#pragma unroll
+    for (int i = 0; i < HK; ++i) hs[i] = hp[i];
+    const float* pp = wb + h * PF;
+    if constexpr (P == 2) {
+      const float4 v = *reinterpret_cast<const float4*>(pp + lane * 4);
+      const float2 u = *reinterpret_cast<const float2*>(pp + 256 + lane * 2);
+      bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w; bv[4] = u.x; bv[5] = u.y;
+    } else if constexpr (P == 1) {
+      const float2 v = *reinterpret_cast<const float2*>(pp + lane * 2);
+      bv[0] = v.x; bv[1] = v.y; bv[2] = pp[128 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * P; ++i) bv[i] = pp[lane * 2 * P + i];
+#pragma unroll
+      for (int t = 0; t < P; ++t) bv[2 * P + t] = pp[128 * P + lane * P + t];
     }
   }
 
-  // Header and B-operand entries of sample s of the chunk in LDS.
-  __device__ static __forceinline__ void load_sample(const float* __restrict__ hb,
-                                                     const float* __restrict__ wb, int s, int lane,
-                                                     float (&hs)[HK], float (&bv)[T]) {
+  __device__ static __forceinline__ void mfmas(const float (&av)[3], const float (&bv)[3 * P],
+                                               f32x16 (&acc)[3][P]) {
 #pragma unroll
-    for (int i = 0; i < HK; ++i) hs[i] = hb[s * HF + i];
-    // the lane's T entries are contiguous: one LDS read
-    if constexpr (T == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(wb + (s * 64 + lane) * 4);
-      bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w;
-    } else if constexpr (T == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(wb + (s * 64 + lane) * 2);
-      bv[0] = v.x; bv[1] = v.y;
-    } else {
-#pragma unroll
-      for (int t = 0; t < T; ++t) bv[t] = wb[(s * 64 + lane) * T + t];
+    for (int t = 0; t < P; ++t) {
+      acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[1], bv[P + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[2], bv[2 * P + t], acc[2][t], 0, 0, 0);
     }
   }
 
   // One chunk for a wave on the common offsets, software-pipelined by one
-  // sample: the next sample's LDS reads are issued before this sample's
-  // MFMAs (the fences keep the scheduler from moving them).  The A entry of
-  // the HW path (three FMAs, fract, sine) is computed right before the
-  // sample's own MFMAs; the accurate path's longer chain (exact reduction and
-  // polynomial) is computed one sample ahead, right after the previous
-  // sample's MFMAs, so it runs while the matrix pipe works (measured at
-  // 128^3: the HW path is 2.8 % faster in the first order, the accurate path
-  // 1.7 % faster in the second).
+  // pair: the next pair's LDS reads are issued before this pair's MFMAs (the
+  // fences keep the scheduler from moving them).  The A entries of the HW
+  // path (three FMAs, fract, sine, cosine) are computed right before the
+  // pair's own MFMAs; the accurate path's longer chain (exact reduction and
+  // polynomials) is computed one pair ahead, right after the previous pair's
+  // MFMAs, so it runs while the matrix pipe works.
   __device__ static __forceinline__ void regular_chunk(const float* __restrict__ hb,
                                                        const float* __restrict__ wb, int lane,
-                                                       float gx, float gy, float gz, float q,
-                                                       f32x16 (&acc)[T]) {
-    float hc[HK], bc[T];
-    load_sample(hb, wb, 0, lane, hc, bc);
+                                                       float gx, float gy, float gz,
+                                                       f32x16 (&acc)[3][P]) {
+    constexpr int NP = C / 2;
+    float hc[HK], bc[3 * P], av[3];
+    load_pair(hb, wb, 0, lane, hc, bc);
     if constexpr (TRIG == kTrigHw) {
 #pragma unroll
-      for (int s = 0; s < C; ++s) {
-        float hn[HK], bn[T];
-        if (s + 1 < C) load_sample(hb, wb, s + 1, lane, hn, bn);
+      for (int h = 0; h < NP; ++h) {
+        float hn[HK], bn[3 * P];
+        if (h + 1 < NP) load_pair(hb, wb, h + 1, lane, hn, bn);
         sched_fence();
-        const float a = group_entry(hc, gx, gy, gz, q);
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bc[t], acc[t], 0, 0, 0);
+        group_entries(hc, gx, gy, gz, av);
+        mfmas(av, bc, acc);
         sched_fence();
-        if (s + 1 < C) {
+        if (h + 1 < NP) {
 #pragma unroll
           for (int i = 0; i < HK; ++i) hc[i] = hn[i];
 #pragma unroll
-          for (int t = 0; t < T; ++t) bc[t] = bn[t];
+          for (int i = 0; i < 3 * P; ++i) bc[i] = bn[i];
         }
       }
     } else {
-      float a = group_entry(hc, gx, gy, gz, q);
+      group_entries(hc, gx, gy, gz, av);
 #pragma unroll
-      for (int s = 0; s < C; ++s) {
-        float hn[HK], bn[T];
-        if (s + 1 < C) load_sample(hb, wb, s + 1, lane, hn, bn);
+      for (int h = 0; h < NP; ++h) {
+        float hn[HK], bn[3 * P];
+        if (h + 1 < NP) load_pair(hb, wb, h + 1, lane, hn, bn);
         sched_fence();
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bc[t], acc[t], 0, 0, 0);
+        mfmas(av, bc, acc);
         sched_fence();
-        if (s + 1 < C) {
-          a = group_entry(hn, gx, gy, gz, q);
+        if (h + 1 < NP) {
+          group_entries(hn, gx, gy, gz, av);
 #pragma unroll
-          for (int t = 0; t < T; ++t) bc[t] = bn[t];
+          for (int i = 0; i < 3 * P; ++i) bc[i] = bn[i];
         }
         sched_fence();
       }
@@ -251,11 +275,11 @@ struct MfmaGather {
   }
 
   // Starts the copy of the chunk at sample c into (lb, lh): wave w copies the
-  // factor blocks w, w + NW, ... and wave 0 the header.
+  // factor blocks w, w + NW, ... and wave 0 the headers.
   __device__ static __forceinline__ void stage(const MfmaArgs& a, int64_t c, int wave_in_wg,
                                                int lane, float4* lb, float4* lh) {
     const __amdgpu_buffer_rsrc_t rb =
-        buffer_rsrc(reinterpret_cast<const float4*>(a.wb) + c * (T * 16), NB * 64 * 16);
+        buffer_rsrc(reinterpret_cast<const float4*>(a.wb) + (c / 2) * (PF / 4), NB * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NB / NW; ++i) {
       const int blk = i * NW + wave_in_wg;
@@ -271,8 +295,19 @@ struct MfmaGather {
     __syncthreads();
   }
 
+  // Tile end: Re = P1 - P3, Im = P2 + P3 into the running totals.
+  __device__ static __forceinline__ void fold(f32x16 (&acc)[3][P], f32x16 (&tre)[P],
+                                              f32x16 (&tim)[P]) {
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      tre[t] += acc[0][t] - acc[2][t];
+      tim[t] += acc[1][t] + acc[2][t];
+      acc[0][t] = f32x16{}; acc[1][t] = f32x16{}; acc[2][t] = f32x16{};
+    }
+  }
+
   __device__ static void run(const MfmaArgs& a) {
-    __shared__ float4 sb0[C * T * 16], sb1[C * T * 16];
+    __shared__ float4 sb0[C / 2 * PF / 4], sb1[C / 2 * PF / 4];
     __shared__ float4 sh0[NH], sh1[NH];
     const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
     const int64_t wave = (int64_t)blockIdx.x * NW + wig;
@@ -280,7 +315,6 @@ struct MfmaGather {
     const int64_t n0 = vbase + (int64_t)(lane & 31) * V;  // first voxel of the lane's group
     const bool gin = n0 < a.N;
     const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
-    const float q = lane < 32 ? 0.25f : 0.0f;
     const bool regular = wave_regular<V>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
     const int32_t row = (int32_t)blockIdx.y;
     int64_t lo, hi;
@@ -292,18 +326,20 @@ struct MfmaGather {
     const int32_t cpt = (int32_t)(a.tile / C);
     if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
     publish();
-    f32x16 acc[T], tot[T];
+    f32x16 acc[3][P], tre[P], tim[P];
 #pragma unroll
-    for (int t = 0; t < T; ++t) { acc[t] = f32x16{}; tot[t] = f32x16{}; }
+    for (int t = 0; t < P; ++t) {
+      acc[0][t] = f32x16{}; acc[1][t] = f32x16{}; acc[2][t] = f32x16{};
+      tre[t] = f32x16{}; tim[t] = f32x16{};
+    }
     int32_t left = cpt;  // chunks left in the current tile
     for (int32_t ch = 0; ch < nch; ch += 2) {
       if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
-                      gx, gy, gz, q, acc);
+                      gx, gy, gz, acc);
       if (--left == 0) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        fold(acc, tre, tim);
         left = cpt;
       }
       publish();
@@ -311,32 +347,29 @@ struct MfmaGather {
       if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
-                      gx, gy, gz, q, acc);
+                      gx, gy, gz, acc);
       if (--left == 0) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        fold(acc, tre, tim);
         left = cpt;
       }
       publish();
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) tot[t] += acc[t];  // the last (partial) tile
+    fold(acc, tre, tim);  // the last (partial) tile
 
     // write-out: out[b][n], or this row's partial sums (irregular waves are
     // written by mfma_direct_kernel)
     if (!regular) return;
     float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
-    float* df = reinterpret_cast<float*>(dst);
     const int c = lane & 31;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int cc = 16 * t + c / 2;
+    for (int t = 0; t < P; ++t) {
+      const int cc = 32 * t + c;
       const int b = cc / V, j = cc % V;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
         const int64_t n = vbase + (int64_t)i * V + j;
-        if (n < a.N) df[2 * ((int64_t)b * a.N + n) + (c & 1)] = tot[t][v];
+        if (n < a.N) dst[(int64_t)b * a.N + n] = make_float2(tre[t][v], tim[t][v]);
       }
     }
   }
@@ -351,6 +384,7 @@ struct MfmaGather {
 template <int T, int BC, int TRIG>
 struct MfmaDirect {
   static constexpr int V = 16 * T / BC;
+  static constexpr int P = T / 2;
   static constexpr int HF = mfma_header_floats(TRIG);
   static constexpr int ND = V / 2;
 
@@ -403,14 +437,16 @@ struct MfmaDirect {
         for (int b = 0; b < BC; ++b) { are[i][b] = 0.0f; aim[i][b] = 0.0f; }
       for (int64_t m = t0; m < t1; ++m) {
         const float* hs = a.hdr + m * HF;
-        const float* wm = a.wb + m * (T * 64);
+        const float* wm = a.wb + (m >> 1) * (192 * P);
+        const int k = (int)(m & 1);
         float mr[BC], mi[BC];
 #pragma unroll
         for (int b = 0; b < BC; ++b) {
-          // Mu_b is the offset-0 column of vector b
+          // Mu_b is the offset-0 column of vector b: (fr, fi) of column cc
           const int cc = b * V;
-          mr[b] = wm[(2 * (cc % 16)) * T + cc / 16];
-          mi[b] = wm[(2 * (cc % 16) + 1) * T + cc / 16];
+          const float* e = wm + (32 * k + cc % 32) * (2 * P) + cc / 32;
+          mr[b] = e[0];
+          mi[b] = e[P];
         }
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
@@ -446,9 +482,10 @@ struct MfmaDirect {
   }
 };
 
-// Resident waves per SIMD the gather is compiled for: 4 with two factor
-// tiles (<= 128 VGPRs; 34 KB of LDS per 4-wave workgroup), 2 with four tiles
-// (64 accumulators + 64 running totals; 66 KB of LDS per workgroup).
+// Resident waves per SIMD the gather is compiled for: 4 with one tile of 32
+// complex columns (48 accumulators + 32 running totals, <= 128 VGPRs; 25 KB
+// of LDS per 4-wave workgroup), 2 with two tiles (96 accumulators + 64
+// running totals, <= 256 VGPRs; 50 KB of LDS per workgroup).
 template <int T>
 constexpr int mfma_waves_per_simd() { return T == 2 ? 4 : 2; }
 

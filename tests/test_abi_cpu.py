@@ -183,19 +183,19 @@ def test_workspace_bytes(lib):
 
 
 def test_workspace_bytes_mfma(lib):
-    # per pass: header [mpad][4 or 8] floats (256-aligned) + factors [mpad][2][64] floats,
+    # per pass: header [mpad][4 or 8] floats (256-aligned) + factors [mpad][48 T] floats (three per complex column; T = 2 on 16^3),
     # mpad = M rounded up to the 32-sample chunk
     def ws(M, N, batch=1, is_q=0, **kw):
         kw.setdefault("sample_splits", 1)
         kw.setdefault("engine", _lib.FHD_ENGINE_MFMA)
         return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
     a256 = lambda b: (b + 255) // 256 * 256
-    assert ws(1000, 4096, trig=1) == a256(1024 * 16) + 1024 * 512
-    assert ws(1000, 4096) == a256(1024 * 32) + 1024 * 512            # accurate: 8 header floats
-    assert ws(1000, 4096, is_q=1, trig=1) == a256(1024 * 16) + 1024 * 512
-    assert ws(33, 4096, trig=1) == a256(64 * 16) + 64 * 512
+    assert ws(1000, 4096, trig=1) == a256(1024 * 16) + 1024 * 384
+    assert ws(1000, 4096) == a256(1024 * 32) + 1024 * 384            # accurate: 8 header floats
+    assert ws(1000, 4096, is_q=1, trig=1) == a256(1024 * 16) + 1024 * 384
+    assert ws(33, 4096, trig=1) == a256(64 * 16) + 64 * 384
     # batch 5: passes of 4 and 1 vectors, same record size; 3 splits add [3][4][N] partials
-    one = a256(1024 * 16) + 1024 * 512
+    one = a256(1024 * 16) + 1024 * 384
     assert ws(1000, 50, batch=5, trig=1) == 2 * one
     assert ws(1000, 50, batch=5, trig=1, sample_splits=3) == 2 * one + a256(3 * 4 * 50 * 8)
     # the default engine is the matrix-core one
@@ -255,15 +255,15 @@ def test_describe_plan_mfma(lib):
     acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
     assert hw["engine"] == acc["engine"] == _lib.FHD_ENGINE_MFMA
     assert hw["voxels_per_lane"] == 64 and acc["voxels_per_lane"] == 64
-    assert hw["record_dwords"] == 4 + 256 and acc["record_dwords"] == 8 + 256
+    assert hw["record_dwords"] == 4 + 192 and acc["record_dwords"] == 8 + 192
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 512
     # 1024 waves of 32 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
-    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1024 + 16 * 128 ** 3 * 8
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 768 + 16 * 128 ** 3 * 8
     # two tiles (groups of 32) on request, or when the edge is not a multiple of 64
     two = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=32)
-    assert two["voxels_per_lane"] == 32 and two["record_dwords"] == 4 + 128 and two["engine"] == _lib.FHD_ENGINE_MFMA
-    assert two["workspace_bytes"] == 262144 * 16 + 262144 * 512 + 16 * 128 ** 3 * 8
+    assert two["voxels_per_lane"] == 32 and two["record_dwords"] == 4 + 96 and two["engine"] == _lib.FHD_ENGINE_MFMA
+    assert two["workspace_bytes"] == 262144 * 16 + 262144 * 384 + 16 * 128 ** 3 * 8
     assert fhd_describe_plan(1000, 96 ** 3, trig="hw")["voxels_per_lane"] == 32
     assert fhd_describe_plan(1000, 100, trig="hw")["voxels_per_lane"] == 32     # not a cube
     # 64^3: 128 waves x 16 rows fill 2 waves per SIMD; 32^3 x 2048: at most 8 rows of 256
@@ -277,7 +277,7 @@ def test_describe_plan_mfma(lib):
     # batched, 16 vectors on 96^3: four tiles, groups of 4 voxels; the partial buffer cap gives 18 rows
     b16 = fhd_describe_plan(500001, 96 ** 3, batch=16)
     assert b16["voxels_per_lane"] == 4 and b16["sample_splits"] == 18 and b16["padded_samples"] == 500032
-    assert b16["record_dwords"] == 8 + 256
+    assert b16["record_dwords"] == 8 + 192
     # 19 = 16 + 2 + 1 vectors: the single-vector pass needs 64 | 96, so two tiles for all passes
     b19 = fhd_describe_plan(500001, 96 ** 3, batch=19)
     assert b19["passes"] == 3 and b19["voxels_per_lane"] == 2
@@ -300,7 +300,7 @@ def test_describe_plan_zero_sizes(lib):
             r = fhd_describe_plan(M, N, is_q=is_q, trig="hw")
             assert r["sample_splits"] == 1
     assert fhd_describe_plan(100, 0, engine="valu")["workspace_bytes"] == (100 * 12 * 4 + 255) // 256 * 256
-    assert fhd_describe_plan(100, 0)["workspace_bytes"] == 128 * 32 + 128 * 512
+    assert fhd_describe_plan(100, 0)["workspace_bytes"] == 128 * 32 + 128 * 384
 
 
 # ----------------------------- forward operator -----------------------------
