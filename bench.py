@@ -5,10 +5,10 @@ One step = one pass of the whole hot path (per-sample Mu/record kernel, gather
 kernel, reduction of the sample-split rows) over the 128^3 stack-of-spirals
 workload, inputs resident in HBM.  Prints one JSON line.  The gather stage (the
 dominant kernel) is also timed on its own with HIP events on the stream it is
-launched on.  Its roofline: for the matrix-core engine, one complex
-multiply-accumulate (8 FLOP) per voxel-sample pair against the MI355X FP32
-matrix peak; for the VALU engine, the direct formulation's 14 FLOP per pair
-against the FP32 vector peak.  The CPU oracle is timed on a bounded voxel
+launched on.  Its roofline: for the matrix-core engine, the three real
+multiply-accumulates (6 FLOP) per voxel-sample pair of the three-multiplication
+complex product against the MI355X FP32 matrix peak; for the VALU engine, the
+direct formulation's 14 FLOP per pair against the FP32 vector peak.  The CPU oracle is timed on a bounded voxel
 sample of the same workload (rank 0, one GPU only).
 """
 from __future__ import annotations
@@ -27,9 +27,12 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # Direct formulation per voxel-sample pair: phase 5 + reduction 1 + complex MAC 8
 # (Q: real MAC 4), plus two transcendentals.
 FLOP_PER_PAIR = {"fhd": 14, "q": 10}
-# Factored formulation on the matrix cores: one complex MAC = 4 real MACs per
-# pair (the group phase and its sine are shared by 32 voxel columns).
-MFMA_FLOP_PER_PAIR = 8
+# Factored formulation on the matrix cores.  F^H D and Q: the complex product
+# of the group phases with the factor columns in the three-multiplication form,
+# 3 real MACs = 6 FLOP per pair (the group phase, its sine and cosine are shared
+# by 32 voxel columns).  Forward operator: the four-product form, 4 real MACs =
+# 8 FLOP per pair.
+MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 8}
 # HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Valid only for the kernel source (with the headers it includes) they were
@@ -37,12 +40,12 @@ MFMA_FLOP_PER_PAIR = 8
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "042fb11bb0a12168",
-        "fetch_bytes": 1249578.1 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b891735ac77011cd",
+        "fetch_bytes": 987410.7 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "042fb11bb0a12168",
-        "fetch_bytes": 1266158.3 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b891735ac77011cd",
+        "fetch_bytes": 1003828.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
         "source": "fhd_forward.hip", "kernel_sha256": "9f0c83307b628d98",
@@ -500,15 +503,15 @@ def main():
     plan = fhd_describe_plan(p.M, p.N, p.B, op=op, **opts)
     engine = {1: "valu", 2: "mfma"}[plan["engine"]]
     if forward:
-        achieved, bound = MFMA_FLOP_PER_PAIR * pairs / (g_avg * 1e-3) / 1e12, "mfma"
+        per_pair = MFMA_FLOP_PER_PAIR["forward"]
+        achieved, bound = per_pair * pairs / (g_avg * 1e-3) / 1e12, "mfma"
         kernel = ("fwd_gather_kernel: its launch rows in one step, timed alone; the image packing, "
                   "row reduction and (on a grid, empty) direct kernels are outside the interval")
-        per_pair = MFMA_FLOP_PER_PAIR
     elif engine == "mfma":
-        achieved, bound = MFMA_FLOP_PER_PAIR * pairs / (g_avg * 1e-3) / 1e12, "mfma"
+        per_pair = MFMA_FLOP_PER_PAIR["gather"]
+        achieved, bound = per_pair * pairs / (g_avg * 1e-3) / 1e12, "mfma"
         kernel = ("mfma_gather_kernel: its launch rows in one step, timed alone with the (empty on a "
                   "grid) mfma_direct_kernel; records and reduction kernels are outside the interval")
-        per_pair = MFMA_FLOP_PER_PAIR
     else:
         achieved, bound = direct_tflops, "alu"
         kernel = ("gather_kernel: its launches in one step, timed alone; the per-sample and reduce "
