@@ -27,12 +27,11 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # Direct formulation per voxel-sample pair: phase 5 + reduction 1 + complex MAC 8
 # (Q: real MAC 4), plus two transcendentals.
 FLOP_PER_PAIR = {"fhd": 14, "q": 10}
-# Factored formulation on the matrix cores.  F^H D and Q: the complex product
-# of the group phases with the factor columns in the three-multiplication form,
-# 3 real MACs = 6 FLOP per pair (the group phase, its sine and cosine are shared
-# by 32 voxel columns).  Forward operator: the four-product form, 4 real MACs =
-# 8 FLOP per pair.
-MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 8}
+# Factored formulation on the matrix cores (F^H D, Q and the forward
+# operator): the complex product of the group phases with the factor columns
+# in the three-multiplication form, 3 real MACs = 6 FLOP per pair (a group
+# phase with its sine and cosine is shared by 32 voxel columns).
+MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Valid only for the kernel source (with the headers it includes) they were

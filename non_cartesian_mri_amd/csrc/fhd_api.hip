@@ -362,10 +362,10 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   p.hdr_bytes = 0;
   p.ws_bytes = 0;
   for (int i = 0; i < p.npass; ++i) {
-    // header [gpad][4], image [gpad][T][64], list of flagged groups [1 + gpad] int32
+    // header [gpad][4], image [gpad][48 T], list of flagged groups [1 + gpad] int32
     p.pass_bytes[i] = p.gpad[i] == 0 ? 0
                       : align256((size_t)p.gpad[i] * 4 * sizeof(float)) +
-                            align256((size_t)p.gpad[i] * p.tiles * 64 * sizeof(float)) +
+                            align256((size_t)p.gpad[i] * ncmri::mfma_factor_floats(p.tiles) * sizeof(float)) +
                             (size_t)(p.gpad[i] + 1) * sizeof(int32_t);
     p.ws_bytes += align256(p.pass_bytes[i]);
   }
@@ -456,7 +456,7 @@ fhd_status run_forward(const float* kx, const float* ky, const float* kz, const 
   for (int i = 0; i < p.npass && result == FHD_OK; ++i) {
     const int bc = p.bc[i];
     const size_t hb = align256((size_t)p.gpad[i] * 4 * sizeof(float));
-    const size_t ib = align256((size_t)p.gpad[i] * p.tiles * 64 * sizeof(float));
+    const size_t ib = align256((size_t)p.gpad[i] * ncmri::mfma_factor_floats(p.tiles) * sizeof(float));
     ncmri::FwdArgs fa{kx, ky, kz, x, y, z, (const float2*)phi,
                       (const float2*)(rho ? rho + (int64_t)b0 * N : nullptr), M, N, p.gpad[i], p.tile,
                       p.g_split[i], (float*)base, (float*)(base + hb),
@@ -632,7 +632,7 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->tile = (int32_t)p.tile;
     info->passes = p.npass;
     info->record_dwords = p.npass == 0 ? 0
-                          : p.op == FHD_OP_FORWARD ? 4 + 64 * p.tiles
+                          : p.op == FHD_OP_FORWARD ? 4 + ncmri::mfma_factor_floats(p.tiles)
                           : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig, p.tiles)
                                                          : ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]);
     info->padded_samples = p.mpad;

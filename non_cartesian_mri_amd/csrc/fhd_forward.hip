@@ -11,16 +11,23 @@
 //   D[b][m] = phi_m sum_j exp(-i 2 pi k_m . d_j) G[m][j][b],
 //   G[m][j][b] = sum_g exp(-i 2 pi k_m . x_g) rho_b[x_g + d_j],
 //
-// and for 32 samples and 16 T complex columns (j, b) the sum over groups is
-// the real matrix product [Re | Im] (32 x 32T) += sum_g E_g (32 x 2) W_g (2 x 32T)
-// with E_g[m] = (cos, sin)(2 pi k_m . x_g) and W_g = [rr ri; ri -rr] per
-// column, i.e. (c - i s)(rr + i ri): one v_mfma_f32_32x32x2_f32 per tile and
-// group.  Each wave owns 32 samples (sample m in lanes m and m + 32: cosine and
-// sine, the cosine with a quarter turn added to the phase); the packed image
-// is streamed through LDS in 32-group chunks by LDS DMA, shared by the 4
-// waves of a workgroup, exactly as the adjoint streams its sample records.
-// After the last group the wave writes G to LDS and lanes 0-31 contract their
-// sample's row with exp(-i 2 pi k_m . d_j) and multiply by phi_m.
+// and for 32 samples and 16 T complex columns (j, b) the sum over groups is a
+// complex matrix product (samples x groups) * (groups x columns) with entries
+// (c - i s)(rr + i ri), (c, s) = (cos, sin)(2 pi k_m . x_g).  As in the
+// adjoint it is formed with three real products (the three-multiplication
+// form of a complex product):
+//
+//   P1 = sum (c - s) rr,   P2 = sum (c + s) ri,   P3 = sum s (rr + ri),
+//   Re = P1 + P3,          Im = P2 - P3,
+//
+// each one v_mfma_f32_32x32x2_f32 per tile of 32 complex columns with K = 2
+// running over a pair of groups.  Each wave owns 32 samples (lane l: sample
+// l % 32 at group 2 h + l / 32 of pair h; one phase, its sine and its cosine
+// per lane and pair); the packed image is streamed through LDS in 32-group
+// chunks by LDS DMA, shared by the 4 waves of a workgroup, exactly as the
+// adjoint streams its sample records.  After the last group the wave writes G
+// to LDS and lanes 0-31 contract their sample's row with
+// exp(-i 2 pi k_m . d_j) and multiply by phi_m.
 //
 // Groups whose voxels are not on the first group's offsets are packed as
 // zeros and flagged; one workgroup then lists them in increasing order
@@ -73,9 +80,13 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_pack_kernel(FwdArgs a, int T, 
   const int b = cc / V, j = cc % V;
   const int64_t n = n0 + j;
   const float2 r = (inside && reg && n < a.N) ? a.rho[(int64_t)b * a.N + n] : make_float2(0.0f, 0.0f);
-  float* w = a.gwb + (g * T + cc / 16) * 64;
-  const int c = cc % 16;
-  w[2 * c] = r.x; w[2 * c + 1] = r.y; w[32 + 2 * c] = r.y; w[33 + 2 * c] = -r.x;
+  // entry of column c = cc % 32 of tile t = cc / 32 at row g % 2 of the pair
+  const int P = T / 2;
+  const int t = cc / 32, lp = 32 * (int)(g & 1) + cc % 32;
+  float* pair = a.gwb + (g >> 1) * (192 * P);
+  float* wr = pair + lp * (2 * P) + t;
+  wr[0] = r.x; wr[P] = r.y;
+  pair[128 * P + lp * P + t] = r.x + r.y;
 }
 
 // Lists the flagged groups: each of the workgroup's lanes counts the flags of
@@ -123,20 +134,6 @@ struct SampleK {
       v[3] = kx - v[0]; v[4] = ky - v[1]; v[5] = kz - v[2];
     }
   }
-  // sin(2 pi (k . p + q)); the accurate path reduces kh . p exactly first.
-  __device__ __forceinline__ float sin_phase(float px, float py, float pz, float q) const {
-    if constexpr (TRIG == kTrigHw) {
-      const float t = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, __builtin_fmaf(v[0], px, q)));
-      return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(t));
-    } else {
-      float th = __builtin_fmaf(v[2], pz, __builtin_fmaf(v[1], py, __builtin_fmaf(v[0], px, q)));
-      th = th - __builtin_rintf(th);
-      const float tl = __builtin_fmaf(v[5], pz, __builtin_fmaf(v[4], py, v[3] * px));
-      float s, c;
-      sincos_turns(th + tl, s, c);
-      return s;
-    }
-  }
   // cos and sin of 2 pi k . p.
   __device__ __forceinline__ void sincos_phase(float px, float py, float pz, float& c, float& s) const {
     if constexpr (TRIG == kTrigHw) {
@@ -158,17 +155,22 @@ struct SampleK {
 template <int T, int BC, int TRIG>
 struct FwdGather {
   static constexpr int V = 16 * T / BC;
+  static constexpr int P = T / 2;                 // tiles of 32 complex columns
   static constexpr int C = kMfmaChunk;
   static constexpr int NW = kWorkgroup / 64;
-  static constexpr int NB = C * T * 16 / 64;  // 1 KiB image blocks per chunk
-  static constexpr int NH = C;                // header float4s per chunk (one per group)
-  static_assert(V >= 1 && V * BC == 16 * T, "group shape");
+  static constexpr int PF = 192 * P;              // image floats per pair of groups
+  static constexpr int NB = C / 2 * PF * 4 / 1024;  // 1 KiB image blocks per chunk
+  static constexpr int NH = C;                    // header float4s per chunk (one per group)
+  static constexpr int SB = C / 2 * PF / 4;       // float4s of one staging buffer
+  static constexpr int GW = 32 * 32 * P * 2 / 4;  // float4s of one wave's G block
+  static constexpr int LDS4 = 2 * SB > NW * GW ? 2 * SB : NW * GW;
+  static_assert(P >= 1 && V >= 1 && V * BC == 16 * T, "group shape");
   static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
 
   __device__ static __forceinline__ void stage(const FwdArgs& a, int64_t g, int wig, int lane,
                                                float4* lb, float4* lh) {
     const __amdgpu_buffer_rsrc_t rb =
-        buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + g * (T * 16), NB * 64 * 16);
+        buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + (g / 2) * (PF / 4), NB * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NB / NW; ++i) {
       const int blk = i * NW + wig;
@@ -183,54 +185,100 @@ struct FwdGather {
     __syncthreads();
   }
 
-  // One chunk of 32 groups, pipelined by one group like the adjoint's loop
-  // (and, on the accurate path, with the next group's A entry computed right
-  // after this group's MFMAs, as the adjoint does).
+  // Header of the lane's group and its B entries of pair h of the chunk.
+  __device__ static __forceinline__ void load_pair(const float* __restrict__ hb,
+                                                   const float* __restrict__ wb, int h, int lane,
+                                                   float (&hs)[3], float (&bv)[3 * P]) {
+    const float* hp = hb + (2 * h + (lane >> 5)) * 4;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) hs[i] = hp[i];
+    const float* pp = wb + h * PF;
+    if constexpr (P == 2) {
+      const float4 v = *reinterpret_cast<const float4*>(pp + lane * 4);
+      const float2 u = *reinterpret_cast<const float2*>(pp + 256 + lane * 2);
+      bv[0] = v.x; bv[1] = v.y; bv[2] = v.z; bv[3] = v.w; bv[4] = u.x; bv[5] = u.y;
+    } else if constexpr (P == 1) {
+      const float2 v = *reinterpret_cast<const float2*>(pp + lane * 2);
+      bv[0] = v.x; bv[1] = v.y; bv[2] = pp[128 + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * P; ++i) bv[i] = pp[lane * 2 * P + i];
+#pragma unroll
+      for (int t = 0; t < P; ++t) bv[2 * P + t] = pp[128 * P + lane * P + t];
+    }
+  }
+
+  // A entries (c - s, c + s, s) of the lane's (sample, group) phase.
+  __device__ static __forceinline__ void entries(const SampleK<TRIG>& k, const float (&hs)[3],
+                                                 float (&av)[3]) {
+    float c, s;
+    k.sincos_phase(hs[0], hs[1], hs[2], c, s);
+    av[0] = c - s;
+    av[1] = c + s;
+    av[2] = s;
+  }
+
+  __device__ static __forceinline__ void mfmas(const float (&av)[3], const float (&bv)[3 * P],
+                                               f32x16 (&acc)[3][P]) {
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[1], bv[P + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[2], bv[2 * P + t], acc[2][t], 0, 0, 0);
+    }
+  }
+
+  // One chunk of 32 groups (16 pairs), pipelined by one pair like the
+  // adjoint's loop (and, on the accurate path, with the next pair's A entries
+  // computed right after this pair's MFMAs, as the adjoint does).
   __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb,
-                                               int lane, const SampleK<TRIG>& k, float q,
-                                               f32x16 (&acc)[T]) {
-    float hc[3], bc[T];
+                                               int lane, const SampleK<TRIG>& k, f32x16 (&acc)[3][P]) {
+    constexpr int NP = C / 2;
+    float hc[3], bc[3 * P], av[3];
+    load_pair(hb, wb, 0, lane, hc, bc);
+    if constexpr (TRIG != kTrigHw) entries(k, hc, av);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) hc[i] = hb[i];
-#pragma unroll
-    for (int t = 0; t < T; ++t) bc[t] = wb[t * 64 + lane];
-    float e = 0.0f;
-    if constexpr (TRIG != kTrigHw) e = k.sin_phase(hc[0], hc[1], hc[2], q);
-#pragma unroll
-    for (int s = 0; s < C; ++s) {
-      float hn[3], bn[T];
-      if (s + 1 < C) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) hn[i] = hb[(s + 1) * 4 + i];
-#pragma unroll
-        for (int t = 0; t < T; ++t) bn[t] = wb[((s + 1) * T + t) * 64 + lane];
-      }
+    for (int h = 0; h < NP; ++h) {
+      float hn[3], bn[3 * P];
+      if (h + 1 < NP) load_pair(hb, wb, h + 1, lane, hn, bn);
       sched_fence();
-      if constexpr (TRIG == kTrigHw) e = k.sin_phase(hc[0], hc[1], hc[2], q);
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(e, bc[t], acc[t], 0, 0, 0);
+      if constexpr (TRIG == kTrigHw) entries(k, hc, av);
+      mfmas(av, bc, acc);
       sched_fence();
-      if (s + 1 < C) {
-        if constexpr (TRIG != kTrigHw) e = k.sin_phase(hn[0], hn[1], hn[2], q);
+      if (h + 1 < NP) {
+        if constexpr (TRIG != kTrigHw) entries(k, hn, av);
 #pragma unroll
         for (int i = 0; i < 3; ++i) hc[i] = hn[i];
 #pragma unroll
-        for (int t = 0; t < T; ++t) bc[t] = bn[t];
+        for (int i = 0; i < 3 * P; ++i) bc[i] = bn[i];
       }
       sched_fence();
     }
   }
 
+  // Tile end: Re = P1 + P3, Im = P2 - P3 into the running totals.
+  __device__ static __forceinline__ void fold(f32x16 (&acc)[3][P], f32x16 (&tre)[P],
+                                              f32x16 (&tim)[P]) {
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      tre[t] += acc[0][t] + acc[2][t];
+      tim[t] += acc[1][t] - acc[2][t];
+      acc[0][t] = f32x16{}; acc[1][t] = f32x16{}; acc[2][t] = f32x16{};
+    }
+  }
+
   __device__ static void run(const FwdArgs& a) {
-    __shared__ float4 sb0[C * T * 16], sb1[C * T * 16];
+    // two staging buffers while the groups stream, then the waves' G blocks
+    __shared__ float4 lds[LDS4];
     __shared__ float4 sh0[NH], sh1[NH];
+    float4* sb0 = lds;
+    float4* sb1 = lds + SB;
     const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
     const int64_t wave = (int64_t)blockIdx.x * NW + wig;
     const int64_t m = wave * 32 + (lane & 31);   // this lane's sample
     const bool valid = m < a.M;
     SampleK<TRIG> k;
     k.load(a, m, valid);
-    const float q = lane < 32 ? 0.25f : 0.0f;
 
     // this launch row's groups
     const int32_t row = (int32_t)blockIdx.y;
@@ -241,49 +289,48 @@ struct FwdGather {
     const int32_t cpt = (int32_t)(a.tile / C);
     if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
     publish();
-    f32x16 acc[T], tot[T];
+    f32x16 acc[3][P], tre[P], tim[P];
 #pragma unroll
-    for (int t = 0; t < T; ++t) { acc[t] = f32x16{}; tot[t] = f32x16{}; }
+    for (int t = 0; t < P; ++t) {
+      acc[0][t] = f32x16{}; acc[1][t] = f32x16{}; acc[2][t] = f32x16{};
+      tre[t] = f32x16{}; tim[t] = f32x16{};
+    }
     int32_t left = cpt;
     for (int32_t ch = 0; ch < nch; ch += 2) {
       if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
-      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, q, acc);
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
       if (--left == 0) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        fold(acc, tre, tim);
         left = cpt;
       }
       publish();
       if (ch + 1 >= nch) break;
       if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
-      chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, q, acc);
+      chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, acc);
       if (--left == 0) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) { tot[t] += acc[t]; acc[t] = f32x16{}; }
+        fold(acc, tre, tim);
         left = cpt;
       }
       publish();
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) tot[t] += acc[t];
+    fold(acc, tre, tim);
 
     // Finish.  Every wave has passed the last barrier, so the staging buffers
-    // are free: each wave stores its 32 x 32T block of G there (waves 0, 1 in
-    // sb0, waves 2, 3 in sb1; 4 T KiB each) ...
-    float* gl = reinterpret_cast<float*>(wig < 2 ? sb0 : sb1) + (wig & 1) * (32 * 32 * T);
+    // are free: each wave stores its 32 x 32 P complex block of G there ...
+    float2* gl = reinterpret_cast<float2*>(lds + wig * GW);
     const int c = lane & 31;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int t = 0; t < P; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-        gl[i * (32 * T) + 32 * t + c] = tot[t][v];
+        gl[i * (32 * P) + 32 * t + c] = make_float2(tre[t][v], tim[t][v]);
       }
     __syncthreads();
     // ... and lane i < 32 contracts row i (its sample) with exp(-i 2 pi k . d_j)
     // over the offsets j, then multiplies by phi_m.
     if (lane >= 32 || !valid) return;
-    const float* gr = gl + lane * (32 * T);
+    const float2* gr = gl + lane * (32 * P);
     float dre[BC], dim[BC];
 #pragma unroll
     for (int b = 0; b < BC; ++b) { dre[b] = 0.0f; dim[b] = 0.0f; }
@@ -294,11 +341,10 @@ struct FwdGather {
       if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
 #pragma unroll
       for (int b = 0; b < BC; ++b) {
-        const int cc = b * V + j;
-        const float gre = gr[2 * cc], gim = gr[2 * cc + 1];
+        const float2 gv = gr[b * V + j];
         // (cj - i sj)(gre + i gim)
-        dre[b] = __builtin_fmaf(cj, gre, __builtin_fmaf(sj, gim, dre[b]));
-        dim[b] = __builtin_fmaf(cj, gim, __builtin_fmaf(-sj, gre, dim[b]));
+        dre[b] = __builtin_fmaf(cj, gv.x, __builtin_fmaf(sj, gv.y, dre[b]));
+        dim[b] = __builtin_fmaf(cj, gv.y, __builtin_fmaf(-sj, gv.x, dim[b]));
       }
     }
     const float2 ph = a.phi[m];

@@ -123,9 +123,11 @@ struct MfmaArgs {
 // Packed image of one pass (groups g < gpad, gpad a multiple of kMfmaChunk):
 //   header ghdr[g][4]: x, y, z of the group's first voxel, and 1.0 when the
 //     group is not on the first group's offsets (0.0 otherwise);
-//   image  gwb[g][T][64]: complex column cc = 16 t + c holds rho_b[g V + j]
-//     (b = cc / V, j = cc % V; zero past N and in irregular groups) as the
-//     MFMA B operand rows [2c] = re, [2c+1] = im, [32+2c] = im, [33+2c] = -re.
+//   image, per pair of groups h = g / 2 (P = T / 2 tiles of 32 complex
+//     columns; complex column cc = 32 t + c holds r = rho_b[g V + j] with
+//     b = cc / V, j = cc % V; zero past N and in irregular groups), 192 P floats:
+//       gwb[h][p][2 P] : [t] = re, [P + t] = im;   gwb[h][128 P + p P + t] = re + im,
+//     p = 32 (g % 2) + c the lane that supplies the MFMA B entry.
 struct FwdArgs {
   const float* kx; const float* ky; const float* kz;
   const float* x; const float* y; const float* z;
@@ -136,7 +138,7 @@ struct FwdArgs {
   int64_t tile;          // groups per summation tile (multiple of kMfmaChunk)
   int64_t g_split;       // groups per launch row (multiple of kMfmaChunk)
   float* ghdr;           // [gpad][4]
-  float* gwb;            // [gpad][T][64]
+  float* gwb;            // [gpad / 2][192 P]
   int32_t* glist;        // [1 + groups]: count of groups off the common offsets, then their
                          // indices in increasing order
   float2* out;           // first output vector of this pass ([BC][M])

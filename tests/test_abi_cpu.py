@@ -342,9 +342,9 @@ def test_forward_plan(lib):
     # 128^3: four tiles, groups of 64 voxels -> 32,768 groups; 8192 waves of 32 samples fill the GPU
     p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
     assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 64
-    assert p["record_dwords"] == 4 + 256 and p["padded_samples"] == 262144
+    assert p["record_dwords"] == 4 + 192 and p["padded_samples"] == 262144
     assert p["sample_splits"] == 1 and p["tile"] == 256
-    pas = lambda g, T: a256(a256(g * 16) + a256(g * 256 * T) + 4 * (g + 1))
+    pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
     assert p["workspace_bytes"] == pas(32768, 4)
     assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw") == p["workspace_bytes"]
     # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 256 groups each)
