@@ -122,10 +122,11 @@ typedef struct fhd_opts {
   int32_t trig;            /* fhd_trig, default FHD_TRIG_ACCURATE */
   int32_t sum;             /* fhd_sum, default FHD_SUM_BLOCKED */
   int32_t voxels_per_lane; /* group size; 0 = automatic.  VALU engine: 1, 2, 4, 8 or 16
-                              voxels per lane.  MFMA engine: 32 or 64 voxels sharing one
-                              group phase in single-vector passes (2 or 4 factor tiles;
-                              batched passes keep the tiles, groups of 16 x tiles / vectors).
-                              With FHD_ENGINE_AUTO, 1-16 select VALU and 32 or 64 MFMA */
+                              voxels per lane.  MFMA engine: 32, 64 or 128 voxels sharing
+                              one group phase in single-vector passes (T = 2, 4 or 8 units
+                              of 16 complex columns; batched passes keep T, groups of
+                              16 T / vectors; 128 runs the four-sample engine).
+                              With FHD_ENGINE_AUTO, 1-16 select VALU and 32-128 MFMA */
   int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
   int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL.  Stages run in
                               separate calls must use the same sizes, options and

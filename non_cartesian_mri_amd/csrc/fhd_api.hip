@@ -108,11 +108,10 @@ int auto_voxels_per_lane(int64_t N, int64_t mpad) {
   return 1;
 }
 
-// The MFMA gather runs one wave per 32 voxel groups, 4 waves per SIMD with
-// two factor tiles and 2 with four.
+// The MFMA gather runs 4 waves per SIMD with T = 2 (one wave per 32 voxel
+// groups) and 2 with T = 4 (32 groups per wave) or T = 8 (16 groups per wave,
+// the four-sample engine).
 int64_t mfma_wave_quantum(int T) { return kSimds * (T == 2 ? 4 : 2); }
-
-int64_t mfma_waves(int64_t N, int V) { return ((N + V - 1) / V + 31) / 32; }
 
 // Edge L of a cubic voxel count N = L^3, else 0.
 int64_t cube_edge(int64_t N) {
@@ -123,16 +122,22 @@ int64_t cube_edge(int64_t N) {
   return 0;
 }
 
-// Factor tiles per group phase.  Groups of 16 T / BC consecutive voxels only
-// take the factored path when they tile the grid rows (x fastest); four tiles
-// halve the phase and sine work per MFMA but double the group length, so
-// they are chosen when N is a cube whose edge every pass's group divides.
-int auto_mfma_tiles(int64_t N, const int* bc, int npass) {
+// Units of 16 complex columns per group phase (T).  Groups of 16 T / BC
+// consecutive voxels only take the factored path when they tile the grid
+// rows (x fastest); more columns per phase cut the phase and sine work per
+// MFMA but lengthen the group, so the largest T <= tmax is chosen whose group
+// every pass's divides the edge when N is a cube (else 2).  T = 8 (groups of
+// 128 voxels for one vector) runs the four-sample engine.
+int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax) {
   const int64_t L = cube_edge(N);
   if (L == 0) return 2;
-  for (int i = 0; i < npass; ++i)
-    if (L % (64 / bc[i]) != 0) return 2;
-  return 4;
+  for (int T = tmax; T > 2; T /= 2) {
+    bool ok = true;
+    for (int i = 0; i < npass; ++i)
+      if (L % (16 * T / bc[i]) != 0) ok = false;
+    if (ok) return T;
+  }
+  return 2;
 }
 
 // Sample splits.  Rows that start at different points of the record stream
@@ -179,8 +184,8 @@ fhd_status validate(int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
   if (o->sample_splits < 0 || o->sample_splits > kMaxSplits)
     return fail(FHD_ERR_INVALID_ARGUMENT, "sample_splits must be in [0, %d] (got %d)", kMaxSplits, o->sample_splits);
   const int V = o->voxels_per_lane;
-  if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16 && V != 32 && V != 64)
-    return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8, 16, 32 or 64 (got %d)", V);
+  if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16 && V != 32 && V != 64 && V != 128)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8, 16, 32, 64 or 128 (got %d)", V);
   if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA)
     return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
   if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
@@ -200,7 +205,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   if (engine == FHD_ENGINE_MFMA && o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the MFMA engine sums blocked or plain, not Kahan");
   if (engine == FHD_ENGINE_MFMA && V != 0 && V < 32)
-    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32 or 64 voxels (got %d)", V);
+    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32, 64 or 128 voxels (got %d)", V);
   if (engine == FHD_ENGINE_VALU && V > 16)
     return fail(FHD_ERR_INVALID_ARGUMENT, "VALU group sizes are 1 to 16 voxels (got %d)", V);
   const bool mfma = engine == FHD_ENGINE_MFMA;
@@ -222,7 +227,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
   p.tiles = 0;
   if (mfma) {
-    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass);
+    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8);
     V = 16 * p.tiles / p.bc[0];  // columns of a group: voxels x vectors
   } else if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
@@ -245,7 +250,8 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   int32_t splits = o->sample_splits;
   if (o->sum == FHD_SUM_PLAIN) splits = 1;  // a single running sum by definition
   else if (splits == 0)
-    splits = mfma ? auto_splits(mfma_waves(N, V), mfma_wave_quantum(p.tiles), N, p.bc[0], p.mpad)
+    splits = mfma ? auto_splits(ncmri::mfma_gather_waves(N, p.tiles, p.bc[0]), mfma_wave_quantum(p.tiles),
+                                N, p.bc[0], p.mpad)
                   : auto_splits(waves_for(N, V), kWaveQuantum, N, p.bc[0], p.mpad);
   if (p.mpad == 0) splits = 1;
   p.m_split = p.mpad;
@@ -293,8 +299,8 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only");
   if (o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator sums blocked or plain, not Kahan");
-  if (V != 0 && V < 32)
-    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32 or 64 voxels (got %d)", V);
+  if (V != 0 && (V < 32 || V > 64))
+    return fail(FHD_ERR_INVALID_ARGUMENT, "forward-operator group sizes are 32 or 64 voxels (got %d)", V);
   const int64_t C = ncmri::kMfmaChunk;
   p.op = FHD_OP_FORWARD;
   p.is_q = 0;
@@ -310,7 +316,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   int left = batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass);
+  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 4);
   p.V = 16 * p.tiles / p.bc[0];
   int64_t gmax = 0, gmin = -1;
   for (int i = 0; i < p.npass; ++i) {

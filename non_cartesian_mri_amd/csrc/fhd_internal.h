@@ -78,6 +78,15 @@ bool gather_supported(int is_q, int V, int BC);
 // real products per tile (the three-multiplication complex product) with
 // v_mfma_f32_32x32x2_f32, the K dimension running over the two samples.
 constexpr int kMfmaChunk = 32;   // samples per LDS chunk; records are padded to it
+constexpr int kMfma4Waves = 8;   // waves per workgroup of the four-sample engine (T = 8)
+
+// Waves of a gather launch row: 32 groups per wave (T = 2, 4: two samples
+// per v_mfma_f32_32x32x2_f32) or 16 (T = 8: four samples per
+// v_mfma_f32_16x16x4_f32), groups of V = 16 T / BC voxels.
+inline int64_t mfma_gather_waves(int64_t N, int T, int BC) {
+  const int64_t V = 16 * T / BC, G = T == 8 ? 16 : 32;
+  return ((N + V - 1) / V + G - 1) / G;
+}
 
 inline constexpr int mfma_header_floats(int trig) { return trig == kTrigHw ? 4 : 8; }
 // factor floats per sample: 3 values per complex column
@@ -88,7 +97,11 @@ inline constexpr int mfma_record_dwords(int trig, int T) { return mfma_header_fl
 // Records of one sample m for the MFMA engine (all float32):
 //   header hdr[m][]  HW trig:       kx, ky, kz, 0
 //                    accurate trig: khx, khy, khz, 0, klx, kly, klz, 0
-//   factors, per pair of samples h = m / 2 (P = T / 2 tiles of 32 complex
+//   factors, T = 8 (four-sample engine): per block of four samples q = m / 4,
+//     entry e = u T + t (u = 0: fr, 1: fi, 2: fr + fi; tile t of 16 complex
+//     columns, cc = 16 t + c) of lane p = 16 (m % 4) + c at
+//     wb[q][e / 4][p][e % 4] (192 T floats per block);
+//   factors, T = 2, 4 (two-sample engine), per pair of samples h = m / 2 (P = T / 2 tiles of 32 complex
 //     columns; complex column cc = 32 t + c holds f = Mu_b exp(i 2 pi k.d_j)
 //     with b = cc / V, j = cc % V, V = 16 T / BC), 192 P floats per pair:
 //       wb[h][p][2 P]   : [t] = fr, [P + t] = fi

@@ -72,15 +72,29 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   const int HF = mfma_header_floats(trig);
   const int V = cols / BC;
   float* h = a.hdr + m * HF;
-  // entry of column c = cc % 32 of tile t = cc / 32 at row m % 2
-  const int t = cc / 32, lp = 32 * (int)(m & 1) + cc % 32;
-  float* pair = a.wb + (m >> 1) * (192 * P);
-  float* wr = pair + lp * (2 * P) + t;            // fr; fi at + P
-  float* ws = pair + 128 * P + lp * P + t;        // fr + fi
+  float *wr, *wi, *ws;  // destinations of fr, fi, fr + fi
+  if (T == 8) {
+    // four-sample engine: entry e = u T + t (u = fr, fi, fr + fi; tile t =
+    // cc / 16) of lane p = 16 (m % 4) + cc % 16, in float4 slices of a block
+    // of four samples: [m / 4][e / 4][p][e % 4]
+    const int t = cc / 16, lp = 16 * (int)(m & 3) + cc % 16;
+    float* blk = a.wb + (m >> 2) * (192 * T);
+    wr = blk + ((t >> 2) * 64 + lp) * 4 + (t & 3);
+    wi = blk + (((T + t) >> 2) * 64 + lp) * 4 + ((T + t) & 3);
+    ws = blk + (((2 * T + t) >> 2) * 64 + lp) * 4 + ((2 * T + t) & 3);
+  } else {
+    // two-sample engine: entry of column c = cc % 32 of tile t = cc / 32 at
+    // row m % 2 of the pair
+    const int t = cc / 32, lp = 32 * (int)(m & 1) + cc % 32;
+    float* pair = a.wb + (m >> 1) * (192 * P);
+    wr = pair + lp * (2 * P) + t;
+    wi = wr + P;
+    ws = pair + 128 * P + lp * P + t;
+  }
   if (m >= a.M) {  // padding sample: contributes exactly zero
     if (cc == 0)
       for (int i = 0; i < HF; ++i) h[i] = 0.0f;
-    wr[0] = 0.0f; wr[P] = 0.0f; ws[0] = 0.0f;
+    wr[0] = 0.0f; wi[0] = 0.0f; ws[0] = 0.0f;
     return;
   }
   const float kx = a.kx[m], ky = a.ky[m], kz = a.kz[m];
@@ -117,22 +131,25 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
     mi = pr * d.y - pim * d.x;
   }
   const double fr = mr * cj - mi * sj, fi = mr * sj + mi * cj;
-  wr[0] = (float)fr; wr[P] = (float)fi; ws[0] = (float)(fr + fi);
+  wr[0] = (float)fr; wi[0] = (float)fi; ws[0] = (float)(fr + fi);
 }
 
 // ---------------------------------------------------------------------------
-// Wave w of either gather kernel owns the voxel groups 32 w .. 32 w + 31 of V
-// voxels each, i.e. voxels [32 V w, 32 V (w + 1)).  The wave is "regular" when
-// every group's voxels sit at the offsets of the first group (exact double
-// comparison of the coordinate differences); lanes l and l + 32 share group
-// l % 32 and split its voxels.  Returns the wave-uniform vote.
-template <int V>
+// Wave w of either gather kernel owns the voxel groups G w .. G w + G - 1 of V
+// voxels each (G = 32 for the two-sample engine, 16 for the four-sample
+// engine), i.e. voxels [G V w, G V (w + 1)).  The wave is "regular" when every
+// group's voxels sit at the offsets of the first group (exact double
+// comparison of the coordinate differences); the 64 / G lanes l = i mod G of
+// group i split its voxels.  Returns the wave-uniform vote.
+template <int V, int G = 32>
 __device__ __forceinline__ bool wave_regular(const float* __restrict__ x, const float* __restrict__ y,
                                              const float* __restrict__ z, int64_t N, int64_t n0,
                                              int lane, float gx, float gy, float gz) {
+  constexpr int parts = 64 / G, per = (V + parts - 1) / parts;
   bool reg = true;
   const double bx = x[0], by = y[0], bz = z[0];
-  const int j0 = lane < 32 ? 1 : V / 2, j1 = lane < 32 ? V / 2 : V;
+  const int r = lane / G;
+  const int j0 = r * per > 1 ? r * per : 1, j1 = (r + 1) * per < V ? (r + 1) * per : V;
   for (int j = j0; j < j1; ++j) {
     const int64_t n = n0 + j;
     if (n < N)
@@ -152,6 +169,39 @@ __device__ __forceinline__ void row_range(int64_t m_split, int64_t mpad, int32_t
 }
 
 // ---------------------------------------------------------------------------
+// cos and sin of the phase 2 pi k.x of one point (x, y, z) from a sample
+// header hs: HW trig reduces the phase in turns with fract and feeds v_sin /
+// v_cos; the accurate path reduces kh.x exactly (kh a multiple of 2^-12, so
+// kh.x is exact for integer or half-integer coordinates of moderate size),
+// adds kl.x and evaluates the quarter-turn polynomials.
+template <int TRIG>
+__device__ __forceinline__ void phase_sincos(const float* hs, float x, float y, float z, float& c,
+                                             float& s) {
+  if constexpr (TRIG == kTrigHw) {
+    const float t = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
+    const float f = __builtin_amdgcn_fractf(t);
+    s = __builtin_amdgcn_sinf(f);
+    c = __builtin_amdgcn_cosf(f);
+  } else {
+    float th = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
+    th = th - __builtin_rintf(th);
+    const float tl = __builtin_fmaf(hs[6], z, __builtin_fmaf(hs[5], y, hs[4] * x));
+    sincos_turns(th + tl, s, c);
+  }
+}
+
+// A-operand entries of a group phase in the three-product form: (c + s, c - s, s).
+template <int TRIG>
+__device__ __forceinline__ void group_entries(const float* hs, float gx, float gy, float gz,
+                                              float (&av)[3]) {
+  float c, s;
+  phase_sincos<TRIG>(hs, gx, gy, gz, c, s);
+  av[0] = c + s;
+  av[1] = c - s;
+  av[2] = s;
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core gather (regular waves).
 template <int T, int BC, int TRIG>
 struct MfmaGather {
@@ -167,29 +217,6 @@ struct MfmaGather {
   static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
 
   static constexpr int HK = TRIG == kTrigHw ? 3 : 7;  // header floats a sample's phase reads
-
-  // A-operand entries of the lane's group at its sample: (c + s, c - s, s) of
-  // the group phase.
-  __device__ static __forceinline__ void group_entries(const float (&hs)[HK], float gx, float gy,
-                                                       float gz, float (&av)[3]) {
-    float s, c;
-    if constexpr (TRIG == kTrigHw) {
-      const float t = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, hs[0] * gx));
-      const float f = __builtin_amdgcn_fractf(t);
-      s = __builtin_amdgcn_sinf(f);
-      c = __builtin_amdgcn_cosf(f);
-    } else {
-      // kh.x is exact for integer or half-integer coordinates of moderate
-      // size, so its fractional part is exact.
-      float th = __builtin_fmaf(hs[2], gz, __builtin_fmaf(hs[1], gy, hs[0] * gx));
-      th = th - __builtin_rintf(th);
-      const float tl = __builtin_fmaf(hs[6], gz, __builtin_fmaf(hs[5], gy, hs[4] * gx));
-      sincos_turns(th + tl, s, c);
-    }
-    av[0] = c + s;
-    av[1] = c - s;
-    av[2] = s;
-  }
 
   // Header of the lane's sample and its B-operand entries of pair h of the
   // chunk in LDS: fr (P), fi (P) in one read, fr + fi (P) in another.
@@ -245,7 +272,7 @@ struct MfmaGather {
         float hn[HK], bn[3 * P];
         if (h + 1 < NP) load_pair(hb, wb, h + 1, lane, hn, bn);
         sched_fence();
-        group_entries(hc, gx, gy, gz, av);
+        group_entries<TRIG>(hc, gx, gy, gz, av);
         mfmas(av, bc, acc);
         sched_fence();
         if (h + 1 < NP) {
@@ -256,7 +283,7 @@ struct MfmaGather {
         }
       }
     } else {
-      group_entries(hc, gx, gy, gz, av);
+      group_entries<TRIG>(hc, gx, gy, gz, av);
 #pragma unroll
       for (int h = 0; h < NP; ++h) {
         float hn[HK], bn[3 * P];
@@ -265,7 +292,7 @@ struct MfmaGather {
         mfmas(av, bc, acc);
         sched_fence();
         if (h + 1 < NP) {
-          group_entries(hn, gx, gy, gz, av);
+          group_entries<TRIG>(hn, gx, gy, gz, av);
 #pragma unroll
           for (int i = 0; i < 3 * P; ++i) bc[i] = bn[i];
         }
@@ -388,22 +415,6 @@ struct MfmaDirect {
   static constexpr int HF = mfma_header_floats(TRIG);
   static constexpr int ND = V / 2;
 
-  // sin and cos of one voxel's phase (direct path).
-  __device__ static __forceinline__ void voxel_sincos(const float* hs, float x, float y, float z,
-                                                      float& c, float& s) {
-    if constexpr (TRIG == kTrigHw) {
-      const float t = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
-      const float f = __builtin_amdgcn_fractf(t);
-      s = __builtin_amdgcn_sinf(f);
-      c = __builtin_amdgcn_cosf(f);
-    } else {
-      float th = __builtin_fmaf(hs[2], z, __builtin_fmaf(hs[1], y, hs[0] * x));
-      th = th - __builtin_rintf(th);
-      const float tl = __builtin_fmaf(hs[6], z, __builtin_fmaf(hs[5], y, hs[4] * x));
-      sincos_turns(th + tl, s, c);
-    }
-  }
-
   __device__ static void run(const MfmaArgs& a, int32_t splits) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
@@ -451,7 +462,7 @@ struct MfmaDirect {
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
           float c, sn;
-          voxel_sincos(hs, vx[i], vy[i], vz[i], c, sn);
+          phase_sincos<TRIG>(hs, vx[i], vy[i], vz[i], c, sn);
 #pragma unroll
           for (int b = 0; b < BC; ++b) {
             are[i][b] = __builtin_fmaf(mr[b], c, __builtin_fmaf(-mi[b], sn, are[i][b]));
@@ -482,6 +493,285 @@ struct MfmaDirect {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Four-sample matrix-core gather (regular waves), v_mfma_f32_16x16x4_f32:
+// A[i][k] = lane 16 k + i, B[k][j] = lane 16 k + j, D[i][j] = register i % 4
+// of lane 16 (i / 4) + j (checked on gfx950).  A wave owns 16 groups of V
+// voxels; lane l supplies group l % 16 at sample 4 q + l / 16 of block q, so
+// each lane evaluates one phase with its sine and cosine per four samples and
+// the 16 x 16 products take 3 T MFMAs per block: with T = 8 tiles of 16
+// complex columns that is 24 MFMAs (768 matrix cycles) per phase, twice the
+// two-sample engine's 6 per pair at the same register count.  Records stream
+// through LDS in 32-sample chunks (8 blocks, 48 KB with T = 8), so one
+// workgroup of 8 waves (2 per SIMD) per CU shares them.
+template <int T, int BC, int TRIG>
+struct MfmaGather4 {
+  static constexpr int V = 16 * T / BC;                // voxels per group
+  static constexpr int HF = mfma_header_floats(TRIG);
+  static constexpr int C = kMfmaChunk;
+  static constexpr int NW = kMfma4Waves;               // waves per workgroup
+  static constexpr int QF = 192 * T;                   // factor floats per block of 4 samples
+  static constexpr int NS = 3 * T / 4;                 // float4 slices per lane and block
+  static constexpr int NB = C / 4 * QF * 4 / 1024;     // 1 KiB factor blocks per chunk
+  static constexpr int NH = C * HF / 4;                // header float4s per chunk
+  static constexpr int HK = TRIG == kTrigHw ? 3 : 7;
+  static_assert(T % 4 == 0 && V >= 1 && V * BC == 16 * T, "group shape");
+  static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
+
+  __device__ static __forceinline__ void load_block(const float* __restrict__ hb,
+                                                    const float* __restrict__ wb, int q, int lane,
+                                                    float (&hs)[HK], float (&bv)[3 * T]) {
+    const float* hp = hb + (4 * q + (lane >> 4)) * HF;
+#pragma unroll
+    for (int i = 0; i < HK; ++i) hs[i] = hp[i];
+    const float* pp = wb + q * QF;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  __device__ static __forceinline__ void mfmas(const float (&av)[3], const float (&bv)[3 * T],
+                                               f32x4 (&acc)[3][T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[T + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2 * T + t], acc[2][t], 0, 0, 0);
+    }
+  }
+
+  // One chunk, software-pipelined by one block of samples exactly like the
+  // two-sample engine (HW: A entries right before the block's MFMAs;
+  // accurate: one block ahead, right after the previous block's MFMAs).
+  __device__ static __forceinline__ void regular_chunk(const float* __restrict__ hb,
+                                                       const float* __restrict__ wb, int lane,
+                                                       float gx, float gy, float gz,
+                                                       f32x4 (&acc)[3][T]) {
+    constexpr int NQ = C / 4;
+    float hc[HK], bc[3 * T], av[3];
+    load_block(hb, wb, 0, lane, hc, bc);
+    if constexpr (TRIG == kTrigHw) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        float hn[HK], bn[3 * T];
+        if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
+        sched_fence();
+        group_entries<TRIG>(hc, gx, gy, gz, av);
+        mfmas(av, bc, acc);
+        sched_fence();
+        if (q + 1 < NQ) {
+#pragma unroll
+          for (int i = 0; i < HK; ++i) hc[i] = hn[i];
+#pragma unroll
+          for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
+        }
+      }
+    } else {
+      group_entries<TRIG>(hc, gx, gy, gz, av);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        float hn[HK], bn[3 * T];
+        if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
+        sched_fence();
+        mfmas(av, bc, acc);
+        sched_fence();
+        if (q + 1 < NQ) {
+          group_entries<TRIG>(hn, gx, gy, gz, av);
+#pragma unroll
+          for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
+        }
+        sched_fence();
+      }
+    }
+  }
+
+  // Starts the copy of the chunk at sample c: wave w copies the factor blocks
+  // w, w + NW, ... and wave 0 the headers.
+  // Starts the copy of the chunk at sample c: wave w copies the factor blocks
+  // w, w + NW, ... and wave 0 the headers.
+  __device__ static __forceinline__ void stage(const MfmaArgs& a, int64_t c, int wave_in_wg,
+                                               int lane, float4* lb, float4* lh) {
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(reinterpret_cast<const float4*>(a.wb) + (c / 4) * (QF / 4), NB * 64 * 16);
+#pragma unroll
+    for (int i = 0; i < NB / NW; ++i) {
+      const int blk = i * NW + wave_in_wg;
+      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
+    }
+    if (wave_in_wg == 0 && lane < NH)
+      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.hdr) + c * (HF / 4), NH * 16), lane * 16, lh);
+  }
+
+  // Chunk copies complete (this wave's) and visible to the workgroup.
+  __device__ static __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[T], f32x4 (&tim)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      tre[t] += acc[0][t] - acc[2][t];
+      tim[t] += acc[1][t] + acc[2][t];
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
+    }
+  }
+
+  __device__ static void run(const MfmaArgs& a) {
+    __shared__ float4 sb0[C / 4 * QF / 4], sb1[C / 4 * QF / 4];
+    __shared__ float4 sh0[NH], sh1[NH];
+    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int64_t wave = (int64_t)blockIdx.x * NW + wig;
+    const int64_t vbase = wave * 16 * V;                  // first voxel of the wave
+    const int64_t n0 = vbase + (int64_t)(lane & 15) * V;  // first voxel of the lane's group
+    const bool gin = n0 < a.N;
+    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
+    const bool regular = wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
+    const int32_t row = (int32_t)blockIdx.y;
+    int64_t lo, hi;
+    row_range(a.m_split, a.mpad, row, lo, hi);
+
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    const int32_t cpt = (int32_t)(a.tile / C);
+    if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
+    publish();
+    f32x4 acc[3][T], tre[T], tim[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
+      tre[t] = f32x4{}; tim[t] = f32x4{};
+    }
+    int32_t left = cpt;
+    for (int32_t ch = 0; ch < nch; ch += 2) {
+      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
+                      gx, gy, gz, acc);
+      if (--left == 0) {
+        fold(acc, tre, tim);
+        left = cpt;
+      }
+      publish();
+      if (ch + 1 >= nch) break;
+      if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
+                      gx, gy, gz, acc);
+      if (--left == 0) {
+        fold(acc, tre, tim);
+        left = cpt;
+      }
+      publish();
+    }
+    fold(acc, tre, tim);
+
+    if (!regular) return;
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+    const int c = lane & 15;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int cc = 16 * t + c;
+      const int b = cc / V, j = cc % V;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (lane >> 4) + r;
+        const int64_t n = vbase + (int64_t)i * V + j;
+        if (n < a.N) dst[(int64_t)b * a.N + n] = make_float2(tre[t][r], tim[t][r]);
+      }
+    }
+  }
+};
+
+// Direct gather for the irregular waves of the four-sample engine (one launch
+// row; all samples): lane l of wave w owns voxels 16 V w + l + 64 i,
+// i < V / 4, taken four at a time; records are read with wave-uniform scalar
+// loads (Mu_b = (fr, fi) of the offset-0 column of vector b).
+template <int T, int BC, int TRIG>
+struct MfmaDirect4 {
+  static constexpr int V = 16 * T / BC;
+  static constexpr int ND = V / 4;     // voxels per lane
+  static constexpr int NV = ND < 4 ? ND : 4;  // voxels per pass over the samples
+
+  __device__ static void run(const MfmaArgs& a, int32_t splits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
+    const int64_t vbase = wave * 16 * V;
+    if (vbase >= a.N) return;
+    const int64_t n0 = vbase + (int64_t)(lane & 15) * V;
+    const bool gin = n0 < a.N;
+    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
+    if (wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz)) return;
+    constexpr int HF = mfma_header_floats(TRIG);
+    for (int i0 = 0; i0 < ND; i0 += NV) {
+      float vx[NV], vy[NV], vz[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int64_t n = vbase + lane + 64 * (i0 + i);
+        const bool ok = n < a.N;
+        vx[i] = ok ? a.x[n] : 0.0f;
+        vy[i] = ok ? a.y[n] : 0.0f;
+        vz[i] = ok ? a.z[n] : 0.0f;
+      }
+      float tre[NV][BC], tim[NV][BC];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int b = 0; b < BC; ++b) { tre[i][b] = 0.0f; tim[i][b] = 0.0f; }
+      for (int64_t t0 = 0; t0 < a.mpad; t0 += a.tile) {
+        const int64_t t1 = (a.mpad - t0 > a.tile) ? t0 + a.tile : a.mpad;
+        float are[NV][BC], aim[NV][BC];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int b = 0; b < BC; ++b) { are[i][b] = 0.0f; aim[i][b] = 0.0f; }
+        for (int64_t m = t0; m < t1; ++m) {
+          const float* hs = a.hdr + m * HF;
+          const float* blk = a.wb + (m >> 2) * (192 * T);
+          const int k = (int)(m & 3);
+          float mr[BC], mi[BC];
+#pragma unroll
+          for (int b = 0; b < BC; ++b) {
+            const int cc = b * V, t = cc / 16, p = 16 * k + cc % 16;
+            mr[b] = blk[((t >> 2) * 64 + p) * 4 + (t & 3)];
+            mi[b] = blk[(((T + t) >> 2) * 64 + p) * 4 + ((T + t) & 3)];
+          }
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            float c, sn;
+            phase_sincos<TRIG>(hs, vx[i], vy[i], vz[i], c, sn);
+#pragma unroll
+            for (int b = 0; b < BC; ++b) {
+              are[i][b] = __builtin_fmaf(mr[b], c, __builtin_fmaf(-mi[b], sn, are[i][b]));
+              aim[i][b] = __builtin_fmaf(mi[b], c, __builtin_fmaf(mr[b], sn, aim[i][b]));
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+          for (int b = 0; b < BC; ++b) { tre[i][b] += are[i][b]; tim[i][b] += aim[i][b]; }
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int64_t n = vbase + lane + 64 * (i0 + i);
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+          if (a.partial) {
+            for (int32_t r = 0; r < splits; ++r)
+              a.partial[((int64_t)r * BC + b) * a.N + n] =
+                  r == 0 ? make_float2(tre[i][b], tim[i][b]) : make_float2(0.0f, 0.0f);
+          } else {
+            a.out[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
+          }
+        }
+      }
+    }
+  }
+};
+
 // Resident waves per SIMD the gather is compiled for: 4 with one tile of 32
 // complex columns (48 accumulators + 32 running totals, <= 128 VGPRs; 25 KB
 // of LDS per 4-wave workgroup), 2 with two tiles (96 accumulators + 64
@@ -500,6 +790,19 @@ __global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int
   MfmaDirect<T, BC, TRIG>::run(a, splits);
 }
 
+// Four-sample engine: one 8-wave workgroup per CU (96 KB of staging), 2 waves
+// per SIMD.
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
+mfma4_gather_kernel(MfmaArgs a) {
+  MfmaGather4<T, BC, TRIG>::run(a);
+}
+
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a, int32_t splits) {
+  MfmaDirect4<T, BC, TRIG>::run(a, splits);
+}
+
 using MfmaFn = void (*)(MfmaArgs);
 using DirectFn = void (*)(MfmaArgs, int32_t);
 
@@ -510,8 +813,13 @@ struct MfmaPair {
 
 template <int T, int BC>
 MfmaPair pick_mfma(int trig) {
-  if (trig == kTrigHw) return {mfma_gather_kernel<T, BC, kTrigHw>, mfma_direct_kernel<T, BC, kTrigHw>};
-  return {mfma_gather_kernel<T, BC, kTrigAccurate>, mfma_direct_kernel<T, BC, kTrigAccurate>};
+  if constexpr (T == 8) {
+    if (trig == kTrigHw) return {mfma4_gather_kernel<T, BC, kTrigHw>, mfma4_direct_kernel<T, BC, kTrigHw>};
+    return {mfma4_gather_kernel<T, BC, kTrigAccurate>, mfma4_direct_kernel<T, BC, kTrigAccurate>};
+  } else {
+    if (trig == kTrigHw) return {mfma_gather_kernel<T, BC, kTrigHw>, mfma_direct_kernel<T, BC, kTrigHw>};
+    return {mfma_gather_kernel<T, BC, kTrigAccurate>, mfma_direct_kernel<T, BC, kTrigAccurate>};
+  }
 }
 
 template <int T>
@@ -529,6 +837,7 @@ MfmaPair select_bc(int trig, int BC) {
 MfmaPair select_mfma(int trig, int T, int BC) {
   if (T == 2) return select_bc<2>(trig, BC);
   if (T == 4) return select_bc<4>(trig, BC);
+  if (T == 8) return select_bc<8>(trig, BC);
   return {nullptr, nullptr};
 }
 
@@ -558,13 +867,17 @@ hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const Mfm
     return hipErrorInvalidValue;
   if (a.N <= 0) return hipSuccess;
   const int V = 16 * T / BC;
-  const int64_t groups = (a.N + V - 1) / V;
-  const int64_t waves = (groups + 31) / 32;
-  const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
-  hipLaunchKernelGGL(fn.gather, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
+  const int64_t waves = mfma_gather_waves(a.N, T, BC);
+  // gather: workgroups of 4 waves (two-sample engine) or 8 (four-sample);
+  // direct: workgroups of 4 waves over the same wave numbering
+  const int wg_waves = T == 8 ? kMfma4Waves : kWorkgroup / 64;
+  const int64_t blocks = (waves + wg_waves - 1) / wg_waves;
+  const int64_t dblocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  (void)V;
+  hipLaunchKernelGGL(fn.gather, dim3((unsigned)blocks, (unsigned)splits), dim3(64 * wg_waves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn.direct, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, splits);
+  hipLaunchKernelGGL(fn.direct, dim3((unsigned)dblocks), dim3(kWorkgroup), 0, s, a, splits);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 namespace ncmri {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Keeps the compiler's scheduler from moving instructions across this point.

@@ -40,8 +40,9 @@ HBM_BYTES_PER_S = 5.0e12          # sustained streaming rate used for the reduct
 
 # Issue model (cycles on one SIMD), from the gfx950 issue-rate measurements:
 # a wave64 VALU op occupies its SIMD for 4 cycles; on the matrix-core engine a
-# 32x32x2 f32 MFMA keeps the matrix pipe busy 64 cycles, and VALU work that
-# does not overlap it adds ~2.7 cycles per FMA and ~8.8 per v_sin.
+# 32x32x2 f32 MFMA keeps the matrix pipe busy 64 cycles (a 16x16x4 one 32),
+# and VALU work that does not overlap it adds ~2.7 cycles per FMA and ~8.8
+# per v_sin.
 MFMA_CYCLES = 64.0
 MFMA_FMA_EXTRA = 2.7
 MFMA_SIN_EXTRA = 8.8
@@ -94,12 +95,18 @@ def static_metrics(c: Candidate, M: int, N: int, batch: int, is_q: bool, trig: s
     mpad = p["padded_samples"]
     tile = max(1, p["tile"])
     V = max(1, p["voxels_per_lane"])
-    if p["engine"] == 2:   # matrix-core engine: a wave owns 32 groups of V voxels
+    if p["engine"] == 2:   # matrix-core engine, three real products per complex product
         T = max(1, (V * min(batch, 16)) // 16) if not is_q else max(1, V // 16)
-        waves_row = math.ceil(N / (32 * V))
+        four = T >= 8      # four-sample engine: 16 groups per wave, 4 samples per 16x16x4 MFMA
+        ks = 4 if four else 2
+        waves_row = math.ceil(N / ((16 if four else 32) * V))
         capacity = SIMDS * (2 if T >= 4 else 4)
-        trig_extra = MFMA_SIN_EXTRA + 3 * MFMA_FMA_EXTRA if trig == "hw" else 28 * MFMA_FMA_EXTRA
-        per_sample = T * MFMA_CYCLES + trig_extra + (64 * T / tile) * MFMA_FMA_EXTRA
+        # per sample and wave: 3 T / ks MFMAs of 64 cycles (32x32x2, 32 groups x
+        # 32 columns) or 3 T / 4 of 32 cycles (16x16x4); one phase with its sine
+        # and cosine per lane and ks samples; tile folds of the accumulators
+        mfma = 3 * (T / 2) * MFMA_CYCLES / 2 if not four else 3 * T * (MFMA_CYCLES / 2) / 4
+        trig_extra = (2 * MFMA_SIN_EXTRA + 6 * MFMA_FMA_EXTRA) if trig == "hw" else 33 * MFMA_FMA_EXTRA
+        per_sample = mfma + trig_extra / ks + ((28 if four else 56) * T / tile) * MFMA_FMA_EXTRA
     else:                  # VALU engine: a lane owns V voxels, 64 lanes per wave
         waves_row = math.ceil(N / (64 * V))
         capacity = SIMDS * 4
@@ -126,7 +133,7 @@ def candidates(M: int, N: int, batch: int = 1, is_q: bool = False, *, engines=("
     rows_set = [1, 2, 4, 8, 16, 32, 64]
     tiles = [128, 256, 512, 1024, 2048, 4096]
     for engine in engines:
-        groups = [32, 64] if engine == "mfma" else [1, 2, 4, 8, 16]
+        groups = [32, 64, 128] if engine == "mfma" else [1, 2, 4, 8, 16]
         for V in groups:
             if engine == "mfma" and not _regular(V, grid_edge):
                 continue

@@ -111,7 +111,7 @@ def test_stage_combinations(lib):
 
 @pytest.mark.parametrize("field,value", [
     ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 48),
-    ("voxels_per_lane", 128),
+    ("voxels_per_lane", 256),
     ("tile", -4), ("stages", 8), ("sample_splits", -1), ("sample_splits", 1025),
     ("engine", 3), ("engine", -1), ("reserved", 1),
 ])
@@ -249,24 +249,28 @@ def test_describe_plan_valu(lib):
 
 def test_describe_plan_mfma(lib):
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
-    # the 128^3 benchmark shape: a cube whose edge is a multiple of 64 -> four
-    # factor tiles per group phase, groups of 64 voxels (half a row)
+    # the 128^3 benchmark shape: a cube whose edge is a multiple of 128 -> T = 8
+    # units of 16 complex columns per group phase, groups of 128 voxels (one
+    # row), the four-sample engine
     hw = fhd_describe_plan(262144, 128 ** 3, trig="hw")
     acc = fhd_describe_plan(262144, 128 ** 3, trig="accurate")
     assert hw["engine"] == acc["engine"] == _lib.FHD_ENGINE_MFMA
-    assert hw["voxels_per_lane"] == 64 and acc["voxels_per_lane"] == 64
-    assert hw["record_dwords"] == 4 + 192 and acc["record_dwords"] == 8 + 192
+    assert hw["voxels_per_lane"] == 128 and acc["voxels_per_lane"] == 128
+    assert hw["record_dwords"] == 4 + 384 and acc["record_dwords"] == 8 + 384
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 512
-    # 1024 waves of 32 groups; 16 rows of 16384 samples
+    # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
-    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 768 + 16 * 128 ** 3 * 8
-    # two tiles (groups of 32) on request, or when the edge is not a multiple of 64
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8
+    # groups of 64 (T = 4) or 32 (T = 2) on request, two-sample engine
+    four = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=64)
+    assert four["voxels_per_lane"] == 64 and four["record_dwords"] == 4 + 192
+    assert four["workspace_bytes"] == 262144 * 16 + 262144 * 768 + 16 * 128 ** 3 * 8
     two = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=32)
     assert two["voxels_per_lane"] == 32 and two["record_dwords"] == 4 + 96 and two["engine"] == _lib.FHD_ENGINE_MFMA
     assert two["workspace_bytes"] == 262144 * 16 + 262144 * 384 + 16 * 128 ** 3 * 8
     assert fhd_describe_plan(1000, 96 ** 3, trig="hw")["voxels_per_lane"] == 32
     assert fhd_describe_plan(1000, 100, trig="hw")["voxels_per_lane"] == 32     # not a cube
-    # 64^3: 128 waves x 16 rows fill 2 waves per SIMD; 32^3 x 2048: at most 8 rows of 256
+    # 64^3: groups of 64 (128 does not divide the edge); 128 waves x 16 rows fill 2 waves per SIMD
     m64 = fhd_describe_plan(65536, 64 ** 3, trig="hw")
     assert m64["voxels_per_lane"] == 64 and m64["sample_splits"] == 16
     tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
@@ -274,22 +278,17 @@ def test_describe_plan_mfma(lib):
     # fewer voxels than one group: still one wave; samples padded to the 32-sample chunk
     small = fhd_describe_plan(1000, 5, trig="hw")
     assert small["padded_samples"] == 1024 and small["sample_splits"] == 4
-    # batched, 16 vectors on 96^3: four tiles, groups of 4 voxels; the partial buffer cap gives 18 rows
+    # batched, 16 vectors on 96^3: T = 8, groups of 8 voxels; the partial buffer cap gives 18 rows
     b16 = fhd_describe_plan(500001, 96 ** 3, batch=16)
-    assert b16["voxels_per_lane"] == 4 and b16["sample_splits"] == 18 and b16["padded_samples"] == 500032
-    assert b16["record_dwords"] == 8 + 192
-    # 19 = 16 + 2 + 1 vectors: the single-vector pass needs 64 | 96, so two tiles for all passes
+    assert b16["voxels_per_lane"] == 8 and b16["sample_splits"] == 18 and b16["padded_samples"] == 500032
+    assert b16["record_dwords"] == 8 + 384
+    # 19 = 16 + 2 + 1 vectors: the single-vector pass needs 32 | 96, so T = 2 for all passes
     b19 = fhd_describe_plan(500001, 96 ** 3, batch=19)
     assert b19["passes"] == 3 and b19["voxels_per_lane"] == 2
     q = fhd_describe_plan(1048576, 128 ** 3, is_q=True, trig="hw")
-    assert q["voxels_per_lane"] == 64 and q["sample_splits"] == 64
-    assert fhd_describe_plan(4096, 256 ** 3)["sample_splits"] == 1
-    assert fhd_describe_plan(10, 4096, sample_splits=7)["sample_splits"] == 1  # 32 padded samples
-    assert fhd_describe_plan(1000, 100, sum="plain")["tile"] == 1024
-    assert fhd_describe_plan(262144, 128 ** 3, tile=100)["tile"] == 128      # multiple of 32
-    # Kahan or a VALU group size select the VALU engine
-    assert fhd_describe_plan(262144, 128 ** 3, sum="kahan")["engine"] == _lib.FHD_ENGINE_VALU
-    assert fhd_describe_plan(262144, 128 ** 3, voxels_per_lane=8)["engine"] == _lib.FHD_ENGINE_VALU
+    assert q["voxels_per_lane"] == 128 and q["sample_splits"] == 64
+    # the forward operator keeps groups of at most 64 (two-sample engine)
+    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")["voxels_per_lane"] == 64
 
 
 def test_describe_plan_zero_sizes(lib):

@@ -266,8 +266,9 @@ def mfma_grid(oracle_mod):
     return p, dev_problem(p), ref, qref
 
 
-# MFMA group sizes of single-vector passes: 2 and 4 factor tiles
-GROUPS = [32, 64]
+# MFMA group sizes of single-vector passes: T = 2, 4 (two samples per
+# 32x32x2 MFMA) and 8 (four samples per 16x16x4 MFMA)
+GROUPS = [32, 64, 128]
 
 
 @pytest.mark.parametrize("trig", TRIGS)

@@ -29,7 +29,7 @@ def lib():
 
 def test_candidates_have_valid_plans_and_metrics(lib):
     cs = tune.candidates(262144, 128 ** 3, grid_edge=128)
-    assert len(cs) == 2 * 7 * 6
+    assert len(cs) == 3 * 7 * 6      # groups of 32, 64, 128 x rows x tiles
     for c in cs:
         assert c.plan["sample_splits"] == c.sample_splits
         assert c.plan["voxels_per_lane"] == c.voxels_per_lane
@@ -37,7 +37,7 @@ def test_candidates_have_valid_plans_and_metrics(lib):
     front = tune.pareto_front([(c.efficiency, c.utilization) for c in cs])
     assert 1 <= len(front) < len(cs)
     # groups that do not tile the rows of a 48^3 grid are left out of the matrix-core sweep
-    assert all(c.voxels_per_lane != 64 for c in tune.candidates(4096, 48 ** 3, grid_edge=48))
+    assert all(c.voxels_per_lane not in (64, 128) for c in tune.candidates(4096, 48 ** 3, grid_edge=48))
 
 
 def test_more_rows_trade_efficiency_for_utilization(lib):
