@@ -38,21 +38,21 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # taken on (sha256 prefix) and the
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
-    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b891735ac77011cd",
-        "fetch_bytes": 987410.7 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "32afb3d539dc5fc9",
+        "fetch_bytes": 1821390.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b891735ac77011cd",
-        "fetch_bytes": 1003828.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "32afb3d539dc5fc9",
+        "fetch_bytes": 1800589.8 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "9f0c83307b628d98",
-        "fetch_bytes": 1005913.5 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "fa5c033b08d02219",
+        "fetch_bytes": 785441.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "9f0c83307b628d98",
-        "fetch_bytes": 977914.5 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "fa5c033b08d02219",
+        "fetch_bytes": 782319.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",

@@ -1,7 +1,9 @@
 // Issue-rate microbenchmarks for gfx950 that back the gather kernel's cost
 // model: FP32 FMA throughput, v_sin_f32 throughput, whether transcendentals
-// share the VALU issue port with FMAs (mixed loops), the shader clock, and
-// the absolute error of v_sin_f32/v_cos_f32 and of sincospif over one turn.
+// share the VALU issue port with FMAs (mixed loops), whether the group-phase
+// VALU work overlaps FP32 MFMAs (the matrix-core gather's inner loop with and
+// without it, for both MFMA shapes), the shader clock, and the absolute error
+// of v_sin_f32/v_cos_f32 and of sincospif over one turn.
 // Standalone program: built by non_cartesian_mri_amd/build.py
 // (build_issue_rates) and run by `python bench.py --issue-rates`.
 #include <hip/hip_runtime.h>
@@ -9,6 +11,7 @@
 #include <cmath>
 #include <vector>
 #include <cstdlib>
+#include <type_traits>
 
 #define CK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e), __LINE__); exit(1);} } while(0)
 
@@ -48,6 +51,61 @@ __global__ void __launch_bounds__(256) k_mix(float* out, int iters, float a, flo
 #pragma unroll
   for (int j = 0; j < K; ++j) s += acc[j];
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The matrix-core gather's inner loop without its memory traffic: per block
+// of KS samples, 3 NT MFMAs (the three-product form; NT tiles) and, with
+// PHASE, the group phase (3 FMAs), fract, v_sin, v_cos, c + s and c - s of
+// one lane.  KS = 2: v_mfma_f32_32x32x2_f32 (64 cycles); KS = 4:
+// v_mfma_f32_16x16x4_f32 (32 cycles).  The phase inputs are made opaque each
+// block so that the VALU work is not hoisted.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <int KS, int NT, bool PHASE>
+__global__ void __launch_bounds__(512) k_mfma_mix(float* out, int blocks_per_wave, float k0, float k1,
+                                                  float k2) {
+  extern __shared__ float occupancy_pad[];  // sized by the launch to fix waves per SIMD
+  const int lane = threadIdx.x & 63;
+  const float gx = (float)(lane & 15) - 8.0f, gy = 3.0f, gz = -5.0f;
+  float hk[3] = {k0, k1, k2};
+  float bv[3 * NT];
+#pragma unroll
+  for (int i = 0; i < 3 * NT; ++i) bv[i] = 0.01f * (i + 1) + 1e-4f * lane;
+  using Acc = typename std::conditional<KS == 2, f32x16_t, f32x4_t>::type;
+  Acc acc[3][NT];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[u][t] = Acc{};
+  for (int q = 0; q < blocks_per_wave; ++q) {
+    float av[3];
+    if constexpr (PHASE) {
+      const float ph = __builtin_fmaf(hk[2], gz, __builtin_fmaf(hk[1], gy, hk[0] * gx));
+      const float f = __builtin_amdgcn_fractf(ph);
+      const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+      av[0] = cs + sn; av[1] = cs - sn; av[2] = sn;
+      asm volatile("" : "+v"(hk[0]), "+v"(hk[1]), "+v"(hk[2]));
+    } else {
+      av[0] = hk[0]; av[1] = hk[1]; av[2] = hk[2];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        if constexpr (KS == 2)
+          acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u * NT + t], acc[u][t], 0, 0, 0);
+        else
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u * NT + t], acc[u][t], 0, 0, 0);
+      }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      for (int v = 0; v < (KS == 2 ? 16 : 4); ++v) sum += acc[u][t][v];
+  if (blocks_per_wave < 0) { occupancy_pad[threadIdx.x] = sum; __syncthreads(); sum += occupancy_pad[lane]; }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
 __global__ void k_clock(long long* out, int iters, float a, float b, float* sink) {
@@ -117,6 +175,28 @@ int main() {
     printf("MB-MIX T=%d K=%2d: %.3f ms, CU-cycles per wave-iter %.2f (x4 SIMD = %.2f SIMD-cycles)\n", T, K, t * 1e3, slots, slots * 4); }
   MIX(2, 0) MIX(2, 2) MIX(2, 4) MIX(2, 6) MIX(2, 8) MIX(2, 12) MIX(2, 16) MIX(2, 24)
   MIX(4, 0) MIX(4, 8) MIX(4, 16)
+  // FP32 MFMA with and without the per-block phase work, 2 waves per SIMD
+  // (LDS padding: two 4-wave workgroups or one 8-wave workgroup per CU)
+  {
+    const int bpw = 16384;
+#define MFMA_MIX(KS, NT, WG, LDSB, NAME, CYC)                                                        \
+    {                                                                                               \
+      const int wgs = CU * 8 / (WG / 64);                                                           \
+      CK(hipFuncSetAttribute((const void*)k_mfma_mix<KS, NT, false>,                                \
+                             hipFuncAttributeMaxDynamicSharedMemorySize, LDSB));                     \
+      CK(hipFuncSetAttribute((const void*)k_mfma_mix<KS, NT, true>,                                 \
+                             hipFuncAttributeMaxDynamicSharedMemorySize, LDSB));                     \
+      double t0 = time_it([&] { hipLaunchKernelGGL((k_mfma_mix<KS, NT, false>), dim3(wgs), dim3(WG), LDSB, 0, out, bpw, 0.013f, 0.027f, -0.031f); }, 5); \
+      double t1 = time_it([&] { hipLaunchKernelGGL((k_mfma_mix<KS, NT, true>), dim3(wgs), dim3(WG), LDSB, 0, out, bpw, 0.013f, 0.027f, -0.031f); }, 5); \
+      CK(hipGetLastError());                                                                        \
+      const double mfma_cycles = (double)wgs * (WG / 64) * bpw * 3 * NT * CYC;                     \
+      const double ideal = mfma_cycles / (CU * 4 * 2.4e9);                                          \
+      printf("MB-MFMA %s: MFMA only %.3f ms (matrix busy %.3f at 2.4 GHz); + phase/fract/sin/cos/c+s/c-s %.3f ms (%.3f): +%.1f SIMD-cycles per phase over %d MFMA-cycles\n", \
+             NAME, t0 * 1e3, ideal / t0, t1 * 1e3, ideal / t1, (t1 - t0) * CU * 4 * 2.4e9 / ((double)wgs * (WG / 64) * bpw), 3 * NT * CYC); \
+    }
+    MFMA_MIX(2, 2, 256, 70 * 1024, "32x32x2 (2 samples, 6 MFMAs per phase)", 64)
+    MFMA_MIX(4, 8, 512, 100 * 1024, "16x16x4 (4 samples, 24 MFMAs per phase)", 32)
+  }
   // accuracy of builtins on r in [0,1)
   {
     const int n = 1 << 24;
