@@ -122,19 +122,31 @@ int64_t cube_edge(int64_t N) {
   return 0;
 }
 
+// Whether groups of V consecutive voxels (x fastest) of an L^3 grid all sit
+// at the first group's offsets: V divides a row, or V is whole rows of a plane.
+bool groups_regular(int64_t L, int64_t V) { return L % V == 0 || (V % L == 0 && (L * L) % V == 0); }
+
 // Units of 16 complex columns per group phase (T).  Groups of 16 T / BC
-// consecutive voxels only take the factored path when they tile the grid
-// rows (x fastest); more columns per phase cut the phase and sine work per
-// MFMA but lengthen the group, so the largest T <= tmax is chosen whose group
-// every pass's divides the edge when N is a cube (else 2).  T = 8 (groups of
-// 128 voxels for one vector) runs the four-sample engine.
-int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax) {
+// consecutive voxels only take the factored path when they are regular on
+// the grid; more columns per phase cut the phase and sine work per MFMA but
+// give fewer, longer waves, so the largest T <= tmax is chosen whose groups
+// every pass keeps regular when N is a cube and, given mpad > 0, whose waves
+// times the most sample rows still fill the GPU's resident-wave slots (else
+// 2).  T = 8 (groups of 128 voxels for one vector) runs the four-sample
+// engine.  The forward operator (mpad = 0) takes only groups that divide a
+// row.
+int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax, int64_t mpad) {
   const int64_t L = cube_edge(N);
   if (L == 0) return 2;
   for (int T = tmax; T > 2; T /= 2) {
     bool ok = true;
-    for (int i = 0; i < npass; ++i)
-      if (L % (16 * T / bc[i]) != 0) ok = false;
+    for (int i = 0; i < npass; ++i) {
+      const int64_t V = 16 * T / bc[i];
+      if (mpad > 0 ? !groups_regular(L, V) : L % V != 0) ok = false;
+    }
+    if (ok && mpad > 0 &&
+        ncmri::mfma_gather_waves(N, T, bc[0]) * max_splits(mpad) < mfma_wave_quantum(T))
+      ok = false;
     if (ok) return T;
   }
   return 2;
@@ -227,7 +239,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
   p.tiles = 0;
   if (mfma) {
-    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8);
+    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, p.mpad);
     V = 16 * p.tiles / p.bc[0];  // columns of a group: voxels x vectors
   } else if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
@@ -316,7 +328,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   int left = batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 4);
+  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 4, 0);
   p.V = 16 * p.tiles / p.bc[0];
   int64_t gmax = 0, gmin = -1;
   for (int i = 0; i < p.npass; ++i) {

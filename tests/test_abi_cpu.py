@@ -270,11 +270,16 @@ def test_describe_plan_mfma(lib):
     assert two["workspace_bytes"] == 262144 * 16 + 262144 * 384 + 16 * 128 ** 3 * 8
     assert fhd_describe_plan(1000, 96 ** 3, trig="hw")["voxels_per_lane"] == 32
     assert fhd_describe_plan(1000, 100, trig="hw")["voxels_per_lane"] == 32     # not a cube
-    # 64^3: groups of 64 (128 does not divide the edge); 128 waves x 16 rows fill 2 waves per SIMD
+    # 64^3: groups of 128 = two whole rows of a plane (regular); 128 waves x 16 rows
+    # fill 2 waves per SIMD
     m64 = fhd_describe_plan(65536, 64 ** 3, trig="hw")
-    assert m64["voxels_per_lane"] == 64 and m64["sample_splits"] == 16
+    assert m64["voxels_per_lane"] == 128 and m64["sample_splits"] == 16
+    # 32^3 x 2048: regular for every group size, but even 8 rows of the fewest,
+    # longest waves cannot fill the GPU -> the smallest groups
     tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
     assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 8 and tiny["tile"] == 64
+    # 48^3: 128 and 64 are neither divisors of a row nor whole rows of a plane
+    assert fhd_describe_plan(65536, 48 ** 3, trig="hw")["voxels_per_lane"] == 32
     # fewer voxels than one group: still one wave; samples padded to the 32-sample chunk
     small = fhd_describe_plan(1000, 5, trig="hw")
     assert small["padded_samples"] == 1024 and small["sample_splits"] == 4
