@@ -78,7 +78,8 @@ bool gather_supported(int is_q, int V, int BC);
 // real products per tile (the three-multiplication complex product) with
 // v_mfma_f32_32x32x2_f32, the K dimension running over the two samples.
 constexpr int kMfmaChunk = 32;   // samples per LDS chunk; records are padded to it
-constexpr int kMfma4Waves = 8;   // waves per workgroup of the four-sample engine (T = 8)
+constexpr int kMfma4Waves = 4;   // waves per workgroup of the four-sample engine (T = 8)
+constexpr int kMfma4Chunk = 16;  // samples per LDS chunk of the four-sample engine (divides kMfmaChunk)
 
 // Waves of a gather launch row: 32 groups per wave (T = 2, 4: two samples
 // per v_mfma_f32_32x32x2_f32) or 16 (T = 8: four samples per

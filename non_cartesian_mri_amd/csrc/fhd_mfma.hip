@@ -502,13 +502,16 @@ struct MfmaDirect {
 // the 16 x 16 products take 3 T MFMAs per block: with T = 8 tiles of 16
 // complex columns that is 24 MFMAs (768 matrix cycles) per phase, twice the
 // two-sample engine's 6 per pair at the same register count.  Records stream
-// through LDS in 32-sample chunks (8 blocks, 48 KB with T = 8), so one
-// workgroup of 8 waves (2 per SIMD) per CU shares them.
+// through LDS in 16-sample chunks (4 blocks, 24 KB with T = 8) shared by the
+// 4 waves of a workgroup; two workgroups per CU (2 waves per SIMD, one of
+// each), so that one workgroup's barrier or copy burst is covered by the
+// other's MFMAs.  (One 8-wave workgroup per CU with 32-sample chunks was
+// 1.5 % slower at 128^3: its two waves on a SIMD wait at the same barrier.)
 template <int T, int BC, int TRIG>
 struct MfmaGather4 {
   static constexpr int V = 16 * T / BC;                // voxels per group
   static constexpr int HF = mfma_header_floats(TRIG);
-  static constexpr int C = kMfmaChunk;
+  static constexpr int C = kMfma4Chunk;
   static constexpr int NW = kMfma4Waves;               // waves per workgroup
   static constexpr int QF = 192 * T;                   // factor floats per block of 4 samples
   static constexpr int NS = 3 * T / 4;                 // float4 slices per lane and block
@@ -790,8 +793,8 @@ __global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int
   MfmaDirect<T, BC, TRIG>::run(a, splits);
 }
 
-// Four-sample engine: one 8-wave workgroup per CU (96 KB of staging), 2 waves
-// per SIMD.
+// Four-sample engine: two 4-wave workgroups per CU (2 x 49 KB of LDS), 2
+// waves per SIMD.
 template <int T, int BC, int TRIG>
 __global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
 mfma4_gather_kernel(MfmaArgs a) {
