@@ -39,12 +39,12 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "32afb3d539dc5fc9",
-        "fetch_bytes": 1821390.6 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "78956be5223d1d18",
+        "fetch_bytes": 1774067.0 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "32afb3d539dc5fc9",
-        "fetch_bytes": 1800589.8 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "78956be5223d1d18",
+        "fetch_bytes": 1790519.7 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
         "source": "fhd_forward.hip", "kernel_sha256": "fa5c033b08d02219",
