@@ -194,7 +194,7 @@ fhd_status q_compute(const float* kx, const float* ky, const float* kz,
  * D[b][m] = phi[m] sum_n rho[b][n] exp(-i 2 pi k_m . x_n), so that
  * <F rho, d> = <rho, F^H d> with fhd_compute.  Runs on the matrix-core engine
  * only (FHD_ENGINE_VALU and FHD_SUM_KAHAN are rejected); voxels_per_lane may
- * be 0, 32 or 64; sample_splits here splits the voxel groups across launch
+ * be 0, 32, 64 or 128; sample_splits here splits the voxel groups across launch
  * rows.  N == 0 writes zeros; M == 0 does nothing.  Returns FHD_OK or an error
  * code as fhd_compute does.
  */

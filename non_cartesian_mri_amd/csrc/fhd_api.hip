@@ -311,8 +311,8 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only");
   if (o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator sums blocked or plain, not Kahan");
-  if (V != 0 && (V < 32 || V > 64))
-    return fail(FHD_ERR_INVALID_ARGUMENT, "forward-operator group sizes are 32 or 64 voxels (got %d)", V);
+  if (V != 0 && V < 32)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32, 64 or 128 voxels (got %d)", V);
   const int64_t C = ncmri::kMfmaChunk;
   p.op = FHD_OP_FORWARD;
   p.is_q = 0;
@@ -328,7 +328,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   int left = batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 4, 0);
+  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, 0);
   p.V = 16 * p.tiles / p.bc[0];
   int64_t gmax = 0, gmin = -1;
   for (int i = 0; i < p.npass; ++i) {
@@ -350,7 +350,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   // launch rows over the groups: enough for whole rounds of resident waves
   // when the samples alone give fewer; at least 256 groups per row
   int32_t splits = o->sample_splits;
-  const int64_t waves = (M + 31) / 32;
+  const int64_t waves = p.tiles == 8 ? (M + 15) / 16 : (M + 31) / 32;  // samples per wave
   if (o->sum == FHD_SUM_PLAIN) {
     splits = 1;
   } else if (splits == 0) {

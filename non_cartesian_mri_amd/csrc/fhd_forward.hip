@@ -80,6 +80,17 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_pack_kernel(FwdArgs a, int T, 
   const int b = cc / V, j = cc % V;
   const int64_t n = n0 + j;
   const float2 r = (inside && reg && n < a.N) ? a.rho[(int64_t)b * a.N + n] : make_float2(0.0f, 0.0f);
+  if (T == 8) {
+    // four-group engine: entry e = u T + t (u = re, im, re + im; tile t =
+    // cc / 16) of lane p = 16 (g % 4) + cc % 16 in float4 slices of a block of
+    // four groups: [g / 4][e / 4][p][e % 4]
+    const int t = cc / 16, lp = 16 * (int)(g & 3) + cc % 16;
+    float* blk = a.gwb + (g >> 2) * (192 * T);
+    blk[((t >> 2) * 64 + lp) * 4 + (t & 3)] = r.x;
+    blk[(((T + t) >> 2) * 64 + lp) * 4 + ((T + t) & 3)] = r.y;
+    blk[(((2 * T + t) >> 2) * 64 + lp) * 4 + ((2 * T + t) & 3)] = r.x + r.y;
+    return;
+  }
   // entry of column c = cc % 32 of tile t = cc / 32 at row g % 2 of the pair
   const int P = T / 2;
   const int t = cc / 32, lp = 32 * (int)(g & 1) + cc % 32;
@@ -356,6 +367,210 @@ struct FwdGather {
 };
 
 // ---------------------------------------------------------------------------
+// Four-group matrix-core gather (T = 8, groups of 128 voxels for one image):
+// v_mfma_f32_16x16x4_f32 with K = a block of four groups.  A wave owns 16
+// samples; lane l supplies sample l % 16 at group 4 q + l / 16, so each lane
+// evaluates one phase with its sine and cosine per block and it serves
+// 3 T = 24 MFMAs (768 matrix cycles), twice the pair engine's.  The packed
+// groups stream through LDS in 16-group chunks (24 KB) shared by the 4 waves
+// of a workgroup, two workgroups per CU.  After the last group each wave
+// writes its 16 x 128 complex block of G to LDS and all 64 lanes contract it:
+// four lanes per sample take every fourth offset, and their sums are
+// combined in a fixed order.
+template <int T, int BC, int TRIG>
+struct FwdGather4 {
+  static constexpr int V = 16 * T / BC;
+  static constexpr int C = kMfma4Chunk;           // groups per chunk
+  static constexpr int NW = kWorkgroup / 64;
+  static constexpr int QF = 192 * T;              // image floats per block of four groups
+  static constexpr int NS = 3 * T / 4;            // float4 slices per lane and block
+  static constexpr int NB = C / 4 * QF * 4 / 1024;  // 1 KiB image blocks per chunk
+  static constexpr int NH = C;                    // header float4s per chunk (one per group)
+  static constexpr int SB = C / 4 * QF / 4;       // float4s of one staging buffer
+  static constexpr int GW = 16 * 16 * T * 2 / 4;  // float4s of one wave's G block
+  static constexpr int LDS4 = 2 * SB > NW * GW ? 2 * SB : NW * GW;
+  static_assert(T % 4 == 0 && V >= 1 && V * BC == 16 * T, "group shape");
+  static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
+
+  __device__ static __forceinline__ void stage(const FwdArgs& a, int64_t g, int wig, int lane,
+                                               float4* lb, float4* lh) {
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + (g / 4) * (QF / 4), NB * 64 * 16);
+#pragma unroll
+    for (int i = 0; i < NB / NW; ++i) {
+      const int blk = i * NW + wig;
+      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
+    }
+    if (wig == 0 && lane < NH)
+      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.ghdr) + g, NH * 16), lane * 16, lh);
+  }
+
+  __device__ static __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Header of the lane's group and its B entries of block q of the chunk.
+  __device__ static __forceinline__ void load_block(const float* __restrict__ hb,
+                                                    const float* __restrict__ wb, int q, int lane,
+                                                    float (&hs)[3], float (&bv)[3 * T]) {
+    const float* hp = hb + (4 * q + (lane >> 4)) * 4;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) hs[i] = hp[i];
+    const float* pp = wb + q * QF;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  __device__ static __forceinline__ void mfmas(const float (&av)[3], const float (&bv)[3 * T],
+                                               f32x4 (&acc)[3][T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[T + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2 * T + t], acc[2][t], 0, 0, 0);
+    }
+  }
+
+  // One chunk of 16 groups (4 blocks), pipelined by one block as in the
+  // pair engine.
+  __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb,
+                                               int lane, const SampleK<TRIG>& k, f32x4 (&acc)[3][T]) {
+    constexpr int NQ = C / 4;
+    float hc[3], bc[3 * T], av[3];
+    load_block(hb, wb, 0, lane, hc, bc);
+    if constexpr (TRIG != kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hc, av);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float hn[3], bn[3 * T];
+      if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
+      sched_fence();
+      if constexpr (TRIG == kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hc, av);
+      mfmas(av, bc, acc);
+      sched_fence();
+      if (q + 1 < NQ) {
+        if constexpr (TRIG != kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hn, av);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hc[i] = hn[i];
+#pragma unroll
+        for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
+      }
+      sched_fence();
+    }
+  }
+
+  // Tile end: Re = P1 + P3, Im = P2 - P3 into the running totals.
+  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[T], f32x4 (&tim)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      tre[t] += acc[0][t] + acc[2][t];
+      tim[t] += acc[1][t] - acc[2][t];
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
+    }
+  }
+
+  __device__ static void run(const FwdArgs& a) {
+    // two staging buffers while the groups stream, then the waves' G blocks
+    __shared__ float4 lds[LDS4];
+    __shared__ float4 sh0[NH], sh1[NH];
+    float4* sb0 = lds;
+    float4* sb1 = lds + SB;
+    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int64_t wave = (int64_t)blockIdx.x * NW + wig;
+    const int64_t m = wave * 16 + (lane & 15);   // this lane's sample
+    const bool valid = m < a.M;
+    SampleK<TRIG> k;
+    k.load(a, m, valid);
+
+    // this launch row's groups
+    const int32_t row = (int32_t)blockIdx.y;
+    const int64_t lo64 = (int64_t)row * a.g_split;
+    const int64_t lo = lo64 < a.gpad ? lo64 : a.gpad;
+    const int64_t hi = lo64 + a.g_split < a.gpad ? lo64 + a.g_split : a.gpad;
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    const int32_t cpt = (int32_t)(a.tile / C);
+    if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
+    publish();
+    f32x4 acc[3][T], tre[T], tim[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
+      tre[t] = f32x4{}; tim[t] = f32x4{};
+    }
+    int32_t left = cpt;
+    for (int32_t ch = 0; ch < nch; ch += 2) {
+      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
+      if (--left == 0) {
+        fold(acc, tre, tim);
+        left = cpt;
+      }
+      publish();
+      if (ch + 1 >= nch) break;
+      if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+      chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, acc);
+      if (--left == 0) {
+        fold(acc, tre, tim);
+        left = cpt;
+      }
+      publish();
+    }
+    fold(acc, tre, tim);
+
+    // Finish.  Every wave has passed the last barrier, so the staging buffers
+    // are free: each wave stores its 16 x 16 T complex block of G there ...
+    float2* gl = reinterpret_cast<float2*>(lds + wig * GW);
+    const int c = lane & 15;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (lane >> 4) + r;
+        gl[i * (16 * T) + 16 * t + c] = make_float2(tre[t][r], tim[t][r]);
+      }
+    __syncthreads();
+    // ... and lane l contracts the offsets j = l / 16 (mod 4) of row l % 16 (its
+    // sample) with exp(-i 2 pi k . d_j); the four lanes of a row then add
+    // their sums, (p0 + p1) + (p2 + p3), and one of them multiplies by phi_m.
+    const float2* gr = gl + (lane & 15) * (16 * T);
+    float dre[BC], dim[BC];
+#pragma unroll
+    for (int b = 0; b < BC; ++b) { dre[b] = 0.0f; dim[b] = 0.0f; }
+    const bool any_voxel = a.N > 0;
+    const float x0 = any_voxel ? a.x[0] : 0.0f, y0 = any_voxel ? a.y[0] : 0.0f, z0 = any_voxel ? a.z[0] : 0.0f;
+    if (valid) {
+      for (int j = lane >> 4; j < V && j < a.N; j += 4) {
+        float cj = 1.0f, sj = 0.0f;
+        if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+          const float2 gv = gr[b * V + j];
+          // (cj - i sj)(gre + i gim)
+          dre[b] = __builtin_fmaf(cj, gv.x, __builtin_fmaf(sj, gv.y, dre[b]));
+          dim[b] = __builtin_fmaf(cj, gv.y, __builtin_fmaf(-sj, gv.x, dim[b]));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BC; ++b) {
+      dre[b] += __shfl_xor(dre[b], 16);
+      dim[b] += __shfl_xor(dim[b], 16);
+      dre[b] += __shfl_xor(dre[b], 32);
+      dim[b] += __shfl_xor(dim[b], 32);
+    }
+    if (lane >= 16 || !valid) return;
+    const float2 ph = a.phi[m];
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.M : a.out;
+#pragma unroll
+    for (int b = 0; b < BC; ++b)
+      dst[(int64_t)b * a.M + m] = make_float2(ph.x * dre[b] - ph.y * dim[b], ph.x * dim[b] + ph.y * dre[b]);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Direct evaluation of the listed groups: one lane per sample, the groups in
 // increasing order (indices and voxels read as wave-uniform scalars); the sum
 // is blocked by `tile` listed groups and added into the (already reduced)
@@ -411,15 +626,23 @@ fwd_gather_kernel(FwdArgs a) {
   FwdGather<T, BC, TRIG>::run(a);
 }
 
+template <int T, int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(2)))
+fwd4_gather_kernel(FwdArgs a) {
+  FwdGather4<T, BC, TRIG>::run(a);
+}
+
 using FwdFn = void (*)(FwdArgs);
 
 template <int T, int BC>
 void pick(int trig, FwdFn& gather, FwdFn& direct) {
   if (trig == kTrigHw) {
-    gather = fwd_gather_kernel<T, BC, kTrigHw>;
+    if constexpr (T == 8) gather = fwd4_gather_kernel<T, BC, kTrigHw>;
+    else gather = fwd_gather_kernel<T, BC, kTrigHw>;
     direct = fwd_direct_kernel<T, BC, kTrigHw>;
   } else {
-    gather = fwd_gather_kernel<T, BC, kTrigAccurate>;
+    if constexpr (T == 8) gather = fwd4_gather_kernel<T, BC, kTrigAccurate>;
+    else gather = fwd_gather_kernel<T, BC, kTrigAccurate>;
     direct = fwd_direct_kernel<T, BC, kTrigAccurate>;
   }
 }
@@ -439,6 +662,7 @@ bool select_bc(int trig, int BC, FwdFn& gather, FwdFn& direct) {
 bool select_fwd(int trig, int T, int BC, FwdFn& gather, FwdFn& direct) {
   if (T == 2) return select_bc<2>(trig, BC, gather, direct);
   if (T == 4) return select_bc<4>(trig, BC, gather, direct);
+  if (T == 8) return select_bc<8>(trig, BC, gather, direct);
   return false;
 }
 
@@ -467,7 +691,9 @@ hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdA
       a.tile <= 0)
     return hipErrorInvalidValue;
   if (a.M <= 0) return hipSuccess;
-  const int64_t waves = (a.M + 31) / 32;
+  // a wave owns 32 samples (pair engine) or 16 (four-group engine, T = 8)
+  const int64_t per_wave = T == 8 ? 16 : 32;
+  const int64_t waves = (a.M + per_wave - 1) / per_wave;
   const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
   hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
   return hipGetLastError();

@@ -292,8 +292,8 @@ def test_describe_plan_mfma(lib):
     assert b19["passes"] == 3 and b19["voxels_per_lane"] == 2
     q = fhd_describe_plan(1048576, 128 ** 3, is_q=True, trig="hw")
     assert q["voxels_per_lane"] == 128 and q["sample_splits"] == 64
-    # the forward operator keeps groups of at most 64 (two-sample engine)
-    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")["voxels_per_lane"] == 64
+    # the forward operator at 128^3: groups of 128 (the four-group engine)
+    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")["voxels_per_lane"] == 128
 
 
 def test_describe_plan_zero_sizes(lib):
@@ -343,13 +343,16 @@ def test_forward_empty_sample_set_is_a_noop(lib):
 def test_forward_plan(lib):
     from non_cartesian_mri_amd.fhd import fhd_describe_plan, fhd_workspace_bytes
     a256 = lambda b: (b + 255) // 256 * 256
-    # 128^3: four tiles, groups of 64 voxels -> 32,768 groups; 8192 waves of 32 samples fill the GPU
+    # 128^3: T = 8, groups of 128 voxels -> 16,384 groups; 16,384 waves of 16 samples fill the GPU
     p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
-    assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 64
-    assert p["record_dwords"] == 4 + 192 and p["padded_samples"] == 262144
-    assert p["sample_splits"] == 1 and p["tile"] == 256
+    assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 128
+    assert p["record_dwords"] == 4 + 384 and p["padded_samples"] == 262144
+    assert p["sample_splits"] == 1 and p["tile"] == 128
     pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
-    assert p["workspace_bytes"] == pas(32768, 4)
+    assert p["workspace_bytes"] == pas(16384, 8)
+    # groups of 64 on request: the pair engine, 32,768 groups
+    p64 = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw", voxels_per_lane=64)
+    assert p64["record_dwords"] == 4 + 192 and p64["tile"] == 256 and p64["workspace_bytes"] == pas(32768, 4)
     assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw") == p["workspace_bytes"]
     # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 256 groups each)
     s = fhd_describe_plan(2048, 32 ** 3, op="forward", trig="hw")

@@ -16,7 +16,7 @@ from tests.gpu_util import TOL, assert_close, dev_problem, require_gpu
 pytestmark = pytest.mark.gpu
 
 TRIGS = ["accurate", "hw"]
-GROUPS = [32, 64]
+GROUPS = [32, 64, 128]   # 128: the four-group engine (16x16x4, K = four groups)
 
 
 @pytest.fixture(scope="module", autouse=True)
