@@ -133,20 +133,28 @@ bool groups_regular(int64_t L, int64_t V) { return L % V == 0 || (V % L == 0 && 
 // every pass keeps regular when N is a cube and, given mpad > 0, whose waves
 // times the most sample rows still fill the GPU's resident-wave slots (else
 // 2).  T = 8 (groups of 128 voxels for one vector) runs the four-sample
-// engine.  The forward operator (mpad = 0) takes only groups that divide a
-// row.
-int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax, int64_t mpad) {
+// engine.  For the forward operator (fwd_M > 0 samples; mpad unused) the
+// waves own 16 or 32 samples and the launch rows split the groups, at least
+// 256 groups each.
+int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax, int64_t mpad, int64_t fwd_M = 0) {
   const int64_t L = cube_edge(N);
   if (L == 0) return 2;
   for (int T = tmax; T > 2; T /= 2) {
     bool ok = true;
     for (int i = 0; i < npass; ++i) {
       const int64_t V = 16 * T / bc[i];
-      if (mpad > 0 ? !groups_regular(L, V) : L % V != 0) ok = false;
+      if (!groups_regular(L, V)) ok = false;
     }
-    if (ok && mpad > 0 &&
-        ncmri::mfma_gather_waves(N, T, bc[0]) * max_splits(mpad) < mfma_wave_quantum(T))
-      ok = false;
+    int64_t capacity;  // waves x the most launch rows
+    if (fwd_M > 0) {
+      const int64_t per_wave = T == 8 ? 16 : 32, V = 16 * T / bc[0];
+      int64_t rows = ((N + V - 1) / V) / 256;
+      rows = rows < 1 ? 1 : (rows > kMaxSplits ? kMaxSplits : rows);
+      capacity = (fwd_M + per_wave - 1) / per_wave * rows;
+    } else {
+      capacity = ncmri::mfma_gather_waves(N, T, bc[0]) * max_splits(mpad);
+    }
+    if (ok && capacity < mfma_wave_quantum(T)) ok = false;
     if (ok) return T;
   }
   return 2;
@@ -328,7 +336,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   int left = batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, 0);
+  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, 0, M);
   p.V = 16 * p.tiles / p.bc[0];
   int64_t gmax = 0, gmin = -1;
   for (int i = 0; i < p.npass; ++i) {

@@ -43,33 +43,37 @@ namespace {
 
 // Group g of V voxels (first voxel n0 = g V) is on the common offsets when
 // every voxel n0 + j < N satisfies x[n0 + j] - x[n0] == x[j] - x[0] (exact,
-// in double; likewise y, z).
-__device__ bool group_regular(const float* __restrict__ x, const float* __restrict__ y,
-                              const float* __restrict__ z, int64_t N, int64_t n0, int V) {
-  const double bx = x[0], by = y[0], bz = z[0];
-  const double gx = x[n0], gy = y[n0], gz = z[n0];
-  for (int j = 1; j < V; ++j) {
-    const int64_t n = n0 + j;
-    if (n >= N) break;
-    if (!((double)x[n] - gx == (double)x[j] - bx && (double)y[n] - gy == (double)y[j] - by &&
-          (double)z[n] - gz == (double)z[j] - bz))
-      return false;
-  }
-  return true;
+// in double; likewise y, z).  This checks one offset j.
+__device__ bool voxel_on_offsets(const float* __restrict__ x, const float* __restrict__ y,
+                                 const float* __restrict__ z, int64_t N, int64_t n0, int j) {
+  const int64_t n = n0 + j;
+  if (j == 0 || n >= N) return true;
+  return (double)x[n] - (double)x[n0] == (double)x[j] - (double)x[0] &&
+         (double)y[n] - (double)y[n0] == (double)y[j] - (double)y[0] &&
+         (double)z[n] - (double)z[n0] == (double)z[j] - (double)z[0];
 }
 
 // ---------------------------------------------------------------------------
-// Packing: one lane per (padded group, complex column).
+// Packing: one lane per (padded group, complex column); the 16 T lanes of a
+// group (a divisor of the workgroup) check one offset each and combine the
+// result in LDS.
 __global__ void __launch_bounds__(kWorkgroup) fwd_pack_kernel(FwdArgs a, int T, int BC) {
+  __shared__ int regular_s[kWorkgroup / 32];
   const int cols = 16 * T;
   const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
   const int64_t g = idx / cols;
   const int cc = (int)(idx - g * cols);
-  if (g >= a.gpad) return;
+  const int lg = threadIdx.x / cols;  // the group's slot in this workgroup
+  const bool live = g < a.gpad;
   const int V = cols / BC;
   const int64_t n0 = g * V;
-  const bool inside = n0 < a.N;
-  const bool reg = inside ? group_regular(a.x, a.y, a.z, a.N, n0, V) : true;
+  const bool inside = live && n0 < a.N;
+  if (threadIdx.x < kWorkgroup / cols) regular_s[threadIdx.x] = 1;
+  __syncthreads();
+  if (inside && cc < V && !voxel_on_offsets(a.x, a.y, a.z, a.N, n0, cc)) regular_s[lg] = 0;
+  __syncthreads();
+  const bool reg = regular_s[lg] != 0;
+  if (!live) return;
   if (cc == 0) {
     float* h = a.ghdr + g * 4;
     h[0] = inside ? a.x[n0] : 0.0f;

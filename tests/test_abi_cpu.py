@@ -358,10 +358,14 @@ def test_forward_plan(lib):
     s = fhd_describe_plan(2048, 32 ** 3, op="forward", trig="hw")
     assert s["voxels_per_lane"] == 32 and s["sample_splits"] == 4 and s["tile"] == 64
     assert s["workspace_bytes"] == pas(1024, 2) + a256(4 * 2048 * 8)
-    # batch 3 on 64^3: passes of 2 and 1 images, groups of 32 and 64 voxels
+    # batch 3 on 64^3: passes of 2 and 1 images, T = 8: groups of 64 and 128 voxels
+    # (128 = two rows of a plane)
     b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1)
-    assert b["passes"] == 2 and b["voxels_per_lane"] == 32
-    assert b["workspace_bytes"] == pas(8192, 4) + pas(4096, 4)
+    assert b["passes"] == 2 and b["voxels_per_lane"] == 64
+    assert b["workspace_bytes"] == pas(4096, 8) + pas(2048, 8)
+    # with groups of 32 per image on request (T = 2): groups of 16 and 32
+    b2 = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1, voxels_per_lane=32)
+    assert b2["voxels_per_lane"] == 16 and b2["workspace_bytes"] == pas(16384, 2) + pas(8192, 2)
     # explicit group size, plain sum (one row, one tile)
     g = fhd_describe_plan(1000, 128 ** 3, op="forward", voxels_per_lane=32, sum="plain")
     assert g["voxels_per_lane"] == 32 and g["sample_splits"] == 1 and g["tile"] == 65536
