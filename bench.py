@@ -46,13 +46,13 @@ TRAFFIC = {
         "source": "fhd_mfma.hip", "kernel_sha256": "78956be5223d1d18",
         "fetch_bytes": 1790519.7 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "fa5c033b08d02219",
-        "fetch_bytes": 785441.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
+        "source": "fhd_forward.hip", "kernel_sha256": "492f9b0a88e3575e",
+        "fetch_bytes": 1570992.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
-    ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 64): {
-        "source": "fhd_forward.hip", "kernel_sha256": "fa5c033b08d02219",
-        "fetch_bytes": 782319.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+    ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
+        "source": "fhd_forward.hip", "kernel_sha256": "492f9b0a88e3575e",
+        "fetch_bytes": 1566624.7 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
