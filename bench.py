@@ -47,12 +47,12 @@ TRAFFIC = {
         "fetch_bytes": 1790519.7 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "492f9b0a88e3575e",
-        "fetch_bytes": 1570992.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "09a9b92cc7ea3d23",
+        "fetch_bytes": 1571094.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "492f9b0a88e3575e",
-        "fetch_bytes": 1566624.7 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "09a9b92cc7ea3d23",
+        "fetch_bytes": 1566636.1 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",

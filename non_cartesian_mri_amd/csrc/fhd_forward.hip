@@ -165,6 +165,17 @@ struct SampleK {
   }
 };
 
+// A entries (c - s, c + s, s) of one lane's (sample, group) phase in the
+// three-product form of (c - i s)(rr + i ri).
+template <int TRIG>
+__device__ __forceinline__ void fwd_entries(const SampleK<TRIG>& k, const float (&hs)[3], float (&av)[3]) {
+  float c, s;
+  k.sincos_phase(hs[0], hs[1], hs[2], c, s);
+  av[0] = c - s;
+  av[1] = c + s;
+  av[2] = s;
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core gather over the regular groups.
 template <int T, int BC, int TRIG>
@@ -223,16 +234,6 @@ struct FwdGather {
     }
   }
 
-  // A entries (c - s, c + s, s) of the lane's (sample, group) phase.
-  __device__ static __forceinline__ void entries(const SampleK<TRIG>& k, const float (&hs)[3],
-                                                 float (&av)[3]) {
-    float c, s;
-    k.sincos_phase(hs[0], hs[1], hs[2], c, s);
-    av[0] = c - s;
-    av[1] = c + s;
-    av[2] = s;
-  }
-
   __device__ static __forceinline__ void mfmas(const float (&av)[3], const float (&bv)[3 * P],
                                                f32x16 (&acc)[3][P]) {
 #pragma unroll
@@ -251,17 +252,17 @@ struct FwdGather {
     constexpr int NP = C / 2;
     float hc[3], bc[3 * P], av[3];
     load_pair(hb, wb, 0, lane, hc, bc);
-    if constexpr (TRIG != kTrigHw) entries(k, hc, av);
+    if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hc, av);
 #pragma unroll
     for (int h = 0; h < NP; ++h) {
       float hn[3], bn[3 * P];
       if (h + 1 < NP) load_pair(hb, wb, h + 1, lane, hn, bn);
       sched_fence();
-      if constexpr (TRIG == kTrigHw) entries(k, hc, av);
+      if constexpr (TRIG == kTrigHw) fwd_entries<TRIG>(k, hc, av);
       mfmas(av, bc, acc);
       sched_fence();
       if (h + 1 < NP) {
-        if constexpr (TRIG != kTrigHw) entries(k, hn, av);
+        if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hn, av);
 #pragma unroll
         for (int i = 0; i < 3; ++i) hc[i] = hn[i];
 #pragma unroll
@@ -446,17 +447,17 @@ struct FwdGather4 {
     constexpr int NQ = C / 4;
     float hc[3], bc[3 * T], av[3];
     load_block(hb, wb, 0, lane, hc, bc);
-    if constexpr (TRIG != kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hc, av);
+    if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hc, av);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       float hn[3], bn[3 * T];
       if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
       sched_fence();
-      if constexpr (TRIG == kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hc, av);
+      if constexpr (TRIG == kTrigHw) fwd_entries<TRIG>(k, hc, av);
       mfmas(av, bc, acc);
       sched_fence();
       if (q + 1 < NQ) {
-        if constexpr (TRIG != kTrigHw) FwdGather<4, 1, TRIG>::entries(k, hn, av);
+        if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hn, av);
 #pragma unroll
         for (int i = 0; i < 3; ++i) hc[i] = hn[i];
 #pragma unroll
