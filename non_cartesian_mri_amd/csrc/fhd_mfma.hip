@@ -60,7 +60,8 @@ namespace ncmri {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Records: one lane per (padded sample, complex column).
+// Records of the two-sample engine: one lane per (padded sample, complex
+// column).
 __global__ void __launch_bounds__(kWorkgroup)
 mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   const int cols = 16 * T;
@@ -72,25 +73,13 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   const int HF = mfma_header_floats(trig);
   const int V = cols / BC;
   float* h = a.hdr + m * HF;
-  float *wr, *wi, *ws;  // destinations of fr, fi, fr + fi
-  if (T == 8) {
-    // four-sample engine: entry e = u T + t (u = fr, fi, fr + fi; tile t =
-    // cc / 16) of lane p = 16 (m % 4) + cc % 16, in float4 slices of a block
-    // of four samples: [m / 4][e / 4][p][e % 4]
-    const int t = cc / 16, lp = 16 * (int)(m & 3) + cc % 16;
-    float* blk = a.wb + (m >> 2) * (192 * T);
-    wr = blk + ((t >> 2) * 64 + lp) * 4 + (t & 3);
-    wi = blk + (((T + t) >> 2) * 64 + lp) * 4 + ((T + t) & 3);
-    ws = blk + (((2 * T + t) >> 2) * 64 + lp) * 4 + ((2 * T + t) & 3);
-  } else {
-    // two-sample engine: entry of column c = cc % 32 of tile t = cc / 32 at
-    // row m % 2 of the pair
-    const int t = cc / 32, lp = 32 * (int)(m & 1) + cc % 32;
-    float* pair = a.wb + (m >> 1) * (192 * P);
-    wr = pair + lp * (2 * P) + t;
-    wi = wr + P;
-    ws = pair + 128 * P + lp * P + t;
-  }
+  // two-sample engine (T = 2, 4): entry of column c = cc % 32 of tile
+  // t = cc / 32 at row m % 2 of the pair
+  const int t = cc / 32, lp = 32 * (int)(m & 1) + cc % 32;
+  float* pair = a.wb + (m >> 1) * (192 * P);
+  float* wr = pair + lp * (2 * P) + t;  // fr; fi at + P
+  float* wi = wr + P;
+  float* ws = pair + 128 * P + lp * P + t;  // fr + fi
   if (m >= a.M) {  // padding sample: contributes exactly zero
     if (cc == 0)
       for (int i = 0; i < HF; ++i) h[i] = 0.0f;
@@ -132,6 +121,74 @@ mfma_records_kernel(MfmaRecordArgs a, int is_q, int trig, int T, int BC) {
   }
   const double fr = mr * cj - mi * sj, fi = mr * sj + mi * cj;
   wr[0] = (float)fr; wi[0] = (float)fi; ws[0] = (float)(fr + fi);
+}
+
+// Records of the four-sample engine (T = 8): one lane per (padded sample m,
+// column c < 16, tile group g < 2) forms the factors of the four columns
+// cc = 16 t + c, t = 4 g .. 4 g + 3, and writes fr, fi and fr + fi of them as
+// three float4 slices (slices g, 2 + g and 4 + g of lane p = 16 (m % 4) + c;
+// 16 consecutive lanes fill 256 contiguous bytes).
+__global__ void __launch_bounds__(kWorkgroup)
+mfma4_records_kernel(MfmaRecordArgs a, int is_q, int trig, int BC) {
+  constexpr int T = 8;
+  const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  const int64_t m = idx >> 5;
+  const int r = (int)(idx & 31), c = r & 15, g = r >> 4;
+  if (m >= a.mpad) return;
+  const int HF = mfma_header_floats(trig);
+  const int V = 16 * T / BC;
+  float* h = a.hdr + m * HF;
+  float4* blk = reinterpret_cast<float4*>(a.wb) + (m >> 2) * (192 * T / 4);
+  const int p = 16 * (int)(m & 3) + c;
+  float4* wr = blk + g * 64 + p;
+  float4* wi = blk + (2 + g) * 64 + p;
+  float4* ws = blk + (4 + g) * 64 + p;
+  if (m >= a.M) {  // padding sample: contributes exactly zero
+    if (r == 0)
+      for (int i = 0; i < HF; ++i) h[i] = 0.0f;
+    *wr = make_float4(0.0f, 0.0f, 0.0f, 0.0f); *wi = *wr; *ws = *wr;
+    return;
+  }
+  const float kx = a.kx[m], ky = a.ky[m], kz = a.kz[m];
+  if (r == 0) {
+    if (trig == kTrigHw) {
+      h[0] = kx; h[1] = ky; h[2] = kz; h[3] = 0.0f;
+    } else {
+      const float khx = __builtin_rintf(kx * 4096.0f) * (1.0f / 4096.0f);
+      const float khy = __builtin_rintf(ky * 4096.0f) * (1.0f / 4096.0f);
+      const float khz = __builtin_rintf(kz * 4096.0f) * (1.0f / 4096.0f);
+      h[0] = khx; h[1] = khy; h[2] = khz; h[3] = 0.0f;
+      h[4] = kx - khx; h[5] = ky - khy; h[6] = kz - khz; h[7] = 0.0f;
+    }
+  }
+  const double pr = a.phi[m].x, pim = a.phi[m].y;
+  const double x0 = a.x[0], y0 = a.y[0], z0 = a.z[0];
+  float fr[4], fi[4], fs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = 16 * (4 * g + i) + c;
+    const int b = cc / V, j = cc % V;
+    double cj = 1.0, sj = 0.0;
+    if (j > 0 && j < a.N) {
+      const double ph = (double)kx * ((double)a.x[j] - x0) + (double)ky * ((double)a.y[j] - y0) +
+                        (double)kz * ((double)a.z[j] - z0);
+      sincospi(2.0 * ph, &sj, &cj);
+    }
+    double mr, mi;
+    if (is_q) {
+      mr = pr * pr + pim * pim;
+      mi = 0.0;
+    } else {
+      const float2 d = a.D[(int64_t)b * a.M + m];
+      mr = pr * d.x + pim * d.y;  // Mu = conj(phi) * D
+      mi = pr * d.y - pim * d.x;
+    }
+    const double vr = mr * cj - mi * sj, vi = mr * sj + mi * cj;
+    fr[i] = (float)vr; fi[i] = (float)vi; fs[i] = (float)(vr + vi);
+  }
+  *wr = make_float4(fr[0], fr[1], fr[2], fr[3]);
+  *wi = make_float4(fi[0], fi[1], fi[2], fi[3]);
+  *ws = make_float4(fs[0], fs[1], fs[2], fs[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -852,6 +909,12 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
                                hipStream_t s) {
   if (a.mpad <= 0) return hipSuccess;
   if (!mfma_supported(T, BC) || a.mpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  if (T == 8) {  // 32 lanes per sample, four columns each
+    const int64_t blocks = (a.mpad * 32 + kWorkgroup - 1) / kWorkgroup;
+    hipLaunchKernelGGL(mfma4_records_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, is_q,
+                       trig, BC);
+    return hipGetLastError();
+  }
   const int64_t lanes = a.mpad * 16 * T;
   const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
   hipLaunchKernelGGL(mfma_records_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, is_q,
