@@ -262,8 +262,13 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   } else if (o->tile > 0) {
     p.tile = ((int64_t)o->tile + pad - 1) / pad * pad;
   } else {
+    // about sqrt(M) samples per tile; the matrix-core engine's HW-trig path
+    // takes about 4 sqrt(M): its error is set by the hardware sine and the
+    // fp32 phase, far above the blocked sum's, and each tile fold costs
+    // (128^3 x 262,144: tile 2048 is 1 % faster than 512)
+    const int64_t f = (mfma && o->trig == FHD_TRIG_HW) ? 16 : 1;
     int64_t t = 64;
-    while (t * t < p.mpad && t < 8192) t *= 2;
+    while (t * t < f * p.mpad && t < 8192) t *= 2;
     p.tile = t;
   }
   // sample splits: one launch row per split, partial sums reduced afterwards

@@ -257,7 +257,9 @@ def test_describe_plan_mfma(lib):
     assert hw["engine"] == acc["engine"] == _lib.FHD_ENGINE_MFMA
     assert hw["voxels_per_lane"] == 128 and acc["voxels_per_lane"] == 128
     assert hw["record_dwords"] == 4 + 384 and acc["record_dwords"] == 8 + 384
-    assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 512
+    # tile ~sqrt(M) for the accurate path, ~4 sqrt(M) for the HW path
+    assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 2048
+    assert acc["tile"] == 512
     # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
     assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8
@@ -277,7 +279,7 @@ def test_describe_plan_mfma(lib):
     # 32^3 x 2048: regular for every group size, but even 8 rows of the fewest,
     # longest waves cannot fill the GPU -> the smallest groups
     tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
-    assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 8 and tiny["tile"] == 64
+    assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 8 and tiny["tile"] == 256
     # 48^3: 128 and 64 are neither divisors of a row nor whole rows of a plane
     assert fhd_describe_plan(65536, 48 ** 3, trig="hw")["voxels_per_lane"] == 32
     # fewer voxels than one group: still one wave; samples padded to the 32-sample chunk
