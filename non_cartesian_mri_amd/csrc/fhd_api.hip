@@ -286,6 +286,10 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     splits = (int32_t)((p.mpad + p.m_split - 1) / p.m_split);  // no empty rows
   }
   p.splits = splits;
+  // the four-sample engine's HW path sums each launch row as one block: no
+  // tile folds, so its kernel keeps no running totals (3 waves per SIMD)
+  if (mfma && p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && p.tile < p.m_split)
+    p.tile = p.m_split;
   p.ws_bytes = 0;
   p.hdr_bytes = mfma ? align256((size_t)p.mpad * ncmri::mfma_header_floats(p.trig) * sizeof(float)) : 0;
   for (int i = 0; i < p.npass; ++i) {

@@ -564,7 +564,12 @@ struct MfmaDirect {
 // each), so that one workgroup's barrier or copy burst is covered by the
 // other's MFMAs.  (One 8-wave workgroup per CU with 32-sample chunks was
 // 1.5 % slower at 128^3: its two waves on a SIMD wait at the same barrier.)
-template <int T, int BC, int TRIG>
+// FOLD: tiles shorter than the launch row fold into running totals (blocked
+// summation within the row).  Without FOLD the row is one summation block:
+// the accumulators hold the row's sums, no totals are kept (64 VGPRs fewer:
+// 3 waves per SIMD on the HW path), and the rows are added in a fixed order
+// by the reduction kernel.
+template <int T, int BC, int TRIG, bool FOLD>
 struct MfmaGather4 {
   static constexpr int V = 16 * T / BC;                // voxels per group
   static constexpr int HF = mfma_header_floats(TRIG);
@@ -670,7 +675,9 @@ struct MfmaGather4 {
     __syncthreads();
   }
 
-  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[T], f32x4 (&tim)[T]) {
+  template <int NT>
+  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[NT], f32x4 (&tim)[NT]) {
+    static_assert(NT == T, "fold needs the running totals");
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       tre[t] += acc[0][t] - acc[2][t];
@@ -697,11 +704,14 @@ struct MfmaGather4 {
     const int32_t cpt = (int32_t)(a.tile / C);
     if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
     publish();
-    f32x4 acc[3][T], tre[T], tim[T];
+    f32x4 acc[3][T], tre[FOLD ? T : 1], tim[FOLD ? T : 1];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
-      tre[t] = f32x4{}; tim[t] = f32x4{};
+    }
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) { tre[t] = f32x4{}; tim[t] = f32x4{}; }
     }
     int32_t left = cpt;
     for (int32_t ch = 0; ch < nch; ch += 2) {
@@ -709,9 +719,11 @@ struct MfmaGather4 {
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
                       gx, gy, gz, acc);
-      if (--left == 0) {
-        fold(acc, tre, tim);
-        left = cpt;
+      if constexpr (FOLD) {
+        if (--left == 0) {
+          fold(acc, tre, tim);
+          left = cpt;
+        }
       }
       publish();
       if (ch + 1 >= nch) break;
@@ -719,13 +731,16 @@ struct MfmaGather4 {
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
                       gx, gy, gz, acc);
-      if (--left == 0) {
-        fold(acc, tre, tim);
-        left = cpt;
+      if constexpr (FOLD) {
+        if (--left == 0) {
+          fold(acc, tre, tim);
+          left = cpt;
+        }
       }
       publish();
     }
-    fold(acc, tre, tim);
+    if constexpr (FOLD) fold(acc, tre, tim);
+    (void)left;
 
     if (!regular) return;
     float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
@@ -738,7 +753,12 @@ struct MfmaGather4 {
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (lane >> 4) + r;
         const int64_t n = vbase + (int64_t)i * V + j;
-        if (n < a.N) dst[(int64_t)b * a.N + n] = make_float2(tre[t][r], tim[t][r]);
+        if (n >= a.N) continue;
+        if constexpr (FOLD)
+          dst[(int64_t)b * a.N + n] = make_float2(tre[t][r], tim[t][r]);
+        else  // Re = P1 - P3, Im = P2 + P3 of the row's sums
+          dst[(int64_t)b * a.N + n] =
+              make_float2(acc[0][t][r] - acc[2][t][r], acc[1][t][r] + acc[2][t][r]);
       }
     }
   }
@@ -851,11 +871,16 @@ __global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int
 }
 
 // Four-sample engine: two 4-wave workgroups per CU (2 x 49 KB of LDS), 2
-// waves per SIMD.
-template <int T, int BC, int TRIG>
-__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
+// waves per SIMD; without tile folds on the HW path, three (168 VGPRs; the
+// 16-vector pass keeps two).
+template <int BC, int TRIG, bool FOLD>
+constexpr int mfma4_waves_per_simd() { return (!FOLD && TRIG == kTrigHw && BC < 16) ? 3 : 2; }
+
+template <int T, int BC, int TRIG, bool FOLD>
+__global__ void __launch_bounds__(64 * kMfma4Waves)
+__attribute__((amdgpu_waves_per_eu(mfma4_waves_per_simd<BC, TRIG, FOLD>())))
 mfma4_gather_kernel(MfmaArgs a) {
-  MfmaGather4<T, BC, TRIG>::run(a);
+  MfmaGather4<T, BC, TRIG, FOLD>::run(a);
 }
 
 template <int T, int BC, int TRIG>
@@ -869,16 +894,20 @@ using DirectFn = void (*)(MfmaArgs, int32_t);
 struct MfmaPair {
   MfmaFn gather;
   DirectFn direct;
+  MfmaFn gather_row;  // four-sample engine: the row is one summation block
 };
 
 template <int T, int BC>
 MfmaPair pick_mfma(int trig) {
   if constexpr (T == 8) {
-    if (trig == kTrigHw) return {mfma4_gather_kernel<T, BC, kTrigHw>, mfma4_direct_kernel<T, BC, kTrigHw>};
-    return {mfma4_gather_kernel<T, BC, kTrigAccurate>, mfma4_direct_kernel<T, BC, kTrigAccurate>};
+    if (trig == kTrigHw)
+      return {mfma4_gather_kernel<T, BC, kTrigHw, true>, mfma4_direct_kernel<T, BC, kTrigHw>,
+              mfma4_gather_kernel<T, BC, kTrigHw, false>};
+    return {mfma4_gather_kernel<T, BC, kTrigAccurate, true>, mfma4_direct_kernel<T, BC, kTrigAccurate>,
+            mfma4_gather_kernel<T, BC, kTrigAccurate, false>};
   } else {
-    if (trig == kTrigHw) return {mfma_gather_kernel<T, BC, kTrigHw>, mfma_direct_kernel<T, BC, kTrigHw>};
-    return {mfma_gather_kernel<T, BC, kTrigAccurate>, mfma_direct_kernel<T, BC, kTrigAccurate>};
+    if (trig == kTrigHw) return {mfma_gather_kernel<T, BC, kTrigHw>, mfma_direct_kernel<T, BC, kTrigHw>, nullptr};
+    return {mfma_gather_kernel<T, BC, kTrigAccurate>, mfma_direct_kernel<T, BC, kTrigAccurate>, nullptr};
   }
 }
 
@@ -890,7 +919,7 @@ MfmaPair select_bc(int trig, int BC) {
     case 4: return pick_mfma<T, 4>(trig);
     case 8: return pick_mfma<T, 8>(trig);
     case 16: return pick_mfma<T, 16>(trig);
-    default: return {nullptr, nullptr};
+    default: return {nullptr, nullptr, nullptr};
   }
 }
 
@@ -898,7 +927,7 @@ MfmaPair select_mfma(int trig, int T, int BC) {
   if (T == 2) return select_bc<2>(trig, BC);
   if (T == 4) return select_bc<4>(trig, BC);
   if (T == 8) return select_bc<8>(trig, BC);
-  return {nullptr, nullptr};
+  return {nullptr, nullptr, nullptr};
 }
 
 }  // namespace
@@ -932,15 +961,17 @@ hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const Mfm
       a.tile <= 0)
     return hipErrorInvalidValue;
   if (a.N <= 0) return hipSuccess;
-  const int V = 16 * T / BC;
   const int64_t waves = mfma_gather_waves(a.N, T, BC);
-  // gather: workgroups of 4 waves (two-sample engine) or 8 (four-sample);
-  // direct: workgroups of 4 waves over the same wave numbering
+  // gather: workgroups of kWorkgroup / 64 waves (two-sample engine) or
+  // kMfma4Waves (four-sample engine); direct: workgroups of kWorkgroup / 64
+  // waves over the same wave numbering
   const int wg_waves = T == 8 ? kMfma4Waves : kWorkgroup / 64;
   const int64_t blocks = (waves + wg_waves - 1) / wg_waves;
   const int64_t dblocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
-  (void)V;
-  hipLaunchKernelGGL(fn.gather, dim3((unsigned)blocks, (unsigned)splits), dim3(64 * wg_waves), 0, s, a);
+  // a tile as long as a launch row never folds: the four-sample engine then
+  // keeps no running totals
+  const MfmaFn g = (fn.gather_row && a.tile >= a.m_split) ? fn.gather_row : fn.gather;
+  hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(64 * wg_waves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn.direct, dim3((unsigned)dblocks), dim3(kWorkgroup), 0, s, a, splits);

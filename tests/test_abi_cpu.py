@@ -257,8 +257,9 @@ def test_describe_plan_mfma(lib):
     assert hw["engine"] == acc["engine"] == _lib.FHD_ENGINE_MFMA
     assert hw["voxels_per_lane"] == 128 and acc["voxels_per_lane"] == 128
     assert hw["record_dwords"] == 4 + 384 and acc["record_dwords"] == 8 + 384
-    # tile ~sqrt(M) for the accurate path, ~4 sqrt(M) for the HW path
-    assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 2048
+    # tile ~sqrt(M) for the accurate path; the four-sample engine's HW path
+    # sums a whole launch row (16,384 samples) as one block
+    assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 16384
     assert acc["tile"] == 512
     # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16

@@ -380,3 +380,16 @@ def test_mfma_deterministic_and_engines_agree(trig, G):
     assert np.array_equal(a, gpu_fhd(p, d, trig=trig, engine="mfma", voxels_per_lane=G))
     v = gpu_fhd(p, d, trig=trig, engine="valu")
     assert np.linalg.norm(a - v) <= TOL[trig] * np.linalg.norm(v)
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_mfma4_row_block_and_folded_tiles(mfma_grid, trig, splits):
+    """Four-sample engine: a tile as long as the launch row takes the kernel
+    without running totals (each row one summation block); shorter tiles fold
+    into totals.  Both match the oracle, F^H D and Q."""
+    p, d, ref, qref = mfma_grid
+    base = dict(trig=trig, engine="mfma", voxels_per_lane=128, sample_splits=splits)
+    for tile in (64, 8192):   # 8192 >= every row of the 1001 samples
+        assert_close(gpu_fhd(p, d, tile=tile, **base), ref, TOL[trig], f"fhd {trig} rows={splits} tile={tile}")
+        assert_close(gpu_q(p, d, tile=tile, **base), qref, TOL[trig], f"q {trig} rows={splits} tile={tile}")
