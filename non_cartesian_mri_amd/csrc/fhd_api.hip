@@ -396,6 +396,11 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     gs = (gs + C - 1) / C * C;
     p.g_split[i] = gs > 0 ? gs : C;
   }
+  // the four-group engine's HW path sums each launch row as one block: no
+  // tile folds, so its kernel keeps no running totals (3 waves per SIMD)
+  if (p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN)
+    for (int i = 0; i < p.npass; ++i)
+      if (p.g_split[i] > p.tile) p.tile = p.g_split[i];
   p.m_split = 0;
   p.hdr_bytes = 0;
   p.ws_bytes = 0;

@@ -378,11 +378,14 @@ struct FwdGather {
 // evaluates one phase with its sine and cosine per block and it serves
 // 3 T = 24 MFMAs (768 matrix cycles), twice the pair engine's.  The packed
 // groups stream through LDS in 16-group chunks (24 KB) shared by the 4 waves
-// of a workgroup, two workgroups per CU.  After the last group each wave
-// writes its 16 x 128 complex block of G to LDS and all 64 lanes contract it:
-// four lanes per sample take every fourth offset, and their sums are
-// combined in a fixed order.
-template <int T, int BC, int TRIG>
+// of a workgroup.  After the last group each wave writes its 16 x 128
+// complex block of G to LDS, one half of the columns at a time, and all 64
+// lanes contract it: four lanes per sample take every fourth offset, and
+// their sums are combined in a fixed order.  FOLD: tiles shorter than the
+// launch row fold into running totals; without it the launch row is one
+// summation block and the kernel keeps no totals (fewer registers, 3 waves
+// per SIMD on the HW path).
+template <int T, int BC, int TRIG, bool FOLD>
 struct FwdGather4 {
   static constexpr int V = 16 * T / BC;
   static constexpr int C = kMfma4Chunk;           // groups per chunk
@@ -392,9 +395,11 @@ struct FwdGather4 {
   static constexpr int NB = C / 4 * QF * 4 / 1024;  // 1 KiB image blocks per chunk
   static constexpr int NH = C;                    // header float4s per chunk (one per group)
   static constexpr int SB = C / 4 * QF / 4;       // float4s of one staging buffer
-  static constexpr int GW = 16 * 16 * T * 2 / 4;  // float4s of one wave's G block
-  static constexpr int LDS4 = 2 * SB > NW * GW ? 2 * SB : NW * GW;
+  static constexpr int HC = 8 * T;                // G columns per half
+  static constexpr int GH = 16 * HC * 2 / 4;       // float4s of one wave's half G block
+  static constexpr int LDS4 = 2 * SB > NW * GH ? 2 * SB : NW * GH;
   static_assert(T % 4 == 0 && V >= 1 && V * BC == 16 * T, "group shape");
+  static_assert(BC == 1 ? V == 2 * HC : HC % V == 0, "a half holds whole data vectors");
   static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
 
   __device__ static __forceinline__ void stage(const FwdArgs& a, int64_t g, int wig, int lane,
@@ -403,8 +408,8 @@ struct FwdGather4 {
         buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + (g / 4) * (QF / 4), NB * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NB / NW; ++i) {
-      const int blk = i * NW + wig;
-      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
+      const int blk = i * NW + wig;   // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)(lb + blk * 64), 16, lane * 16, blk * 1024, 0, 0);
     }
     if (wig == 0 && lane < NH)
       lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.ghdr) + g, NH * 16), lane * 16, lh);
@@ -440,35 +445,95 @@ struct FwdGather4 {
     }
   }
 
-  // One chunk of 16 groups (4 blocks), pipelined by one block as in the
-  // pair engine.
+  // Slices [sl] of block q for units t of one half: half h = slices h, 2 + h,
+  // 4 + h (the three products' entries for t in [4h, 4h + 4)).
+  __device__ static __forceinline__ void load_half(const float* __restrict__ wb, int q, int lane, int h,
+                                                   float (&bv)[3 * T]) {
+    const float* pp = wb + q * QF;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int sl = 2 * p + h;
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  __device__ static __forceinline__ void load_header(const float* __restrict__ hb, int q, int lane,
+                                                     float (&hs)[3]) {
+    const float* hp = hb + (4 * q + (lane >> 4)) * 4;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) hs[i] = hp[i];
+  }
+
+  template <int H>
+  __device__ static __forceinline__ void mfmas_half(const float (&av)[3], const float (&bv)[3 * T],
+                                                    f32x4 (&acc)[3][T]) {
+#pragma unroll
+    for (int u = 0; u < T / 2; ++u) {
+      const int t = H * (T / 2) + u;
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[T + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2 * T + t], acc[2][t], 0, 0, 0);
+    }
+  }
+
+  // One chunk of 16 groups (4 blocks).  HW trig: one set of B entries; the
+  // next block's first-half slices are read once this block's first-half
+  // MFMAs have issued, its second half after the rest (each a half block of
+  // MFMAs ahead of its use).  Accurate trig: pipelined by one whole block as
+  // in the pair engine.
   __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb,
                                                int lane, const SampleK<TRIG>& k, f32x4 (&acc)[3][T]) {
     constexpr int NQ = C / 4;
-    float hc[3], bc[3 * T], av[3];
-    load_block(hb, wb, 0, lane, hc, bc);
-    if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hc, av);
+    if constexpr (TRIG == kTrigHw) {
+      float hc[3], bv[3 * T], av[3];
+      load_header(hb, 0, lane, hc);
+      load_half(wb, 0, lane, 0, bv);
+      load_half(wb, 0, lane, 1, bv);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      float hn[3], bn[3 * T];
-      if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
-      sched_fence();
-      if constexpr (TRIG == kTrigHw) fwd_entries<TRIG>(k, hc, av);
-      mfmas(av, bc, acc);
-      sched_fence();
-      if (q + 1 < NQ) {
-        if constexpr (TRIG != kTrigHw) fwd_entries<TRIG>(k, hn, av);
+      for (int q = 0; q < NQ; ++q) {
+        float hn[3];
+        if (q + 1 < NQ) load_header(hb, q + 1, lane, hn);
+        sched_fence();
+        fwd_entries<TRIG>(k, hc, av);
+        mfmas_half<0>(av, bv, acc);
+        sched_fence();
+        if (q + 1 < NQ) load_half(wb, q + 1, lane, 0, bv);
+        sched_fence();
+        mfmas_half<1>(av, bv, acc);
+        sched_fence();
+        if (q + 1 < NQ) {
+          load_half(wb, q + 1, lane, 1, bv);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) hc[i] = hn[i];
-#pragma unroll
-        for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
+          for (int i = 0; i < 3; ++i) hc[i] = hn[i];
+        }
+        sched_fence();
       }
-      sched_fence();
+    } else {
+      float hc[3], bc[3 * T], av[3];
+      load_block(hb, wb, 0, lane, hc, bc);
+      fwd_entries<TRIG>(k, hc, av);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        float hn[3], bn[3 * T];
+        if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
+        sched_fence();
+        mfmas(av, bc, acc);
+        sched_fence();
+        if (q + 1 < NQ) {
+          fwd_entries<TRIG>(k, hn, av);
+#pragma unroll
+          for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
+        }
+        sched_fence();
+      }
     }
   }
 
   // Tile end: Re = P1 + P3, Im = P2 - P3 into the running totals.
-  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[T], f32x4 (&tim)[T]) {
+  template <int NT>
+  __device__ static __forceinline__ void fold(f32x4 (&acc)[3][T], f32x4 (&tre)[NT], f32x4 (&tim)[NT]) {
+    static_assert(NT == T, "fold needs the running totals");
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       tre[t] += acc[0][t] + acc[2][t];
@@ -483,7 +548,8 @@ struct FwdGather4 {
     __shared__ float4 sh0[NH], sh1[NH];
     float4* sb0 = lds;
     float4* sb1 = lds + SB;
-    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t wave = (int64_t)blockIdx.x * NW + wig;
     const int64_t m = wave * 16 + (lane & 15);   // this lane's sample
     const bool valid = m < a.M;
@@ -499,66 +565,96 @@ struct FwdGather4 {
     const int32_t cpt = (int32_t)(a.tile / C);
     if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
     publish();
-    f32x4 acc[3][T], tre[T], tim[T];
+    f32x4 acc[3][T], tre[FOLD ? T : 1], tim[FOLD ? T : 1];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
-      tre[t] = f32x4{}; tim[t] = f32x4{};
     }
+#pragma unroll
+    for (int t = 0; t < (FOLD ? T : 1); ++t) { tre[t] = f32x4{}; tim[t] = f32x4{}; }
     int32_t left = cpt;
-    for (int32_t ch = 0; ch < nch; ch += 2) {
-      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
-      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
-      if (--left == 0) {
-        fold(acc, tre, tim);
-        left = cpt;
+    auto tile_end = [&]() {
+      if constexpr (FOLD) {
+        if (--left == 0) {
+          fold(acc, tre, tim);
+          left = cpt;
+        }
       }
+    };
+    int32_t ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
+      tile_end();
       publish();
-      if (ch + 1 >= nch) break;
       if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
       chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, acc);
-      if (--left == 0) {
-        fold(acc, tre, tim);
-        left = cpt;
-      }
+      tile_end();
       publish();
     }
-    fold(acc, tre, tim);
+    if (ch < nch) {
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
+      tile_end();
+      publish();
+    }
+    if constexpr (FOLD) fold(acc, tre, tim);
+    (void)left;
+    // the block's Re = P1 + P3, Im = P2 - P3 (the accumulators end here)
+    f32x4 ore[T], oim[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      ore[t] = FOLD ? tre[FOLD ? t : 0] : acc[0][t] + acc[2][t];
+      oim[t] = FOLD ? tim[FOLD ? t : 0] : acc[1][t] - acc[2][t];
+    }
 
     // Finish.  Every wave has passed the last barrier, so the staging buffers
-    // are free: each wave stores its 16 x 16 T complex block of G there ...
-    float2* gl = reinterpret_cast<float2*>(lds + wig * GW);
+    // are free.  Per half of the columns (units t of one half): each wave
+    // stores its 16 x 8 T complex block of G there ...
+    float2* gl = reinterpret_cast<float2*>(lds + wig * GH);
+    const float2* gr = gl + (lane & 15) * HC;
     const int c = lane & 15;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * (lane >> 4) + r;
-        gl[i * (16 * T) + 16 * t + c] = make_float2(tre[t][r], tim[t][r]);
-      }
-    __syncthreads();
-    // ... and lane l contracts the offsets j = l / 16 (mod 4) of row l % 16 (its
-    // sample) with exp(-i 2 pi k . d_j); the four lanes of a row then add
-    // their sums, (p0 + p1) + (p2 + p3), and one of them multiplies by phi_m.
-    const float2* gr = gl + (lane & 15) * (16 * T);
     float dre[BC], dim[BC];
 #pragma unroll
     for (int b = 0; b < BC; ++b) { dre[b] = 0.0f; dim[b] = 0.0f; }
     const bool any_voxel = a.N > 0;
     const float x0 = any_voxel ? a.x[0] : 0.0f, y0 = any_voxel ? a.y[0] : 0.0f, z0 = any_voxel ? a.z[0] : 0.0f;
-    if (valid) {
-      for (int j = lane >> 4; j < V && j < a.N; j += 4) {
-        float cj = 1.0f, sj = 0.0f;
-        if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
 #pragma unroll
-        for (int b = 0; b < BC; ++b) {
-          const float2 gv = gr[b * V + j];
-          // (cj - i sj)(gre + i gim)
-          dre[b] = __builtin_fmaf(cj, gv.x, __builtin_fmaf(sj, gv.y, dre[b]));
-          dim[b] = __builtin_fmaf(cj, gv.y, __builtin_fmaf(-sj, gv.x, dim[b]));
+    for (int h = 0; h < 2; ++h) {
+      if (h > 0) __syncthreads();   // the first half's reads are done
+#pragma unroll
+      for (int u = 0; u < T / 2; ++u) {
+        const int t = h * (T / 2) + u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * (lane >> 4) + r;
+          gl[i * HC + 16 * u + c] = make_float2(ore[t][r], oim[t][r]);
+        }
+      }
+      __syncthreads();
+      // ... and lane l contracts the offsets j = l / 16 (mod 4) of row l % 16
+      // (its sample) with exp(-i 2 pi k . d_j).  One vector: this half holds
+      // the offsets [h HC, (h + 1) HC); several: it holds vectors
+      // [h BC/2, (h + 1) BC/2), every offset.
+      if (valid) {
+        constexpr int JN = BC == 1 ? HC : V;
+        const int j0 = BC == 1 ? h * HC : 0;
+        for (int jj = lane >> 4; jj < JN && j0 + jj < a.N; jj += 4) {
+          const int j = j0 + jj;
+          float cj = 1.0f, sj = 0.0f;
+          if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
+#pragma unroll
+          for (int bb = 0; bb < (BC == 1 ? 1 : BC / 2); ++bb) {
+            const int b = BC == 1 ? 0 : h * (BC / 2) + bb;
+            const float2 gv = gr[bb * V + jj];
+            // (cj - i sj)(gre + i gim)
+            dre[b] = __builtin_fmaf(cj, gv.x, __builtin_fmaf(sj, gv.y, dre[b]));
+            dim[b] = __builtin_fmaf(cj, gv.y, __builtin_fmaf(-sj, gv.x, dim[b]));
+          }
         }
       }
     }
+    // the four lanes of a row add their sums, (p0 + p1) + (p2 + p3), and one
+    // of them multiplies by phi_m
 #pragma unroll
     for (int b = 0; b < BC; ++b) {
       dre[b] += __shfl_xor(dre[b], 16);
@@ -631,51 +727,56 @@ fwd_gather_kernel(FwdArgs a) {
   FwdGather<T, BC, TRIG>::run(a);
 }
 
-template <int T, int BC, int TRIG>
-__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(2)))
+template <int BC, int TRIG, bool FOLD>
+constexpr int fwd4_waves_per_simd() { return (!FOLD && TRIG == kTrigHw && BC < 16) ? 3 : 2; }
+
+template <int T, int BC, int TRIG, bool FOLD>
+__global__ void __launch_bounds__(kWorkgroup)
+__attribute__((amdgpu_waves_per_eu(fwd4_waves_per_simd<BC, TRIG, FOLD>())))
 fwd4_gather_kernel(FwdArgs a) {
-  FwdGather4<T, BC, TRIG>::run(a);
+  FwdGather4<T, BC, TRIG, FOLD>::run(a);
 }
 
 using FwdFn = void (*)(FwdArgs);
 
-template <int T, int BC>
-void pick(int trig, FwdFn& gather, FwdFn& direct) {
-  if (trig == kTrigHw) {
-    if constexpr (T == 8) gather = fwd4_gather_kernel<T, BC, kTrigHw>;
-    else gather = fwd_gather_kernel<T, BC, kTrigHw>;
-    direct = fwd_direct_kernel<T, BC, kTrigHw>;
-  } else {
-    if constexpr (T == 8) gather = fwd4_gather_kernel<T, BC, kTrigAccurate>;
-    else gather = fwd_gather_kernel<T, BC, kTrigAccurate>;
-    direct = fwd_direct_kernel<T, BC, kTrigAccurate>;
-  }
+// gather: the kernel for tiles shorter than a launch row; gather_row (four-
+// group engine only) the one for a tile that spans the row.
+struct FwdKernels { FwdFn gather; FwdFn direct; FwdFn gather_row; };
+
+template <int T, int BC, int TRIG>
+FwdKernels pick() {
+  if constexpr (T == 8)
+    return {fwd4_gather_kernel<T, BC, TRIG, true>, fwd_direct_kernel<T, BC, TRIG>,
+            fwd4_gather_kernel<T, BC, TRIG, false>};
+  else
+    return {fwd_gather_kernel<T, BC, TRIG>, fwd_direct_kernel<T, BC, TRIG>, nullptr};
 }
 
 template <int T>
-bool select_bc(int trig, int BC, FwdFn& gather, FwdFn& direct) {
+bool select_bc(int trig, int BC, FwdKernels& fn) {
+  const bool hw = trig == kTrigHw;
   switch (BC) {
-    case 1: pick<T, 1>(trig, gather, direct); return true;
-    case 2: pick<T, 2>(trig, gather, direct); return true;
-    case 4: pick<T, 4>(trig, gather, direct); return true;
-    case 8: pick<T, 8>(trig, gather, direct); return true;
-    case 16: pick<T, 16>(trig, gather, direct); return true;
+    case 1: fn = hw ? pick<T, 1, kTrigHw>() : pick<T, 1, kTrigAccurate>(); return true;
+    case 2: fn = hw ? pick<T, 2, kTrigHw>() : pick<T, 2, kTrigAccurate>(); return true;
+    case 4: fn = hw ? pick<T, 4, kTrigHw>() : pick<T, 4, kTrigAccurate>(); return true;
+    case 8: fn = hw ? pick<T, 8, kTrigHw>() : pick<T, 8, kTrigAccurate>(); return true;
+    case 16: fn = hw ? pick<T, 16, kTrigHw>() : pick<T, 16, kTrigAccurate>(); return true;
     default: return false;
   }
 }
 
-bool select_fwd(int trig, int T, int BC, FwdFn& gather, FwdFn& direct) {
-  if (T == 2) return select_bc<2>(trig, BC, gather, direct);
-  if (T == 4) return select_bc<4>(trig, BC, gather, direct);
-  if (T == 8) return select_bc<8>(trig, BC, gather, direct);
+bool select_fwd(int trig, int T, int BC, FwdKernels& fn) {
+  if (T == 2) return select_bc<2>(trig, BC, fn);
+  if (T == 4) return select_bc<4>(trig, BC, fn);
+  if (T == 8) return select_bc<8>(trig, BC, fn);
   return false;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_pack(int T, int BC, const FwdArgs& a, hipStream_t s) {
-  FwdFn g, d;
-  if (!select_fwd(kTrigHw, T, BC, g, d) || a.gpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  FwdKernels fn;
+  if (!select_fwd(kTrigHw, T, BC, fn) || a.gpad % kMfmaChunk != 0) return hipErrorInvalidValue;
   if (a.gpad <= 0) return hipSuccess;
   if (!a.glist) return hipErrorInvalidValue;
   const int64_t lanes = a.gpad * 16 * T;
@@ -689,8 +790,8 @@ hipError_t launch_fwd_pack(int T, int BC, const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdArgs& a,
                              hipStream_t s) {
-  FwdFn g, d;
-  if (!select_fwd(trig, T, BC, g, d) || splits < 1 || (splits > 1) != (a.partial != nullptr))
+  FwdKernels fn;
+  if (!select_fwd(trig, T, BC, fn) || splits < 1 || (splits > 1) != (a.partial != nullptr))
     return hipErrorInvalidValue;
   if (a.gpad % kMfmaChunk != 0 || a.g_split % kMfmaChunk != 0 || a.tile % kMfmaChunk != 0 ||
       a.tile <= 0)
@@ -700,17 +801,18 @@ hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdA
   const int64_t per_wave = T == 8 ? 16 : 32;
   const int64_t waves = (a.M + per_wave - 1) / per_wave;
   const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  const FwdFn g = (fn.gather_row && a.tile >= a.g_split) ? fn.gather_row : fn.gather;
   hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStream_t s) {
-  FwdFn g, d;
-  if (!select_fwd(trig, T, BC, g, d) || a.tile <= 0) return hipErrorInvalidValue;
+  FwdKernels fn;
+  if (!select_fwd(trig, T, BC, fn) || a.tile <= 0) return hipErrorInvalidValue;
   if (a.M <= 0 || a.N <= 0 || a.gpad <= 0) return hipSuccess;
   if (!a.glist) return hipErrorInvalidValue;
   const int64_t blocks = (a.M + kWorkgroup - 1) / kWorkgroup;
-  hipLaunchKernelGGL(d, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a);
+  hipLaunchKernelGGL(fn.direct, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a);
   return hipGetLastError();
 }
 

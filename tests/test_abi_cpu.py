@@ -350,7 +350,10 @@ def test_forward_plan(lib):
     p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
     assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 128
     assert p["record_dwords"] == 4 + 384 and p["padded_samples"] == 262144
-    assert p["sample_splits"] == 1 and p["tile"] == 512      # ~4 sqrt(groups) on the HW path
+    # HW trig: the launch row (all 16,384 groups) is one summation block
+    assert p["sample_splits"] == 1 and p["tile"] == 16384
+    # accurate trig keeps ~sqrt(groups) per tile
+    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate")["tile"] == 128
     pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
     assert p["workspace_bytes"] == pas(16384, 8)
     # groups of 64 on request: the pair engine, 32,768 groups
@@ -364,7 +367,7 @@ def test_forward_plan(lib):
     # batch 3 on 64^3: passes of 2 and 1 images, T = 8: groups of 64 and 128 voxels
     # (128 = two rows of a plane)
     b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1)
-    assert b["passes"] == 2 and b["voxels_per_lane"] == 64
+    assert b["passes"] == 2 and b["voxels_per_lane"] == 64 and b["tile"] == 4096
     assert b["workspace_bytes"] == pas(4096, 8) + pas(2048, 8)
     # with groups of 32 per image on request (T = 2): groups of 16 and 32
     b2 = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1, voxels_per_lane=32)

@@ -227,3 +227,22 @@ def test_forward_512cubed_sampled(oracle_mod, trig):
     print(f"[oracle] forward 512^3 x 16 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
     got = gpu_forward(p, rho, trig=trig)
     assert_close(got[:, idx], ref, TOL[trig], f"forward 512^3 {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("B", [1, 3])
+def test_forward_four_group_row_block_and_folded_tiles(oracle_mod, fwd_grid, trig, splits, B):
+    """Four-group engine (groups of 128): a tile that spans the launch row
+    takes the kernel without running totals; shorter tiles fold into totals.
+    One vector, and three (passes of two and one: each half of the G block
+    then holds whole vectors)."""
+    p, d, rho1, ref1 = fwd_grid
+    if B == 1:
+        rho, ref = rho1, ref1
+    else:
+        rho = _images(403, B, p.N)
+        ref = oracle_mod.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho)
+    for tile in (32, 1 << 20):
+        got = gpu_forward(p, rho, d, trig=trig, tile=tile, sample_splits=splits, voxels_per_lane=128)
+        assert_close(got, ref, TOL[trig], f"forward G=128 {trig} B={B} rows={splits} tile={tile}")
