@@ -607,33 +607,76 @@ struct MfmaGather4 {
     }
   }
 
-  // One chunk, software-pipelined by one block of samples exactly like the
-  // two-sample engine (HW: A entries right before the block's MFMAs;
-  // accurate: one block ahead, right after the previous block's MFMAs).
+  // Slices of block q for the units t of one half h: slices h, 2 + h, 4 + h
+  // (the three products' entries for t in [4h, 4h + 4)).
+  __device__ static __forceinline__ void load_half(const float* __restrict__ wb, int q, int lane, int h,
+                                                   float (&bv)[3 * T]) {
+    const float* pp = wb + q * QF;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int sl = 2 * p + h;
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  __device__ static __forceinline__ void load_header(const float* __restrict__ hb, int q, int lane,
+                                                     float (&hs)[HK]) {
+    const float* hp = hb + (4 * q + (lane >> 4)) * HF;
+#pragma unroll
+    for (int i = 0; i < HK; ++i) hs[i] = hp[i];
+  }
+
+  template <int H>
+  __device__ static __forceinline__ void mfmas_half(const float (&av)[3], const float (&bv)[3 * T],
+                                                    f32x4 (&acc)[3][T]) {
+#pragma unroll
+    for (int u = 0; u < T / 2; ++u) {
+      const int t = H * (T / 2) + u;
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[T + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2 * T + t], acc[2][t], 0, 0, 0);
+    }
+  }
+
+  // One chunk.  HW trig: one set of B entries; the next block's first-half
+  // slices are read once this block's first-half MFMAs have issued, its
+  // second half after the rest (each half a block of MFMAs ahead of its use),
+  // and the A entries are formed right before the block's MFMAs.  Accurate
+  // trig: software-pipelined by one whole block (A entries one block ahead,
+  // right after the previous block's MFMAs), as in the two-sample engine.
   __device__ static __forceinline__ void regular_chunk(const float* __restrict__ hb,
                                                        const float* __restrict__ wb, int lane,
                                                        float gx, float gy, float gz,
                                                        f32x4 (&acc)[3][T]) {
     constexpr int NQ = C / 4;
-    float hc[HK], bc[3 * T], av[3];
-    load_block(hb, wb, 0, lane, hc, bc);
     if constexpr (TRIG == kTrigHw) {
+      float hc[HK], bv[3 * T], av[3];
+      load_header(hb, 0, lane, hc);
+      load_half(wb, 0, lane, 0, bv);
+      load_half(wb, 0, lane, 1, bv);
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        float hn[HK], bn[3 * T];
-        if (q + 1 < NQ) load_block(hb, wb, q + 1, lane, hn, bn);
+        float hn[HK];
+        if (q + 1 < NQ) load_header(hb, q + 1, lane, hn);
         sched_fence();
         group_entries<TRIG>(hc, gx, gy, gz, av);
-        mfmas(av, bc, acc);
+        mfmas_half<0>(av, bv, acc);
+        sched_fence();
+        if (q + 1 < NQ) load_half(wb, q + 1, lane, 0, bv);
+        sched_fence();
+        mfmas_half<1>(av, bv, acc);
         sched_fence();
         if (q + 1 < NQ) {
+          load_half(wb, q + 1, lane, 1, bv);
 #pragma unroll
           for (int i = 0; i < HK; ++i) hc[i] = hn[i];
-#pragma unroll
-          for (int i = 0; i < 3 * T; ++i) bc[i] = bn[i];
         }
+        sched_fence();
       }
     } else {
+      float hc[HK], bc[3 * T], av[3];
+      load_block(hb, wb, 0, lane, hc, bc);
       group_entries<TRIG>(hc, gx, gy, gz, av);
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
@@ -662,8 +705,9 @@ struct MfmaGather4 {
         buffer_rsrc(reinterpret_cast<const float4*>(a.wb) + (c / 4) * (QF / 4), NB * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NB / NW; ++i) {
-      const int blk = i * NW + wave_in_wg;
-      lds_dma16(rb, (blk * 64 + lane) * 16, lb + blk * 64);
+      const int blk = i * NW + wave_in_wg;   // wave-uniform: an SGPR offset
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)(lb + blk * 64), 16, lane * 16,
+                                               blk * 1024, 0, 0);
     }
     if (wave_in_wg == 0 && lane < NH)
       lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.hdr) + c * (HF / 4), NH * 16), lane * 16, lh);
@@ -689,7 +733,8 @@ struct MfmaGather4 {
   __device__ static void run(const MfmaArgs& a) {
     __shared__ float4 sb0[C / 4 * QF / 4], sb1[C / 4 * QF / 4];
     __shared__ float4 sh0[NH], sh1[NH];
-    const int tid = threadIdx.x, lane = tid & 63, wig = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave in the workgroup
     const int64_t wave = (int64_t)blockIdx.x * NW + wig;
     const int64_t vbase = wave * 16 * V;                  // first voxel of the wave
     const int64_t n0 = vbase + (int64_t)(lane & 15) * V;  // first voxel of the lane's group
@@ -714,29 +759,36 @@ struct MfmaGather4 {
       for (int t = 0; t < T; ++t) { tre[t] = f32x4{}; tim[t] = f32x4{}; }
     }
     int32_t left = cpt;
-    for (int32_t ch = 0; ch < nch; ch += 2) {
-      if (ch + 1 < nch) stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
-      if (regular)
-        regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
-                      gx, gy, gz, acc);
+    auto tile_end = [&]() {
       if constexpr (FOLD) {
         if (--left == 0) {
           fold(acc, tre, tim);
           left = cpt;
         }
       }
+    };
+    // pairs of chunks (sb0, then sb1), then an odd last chunk, already in
+    // sb0: one exit from the loop, so the accumulators are updated in place
+    int32_t ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
+                      gx, gy, gz, acc);
+      tile_end();
       publish();
-      if (ch + 1 >= nch) break;
       if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
       if (regular)
         regular_chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane,
                       gx, gy, gz, acc);
-      if constexpr (FOLD) {
-        if (--left == 0) {
-          fold(acc, tre, tim);
-          left = cpt;
-        }
-      }
+      tile_end();
+      publish();
+    }
+    if (ch < nch) {
+      if (regular)
+        regular_chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane,
+                      gx, gy, gz, acc);
+      tile_end();
       publish();
     }
     if constexpr (FOLD) fold(acc, tre, tim);
@@ -870,15 +922,16 @@ __global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int
   MfmaDirect<T, BC, TRIG>::run(a, splits);
 }
 
-// Four-sample engine: two 4-wave workgroups per CU (2 x 49 KB of LDS), 2
-// waves per SIMD; without tile folds on the HW path, three (168 VGPRs; the
-// 16-vector pass keeps two).
-template <int BC, int TRIG, bool FOLD>
-constexpr int mfma4_waves_per_simd() { return (!FOLD && TRIG == kTrigHw && BC < 16) ? 3 : 2; }
+// Four-sample engine: 4-wave workgroups of ~49 KB of LDS.  With running
+// totals 2 waves per SIMD (two workgroups per CU); without them (the launch
+// row one summation block) the kernel fits 168 VGPRs: 3 waves per SIMD,
+// three workgroups per CU.
+template <bool FOLD>
+constexpr int mfma4_waves_per_simd() { return FOLD ? 2 : 3; }
 
 template <int T, int BC, int TRIG, bool FOLD>
 __global__ void __launch_bounds__(64 * kMfma4Waves)
-__attribute__((amdgpu_waves_per_eu(mfma4_waves_per_simd<BC, TRIG, FOLD>())))
+__attribute__((amdgpu_waves_per_eu(mfma4_waves_per_simd<FOLD>())))
 mfma4_gather_kernel(MfmaArgs a) {
   MfmaGather4<T, BC, TRIG, FOLD>::run(a);
 }
