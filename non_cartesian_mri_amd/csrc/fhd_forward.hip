@@ -728,7 +728,7 @@ fwd_gather_kernel(FwdArgs a) {
 }
 
 template <int BC, int TRIG, bool FOLD>
-constexpr int fwd4_waves_per_simd() { return (!FOLD && TRIG == kTrigHw && BC < 16) ? 3 : 2; }
+constexpr int fwd4_waves_per_simd() { return (!FOLD && TRIG == kTrigHw) ? 3 : 2; }
 
 template <int T, int BC, int TRIG, bool FOLD>
 __global__ void __launch_bounds__(kWorkgroup)
