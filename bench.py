@@ -39,20 +39,20 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "ae04ce155c76a56f",
-        "fetch_bytes": 1763621.1 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9",
+        "fetch_bytes": 1975686.9 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "ae04ce155c76a56f",
-        "fetch_bytes": 1790527.8 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9",
+        "fetch_bytes": 1782119.0 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "09a9b92cc7ea3d23",
-        "fetch_bytes": 1571094.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "1bfd70071cd52ea6",
+        "fetch_bytes": 1577119.5 * 1024 * 2.0, "write_bytes": 31299.3 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "09a9b92cc7ea3d23",
-        "fetch_bytes": 1566636.1 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "1bfd70071cd52ea6",
+        "fetch_bytes": 1521269.3 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
