@@ -397,10 +397,15 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     p.g_split[i] = gs > 0 ? gs : C;
   }
   // the four-group engine's HW path sums each launch row as one block: no
-  // tile folds, so its kernel keeps no running totals (3 waves per SIMD)
-  if (p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN)
-    for (int i = 0; i < p.npass; ++i)
-      if (p.g_split[i] > p.tile) p.tile = p.g_split[i];
+  // tile folds, so its kernel keeps no running totals (3 waves per SIMD).
+  // Only for rows of at most 65,536 groups (128^3: 16,384): at 512^3 (rows
+  // of 1,048,576 groups, 1.6 GB of packed groups per wave's stream) the
+  // three resident workgroups per CU were 1.2 % slower than two with tiles.
+  if (p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN) {
+    int64_t gs = 0;
+    for (int i = 0; i < p.npass; ++i) gs = p.g_split[i] > gs ? p.g_split[i] : gs;
+    if (gs <= 65536 && gs > p.tile) p.tile = gs;
+  }
   p.m_split = 0;
   p.hdr_bytes = 0;
   p.ws_bytes = 0;

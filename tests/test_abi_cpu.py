@@ -352,7 +352,9 @@ def test_forward_plan(lib):
     assert p["record_dwords"] == 4 + 384 and p["padded_samples"] == 262144
     # HW trig: the launch row (all 16,384 groups) is one summation block
     assert p["sample_splits"] == 1 and p["tile"] == 16384
-    # accurate trig keeps ~sqrt(groups) per tile
+    # accurate trig keeps ~sqrt(groups) per tile; so does HW with rows of more
+    # than 65,536 groups (512^3: ~4 sqrt(G))
+    assert fhd_describe_plan(262144, 512 ** 3, op="forward", trig="hw")["tile"] == 4096
     assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate")["tile"] == 128
     pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
     assert p["workspace_bytes"] == pas(16384, 8)
