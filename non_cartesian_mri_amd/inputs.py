@@ -232,6 +232,9 @@ CONFIGS = {
     "fhd_64cube_65536_radial": "FhD 64^3 voxels, M=65,536 on 256 Fibonacci spokes x 256 points",
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels, M=262,144 on 64 kz planes x 4096-point spirals",
     "fhd_512cube_262144_spirals": "FhD 512^3 voxels (N beyond 128^3), the same 262,144-sample spiral stack",
+    "fhd_128cube_262144_spirals_jittered": "FhD at 2,097,152 off-grid points (each 128^3 voxel centre displaced by "
+                                           "a seeded uniform offset in [-0.25, 0.25)^3), the 128^3 workload's "
+                                           "samples, phi and D",
     "q_128cube_halfstep_1048576_uniform": "Q on a 2x-oversampled 128^3 grid (step 0.5), M=1,048,576 uniform-random k",
     "q_128cube_unitstep_1048576_uniform": "Q on a 128^3 grid with step 1 (coords -64..63), M=1,048,576 uniform-random k",
     "fhd16_96cube_500001_radial": "FhD x16 D vectors, 96^3 voxels, M=500,001 radial (odd tail)",
@@ -264,6 +267,11 @@ def make_config(name: str) -> Problem:
         phi = complex_normal(rng, M)
         D = complex_normal(rng, M)[None, :]
         return Problem(name, "fhd", kx, ky, kz, x, y, z, phi, D, 103, 128)
+    if name == "fhd_128cube_262144_spirals_jittered":
+        p = make_config("fhd_128cube_262144_spirals")
+        j = _rng(107).random((3, p.N)) - 0.5
+        x, y, z = ((c.astype(np.float64) + 0.5 * j[i]).astype(np.float32) for i, c in enumerate((p.x, p.y, p.z)))
+        return Problem(name, "fhd", p.kx, p.ky, p.kz, x, y, z, p.phi, p.D, 103, 128, extra={"jitter": 0.25})
     if name == "fhd_512cube_262144_spirals":
         rng = _rng(106)
         kx, ky, kz = stack_of_spirals_k(64, 4096, 64)

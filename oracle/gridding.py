@@ -69,16 +69,21 @@ def lattice_image(G: np.ndarray) -> np.ndarray:
 
 
 def lattice_image_at(G: np.ndarray, idx) -> np.ndarray:
-    """The same sum as lattice_image at the voxels idx only (flat indices, x fastest)."""
+    """The same sum as lattice_image at the voxels idx only (flat indices, x
+    fastest): over jx (once per distinct voxel x index), then jy, then jz."""
     nz, ny, nx = G.shape
     idx = np.asarray(idx, np.int64)
     ix, iy, iz = idx % nx, (idx // nx) % ny, idx // (nx * ny)
-    ex = np.exp(2j * math.pi * np.outer(positions(nx)[ix], lattice(nx)))   # [count, nx]
-    ey = np.exp(2j * math.pi * np.outer(positions(ny)[iy], lattice(ny)))
+    ux, inv = np.unique(ix, return_inverse=True)
+    ex = np.exp(2j * math.pi * np.outer(positions(nx)[ux], lattice(nx)))   # [distinct x, nx]
+    ey = np.exp(2j * math.pi * np.outer(positions(ny)[iy], lattice(ny)))   # [count, ny]
     ez = np.exp(2j * math.pi * np.outer(positions(nz)[iz], lattice(nz)))
+    t = (G.reshape(nz * ny, nx) @ ex.T).reshape(nz, ny, ux.size)       # sum over jx
     out = np.empty(idx.size, np.complex128)
-    for t in range(idx.size):
-        out[t] = np.einsum("zyx,x,y,z->", G, ex[t], ey[t], ez[t])
+    for c0 in range(0, idx.size, 256):
+        c = slice(c0, min(c0 + 256, idx.size))
+        u = np.einsum("zyc,cy->zc", t[:, :, inv[c]], ey[c])              # then jy
+        out[c] = np.einsum("zc,cz->c", u, ez[c])                         # then jz
     return out
 
 

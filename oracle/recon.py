@@ -11,6 +11,8 @@ Plain double-precision steps, small grids only (the Toeplitz product is an
 O(N^2) sum):
   toeplitz_apply() -- (F^H F p)[n] = sum_n' Q(x_n - x_n') p[n'] on a unit grid,
                       Q from oracle.q at every coordinate difference
+  normal_direct()  -- F^H F p (+ lam W^H W p) by the definition F^H (F p), one
+                      sample at a time: O(M N), so any grid size for a few samples
   laplacian()      -- (W^H W p)[n] = sum over grid neighbours n' of p[n] - p[n']
   cg()             -- textbook conjugate gradient, fixed iteration count
 Only the tests may use this module; it shares nothing with the HIP library.
@@ -48,6 +50,27 @@ def toeplitz_apply(qd: np.ndarray, p: np.ndarray, nx: int, ny: int, nz: int) -> 
                 sub = qd[z + nz - 1 - np.arange(nz)][:, y + ny - 1 - np.arange(ny)][:, :, x + nx - 1 - np.arange(nx)]
                 out[z, y, x] = np.sum(sub * p)
     return out.ravel()
+
+
+def normal_direct(kx, ky, kz, phi, p: np.ndarray, nx: int, ny: int, nz: int, lam: float = 0.0) -> np.ndarray:
+    """F^H F p + lam W^H W p on the unit grid of grid_coords, from the definition
+    of F (F[m][n] = phi_m exp(-i 2 pi k_m . x_n)): for each sample m in turn,
+    (F p)[m] = phi_m sum_n exp(-i 2 pi k_m . x_n) p[n], then
+    conj(phi_m) exp(+i 2 pi k_m . x_n) (F p)[m] is added at every voxel n.  All
+    in double from the float32 inputs; complex128 [N]."""
+    x, y, z = (a.astype(np.float64) for a in grid_coords(nx, ny, nz))
+    pv = np.asarray(p, np.complex128).ravel()
+    out = np.zeros(pv.size, np.complex128)
+    ph = np.asarray(phi, np.complex64).astype(np.complex128)
+    for m in range(len(kx)):
+        theta = 2.0 * np.pi * (float(kx[m]) * x + float(ky[m]) * y + float(kz[m]) * z)
+        e = np.exp(1j * theta)                    # exp(+i 2 pi k_m . x_n)
+        fp = ph[m] * np.sum(np.conj(e) * pv)      # (F p)[m]
+        out += np.conj(ph[m]) * fp * e
+        del theta, e
+    if lam:
+        out += lam * laplacian(pv, nx, ny, nz)
+    return out
 
 
 def laplacian(p: np.ndarray, nx: int, ny: int, nz: int) -> np.ndarray:

@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (default options: automatic group size and tile).
 
-The oracle evaluates seeded voxel subsets (all voxels for the 32^3 case), the
+The oracle evaluates seeded voxel subsets (all voxels for the 32^3 and 64^3
+cases), the
 phantom round trip compares PSNR of the GPU and oracle images on the three
 central slices, and Q is also checked at its closed forms: Q(0) = sum |phi|^2
 and Hermitian symmetry on the grid.
@@ -18,7 +19,11 @@ from tests.gpu_util import TOL, assert_close, dev_problem, gpu_fhd, gpu_q, requi
 pytestmark = pytest.mark.gpu
 
 TRIGS = ["accurate", "hw"]
-SUBSET = {"fhd_512cube_262144_spirals": 1024, "fhd_64cube_65536_radial": 16384, "fhd_128cube_262144_spirals": 4096, "q_128cube_halfstep_1048576_uniform": 4096, "q_128cube_unitstep_1048576_uniform": 2048, "fhd16_96cube_500001_radial": 2048}
+# oracle voxels per workload (None: every voxel)
+SUBSET = {"fhd_32cube_2048_uniform": None, "fhd_64cube_65536_radial": None, "fhd_512cube_262144_spirals": 1024,
+          "fhd_128cube_262144_spirals": 4096, "fhd_128cube_262144_spirals_jittered": 4096,
+          "q_128cube_halfstep_1048576_uniform": 4096, "q_128cube_unitstep_1048576_uniform": 2048,
+          "fhd16_96cube_500001_radial": 2048}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,7 +37,7 @@ _cache = {}
 def _problem_and_ref(name, oracle_mod):
     if name not in _cache:
         p = inputs.make_config(name)
-        idx = None if name == "fhd_32cube_2048_uniform" else inputs.subset_indices(p.N, SUBSET[name], p.seed)
+        idx = None if SUBSET[name] is None else inputs.subset_indices(p.N, SUBSET[name], p.seed)
         if p.kind == "q":
             ref = oracle_mod.q(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, idx=idx)
         else:
@@ -56,6 +61,31 @@ def test_fhd_config(oracle_mod, name, trig, engine):
     if idx is not None:
         got = got[:, idx]
     assert_close(got, ref, TOL[trig], f"{name} {trig} {engine}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_fhd_per_pair_kernel_full_size(oracle_mod, trig):
+    """The pages' own form of the gather (one voxel per lane, one phase, sine,
+    cosine and complex multiply-accumulate per voxel-sample pair: the VALU
+    engine with one voxel per lane) at 128^3 x 262,144 with its planned
+    launch rows."""
+    name = "fhd_128cube_262144_spirals"
+    p, idx, ref, d = _problem_and_ref(name, oracle_mod)
+    got = gpu_fhd(p, d, trig=trig, engine="valu", voxels_per_lane=1)
+    assert_close(got[:, idx], ref, TOL[trig], f"{name} {trig} per-pair")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("trig", TRIGS)
+def test_fhd_off_grid_full_size(oracle_mod, trig, engine):
+    """2,097,152 voxel centres off the grid (the 128^3 centres displaced by up
+    to a quarter voxel per axis): no voxel group shares common offsets, so
+    every wave takes the direct per-voxel evaluation of its engine."""
+    name = "fhd_128cube_262144_spirals_jittered"
+    p, idx, ref, d = _problem_and_ref(name, oracle_mod)
+    print(f"[gpu] {name} trig={trig} engine={engine}", flush=True)
+    got = gpu_fhd(p, d, trig=trig, engine=engine)
+    assert_close(got[:, idx], ref, TOL[trig], f"{name} {trig} {engine}")
 
 
 @pytest.mark.parametrize("engine", ENGINES)

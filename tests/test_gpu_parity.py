@@ -393,3 +393,66 @@ def test_mfma4_row_block_and_folded_tiles(mfma_grid, trig, splits):
     for tile in (64, 8192):   # 8192 >= every row of the 1001 samples
         assert_close(gpu_fhd(p, d, tile=tile, **base), ref, TOL[trig], f"fhd {trig} rows={splits} tile={tile}")
         assert_close(gpu_q(p, d, tile=tile, **base), qref, TOL[trig], f"q {trig} rows={splits} tile={tile}")
+
+
+def test_kahan_folds_hold_a_coherent_sum(oracle_mod):
+    """Q at x = 0 is the coherent sum sum_m |phi_m|^2 (its closed form).  With
+    2^22 samples summed on one lane (VALU engine, one launch row, tiles of 64
+    samples) a single running fp32 sum drifts far past the 1e-5 bar; blocked
+    summation folds 65,536 tile sums in plain fp32; Kahan-compensated folds
+    keep the total within 1e-6 and below the blocked error.  The other voxels
+    (incoherent sums) are checked against the oracle."""
+    from non_cartesian_mri_amd import q_compute
+    M = 1 << 22
+    rng = np.random.Generator(np.random.PCG64(1000))
+    kx, ky, kz = inputs.uniform_k(M, rng)
+    phi = inputs.complex_normal(rng, M)
+    x = np.array([0.0, 1.0, -3.0, 7.0], np.float32)
+    y = np.array([0.0, 2.0, 1.0, -5.0], np.float32)
+    z = np.array([0.0, -1.0, 5.0, 2.0], np.float32)
+    exact = float(np.sum(np.abs(phi.astype(np.complex128)) ** 2))
+    ref = oracle_mod.q(kx, ky, kz, x, y, z, phi)
+    assert abs(ref[0] - exact) <= 1e-12 * exact
+    t = [torch.from_numpy(a).to("cuda:0") for a in (kx, ky, kz, x, y, z, phi)]
+    err = {}
+    for sum_ in ("plain", "blocked", "kahan"):
+        got = q_compute(*t, trig="accurate", sum=sum_, engine="valu", voxels_per_lane=1,
+                        sample_splits=1, tile=64)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        err[sum_] = abs(complex(got[0]) - exact) / exact
+        print(f"[kahan] Q(0) of 2^22 samples, {sum_}: rel err {err[sum_]:.3e}", flush=True)
+        if sum_ == "kahan":
+            assert_close(got, ref, TOL["accurate"], "Q kahan 2^22 samples")
+    assert err["plain"] > 1e-5
+    assert err["kahan"] < 1e-6
+    assert err["kahan"] < err["blocked"]
+
+
+def test_row_block_sum_of_a_coherent_sum(oracle_mod):
+    """The matrix-core engine's HW path sums a whole launch row as one block
+    (no tile folds); the longest rows the planner makes are the 512^3
+    adjoint's 131,072 samples.  Q(0) = sum |phi|^2 over two such rows on a 32^3
+    grid stays within the accurate path's bar, and the grid matches the
+    oracle within the HW bar."""
+    from non_cartesian_mri_amd import fhd_describe_plan, q_compute
+    M = 262144
+    rng = np.random.Generator(np.random.PCG64(2000))
+    kx, ky, kz = inputs.uniform_k(M, rng)
+    phi = inputs.complex_normal(rng, M)
+    x, y, z = inputs.voxel_grid(32)
+    opts = dict(trig="hw", engine="mfma", voxels_per_lane=128, sample_splits=2)
+    plan = fhd_describe_plan(M, x.size, 1, is_q=True, **opts)
+    assert plan["tile"] == 131072 and plan["sample_splits"] == 2
+    t = [torch.from_numpy(a).to("cuda:0") for a in (kx, ky, kz, x, y, z, phi)]
+    got = q_compute(*t, **opts)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    o = int(np.nonzero((x == 0) & (y == 0) & (z == 0))[0][0])
+    exact = float(np.sum(np.abs(phi.astype(np.complex128)) ** 2))
+    e0 = abs(complex(got[o]) - exact) / exact
+    print(f"[row-block] Q(0), two rows of 131,072 samples: rel err {e0:.3e}", flush=True)
+    assert e0 <= TOL["accurate"]
+    idx = inputs.subset_indices(x.size, 2048, 2001)
+    ref = oracle_mod.q(kx, ky, kz, x, y, z, phi, idx=idx)
+    assert_close(got[idx], ref, TOL["hw"], "Q row-block hw 32^3")

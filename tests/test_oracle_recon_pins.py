@@ -4,6 +4,10 @@
   ----------------  ------------------------------------------------------------
   toeplitz_apply    an explicit dense F^H F built from F[m,n] = phi_m e^{-i2pi k.x};
                     Hermitian; <p, F^H F p> = ||F p||^2 with the pinned forward oracle
+  normal_direct     equals toeplitz_apply (+ lam laplacian) on small grids (the
+                    Q-difference route, in double); equals the compiled adjoint
+                    oracle applied to the compiled forward oracle's F p; one
+                    sample gives a plane wave times the image's projection
   laplacian         constant images -> 0; a single voxel -> degree at the voxel,
                     -1 at each neighbour; symmetric and positive semidefinite;
                     an explicit sparse matrix of the neighbour graph
@@ -132,3 +136,41 @@ def test_cg_first_step_and_orthogonal_residuals():
     for i in range(4):
         for j in range(i):
             assert abs(np.vdot(rs[i], rs[j])) <= 1e-9 * np.linalg.norm(rs[i]) * np.linalg.norm(rs[j]) + 1e-12
+
+
+def test_normal_direct_equals_toeplitz_route(oracle_mod):
+    for seed, M, (nx, ny, nz), lam in ((41, 1, (5, 4, 3), 0.0), (42, 3, (4, 6, 2), 0.0), (43, 50, (3, 4, 5), 0.7)):
+        rng, kx, ky, kz, phi, x, y, z = _problem(seed, M, nx, ny, nz)
+        p = _cn(rng, nx * ny * nz)
+        qd = recon.q_differences(kx, ky, kz, phi, nx, ny, nz)
+        want = recon.toeplitz_apply(qd, p, nx, ny, nz) + lam * recon.laplacian(p, nx, ny, nz)
+        got = recon.normal_direct(kx, ky, kz, phi, p, nx, ny, nz, lam)
+        assert np.max(np.abs(got - want)) <= 1e-11 * np.max(np.abs(want)), (seed, M)
+
+
+def test_normal_direct_equals_forward_then_adjoint(oracle_mod):
+    nx, ny, nz = 6, 5, 4
+    rng, kx, ky, kz, phi, x, y, z = _problem(44, 3, nx, ny, nz)
+    p = _cn(rng, nx * ny * nz)
+    d = oracle_mod.forward(kx, ky, kz, x, y, z, phi, p)[0]
+    # the compiled adjoint takes float32 data: F p rounded once to complex64
+    want = oracle_mod.fhd(kx, ky, kz, x, y, z, phi, d.astype(np.complex64))[0]
+    got = recon.normal_direct(kx, ky, kz, phi, p, nx, ny, nz)
+    assert np.max(np.abs(got - want)) <= 1e-6 * np.max(np.abs(want))
+
+
+def test_normal_direct_one_sample_is_a_plane_wave(oracle_mod):
+    """M = 1: F^H F p = |phi|^2 e^{+i2pi k.x_n} sum_n' e^{-i2pi k.x_n'} p[n'], so
+    every output has the same modulus and neighbouring voxels along x differ
+    by the phase factor e^{i 2 pi kx}."""
+    nx, ny, nz = 8, 3, 2
+    rng, kx, ky, kz, phi, x, y, z = _problem(45, 1, nx, ny, nz)
+    p = _cn(rng, nx * ny * nz)
+    got = recon.normal_direct(kx, ky, kz, phi, p, nx, ny, nz).reshape(nz, ny, nx)
+    mod = np.abs(got)
+    assert np.max(np.abs(mod - mod.flat[0])) <= 1e-12 * mod.flat[0]
+    ratio = got[:, :, 1:] / got[:, :, :-1]
+    assert np.max(np.abs(ratio - np.exp(2j * np.pi * float(kx[0])))) <= 1e-12
+    # |F^H F p| = |phi|^2 |(F p) / phi|
+    d = oracle_mod.forward(kx, ky, kz, x, y, z, phi, p)[0, 0]
+    assert abs(mod.flat[0] - abs(complex(phi[0])) * abs(d)) <= 1e-12 * mod.flat[0]
