@@ -172,6 +172,35 @@ fhd_status fhd_compute(const float* kx, const float* ky, const float* kz,
                        const fhd_opts* opts, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): F^H D as
+ * fhd_compute, with the workspace taken from a fixed device array inside the
+ * library instead of the caller or the stream-ordered allocator.  The array
+ * holds FHD_NOALLOC_SCRATCH_BYTES (512 MiB); every GPU the library's code is
+ * loaded on holds its own copy until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipMallocAsync or hipFree).
+ *   Arguments, layouts, semantics and errors are those of fhd_compute, plus:
+ *   - opts->workspace must be NULL and opts->stages FHD_STAGE_ALL (or 0),
+ *     else FHD_ERR_INVALID_ARGUMENT;
+ *   - with sample_splits = 0 the planned row count is lowered until the
+ *     plan's workspace fits the array (the same sums in another order);
+ *     a plan that still needs more than FHD_NOALLOC_SCRATCH_BYTES returns
+ *     FHD_ERR_WORKSPACE before anything is enqueued (fhd_workspace_bytes
+ *     gives a plan's need).
+ *   Every call on one GPU shares that GPU's array and leaves the last call's
+ *   contents in it: calls that overlap on one GPU (other host threads, or
+ *   other streams before the earlier call's work has finished) race and give
+ *   undefined results.  Calls ordered on one stream are safe.
+ */
+#define FHD_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
+
+fhd_status fhd_compute_noalloc(const float* kx, const float* ky, const float* kz,
+                               const float* x, const float* y, const float* z,
+                               const fhd_c32* phi, const fhd_c32* D, fhd_c32* FhD,
+                               int64_t M, int64_t N, int32_t batch,
+                               const fhd_opts* opts, void* stream);
+
+/*
  * Q for one trajectory: as fhd_compute with the real weight |phi[m]|^2 in place
  * of conj(phi[m]) D[m].   Q : fhd_c32[N] output, overwritten.
  */

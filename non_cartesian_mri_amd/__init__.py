@@ -2,6 +2,7 @@
 
 Public entry points (thin wrappers over the C ABI in include/fhd.h):
   fhd_compute(kx, ky, kz, x, y, z, phi, D, ...) -> complex64 [N] or [B, N]
+  fhd_compute_noalloc(...)                      -> as fhd_compute, workspace in the library's fixed array
   q_compute(kx, ky, kz, x, y, z, phi, ...)      -> complex64 [N]
   fhd_forward(kx, ky, kz, x, y, z, phi, rho, ...) -> complex64 [M] or [B, M]
   fhd_workspace_bytes(M, N, batch, is_q, ..., op=...), fhd_describe_plan(...)
@@ -16,7 +17,7 @@ generators (trajectories, voxel grids, phantom).
 """
 from . import inputs  # noqa: F401
 
-__all__ = ["fhd_compute", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan",
+__all__ = ["fhd_compute", "fhd_compute_noalloc", "q_compute", "fhd_forward", "fhd_workspace_bytes", "fhd_describe_plan",
            "fhd_toeplitz_kernel", "fhd_normal_apply", "fhd_cg_solve", "fhd_toeplitz_bytes",
            "fhd_cg_workspace_bytes", "fhd_gridding", "inputs", "library_path"]
 

@@ -38,8 +38,11 @@ FHD_STAGE_GATHER = 2
 FHD_STAGE_REDUCE = 4
 FHD_STAGE_ALL = 7
 
+# size of the device array behind fhd_compute_noalloc (FHD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 512 << 20
+
 # every symbol the header declares
-EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "q_compute",
+EXPORTED = ("fhd_default_opts", "fhd_workspace_bytes", "fhd_compute", "fhd_compute_noalloc", "q_compute",
             "fhd_forward", "fhd_toeplitz_bytes", "fhd_toeplitz_kernel", "fhd_cg_workspace_bytes",
             "fhd_normal_apply", "fhd_cg_solve", "fhd_gridding", "fhd_describe_plan", "fhd_status_string",
             "fhd_last_error", "fhd_version")
@@ -102,6 +105,8 @@ def load() -> ctypes.CDLL:
     lib.fhd_workspace_bytes.restype = sz
     lib.fhd_compute.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, ctypes.POINTER(FhdOpts), P]
     lib.fhd_compute.restype = ctypes.c_int
+    lib.fhd_compute_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, ctypes.POINTER(FhdOpts), P]
+    lib.fhd_compute_noalloc.restype = ctypes.c_int
     lib.q_compute.argtypes = [P, P, P, P, P, P, P, P, i64, i64, ctypes.POINTER(FhdOpts), P]
     lib.q_compute.restype = ctypes.c_int
     lib.fhd_forward.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, ctypes.POINTER(FhdOpts), P]

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #define NCMRI_API extern "C" __attribute__((visibility("default")))
 
@@ -536,9 +537,38 @@ fhd_status run_forward(const float* kx, const float* ky, const float* kz, const 
   return result;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free F^H D: the workspace is a fixed device array of the library
+// (one copy per GPU, held until the process ends).  In host code the array's
+// name is only a registration handle; its device address is taken once per
+// device with hipGetSymbolAddress and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = FHD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fhd_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FHD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FHD_ERR_UNSUPPORTED_DEVICE, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FHD_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FHD_OK;
+}
+
 fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, const float* x,
                const float* y, const float* z, const fhd_c32* phi, const fhd_c32* D, fhd_c32* out,
-               int64_t M, int64_t N, int32_t batch, const fhd_opts* opts, void* stream) {
+               int64_t M, int64_t N, int32_t batch, const fhd_opts* opts, void* stream,
+               bool lib_scratch = false) {
   g_err[0] = '\0';
   Plan p;
   fhd_status st = make_plan(p, is_q, M, N, batch, opts);
@@ -579,7 +609,10 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
 
   hipStream_t s = (hipStream_t)stream;
   bool own = false;
-  if (!ws && p.ws_bytes > 0) {
+  if (lib_scratch) {  // the allocation-free entry point: the library's fixed array
+    st = scratch_for_current_device(&ws);
+    if (st != FHD_OK) return st;
+  } else if (!ws && p.ws_bytes > 0) {
     hipError_t e = hipMallocAsync(&ws, p.ws_bytes, s);
     if (e != hipSuccess) return fail(FHD_ERR_HIP, "hipMallocAsync(%zu): %s", p.ws_bytes, hipGetErrorString(e));
     own = true;
@@ -646,6 +679,38 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   return result;
 }
 
+fhd_status run_noalloc(const float* kx, const float* ky, const float* kz, const float* x,
+                       const float* y, const float* z, const fhd_c32* phi, const fhd_c32* D,
+                       fhd_c32* out, int64_t M, int64_t N, int32_t batch, const fhd_opts* opts,
+                       void* stream) {
+  g_err[0] = '\0';
+  fhd_opts o;
+  if (opts) o = *opts;
+  else fhd_default_opts(&o);
+  if (o.workspace || o.workspace_bytes)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "fhd_compute_noalloc uses the library's scratch; opts.workspace must be NULL");
+  if (o.stages != 0 && o.stages != FHD_STAGE_ALL)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "fhd_compute_noalloc runs all stages in one call");
+  Plan p;
+  fhd_status st = make_plan(p, 0, M, N, batch, &o);
+  if (st != FHD_OK) return st;
+  // an automatic row count is lowered until the rows' partial sums fit beside
+  // the records (fewer rows: the same sums in a different order)
+  if (o.sample_splits == 0 && p.ws_bytes > kNoAllocScratchBytes) {
+    for (int32_t s = p.splits - 1; s >= 1 && p.ws_bytes > kNoAllocScratchBytes; --s) {
+      o.sample_splits = s;
+      st = make_plan(p, 0, M, N, batch, &o);
+      if (st != FHD_OK) return st;
+    }
+  }
+  if (p.ws_bytes > kNoAllocScratchBytes)
+    return fail(FHD_ERR_WORKSPACE,
+                "this plan needs %zu bytes of workspace; fhd_compute_noalloc holds at most %zu "
+                "(fewer sample_splits, a smaller group or fewer samples per call fit in less)",
+                p.ws_bytes, kNoAllocScratchBytes);
+  return run(0, kx, ky, kz, x, y, z, phi, D, out, M, N, batch, &o, stream, true);
+}
+
 }  // namespace
 
 NCMRI_API void fhd_default_opts(fhd_opts* o) {
@@ -699,6 +764,18 @@ NCMRI_API fhd_status fhd_compute(const float* kx, const float* ky, const float* 
                                  int32_t batch, const fhd_opts* opts, void* stream) {
   try {
     return run(0, kx, ky, kz, x, y, z, phi, D, FhD, M, N, batch, opts, stream);
+  } catch (...) {
+    return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
+  }
+}
+
+NCMRI_API fhd_status fhd_compute_noalloc(const float* kx, const float* ky, const float* kz,
+                                         const float* x, const float* y, const float* z,
+                                         const fhd_c32* phi, const fhd_c32* D, fhd_c32* FhD,
+                                         int64_t M, int64_t N, int32_t batch, const fhd_opts* opts,
+                                         void* stream) {
+  try {
+    return run_noalloc(kx, ky, kz, x, y, z, phi, D, FhD, M, N, batch, opts, stream);
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");
   }

@@ -2,7 +2,8 @@
 
 torch provides device memory and the stream; every step of the computation
 runs in the HIP kernels behind the C ABI (include/fhd.h).  Names match the C
-entry points: fhd_compute, q_compute, fhd_forward, fhd_workspace_bytes, and the
+entry points: fhd_compute, fhd_compute_noalloc, q_compute, fhd_forward,
+fhd_workspace_bytes, and the
 reconstruction calls fhd_toeplitz_kernel, fhd_normal_apply, fhd_cg_solve.
 """
 from __future__ import annotations
@@ -122,6 +123,39 @@ def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
     st = _lib.load().fhd_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                  y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
                                  out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
+    _lib.check(st)
+    return out.reshape(N) if squeeze else out.reshape(B, N)
+
+
+def fhd_compute_noalloc(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
+                        voxels_per_lane=0, tile=0, out=None, stream=None, sample_splits=0,
+                        engine="auto") -> torch.Tensor:
+    """F^H D through the allocation-free entry point: the library's fixed device
+    array is the workspace (no device allocation by the library).  Same
+    arguments as fhd_compute without workspace and stages; pass `out` to keep
+    the call itself free of allocations."""
+    for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
+        _dev_f32(t, n)
+    _dev_c64(phi, "phi")
+    _dev_c64(D, "D")
+    M, N = kx.numel(), x.numel()
+    if not (ky.numel() == kz.numel() == phi.numel() == M) or not (y.numel() == z.numel() == N):
+        raise ValueError("inconsistent sizes")
+    squeeze = D.dim() == 1
+    D2 = D.reshape(1, -1) if squeeze else D
+    if D2.dim() != 2 or D2.shape[1] != M:
+        raise ValueError("D must be [M] or [B, M]")
+    B = D2.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.complex64, device=x.device)
+    else:
+        _dev_c64(out, "out")
+        if out.numel() != B * N:
+            raise ValueError("out must hold B*N complex values")
+    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine)
+    st = _lib.load().fhd_compute_noalloc(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
+                                         y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
+                                         out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
     _lib.check(st)
     return out.reshape(N) if squeeze else out.reshape(B, N)
 

@@ -23,6 +23,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines
     names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text)
     return sorted(set(n for n in names if n not in ("sizeof",)))
 
@@ -34,6 +35,12 @@ def test_header_declarations_match_binding():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FHD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_opts_struct_layout(lib):
@@ -144,6 +151,37 @@ def test_workspace_errors(lib):
     # workspace overlapping an input or the output
     assert _fhd(lib, opts=_opts(workspace=A + 0x6000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert _fhd(lib, opts=_opts(workspace=A + 0x100000, workspace_bytes=need)) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def _noalloc(lib, M=16, N=8, batch=1, opts=None, **ptrs):
+    p = dict(kx=A, ky=A + 0x1000, kz=A + 0x2000, x=A + 0x3000, y=A + 0x4000, z=A + 0x5000,
+             phi=A + 0x6000, D=A + 0x8000, out=A + 0x100000)
+    p.update(ptrs)
+    return lib.fhd_compute_noalloc(p["kx"], p["ky"], p["kz"], p["x"], p["y"], p["z"], p["phi"], p["D"],
+                                   p["out"], M, N, batch, None if opts is None else ctypes.byref(opts), None)
+
+
+def test_noalloc_argument_errors(lib):
+    """fhd_compute_noalloc checks its arguments as fhd_compute does, refuses a
+    caller workspace or a partial stage mask, and refuses a plan larger than
+    its fixed array -- all before any device call."""
+    E = _lib.FHD_ERR_INVALID_ARGUMENT
+    assert _noalloc(lib, M=-1) == E
+    assert _noalloc(lib, kx=None) == E
+    assert _noalloc(lib, out=A + 0x3000) == E
+    assert _noalloc(lib, opts=_opts(trig=7)) == E
+    assert _noalloc(lib, opts=_opts(workspace=A + 0x200000, workspace_bytes=1 << 20)) == E
+    assert b"workspace must be NULL" in lib.fhd_last_error()
+    assert _noalloc(lib, opts=_opts(stages=_lib.FHD_STAGE_MU)) == E
+    assert b"all stages" in lib.fhd_last_error()
+    # 2^22 samples on the four-sample engine: 6.4 GB of factor records even with one row
+    big = dict(M=1 << 22, N=1 << 21, D=A + 0x40000000, out=A + 0x80000000,
+               x=A + 0x10000000, y=A + 0x18000000, z=A + 0x20000000, phi=A + 0x30000000)
+    assert _noalloc(lib, **big) == _lib.FHD_ERR_WORKSPACE
+    assert b"at most 536870912" in lib.fhd_last_error()
+    assert _noalloc(lib, opts=_opts(sample_splits=1, engine=_lib.FHD_ENGINE_MFMA), **big) == _lib.FHD_ERR_WORKSPACE
+    # N == 0 is a no-op before any device call, as for fhd_compute
+    assert _noalloc(lib, N=0, x=None, y=None, z=None, out=None) == _lib.FHD_OK
 
 
 def test_empty_voxel_set_is_a_noop(lib):
