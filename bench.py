@@ -5,11 +5,21 @@ One step = one pass of the whole hot path (per-sample Mu/record kernel, gather
 kernel, reduction of the sample-split rows) over the 128^3 stack-of-spirals
 workload, inputs resident in HBM.  Prints one JSON line.  The gather stage (the
 dominant kernel) is also timed on its own with HIP events on the stream it is
-launched on.  Its roofline: for the matrix-core engine, the three real
-multiply-accumulates (6 FLOP) per voxel-sample pair of the three-multiplication
-complex product against the MI355X FP32 matrix peak; for the VALU engine, the
-direct formulation's 14 FLOP per pair against the FP32 vector peak.  The CPU oracle is timed on a bounded voxel
-sample of the same workload (rank 0, one GPU only).
+launched on.
+
+Roofline (the method's work, as the FP32/transcendental roofline counts it):
+per voxel-sample pair the pages' kernel computes a phase (1 mul + 2 FMA), its
+reduction, a sine and a cosine, and a complex multiply-accumulate (4 FMA): 14
+FLOP and 2 transcendentals (PMPP ch. 17, section 17.3: about 13 FP operations
+per 2 trig).  `roofline.achieved` is that work over the gather's time against
+the MI355X FP32 peak; `roofline.method_roofline` gives the pairs/s roofline
+min(R_trans / 2, FP32 peak / 14) with the transcendental rate measured on the
+GPU, and the fraction of it reached; `roofline.engine` gives what the timed
+kernel itself executes against its own pipe.  The default matrix-core engine
+factors the phase over voxel groups on a grid and executes far less than the
+per-pair work, so the method fractions exceed 1; the per-pair kernel (one voxel
+per lane on the vector ALU) is timed in the same run (`method`).  The CPU
+oracle is timed on a bounded voxel sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,14 +34,44 @@ import numpy as np
 METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roofline"
 FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 peak (vector, and dense matrix)
 HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
-# Direct formulation per voxel-sample pair: phase 5 + reduction 1 + complex MAC 8
-# (Q: real MAC 4), plus two transcendentals.
-FLOP_PER_PAIR = {"fhd": 14, "q": 10}
-# Factored formulation on the matrix cores (F^H D, Q and the forward
-# operator): the complex product of the group phases with the factor columns
-# in the three-multiplication form, 3 real MACs = 6 FLOP per pair (a group
-# phase with its sine and cosine is shared by 32 voxel columns).
+# The method's work per voxel-sample pair: phase 5 + reduction 1 + complex
+# MAC 8 (Q: real weight, MAC 4), plus two transcendentals; with B data vectors
+# sharing one phase, 6 + 8 B per (voxel, sample).
+FLOP_PER_PAIR = {"fhd": 14, "q": 10, "forward": 14}
+TRANS_PER_PAIR = 2
+# Measured on one MI355X by `python bench.py --issue-rates`
+# (profiles/issue_rates_gfx950.md): MB-TRANS v_sin_f32 throughput of the whole
+# GPU, and MB-PAIR, the pages' per-pair loop body (phase, fract, v_sin, v_cos,
+# four-FMA MAC) with no memory traffic at full occupancy: the issue ceiling of
+# the per-pair form on this chip (transcendentals share the VALU issue port).
+R_TRANS_PER_S = 17.528e12
+PAIR_ISSUE_CEILING = 3.307e12
+# What the matrix-core kernels execute: the three real multiply-accumulates
+# (6 FLOP) per pair of the three-multiplication complex product on the FP32
+# matrix pipe; a group phase with its sine and cosine serves 128 voxel columns.
 MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
+# Matrix-pipe busy share of the gather from SQ_VALU_MFMA_BUSY_CYCLES (valid for
+# the kernel source it was taken on, like TRAFFIC below)
+MFMA_BUSY = {
+    ("fhd_128cube_262144_spirals", "hw", 128): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9", "busy": 0.923,
+        "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
+    ("fhd_128cube_262144_spirals", "accurate", 128): {
+        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9", "busy": 0.856,
+        "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
+}
+
+
+def method_roofline(kind: str, B: int) -> dict:
+    """Pairs/s roofline of the per-pair method: min(R_trans / n_trans,
+    FP32 peak / n_flop) per (voxel, sample), times B vectors."""
+    flop_vs = (6 + 8 * B) if kind != "q" else 10   # per (voxel, sample)
+    p_trans = R_TRANS_PER_S / TRANS_PER_PAIR
+    p_flop = FP32_PEAK_TFLOPS * 1e12 / flop_vs
+    return {"p_roof_pairs_per_s": B * min(p_trans, p_flop), "bound": "trans" if p_trans <= p_flop else "fp32",
+            "r_trans_per_s": R_TRANS_PER_S, "flop_per_voxel_sample": flop_vs, "trans_per_voxel_sample": TRANS_PER_PAIR}
+
+
 # HBM bytes of the gather kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # scaled by a 1 GiB copy (FETCH_SIZE reads half the bytes, WRITE_SIZE all).
 # Valid only for the kernel source (with the headers it includes) they were
@@ -71,6 +111,8 @@ TRAFFIC = {
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
     "fhd_64cube_65536_radial": "FhD 64^3 voxels x 65,536 radial samples",
+    "fhd_128cube_262144_spirals_jittered": "FhD at 2,097,152 off-grid points (128^3 centres displaced by up to a "
+                                           "quarter voxel per axis) x the 262,144 stack-of-spirals samples",
     "fhd_512cube_262144_spirals": "FhD 512^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
     "q_128cube_halfstep_1048576_uniform": "Q on 128^3 voxels (step 0.5) x 1,048,576 uniform samples",
     "fhd16_96cube_500001_radial": "FhD x16 vectors, 96^3 voxels x 500,001 radial samples",
@@ -97,6 +139,8 @@ def parse():
                     help="regulariser weight relative to sum |phi|^2 / 6 (--op cg)")
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--method-steps", type=int, default=3,
+                    help="gather launches of the per-pair kernel timed beside the benchmark (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -403,6 +447,50 @@ def oracle_threads_hint() -> int:
         return os.cpu_count() or 1
 
 
+def time_per_pair_kernel(p, t, D, args, stream, mr) -> dict:
+    """The pages' per-pair gather (VALU engine, one voxel per lane) on the same
+    workload and trig path: its gather stage timed alone with HIP events on the
+    stream it runs on (records built once beforehand)."""
+    import torch
+    from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes, q_compute
+    is_q = p.kind == "q"
+    opts = dict(trig=args.trig, sum="blocked", engine="valu", voxels_per_lane=1)
+    ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, is_q=is_q, **opts)), dtype=torch.uint8,
+                     device=t["kx"].device)
+    out = torch.empty((p.B, p.N), dtype=torch.complex64, device=t["kx"].device)
+
+    def stage(which):
+        if is_q:
+            q_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], stages=which, workspace=ws,
+                      out=out.view(-1), **opts)
+        else:
+            fhd_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], D, stages=which,
+                        workspace=ws, out=out, **opts)
+
+    stage("mu")
+    stage("gather")
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.method_steps)]
+    for a, b in ev:
+        a.record(stream)
+        stage("gather")
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pairs = p.N * p.M * p.B
+    rate = pairs / (ms * 1e-3)
+    tflops = mr["flop_per_voxel_sample"] * p.N * p.M / (ms * 1e-3) / 1e12
+    return {"kernel": "gather_kernel with one voxel per lane (VALU engine, voxels_per_lane=1): the pages' "
+                      "per-pair form, one phase, fract, sin, cos and complex MAC per voxel-sample pair",
+            "gather_event_mean_ms": round(ms, 3), "launches_timed": args.method_steps,
+            "value": round(rate / 1e9, 3), "unit": "Gpair/s",
+            "achieved": round(tflops, 3), "peak": FP32_PEAK_TFLOPS, "achieved_unit": "TFLOP/s",
+            "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+            "frac_method": round(rate / mr["p_roof_pairs_per_s"], 4),
+            "issue_ceiling_pairs_per_s": PAIR_ISSUE_CEILING,
+            "frac_issue": None if not PAIR_ISSUE_CEILING else round(rate / PAIR_ISSUE_CEILING, 4)}
+
+
 def main():
     args = parse()
     if args.issue_rates:
@@ -497,27 +585,55 @@ def main():
     pairs = p.N * p.M * p.B
     value = pairs / (ms_per_step * 1e-3) / 1e9
     g_avg = float(gather_ms.mean())
-    direct_tflops = FLOP_PER_PAIR[p.kind] * pairs / (g_avg * 1e-3) / 1e12
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
     plan = fhd_describe_plan(p.M, p.N, p.B, op=op, **opts)
     engine = {1: "valu", 2: "mfma"}[plan["engine"]]
-    if forward:
-        per_pair = MFMA_FLOP_PER_PAIR["forward"]
-        achieved, bound = per_pair * pairs / (g_avg * 1e-3) / 1e12, "mfma"
-        kernel = ("fwd_gather_kernel: its launch rows in one step, timed alone; the image packing, "
-                  "row reduction and (on a grid, empty) direct kernels are outside the interval")
-    elif engine == "mfma":
-        per_pair = MFMA_FLOP_PER_PAIR["gather"]
-        achieved, bound = per_pair * pairs / (g_avg * 1e-3) / 1e12, "mfma"
-        kernel = ("mfma_gather_kernel: its launch rows in one step, timed alone with the (empty on a "
-                  "grid) mfma_direct_kernel; records and reduction kernels are outside the interval")
+    kind = "forward" if forward else p.kind
+    # the method's work: per (voxel, sample) one phase, reduction and sin/cos,
+    # and per vector a complex MAC (14 FLOP + 2 transcendentals for one vector,
+    # PMPP ch. 17 section 17.3's count of ~13 FP operations per 2 trig)
+    mr = method_roofline(kind, p.B)
+    method_flop = mr["flop_per_voxel_sample"] * p.N * p.M
+    achieved = method_flop / (g_avg * 1e-3) / 1e12
+    gather_rate = pairs / (g_avg * 1e-3)
+    mr["frac"] = round(gather_rate / mr["p_roof_pairs_per_s"], 4)
+    mr["per_pair_issue_ceiling_pairs_per_s"] = PAIR_ISSUE_CEILING
+    if forward or engine == "mfma":
+        ex = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"] * pairs / (g_avg * 1e-3) / 1e12
+        busy = MFMA_BUSY.get((args.config, args.trig, plan["voxels_per_lane"])) if not forward else None
+        if busy is not None and busy["kernel_sha256"] != kernel_source_sha(busy["source"]):
+            busy = None
+        bound = "mfma"
+        eng = {"engine": "mfma", "bound": "mfma", "executed_flop_per_pair": 6, "achieved": round(ex, 3),
+               "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ex / FP32_PEAK_TFLOPS, 4),
+               "matrix_busy_counter": None if busy is None else busy["busy"],
+               "matrix_busy_profile": None if busy is None else busy["profile"],
+               "note": "grid-separable factorisation: voxels in groups of %d on a common grid share one phase, "
+                       "sine and cosine per sample; the rest is an FP32 matrix product of the group phases with "
+                       "per-sample factor columns (3 real MACs per pair), so the kernel executes %.3g of the "
+                       "method's transcendentals and the method fractions exceed 1"
+                       % (plan["voxels_per_lane"], 1.0 / max(plan["voxels_per_lane"], 1))}
+        if forward:
+            kernel = ("fwd_gather_kernel: its launch rows in one step, timed alone; the image packing, "
+                      "row reduction and (on a grid, empty) direct kernels are outside the interval")
+        else:
+            kernel = ("mfma_gather_kernel: its launch rows in one step, timed alone with the (empty on a "
+                      "grid) mfma_direct_kernel; records and reduction kernels are outside the interval")
     else:
-        achieved, bound = direct_tflops, "alu"
+        bound = "alu"
+        V = plan["voxels_per_lane"]
+        eng = {"engine": "valu", "bound": "alu", "voxels_per_lane": V,
+               "note": "one voxel per lane: the per-pair form (phase, fract, sin, cos, MAC per pair)" if V == 1 else
+                       "%d voxels per lane share one phase, sine and cosine per sample (their offsets are folded "
+                       "into per-sample factors); 3 FMAs per pair plus the shared work / %d" % (V, V)}
         kernel = ("gather_kernel: its launches in one step, timed alone; the per-sample and reduce "
                   "kernels are outside this interval")
-        per_pair = FLOP_PER_PAIR[p.kind]
     traffic, traffic_detail = traffic_for(args.config + ("/forward" if forward else ""), args.trig,
                                           args.sum, engine, plan["voxels_per_lane"], g_avg)
+    summ = args.sum
+    if engine == "mfma" and plan["tile"] >= (plan["padded_samples"] + plan["sample_splits"] - 1) // plan["sample_splits"] \
+            and args.sum == "blocked" and not forward:
+        summ = "row-block"   # each launch row summed as one block, rows added in a fixed order
     res = {
         "metric": METRIC if not forward else METRIC.replace("FhD", "Forward-operator F rho"),
         "value": round(value, 3),
@@ -534,7 +650,7 @@ def main():
         "config": {"workload": WORKLOADS[args.config] + ("; forward operator F rho of a seeded "
                                                           "complex N(0,1) image" if forward else ""),
                    "op": op, "name": args.config, "voxels": p.N,
-                   "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": args.sum,
+                   "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": summ,
                    "engine": engine, "group_voxels": plan["voxels_per_lane"], "tile": plan["tile"],
                    "sample_splits": plan["sample_splits"], "gather_launches": plan["passes"],
                    "parallelism": "single GPU, data-parallel over voxels"},
@@ -548,9 +664,13 @@ def main():
                      "traffic": None if traffic is None else round(traffic, 3),
                      "traffic_unit": "GB/s (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE / launch time)",
                      "traffic_detail": traffic_detail,
-                     "kernel": kernel, "flop_per_pair": per_pair,
-                     "direct_formulation_tflops": round(direct_tflops, 3)},
+                     "kernel": kernel,
+                     "flop_per_pair": round(mr["flop_per_voxel_sample"] / p.B, 4),
+                     "achieved_is": "the method's FLOP per launch (flop_per_pair x pairs) / gather time",
+                     "method_roofline": mr, "engine": eng},
     }
+    if not forward and not (engine == "valu" and plan["voxels_per_lane"] == 1) and args.method_steps > 0:
+        res["method"] = time_per_pair_kernel(p, t, D, args, stream, mr)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, rho.cpu().numpy() if forward else None)
     print(json.dumps(res), flush=True)

@@ -81,7 +81,11 @@ typedef enum fhd_trig {
 
 /* How the fp32 accumulators sum over the samples. */
 typedef enum fhd_sum {
-  FHD_SUM_BLOCKED = 0, /* per-tile partial sums folded into running totals */
+  FHD_SUM_BLOCKED = 0, /* per-tile partial sums folded into running totals; with
+                          tile = 0 the matrix-core four-sample engine on the HW
+                          trig path makes each launch row one tile ("row-block":
+                          the row's sums stay in the MFMA accumulators, rows are
+                          added in a fixed order afterwards) */
   FHD_SUM_KAHAN = 1,   /* as BLOCKED, with Kahan-compensated folding of the tiles */
   FHD_SUM_PLAIN = 2    /* one running fp32 sum over all samples */
 } fhd_sum;
@@ -93,10 +97,15 @@ typedef enum fhd_engine {
   FHD_ENGINE_VALU = 1, /* vector-ALU kernels: a lane owns voxels_per_lane voxels, three-FMA
                           complex multiply-accumulate per voxel and sample */
   FHD_ENGINE_MFMA = 2  /* matrix-core kernels: groups of consecutive voxels share one
-                          phase per sample; the per-sample sum is a 32x2 by 2x32
-                          v_mfma_f32_32x32x2_f32 product per factor tile (blocked or
-                          plain summation only).  Groups that do not tile the grid rows
-                          (x fastest) fall back to a direct evaluation, correct but slow */
+                          phase per sample and the sum over samples is a complex matrix
+                          product (group phases x per-sample factor columns) in three
+                          real products: v_mfma_f32_16x16x4_f32 over blocks of four
+                          samples for groups of 128 voxels (the default on cubic grids),
+                          v_mfma_f32_32x32x2_f32 over pairs of samples for groups of 32
+                          or 64 (blocked or plain summation only).  Waves whose groups do
+                          not sit at common offsets (any non-grid coordinates) are
+                          evaluated per voxel on the vector ALU over the same launch
+                          rows, at about the rate of the VALU engine's per-voxel path */
 } fhd_engine;
 
 /* Operation codes of fhd_workspace_bytes and fhd_describe_plan. */
@@ -127,7 +136,9 @@ typedef struct fhd_opts {
                               of 16 complex columns; batched passes keep T, groups of
                               16 T / vectors; 128 runs the four-sample engine).
                               With FHD_ENGINE_AUTO, 1-16 select VALU and 32-128 MFMA */
-  int32_t tile;            /* samples per summation tile; 0 = automatic (~sqrt(M)) */
+  int32_t tile;            /* samples per summation tile; 0 = automatic: ~sqrt(M) (VALU,
+                              accurate trig), ~4 sqrt(M) on the matrix cores with HW trig,
+                              the whole launch row on the four-sample engine with HW trig */
   int32_t stages;          /* FHD_STAGE_* mask; 0 means FHD_STAGE_ALL.  Stages run in
                               separate calls must use the same sizes, options and
                               workspace, in the order MU, GATHER, REDUCE */

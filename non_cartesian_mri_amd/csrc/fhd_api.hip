@@ -74,6 +74,7 @@ struct Plan {
   int bc[40];          // vectors per pass (<= 31 + 4 for batch <= 512)
   size_t pass_bytes[40];
   size_t hdr_bytes;    // MFMA: header part of each pass's records (256-aligned)
+  size_t flag_bytes;   // MFMA: per-wave regularity flags shared by the passes
   int64_t gpad[40];    // forward: padded group count of each pass
   int64_t g_split[40]; // forward: groups per launch row of each pass
   size_t ws_bytes;
@@ -171,6 +172,9 @@ int auto_mfma_tiles(int64_t N, const int* bc, int npass, int tmax, int64_t mpad,
 // the rows' partial sums.
 constexpr int64_t kSplitSamples = 16384;
 constexpr int64_t kMaxPartialBytes = 2LL << 30;
+// Forward operator, HW path: largest row (in bytes of packed voxel groups)
+// summed as one block by the kernel without running totals.
+constexpr int64_t kRowBlockBytes = 256LL << 20;
 
 int32_t auto_splits(int64_t waves, int64_t quantum, int64_t N, int BC, int64_t mpad) {
   if (waves <= 0 || mpad <= 0) return 1;
@@ -307,6 +311,18 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   // one partial-sum buffer, reused by every pass (passes run in stream order)
   p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
   p.ws_bytes += align256(p.partial_bytes);
+  // the matrix-core gather's per-wave regularity flags (the first pass has
+  // the most waves: the most vectors per pass, the largest groups)
+  p.flag_bytes = 0;
+  if (mfma && p.npass > 0) {
+    int64_t w = 0;
+    for (int i = 0; i < p.npass; ++i) {
+      const int64_t wi = ncmri::mfma_gather_waves(N, p.tiles, p.bc[i]);
+      w = wi > w ? wi : w;
+    }
+    p.flag_bytes = (size_t)w * sizeof(int32_t);
+  }
+  p.ws_bytes += align256(p.flag_bytes);
   return FHD_OK;
 }
 
@@ -399,13 +415,15 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   }
   // the four-group engine's HW path sums each launch row as one block: no
   // tile folds, so its kernel keeps no running totals (3 waves per SIMD).
-  // Only for rows of at most 65,536 groups (128^3: 16,384): at 512^3 (rows
-  // of 1,048,576 groups, 1.6 GB of packed groups per wave's stream) the
+  // Every wave streams its row's packed groups, so this is kept to rows of at
+  // most kRowBlockBytes of packed groups: measured, 128^3 (25 MB per row) and
+  // the 16-image 96^3 pass (170 MB) gain from it, while at 512^3 (1.6 GB) the
   // three resident workgroups per CU were 1.2 % slower than two with tiles.
   if (p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN) {
     int64_t gs = 0;
     for (int i = 0; i < p.npass; ++i) gs = p.g_split[i] > gs ? p.g_split[i] : gs;
-    if (gs <= 65536 && gs > p.tile) p.tile = gs;
+    const int64_t row_bytes = gs * ncmri::mfma_factor_floats(p.tiles) * (int64_t)sizeof(float);
+    if (row_bytes <= kRowBlockBytes && gs > p.tile) p.tile = gs;
   }
   p.m_split = 0;
   p.hdr_bytes = 0;
@@ -620,10 +638,12 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   fhd_status result = FHD_OK;
   char* base = (char*)ws;
   float2* partial = nullptr;
-  if (p.partial_bytes > 0) {
+  int32_t* flags = nullptr;
+  {
     size_t recs = 0;
     for (int i = 0; i < p.npass; ++i) recs += align256(p.pass_bytes[i]);
-    partial = (float2*)(base + recs);
+    if (p.partial_bytes > 0) partial = (float2*)(base + recs);
+    if (p.flag_bytes > 0) flags = (int32_t*)(base + recs + align256(p.partial_bytes));
   }
   int b0 = 0;
   const bool kahan = p.sum == FHD_SUM_KAHAN;
@@ -647,7 +667,7 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
       if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
         what = "gather";
         ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
-                           p.splits > 1 ? partial : nullptr};
+                           p.splits > 1 ? partial : nullptr, flags};
         e = ncmri::launch_mfma_gather(p.trig, p.tiles, bc, p.splits, ma, s);
       }
     } else {

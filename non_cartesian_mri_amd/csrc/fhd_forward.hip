@@ -449,6 +449,7 @@ struct FwdGather4 {
   // 4 + h (the three products' entries for t in [4h, 4h + 4)).
   __device__ static __forceinline__ void load_half(const float* __restrict__ wb, int q, int lane, int h,
                                                    float (&bv)[3 * T]) {
+    static_assert(T == 8, "half-block slices 2 p + h of four units each: the layout of T = 8");
     const float* pp = wb + q * QF;
 #pragma unroll
     for (int p = 0; p < 3; ++p) {

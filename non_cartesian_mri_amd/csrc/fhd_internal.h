@@ -129,6 +129,9 @@ struct MfmaArgs {
   float2* out;           // first output vector of this pass ([BC][N])
   int64_t m_split;       // samples per launch row (multiple of kMfmaChunk)
   float2* partial;       // [rows][BC][N] when rows > 1, else nullptr
+  int32_t* flags;        // [waves]: 1 when the gather wave's groups sit at common
+                         // offsets (written by the gather's row 0, read by the
+                         // direct kernel, which then skips the wave)
 };
 
 // ---------------------------------------------------------------------------

@@ -45,10 +45,11 @@
 // chunk.  The headers (k) are read from LDS, two addresses per wave.
 //
 // Waves whose voxels are not on the common offsets (any non-grid coordinate
-// set) only help stage the chunks; a second kernel (mfma_direct_kernel)
-// evaluates every voxel phase of those waves directly on the vector ALU from
-// the same records (the offset-0 columns hold fr, fi = Mu_b), and exits at once
-// for the other waves.  Both kernels take the same decision per wave.
+// set) only help stage the chunks (a workgroup of such waves only leaves at
+// once); a second kernel (mfma_direct_kernel) evaluates every voxel phase of
+// those waves directly on the vector ALU from the same records (the offset-0
+// columns hold fr, fi = Mu_b), and exits at once for the other waves: the
+// gather's first launch row records each wave's decision in a flag array.
 //
 // Summation is blocked as in the VALU engine: tile partial sums in the MFMA
 // accumulators, folded (as Re, Im) into running totals at tile ends.
@@ -206,13 +207,16 @@ __device__ __forceinline__ bool wave_regular(const float* __restrict__ x, const 
   bool reg = true;
   const double bx = x[0], by = y[0], bz = z[0];
   const int r = lane / G;
-  const int j0 = r * per > 1 ? r * per : 1, j1 = (r + 1) * per < V ? (r + 1) * per : V;
-  for (int j = j0; j < j1; ++j) {
+  // offsets j = r per + t of the group (j >= 1), unrolled so that the
+  // coordinate loads of several offsets are in flight together
+#pragma unroll 8
+  for (int t = 0; t < per; ++t) {
+    const int j = r * per + t;
     const int64_t n = n0 + j;
-    if (n < N)
-      reg = reg && ((double)x[n] - (double)gx == (double)x[j] - bx) &&
-            ((double)y[n] - (double)gy == (double)y[j] - by) &&
-            ((double)z[n] - (double)gz == (double)z[j] - bz);
+    if (j >= 1 && j < V && n < N)
+      reg &= ((double)x[n] - (double)gx == (double)x[j] - bx) &
+             ((double)y[n] - (double)gy == (double)y[j] - by) &
+             ((double)z[n] - (double)gz == (double)z[j] - bz);
   }
   return __all(reg);
 }
@@ -400,6 +404,10 @@ struct MfmaGather {
     const bool gin = n0 < a.N;
     const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
     const bool regular = wave_regular<V>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
+    // the decision for the direct kernel, once per wave
+    if (blockIdx.y == 0 && lane == 0 && vbase < a.N) a.flags[wave] = regular ? 1 : 0;
+    // a workgroup without a regular wave has no chunk to stage for anyone
+    if (!__syncthreads_or(regular)) return;
     const int32_t row = (int32_t)blockIdx.y;
     int64_t lo, hi;
     row_range(a.m_split, a.mpad, row, lo, hi);
@@ -460,11 +468,11 @@ struct MfmaGather {
 };
 
 // ---------------------------------------------------------------------------
-// Direct gather for the irregular waves (one launch row; all samples).  Lane
-// l of wave w owns voxels 32 V w + l + 64 i, i < V / 2, and evaluates each
-// voxel's phase; records are read with wave-uniform scalar loads.  With
-// sample splits the totals go to partial row 0 and the other rows get zeros,
-// so the fixed-order reduction returns them unchanged.
+// Direct gather for the irregular waves, over the same launch rows as the
+// gather (row blockIdx.y sums its share of the samples into its partial-sum
+// row; one row writes the output).  Lane l of wave w owns voxels
+// 32 V w + l + 64 i, i < V / 2, and evaluates each voxel's phase; records are
+// read with wave-uniform scalar loads.
 template <int T, int BC, int TRIG>
 struct MfmaDirect {
   static constexpr int V = 16 * T / BC;
@@ -472,15 +480,15 @@ struct MfmaDirect {
   static constexpr int HF = mfma_header_floats(TRIG);
   static constexpr int ND = V / 2;
 
-  __device__ static void run(const MfmaArgs& a, int32_t splits) {
+  __device__ static void run(const MfmaArgs& a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
     const int64_t vbase = wave * 32 * V;
+    const int32_t row = (int32_t)blockIdx.y;
+    int64_t lo, hi;
+    row_range(a.m_split, a.mpad, row, lo, hi);
     if (vbase >= a.N) return;
-    const int64_t n0 = vbase + (int64_t)(lane & 31) * V;
-    const bool gin = n0 < a.N;
-    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
-    if (wave_regular<V>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz)) return;
+    if (a.flags[wave]) return;   // a regular wave: the gather kernel summed it
 
     float vx[ND], vy[ND], vz[ND];
 #pragma unroll
@@ -496,8 +504,8 @@ struct MfmaDirect {
     for (int i = 0; i < ND; ++i)
 #pragma unroll
       for (int b = 0; b < BC; ++b) { tre[i][b] = 0.0f; tim[i][b] = 0.0f; }
-    for (int64_t t0 = 0; t0 < a.mpad; t0 += a.tile) {
-      const int64_t t1 = (a.mpad - t0 > a.tile) ? t0 + a.tile : a.mpad;
+    for (int64_t t0 = lo; t0 < hi; t0 += a.tile) {
+      const int64_t t1 = (hi - t0 > a.tile) ? t0 + a.tile : hi;
       float are[ND][BC], aim[ND][BC];
 #pragma unroll
       for (int i = 0; i < ND; ++i)
@@ -538,13 +546,8 @@ struct MfmaDirect {
       if (n >= a.N) continue;
 #pragma unroll
       for (int b = 0; b < BC; ++b) {
-        if (a.partial) {
-          for (int32_t r = 0; r < splits; ++r)
-            a.partial[((int64_t)r * BC + b) * a.N + n] =
-                r == 0 ? make_float2(tre[i][b], tim[i][b]) : make_float2(0.0f, 0.0f);
-        } else {
-          a.out[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
-        }
+        float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+        dst[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
       }
     }
   }
@@ -611,6 +614,7 @@ struct MfmaGather4 {
   // (the three products' entries for t in [4h, 4h + 4)).
   __device__ static __forceinline__ void load_half(const float* __restrict__ wb, int q, int lane, int h,
                                                    float (&bv)[3 * T]) {
+    static_assert(T == 8, "half-block slices 2 p + h of four units each: the layout of T = 8");
     const float* pp = wb + q * QF;
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
@@ -741,6 +745,10 @@ struct MfmaGather4 {
     const bool gin = n0 < a.N;
     const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
     const bool regular = wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
+    // the decision for the direct kernel, once per wave
+    if (blockIdx.y == 0 && lane == 0 && vbase < a.N) a.flags[wave] = regular ? 1 : 0;
+    // a workgroup without a regular wave has no chunk to stage for anyone
+    if (!__syncthreads_or(regular)) return;
     const int32_t row = (int32_t)blockIdx.y;
     int64_t lo, hi;
     row_range(a.m_split, a.mpad, row, lo, hi);
@@ -816,25 +824,25 @@ struct MfmaGather4 {
   }
 };
 
-// Direct gather for the irregular waves of the four-sample engine (one launch
-// row; all samples): lane l of wave w owns voxels 16 V w + l + 64 i,
-// i < V / 4, taken four at a time; records are read with wave-uniform scalar
-// loads (Mu_b = (fr, fi) of the offset-0 column of vector b).
+// Direct gather for the irregular waves of the four-sample engine, over the
+// gather's launch rows as in MfmaDirect: lane l of wave w owns voxels
+// 16 V w + l + 64 i, i < V / 4, taken four at a time; records are read with
+// wave-uniform scalar loads (Mu_b = (fr, fi) of the offset-0 column of vector b).
 template <int T, int BC, int TRIG>
 struct MfmaDirect4 {
   static constexpr int V = 16 * T / BC;
   static constexpr int ND = V / 4;     // voxels per lane
   static constexpr int NV = ND < 4 ? ND : 4;  // voxels per pass over the samples
 
-  __device__ static void run(const MfmaArgs& a, int32_t splits) {
+  __device__ static void run(const MfmaArgs& a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
     const int64_t vbase = wave * 16 * V;
+    const int32_t row = (int32_t)blockIdx.y;
+    int64_t lo, hi;
+    row_range(a.m_split, a.mpad, row, lo, hi);
     if (vbase >= a.N) return;
-    const int64_t n0 = vbase + (int64_t)(lane & 15) * V;
-    const bool gin = n0 < a.N;
-    const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
-    if (wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz)) return;
+    if (a.flags[wave]) return;   // a regular wave: the gather kernel summed it
     constexpr int HF = mfma_header_floats(TRIG);
     for (int i0 = 0; i0 < ND; i0 += NV) {
       float vx[NV], vy[NV], vz[NV];
@@ -851,8 +859,8 @@ struct MfmaDirect4 {
       for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int b = 0; b < BC; ++b) { tre[i][b] = 0.0f; tim[i][b] = 0.0f; }
-      for (int64_t t0 = 0; t0 < a.mpad; t0 += a.tile) {
-        const int64_t t1 = (a.mpad - t0 > a.tile) ? t0 + a.tile : a.mpad;
+      for (int64_t t0 = lo; t0 < hi; t0 += a.tile) {
+        const int64_t t1 = (hi - t0 > a.tile) ? t0 + a.tile : hi;
         float are[NV][BC], aim[NV][BC];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -891,13 +899,8 @@ struct MfmaDirect4 {
         if (n >= a.N) continue;
 #pragma unroll
         for (int b = 0; b < BC; ++b) {
-          if (a.partial) {
-            for (int32_t r = 0; r < splits; ++r)
-              a.partial[((int64_t)r * BC + b) * a.N + n] =
-                  r == 0 ? make_float2(tre[i][b], tim[i][b]) : make_float2(0.0f, 0.0f);
-          } else {
-            a.out[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
-          }
+          float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+          dst[(int64_t)b * a.N + n] = make_float2(tre[i][b], tim[i][b]);
         }
       }
     }
@@ -918,8 +921,8 @@ mfma_gather_kernel(MfmaArgs a) {
 }
 
 template <int T, int BC, int TRIG>
-__global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a, int32_t splits) {
-  MfmaDirect<T, BC, TRIG>::run(a, splits);
+__global__ void __launch_bounds__(kWorkgroup) mfma_direct_kernel(MfmaArgs a) {
+  MfmaDirect<T, BC, TRIG>::run(a);
 }
 
 // Four-sample engine: 4-wave workgroups of ~49 KB of LDS.  With running
@@ -937,12 +940,12 @@ mfma4_gather_kernel(MfmaArgs a) {
 }
 
 template <int T, int BC, int TRIG>
-__global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a, int32_t splits) {
-  MfmaDirect4<T, BC, TRIG>::run(a, splits);
+__global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a) {
+  MfmaDirect4<T, BC, TRIG>::run(a);
 }
 
 using MfmaFn = void (*)(MfmaArgs);
-using DirectFn = void (*)(MfmaArgs, int32_t);
+using DirectFn = void (*)(MfmaArgs);
 
 struct MfmaPair {
   MfmaFn gather;
@@ -1004,12 +1007,12 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
   return hipGetLastError();
 }
 
-// Launches the matrix-core kernel (regular waves, one launch row per sample
-// split) and the direct kernel (irregular waves, one row).
+// Launches the matrix-core kernel (regular waves) and the direct kernel
+// (irregular waves), each with one launch row per sample split.
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,
                               hipStream_t s) {
   MfmaPair fn = select_mfma(trig, T, BC);
-  if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr)) return hipErrorInvalidValue;
+  if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr) || !a.flags) return hipErrorInvalidValue;
   if (a.mpad % kMfmaChunk != 0 || a.m_split % kMfmaChunk != 0 || a.tile % kMfmaChunk != 0 ||
       a.tile <= 0)
     return hipErrorInvalidValue;
@@ -1027,7 +1030,7 @@ hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const Mfm
   hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(64 * wg_waves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn.direct, dim3((unsigned)dblocks), dim3(kWorkgroup), 0, s, a, splits);
+  hipLaunchKernelGGL(fn.direct, dim3((unsigned)dblocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
   return hipGetLastError();
 }
 

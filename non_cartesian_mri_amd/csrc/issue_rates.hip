@@ -108,6 +108,43 @@ __global__ void __launch_bounds__(512) k_mfma_mix(float* out, int blocks_per_wav
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+// The per-pair gather body of the pages' kernel without its memory traffic:
+// one voxel per lane; per sample the phase (1 mul + 2 FMA), fract, v_sin,
+// v_cos and the complex multiply-accumulate -- four FMAs (re += mr c - mi s,
+// im += mi c + mr s) or, with GAUSS, c + s and s - c then three FMAs on
+// (fr + fi, fr, fi) as the VALU engine's records hold them.  The sample's k
+// and weights are wave-uniform values whose bit patterns advance by scalar
+// integer adds each sample, so they cost no VALU work and nothing is hoisted.
+template <int U, bool GAUSS>
+__global__ void __launch_bounds__(256) k_pair(float* out, int iters, int kb0, int kb1, int kb2) {
+  const float x = (float)(threadIdx.x & 63) - 32.0f, y = (float)(blockIdx.x & 127) - 64.0f;
+  const float z = (float)(threadIdx.x >> 6) - 2.0f;
+  float re = 0.0f, im = 0.0f, cr = 0.0f;
+  int kxb = kb0, kyb = kb1, kzb = kb2, mrb = 0x3e99999a, mib = 0xbf333333, sb = 0xbecccccd;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float kx = __builtin_bit_cast(float, kxb), ky = __builtin_bit_cast(float, kyb);
+      const float kz = __builtin_bit_cast(float, kzb), mr = __builtin_bit_cast(float, mrb);
+      const float mi = __builtin_bit_cast(float, mib), mpi = __builtin_bit_cast(float, sb);
+      const float t = __builtin_fmaf(kz, z, __builtin_fmaf(ky, y, kx * x));
+      const float f = __builtin_amdgcn_fractf(t);
+      const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+      if constexpr (GAUSS) {
+        const float cps = cs + sn, smc = sn - cs;
+        re = __builtin_fmaf(mpi, cs, re);        // (fr + fi) is a record value: uniform
+        im = __builtin_fmaf(mi, cps, im);
+        cr = __builtin_fmaf(mr, smc, cr);
+      } else {
+        re = __builtin_fmaf(mr, cs, __builtin_fmaf(-mi, sn, re));
+        im = __builtin_fmaf(mi, cs, __builtin_fmaf(mr, sn, im));
+      }
+      kxb += 17; kyb -= 29; kzb += 13; mrb += 7; mib -= 11; sb += 5;
+    }
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = re + im + cr;
+}
+
 __global__ void k_clock(long long* out, int iters, float a, float b, float* sink) {
   long long c0 = clock64();
   long long w0 = wall_clock64();
@@ -175,6 +212,13 @@ int main() {
     printf("MB-MIX T=%d K=%2d: %.3f ms, CU-cycles per wave-iter %.2f (x4 SIMD = %.2f SIMD-cycles)\n", T, K, t * 1e3, slots, slots * 4); }
   MIX(2, 0) MIX(2, 2) MIX(2, 4) MIX(2, 6) MIX(2, 8) MIX(2, 12) MIX(2, 16) MIX(2, 24)
   MIX(4, 0) MIX(4, 8) MIX(4, 16)
+  // the per-pair body: pairs/s at 8 waves per SIMD (the pages' form and the
+  // VALU engine's three-FMA form)
+#define PAIR(U, G, NAME) { double t = time_it([&] { hipLaunchKernelGGL((k_pair<U, G>), dim3(blocks), dim3(256), 0, 0, out, iters, 0x3d4ccccd, 0xbe19999a, 0x3c23d70a); }, 10); \
+    double pairs = threads * iters * U; \
+    printf("MB-PAIR %s: %.3e pairs/s, %.2f CU-cycles per wave-pair at 2.4 GHz (%.3f ms)\n", NAME, pairs / t, \
+           t * CU * 2.4e9 / (pairs / 64), t * 1e3); }
+  PAIR(4, false, "4-FMA MAC (pages' form)") PAIR(4, true, "3-FMA MAC + c+s, s-c")
   // FP32 MFMA with and without the per-block phase work, 2 waves per SIMD
   // (LDS padding: two 4-wave workgroups or one 8-wave workgroup per CU)
   {

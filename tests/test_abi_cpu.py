@@ -228,14 +228,18 @@ def test_workspace_bytes_mfma(lib):
         kw.setdefault("engine", _lib.FHD_ENGINE_MFMA)
         return lib.fhd_workspace_bytes(M, N, batch, is_q, ctypes.byref(_opts(**kw)))
     a256 = lambda b: (b + 255) // 256 * 256
-    assert ws(1000, 4096, trig=1) == a256(1024 * 16) + 1024 * 384
-    assert ws(1000, 4096) == a256(1024 * 32) + 1024 * 384            # accurate: 8 header floats
-    assert ws(1000, 4096, is_q=1, trig=1) == a256(1024 * 16) + 1024 * 384
-    assert ws(33, 4096, trig=1) == a256(64 * 16) + 64 * 384
-    # batch 5: passes of 4 and 1 vectors, same record size; 3 splits add [3][4][N] partials
+    # plus one int32 regularity flag per gather wave (groups of V = 16 T / BC, 32 groups
+    # per wave for T = 2, 4 and 16 for T = 8): 16^3 with T = 2 -> 4 waves, one 256-byte block
+    fl = a256(4 * 4)
+    assert ws(1000, 4096, trig=1) == a256(1024 * 16) + 1024 * 384 + fl
+    assert ws(1000, 4096) == a256(1024 * 32) + 1024 * 384 + fl       # accurate: 8 header floats
+    assert ws(1000, 4096, is_q=1, trig=1) == a256(1024 * 16) + 1024 * 384 + fl
+    assert ws(33, 4096, trig=1) == a256(64 * 16) + 64 * 384 + fl
+    # batch 5: passes of 4 and 1 vectors, same record size; 3 splits add [3][4][N] partials;
+    # the passes share the flags (one wave each here)
     one = a256(1024 * 16) + 1024 * 384
-    assert ws(1000, 50, batch=5, trig=1) == 2 * one
-    assert ws(1000, 50, batch=5, trig=1, sample_splits=3) == 2 * one + a256(3 * 4 * 50 * 8)
+    assert ws(1000, 50, batch=5, trig=1) == 2 * one + a256(4)
+    assert ws(1000, 50, batch=5, trig=1, sample_splits=3) == 2 * one + a256(3 * 4 * 50 * 8) + a256(4)
     # the default engine is the matrix-core one
     assert lib.fhd_workspace_bytes(1000, 4096, 1, 0, ctypes.byref(_opts(trig=1, sample_splits=1))) == ws(1000, 4096, trig=1)
     assert lib.fhd_workspace_bytes(1000, 4096, 1, 0, ctypes.byref(_opts(trig=1, sample_splits=1, sum=1))) == \
@@ -301,14 +305,15 @@ def test_describe_plan_mfma(lib):
     assert acc["tile"] == 512
     # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
-    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8
+    # headers, factors, 16 rows of partial sums, 1024 per-wave flags
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8 + 1024 * 4
     # groups of 64 (T = 4) or 32 (T = 2) on request, two-sample engine
     four = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=64)
     assert four["voxels_per_lane"] == 64 and four["record_dwords"] == 4 + 192
-    assert four["workspace_bytes"] == 262144 * 16 + 262144 * 768 + 16 * 128 ** 3 * 8
+    assert four["workspace_bytes"] == 262144 * 16 + 262144 * 768 + 16 * 128 ** 3 * 8 + 1024 * 4
     two = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=32)
     assert two["voxels_per_lane"] == 32 and two["record_dwords"] == 4 + 96 and two["engine"] == _lib.FHD_ENGINE_MFMA
-    assert two["workspace_bytes"] == 262144 * 16 + 262144 * 384 + 16 * 128 ** 3 * 8
+    assert two["workspace_bytes"] == 262144 * 16 + 262144 * 384 + 16 * 128 ** 3 * 8 + 2048 * 4
     assert fhd_describe_plan(1000, 96 ** 3, trig="hw")["voxels_per_lane"] == 32
     assert fhd_describe_plan(1000, 100, trig="hw")["voxels_per_lane"] == 32     # not a cube
     # 64^3: groups of 128 = two whole rows of a plane (regular); 128 waves x 16 rows
@@ -391,8 +396,12 @@ def test_forward_plan(lib):
     # HW trig: the launch row (all 16,384 groups) is one summation block
     assert p["sample_splits"] == 1 and p["tile"] == 16384
     # accurate trig keeps ~sqrt(groups) per tile; so does HW with rows of more
-    # than 65,536 groups (512^3: ~4 sqrt(G))
+    # than 256 MiB of packed groups (512^3: 1.6 GB per row, ~4 sqrt(G))
     assert fhd_describe_plan(262144, 512 ** 3, op="forward", trig="hw")["tile"] == 4096
+    # the 16-image pass on 96^3 (groups of 8 voxels: 110,592 groups, 170 MB per
+    # row) is one block per row
+    b16 = fhd_describe_plan(500001, 96 ** 3, batch=16, op="forward", trig="hw")
+    assert b16["sample_splits"] == 1 and b16["tile"] == 110592 and b16["voxels_per_lane"] == 8
     assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate")["tile"] == 128
     pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
     assert p["workspace_bytes"] == pas(16384, 8)

@@ -91,7 +91,9 @@ def test_batched(oracle_mod, trig, B):
 @pytest.mark.parametrize("trig", TRIGS)
 def test_batch_rows_equal_single_calls_bitwise(trig):
     """VALU engine: row b of a batched call equals a single call on D[b] (same
-    per-sample arithmetic: one voxel per lane in both)."""
+    per-sample arithmetic: one voxel per lane in both), and permuting the data
+    vectors of a batch permutes its output rows bit for bit (the vectors share
+    one phase, sine and cosine per sample and keep their own sums)."""
     p = inputs.random_problem(205, M=300, L=8, B=16)
     d = dev_problem(p)
     full = gpu_fhd(p, d, trig=trig, engine="valu")
@@ -99,6 +101,9 @@ def test_batch_rows_equal_single_calls_bitwise(trig):
         q = inputs.Problem(p.name, "fhd", p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D[b:b + 1], p.seed)
         one = gpu_fhd(q, trig=trig, voxels_per_lane=1)
         assert np.array_equal(one[0], full[b])
+    perm = np.random.Generator(np.random.PCG64(2051)).permutation(p.B)
+    q = inputs.Problem(p.name, "fhd", p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, np.ascontiguousarray(p.D[perm]), p.seed)
+    assert np.array_equal(gpu_fhd(q, trig=trig, engine="valu"), full[perm])
 
 
 @pytest.mark.parametrize("trig", TRIGS)

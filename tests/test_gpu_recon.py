@@ -129,7 +129,9 @@ def _few_sample_case(L, M, lam):
         kx, ky, kz = inputs.uniform_k(M, rng)
         phi = inputs.complex_normal(rng, M)
         p = inputs.complex_normal(rng, L ** 3)
-        lam_abs = lam * float(np.sum(np.abs(phi.astype(np.complex128)) ** 2)) / 6.0
+        # F^H F p of a few samples has norm ~ sum |phi|^2 sqrt(N) |p| / sqrt(N): this lam
+        # makes lam W^H W p (up to 12 |p| per voxel) about as large
+        lam_abs = lam * float(np.sum(np.abs(phi.astype(np.complex128)) ** 2)) * L ** 1.5 / 12.0
         ref = recon.normal_direct(kx, ky, kz, phi, p, L, L, L, lam_abs)
         _direct_cache.clear()
         _direct_cache[key] = (kx, ky, kz, phi, p, lam_abs, ref)
