@@ -54,10 +54,10 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # the kernel source it was taken on, like TRAFFIC below)
 MFMA_BUSY = {
     ("fhd_128cube_262144_spirals", "hw", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9", "busy": 0.923,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a", "busy": 0.923,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9", "busy": 0.856,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a", "busy": 0.849,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
 }
 
@@ -79,28 +79,28 @@ def method_roofline(kind: str, B: int) -> dict:
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9",
-        "fetch_bytes": 1975686.9 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a",
+        "fetch_bytes": 1806249.6 * 1024 * 2.0, "write_bytes": 262153.5 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "10d249c9f859bdb9",
-        "fetch_bytes": 1782119.0 * 1024 * 2.0, "write_bytes": 262144.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a",
+        "fetch_bytes": 1784694.1 * 1024 * 2.0, "write_bytes": 262152.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "1bfd70071cd52ea6",
-        "fetch_bytes": 1577119.5 * 1024 * 2.0, "write_bytes": 31299.3 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "b0fa4414bc124d10",
+        "fetch_bytes": 1577159.7 * 1024 * 2.0, "write_bytes": 31170.2 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "1bfd70071cd52ea6",
-        "fetch_bytes": 1521269.3 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "b0fa4414bc124d10",
+        "fetch_bytes": 1519603.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
-        "fetch_bytes": 984501.3 * 1024 * 2.0, "write_bytes": 262145.5 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "eff1a443cd376689",
+        "fetch_bytes": 984433.6 * 1024 * 2.0, "write_bytes": 262149.7 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "83866d8c726ffcf7",
-        "fetch_bytes": 1047793.4 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "eff1a443cd376689",
+        "fetch_bytes": 1047473.6 * 1024 * 2.0, "write_bytes": 262151.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
