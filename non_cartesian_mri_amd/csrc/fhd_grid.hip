@@ -17,8 +17,10 @@
 //
 //   image = IDFT(L),   L[j'] = (-1)^(j'x + j'y + j'z) G[j' - n/2 (mod n, per axis)],
 //
-// an unnormalised inverse DFT of the rolled, sign-alternated lattice, run as
-// three passes of the library's line FFTs in place in the output.
+// an unnormalised inverse DFT of the rolled, sign-alternated lattice: the x
+// transform inside the deposit kernel (a tile holds whole x-rows of a
+// plane), then two passes of the library's line FFTs (y, z) in place in the
+// output.
 //
 // The spreading uses no global atomics (scattered float atomics run at a
 // fraction of the rate of scattered stores).  A counting sort lists every
@@ -26,9 +28,9 @@
 // jz and jz + 1 (mod nz), so it makes two entries, each holding the sample's
 // x / y cell, x / y fractions and Mu times its z weight.  Then one workgroup
 // per tile of TY rows of a plane (TY nx <= 4096 cells) adds the entries of its
-// plane that touch its rows into the tile and writes the tile once, rolled and
-// sign-alternated into L.  The tile sums are 64-bit fixed point with LDS
-// integer atomics (on this GPU an LDS float atomic add runs at about a ninth
+// plane that touch its rows into the tile, then transforms the tile's rows
+// (rolled and sign-alternated: rows of L) along x and writes them once.  The
+// tile sums are 64-bit fixed point with LDS integer atomics (on this GPU an LDS float atomic add runs at about a ninth
 // of the rate of an integer one): with c the largest |Re| or |Im| of any Mu,
 // no cell receives more than M contributions of size <= c, so terms scaled by
 // 2^s with M c 2^s < 2^61 cannot overflow, and each term is the double
@@ -39,6 +41,7 @@
 // double, so every sample lands in the cells its exact coordinate selects.
 #include "fhd.h"
 #include "fhd_cg.h"
+#include "fhd_fft.h"
 #include "fhd_lines.h"
 
 namespace ncmri {
@@ -204,12 +207,9 @@ fill_kernel(const float* __restrict__ kx, const float* __restrict__ ky, const fl
   }
 }
 
-// One tile: rows [row0, row0 + TY) of plane z.  The plane's entries that touch
-// those rows go into the tile as 64-bit fixed-point sums (LDS integer
-// atomics); the tile is then written once into L: cell (x, y, z) to
-// ((x, y, z) + n/2 mod n), times (-1) to the sum of the new coordinates.
-constexpr int kDepositThreads = 1024;
-
+// One tile: rows [row0, row0 + TY) of plane z.  The plane's entries that
+// touch those rows go into the tile as 64-bit fixed-point sums (LDS integer
+// atomics).
 __device__ __forceinline__ void add_fixed(unsigned long long* t, int i, double re, double im) {
   atomicAdd(&t[2 * i], (unsigned long long)(long long)__builtin_rint(re));
   atomicAdd(&t[2 * i + 1], (unsigned long long)(long long)__builtin_rint(im));
@@ -235,18 +235,66 @@ __device__ __forceinline__ void deposit_entry(unsigned long long* t, unsigned c,
   }
 }
 
-__global__ void __launch_bounds__(kDepositThreads)
-deposit_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ count,
-               const unsigned* __restrict__ cell, const float4* __restrict__ val, const unsigned* __restrict__ maxbits,
-               int64_t M, int nx, int lx, int ny, int nz, int ty, float2* __restrict__ L) {
+// The deposit with the inverse x transform fused in: a tile holds whole
+// x-rows of its plane, so after the fixed-point sums its rows are
+// transformed in LDS and written to the image already x-transformed (one
+// pass over the lattice fewer).  The row transforms take the first
+// Lds<N, kRows>::kThreads threads; the others only keep the barriers in step.
+constexpr int kFusedThreads = 512;
+
+// First-stage inputs: point x' of tile row l is L[x'] =
+// (-1)^(x' + yr + zr) G[(x' + nx/2) mod nx] (rolled, sign-alternated), from
+// the tile's fixed-point sums.
+struct TileRows {
+  const unsigned long long* tile;
+  int nx, ty, row0, ny, zr;
+  double unscale;
+  template <int RN, int STEP>
+  __device__ __forceinline__ void get(int l, int j, float2* w) const {
+    const bool ok = l < ty;
+    const int yr = (row0 + l + ny / 2) & (ny - 1);
+    const int s0 = (yr + zr) & 1;
+#pragma unroll
+    for (int r = 0; r < RN; ++r) {
+      const int xp = j + r * STEP;
+      const int k = l * nx + ((xp + nx / 2) & (nx - 1));
+      const float re = ok ? (float)((double)(long long)tile[2 * k] * unscale) : 0.0f;
+      const float im = ok ? (float)((double)(long long)tile[2 * k + 1] * unscale) : 0.0f;
+      w[r] = ((xp + s0) & 1) ? make_float2(-re, -im) : make_float2(re, im);
+    }
+  }
+};
+
+// Last-stage outputs: transformed row l to image[zr][yr][x].
+struct ImageRows {
+  float2* image;
+  int nx, ty, row0, ny, zr;
+  template <int RN, int STEP>
+  __device__ __forceinline__ void put(int l, int j, const float2* w) const {
+    if (l >= ty) return;
+    const int yr = (row0 + l + ny / 2) & (ny - 1);
+    float2* p = image + (((int64_t)zr * ny + yr) * nx + j);
+#pragma unroll
+    for (int r = 0; r < RN; ++r) p[r * STEP] = w[r];
+  }
+};
+
+template <int N>
+__global__ void __launch_bounds__(kFusedThreads)
+deposit_x_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ count,
+                 const unsigned* __restrict__ cell, const float4* __restrict__ val,
+                 const unsigned* __restrict__ maxbits, int64_t M, int ny, int nz, int ty,
+                 float2* __restrict__ image) {
+  using L = fft::Lds<N, fft::kRows>;
+  static_assert(L::kSize * sizeof(float2) <= 2 * kTileCells * sizeof(unsigned long long), "buffer in the tile");
+  static_assert(L::kThreads <= kFusedThreads && L::kLines * N == kTileCells, "a tile is one transform group");
+  constexpr int nx = N;
   __shared__ unsigned long long tile[2 * kTileCells];   // 64 KB: (Re, Im) per cell
-  // plane = block mod nz, tile = block div nz: blocks go to the 8 XCDs in
-  // turn, so every XCD gets every tile index (the middle rows of a plane
-  // usually hold most of the samples)
+  __shared__ float2 tw[N];
+  fft::fill_twiddles<N>(tw);
   const int z = (int)(blockIdx.x % (unsigned)nz), row0 = (int)(blockIdx.x / (unsigned)nz) * ty;
   const int cells = ty * nx;
-  for (int i = threadIdx.x; i < 2 * cells; i += kDepositThreads) tile[i] = 0ull;
-  // scale 2^s with M c 2^s < 2^61 (c: the largest |Re|, |Im| of any value)
+  for (int i = threadIdx.x; i < 2 * cells; i += kFusedThreads) tile[i] = 0ull;
   unsigned cb = maxbits[threadIdx.x & (kMaxSlots - 1)];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -258,23 +306,51 @@ deposit_kernel(const unsigned* __restrict__ start, const unsigned* __restrict__ 
   const double scale = ldexp(1.0, 61 - e), unscale = ldexp(1.0, e - 61);
   __syncthreads();
   const unsigned e0 = start[z], e1 = e0 + count[z];
-  // two entries per thread and trip, so two loads are in flight
   unsigned i = e0 + threadIdx.x;
-  for (; (int64_t)i + kDepositThreads < (int64_t)e1; i += 2 * kDepositThreads) {
-    const unsigned ca = cell[i], cb = cell[i + kDepositThreads];
-    const float4 fa = val[i], fb = val[i + kDepositThreads];
+  for (; (int64_t)i + kFusedThreads < (int64_t)e1; i += 2 * kFusedThreads) {
+    const unsigned ca = cell[i], cb2 = cell[i + kFusedThreads];
+    const float4 fa = val[i], fb = val[i + kFusedThreads];
     deposit_entry(tile, ca, fa, nx, ny, ty, row0, scale);
-    deposit_entry(tile, cb, fb, nx, ny, ty, row0, scale);
+    deposit_entry(tile, cb2, fb, nx, ny, ty, row0, scale);
   }
   if (i < e1) deposit_entry(tile, cell[i], val[i], nx, ny, ty, row0, scale);
   __syncthreads();
   const int zr = (z + nz / 2) & (nz - 1);
-  for (int k = threadIdx.x; k < cells; k += kDepositThreads) {
-    const int y = k >> lx, x = k & (nx - 1);
-    const int yr = (row0 + y + ny / 2) & (ny - 1), xr = (x + nx / 2) & (nx - 1);
-    const double re = (double)(long long)tile[2 * k] * unscale, im = (double)(long long)tile[2 * k + 1] * unscale;
-    const float2 v = make_float2((float)re, (float)im);
-    L[((int64_t)zr * ny + yr) * nx + xr] = ((xr + yr + zr) & 1) ? make_float2(-v.x, -v.y) : v;
+  if (threadIdx.x < L::kThreads) {
+    float2 v[fft::kPerThread];
+    // the first stage reads the tile; the exchanges reuse its LDS after a barrier
+    fft::transform<N, fft::kRows, true, false, false>(TileRows{tile, nx, ty, row0, ny, zr, unscale},
+                                                      reinterpret_cast<float2*>(tile), tw, v);
+    fft::last_stage<N, fft::kRows, false, false>(ImageRows{image, nx, ty, row0, ny, zr}, v);
+  } else {
+    for (int b = 0; b < 2 * (fft::Sched<N>::kStages - 1); ++b) __syncthreads();
+  }
+}
+
+template <int N>
+hipError_t launch_deposit_x(int64_t blocks, const unsigned* start, const unsigned* count, const unsigned* cell,
+                            const float4* val, const unsigned* maxbits, int64_t M, int ny, int nz, int ty,
+                            float2* image, hipStream_t s) {
+  hipLaunchKernelGGL(deposit_x_kernel<N>, dim3((unsigned)blocks), dim3(kFusedThreads), 0, s, start, count, cell,
+                     val, maxbits, M, ny, nz, ty, image);
+  return hipGetLastError();
+}
+
+hipError_t launch_deposit_x_n(int nx, int64_t blocks, const unsigned* start, const unsigned* count,
+                              const unsigned* cell, const float4* val, const unsigned* maxbits, int64_t M, int ny,
+                              int nz, int ty, float2* image, hipStream_t s) {
+  switch (nx) {
+    case 2: return launch_deposit_x<2>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 4: return launch_deposit_x<4>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 8: return launch_deposit_x<8>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 16: return launch_deposit_x<16>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 32: return launch_deposit_x<32>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 64: return launch_deposit_x<64>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 128: return launch_deposit_x<128>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 256: return launch_deposit_x<256>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 512: return launch_deposit_x<512>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    case 1024: return launch_deposit_x<1024>(blocks, start, count, cell, val, maxbits, M, ny, nz, ty, image, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -313,15 +389,11 @@ const char* gridding_run(const float* kx, const float* ky, const float* kz, cons
     if (hipGetLastError() != hipSuccess) return "fill kernel launch failed";
   }
   const int ty = ny < kTileCells / nx ? ny : kTileCells / nx;   // powers of two: ty divides ny
-  int lx = 0;
-  while ((1 << lx) < nx) ++lx;
-  hipLaunchKernelGGL(deposit_kernel, dim3((unsigned)((int64_t)nz * (ny / ty))), dim3(kDepositThreads), 0, s, start,
-                     count, cell, val, maxbits, M, nx, lx, ny, nz, ty, image);
-  if (hipGetLastError() != hipSuccess) return "deposit kernel launch failed";
-  const int64_t plane = (int64_t)nx * ny;
-  if (launch_lines(true, kLineInv, nx, line_pass(image, image, (int64_t)nz * ny, 1, nx, 0, 1, nx, nx), s) !=
+  // deposit + inverse x transform of the tile rows, straight into the image
+  if (launch_deposit_x_n(nx, (int64_t)nz * (ny / ty), start, count, cell, val, maxbits, M, ny, nz, ty, image, s) !=
       hipSuccess)
-    return "x transform launch failed";
+    return "deposit kernel launch failed";
+  const int64_t plane = (int64_t)nx * ny;
   if (launch_lines(false, kLineInv, ny, line_pass(image, image, (int64_t)nz * nx, nx, plane, 1, nx, ny, ny), s) !=
       hipSuccess)
     return "y transform launch failed";
