@@ -267,9 +267,12 @@ fhd_status fhd_forward(const float* kx, const float* ky, const float* kz,
 size_t fhd_toeplitz_bytes(int32_t nx, int32_t ny, int32_t nz);
 
 /*
- * Qhat = DFT(Q embedded in the padded grid) / (px py pz), real: float[pz][py][px].
+ * Qhat = DFT(Q embedded in the padded grid) / (px py pz), real, px py pz floats.
  * Q at difference d sits at d mod p per axis for |d| < n, zero elsewhere; as
- * Q(-d) = conj(Q(d)) the spectrum is real and only its real part is kept.  Q
+ * Q(-d) = conj(Q(d)) the spectrum is real and only its real part is kept.
+ * Layout (read by fhd_normal_apply / fhd_cg_solve only): the (ky, kx) columns
+ * c = ky px + kx in blocks of W = min(32, px py) consecutive ones, each block
+ * float[pz][W]; Qhat(kz, ky, kx) is at (c / W) pz W + kz W + c mod W.  Q
  * is computed by the q_compute path on the (2nz, 2ny, 2nx) grid of
  * differences (opts as for q_compute, without workspace or stages: the call
  * allocates its scratch with hipMallocAsync on `stream`).  Qhat is

@@ -14,6 +14,11 @@
 //
 // Q(-d) = conj(Q(d)), so the embedded grid is Hermitian and Qhat is real; the
 // entry at d = -n, never used by the product, is left zero to keep it so.
+// Qhat is stored in the order the z pass reads it: the (ky, kx) columns in
+// blocks of W = 32 consecutive ones (kx fastest), each block holding its W
+// columns point by point along kz (W floats = 128 bytes per kz), so a tile of
+// the z pass reads one contiguous 128 KB block (at Pz = 1024) instead of a
+// short row in each of Pz planes, which costs an address translation apiece.
 //
 // The transforms are the library's own line FFTs (fhd_fft.h), one kernel per
 // axis, and the product skips what the padding makes trivial:
@@ -78,9 +83,20 @@ embed_kernel(const float2* __restrict__ Q2, float2* __restrict__ G, int nx, int 
 }
 
 __global__ void __launch_bounds__(kThreads)
-real_scale_kernel(const float2* __restrict__ G, float* __restrict__ Qhat, int64_t n, float scale) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
-    Qhat[i] = G[i].x * scale;
+real_scale_kernel(const float2* __restrict__ G, float* __restrict__ Qhat, int64_t n, float scale, int64_t plane,
+                  int pz, int shift) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    // G[kz][ky][kx] -> column c = ky px + kx, point kz of its block
+    const int64_t z = i / plane, c = i - z * plane;
+    Qhat[(c >> shift) * ((int64_t)pz << shift) + (z << shift) + (c & ((1 << shift) - 1))] = G[i].x * scale;
+  }
+}
+
+// log2 of the spectrum's block width: 32 columns, fewer on grids with fewer.
+int spectrum_block_shift(int64_t plane) {
+  int s = 0;
+  while (s < 5 && ((int64_t)2 << s) <= plane) ++s;
+  return s;
 }
 
 // Block sum of a double in LDS (fixed tree: deterministic).
@@ -418,7 +434,7 @@ const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G
   if (launch_lines(false, kLineFwd, d.pz, line_pass(G, G, plane, 1, 1, 0, plane, d.pz, d.pz), s) != hipSuccess)
     return "z transform launch failed";
   hipLaunchKernelGGL(real_scale_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, s, G, Qhat, total,
-                     (float)(1.0 / (double)total));
+                     (float)(1.0 / (double)total), plane, d.pz, spectrum_block_shift(plane));
   if (hipGetLastError() != hipSuccess) return "spectrum scale kernel launch failed";
   return nullptr;
 }
@@ -437,7 +453,8 @@ const char* normal_apply_rest(const ToeplitzDims& d, const float* Qhat, float la
   // z: columns (ky, kx): nz points, spectral product, nz points back
   LinePass zq = line_pass(T, T, plane, 1, 1, 0, plane, d.nz, d.nz);
   zq.q = Qhat;
-  zq.q_es = plane;
+  zq.q_shift = spectrum_block_shift(plane);
+  zq.q_bs = (int64_t)d.pz << zq.q_shift;
   if (launch_lines(false, kLineFwdQInv, d.pz, zq, s) != hipSuccess) return "z transform launch failed";
   // y inverse: py points in, ny out
   if (launch_lines(false, kLineInv, d.py, line_pass(T, T, (int64_t)d.nz * d.px, d.px, plane, 1, d.px, d.py, d.ny), s) !=

@@ -16,12 +16,15 @@ namespace ncmri {
 struct LinePass {
   const float2* in;
   float2* out;
-  const float* q;  // kLineFwdQInv: the real spectrum at q[c + i * q_es]
+  // kLineFwdQInv: the real spectrum in blocks of W = 2^q_shift lines, point-major
+  // within a block: point i of line c at q[(c >> q_shift) q_bs + (c mod W) + i W]
+  const float* q;
   int count;       // lines
   int inner;
   int64_t in_os, in_ws, in_es;
   int64_t out_os, out_ws, out_es;
-  int64_t q_es;
+  int q_shift;
+  int64_t q_bs;
   int nin;         // points read per line (the rest are zero)
   int nout;        // points written per line (the first nout)
 };

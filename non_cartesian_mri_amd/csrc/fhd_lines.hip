@@ -124,8 +124,9 @@ __global__ void __launch_bounds__((fft::Lds<N, layout<N, ROW, MODE>()>::kThreads
         int l, j;
         fft::locate<N, RL, LAY>(k, l, j);
         const int c = c0 + l;
-        const float* qp = a.q + (c + (int64_t)j * a.q_es);
-        const int64_t qst = (int64_t)kStep * a.q_es;
+        const float* qp = a.q + ((int64_t)(c >> a.q_shift) * a.q_bs + (c & ((1 << a.q_shift) - 1)) +
+                                 ((int64_t)j << a.q_shift));
+        const int64_t qst = (int64_t)kStep << a.q_shift;
 #pragma unroll
         for (int r = 0; r < RL; ++r) {
           qv[k * RL + r] = c < a.count ? *qp : 0.0f;
@@ -207,7 +208,8 @@ LinePass line_pass(const float2* in, float2* out, int64_t count, int64_t inner, 
   a.in_os = a.out_os = os;
   a.in_ws = a.out_ws = ws;
   a.in_es = a.out_es = es;
-  a.q_es = 0;
+  a.q_shift = 0;
+  a.q_bs = 0;
   a.nin = nin;
   a.nout = nout;
   return a;

@@ -255,7 +255,10 @@ def toeplitz_lengths(shape) -> tuple[int, int, int]:
 def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked",
                         voxels_per_lane=0, tile=0, sample_splits=0, engine="auto",
                         out=None, stream=None) -> torch.Tensor:
-    """Qhat for an image grid of `shape` = (nz, ny, nx): float32 [pz, py, px].
+    """Qhat for an image grid of `shape` = (nz, ny, nx): pz * py * px float32 values,
+    returned as a [pz, py, px] tensor whose storage order is the library's
+    (blocks of min(32, px py) consecutive (ky, kx) columns, kz-major within a
+    block: see fhd_toeplitz_kernel in include/fhd.h).
 
     The (real) DFT of Q embedded in the padded grid of coordinate differences,
     divided by px py pz, so that fhd_normal_apply applies F^H F as a cyclic
