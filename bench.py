@@ -104,8 +104,8 @@ TRAFFIC = {
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "205decdbeb103aa9",
-        "fetch_bytes": 147713.8 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "dade316886c918a3",
+        "fetch_bytes": 147718.1 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
         "profile": "profiles/cg_normal_operator_128cubed_kernel_stats.md"},
 }
 WORKLOADS = {
