@@ -207,6 +207,33 @@ def test_cg_degenerate_cases():
     assert abs(r.item() - want) <= 1e-6 * want
 
 
+def _embedded_spectrum(qd, nx, ny, nz):
+    """Re DFT(Q embedded in the padded grid) / (px py pz), [pz][py][px], from the
+    oracle's Q at the differences in (-n, n): Q(d) at d mod p per axis."""
+    from non_cartesian_mri_amd.fhd import toeplitz_lengths
+    pz, py, px = toeplitz_lengths((nz, ny, nx))
+    G = np.zeros((pz, py, px), np.complex128)
+    d = [np.arange(-(n - 1), n) for n in (nz, ny, nx)]
+    G[np.ix_(d[0] % pz, d[1] % py, d[2] % px)] = qd
+    return np.fft.fftn(G).real / (px * py * pz)
+
+
+@pytest.mark.parametrize("grid", [(3, 5, 2), (4, 2, 3), (1, 1, 1)])
+def test_toeplitz_spectrum_layout(grid):
+    """fhd_toeplitz_kernel's values in the order include/fhd.h documents: the
+    (ky, kx) columns c = ky px + kx in blocks of W = min(32, px py), each block
+    float[pz][W] -- against the oracle's Q, embedded and transformed in double."""
+    from oracle import recon
+    nx, ny, nz = grid
+    _, kx, ky, kz, phi = _traj(733, 400)
+    spec = _embedded_spectrum(recon.q_differences(kx, ky, kz, phi, nx, ny, nz), nx, ny, nz)
+    pz, py, px = spec.shape
+    W = min(32, px * py)
+    want = spec.reshape(pz, px * py // W, W).transpose(1, 0, 2).ravel()
+    got = _qhat(kx, ky, kz, phi, (nz, ny, nx), trig="accurate").cpu().numpy().ravel()
+    assert_close(got, want, OP_TOL["accurate"], f"Qhat layout {grid}")
+
+
 def test_single_voxel_grid(oracle_mod):
     """1 x 1 x 1: F^H F is the scalar Q(0) = sum |phi|^2."""
     from non_cartesian_mri_amd import fhd_normal_apply
