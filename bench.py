@@ -102,6 +102,15 @@ TRAFFIC = {
         "source": "fhd_kernels.hip", "kernel_sha256": "eff1a443cd376689",
         "fetch_bytes": 1047473.6 * 1024 * 2.0, "write_bytes": 262151.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    # the whole gridding reconstruction (sort, deposit + x transform, y and z passes)
+    ("fhd_128cube_262144_spirals/gridding", "-", "-", "-", 0): {
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "0235fdc59edd0488",
+        "fetch_bytes": 25871.8 * 1024 * 2.0, "write_bytes": 59449.8 * 1024 * 1.0,
+        "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
+    ("fhd_512cube_262144_spirals/gridding", "-", "-", "-", 0): {
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "0235fdc59edd0488",
+        "fetch_bytes": 1380798.0 * 1024 * 2.0, "write_bytes": 3156022.2 * 1024 * 1.0,
+        "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
         "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "dade316886c918a3",
@@ -315,7 +324,10 @@ def bench_cg(args, p, t, D, dev) -> dict:
                       "fhd_setup": round(fhd_ms, 3), "toeplitz_setup": round(toe_ms, 3)},
         "residual": {"first": float(rr[0]), "last": float(rr[-1])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 3),
+                     "traffic_unit": "GB/s (HBM bytes per reconstruction from FETCH_SIZE/WRITE_SIZE / its time)",
+                     "traffic_detail": traffic_detail,
                      "kernel": "the normal operator timed as one unit: x, y transforms, z transform with the "
                                "spectral product, inverse y, inverse x with the regulariser and <p, Ap>",
                      "algorithmic_bytes": op_bytes},
@@ -390,6 +402,7 @@ def bench_gridding(args, p, t, D, dev) -> dict:
     # z passes (the sort's entries are the implementation's, not counted)
     alg = p.M * 28 + 8 * n + 2 * 16 * n
     achieved = alg / (step_ms * 1e-3) / 1e9
+    traffic, traffic_detail = traffic_for(args.config + "/gridding", "-", "-", "-", 0, step_ms)
     res = {
         "metric": f"gridding/iFFT reconstructions/s, {L}^3 grid",
         "value": round(1e3 / ms_per_step, 3), "unit": "images/s",
