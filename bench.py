@@ -683,6 +683,11 @@ def main():
                      "achieved_is": "the method's FLOP per launch (flop_per_pair x pairs) / gather time",
                      "method_roofline": mr, "engine": eng},
     }
+    if p.B > 1:
+        # value counts voxel-sample-vector triples; a trajectory pass is the N M
+        # voxel-sample pairs whose phase, sine and cosine the B vectors share
+        res["per_trajectory_pass"] = {"value": round(value / p.B, 3), "unit": "Gpair/s",
+                                      "is": "N M / step time (value = B N M / step time)"}
     if not forward and not (engine == "valu" and plan["voxels_per_lane"] == 1) and args.method_steps > 0:
         res["method"] = time_per_pair_kernel(p, t, D, args, stream, mr)
     if args.cpu_seconds > 0:
