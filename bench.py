@@ -33,6 +33,7 @@ import numpy as np
 
 METRIC = "FhD voxel·sample pairs/s at 128³×262144 (G/s) + % of FP32/trig roofline"
 FP32_PEAK_TFLOPS = 157.3          # MI355X published FP32 peak (vector, and dense matrix)
+FP16_PEAK_TFLOPS = 2500.0         # MI355X published dense fp16 matrix peak
 HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # The method's work per voxel-sample pair: phase 5 + reduction 1 + complex
 # MAC 8 (Q: real weight, MAC 4), plus two transcendentals; with B data vectors
@@ -137,7 +138,10 @@ def parse():
     ap.add_argument("--config", default="fhd_128cube_262144_spirals", choices=sorted(WORKLOADS))
     ap.add_argument("--trig", default="hw", choices=["accurate", "hw"])
     ap.add_argument("--sum", default="blocked", choices=["blocked", "kahan", "plain"])
-    ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--engine", default="auto", choices=["auto", "valu", "mfma", "mfma16"])
+    ap.add_argument("--half-steps", type=int, default=5,
+                    help="steps of the opt-in half-split engine (engine=mfma16) timed beside the matrix-core "
+                         "engine's (0: skip)")
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "cg", "gridding"],
                     help="fhd: F^H D (or Q for a Q workload); forward: F rho of a seeded image "
                          "on the same trajectory and voxels; cg: conjugate-gradient reconstruction "
@@ -505,6 +509,56 @@ def time_per_pair_kernel(p, t, D, args, stream, mr) -> dict:
             "frac_issue": None if not PAIR_ISSUE_CEILING else round(rate / PAIR_ISSUE_CEILING, 4)}
 
 
+def time_half_engine(p, t, D, args, stream) -> dict:
+    """The opt-in half-split engine (engine="mfma16") on the same workload and
+    trig path: whole steps (scale + records, gather, row reduction) and the
+    gather alone, timed with HIP events on its stream."""
+    import torch
+    from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes, q_compute
+    is_q = p.kind == "q"
+    opts = dict(trig=args.trig, sum=args.sum, engine="mfma16")
+    ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, is_q=is_q, **opts)), dtype=torch.uint8,
+                     device=t["kx"].device)
+    out = torch.empty((p.B, p.N), dtype=torch.complex64, device=t["kx"].device)
+
+    def stage(which):
+        if is_q:
+            q_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], stages=which, workspace=ws,
+                      out=out.view(-1), **opts)
+        else:
+            fhd_compute(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], t["phi"], D, stages=which,
+                        workspace=ws, out=out, **opts)
+
+    for _ in range(2):
+        for w in ("mu", "gather", "reduce"):
+            stage(w)
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.half_steps)]
+    for e0, e1, e2, e3 in ev:
+        e0.record(stream)
+        stage("mu")
+        e1.record(stream)
+        stage("gather")
+        e2.record(stream)
+        stage("reduce")
+        e3.record(stream)
+    torch.cuda.synchronize()
+    step = float(np.median([a.elapsed_time(d) for a, b, c, d in ev]))
+    gather = float(np.mean([b.elapsed_time(c) for a, b, c, d in ev]))
+    pairs = p.N * p.M * p.B
+    ex = 18 * pairs / (gather * 1e-3) / 1e12
+    return {"engine": "mfma16", "steps": args.half_steps,
+            "value": round(pairs / (step * 1e-3) / 1e9, 3), "unit": "Gpair/s", "step_event_median_ms": round(step, 4),
+            "gather_event_mean_ms": round(gather, 4),
+            "gather_pairs_per_s": round(pairs / (gather * 1e-3), 1),
+            "achieved": round(ex, 3), "peak": FP16_PEAK_TFLOPS, "unit_engine": "TFLOP/s",
+            "frac": round(ex / FP16_PEAK_TFLOPS, 4), "executed_flop_per_pair": 18,
+            "note": "opt-in engine (not the default that value reports): the same factored sum with every fp32 "
+                    "product formed from fp16 parts (hi hi + hi lo + lo hi) on v_mfma_f32_16x16x32_f16 with fp32 "
+                    "accumulation; parity against the oracle at the fp32 bars in tests/test_gpu_half.py and "
+                    "tests/test_gpu_configs.py"}
+
+
 def main():
     args = parse()
     if args.issue_rates:
@@ -601,7 +655,7 @@ def main():
     g_avg = float(gather_ms.mean())
     from non_cartesian_mri_amd.fhd import fhd_describe_plan
     plan = fhd_describe_plan(p.M, p.N, p.B, op=op, **opts)
-    engine = {1: "valu", 2: "mfma"}[plan["engine"]]
+    engine = {1: "valu", 2: "mfma", 3: "mfma16"}[plan["engine"]]
     kind = "forward" if forward else p.kind
     # the method's work: per (voxel, sample) one phase, reduction and sin/cos,
     # and per vector a complex MAC (14 FLOP + 2 transcendentals for one vector,
@@ -612,7 +666,18 @@ def main():
     gather_rate = pairs / (g_avg * 1e-3)
     mr["frac"] = round(gather_rate / mr["p_roof_pairs_per_s"], 4)
     mr["per_pair_issue_ceiling_pairs_per_s"] = PAIR_ISSUE_CEILING
-    if forward or engine == "mfma":
+    if engine == "mfma16":
+        # three real products per complex pair, each as three fp16 products
+        ex = 18 * pairs / (g_avg * 1e-3) / 1e12
+        bound = "mfma"
+        eng = {"engine": "mfma16", "bound": "mfma", "executed_flop_per_pair": 18, "achieved": round(ex, 3),
+               "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ex / FP16_PEAK_TFLOPS, 4),
+               "note": "half-split factorisation: the grid-factored sum of the MFMA engine with every fp32 "
+                       "product formed from fp16 parts (hi hi + hi lo + lo hi, fp32 accumulation) on "
+                       "v_mfma_f32_16x16x32_f16; the factors are scaled by a power of two into fp16 range"}
+        kernel = ("half_gather_kernel: its launch rows in one step, timed alone with the (empty on a grid) "
+                  "half_direct_kernel; the scale, records and reduction kernels are outside the interval")
+    elif forward or engine == "mfma":
         ex = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"] * pairs / (g_avg * 1e-3) / 1e12
         busy = MFMA_BUSY.get((args.config, args.trig, plan["voxels_per_lane"])) if not forward else None
         if busy is not None and busy["kernel_sha256"] != kernel_source_sha(busy["source"]):
@@ -645,7 +710,7 @@ def main():
     traffic, traffic_detail = traffic_for(args.config + ("/forward" if forward else ""), args.trig,
                                           args.sum, engine, plan["voxels_per_lane"], g_avg)
     summ = args.sum
-    if engine == "mfma" and plan["tile"] >= (plan["padded_samples"] + plan["sample_splits"] - 1) // plan["sample_splits"] \
+    if engine in ("mfma", "mfma16") and plan["tile"] >= (plan["padded_samples"] + plan["sample_splits"] - 1) // plan["sample_splits"] \
             and args.sum == "blocked" and not forward:
         summ = "row-block"   # each launch row summed as one block, rows added in a fixed order
     res = {
@@ -688,6 +753,8 @@ def main():
         # voxel-sample pairs whose phase, sine and cosine the B vectors share
         res["per_trajectory_pass"] = {"value": round(value / p.B, 3), "unit": "Gpair/s",
                                       "is": "N M / step time (value = B N M / step time)"}
+    if not forward and engine == "mfma" and args.half_steps > 0:
+        res["half_split_engine"] = time_half_engine(p, t, D, args, stream)
     if not forward and not (engine == "valu" and plan["voxels_per_lane"] == 1) and args.method_steps > 0:
         res["method"] = time_per_pair_kernel(p, t, D, args, stream, mr)
     if args.cpu_seconds > 0:

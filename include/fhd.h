@@ -105,7 +105,16 @@ typedef enum fhd_engine {
                           or 64 (blocked or plain summation only).  Waves whose groups do
                           not sit at common offsets (any non-grid coordinates) are
                           evaluated per voxel on the vector ALU over the same launch
-                          rows, at about the rate of the VALU engine's per-voxel path */
+                          rows, at about the rate of the VALU engine's per-voxel path */,
+  FHD_ENGINE_MFMA16 = 3 /* half-split matrix-core kernels (F^H D and Q only; opt-in, never
+                          chosen by FHD_ENGINE_AUTO): the same factored sum in groups of
+                          128 / vectors voxels, each fp32 product formed from fp16 parts
+                          (x = hi + lo, hi = fp16(x), lo = fp16(x - hi); hi hi + hi lo +
+                          lo hi) on v_mfma_f32_16x16x32_f16 with fp32 accumulation, the
+                          factors scaled by a power of two into fp16 range.  Products
+                          carry ~2^-22 relative error (fp32: 2^-24); each launch row is
+                          one summation block (FHD_SUM_BLOCKED or PLAIN; tile is not
+                          used).  Irregular waves run per voxel in fp32 as above */
 } fhd_engine;
 
 /* Operation codes of fhd_workspace_bytes and fhd_describe_plan. */

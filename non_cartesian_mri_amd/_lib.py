@@ -32,6 +32,7 @@ FHD_OP_FORWARD = 2
 FHD_ENGINE_AUTO = 0
 FHD_ENGINE_VALU = 1
 FHD_ENGINE_MFMA = 2
+FHD_ENGINE_MFMA16 = 3
 
 FHD_STAGE_MU = 1
 FHD_STAGE_GATHER = 2

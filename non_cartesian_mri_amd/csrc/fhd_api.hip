@@ -61,7 +61,7 @@ struct Plan {
   int is_q;
   int trig;
   int sum;
-  int engine;          // FHD_ENGINE_VALU or FHD_ENGINE_MFMA
+  int engine;          // FHD_ENGINE_VALU, FHD_ENGINE_MFMA or FHD_ENGINE_MFMA16
   int tiles;           // MFMA: 32-column factor tiles per group phase (2 or 4)
   int V;               // group size of the first pass
   int stages;
@@ -211,7 +211,8 @@ fhd_status validate(int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
   const int V = o->voxels_per_lane;
   if (V != 0 && V != 1 && V != 2 && V != 4 && V != 8 && V != 16 && V != 32 && V != 64 && V != 128)
     return fail(FHD_ERR_INVALID_ARGUMENT, "voxels_per_lane must be 0, 1, 2, 4, 8, 16, 32, 64 or 128 (got %d)", V);
-  if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA)
+  if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA &&
+      o->engine != FHD_ENGINE_MFMA16)
     return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
   if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
   return FHD_OK;
@@ -229,11 +230,16 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     engine = (o->sum == FHD_SUM_KAHAN || (V != 0 && V <= 16)) ? FHD_ENGINE_VALU : FHD_ENGINE_MFMA;
   if (engine == FHD_ENGINE_MFMA && o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the MFMA engine sums blocked or plain, not Kahan");
+  const bool half = engine == FHD_ENGINE_MFMA16;
+  if (half && o->sum == FHD_SUM_KAHAN)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the half-split engine sums blocked or plain, not Kahan");
+  if (half && V != 0 && V != 128)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the half-split engine takes groups of 128 voxels (got %d)", V);
   if (engine == FHD_ENGINE_MFMA && V != 0 && V < 32)
     return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32, 64 or 128 voxels (got %d)", V);
   if (engine == FHD_ENGINE_VALU && V > 16)
     return fail(FHD_ERR_INVALID_ARGUMENT, "VALU group sizes are 1 to 16 voxels (got %d)", V);
-  const bool mfma = engine == FHD_ENGINE_MFMA;
+  const bool mfma = engine == FHD_ENGINE_MFMA || half;
   const int64_t pad = mfma ? ncmri::kMfmaChunk : ncmri::kUnroll;
   p.engine = engine;
   p.op = is_q ? FHD_OP_Q : FHD_OP_FHD;
@@ -252,7 +258,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
   p.tiles = 0;
   if (mfma) {
-    p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, p.mpad);
+    p.tiles = half ? 8 : (V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, p.mpad));
     V = 16 * p.tiles / p.bc[0];  // columns of a group: voxels x vectors
   } else if (p.batch > 1) {
     V = 1;  // batched passes amortise the phase over the vectors instead of voxels
@@ -295,10 +301,18 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   // tile folds, so its kernel keeps no running totals (3 waves per SIMD)
   if (mfma && p.tiles == 8 && o->trig == FHD_TRIG_HW && o->tile == 0 && p.tile < p.m_split)
     p.tile = p.m_split;
+  // the half-split engine's HW path sums each launch row as one block, as
+  // the four-sample engine's does; its accurate path folds tiles of ~sqrt(M)
+  if (half && o->trig == FHD_TRIG_HW && o->tile == 0) p.tile = p.m_split;
+  if (half && p.tile > p.m_split && p.m_split > 0) p.tile = p.m_split;
   p.ws_bytes = 0;
   p.hdr_bytes = mfma ? align256((size_t)p.mpad * ncmri::mfma_header_floats(p.trig) * sizeof(float)) : 0;
   for (int i = 0; i < p.npass; ++i) {
-    if (mfma) {
+    if (half) {
+      if (!ncmri::half_supported(p.bc[i])) return fail(FHD_ERR_INTERNAL, "no half-split kernel for BC=%d", p.bc[i]);
+      p.pass_bytes[i] = p.hdr_bytes + align256(ncmri::half_factor_bytes(p.mpad)) +
+                        align256((size_t)p.mpad * p.bc[i] * sizeof(fhd_c32)) + align256((2 + 256) * sizeof(float));
+    } else if (mfma) {
       if (!ncmri::mfma_supported(p.tiles, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for T=%d BC=%d", p.tiles, p.bc[i]);
       p.pass_bytes[i] = p.hdr_bytes + (size_t)p.mpad * ncmri::mfma_factor_floats(p.tiles) * sizeof(float);
     } else {
@@ -341,7 +355,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   fhd_status vst = validate(M, N, batch, o);
   if (vst != FHD_OK) return vst;
   const int V = o->voxels_per_lane;
-  if (o->engine == FHD_ENGINE_VALU)
+  if (o->engine == FHD_ENGINE_VALU || o->engine == FHD_ENGINE_MFMA16)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only");
   if (o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator sums blocked or plain, not Kahan");
@@ -656,7 +670,24 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
                          p.splits > 1 ? partial : nullptr};
     hipError_t e = hipSuccess;
     const char* what = "records";
-    if (p.engine == FHD_ENGINE_MFMA) {
+    if (p.engine == FHD_ENGINE_MFMA16) {
+      float* hdr = (float*)base;
+      char* wh = base + p.hdr_bytes;
+      float2* mu = (float2*)(wh + align256(ncmri::half_factor_bytes(p.mpad)));
+      float* scale = (float*)((char*)mu + align256((size_t)p.mpad * bc * sizeof(fhd_c32)));
+      if (p.stages & FHD_STAGE_MU) {
+        ncmri::HalfRecordArgs ha{{kx, ky, kz, x, y, z, (const float2*)phi, (const float2*)Dp, M, N, p.mpad, hdr,
+                                  nullptr},
+                                 wh, mu, scale};
+        e = ncmri::launch_half_records(is_q, p.trig, bc, ha, s);
+      }
+      if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
+        what = "gather";
+        ncmri::MfmaArgs ma{hdr, (const float*)wh, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+                           p.splits > 1 ? partial : nullptr, flags, mu, scale};
+        e = ncmri::launch_half_gather(p.trig, bc, p.splits, ma, s);
+      }
+    } else if (p.engine == FHD_ENGINE_MFMA) {
       float* hdr = (float*)base;
       float* wb = (float*)(base + p.hdr_bytes);
       if (p.stages & FHD_STAGE_MU) {
@@ -767,6 +798,7 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->record_dwords = p.npass == 0 ? 0
                           : p.op == FHD_OP_FORWARD ? 4 + ncmri::mfma_factor_floats(p.tiles)
                           : p.engine == FHD_ENGINE_MFMA ? ncmri::mfma_record_dwords(p.trig, p.tiles)
+                          : p.engine == FHD_ENGINE_MFMA16 ? ncmri::mfma_header_floats(p.trig) + 384 + 2 * p.bc[0]
                                                          : ncmri::record_dwords(p.is_q, p.trig, p.V, p.bc[0]);
     info->padded_samples = p.mpad;
     info->workspace_bytes = p.ws_bytes;

@@ -132,6 +132,33 @@ struct MfmaArgs {
   int32_t* flags;        // [waves]: 1 when the gather wave's groups sit at common
                          // offsets (written by the gather's row 0, read by the
                          // direct kernel, which then skips the wave)
+  // half-split engine only (nullptr otherwise)
+  const float2* mu;      // [mpad][BC] Mu_b of each sample in fp32 (the direct kernel's weights)
+  const float* scale;    // [2]: the factors' scale 2^e and its inverse (of a [2 + 256] buffer)
+};
+
+// ---------------------------------------------------------------------------
+// Half-split matrix-core engine (F^H D and Q, groups of 128 / BC voxels, 16
+// groups per wave as the four-sample engine): every fp32 product is formed
+// from fp16 parts, x = hi + lo with hi = fp16(x) and lo = fp16(x - hi), as
+// hi_a hi_b + hi_a lo_b + lo_a hi_b on v_mfma_f32_16x16x32_f16 (K = 32
+// samples), accumulated in fp32.  The factors are scaled by a power of two
+// 2^e that puts the largest near 2^14 (fp16 range), undone at the store.
+// Records per pass: headers as the four-sample engine; factor parts per
+// 32-sample block q: for tile t < 8 (16 complex columns cc = 16 t + c),
+// product u < 3 (fr, fi, fr + fi) and part s < 2 (hi, lo), 64 lanes x 8 fp16
+// (lane c + 16 (k / 8) holds samples 32 q + k, k = 8 (lane / 16) .. + 7) at
+// wh[(((q * 8 + t) * 3 + u) * 2 + s) * 64 + lane] (16 bytes each; 1536 bytes
+// per sample); Mu_b per sample in fp32 for the direct kernel; the scale pair.
+constexpr int kHalfChunk = 32;    // samples per chunk: one MFMA K block (divides kMfmaChunk)
+constexpr int kHalfWaves = 8;     // waves per workgroup (one workgroup per CU: 96 KB of LDS)
+inline constexpr size_t half_factor_bytes(int64_t mpad) { return (size_t)mpad * 1536; }
+
+struct HalfRecordArgs {
+  MfmaRecordArgs r;      // hdr as the four-sample engine; r.wb unused
+  void* wh;              // factor parts (uint4 units), see above
+  float2* mu;            // [mpad][BC]
+  float* scale;          // [2 + 256]: the scale pair, then per-workgroup maxima
 };
 
 // ---------------------------------------------------------------------------
@@ -175,6 +202,10 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
                                hipStream_t s);
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,
                               hipStream_t s);
+// Half-split engine: scale, records; gather (regular waves) + direct kernel.
+bool half_supported(int BC);
+hipError_t launch_half_records(int is_q, int trig, int BC, const HalfRecordArgs& a, hipStream_t s);
+hipError_t launch_half_gather(int trig, int BC, int32_t splits, const MfmaArgs& a, hipStream_t s);
 bool mfma_supported(int T, int BC);
 
 }  // namespace ncmri

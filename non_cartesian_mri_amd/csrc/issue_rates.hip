@@ -2,8 +2,10 @@
 // model: FP32 FMA throughput, v_sin_f32 throughput, whether transcendentals
 // share the VALU issue port with FMAs (mixed loops), whether the group-phase
 // VALU work overlaps FP32 MFMAs (the matrix-core gather's inner loop with and
-// without it, for both MFMA shapes), the shader clock, and the absolute error
-// of v_sin_f32/v_cos_f32 and of sincospif over one turn.
+// without it, for both MFMA shapes), the same inner loop with its products
+// formed from fp16 high/low parts on the fp16 matrix cores (a design option
+// weighed and not built), the shader clock, and the absolute error of
+// v_sin_f32/v_cos_f32 and of sincospif over one turn.
 // Standalone program: built by non_cartesian_mri_amd/build.py
 // (build_issue_rates) and run by `python bench.py --issue-rates`.
 #include <hip/hip_runtime.h>
@@ -105,6 +107,90 @@ __global__ void __launch_bounds__(512) k_mfma_mix(float* out, int blocks_per_wav
     for (int t = 0; t < NT; ++t)
       for (int v = 0; v < (KS == 2 ? 16 : 4); ++v) sum += acc[u][t][v];
   if (blocks_per_wave < 0) { occupancy_pad[threadIdx.x] = sum; __syncthreads(); sum += occupancy_pad[lane]; }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+// The matrix-core gather's inner loop with each fp32 product formed from fp16
+// parts: x = hi + lo (hi = fp16(x), lo = fp16(x - hi)), x y ~ hi_x hi_y +
+// hi_x lo_y + lo_x hi_y with fp32 accumulation, on v_mfma_f32_16x16x32_f16
+// (K = 32 samples per MFMA; A[i][k] = lane i + 16 (k / 8), element k % 8).
+// Per 32-sample block a wave evaluates 8 group phases per lane (16 groups),
+// splits (c + s, c - s, s) into hi / lo, reads the B parts of 8 tiles of 16
+// columns from LDS (3 products x 2 parts, 16 bytes per lane each) and issues
+// 8 x 3 x 3 = 72 MFMAs (16 cycles each): the four-sample engine's pairs per
+// block (16 groups x 128 columns x 32 samples).  STAGE 0: MFMAs only; 1: with
+// the phases and splits; 2: also the B parts from LDS.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+template <int STAGE>
+__global__ void __launch_bounds__(512) k_mfma16(float* out, int blocks_per_wave, float k0, float k1, float k2) {
+  constexpr int CT = 8;
+  __shared__ uint4 lb[CT * 6 * 64];
+  __shared__ float hdr[32 * 3];
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < CT * 6 * 64; i += 512) {
+    const unsigned v = 0x3c003c00u ^ (unsigned)(i & 7);
+    lb[i] = make_uint4(v, v, v, v);
+  }
+  for (int i = threadIdx.x; i < 96; i += 512) hdr[i] = (i % 3 == 0 ? k0 : i % 3 == 1 ? k1 : k2) * (1 + i);
+  __syncthreads();
+  const float gx = (float)(lane & 15) - 8.0f, gy = 3.0f, gz = -5.0f;
+  f32x4_t acc[3][CT];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int t = 0; t < CT; ++t) acc[u][t] = f32x4_t{};
+  half8_t A[3][2];
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { A[u][0][e] = (_Float16)(0.01f * (lane + e + u)); A[u][1][e] = (_Float16)0.0f; }
+  float hk = k0;
+  for (int q = 0; q < blocks_per_wave; ++q) {
+    if constexpr (STAGE >= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float* h = &hdr[(8 * (lane >> 4) + e) * 3];
+        const float ph = __builtin_fmaf(h[2], gz, __builtin_fmaf(h[1], gy, h[0] * gx + hk));
+        const float f = __builtin_amdgcn_fractf(ph);
+        const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+        const float v[3] = {cs + sn, cs - sn, sn};
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const _Float16 hi = (_Float16)v[u];
+          A[u][0][e] = hi;
+          A[u][1][e] = (_Float16)(v[u] - (float)hi);
+        }
+      }
+      asm volatile("" : "+v"(hk));
+    }
+#pragma unroll
+    for (int t = 0; t < CT; ++t) {
+      half8_t B[3][2];
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if constexpr (STAGE >= 2) {
+            const uint4 w = lb[((t * 3 + u) * 2 + s) * 64 + lane];
+            B[u][s] = *reinterpret_cast<const half8_t*>(&w);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) B[u][s][e] = (_Float16)(0.5f + 0.001f * (t + u + s + e));
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u][0], B[u][0], acc[u][t], 0, 0, 0);
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u][0], B[u][1], acc[u][t], 0, 0, 0);
+        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u][1], B[u][0], acc[u][t], 0, 0, 0);
+      }
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int t = 0; t < CT; ++t) sum += acc[u][t][0] + acc[u][t][3];
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
@@ -240,6 +326,20 @@ int main() {
     }
     MFMA_MIX(2, 2, 256, 70 * 1024, "32x32x2 (2 samples, 6 MFMAs per phase)", 64)
     MFMA_MIX(4, 8, 512, 100 * 1024, "16x16x4 (4 samples, 24 MFMAs per phase)", 32)
+  }
+  // the same work per pair with fp16 high/low products (one 8-wave workgroup per CU)
+  {
+    const int bpw = 2048;
+    double t[3];
+    t[0] = time_it([&] { hipLaunchKernelGGL(k_mfma16<0>, dim3(CU), dim3(512), 0, 0, out, bpw, 0.013f, 0.027f, -0.031f); }, 5);
+    t[1] = time_it([&] { hipLaunchKernelGGL(k_mfma16<1>, dim3(CU), dim3(512), 0, 0, out, bpw, 0.013f, 0.027f, -0.031f); }, 5);
+    t[2] = time_it([&] { hipLaunchKernelGGL(k_mfma16<2>, dim3(CU), dim3(512), 0, 0, out, bpw, 0.013f, 0.027f, -0.031f); }, 5);
+    CK(hipGetLastError());
+    const double pairs = (double)CU * 8 * bpw * 16 * 128 * 32;
+    const double ideal = (double)CU * 8 * bpw * 72 * 16 / (CU * 4 * 2.4e9);
+    printf("MB-MFMA16 fp16 hi/lo 16x16x32 (32 samples, 72 MFMAs per 8 phases): MFMA only %.3e pairs/s (matrix busy %.3f); "
+           "+ phases and splits %.3e; + B parts from LDS %.3e pairs/s (%.0f SIMD-cycles per 32-sample block over %d MFMA-cycles)\n",
+           pairs / t[0], ideal / t[0], pairs / t[1], pairs / t[2], t[2] * CU * 4 * 2.4e9 / ((double)CU * 8 * bpw), 72 * 16);
   }
   // accuracy of builtins on r in [0,1)
   {

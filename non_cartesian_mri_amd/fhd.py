@@ -16,7 +16,8 @@ from . import _lib
 
 _TRIG = {"accurate": _lib.FHD_TRIG_ACCURATE, "hw": _lib.FHD_TRIG_HW}
 _SUM = {"blocked": _lib.FHD_SUM_BLOCKED, "kahan": _lib.FHD_SUM_KAHAN, "plain": _lib.FHD_SUM_PLAIN}
-_ENGINE = {"auto": _lib.FHD_ENGINE_AUTO, "valu": _lib.FHD_ENGINE_VALU, "mfma": _lib.FHD_ENGINE_MFMA}
+_ENGINE = {"auto": _lib.FHD_ENGINE_AUTO, "valu": _lib.FHD_ENGINE_VALU, "mfma": _lib.FHD_ENGINE_MFMA,
+           "mfma16": _lib.FHD_ENGINE_MFMA16}
 _STAGES = {"all": _lib.FHD_STAGE_ALL, "mu": _lib.FHD_STAGE_MU, "gather": _lib.FHD_STAGE_GATHER,
            "reduce": _lib.FHD_STAGE_REDUCE,
            "gather+reduce": _lib.FHD_STAGE_GATHER | _lib.FHD_STAGE_REDUCE}

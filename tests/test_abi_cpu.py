@@ -120,7 +120,7 @@ def test_stage_combinations(lib):
     ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 48),
     ("voxels_per_lane", 256),
     ("tile", -4), ("stages", 8), ("sample_splits", -1), ("sample_splits", 1025),
-    ("engine", 3), ("engine", -1), ("reserved", 1),
+    ("engine", 4), ("engine", -1), ("reserved", 1),
 ])
 def test_bad_options(lib, field, value):
     assert _fhd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
@@ -135,6 +135,11 @@ def test_engine_option_conflicts(lib):
     assert b"MFMA group sizes" in lib.fhd_last_error()
     assert _fhd(lib, opts=_opts(engine=_lib.FHD_ENGINE_VALU, voxels_per_lane=32)) == E
     assert b"VALU group sizes" in lib.fhd_last_error()
+    # the half-split engine: blocked or plain sums, groups of 128 voxels, F^H D and Q only
+    assert _fhd(lib, opts=_opts(engine=_lib.FHD_ENGINE_MFMA16, sum=_lib.FHD_SUM_KAHAN)) == E
+    assert b"half-split" in lib.fhd_last_error()
+    assert _fhd(lib, opts=_opts(engine=_lib.FHD_ENGINE_MFMA16, voxels_per_lane=64)) == E
+    assert b"groups of 128" in lib.fhd_last_error()
 
 
 def test_workspace_errors(lib):
@@ -287,6 +292,26 @@ def test_describe_plan_valu(lib):
     info = _lib.FhdPlanInfo()
     assert lib.fhd_describe_plan(-1, 4, 1, 0, None, ctypes.byref(info)) == _lib.FHD_ERR_INVALID_ARGUMENT
     assert lib.fhd_describe_plan(4, 4, 1, 0, None, None) == _lib.FHD_ERR_INVALID_ARGUMENT
+
+
+def test_describe_plan_half_split(lib):
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan, fhd_workspace_bytes
+    # groups of 128 / vectors voxels; the HW path sums each launch row as one
+    # block (tile = the row), the accurate path folds tiles of ~sqrt(M);
+    # records: header + 1536 bytes of fp16 factor parts + Mu of each vector in fp32
+    for trig, hf in (("hw", 4), ("accurate", 8)):
+        p = fhd_describe_plan(262144, 128 ** 3, engine="mfma16", trig=trig)
+        assert p["engine"] == _lib.FHD_ENGINE_MFMA16 and p["voxels_per_lane"] == 128
+        assert p["record_dwords"] == hf + 384 + 2
+        assert p["padded_samples"] == 262144
+        assert p["tile"] == (262144 // p["sample_splits"] if trig == "hw" else 512)
+    b = fhd_describe_plan(500001, 96 ** 3, 16, engine="mfma16")
+    assert b["voxels_per_lane"] == 8 and b["passes"] == 1 and b["padded_samples"] == 500032
+    assert fhd_describe_plan(1000, 100, engine="mfma16", sum="plain")["sample_splits"] == 1
+    # workspace: headers, factor parts, Mu, the scale pair, partial sums, flags
+    assert fhd_workspace_bytes(262144, 128 ** 3, engine="mfma16", trig="accurate") == p["workspace_bytes"] > 0
+    with pytest.raises(Exception):
+        fhd_describe_plan(1000, 4096, op="forward", engine="mfma16")
 
 
 def test_describe_plan_mfma(lib):

@@ -47,7 +47,7 @@ def _problem_and_ref(name, oracle_mod):
     return _cache[name]
 
 
-ENGINES = ["auto", "valu"]   # auto = the matrix-core engine for these options
+ENGINES = ["auto", "valu", "mfma16"]   # auto = the matrix-core engine for these options; mfma16 the half-split one
 
 
 @pytest.mark.parametrize("engine", ENGINES)
