@@ -112,9 +112,11 @@ typedef enum fhd_engine {
                           (x = hi + lo, hi = fp16(x), lo = fp16(x - hi); hi hi + hi lo +
                           lo hi) on v_mfma_f32_16x16x32_f16 with fp32 accumulation, the
                           factors scaled by a power of two into fp16 range.  Products
-                          carry ~2^-22 relative error (fp32: 2^-24); each launch row is
-                          one summation block (FHD_SUM_BLOCKED or PLAIN; tile is not
-                          used).  Irregular waves run per voxel in fp32 as above */
+                          carry ~2^-22 relative error (fp32: 2^-24).  FHD_SUM_BLOCKED
+                          or PLAIN: on the HW path each launch row is one summation
+                          block; the accurate path folds tiles of about sqrt(M)
+                          samples (tile rounds up to a multiple of 32).  Irregular
+                          waves run per voxel in fp32 as above */
 } fhd_engine;
 
 /* Operation codes of fhd_workspace_bytes and fhd_describe_plan. */
