@@ -45,6 +45,21 @@ __device__ __forceinline__ void split_half(float x, _Float16& hi, _Float16& lo) 
   lo = (_Float16)(x - (float)hi);
 }
 
+// Two values at once: hi = (fp16(x0), fp16(x1)) packed by one conversion,
+// and lo = fp16(x - hi) formed by the mixed-precision FMA, which reads the
+// fp16 hi from either half of the packed register, adds x in fp32 (exact:
+// x - hi is representable) and rounds once to fp16 into the low or high
+// half of lo: the same bits as split_half, in 3 instructions instead of 8.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const half2v h = {(_Float16)x0, (_Float16)x1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(hi), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l) : "v"(hi), "v"(x1));
+  lo = l;
+}
+
 // The factors' scale: 2^e with sqrt(2) max_m,b |Mu_b[m]| 2^e <= 2^14, so that
 // every factor part (|fr|, |fi| <= |Mu|, |fr + fi| <= sqrt(2) |Mu|) stays
 // below fp16's 65504 with room for rounding.  Two passes: kHalfScaleBlocks
@@ -228,15 +243,19 @@ struct HalfGather {
                                                int lane, float gx, float gy, float gz, f32x4 (&acc)[3][T]) {
     half8 ah[3], al[3];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float av[3];
-      group_entries<TRIG>(hb + (4 * e + (lane >> 4)) * HF, gx, gy, gz, av);   // sample 8 (lane / 16) + e
+    for (int p = 0; p < 4; ++p) {
+      float av0[3], av1[3];   // samples 8 (lane / 16) + 2 p and + 2 p + 1
+      group_entries<TRIG>(hb + (4 * (2 * p) + (lane >> 4)) * HF, gx, gy, gz, av0);
+      group_entries<TRIG>(hb + (4 * (2 * p + 1) + (lane >> 4)) * HF, gx, gy, gz, av1);
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        _Float16 hi, lo;
-        split_half(av[u], hi, lo);
-        ah[u][e] = hi;
-        al[u][e] = lo;
+        uint32_t hi, lo;
+        split_pair(av0[u], av1[u], hi, lo);
+        const half2v h = __builtin_bit_cast(half2v, hi), l = __builtin_bit_cast(half2v, lo);
+        ah[u][2 * p] = h[0];
+        ah[u][2 * p + 1] = h[1];
+        al[u][2 * p] = l[0];
+        al[u][2 * p + 1] = l[1];
       }
     }
 #pragma unroll

@@ -121,6 +121,7 @@ __global__ void __launch_bounds__(512) k_mfma_mix(float* out, int blocks_per_wav
 // block (16 groups x 128 columns x 32 samples).  STAGE 0: MFMAs only; 1: with
 // the phases and splits; 2: also the B parts from LDS.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 template <int STAGE>
 __global__ void __launch_bounds__(512) k_mfma16(float* out, int blocks_per_wave, float k0, float k1, float k2) {
   constexpr int CT = 8;
@@ -147,20 +148,35 @@ __global__ void __launch_bounds__(512) k_mfma16(float* out, int blocks_per_wave,
   float hk = k0;
   for (int q = 0; q < blocks_per_wave; ++q) {
     if constexpr (STAGE >= 1) {
+      float v[8][3];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float* h = &hdr[(8 * (lane >> 4) + e) * 3];
         const float ph = __builtin_fmaf(h[2], gz, __builtin_fmaf(h[1], gy, h[0] * gx + hk));
         const float f = __builtin_amdgcn_fractf(ph);
         const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
-        const float v[3] = {cs + sn, cs - sn, sn};
+        v[e][0] = cs + sn;
+        v[e][1] = cs - sn;
+        v[e][2] = sn;
+      }
+      // hi pairs by one packed conversion, lo = fp16(x - hi) by the
+      // mixed-precision FMA into either half (the gather's split)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
-          const _Float16 hi = (_Float16)v[u];
-          A[u][0][e] = hi;
-          A[u][1][e] = (_Float16)(v[u] - (float)hi);
+          const half2_t h = {(_Float16)v[2 * p][u], (_Float16)v[2 * p + 1][u]};
+          const unsigned hb = __builtin_bit_cast(unsigned, h);
+          unsigned lb2;
+          asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lb2) : "v"(hb), "v"(v[2 * p][u]));
+          asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+              : "+v"(lb2) : "v"(hb), "v"(v[2 * p + 1][u]));
+          const half2_t l = __builtin_bit_cast(half2_t, lb2);
+          A[u][0][2 * p] = h[0];
+          A[u][0][2 * p + 1] = h[1];
+          A[u][1][2 * p] = l[0];
+          A[u][1][2 * p + 1] = l[1];
         }
-      }
       asm volatile("" : "+v"(hk));
     }
 #pragma unroll
