@@ -55,10 +55,10 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # the kernel source it was taken on, like TRAFFIC below)
 MFMA_BUSY = {
     ("fhd_128cube_262144_spirals", "hw", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a", "busy": 0.923,
+        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257", "busy": 0.925,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a", "busy": 0.849,
+        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257", "busy": 0.851,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
 }
 
@@ -80,29 +80,33 @@ def method_roofline(kind: str, B: int) -> dict:
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a",
-        "fetch_bytes": 1806249.6 * 1024 * 2.0, "write_bytes": 262153.5 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257",
+        "fetch_bytes": 1801995.4 * 1024 * 2.0, "write_bytes": 262153.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "b7e9228697b73d9a",
-        "fetch_bytes": 1784694.1 * 1024 * 2.0, "write_bytes": 262152.1 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257",
+        "fetch_bytes": 1785493.0 * 1024 * 2.0, "write_bytes": 262152.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "b0fa4414bc124d10",
-        "fetch_bytes": 1577159.7 * 1024 * 2.0, "write_bytes": 31170.2 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "aed6bcc555a67ff0",
+        "fetch_bytes": 1577176.3 * 1024 * 2.0, "write_bytes": 31394.2 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "b0fa4414bc124d10",
-        "fetch_bytes": 1519603.0 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "aed6bcc555a67ff0",
+        "fetch_bytes": 1521180.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "eff1a443cd376689",
-        "fetch_bytes": 984433.6 * 1024 * 2.0, "write_bytes": 262149.7 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "22004205ff484185",
+        "fetch_bytes": 984574.4 * 1024 * 2.0, "write_bytes": 262145.7 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "eff1a443cd376689",
-        "fetch_bytes": 1047473.6 * 1024 * 2.0, "write_bytes": 262151.1 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "22004205ff484185",
+        "fetch_bytes": 1047842.2 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma16", 128): {
+        "source": "fhd_half.hip", "kernel_sha256": "b74be4bb6a33f536",
+        "fetch_bytes": 2298994.8 * 1024 * 2.0, "write_bytes": 262148.0 * 1024 * 1.0,
+        "profile": "profiles/half_gather_128cubed_x_262144_kernel_stats.md"},
     # the whole gridding reconstruction (sort, deposit + x transform, y and z passes)
     ("fhd_128cube_262144_spirals/gridding", "-", "-", "-", 0): {
         "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "0235fdc59edd0488",
@@ -515,6 +519,7 @@ def time_half_engine(p, t, D, args, stream) -> dict:
     gather alone, timed with HIP events on its stream."""
     import torch
     from non_cartesian_mri_amd import fhd_compute, fhd_workspace_bytes, q_compute
+    from non_cartesian_mri_amd.fhd import fhd_describe_plan
     is_q = p.kind == "q"
     opts = dict(trig=args.trig, sum=args.sum, engine="mfma16")
     ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, is_q=is_q, **opts)), dtype=torch.uint8,
@@ -547,12 +552,15 @@ def time_half_engine(p, t, D, args, stream) -> dict:
     gather = float(np.mean([b.elapsed_time(c) for a, b, c, d in ev]))
     pairs = p.N * p.M * p.B
     ex = 18 * pairs / (gather * 1e-3) / 1e12
+    plan = fhd_describe_plan(p.M, p.N, p.B, op="q" if is_q else "fhd", **opts)
+    traffic, traffic_detail = traffic_for(args.config, args.trig, args.sum, "mfma16", plan["voxels_per_lane"], gather)
     return {"engine": "mfma16", "steps": args.half_steps,
             "value": round(pairs / (step * 1e-3) / 1e9, 3), "unit": "Gpair/s", "step_event_median_ms": round(step, 4),
             "gather_event_mean_ms": round(gather, 4),
             "gather_pairs_per_s": round(pairs / (gather * 1e-3), 1),
             "achieved": round(ex, 3), "peak": FP16_PEAK_TFLOPS, "unit_engine": "TFLOP/s",
             "frac": round(ex / FP16_PEAK_TFLOPS, 4), "executed_flop_per_pair": 18,
+            "traffic": None if traffic is None else round(traffic, 3), "traffic_detail": traffic_detail,
             "note": "opt-in engine (not the default that value reports): the same factored sum with every fp32 "
                     "product formed from fp16 parts (hi hi + hi lo + lo hi) on v_mfma_f32_16x16x32_f16 with fp32 "
                     "accumulation; parity against the oracle at the fp32 bars in tests/test_gpu_half.py and "
