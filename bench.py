@@ -333,9 +333,9 @@ def bench_cg(args, p, t, D, dev) -> dict:
         "residual": {"first": float(rr[0]), "last": float(rr[-1])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic, 3),
-                     "traffic_unit": "GB/s (HBM bytes per reconstruction from FETCH_SIZE/WRITE_SIZE / its time)",
-                     "traffic_detail": traffic_detail,
+                     "traffic": None,
+                     "traffic_unit": "GB/s (HBM bytes per application from FETCH_SIZE/WRITE_SIZE / time)",
+                     "traffic_detail": None,
                      "kernel": "the normal operator timed as one unit: x, y transforms, z transform with the "
                                "spectral product, inverse y, inverse x with the regulariser and <p, Ap>",
                      "algorithmic_bytes": op_bytes},
@@ -423,7 +423,10 @@ def bench_gridding(args, p, t, D, dev) -> dict:
                    "samples": p.M, "parallelism": "single GPU"},
         "timing_ms": {"step_event_median": round(step_ms, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 3),
+                     "traffic_unit": "GB/s (HBM bytes per reconstruction from FETCH_SIZE/WRITE_SIZE / its time)",
+                     "traffic_detail": traffic_detail,
                      "kernel": "the whole reconstruction timed as one unit (plane sort of the deposits, LDS tile "
                                "deposit fused with the x transform, y and z FFT passes)",
                      "algorithmic_bytes": alg},

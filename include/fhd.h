@@ -295,7 +295,8 @@ fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const float* kz
                                float* Qhat, const fhd_opts* opts, void* stream);
 
 /* Workspace bytes of fhd_normal_apply / fhd_cg_solve (0 for an invalid grid):
- * the nz x py x px working grid of the transforms, three images and two
+ * two nz x py x px working grids of the transforms (the second holds the y
+ * transform's output in the blocks the z pass reads), three images and two
  * sets of 1024 dot-product partial sums. */
 size_t fhd_cg_workspace_bytes(int32_t nx, int32_t ny, int32_t nz);
 

@@ -954,7 +954,7 @@ NCMRI_API fhd_status fhd_normal_apply(const float* Qhat, int32_t nx, int32_t ny,
     st = check_device();
     if (st != FHD_OK) return st;
     ncmri::CgWorkspace w = ncmri::cg_workspace(workspace, d);
-    if (const char* e = ncmri::normal_apply(d, Qhat, lambda, (const float2*)p, (float2*)Ap, w.T, nullptr,
+    if (const char* e = ncmri::normal_apply(d, Qhat, lambda, (const float2*)p, (float2*)Ap, w.T, w.T2, nullptr,
                                             (hipStream_t)stream))
       return fail(FHD_ERR_HIP, "normal operator: %s", e);
     return FHD_OK;

@@ -32,6 +32,7 @@ inline ToeplitzDims toeplitz_dims(int nx, int ny, int nz) {
 // Device buffers of one CG solve / normal-operator application.
 struct CgWorkspace {
   float2* T;        // [nz][py][px] working grid of the transforms
+  float2* T2;       // the same nz py px values after the y transform, in z-line blocks (fhd_cg.hip)
   float2* r;        // [n] residual
   float2* p;        // [n] search direction
   float2* Ap;       // [n] operator applied to p
@@ -44,13 +45,14 @@ constexpr int kCgPartials = 1024;
 
 inline size_t cg_align(size_t b) { return (b + 255) / 256 * 256; }
 inline size_t cg_workspace_bytes(const ToeplitzDims& d) {
-  return cg_align((size_t)d.lines() * 8) + 3 * cg_align((size_t)d.voxels() * 8) +
+  return 2 * cg_align((size_t)d.lines() * 8) + 3 * cg_align((size_t)d.voxels() * 8) +
          2 * cg_align(kCgPartials * sizeof(double)) + cg_align(8 * sizeof(double));
 }
 inline CgWorkspace cg_workspace(void* base, const ToeplitzDims& d) {
   char* c = (char*)base;
   CgWorkspace w;
   w.T = (float2*)c;  c += cg_align((size_t)d.lines() * 8);
+  w.T2 = (float2*)c; c += cg_align((size_t)d.lines() * 8);
   w.r = (float2*)c;  c += cg_align((size_t)d.voxels() * 8);
   w.p = (float2*)c;  c += cg_align((size_t)d.voxels() * 8);
   w.Ap = (float2*)c; c += cg_align((size_t)d.voxels() * 8);
@@ -70,7 +72,7 @@ inline size_t toeplitz_scratch_bytes(const ToeplitzDims& d) { return (size_t)d.s
 const char* toeplitz_spectrum(const ToeplitzDims& d, const float2* Q2, float2* G, float* Qhat,
                               hipStream_t s);
 const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* p,
-                         float2* Ap, float2* T, double* partial, hipStream_t s);
+                         float2* Ap, float2* T, float2* T2, double* partial, hipStream_t s);
 const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* b, float2* x,
                    int iters, double* resid, const CgWorkspace& w, hipStream_t s);
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s);

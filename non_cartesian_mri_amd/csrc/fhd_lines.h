@@ -11,8 +11,10 @@ namespace ncmri {
 
 // One axis of transforms over a batch of lines.  Line c sits at outer index
 // o = c / inner and inner index w = c % inner; its point i is at
-// o * os + w * ws + i * es of the array (in and out may be the same array:
-// every line is read whole before any of it is written).
+// o * os + (w >> sh) * wh + (w mod 2^sh) * ws + i * es of the array (sh = 30,
+// wh = 0 for the plain o * os + w * ws; a smaller sh splits w into blocks of
+// 2^sh lines that sit wh apart).  In and out may be the same array when they
+// share a layout: every line is read whole before any of it is written.
 struct LinePass {
   const float2* in;
   float2* out;
@@ -23,6 +25,8 @@ struct LinePass {
   int inner;
   int64_t in_os, in_ws, in_es;
   int64_t out_os, out_ws, out_es;
+  int in_sh, out_sh;
+  int64_t in_wh, out_wh;
   int q_shift;
   int64_t q_bs;
   int nin;         // points read per line (the rest are zero)

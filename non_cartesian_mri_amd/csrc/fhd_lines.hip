@@ -13,10 +13,11 @@
 namespace ncmri {
 namespace {
 
-// Offset of line c: outer index o = c / inner, inner index w = c mod inner.
-__device__ __forceinline__ int64_t line_offset(int c, int inner, int64_t os, int64_t ws) {
+// Offset of line c: outer index o = c / inner, inner index w = c mod inner,
+// w split into blocks of 2^sh lines wh apart.
+__device__ __forceinline__ int64_t line_offset(int c, int inner, int64_t os, int64_t ws, int sh, int64_t wh) {
   const int o = c / inner, w = c - o * inner;
-  return o * os + w * ws;
+  return o * os + (int64_t)(w >> sh) * wh + (int64_t)(w & ((1 << sh) - 1)) * ws;
 }
 
 // Inputs of the first stage: point i of line c0 + l, zero past nin points
@@ -25,11 +26,13 @@ struct LineLoad {
   const float2* in;
   int c0, count, inner, nin;
   int64_t os, ws, es;
+  int sh;
+  int64_t wh;
   template <int RN, int STEP>
   __device__ __forceinline__ void get(int l, int j, float2* w) const {
     const int c = c0 + l;
     const bool ok = c < count;
-    const float2* p = in + (line_offset(ok ? c : 0, inner, os, ws) + j * es);
+    const float2* p = in + (line_offset(ok ? c : 0, inner, os, ws, sh, wh) + j * es);
     const int64_t st = (int64_t)STEP * es;
 #pragma unroll
     for (int r = 0; r < RN; ++r) {
@@ -44,11 +47,13 @@ struct LineStore {
   float2* out;
   int c0, count, inner, nout;
   int64_t os, ws, es;
+  int sh;
+  int64_t wh;
   template <int RN, int STEP>
   __device__ __forceinline__ void put(int l, int j, const float2* w) const {
     const int c = c0 + l;
     if (c >= count) return;
-    float2* p = out + (line_offset(c, inner, os, ws) + j * es);
+    float2* p = out + (line_offset(c, inner, os, ws, sh, wh) + j * es);
     const int64_t st = (int64_t)STEP * es;
 #pragma unroll
     for (int r = 0; r < RN; ++r) {
@@ -107,8 +112,8 @@ __global__ void __launch_bounds__((fft::Lds<N, layout<N, ROW, MODE>()>::kThreads
   fft::fill_twiddles<N>(tw);
   const int tile = grouped_tile<tile_group<N, ROW, MODE>()>((int)blockIdx.x);
   const int c0 = tile * L::kLines;   // past the last line (padding blocks): nothing read or written
-  const LineLoad load{a.in, c0, a.count, a.inner, a.nin, a.in_os, a.in_ws, a.in_es};
-  const LineStore store{a.out, c0, a.count, a.inner, a.nout, a.out_os, a.out_ws, a.out_es};
+  const LineLoad load{a.in, c0, a.count, a.inner, a.nin, a.in_os, a.in_ws, a.in_es, a.in_sh, a.in_wh};
+  const LineStore store{a.out, c0, a.count, a.inner, a.nout, a.out_os, a.out_ws, a.out_es, a.out_sh, a.out_wh};
   float2 v[fft::kPerThread];
   if constexpr (MODE == kLineFwdQInv) {
     static_assert(!ROW, "the spectral product runs on column tiles");
@@ -208,6 +213,8 @@ LinePass line_pass(const float2* in, float2* out, int64_t count, int64_t inner, 
   a.in_os = a.out_os = os;
   a.in_ws = a.out_ws = ws;
   a.in_es = a.out_es = es;
+  a.in_sh = a.out_sh = 30;
+  a.in_wh = a.out_wh = 0;
   a.q_shift = 0;
   a.q_bs = 0;
   a.nin = nin;

@@ -466,11 +466,11 @@ def test_reconstruction_sizes(lib):
     assert lib.fhd_toeplitz_bytes(513, 2, 2) == 0            # at most 512 voxels per axis
     assert lib.fhd_toeplitz_bytes(512, 512, 512) == 1024 ** 3 * 4
     n = 4 * 5 * 6
-    # working grid nz x py x px, three images, two sets of 1024 partial sums, CG state
-    assert lib.fhd_cg_workspace_bytes(4, 5, 6) == (a256(6 * 16 * 8 * 8) + 3 * a256(8 * n) + 2 * a256(8 * 1024)
+    # two working grids nz x py x px, three images, two sets of 1024 partial sums, CG state
+    assert lib.fhd_cg_workspace_bytes(4, 5, 6) == (2 * a256(6 * 16 * 8 * 8) + 3 * a256(8 * n) + 2 * a256(8 * 1024)
                                                     + a256(64))
     assert lib.fhd_cg_workspace_bytes(4, -1, 6) == 0
-    assert lib.fhd_cg_workspace_bytes(1, 1, 1) == a256(2 * 2 * 8) + 3 * 256 + 2 * 8192 + 256
+    assert lib.fhd_cg_workspace_bytes(1, 1, 1) == 2 * a256(2 * 2 * 8) + 3 * 256 + 2 * 8192 + 256
 
 
 def _toe(lib, M=16, nx=4, ny=4, nz=4, opts=None, **ptrs):
