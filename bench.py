@@ -109,18 +109,22 @@ TRAFFIC = {
         "profile": "profiles/half_gather_128cubed_x_262144_kernel_stats.md"},
     # the whole gridding reconstruction (sort, deposit + x transform, y and z passes)
     ("fhd_128cube_262144_spirals/gridding", "-", "-", "-", 0): {
-        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "0235fdc59edd0488",
-        "fetch_bytes": 25871.8 * 1024 * 2.0, "write_bytes": 59449.8 * 1024 * 1.0,
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "3f5564858fd83b41",
+        "fetch_bytes": 25875.8 * 1024 * 2.0, "write_bytes": 59449.8 * 1024 * 1.0,
         "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     ("fhd_512cube_262144_spirals/gridding", "-", "-", "-", 0): {
-        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "0235fdc59edd0488",
-        "fetch_bytes": 1380798.0 * 1024 * 2.0, "write_bytes": 3156022.2 * 1024 * 1.0,
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "3f5564858fd83b41",
+        "fetch_bytes": 1380804.8 * 1024 * 2.0, "write_bytes": 3156022.2 * 1024 * 1.0,
         "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "dade316886c918a3",
-        "fetch_bytes": 147718.1 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "f85bc62ac6983f44",
+        "fetch_bytes": 147709.8 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
         "profile": "profiles/cg_normal_operator_128cubed_kernel_stats.md"},
+    ("fhd_512cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "f85bc62ac6983f44",
+        "fetch_bytes": 9437528.5 * 1024 * 2.0, "write_bytes": 13639020.2 * 1024 * 1.0,
+        "profile": "profiles/scale_512cubed_summary.md"},
 }
 WORKLOADS = {
     "fhd_128cube_262144_spirals": "FhD 128^3 voxels x 262,144 stack-of-spirals samples (64 kz planes x 4096-point spirals), complex N(0,1) phi and D",
