@@ -34,16 +34,19 @@ def _both(p, d, **opts):
     return got.cpu().numpy().reshape(p.B, p.N), want.cpu().numpy().reshape(p.B, p.N)
 
 
+@pytest.mark.parametrize("engine", ["auto", "mfma16"])
 @pytest.mark.parametrize("trig", ["hw", "accurate"])
-def test_two_calls_in_a_row_second_smaller(oracle_mod, trig):
+def test_two_calls_in_a_row_second_smaller(oracle_mod, trig, engine):
+    # engine "mfma16": the half-split kernels, whose scale, factor parts and Mu
+    # also live in the array
     big = inputs.make_config("fhd_64cube_65536_radial")
     small = inputs.random_problem(901, M=2047, L=16, B=3)
     for p in (big, small):
-        print(f"[noalloc] {p.name} trig={trig} N={p.N} M={p.M} B={p.B}", flush=True)
-        got, want = _both(p, dev_problem(p), trig=trig)
+        print(f"[noalloc] {p.name} trig={trig} engine={engine} N={p.N} M={p.M} B={p.B}", flush=True)
+        got, want = _both(p, dev_problem(p), trig=trig, engine=engine)
         assert np.array_equal(got, want), f"{p.name}: noalloc differs from fhd_compute"
     ref = oracle_mod.fhd(small.kx, small.ky, small.kz, small.x, small.y, small.z, small.phi, small.D)
-    assert_close(got, ref, TOL[trig], f"noalloc {small.name} {trig}")
+    assert_close(got, ref, TOL[trig], f"noalloc {small.name} {trig} {engine}")
 
 
 def test_plan_lowered_to_fit_the_array():
