@@ -29,7 +29,7 @@ def lib():
 
 def test_candidates_have_valid_plans_and_metrics(lib):
     cs = tune.candidates(262144, 128 ** 3, grid_edge=128)
-    assert len(cs) == 3 * 7 * 6      # groups of 32, 64, 128 x rows x tiles
+    assert len(cs) == 3 * 7 * 7      # groups of 32, 64, 128 x rows x (6 tiles + the whole row)
     for c in cs:
         assert c.plan["sample_splits"] == c.sample_splits
         assert c.plan["voxels_per_lane"] == c.voxels_per_lane
