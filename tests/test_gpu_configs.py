@@ -114,7 +114,10 @@ def test_q_config(oracle_mod, name, trig, engine):
 
 def test_phantom_round_trip_psnr(oracle_mod):
     """Ellipsoid phantom -> analytic k-space on the radial trajectory -> F^H D with
-    density weights |k|^2: PSNR of the GPU image may drop at most 0.1 dB from the oracle's."""
+    density weights |k|^2: PSNR of the GPU image may drop at most 0.1 dB from the oracle's
+    (the drop the pages report for hardware trigonometry, tests/golden/pages_figures.json)."""
+    from tests.test_golden_cpu import psnr_drop_gate_db
+    gate = psnr_drop_gate_db()
     p = inputs.make_config("phantom_96cube_500001_radial")
     sl = p.extra["slices"]
     ref = oracle_mod.fhd(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, p.D, idx=sl)[0]
@@ -129,5 +132,5 @@ def test_phantom_round_trip_psnr(oracle_mod):
             ps = oracle_mod.psnr_db(I0, got, alpha)
             print(f"[psnr] oracle {ps_ref:.3f} dB, gpu {trig}/{engine} {ps:.3f} dB", flush=True)
             assert math.isfinite(ps_ref) and ps_ref > 5.0
-            assert ps_ref - ps <= 0.1
+            assert ps_ref - ps <= gate
             assert_close(got, ref, TOL[trig], f"phantom {trig} {engine}")
