@@ -345,15 +345,16 @@ def test_describe_plan_mfma(lib):
     # fill 2 waves per SIMD
     m64 = fhd_describe_plan(65536, 64 ** 3, trig="hw")
     assert m64["voxels_per_lane"] == 128 and m64["sample_splits"] == 16
-    # 32^3 x 2048: regular for every group size, but even 8 rows of the fewest,
-    # longest waves cannot fill the GPU -> the smallest groups
+    # 32^3 x 2048: regular for every group size, but even 16 rows (of 128
+    # samples, the shortest a matrix-core row takes) of the fewest, longest
+    # waves cannot fill the GPU -> the smallest groups, and the most rows
     tiny = fhd_describe_plan(2048, 32 ** 3, trig="hw")
-    assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 8 and tiny["tile"] == 256
+    assert tiny["voxels_per_lane"] == 32 and tiny["sample_splits"] == 16 and tiny["tile"] == 256
     # 48^3: 128 and 64 are neither divisors of a row nor whole rows of a plane
     assert fhd_describe_plan(65536, 48 ** 3, trig="hw")["voxels_per_lane"] == 32
     # fewer voxels than one group: still one wave; samples padded to the 32-sample chunk
     small = fhd_describe_plan(1000, 5, trig="hw")
-    assert small["padded_samples"] == 1024 and small["sample_splits"] == 4
+    assert small["padded_samples"] == 1024 and small["sample_splits"] == 8
     # batched, 16 vectors on 96^3: T = 8, groups of 8 voxels; the partial buffer cap gives 18 rows
     b16 = fhd_describe_plan(500001, 96 ** 3, batch=16)
     assert b16["voxels_per_lane"] == 8 and b16["sample_splits"] == 18 and b16["padded_samples"] == 500032
