@@ -925,8 +925,14 @@ NCMRI_API fhd_status fhd_toeplitz_kernel(const float* kx, const float* ky, const
     fhd_status result = FHD_OK;
     e = ncmri::launch_diff_grid(nx, ny, nz, coords, coords + n2, coords + 2 * n2, s);
     if (e != hipSuccess) result = fail(FHD_ERR_HIP, "difference grid kernel: %s", hipGetErrorString(e));
-    if (result == FHD_OK)   // Q on the difference grid through the library's Q path
-      result = run(1, kx, ky, kz, coords, coords + n2, coords + 2 * n2, phi, nullptr, Q2, M, n2, 1, opts, stream);
+    // Q on the difference grid through the library's Q path: the planes dz >= 0
+    // (the first half of the grid), the others by Hermitian symmetry
+    if (result == FHD_OK)
+      result = run(1, kx, ky, kz, coords, coords + n2, coords + 2 * n2, phi, nullptr, Q2, M, n2 / 2, 1, opts, stream);
+    if (result == FHD_OK) {
+      e = ncmri::launch_hermitian_fill(nx, ny, nz, (float2*)Q2, s);
+      if (e != hipSuccess) result = fail(FHD_ERR_HIP, "Hermitian fill kernel: %s", hipGetErrorString(e));
+    }
     if (result == FHD_OK) {
       if (const char* fe = ncmri::toeplitz_spectrum(d, (const float2*)Q2, G, Qhat, s))
         result = fail(FHD_ERR_HIP, "spectrum of Q: %s", fe);

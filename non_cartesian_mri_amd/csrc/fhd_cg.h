@@ -76,6 +76,9 @@ const char* normal_apply(const ToeplitzDims& d, const float* Qhat, float lambda,
 const char* cg_run(const ToeplitzDims& d, const float* Qhat, float lambda, const float2* b, float2* x,
                    int iters, double* resid, const CgWorkspace& w, hipStream_t s);
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s);
+// Q2's planes dz < 0 from the planes dz > 0 by Q(-d) = conj Q(d) (only the
+// first nz planes of Q2 need computing).
+hipError_t launch_hermitian_fill(int nx, int ny, int nz, float2* Q2, hipStream_t s);
 
 // Gridding reconstruction (fhd_grid.hip): image (complex [nz][ny][nx], each
 // axis a power of two in [2, kToeplitzMaxLen]) = the centred lattice inverse

@@ -62,6 +62,30 @@ diff_grid_kernel(int nx, int ny, int nz, float* x, float* y, float* z) {
   }
 }
 
+// Q(-d) = sum_m |phi_m|^2 exp(-i 2 pi k_m . d) = conj Q(d): the planes with
+// dz < 0 (index iz in (nz, 2 nz)) are the conjugates of the computed planes
+// dz = -(iz - 2 nz) in [1, nz), with dx, dy negated (index (2n - i) mod 2n).
+// Plane iz = nz (dz = -nz) is zeroed, and the entries dx = -nx or dy = -ny
+// (index nx or ny, whose negation is not on the grid) take another entry's
+// value: the embedding reads only differences |d| < n per axis.
+__global__ void __launch_bounds__(kThreads)
+hermitian_fill_kernel(float2* __restrict__ Q2, int nx, int ny, int nz) {
+  const int64_t plane = (int64_t)4 * nx * ny;
+  const int64_t n = plane * nz;                       // planes iz = nz .. 2 nz - 1
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const int iz = nz + (int)(i / plane);
+    const int64_t r = i - (int64_t)(iz - nz) * plane;
+    const int iy = (int)(r / (2 * nx)), ix = (int)(r - (int64_t)iy * 2 * nx);
+    float2 v = make_float2(0.0f, 0.0f);
+    if (iz > nz) {
+      const int sz = 2 * nz - iz, sy = iy == 0 ? 0 : 2 * ny - iy, sx = ix == 0 ? 0 : 2 * nx - ix;
+      const float2 q = Q2[((int64_t)sz * 2 * ny + sy) * 2 * nx + sx];
+      v = make_float2(q.x, -q.y);
+    }
+    Q2[(int64_t)iz * plane + r] = v;
+  }
+}
+
 // Index in the circular 2n grid of the difference held at padded index a
 // (a < n: d = a; a > P - n: d = a - P), or -1 where the padded grid is zero.
 __device__ __forceinline__ int embed_src(int a, int n, int P) {
@@ -412,6 +436,12 @@ hipError_t launch_crop(const ToeplitzDims& d, const float2* T, const float2* p, 
 }
 
 }  // namespace
+
+hipError_t launch_hermitian_fill(int nx, int ny, int nz, float2* Q2, hipStream_t s) {
+  const int64_t n = (int64_t)4 * nx * ny * nz;
+  hipLaunchKernelGGL(hermitian_fill_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, Q2, nx, ny, nz);
+  return hipGetLastError();
+}
 
 hipError_t launch_diff_grid(int nx, int ny, int nz, float* x, float* y, float* z, hipStream_t s) {
   const int64_t n2 = (int64_t)8 * nx * ny * nz;
