@@ -118,12 +118,12 @@ TRAFFIC = {
         "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "f85bc62ac6983f44",
-        "fetch_bytes": 147709.8 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "854d727e0e18b705",
+        "fetch_bytes": 147709.3 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
         "profile": "profiles/cg_normal_operator_128cubed_kernel_stats.md"},
     ("fhd_512cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "f85bc62ac6983f44",
-        "fetch_bytes": 9437528.5 * 1024 * 2.0, "write_bytes": 13639020.2 * 1024 * 1.0,
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "854d727e0e18b705",
+        "fetch_bytes": 9437532.7 * 1024 * 2.0, "write_bytes": 13639403.9 * 1024 * 1.0,
         "profile": "profiles/scale_512cubed_summary.md"},
 }
 WORKLOADS = {
