@@ -435,10 +435,10 @@ def test_forward_plan(lib):
     p64 = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw", voxels_per_lane=64)
     assert p64["record_dwords"] == 4 + 192 and p64["tile"] == 1024 and p64["workspace_bytes"] == pas(32768, 4)
     assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw") == p["workspace_bytes"]
-    # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 256 groups each)
+    # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 64 groups each)
     s = fhd_describe_plan(2048, 32 ** 3, op="forward", trig="hw")
-    assert s["voxels_per_lane"] == 32 and s["sample_splits"] == 4 and s["tile"] == 128
-    assert s["workspace_bytes"] == pas(1024, 2) + a256(4 * 2048 * 8)
+    assert s["voxels_per_lane"] == 32 and s["sample_splits"] == 16 and s["tile"] == 128
+    assert s["workspace_bytes"] == pas(1024, 2) + a256(16 * 2048 * 8)
     # batch 3 on 64^3: passes of 2 and 1 images, T = 8: groups of 64 and 128 voxels
     # (128 = two rows of a plane)
     b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1)
