@@ -643,13 +643,21 @@ def main():
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        stage("mu")
-        stage("gather")
-        stage("reduce")
+        stage("all")
     torch.cuda.synchronize()
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    # the timed steps: one whole call per step (records, gather, row reduction)
+    sev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for e0, e3 in sev:
+        e0.record(stream)
+        stage("all")
+        e3.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(d) for a, d in sev])
+    # the same steps again, one call per stage, to time the gather alone
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     for e0, e1, e2, e3 in ev:
         e0.record(stream)
         stage("mu")
@@ -659,8 +667,6 @@ def main():
         stage("reduce")
         e3.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(d) for a, b, c, d in ev])
     gather_ms = np.array([b.elapsed_time(c) for a, b, c, d in ev])
     mu_ms = np.array([a.elapsed_time(b) for a, b, c, d in ev])
     reduce_ms = np.array([c.elapsed_time(d) for a, b, c, d in ev])
