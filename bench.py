@@ -698,6 +698,10 @@ def main():
                        "v_mfma_f32_16x16x32_f16; the factors are scaled by a power of two into fp16 range"}
         kernel = ("half_gather_kernel: its launch rows in one step, timed alone with the (empty on a grid) "
                   "half_direct_kernel; the scale, records and reduction kernels are outside the interval")
+        if forward:
+            kernel = ("fwd_half_gather_kernel: its launch rows in one step, timed alone; the image packing, "
+                      "scale and fp16 parts, row reduction and (on a grid, empty) direct kernels are outside "
+                      "the interval")
     elif forward or engine == "mfma":
         ex = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"] * pairs / (g_avg * 1e-3) / 1e12
         busy = MFMA_BUSY.get((args.config, args.trig, plan["voxels_per_lane"])) if not forward else None

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libncmri_fhd.so")
-SOURCES = ["fhd_kernels.hip", "fhd_mfma.hip", "fhd_half.hip", "fhd_forward.hip", "fhd_lines.hip", "fhd_cg.hip",
+SOURCES = ["fhd_kernels.hip", "fhd_mfma.hip", "fhd_half.hip", "fhd_forward.hip", "fhd_forward_half.hip", "fhd_lines.hip", "fhd_cg.hip",
            "fhd_grid.hip", "fhd_api.hip"]
 ARCH = "gfx950"
 

@@ -2,6 +2,7 @@
 // two stream-ordered launches (see include/fhd.h for the contract).
 #include "fhd.h"
 #include "fhd_cg.h"
+#include "fhd_forward_half.h"
 #include "fhd_internal.h"
 
 #include <atomic>
@@ -359,16 +360,19 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   fhd_status vst = validate(M, N, batch, o);
   if (vst != FHD_OK) return vst;
   const int V = o->voxels_per_lane;
-  if (o->engine == FHD_ENGINE_VALU || o->engine == FHD_ENGINE_MFMA16)
-    return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only");
+  if (o->engine == FHD_ENGINE_VALU)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator runs on the MFMA engine only (fp32 or half-split)");
+  const bool half = o->engine == FHD_ENGINE_MFMA16;
   if (o->sum == FHD_SUM_KAHAN)
     return fail(FHD_ERR_INVALID_ARGUMENT, "the forward operator sums blocked or plain, not Kahan");
+  if (half && V != 0 && V != 128)
+    return fail(FHD_ERR_INVALID_ARGUMENT, "the half-split engine takes groups of 128 voxels (got %d)", V);
   if (V != 0 && V < 32)
     return fail(FHD_ERR_INVALID_ARGUMENT, "MFMA group sizes are 32, 64 or 128 voxels (got %d)", V);
   const int64_t C = ncmri::kMfmaChunk;
   p.op = FHD_OP_FORWARD;
   p.is_q = 0;
-  p.engine = FHD_ENGINE_MFMA;
+  p.engine = half ? FHD_ENGINE_MFMA16 : FHD_ENGINE_MFMA;
   p.trig = o->trig;
   p.sum = o->sum;
   p.stages = o->stages == 0 ? FHD_STAGE_ALL : o->stages;
@@ -380,10 +384,12 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   int left = batch;
   for (int g = 16; g >= 1; g /= 2)
     while (left >= g) { p.bc[p.npass++] = g; left -= g; }
-  p.tiles = V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, 0, M);
+  p.tiles = half ? 8 : (V != 0 ? V / 16 : auto_mfma_tiles(N, p.bc, p.npass, 8, 0, M));
   p.V = 16 * p.tiles / p.bc[0];
   int64_t gmax = 0, gmin = -1;
   for (int i = 0; i < p.npass; ++i) {
+    if (half && !ncmri::fwd_half_supported(p.bc[i]))
+      return fail(FHD_ERR_INTERNAL, "no half-split forward kernel for BC=%d", p.bc[i]);
     if (!ncmri::mfma_supported(p.tiles, p.bc[i])) return fail(FHD_ERR_INTERNAL, "no MFMA kernel for T=%d BC=%d", p.tiles, p.bc[i]);
     p.gpad[i] = fwd_gpad(N, p.tiles, p.bc[i]);
     if (p.gpad[i] > gmax) gmax = p.gpad[i];
@@ -445,6 +451,14 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     const int64_t row_bytes = gs * ncmri::mfma_factor_floats(p.tiles) * (int64_t)sizeof(float);
     if (row_bytes <= kRowBlockBytes && gs > p.tile) p.tile = gs;
   }
+  // the half-split engine's HW path sums each launch row as one block at
+  // every size (its parts stream from L2 as the four-group engine's image
+  // does; one resident workgroup of eight waves per CU either way)
+  if (half && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN) {
+    int64_t gs = 0;
+    for (int i = 0; i < p.npass; ++i) gs = p.g_split[i] > gs ? p.g_split[i] : gs;
+    if (gs > p.tile) p.tile = gs;
+  }
   p.m_split = 0;
   p.hdr_bytes = 0;
   p.ws_bytes = 0;
@@ -454,6 +468,10 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
                       : align256((size_t)p.gpad[i] * 4 * sizeof(float)) +
                             align256((size_t)p.gpad[i] * ncmri::mfma_factor_floats(p.tiles) * sizeof(float)) +
                             (size_t)(p.gpad[i] + 1) * sizeof(int32_t);
+    // half-split: the fp16 parts of the packed image and its scale
+    if (half && p.gpad[i] > 0)
+      p.pass_bytes[i] = align256(p.pass_bytes[i]) + align256(ncmri::fwd_half_parts_bytes(p.gpad[i])) +
+                        align256(ncmri::kFwdHalfScaleFloats * sizeof(float));
     p.ws_bytes += align256(p.pass_bytes[i]);
   }
   p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)M * sizeof(fhd_c32) : 0;
@@ -549,12 +567,23 @@ fhd_status run_forward(const float* kx, const float* ky, const float* kz, const 
                       p.g_split[i], (float*)base, (float*)(base + hb),
                       p.gpad[i] > 0 ? (int32_t*)(base + hb + ib) : nullptr,
                       (float2*)(out + (int64_t)b0 * M), p.splits > 1 ? partial : nullptr};
+    const bool half = p.engine == FHD_ENGINE_MFMA16;
+    ncmri::FwdHalfArgs ha{fa, nullptr, nullptr};
+    if (half && p.gpad[i] > 0) {
+      const size_t lb = align256(hb + ib + (size_t)(p.gpad[i] + 1) * sizeof(int32_t));
+      ha.wh = base + lb;
+      ha.scale = (float*)(base + lb + align256(ncmri::fwd_half_parts_bytes(p.gpad[i])));
+    }
     hipError_t e = hipSuccess;
     const char* what = "pack";
-    if (p.stages & FHD_STAGE_MU) e = ncmri::launch_fwd_pack(p.tiles, bc, fa, s);
+    if (p.stages & FHD_STAGE_MU) {
+      e = ncmri::launch_fwd_pack(p.tiles, bc, fa, s);
+      if (e == hipSuccess && half && p.gpad[i] > 0) e = ncmri::launch_fwd_half_pack(bc, ha, s);
+    }
     if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
       what = "gather";
-      e = ncmri::launch_fwd_gather(p.trig, p.tiles, bc, p.splits, fa, s);
+      e = half && p.gpad[i] > 0 ? ncmri::launch_fwd_half_gather(p.trig, bc, p.splits, ha, s)
+                                : ncmri::launch_fwd_gather(p.trig, p.tiles, bc, p.splits, fa, s);
     }
     if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE)) {
       what = "reduce";

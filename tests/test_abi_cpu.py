@@ -310,8 +310,19 @@ def test_describe_plan_half_split(lib):
     assert fhd_describe_plan(1000, 100, engine="mfma16", sum="plain")["sample_splits"] == 1
     # workspace: headers, factor parts, Mu, the scale pair, partial sums, flags
     assert fhd_workspace_bytes(262144, 128 ** 3, engine="mfma16", trig="accurate") == p["workspace_bytes"] > 0
+    # the forward operator: groups of 128 / vectors voxels; fp16 parts of the
+    # packed image (gpad x 1536 bytes) and the scale beside the fp32 workspace
+    f = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma16", trig="hw")
+    f32 = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma", trig="hw")
+    assert f["engine"] == _lib.FHD_ENGINE_MFMA16 and f["voxels_per_lane"] == 128
+    assert f["workspace_bytes"] - f32["workspace_bytes"] == 16384 * 1536 + 1280
+    # one launch row of all 16,384 groups: HW sums it as one block, accurate folds ~sqrt(G)
+    assert f["sample_splits"] == 1 and f["tile"] == 16384
+    assert fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma16", trig="accurate")["tile"] == 128
     with pytest.raises(Exception):
-        fhd_describe_plan(1000, 4096, op="forward", engine="mfma16")
+        fhd_describe_plan(1000, 4096, op="forward", engine="mfma16", voxels_per_lane=64)
+    with pytest.raises(Exception):
+        fhd_describe_plan(1000, 4096, op="forward", engine="valu")
 
 
 def test_describe_plan_mfma(lib):

@@ -1,0 +1,172 @@
+"""GPU parity of the half-split forward operator (fhd_forward with
+engine="mfma16": the four-group engine's sum over voxel groups with every
+fp32 product formed from fp16 hi/lo parts on the fp16 matrix cores, fp32
+accumulation) against the double-precision oracle, at the fp32 engines' bars
+(tests/gpu_util.TOL).
+
+  - grids whose groups of 128 / vectors voxels line up with x rows, with a
+    partial last group and chunk of 32 groups, ragged sample counts (a
+    partial last wave of 16), one and several launch rows, tiles folded into
+    running totals and a tile that spans the launch row, blocked and plain
+    sums, both trig paths;
+  - batches of 2 to 19 images (passes of 16, 8, 4, 2 and 1 vectors);
+  - irregular voxels (every group off the common offsets: all direct), one
+    displaced voxel, tiny voxel counts, an all-zero image (scale 1);
+  - an image whose magnitudes span nine orders of magnitude (the power-of-two
+    scale and the fp16 parts' range);
+  - the 128^3 x 262,144 workload on sampled outputs; adjointness with the
+    half-split F^H D; two runs bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+from non_cartesian_mri_amd import inputs
+from tests.gpu_util import TOL, assert_close, dev_problem, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TRIGS = ["accurate", "hw"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _images(seed, B, N, mag_range=None):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    r = np.stack([inputs.complex_normal(rng, N) for _ in range(B)]).reshape(B, N)
+    if mag_range is not None:   # per-voxel magnitudes 10^U(-r, r)
+        r = (r * (10.0 ** rng.uniform(-mag_range, mag_range, (B, N)))).astype(np.complex64)
+    return r
+
+
+def _forward(p, rho, d=None, **opts):
+    from non_cartesian_mri_amd import fhd_forward
+    d = d or dev_problem(p)
+    r = torch.from_numpy(np.ascontiguousarray(rho)).to("cuda:0")
+    out = fhd_forward(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], r, engine="mfma16", **opts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(rho.shape[0], p.M)
+
+
+def _ref(oracle_mod, p, rho, idx=None):
+    return oracle_mod.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho, idx=idx)
+
+
+@pytest.fixture(scope="module")
+def grid(oracle_mod):
+    # 30,000 of the 32^3 voxels: 235 groups of 128 (the last partial), 8
+    # chunks of 32 groups (the last partial); 1001 samples (a partial wave)
+    p = inputs.random_problem(501, M=1001, L=32, N=30000)
+    rho = _images(502, 1, p.N)
+    return p, dev_problem(p), rho, _ref(oracle_mod, p, rho)
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("tile", [32, 64, 0, 1 << 20])
+def test_grid(grid, trig, splits, tile):
+    p, d, rho, ref = grid
+    got = _forward(p, rho, d, trig=trig, tile=tile, sample_splits=splits)
+    assert_close(got, ref, TOL[trig], f"half forward grid {trig} rows={splits} tile={tile}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_plain_sum(grid, trig):
+    p, d, rho, ref = grid
+    assert_close(_forward(p, rho, d, trig=trig, sum="plain"), ref, TOL[trig], f"half forward plain {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("B", [2, 3, 16, 19])
+def test_batch(oracle_mod, trig, B):
+    p = inputs.random_problem(503, M=777, L=16)
+    rho = _images(504, B, p.N)
+    assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig], f"half forward B={B} {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_irregular_voxels(oracle_mod, trig):
+    p = inputs.random_problem(505, M=900, L=12, N=1500, coords="random")
+    rho = _images(506, 2, p.N)
+    assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig], f"half forward irregular {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_one_displaced_voxel(oracle_mod, trig):
+    p = inputs.random_problem(507, M=700, L=16)
+    x = p.x.copy()
+    x[1000] += np.float32(0.3)   # its group of 128 goes to the direct kernel, the others stay regular
+    p.x = x
+    rho = _images(508, 1, p.N)
+    assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig], f"half forward displaced {trig}")
+
+
+@pytest.mark.parametrize("N", [1, 3, 129])
+def test_tiny_voxel_counts(oracle_mod, N):
+    p = inputs.random_problem(509, M=321, L=16, N=N)
+    rho = _images(510, 1, N)
+    for trig in TRIGS:
+        assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig], f"half forward N={N} {trig}")
+
+
+@pytest.mark.parametrize("M", [1, 15, 16, 17, 4099])
+def test_sample_count_tails(oracle_mod, M):
+    p = inputs.random_problem(511, M=M, L=8)
+    rho = _images(512, 2, p.N)
+    ref = _ref(oracle_mod, p, rho)
+    for trig in TRIGS:
+        assert_close(_forward(p, rho, trig=trig), ref, TOL[trig], f"half forward M={M} {trig}")
+
+
+def test_zero_image():
+    p = inputs.random_problem(513, M=200, L=8)
+    got = _forward(p, np.zeros((1, p.N), np.complex64), trig="accurate")
+    assert np.all(got == 0)
+
+
+def test_wide_dynamic_range(oracle_mod):
+    # |rho| over nine orders of magnitude: the parts' power-of-two scale puts
+    # the largest entry near 2^14; the smallest fall to fp16 subnormals
+    p = inputs.random_problem(514, M=1500, L=16)
+    rho = _images(515, 1, p.N, mag_range=4.5)
+    assert_close(_forward(p, rho, trig="accurate"), _ref(oracle_mod, p, rho), TOL["accurate"],
+                 "half forward |rho| over 1e9")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_full_size_sampled(oracle_mod, trig):
+    """128^3 voxels x 262,144 stack-of-spirals samples in the default launch
+    plan; the oracle evaluates 256 seeded samples."""
+    p = inputs.make_config("fhd_128cube_262144_spirals")
+    rho = _images(516, 1, p.N)
+    idx = inputs.subset_indices(p.M, 256, p.seed)
+    ref = _ref(oracle_mod, p, rho, idx=idx)
+    print(f"[oracle] forward 128^3 x 256 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
+    got = _forward(p, rho, trig=trig)
+    assert_close(got[:, idx], ref, TOL[trig], f"half forward 128^3 {trig}")
+
+
+def test_adjoint_of_half_fhd():
+    """<F rho, D> = <rho, F^H D> with both sides on the half-split engine."""
+    from tests.gpu_util import gpu_fhd
+    p = inputs.random_problem(517, M=3000, L=16)
+    d = dev_problem(p)
+    rho = _images(518, 1, p.N)
+    Frho = _forward(p, rho, d, trig="accurate")[0].astype(np.complex128)
+    FHd = gpu_fhd(p, d, trig="accurate", engine="mfma16")[0].astype(np.complex128)
+    lhs = np.vdot(Frho, p.D[0].astype(np.complex128))
+    rhs = np.vdot(rho[0].astype(np.complex128), FHd)
+    scale = np.linalg.norm(Frho) * np.linalg.norm(p.D[0])
+    assert abs(lhs - rhs) <= TOL["accurate"] * scale, (lhs, rhs)
+
+
+def test_deterministic():
+    p = inputs.random_problem(519, M=2500, L=16)
+    d = dev_problem(p)
+    rho = _images(520, 1, p.N)
+    a = _forward(p, rho, d, trig="hw")
+    b = _forward(p, rho, d, trig="hw")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
