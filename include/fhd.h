@@ -106,8 +106,9 @@ typedef enum fhd_engine {
                           not sit at common offsets (any non-grid coordinates) are
                           evaluated per voxel on the vector ALU over the same launch
                           rows, at about the rate of the VALU engine's per-voxel path */,
-  FHD_ENGINE_MFMA16 = 3 /* half-split matrix-core kernels (F^H D and Q only; opt-in, never
-                          chosen by FHD_ENGINE_AUTO): the same factored sum in groups of
+  FHD_ENGINE_MFMA16 = 3 /* half-split matrix-core kernels (F^H D, Q and the forward
+                          operator; opt-in, never chosen by FHD_ENGINE_AUTO): the same
+                          factored sum in groups of
                           128 / vectors voxels, each fp32 product formed from fp16 parts
                           (x = hi + lo, hi = fp16(x), lo = fp16(x - hi); hi hi + hi lo +
                           lo hi) on v_mfma_f32_16x16x32_f16 with fp32 accumulation, the
@@ -246,7 +247,9 @@ fhd_status q_compute(const float* kx, const float* ky, const float* kz,
  * <F rho, d> = <rho, F^H d> with fhd_compute.  Runs on the matrix-core engine
  * only (FHD_ENGINE_VALU and FHD_SUM_KAHAN are rejected); voxels_per_lane may
  * be 0, 32, 64 or 128; sample_splits here splits the voxel groups across launch
- * rows.  N == 0 writes zeros; M == 0 does nothing.  Returns FHD_OK or an error
+ * rows.  FHD_ENGINE_MFMA16 sums over the voxel groups from fp16 parts of the
+ * image entries (scaled by a power of two; groups of 128 / vectors voxels,
+ * 32 groups per MFMA), the rest as on the fp32 engine.  N == 0 writes zeros; M == 0 does nothing.  Returns FHD_OK or an error
  * code as fhd_compute does.
  */
 fhd_status fhd_forward(const float* kx, const float* ky, const float* kz,

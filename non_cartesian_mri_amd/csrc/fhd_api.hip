@@ -451,13 +451,15 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     const int64_t row_bytes = gs * ncmri::mfma_factor_floats(p.tiles) * (int64_t)sizeof(float);
     if (row_bytes <= kRowBlockBytes && gs > p.tile) p.tile = gs;
   }
-  // the half-split engine's HW path sums each launch row as one block at
-  // every size (its parts stream from L2 as the four-group engine's image
-  // does; one resident workgroup of eight waves per CU either way)
+  // the half-split engine's HW path likewise sums rows of at most
+  // kRowBlockBytes of packed groups as one block (its kernel keeps no running
+  // totals either way: one resident workgroup of eight waves per CU); longer
+  // rows fold tiles, which keeps its error at 512^3 at the fp32 engine's
   if (half && o->trig == FHD_TRIG_HW && o->tile == 0 && o->sum != FHD_SUM_PLAIN) {
     int64_t gs = 0;
     for (int i = 0; i < p.npass; ++i) gs = p.g_split[i] > gs ? p.g_split[i] : gs;
-    if (gs > p.tile) p.tile = gs;
+    const int64_t row_bytes = gs * ncmri::mfma_factor_floats(p.tiles) * (int64_t)sizeof(float);
+    if (row_bytes <= kRowBlockBytes && gs > p.tile) p.tile = gs;
   }
   p.m_split = 0;
   p.hdr_bytes = 0;
@@ -471,6 +473,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     // half-split: the fp16 parts of the packed image and its scale
     if (half && p.gpad[i] > 0)
       p.pass_bytes[i] = align256(p.pass_bytes[i]) + align256(ncmri::fwd_half_parts_bytes(p.gpad[i])) +
+                        align256(ncmri::fwd_half_header_bytes(p.gpad[i])) +
                         align256(ncmri::kFwdHalfScaleFloats * sizeof(float));
     p.ws_bytes += align256(p.pass_bytes[i]);
   }
@@ -568,11 +571,13 @@ fhd_status run_forward(const float* kx, const float* ky, const float* kz, const 
                       p.gpad[i] > 0 ? (int32_t*)(base + hb + ib) : nullptr,
                       (float2*)(out + (int64_t)b0 * M), p.splits > 1 ? partial : nullptr};
     const bool half = p.engine == FHD_ENGINE_MFMA16;
-    ncmri::FwdHalfArgs ha{fa, nullptr, nullptr};
+    ncmri::FwdHalfArgs ha{fa, nullptr, nullptr, nullptr};
     if (half && p.gpad[i] > 0) {
       const size_t lb = align256(hb + ib + (size_t)(p.gpad[i] + 1) * sizeof(int32_t));
+      const size_t pb = align256(ncmri::fwd_half_parts_bytes(p.gpad[i]));
       ha.wh = base + lb;
-      ha.scale = (float*)(base + lb + align256(ncmri::fwd_half_parts_bytes(p.gpad[i])));
+      ha.hh = (float4*)(base + lb + pb);
+      ha.scale = (float*)(base + lb + pb + align256(ncmri::fwd_half_header_bytes(p.gpad[i])));
     }
     hipError_t e = hipSuccess;
     const char* what = "pack";

@@ -10,16 +10,21 @@ namespace ncmri {
 // One pass of the half-split forward operator: f as for the four-group engine
 // (groups of 128 / BC voxels, its packed image f.gwb is the source of the
 // parts), wh the fp16 parts [gpad / 32][8 tiles][3][2][64 lanes] (uint4 each:
-// gpad x 1536 bytes), scale [2 + 256] floats (2^e, 2^-e, per-block maxima).
+// gpad x 1536 bytes), hh the gather's group headers [gpad] (x, y, z of the
+// group's first voxel; w: per octet of groups 8 o .. 8 o + 7, element 0 holds
+// 1 when the octet's bases are equally spaced, elements 1-3 the spacing),
+// scale [2 + 256] floats (2^e, 2^-e, per-block maxima).
 struct FwdHalfArgs {
   FwdArgs f;
   void* wh;
+  float4* hh;
   float* scale;
 };
 
 constexpr int kFwdHalfWaves = 8;   // waves per workgroup of the half-split forward gather
 
 inline size_t fwd_half_parts_bytes(int64_t gpad) { return (size_t)gpad * 1536; }
+inline size_t fwd_half_header_bytes(int64_t gpad) { return (size_t)gpad * 16; }
 constexpr int kFwdHalfScaleFloats = 2 + 256;
 
 bool fwd_half_supported(int BC);

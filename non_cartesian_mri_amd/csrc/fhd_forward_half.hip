@@ -104,11 +104,30 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       w[(((q * 8 + t) * 3 + u) * 2 + s) * 64 + lane] = *reinterpret_cast<const uint4*>(&part[u][s]);
+  if (cc == 0) {
+    // the gather's headers of the octet: the group bases, and whether they
+    // are equally spaced (then a lane steps its phase from group to group by
+    // one rotation) with the spacing; exact float comparisons
+    const float4* gh = reinterpret_cast<const float4*>(a.ghdr) + o * 8;
+    float4 hd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hd[e] = gh[e];
+    const float dx = hd[1].x - hd[0].x, dy = hd[1].y - hd[0].y, dz = hd[1].z - hd[0].z;
+    bool even = true;
+#pragma unroll
+    for (int e = 2; e < 8; ++e)
+      even = even && hd[e].x - hd[0].x == (float)e * dx && hd[e].y - hd[0].y == (float)e * dy &&
+             hd[e].z - hd[0].z == (float)e * dz;
+    const float wv[4] = {even ? 1.0f : 0.0f, dx, dy, dz};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h.hh[o * 8 + e] = make_float4(hd[e].x, hd[e].y, hd[e].z, e < 4 ? wv[e & 3] : 0.0f);
+  }
 }
 
 // Gather: a wave owns 16 samples (lane l: sample l % 16); per 32-group chunk
-// lane l evaluates the phases of its sample at groups 8 (l / 16) .. + 7 of
-// the chunk, splits (c - s, c + s, s) into A parts, and for each tile of 16
+// lane l forms the phases of its sample at groups 8 (l / 16) .. + 7 of the
+// chunk (each evaluated, or on the HW path stepped by rotations where the
+// octet's bases are equally spaced, as on a grid), splits (c - s, c + s, s) into A parts, and for each tile of 16
 // columns reads the six B parts from LDS and issues 9 MFMAs.  Chunks are
 // staged into LDS by LDS DMA, double buffered, shared by the 8 waves of the
 // workgroup; the group headers are stored transposed (group 8 (j % 4) + j / 4
@@ -136,7 +155,7 @@ struct FwdHalfGather {
     }
     if (wig == 0 && lane < C) {
       const int m = 8 * (lane % 4) + lane / 4;
-      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(h.f.ghdr) + g0, C * 16), m * 16, lh);
+      lds_dma16(buffer_rsrc(h.hh + g0, C * 16), m * 16, lh);
     }
   }
 
@@ -147,18 +166,48 @@ struct FwdHalfGather {
 
   __device__ static __forceinline__ void chunk(const float4* __restrict__ hb, const uint4* __restrict__ lb, int lane,
                                                const SampleK<TRIG>& k, f32x4 (&acc)[3][T]) {
+    // A entries (c - s, c + s, s) of groups 8 (lane / 16) + e, e < 8, of the
+    // chunk (slot 4 e + lane / 16).  HW trig and equally spaced bases: the
+    // first group's phase and the spacing's, then seven rotations (2 sines
+    // and cosines per octet instead of 8 of each); otherwise per group.
+    const int oc = lane >> 4;
+    float ent[8][3];
+    bool stepped = false;
+    if constexpr (TRIG == kTrigHw) {
+      const float4 h0 = hb[oc];
+      if (h0.w != 0.0f) {
+        stepped = true;
+        float c, s, cd, sd;
+        k.sincos_phase(h0.x, h0.y, h0.z, c, s);
+        k.sincos_phase(hb[4 + oc].w, hb[8 + oc].w, hb[12 + oc].w, cd, sd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ent[e][0] = c - s;
+          ent[e][1] = c + s;
+          ent[e][2] = s;
+          if (e < 7) {
+            const float cn = __builtin_fmaf(c, cd, -(s * sd));
+            s = __builtin_fmaf(s, cd, c * sd);
+            c = cn;
+          }
+        }
+      }
+    }
+    if (!stepped) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 he = hb[4 * e + oc];
+        const float hs[3] = {he.x, he.y, he.z};
+        fwd_entries<TRIG>(k, hs, ent[e]);
+      }
+    }
     half8 ah[3], al[3];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      float av0[3], av1[3];   // groups 8 (lane / 16) + 2 p and + 2 p + 1
-      const float4 h0 = hb[4 * (2 * p) + (lane >> 4)], h1 = hb[4 * (2 * p + 1) + (lane >> 4)];
-      const float hs0[3] = {h0.x, h0.y, h0.z}, hs1[3] = {h1.x, h1.y, h1.z};
-      fwd_entries<TRIG>(k, hs0, av0);
-      fwd_entries<TRIG>(k, hs1, av1);
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
         uint32_t hi, lo;
-        split_pair(av0[u], av1[u], hi, lo);
+        split_pair(ent[2 * p][u], ent[2 * p + 1][u], hi, lo);
         const half2v hh = __builtin_bit_cast(half2v, hi), ll = __builtin_bit_cast(half2v, lo);
         ah[u][2 * p] = hh[0];
         ah[u][2 * p + 1] = hh[1];
@@ -296,6 +345,7 @@ bool fwd_half_supported(int BC) { return select_fwd_half(kTrigHw, BC).gather != 
 
 hipError_t launch_fwd_half_pack(int BC, const FwdHalfArgs& h, hipStream_t s) {
   if (!fwd_half_supported(BC) || h.f.gpad % 32 != 0 || !h.scale) return hipErrorInvalidValue;
+  if (h.f.gpad > 0 && (!h.wh || !h.hh)) return hipErrorInvalidValue;
   // the scale first, also for an empty pass (then 1)
   const int64_t n = h.f.gpad * 384;   // floats of the packed image (T = 8)
   hipLaunchKernelGGL(fwd_half_scale_partial_kernel, dim3(kScaleBlocks), dim3(256), 0, s, h.f.gwb, n, h.scale);
@@ -304,7 +354,6 @@ hipError_t launch_fwd_half_pack(int BC, const FwdHalfArgs& h, hipStream_t s) {
   hipLaunchKernelGGL(fwd_half_scale_kernel, dim3(1), dim3(256), 0, s, h.scale);
   e = hipGetLastError();
   if (e != hipSuccess || h.f.gpad <= 0) return e;
-  if (!h.wh) return hipErrorInvalidValue;
   const int64_t lanes = h.f.gpad / 8 * 128;
   hipLaunchKernelGGL(fwd_half_pack_kernel, dim3((unsigned)((lanes + kWorkgroup - 1) / kWorkgroup)), dim3(kWorkgroup), 0,
                      s, h);
@@ -314,7 +363,7 @@ hipError_t launch_fwd_half_pack(int BC, const FwdHalfArgs& h, hipStream_t s) {
 hipError_t launch_fwd_half_gather(int trig, int BC, int32_t splits, const FwdHalfArgs& h, hipStream_t s) {
   const FwdArgs& a = h.f;
   FwdHalfPair fn = select_fwd_half(trig, BC);
-  if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr) || !h.scale || !h.wh)
+  if (!fn.gather || splits < 1 || (splits > 1) != (a.partial != nullptr) || !h.scale || !h.wh || !h.hh)
     return hipErrorInvalidValue;
   if (a.gpad % 32 != 0 || a.g_split % 32 != 0 || a.tile % 32 != 0 || a.tile <= 0) return hipErrorInvalidValue;
   if (a.M <= 0) return hipSuccess;

@@ -311,14 +311,17 @@ def test_describe_plan_half_split(lib):
     # workspace: headers, factor parts, Mu, the scale pair, partial sums, flags
     assert fhd_workspace_bytes(262144, 128 ** 3, engine="mfma16", trig="accurate") == p["workspace_bytes"] > 0
     # the forward operator: groups of 128 / vectors voxels; fp16 parts of the
-    # packed image (gpad x 1536 bytes) and the scale beside the fp32 workspace
+    # packed image (gpad x 1536 bytes), the gather's headers (gpad x 16) and the
+    # scale beside the fp32 workspace
     f = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma16", trig="hw")
     f32 = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma", trig="hw")
     assert f["engine"] == _lib.FHD_ENGINE_MFMA16 and f["voxels_per_lane"] == 128
-    assert f["workspace_bytes"] - f32["workspace_bytes"] == 16384 * 1536 + 1280
+    assert f["workspace_bytes"] - f32["workspace_bytes"] == 16384 * 1536 + 16384 * 16 + 1280
     # one launch row of all 16,384 groups: HW sums it as one block, accurate folds ~sqrt(G)
     assert f["sample_splits"] == 1 and f["tile"] == 16384
     assert fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma16", trig="accurate")["tile"] == 128
+    # rows beyond 256 MB of packed groups fold tiles, as on the fp32 engine (512^3: 1.6 GB)
+    assert fhd_describe_plan(262144, 512 ** 3, op="forward", engine="mfma16", trig="hw")["tile"] == 4096
     with pytest.raises(Exception):
         fhd_describe_plan(1000, 4096, op="forward", engine="mfma16", voxels_per_lane=64)
     with pytest.raises(Exception):

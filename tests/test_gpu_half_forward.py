@@ -14,8 +14,11 @@ accumulation) against the double-precision oracle, at the fp32 engines' bars
     displaced voxel, tiny voxel counts, an all-zero image (scale 1);
   - an image whose magnitudes span nine orders of magnitude (the power-of-two
     scale and the fp16 parts' range);
-  - the 128^3 x 262,144 workload on sampled outputs; adjointness with the
-    half-split F^H D; two runs bitwise equal.
+  - 128-voxel rows whose octets of groups are equally spaced (the HW path
+    steps the phases by rotations), not (evaluated per group), or both in one
+    wave;
+  - the 128^3 and 512^3 x 262,144 workloads on sampled outputs; adjointness
+    with the half-split F^H D; two runs bitwise equal.
 """
 import numpy as np
 import pytest
@@ -104,6 +107,35 @@ def test_one_displaced_voxel(oracle_mod, trig):
     assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig], f"half forward displaced {trig}")
 
 
+def _rows(ys, nz, nx=128):
+    """Voxel coordinates of x rows of nx voxels at the y values ys on nz planes."""
+    iz, iy, ix = np.meshgrid(np.arange(nz), np.asarray(ys), np.arange(nx), indexing="ij")
+    return tuple((a.ravel() - 8).astype(np.float32) for a in (ix, iy, iz))
+
+
+def _rows_problem(seed, M, coords):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kx, ky, kz = inputs.uniform_k(M, rng)
+    x, y, z = coords
+    return inputs.Problem(f"rows{seed}", "fhd", kx, ky, kz, x, y, z, inputs.complex_normal(rng, M), None, seed)
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+@pytest.mark.parametrize("ys,nz,B", [(range(8), 5, 1), (range(12), 3, 1), ([0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11, 12, 15], 4, 1),
+                                     (range(8), 5, 2), (range(12), 3, 3)])
+def test_octet_spacing(oracle_mod, trig, ys, nz, B):
+    """Groups are 128-voxel x rows.  The HW path steps a lane's phase over
+    its octet of groups by rotations where the octet's bases are equally
+    spaced: every octet with 8 rows per plane; with 12 rows per plane, or
+    rows missing from the sequence, some octets are not (phases evaluated
+    per group) and the others are, in the same wave.  Two and three vectors:
+    groups of 64 voxels, half rows, never equally spaced over an octet."""
+    p = _rows_problem(521, 1500, _rows(list(ys), nz))
+    rho = _images(522, B, p.N)
+    assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig],
+                 f"half forward rows ys={list(ys)[:3]}... nz={nz} B={B} {trig}")
+
+
 @pytest.mark.parametrize("N", [1, 3, 129])
 def test_tiny_voxel_counts(oracle_mod, N):
     p = inputs.random_problem(509, M=321, L=16, N=N)
@@ -147,6 +179,19 @@ def test_full_size_sampled(oracle_mod, trig):
     print(f"[oracle] forward 128^3 x 256 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
     got = _forward(p, rho, trig=trig)
     assert_close(got[:, idx], ref, TOL[trig], f"half forward 128^3 {trig}")
+
+
+@pytest.mark.parametrize("trig", TRIGS)
+def test_512cubed_sampled(oracle_mod, trig):
+    """512^3 voxels x 262,144 spiral samples (rows of 1.6 GB of packed groups:
+    tiles folded on both trig paths): 16 seeded samples against the oracle."""
+    p = inputs.make_config("fhd_512cube_262144_spirals")
+    rho = _images(523, 1, p.N)
+    idx = inputs.subset_indices(p.M, 16, p.seed)
+    ref = _ref(oracle_mod, p, rho, idx=idx)
+    print(f"[oracle] forward 512^3 x 16 samples: {oracle_mod.last.seconds:.1f}s", flush=True)
+    got = _forward(p, rho, trig=trig)
+    assert_close(got[:, idx], ref, TOL[trig], f"half forward 512^3 {trig}")
 
 
 def test_adjoint_of_half_fhd():
