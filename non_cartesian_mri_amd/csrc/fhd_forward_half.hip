@@ -126,8 +126,8 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h
 
 // Gather: a wave owns 16 samples (lane l: sample l % 16); per 32-group chunk
 // lane l forms the phases of its sample at groups 8 (l / 16) .. + 7 of the
-// chunk (each evaluated, or on the HW path stepped by rotations where the
-// octet's bases are equally spaced, as on a grid), splits (c - s, c + s, s) into A parts, and for each tile of 16
+// chunk (each evaluated, or stepped by rotations where the octet's bases are
+// equally spaced, as on a grid), splits (c - s, c + s, s) into A parts, and for each tile of 16
 // columns reads the six B parts from LDS and issues 9 MFMAs.  Chunks are
 // staged into LDS by LDS DMA, double buffered, shared by the 8 waves of the
 // workgroup; the group headers are stored transposed (group 8 (j % 4) + j / 4
@@ -167,33 +167,31 @@ struct FwdHalfGather {
   __device__ static __forceinline__ void chunk(const float4* __restrict__ hb, const uint4* __restrict__ lb, int lane,
                                                const SampleK<TRIG>& k, f32x4 (&acc)[3][T]) {
     // A entries (c - s, c + s, s) of groups 8 (lane / 16) + e, e < 8, of the
-    // chunk (slot 4 e + lane / 16).  HW trig and equally spaced bases: the
-    // first group's phase and the spacing's, then seven rotations (2 sines
-    // and cosines per octet instead of 8 of each); otherwise per group.
+    // chunk (slot 4 e + lane / 16).  Equally spaced bases: the first group's
+    // phase and the spacing's (each as the trig path evaluates a phase), then
+    // seven rotations by the spacing's (2 sines and cosines per octet instead
+    // of 8 of each; each rotation adds about one rounding to c and s, and
+    // after seven they stay within ~5e-7 of the exact values, against ~1e-7
+    // for one accurate evaluation); otherwise per group.
     const int oc = lane >> 4;
     float ent[8][3];
-    bool stepped = false;
-    if constexpr (TRIG == kTrigHw) {
-      const float4 h0 = hb[oc];
-      if (h0.w != 0.0f) {
-        stepped = true;
-        float c, s, cd, sd;
-        k.sincos_phase(h0.x, h0.y, h0.z, c, s);
-        k.sincos_phase(hb[4 + oc].w, hb[8 + oc].w, hb[12 + oc].w, cd, sd);
+    const float4 h0 = hb[oc];
+    if (h0.w != 0.0f) {
+      float c, s, cd, sd;
+      k.sincos_phase(h0.x, h0.y, h0.z, c, s);
+      k.sincos_phase(hb[4 + oc].w, hb[8 + oc].w, hb[12 + oc].w, cd, sd);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ent[e][0] = c - s;
-          ent[e][1] = c + s;
-          ent[e][2] = s;
-          if (e < 7) {
-            const float cn = __builtin_fmaf(c, cd, -(s * sd));
-            s = __builtin_fmaf(s, cd, c * sd);
-            c = cn;
-          }
+      for (int e = 0; e < 8; ++e) {
+        ent[e][0] = c - s;
+        ent[e][1] = c + s;
+        ent[e][2] = s;
+        if (e < 7) {
+          const float cn = __builtin_fmaf(c, cd, -(s * sd));
+          s = __builtin_fmaf(s, cd, c * sd);
+          c = cn;
         }
       }
-    }
-    if (!stepped) {
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float4 he = hb[4 * e + oc];
