@@ -10,10 +10,12 @@ namespace ncmri {
 // One pass of the half-split forward operator: f as for the four-group engine
 // (groups of 128 / BC voxels, its packed image f.gwb is the source of the
 // parts), wh the fp16 parts [gpad / 32][8 tiles][3][2][64 lanes] (uint4 each:
-// gpad x 1536 bytes), hh the gather's group headers [gpad] (x, y, z of the
-// group's first voxel; w: per octet of groups 8 o .. 8 o + 7, element 0 holds
-// 1 when the octet's bases are equally spaced, elements 1-3 the spacing),
-// scale [2 + 256] floats (2^e, 2^-e, per-block maxima).
+// gpad x 1536 bytes; each 32-group chunk in the slot order its order kernel
+// picks), hh the gather's headers [gpad] in the same order (x, y, z of the
+// slot's group's first voxel; w: per octet of slots 8 o .. 8 o + 7, element
+// 0 holds 1 when the octet's bases are equally spaced, elements 1-3 the
+// spacing; element 4 of a chunk's first octet the chunk's order), scale
+// [2 + 256] floats (2^e, 2^-e, per-block maxima).
 struct FwdHalfArgs {
   FwdArgs f;
   void* wh;

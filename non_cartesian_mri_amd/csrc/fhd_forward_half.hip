@@ -65,13 +65,64 @@ __global__ void __launch_bounds__(256) fwd_half_scale_kernel(float* __restrict__
   }
 }
 
-// Parts: one lane per (octet of groups o, complex column cc < 128).  Entry u
+// Slot v = 8 j + e (octet j < 4, element e < 8) of a 32-group chunk holds
+// group (j mod s) + s e + 8 s (j div s) of the chunk, s = 1, 2 or 4: s = 1 the
+// identity; on a grid whose x rows hold s groups, s makes every octet a run
+// of equally spaced groups (one from each of 8 consecutive rows).
+__device__ __forceinline__ int chunk_slot_group(int v, int s) {
+  const int j = v >> 3, e = v & 7;
+  return (j % s) + s * e + 8 * s * (j / s);
+}
+
+// Order: one thread per chunk picks the s under which most of its octets are
+// equally spaced (the smallest s on ties) and writes the gather's headers in
+// slot order: x, y, z of the slot's group; w of the octet's element 0: 1 when
+// its bases are equally spaced (exact float comparisons), elements 1-3: the
+// spacing, element 4 of octet 0: s.
+__global__ void __launch_bounds__(kWorkgroup) fwd_half_order_kernel(FwdHalfArgs h) {
+  const int64_t q = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  if (q * 32 >= h.f.gpad) return;
+  const float4* gh = reinterpret_cast<const float4*>(h.f.ghdr) + q * 32;
+  int best = 1, best_n = -1;
+  for (int s = 1; s <= 4; s *= 2) {
+    int n = 0;
+    for (int j = 0; j < 4; ++j) {
+      const float4 a = gh[chunk_slot_group(8 * j, s)], b = gh[chunk_slot_group(8 * j + 1, s)];
+      const float dx = b.x - a.x, dy = b.y - a.y, dz = b.z - a.z;
+      bool even = true;
+      for (int e = 2; e < 8; ++e) {
+        const float4 c = gh[chunk_slot_group(8 * j + e, s)];
+        even = even && c.x - a.x == (float)e * dx && c.y - a.y == (float)e * dy && c.z - a.z == (float)e * dz;
+      }
+      n += even ? 1 : 0;
+    }
+    if (n > best_n) { best = s; best_n = n; }
+  }
+  float4* out = h.hh + q * 32;
+  for (int j = 0; j < 4; ++j) {
+    const float4 a = gh[chunk_slot_group(8 * j, best)], b = gh[chunk_slot_group(8 * j + 1, best)];
+    const float dx = b.x - a.x, dy = b.y - a.y, dz = b.z - a.z;
+    bool even = true;
+    for (int e = 2; e < 8; ++e) {
+      const float4 c = gh[chunk_slot_group(8 * j + e, best)];
+      even = even && c.x - a.x == (float)e * dx && c.y - a.y == (float)e * dy && c.z - a.z == (float)e * dz;
+    }
+    const float wv[5] = {even ? 1.0f : 0.0f, dx, dy, dz, j == 0 ? (float)best : 0.0f};
+    for (int e = 0; e < 8; ++e) {
+      const float4 c = gh[chunk_slot_group(8 * j + e, best)];
+      out[8 * j + e] = make_float4(c.x, c.y, c.z, e < 5 ? wv[e] : 0.0f);
+    }
+  }
+}
+
+// Parts: one lane per (octet of slots o, complex column cc < 128).  Entry u
 // (rr, ri, rr + ri) of group g and column cc sits in the four-group engine's
 // packed image at block g / 4, float4 slice (8 u + t) / 4 (t = cc / 16) of
-// lane 16 (g % 4) + cc % 16; the lane scales and splits the entries of groups
-// 8 o .. 8 o + 7 and stores them as the B parts of lane cc % 16 + 16 (o % 4)
-// of tile t in the 32-group chunk o / 4: B[k][j] = element k % 8 of lane
-// j + 16 (k / 8), k the group within the chunk, j the column within the tile.
+// lane 16 (g % 4) + cc % 16; the lane scales and splits the entries of the
+// groups in slots 8 o .. 8 o + 7 (the order kernel's s of chunk o / 4) and
+// stores them as the B parts of lane cc % 16 + 16 (o % 4) of tile t in that
+// chunk: B[k][j] = element k % 8 of lane j + 16 (k / 8), k the slot within the
+// chunk, j the column within the tile.
 __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h) {
   const FwdArgs& a = h.f;
   const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
@@ -80,10 +131,12 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h
   if (o * 8 >= a.gpad) return;
   const float sc = h.scale[0];
   const int t = cc >> 4;
+  const int64_t q = o >> 2;
+  const int so = (int)h.hh[q * 32 + 4].w;
   half8 part[3][2];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int64_t g = o * 8 + e;
+    const int64_t g = q * 32 + chunk_slot_group(8 * (int)(o & 3) + e, so);
     const float* blk = a.gwb + (g >> 2) * 1536;
     const int lp = 16 * (int)(g & 3) + (cc & 15);
 #pragma unroll
@@ -96,7 +149,6 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h
       part[u][1][e] = lo;
     }
   }
-  const int64_t q = o >> 2;
   const int lane = (cc & 15) + 16 * (int)(o & 3);
   uint4* w = reinterpret_cast<uint4*>(h.wh);
 #pragma unroll
@@ -104,36 +156,19 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_half_pack_kernel(FwdHalfArgs h
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       w[(((q * 8 + t) * 3 + u) * 2 + s) * 64 + lane] = *reinterpret_cast<const uint4*>(&part[u][s]);
-  if (cc == 0) {
-    // the gather's headers of the octet: the group bases, and whether they
-    // are equally spaced (then a lane steps its phase from group to group by
-    // one rotation) with the spacing; exact float comparisons
-    const float4* gh = reinterpret_cast<const float4*>(a.ghdr) + o * 8;
-    float4 hd[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hd[e] = gh[e];
-    const float dx = hd[1].x - hd[0].x, dy = hd[1].y - hd[0].y, dz = hd[1].z - hd[0].z;
-    bool even = true;
-#pragma unroll
-    for (int e = 2; e < 8; ++e)
-      even = even && hd[e].x - hd[0].x == (float)e * dx && hd[e].y - hd[0].y == (float)e * dy &&
-             hd[e].z - hd[0].z == (float)e * dz;
-    const float wv[4] = {even ? 1.0f : 0.0f, dx, dy, dz};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h.hh[o * 8 + e] = make_float4(hd[e].x, hd[e].y, hd[e].z, e < 4 ? wv[e & 3] : 0.0f);
-  }
 }
 
 // Gather: a wave owns 16 samples (lane l: sample l % 16); per 32-group chunk
-// lane l forms the phases of its sample at groups 8 (l / 16) .. + 7 of the
-// chunk (each evaluated, or stepped by rotations where the octet's bases are
-// equally spaced, as on a grid), splits (c - s, c + s, s) into A parts, and for each tile of 16
-// columns reads the six B parts from LDS and issues 9 MFMAs.  Chunks are
-// staged into LDS by LDS DMA, double buffered, shared by the 8 waves of the
-// workgroup; the group headers are stored transposed (group 8 (j % 4) + j / 4
-// at slot j) so that the four lane groups, which read groups 8 g + e at once,
-// hit consecutive slots.  FOLD: tiles of a.tile groups fold into running
-// totals; without it the launch row is one summation block.
+// lane l forms the phases of its sample at the groups of slots 8 (l / 16) ..
+// + 7 (each evaluated, or stepped by rotations where the octet's bases are
+// equally spaced, as on a grid), splits (c - s, c + s, s) into A parts, and
+// for each tile of 16 columns reads the six B parts from LDS and issues 9
+// MFMAs.  Chunks are staged into LDS by LDS DMA, double buffered, shared by
+// the 8 waves of the workgroup; the headers are stored transposed in LDS
+// (slot 8 (j % 4) + j / 4 at LDS slot j) so that the four lane groups, which
+// read slots 8 g + e at once, hit consecutive LDS slots.  FOLD: tiles of
+// a.tile groups fold into running totals; without it the launch row is one
+// summation block.
 template <int BC, int TRIG, bool FOLD>
 struct FwdHalfGather {
   static constexpr int T = 8;
@@ -352,6 +387,11 @@ hipError_t launch_fwd_half_pack(int BC, const FwdHalfArgs& h, hipStream_t s) {
   hipLaunchKernelGGL(fwd_half_scale_kernel, dim3(1), dim3(256), 0, s, h.scale);
   e = hipGetLastError();
   if (e != hipSuccess || h.f.gpad <= 0) return e;
+  const int64_t chunks = h.f.gpad / 32;
+  hipLaunchKernelGGL(fwd_half_order_kernel, dim3((unsigned)((chunks + kWorkgroup - 1) / kWorkgroup)), dim3(kWorkgroup),
+                     0, s, h);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t lanes = h.f.gpad / 8 * 128;
   hipLaunchKernelGGL(fwd_half_pack_kernel, dim3((unsigned)((lanes + kWorkgroup - 1) / kWorkgroup)), dim3(kWorkgroup), 0,
                      s, h);

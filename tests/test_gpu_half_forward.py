@@ -14,9 +14,9 @@ accumulation) against the double-precision oracle, at the fp32 engines' bars
     displaced voxel, tiny voxel counts, an all-zero image (scale 1);
   - an image whose magnitudes span nine orders of magnitude (the power-of-two
     scale and the fp16 parts' range);
-  - 128-voxel rows whose octets of groups are equally spaced (the HW path
-    steps the phases by rotations), not (evaluated per group), or both in one
-    wave;
+  - x rows whose octets of groups are equally spaced (phases stepped by
+    rotations) in the identity order or a strided chunk order, not at all
+    (evaluated per group), or both in one wave;
   - the 128^3 and 512^3 x 262,144 workloads on sampled outputs; adjointness
     with the half-split F^H D; two runs bitwise equal.
 """
@@ -121,19 +121,25 @@ def _rows_problem(seed, M, coords):
 
 
 @pytest.mark.parametrize("trig", TRIGS)
-@pytest.mark.parametrize("ys,nz,B", [(range(8), 5, 1), (range(12), 3, 1), ([0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11, 12, 15], 4, 1),
-                                     (range(8), 5, 2), (range(12), 3, 3)])
-def test_octet_spacing(oracle_mod, trig, ys, nz, B):
-    """Groups are 128-voxel x rows.  The HW path steps a lane's phase over
-    its octet of groups by rotations where the octet's bases are equally
-    spaced: every octet with 8 rows per plane; with 12 rows per plane, or
-    rows missing from the sequence, some octets are not (phases evaluated
-    per group) and the others are, in the same wave.  Two and three vectors:
-    groups of 64 voxels, half rows, never equally spaced over an octet."""
-    p = _rows_problem(521, 1500, _rows(list(ys), nz))
+@pytest.mark.parametrize("ys,nz,nx,B", [(range(8), 5, 128, 1), (range(12), 3, 128, 1),
+                                        ([0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11, 12, 15], 4, 128, 1),
+                                        (range(8), 5, 128, 2), (range(12), 3, 128, 3), (range(9), 2, 512, 1),
+                                        (range(10), 2, 256, 1), (range(6), 3, 256, 4)])
+def test_octet_spacing(oracle_mod, trig, ys, nz, nx, B):
+    """Voxels on x rows of nx.  A lane steps its phase over an octet of
+    groups by rotations where the octet's bases are equally spaced; a chunk
+    of 32 groups takes them in the order (stride 1, 2 or 4 over the chunk)
+    that makes most octets so.  128-voxel groups: one per 128-row (8 rows per
+    plane: every octet; 12 rows per plane or rows missing from the sequence:
+    some octets, the others evaluated per group, in one wave), four per
+    512-row and two per 256-row (stride 4 and 2, with a ragged plane end);
+    two vectors: 64-voxel groups, two per 128-row; three: a pass of two and
+    one; four: 32-voxel groups, eight per 256-row (no stride fits: evaluated
+    per group)."""
+    p = _rows_problem(521, 1500, _rows(list(ys), nz, nx=nx))
     rho = _images(522, B, p.N)
     assert_close(_forward(p, rho, trig=trig), _ref(oracle_mod, p, rho), TOL[trig],
-                 f"half forward rows ys={list(ys)[:3]}... nz={nz} B={B} {trig}")
+                 f"half forward rows ys={list(ys)[:3]}... nz={nz} nx={nx} B={B} {trig}")
 
 
 @pytest.mark.parametrize("N", [1, 3, 129])
