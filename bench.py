@@ -55,10 +55,10 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # the kernel source it was taken on, like TRAFFIC below)
 MFMA_BUSY = {
     ("fhd_128cube_262144_spirals", "hw", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257", "busy": 0.925,
+        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0", "busy": 0.925,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257", "busy": 0.851,
+        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0", "busy": 0.851,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
 }
 
@@ -80,21 +80,29 @@ def method_roofline(kind: str, B: int) -> dict:
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257",
+        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0",
         "fetch_bytes": 1801995.4 * 1024 * 2.0, "write_bytes": 262153.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "9dfccd67274ed257",
+        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0",
         "fetch_bytes": 1785493.0 * 1024 * 2.0, "write_bytes": 262152.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "aed6bcc555a67ff0",
-        "fetch_bytes": 1577176.3 * 1024 * 2.0, "write_bytes": 31394.2 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "52d901a194293be4",
+        "fetch_bytes": 1577175.4 * 1024 * 2.0, "write_bytes": 31086.9 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "aed6bcc555a67ff0",
-        "fetch_bytes": 1521180.2 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "52d901a194293be4",
+        "fetch_bytes": 1520017.6 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
+    ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma16", 128): {
+        "source": "fhd_forward_half.hip", "kernel_sha256": "f4aa14a7d648053b",
+        "fetch_bytes": 797316.1 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "profile": "profiles/forward_half_gather_128cubed_x_262144_kernel_stats.md"},
+    ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma16", 128): {
+        "source": "fhd_forward_half.hip", "kernel_sha256": "f4aa14a7d648053b",
+        "fetch_bytes": 797340.6 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "profile": "profiles/forward_half_gather_128cubed_x_262144_kernel_stats.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
         "source": "fhd_kernels.hip", "kernel_sha256": "22004205ff484185",
         "fetch_bytes": 984574.4 * 1024 * 2.0, "write_bytes": 262145.7 * 1024 * 1.0,
@@ -104,25 +112,25 @@ TRAFFIC = {
         "fetch_bytes": 1047842.2 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma16", 128): {
-        "source": "fhd_half.hip", "kernel_sha256": "b74be4bb6a33f536",
-        "fetch_bytes": 2298994.8 * 1024 * 2.0, "write_bytes": 262148.0 * 1024 * 1.0,
+        "source": "fhd_half.hip", "kernel_sha256": "cb9b5c05d5ca9c9b",
+        "fetch_bytes": 6491823.3 * 1024 * 2.0, "write_bytes": 262148.3 * 1024 * 1.0,
         "profile": "profiles/half_gather_128cubed_x_262144_kernel_stats.md"},
     # the whole gridding reconstruction (sort, deposit + x transform, y and z passes)
     ("fhd_128cube_262144_spirals/gridding", "-", "-", "-", 0): {
-        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "3f5564858fd83b41",
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "da0ebbbcb4b5f75b",
         "fetch_bytes": 25875.8 * 1024 * 2.0, "write_bytes": 59449.8 * 1024 * 1.0,
         "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     ("fhd_512cube_262144_spirals/gridding", "-", "-", "-", 0): {
-        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "3f5564858fd83b41",
+        "source": ["fhd_grid.hip", "fhd_lines.hip"], "kernel_sha256": "da0ebbbcb4b5f75b",
         "fetch_bytes": 1380804.8 * 1024 * 2.0, "write_bytes": 3156022.2 * 1024 * 1.0,
         "profile": "profiles/gridding_128cubed_x_262144_kernel_stats.md"},
     # the normal operator's five kernels, per application (128^3, lambda = 0)
     ("fhd_128cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "854d727e0e18b705",
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "aade9157aa9416cf",
         "fetch_bytes": 147709.3 * 1024 * 2.0, "write_bytes": 213007.2 * 1024 * 1.0,
         "profile": "profiles/cg_normal_operator_128cubed_kernel_stats.md"},
     ("fhd_512cube_262144_spirals/cg", "hw", "blocked", "mfma", 64): {
-        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "854d727e0e18b705",
+        "source": ["fhd_cg.hip", "fhd_lines.hip"], "kernel_sha256": "aade9157aa9416cf",
         "fetch_bytes": 9437532.7 * 1024 * 2.0, "write_bytes": 13639403.9 * 1024 * 1.0,
         "profile": "profiles/scale_512cubed_summary.md"},
 }
@@ -442,20 +450,27 @@ def bench_gridding(args, p, t, D, dev) -> dict:
 
 def kernel_source_sha(name) -> str:
     """sha256 prefix of a kernel source (or a list of them, in order) together
-    with the library headers each includes."""
+    with every library header it includes, directly or through other headers
+    (each once, depth first in sorted order)."""
     import hashlib
     import re
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "non_cartesian_mri_amd", "csrc")
     h = hashlib.sha256()
-    for one in ([name] if isinstance(name, str) else name):
-        with open(os.path.join(csrc, one), "rb") as f:
+    seen = set()
+
+    def add(fname):
+        path = os.path.join(csrc, fname)
+        if fname in seen or not os.path.exists(path):
+            return
+        seen.add(fname)
+        with open(path, "rb") as f:
             text = f.read()
         h.update(text)
         for inc in sorted(set(re.findall(rb'#include "([^"]+)"', text))):
-            path = os.path.join(csrc, inc.decode())
-            if os.path.exists(path):
-                with open(path, "rb") as f:
-                    h.update(f.read())
+            add(inc.decode())
+
+    for one in ([name] if isinstance(name, str) else name):
+        add(one)
     return h.hexdigest()[:16]
 
 
