@@ -166,6 +166,8 @@ def parse():
     ap.add_argument("--cg-iters", type=int, default=10, help="CG iterations per step (--op cg)")
     ap.add_argument("--cg-lambda", type=float, default=0.0,
                     help="regulariser weight relative to sum |phi|^2 / 6 (--op cg)")
+    ap.add_argument("--no-mirror-pairs", action="store_true",
+                    help="sum every voxel group alone (FHD_FLAG_NO_MIRROR_PAIRS) on the four-sample HW path")
     ap.add_argument("--voxels-per-lane", type=int, default=0)
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--method-steps", type=int, default=3,
@@ -484,6 +486,33 @@ def traffic_for(config: str, trig: str, summ: str, engine: str, group: int, gath
                                                "write_bytes": t["write_bytes"], "profile": t["profile"]}
 
 
+def mirror_pair_work(ws, ws_bytes: int, p, plan: dict) -> dict:
+    """The pair plan the device wrote for the last gather pass (at the end of
+    the workspace: 16 int32 of header, then one int2 per voxel group), and the
+    matrix work it implies: per block of four samples a wave of paired groups
+    issues 4 MFMAs per tile of 16 columns (8 tiles), a wave of groups alone 3;
+    each v_mfma_f32_16x16x4_f32 is 16 x 16 x 4 multiply-adds."""
+    V = plan["voxels_per_lane"]
+    G = -(-p.N // V)
+    pair_bytes = (64 + 8 * G + 255) // 256 * 256
+    head = ws[ws_bytes - pair_bytes:ws_bytes - pair_bytes + 64].view(torch_int32()).cpu().numpy()
+    E, Cp, R, U = int(head[0]), int(head[1]), int(head[2]), int(head[4])
+    slots_p = -(-Cp // 16)
+    slots_s = U - slots_p
+    mpad = plan["padded_samples"]
+    mfmas = (slots_p * 32 + slots_s * 24) * (mpad // 4) * plan["passes"]
+    flop = mfmas * 16 * 16 * 4 * 2
+    alone_mfmas = -(-G // 16) * 24 * (mpad // 4) * plan["passes"]
+    return {"paired_groups": Cp, "groups_alone": E - Cp, "groups": G, "launch_rows": R,
+            "wave_slots": U, "executed_flop_per_pair": flop / (p.N * p.M * p.B),
+            "mfma_ratio_to_unpaired": round(mfmas / alone_mfmas, 4)}
+
+
+def torch_int32():
+    import torch
+    return torch.int32
+
+
 def oracle_threads_hint() -> int:
     try:
         return int(os.environ.get("OMP_NUM_THREADS", "")) or os.cpu_count() or 1
@@ -636,8 +665,11 @@ def main():
         sys.exit(2)
     opts = dict(trig=args.trig, sum=args.sum, voxels_per_lane=args.voxels_per_lane, tile=args.tile,
                 engine=args.engine)
+    if args.no_mirror_pairs:
+        opts["mirror_pairs"] = False
     op = "forward" if forward else ("q" if is_q else "fhd")
-    ws = torch.empty(max(1, fhd_workspace_bytes(p.M, p.N, p.B, op=op, **opts)), dtype=torch.uint8, device=dev)
+    ws_bytes = max(1, fhd_workspace_bytes(p.M, p.N, p.B, op=op, **opts))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if forward:
         rng = np.random.Generator(np.random.PCG64(p.seed + 2000))
         rho = torch.from_numpy(np.stack([inputs.complex_normal(rng, p.N) for _ in range(p.B)])).to(dev)
@@ -718,12 +750,18 @@ def main():
                       "scale and fp16 parts, row reduction and (on a grid, empty) direct kernels are outside "
                       "the interval")
     elif forward or engine == "mfma":
-        ex = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"] * pairs / (g_avg * 1e-3) / 1e12
+        flop_per_pair = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"]
+        pairing = None
+        if not forward and plan.get("mirror_pairs"):
+            pairing = mirror_pair_work(ws, ws_bytes, p, plan)
+            flop_per_pair = pairing["executed_flop_per_pair"]
+        ex = flop_per_pair * pairs / (g_avg * 1e-3) / 1e12
         busy = MFMA_BUSY.get((args.config, args.trig, plan["voxels_per_lane"])) if not forward else None
         if busy is not None and busy["kernel_sha256"] != kernel_source_sha(busy["source"]):
             busy = None
         bound = "mfma"
-        eng = {"engine": "mfma", "bound": "mfma", "executed_flop_per_pair": 6, "achieved": round(ex, 3),
+        eng = {"engine": "mfma", "bound": "mfma", "executed_flop_per_pair": round(flop_per_pair, 4),
+               "achieved": round(ex, 3),
                "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ex / FP32_PEAK_TFLOPS, 4),
                "matrix_busy_counter": None if busy is None else busy["busy"],
                "matrix_busy_profile": None if busy is None else busy["profile"],
@@ -732,6 +770,11 @@ def main():
                        "per-sample factor columns (3 real MACs per pair), so the kernel executes %.3g of the "
                        "method's transcendentals and the method fractions exceed 1"
                        % (plan["voxels_per_lane"], 1.0 / max(plan["voxels_per_lane"], 1))}
+        if pairing is not None:
+            eng["mirror_pairs"] = pairing
+            eng["note"] += ("; mirror pairs: a group and the group at the negated reference share the phase "
+                            "(conjugate), so two groups take one phase and 4 real MACs per pair of columns "
+                            "where alone they take two phases and 6")
         if forward:
             kernel = ("fwd_gather_kernel: its launch rows in one step, timed alone; the image packing, "
                       "row reduction and (on a grid, empty) direct kernels are outside the interval")
@@ -772,6 +815,7 @@ def main():
                    "samples": p.M, "vectors": p.B, "trig": args.trig, "sum": summ,
                    "engine": engine, "group_voxels": plan["voxels_per_lane"], "tile": plan["tile"],
                    "sample_splits": plan["sample_splits"], "gather_launches": plan["passes"],
+                   "mirror_pairs": bool(plan.get("mirror_pairs")),
                    "parallelism": "single GPU, data-parallel over voxels"},
         "timing_ms": {"step_event_median": round(float(np.median(step_ms)), 4),
                       "gather_event_mean": round(g_avg, 4),

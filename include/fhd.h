@@ -136,6 +136,23 @@ enum {
   FHD_STAGE_ALL = 7
 };
 
+/* Option bits (fhd_opts.flags).
+ *
+ * FHD_FLAG_NO_MIRROR_PAIRS: turn off mirror pairing on the four-sample
+ *   matrix-core engine's hardware-trig path.  With pairing on (the default),
+ *   voxel groups of 16 T / vectors consecutive voxels take their reference
+ *   voxel at column V / 2; a group whose reference is exactly the negated
+ *   reference of another has, at every sample, the conjugate group phase
+ *   (e^{-i2 pi k.x} = conj e^{i2 pi k.x} for real k and x: PMPP ch. 17
+ *   section 17.3, the phase of Eq. 17.1), so one phase and four real products
+ *   give both groups' sums where two groups otherwise take two phases and
+ *   six products.  The pairing is found on the device and checked exactly
+ *   (coordinate equality); groups without a partner are summed alone.  On
+ *   this path the launch rows are chosen on the device too, between half and
+ *   twice the automatic count (exactly sample_splits when that is given), so
+ *   that the paired waves fill whole rounds of resident workgroups. */
+enum { FHD_FLAG_NO_MIRROR_PAIRS = 1 };
+
 /* Options; pass NULL for all defaults (accurate trig, blocked sum, automatic
  * engine and tuning, library-allocated workspace, all stages).  Start from
  * fhd_default_opts() so that fields added later keep their defaults. */
@@ -158,7 +175,7 @@ typedef struct fhd_opts {
                               contiguous share of the samples (partial sums, then a
                               fixed-order reduction); FHD_SUM_PLAIN always uses 1 */
   int32_t engine;          /* fhd_engine, default FHD_ENGINE_AUTO */
-  int32_t reserved;        /* must be 0 */
+  int32_t flags;           /* FHD_FLAG_* bits; 0 = defaults */
   void* workspace;         /* device buffer (16-byte aligned), or NULL: the library then allocates it
                               stream-ordered (hipMallocAsync/hipFreeAsync) for this
                               call; running the stages in separate calls requires a
@@ -365,6 +382,10 @@ typedef struct fhd_plan_info {
   int32_t sample_splits;    /* launch rows splitting the samples (forward: the voxel
                                groups); 1: no reduction step */
   int32_t engine;           /* FHD_ENGINE_VALU or FHD_ENGINE_MFMA */
+  int32_t mirror_pairs;     /* 1: the gather pairs mirror groups (FHD_FLAG_NO_MIRROR_PAIRS);
+                               the device then picks the launch rows, at most
+                               max_sample_splits */
+  int32_t max_sample_splits;/* most launch rows the plan's partial-sum buffer holds */
 } fhd_plan_info;
 
 /* Fills *info with the plan for these sizes and options (opts may be NULL);

@@ -39,6 +39,8 @@ FHD_STAGE_GATHER = 2
 FHD_STAGE_REDUCE = 4
 FHD_STAGE_ALL = 7
 
+FHD_FLAG_NO_MIRROR_PAIRS = 1
+
 # size of the device array behind fhd_compute_noalloc (FHD_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 512 << 20
 
@@ -58,7 +60,7 @@ class FhdOpts(ctypes.Structure):
         ("stages", ctypes.c_int32),
         ("sample_splits", ctypes.c_int32),
         ("engine", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -74,6 +76,8 @@ class FhdPlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("sample_splits", ctypes.c_int32),
         ("engine", ctypes.c_int32),
+        ("mirror_pairs", ctypes.c_int32),
+        ("max_sample_splits", ctypes.c_int32),
     ]
 
 

@@ -78,8 +78,17 @@ struct Plan {
   size_t flag_bytes;   // MFMA: per-wave regularity flags shared by the passes
   int64_t gpad[40];    // forward: padded group count of each pass
   int64_t g_split[40]; // forward: groups per launch row of each pass
+  int pair;            // four-sample engine, HW trig, row blocks: mirror-pair gather
+  int32_t rows_lo, rows_hi;  // launch rows the device picks from (pair); else both = splits
+  size_t pair_bytes;   // pair plan (header + list) shared by the passes
   size_t ws_bytes;
 };
+
+// Reference column of a mirror-pair pass: the middle of the group, so that
+// on a grid with coordinates i - L/2 the reference sits at x = 0 (or, for a
+// group of several per row, its partner group's middle mirrors it); column
+// 0 when the voxels do not reach it.
+int32_t pair_jref(int64_t N, int V) { return N > V / 2 ? V / 2 : 0; }
 
 // Launch-shape choices when the caller leaves them to the library; all
 // measured on MI355X (256 CUs x 4 SIMDs).  Waves of one gather launch all do
@@ -219,7 +228,7 @@ fhd_status validate(int64_t M, int64_t N, int32_t batch, const fhd_opts* o) {
   if (o->engine != FHD_ENGINE_AUTO && o->engine != FHD_ENGINE_VALU && o->engine != FHD_ENGINE_MFMA &&
       o->engine != FHD_ENGINE_MFMA16)
     return fail(FHD_ERR_INVALID_ARGUMENT, "unknown engine %d", o->engine);
-  if (o->reserved != 0) return fail(FHD_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
+  if (o->flags & ~FHD_FLAG_NO_MIRROR_PAIRS) return fail(FHD_ERR_INVALID_ARGUMENT, "unknown opts.flags bits 0x%x", o->flags);
   return FHD_OK;
 }
 
@@ -310,6 +319,31 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   // the four-sample engine's does; its accurate path folds tiles of ~sqrt(M)
   if (half && o->trig == FHD_TRIG_HW && o->tile == 0) p.tile = p.m_split;
   if (half && p.tile > p.m_split && p.m_split > 0) p.tile = p.m_split;
+  // mirror pairs: the four-sample engine summing each launch row as one block
+  // on the HW path; with automatic rows the device picks between half and
+  // twice the count above
+  p.pair = engine == FHD_ENGINE_MFMA && p.tiles == 8 && o->trig == FHD_TRIG_HW && p.tile >= p.m_split &&
+           !(o->flags & FHD_FLAG_NO_MIRROR_PAIRS);
+  p.rows_lo = p.rows_hi = p.splits;
+  if (p.pair && o->sample_splits == 0 && o->sum != FHD_SUM_PLAIN && p.mpad > 0) {
+    int64_t hi = 2 * (int64_t)p.splits;
+    const int64_t cap = max_splits(p.mpad, kMinSplitSamplesMfma);
+    const int64_t row_bytes = (int64_t)p.bc[0] * N * (int64_t)sizeof(fhd_c32);
+    if (hi > cap) hi = cap;
+    if (row_bytes > 0 && hi > kMaxPartialBytes / row_bytes) hi = kMaxPartialBytes / row_bytes;
+    const int64_t lo = (p.splits + 1) / 2;
+    p.rows_lo = (int32_t)lo;
+    p.rows_hi = (int32_t)(hi > lo ? hi : lo);
+  }
+  p.pair_bytes = 0;
+  if (p.pair) {
+    int64_t g = 0;
+    for (int i = 0; i < p.npass; ++i) {
+      const int64_t V = 16 * p.tiles / p.bc[i], gi = (N + V - 1) / V;
+      g = gi > g ? gi : g;
+    }
+    p.pair_bytes = align256(ncmri::pair_plan_bytes(g));
+  }
   p.ws_bytes = 0;
   p.hdr_bytes = mfma ? align256((size_t)p.mpad * ncmri::mfma_header_floats(p.trig) * sizeof(float)) : 0;
   for (int i = 0; i < p.npass; ++i) {
@@ -328,7 +362,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     p.ws_bytes += align256(p.pass_bytes[i]);
   }
   // one partial-sum buffer, reused by every pass (passes run in stream order)
-  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
+  p.partial_bytes = p.rows_hi > 1 ? (size_t)p.rows_hi * (size_t)p.bc[0] * (size_t)N * sizeof(fhd_c32) : 0;
   p.ws_bytes += align256(p.partial_bytes);
   // the matrix-core gather's per-wave regularity flags (the first pass has
   // the most waves: the most vectors per pass, the largest groups)
@@ -342,6 +376,7 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     p.flag_bytes = (size_t)w * sizeof(int32_t);
   }
   p.ws_bytes += align256(p.flag_bytes);
+  p.ws_bytes += p.pair_bytes;
   return FHD_OK;
 }
 
@@ -372,6 +407,8 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   const int64_t C = ncmri::kMfmaChunk;
   p.op = FHD_OP_FORWARD;
   p.is_q = 0;
+  p.pair = 0;
+  p.pair_bytes = 0;
   p.engine = half ? FHD_ENGINE_MFMA16 : FHD_ENGINE_MFMA;
   p.trig = o->trig;
   p.sum = o->sum;
@@ -434,6 +471,7 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
   }
   if (gmax == 0 || M == 0) splits = 1;
   p.splits = splits;
+  p.rows_lo = p.rows_hi = splits;
   for (int i = 0; i < p.npass; ++i) {
     int64_t gs = (p.gpad[i] + splits - 1) / splits;
     gs = (gs + C - 1) / C * C;
@@ -671,7 +709,7 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   } else if (p.stages != FHD_STAGE_ALL && p.ws_bytes > 0) {
     return fail(FHD_ERR_WORKSPACE, "running stages separately needs a caller workspace");
   }
-  if (p.npass > 1 && p.splits > 1 &&
+  if (p.npass > 1 && p.rows_hi > 1 &&
       ((p.stages & FHD_STAGE_GATHER) != 0) != ((p.stages & FHD_STAGE_REDUCE) != 0))
     return fail(FHD_ERR_INVALID_ARGUMENT,
                 "batch passes share the partial-sum buffer: run GATHER and REDUCE in the same call");
@@ -693,11 +731,13 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
   char* base = (char*)ws;
   float2* partial = nullptr;
   int32_t* flags = nullptr;
+  int32_t* pairplan = nullptr;
   {
     size_t recs = 0;
     for (int i = 0; i < p.npass; ++i) recs += align256(p.pass_bytes[i]);
     if (p.partial_bytes > 0) partial = (float2*)(base + recs);
     if (p.flag_bytes > 0) flags = (int32_t*)(base + recs + align256(p.partial_bytes));
+    if (p.pair_bytes > 0) pairplan = (int32_t*)(base + recs + align256(p.partial_bytes) + align256(p.flag_bytes));
   }
   int b0 = 0;
   const bool kahan = p.sum == FHD_SUM_KAHAN;
@@ -707,7 +747,9 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
     float2* outp = (float2*)(out + (int64_t)b0 * N);
     // the reduction only needs the output, partial buffer and sizes
     ncmri::GatherArgs ga{nullptr, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
-                         p.splits > 1 ? partial : nullptr};
+                         p.rows_hi > 1 ? partial : nullptr};
+    const int Vp = p.pair ? 16 * p.tiles / bc : 0;
+    const int32_t jref = p.pair ? pair_jref(N, Vp) : 0;
     hipError_t e = hipSuccess;
     const char* what = "records";
     if (p.engine == FHD_ENGINE_MFMA16) {
@@ -732,14 +774,22 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
       float* wb = (float*)(base + p.hdr_bytes);
       if (p.stages & FHD_STAGE_MU) {
         ncmri::MfmaRecordArgs ra{kx, ky, kz, x, y, z, (const float2*)phi, (const float2*)Dp,
-                                 M, N, p.mpad, hdr, wb};
+                                 M, N, p.mpad, hdr, wb, jref};
         e = ncmri::launch_mfma_records(is_q, p.trig, p.tiles, bc, ra, s);
       }
       if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
         what = "gather";
-        ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
-                           p.splits > 1 ? partial : nullptr, flags};
-        e = ncmri::launch_mfma_gather(p.trig, p.tiles, bc, p.splits, ma, s);
+        if (p.pair) {
+          const int64_t G = (N + Vp - 1) / Vp;
+          ncmri::PairPlanArgs pa{x, y, z, N, Vp, jref, G, flags, pairplan, 1, p.rows_lo, p.rows_hi, p.mpad};
+          ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+                             p.rows_hi > 1 ? partial : nullptr, flags, nullptr, nullptr, pairplan, jref, G};
+          e = ncmri::launch_mfma_pair_gather(bc, pa, ma, s);
+        } else {
+          ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+                             p.splits > 1 ? partial : nullptr, flags};
+          e = ncmri::launch_mfma_gather(p.trig, p.tiles, bc, p.splits, ma, s);
+        }
       }
     } else {
       ncmri::Layout L{is_q, p.trig, p.V, bc, ncmri::header_dwords(p.trig),
@@ -757,7 +807,8 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
     }
     if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE)) {
       what = "reduce";
-      e = ncmri::launch_reduce(bc, kahan, p.splits, ga, s);
+      e = p.pair ? ncmri::launch_reduce_dev_rows(bc, pairplan, ga, s)
+                 : ncmri::launch_reduce(bc, kahan, p.splits, ga, s);
     }
     if (e != hipSuccess) result = fail(FHD_ERR_HIP, "%s kernel launch: %s", what, hipGetErrorString(e));
     base += align256(p.pass_bytes[i]);
@@ -844,6 +895,8 @@ NCMRI_API fhd_status fhd_describe_plan(int64_t M, int64_t N, int32_t batch, int3
     info->workspace_bytes = p.ws_bytes;
     info->sample_splits = p.splits;
     info->engine = p.engine;
+    info->mirror_pairs = p.pair;
+    info->max_sample_splits = p.rows_hi;
     return FHD_OK;
   } catch (...) {
     return fail(FHD_ERR_INTERNAL, "unexpected C++ exception");

@@ -117,6 +117,7 @@ struct MfmaRecordArgs {
   int64_t M, N, mpad;    // mpad: multiple of kMfmaChunk
   float* hdr;            // [mpad][mfma_header_floats]
   float* wb;             // [mpad / 2][192 P] (P = T / 2)
+  int32_t jref;          // reference column: factors hold Mu_b exp(i 2 pi k.(x_j - x_jref))
 };
 
 struct MfmaArgs {
@@ -135,6 +136,33 @@ struct MfmaArgs {
   // half-split engine only (nullptr otherwise)
   const float2* mu;      // [mpad][BC] Mu_b of each sample in fp32 (the direct kernel's weights)
   const float* scale;    // [2]: the factors' scale 2^e and its inverse (of a [2 + 256] buffer)
+  // four-sample engine with mirror pairs (nullptr / 0 otherwise)
+  const int32_t* pairs;  // pair plan: kPairHeader int32 then the int2 list (see below)
+  int32_t jref;          // reference column of the factors (0 without pairs)
+  int64_t gcap;          // list slots (groups of the pass)
+};
+
+// Mirror pairs (four-sample engine, HW trig, each launch row one summation
+// block).  The pair plan, written on the device before the gather:
+//   [0] E list entries, [1] Cp of them paired (the first Cp), [2] launch rows R,
+//   [3] samples per row, [4] wave slots U = ceil(E / 16), [5] workgroup slots
+//   Q = ceil(U / kMfma4Waves) per row, [6] the index sum S of a pair (-1: none),
+//   then int2 entries (g, partner or -1): paired entries e < Cp at slot e,
+//   the others at slot gcap - 1 - (e - Cp).
+constexpr int kPairHeader = 16;
+constexpr int kPairResidentWgs = 2 * 256;  // resident 4-wave workgroups of the pair gather (2 per CU)
+inline size_t pair_plan_bytes(int64_t groups) { return (size_t)kPairHeader * 4 + (size_t)groups * 8; }
+
+struct PairPlanArgs {
+  const float* x; const float* y; const float* z;
+  int64_t N;
+  int32_t V, jref;
+  int64_t G;             // groups ceil(N / V): the list's slots
+  int32_t* flags;        // [ceil(G / 16)] regular waves
+  int32_t* plan;         // pair plan
+  int32_t pair;          // 0: every group alone (no partner search)
+  int32_t rows_lo, rows_hi;  // the device picks the launch rows in this range
+  int64_t mpad;
 };
 
 // ---------------------------------------------------------------------------
@@ -200,6 +228,13 @@ hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStrea
 // complex columns); BC: vectors of the pass.
 hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
                                hipStream_t s);
+// Mirror-pair gather of the four-sample engine (HW trig, rows one summation
+// block): pair plan kernels, the gather over the plan's list and the direct
+// kernel for irregular waves, with the device's launch rows (at most
+// pa.rows_hi; a.partial holds that many rows when pa.rows_hi > 1).
+hipError_t launch_mfma_pair_gather(int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s);
+// Adds the device-chosen rows' partial sums (rows from the pair plan).
+hipError_t launch_reduce_dev_rows(int BC, const int32_t* plan, const GatherArgs& a, hipStream_t s);
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,
                               hipStream_t s);
 // Half-split engine: scale, records; gather (regular waves) + direct kernel.

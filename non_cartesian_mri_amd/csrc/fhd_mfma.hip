@@ -164,14 +164,15 @@ mfma4_records_kernel(MfmaRecordArgs a, int is_q, int trig, int BC) {
     }
   }
   const double pr = a.phi[m].x, pim = a.phi[m].y;
-  const double x0 = a.x[0], y0 = a.y[0], z0 = a.z[0];
+  // offsets relative to the reference column jref (< N): its factor is Mu_b itself
+  const double x0 = a.x[a.jref], y0 = a.y[a.jref], z0 = a.z[a.jref];
   float fr[4], fi[4], fs[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int cc = 16 * (4 * g + i) + c;
     const int b = cc / V, j = cc % V;
     double cj = 1.0, sj = 0.0;
-    if (j > 0 && j < a.N) {
+    if (j != a.jref && j < a.N) {
       const double ph = (double)kx * ((double)a.x[j] - x0) + (double)ky * ((double)a.y[j] - y0) +
                         (double)kz * ((double)a.z[j] - z0);
       sincospi(2.0 * ph, &sj, &cj);
@@ -758,7 +759,8 @@ struct MfmaGather4 {
 // Direct gather for the irregular waves of the four-sample engine, over the
 // gather's launch rows as in MfmaDirect: lane l of wave w owns voxels
 // 16 V w + l + 64 i, i < V / 4, taken four at a time; records are read with
-// wave-uniform scalar loads (Mu_b = (fr, fi) of the offset-0 column of vector b).
+// wave-uniform scalar loads (Mu_b = (fr, fi) of the reference column jref of
+// vector b).  With a pair plan the launch rows are the plan's.
 template <int T, int BC, int TRIG>
 struct MfmaDirect4 {
   static constexpr int V = 16 * T / BC;
@@ -770,8 +772,13 @@ struct MfmaDirect4 {
     const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
     const int64_t vbase = wave * 16 * V;
     const int32_t row = (int32_t)blockIdx.y;
+    int64_t m_split = a.m_split;
+    if (a.pairs) {
+      if (row >= a.pairs[2]) return;
+      m_split = a.pairs[3];
+    }
     int64_t lo, hi;
-    row_range(a.m_split, a.mpad, row, lo, hi);
+    row_range(m_split, a.mpad, row, lo, hi);
     if (vbase >= a.N) return;
     if (a.flags[wave]) return;   // a regular wave: the gather kernel summed it
     constexpr int HF = mfma_header_floats(TRIG);
@@ -804,7 +811,7 @@ struct MfmaDirect4 {
           float mr[BC], mi[BC];
 #pragma unroll
           for (int b = 0; b < BC; ++b) {
-            const int cc = b * V, t = cc / 16, p = 16 * k + cc % 16;
+            const int cc = b * V + a.jref, t = cc / 16, p = 16 * k + cc % 16;
             mr[b] = blk[((t >> 2) * 64 + p) * 4 + (t & 3)];
             mi[b] = blk[(((T + t) >> 2) * 64 + p) * 4 + ((T + t) & 3)];
           }
@@ -837,6 +844,362 @@ struct MfmaDirect4 {
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// Mirror pairs of the four-sample engine (HW trig, each launch row summed as
+// one block).  Take each group's reference at column jref, x_g = x[g V + jref],
+// with factors f_j = Mu exp(i 2 pi k.(x_j - x_jref)).  A group h whose
+// reference is exactly -x_g holds at column j the voxel -x_g + (x_j - x_jref)
+// (both groups on the common offsets), so with (c, s) = (cos, sin)(2 pi k.x_g)
+//   out[g][j] = sum_m (c + i s) f_j,      out[h][j] = sum_m (c - i s) f_j
+// (e^{-i t} = conj e^{i t} for a real phase t).  Four real products
+//   Pcr = sum c fr,  Pci = sum c fi,  Psr = sum s fr,  Psi = sum s fi
+// give out[g] = (Pcr - Psi, Pci + Psr) and out[h] = (Pcr + Psi, Pci - Psr):
+// one phase and 4 MFMAs per tile for two groups, where the three-product form
+// takes two phases and 6 MFMAs.  On a grid with coordinates i - L/2 and jref
+// the middle column, the partner of row (y, z) is row (-y, -z).
+
+// Regularity of the gather's waves (the vote of the gather kernels), also
+// requiring every present group's reference voxel to exist.
+template <int V>
+__global__ void __launch_bounds__(kWorkgroup) pair_flags_kernel(PairPlanArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kWorkgroup / 64) + (threadIdx.x >> 6);
+  const int64_t vbase = wave * 16 * V;
+  if (vbase >= a.N) return;
+  const int64_t n0 = vbase + (int64_t)(lane & 15) * V;
+  const bool gin = n0 < a.N;
+  const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
+  bool reg = wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
+  reg = __all(reg && (!gin || n0 + a.jref < a.N));
+  if (lane == 0) a.flags[wave] = reg ? 1 : 0;
+}
+
+constexpr int kListThreads = 1024;
+constexpr int kListPer = 8;   // groups per thread and step of the list kernel
+
+// Block-wide max / min of an int64 (every thread gets the result).
+__device__ __forceinline__ int64_t block_reduce64(int64_t v, bool is_max, int64_t* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int64_t o = __shfl_xor(v, d);
+    v = is_max ? (o > v ? o : v) : (o < v ? o : v);
+  }
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  v = sh[0];
+  for (int i = 1; i < kListThreads / 64; ++i) v = is_max ? (sh[i] > v ? sh[i] : v) : (sh[i] < v ? sh[i] : v);
+  __syncthreads();
+  return v;
+}
+
+// Exclusive block scan of two counts; also returns the block totals.
+__device__ __forceinline__ void block_exscan2(int a, int b, int& ea, int& eb, int& ta, int& tb, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int xa = __shfl_up(ia, d), xb = __shfl_up(ib, d);
+    if (lane >= d) { ia += xa; ib += xb; }
+  }
+  if (lane == 63) { sh[w] = ia; sh[16 + w] = ib; }
+  __syncthreads();
+  int oa = 0, ob = 0;
+  ta = 0; tb = 0;
+  for (int i = 0; i < kListThreads / 64; ++i) {
+    if (i < w) { oa += sh[i]; ob += sh[16 + i]; }
+    ta += sh[i]; tb += sh[16 + i];
+  }
+  __syncthreads();
+  ea = oa + ia - a;
+  eb = ob + ib - b;
+}
+
+// One workgroup: finds the index sum S of the mirror pairs from the last full
+// group of a regular wave and its mirror, classifies every group (partner
+// h = S - g checked exactly: both full, on regular waves, reference -x_g;
+// the smaller index of a pair is listed with its partner, the larger not at
+// all; every other group of a regular wave alone) and lists them in index
+// order, then picks the launch rows: in [rows_lo, rows_hi] the count whose
+// workgroups (Q per row) fill whole rounds of the resident slots best, the
+// fewest rows among equals.
+__global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a) {
+  __shared__ int64_t red[kListThreads / 64];
+  __shared__ int scan[32];
+  const int tid = threadIdx.x;
+  const int64_t V = a.V, G = a.G, Gfull = a.N / a.V;
+  const int64_t waves = (G + 15) / 16;
+  int64_t last = -1;
+  for (int64_t w = tid; w < waves; w += kListThreads) {
+    if (!a.flags[w]) continue;
+    int64_t g = 16 * w + 15;
+    if (g > Gfull - 1) g = Gfull - 1;
+    if (g >= 16 * w && g > last) last = g;
+  }
+  last = block_reduce64(last, true, red);
+  int64_t S = -1;
+  if (a.pair && last >= 0) {
+    const int64_t rb = last * V + a.jref;
+    const float tx = -a.x[rb], ty = -a.y[rb], tz = -a.z[rb];
+    for (int64_t base = 0; base < Gfull; base += (int64_t)kListThreads * kListPer) {
+      int64_t mine = INT64_MAX;
+      for (int i = 0; i < kListPer; ++i) {
+        const int64_t g = base + (int64_t)i * kListThreads + tid;
+        if (g < Gfull && a.flags[g >> 4]) {
+          const int64_t r = g * V + a.jref;
+          if (a.x[r] == tx && a.y[r] == ty && a.z[r] == tz && g < mine) mine = g;
+        }
+      }
+      const int64_t found = block_reduce64(mine, false, red);
+      if (found != INT64_MAX) {
+        S = last + found;
+        break;
+      }
+    }
+  }
+  int2* list = reinterpret_cast<int2*>(a.plan + kPairHeader);
+  int64_t cp = 0, cs = 0;
+  for (int64_t base = 0; base < G; base += (int64_t)kListThreads * kListPer) {
+    const int64_t g0 = base + (int64_t)tid * kListPer;
+    int part[kListPer];  // -2: not listed, -1: alone, else the partner
+    int np = 0, ns = 0;
+#pragma unroll
+    for (int i = 0; i < kListPer; ++i) {
+      const int64_t g = g0 + i;
+      part[i] = -2;
+      if (g >= G || !a.flags[g >> 4]) continue;
+      part[i] = -1;
+      const int64_t h = S - g;
+      if (S >= 0 && g < Gfull && h >= 0 && h < Gfull && h != g && a.flags[h >> 4]) {
+        const int64_t rg = g * V + a.jref, rh = h * V + a.jref;
+        if (a.x[rh] == -a.x[rg] && a.y[rh] == -a.y[rg] && a.z[rh] == -a.z[rg]) part[i] = h > g ? (int)h : -2;
+      }
+      np += part[i] >= 0;
+      ns += part[i] == -1;
+    }
+    int ep, es, tp, ts;
+    block_exscan2(np, ns, ep, es, tp, ts, scan);
+    int64_t wp = cp + ep, wsg = cs + es;
+#pragma unroll
+    for (int i = 0; i < kListPer; ++i) {
+      const int g = (int)(g0 + i);
+      if (part[i] >= 0) list[wp++] = make_int2(g, part[i]);
+      else if (part[i] == -1) list[G - 1 - (wsg++)] = make_int2(g, -1);
+    }
+    cp += tp;
+    cs += ts;
+  }
+  if (tid == 0) {
+    const int64_t E = cp + cs, U = (E + 15) / 16, Q = (U + kMfma4Waves - 1) / kMfma4Waves;
+    int32_t R = a.rows_lo;
+    int64_t ms = 0;
+    double best = -1.0;
+    for (int32_t r = a.rows_lo; r <= a.rows_hi; ++r) {
+      int64_t m = (a.mpad + r - 1) / r;
+      m = (m + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
+      const int64_t reff = m > 0 ? (a.mpad + m - 1) / m : 1;
+      if (reff != r && r != a.rows_lo) continue;  // a count that leaves empty rows
+      const int64_t items = Q * reff, rounds = (items + kPairResidentWgs - 1) / kPairResidentWgs;
+      const double eff = rounds > 0 ? (double)items / (double)(rounds * kPairResidentWgs) : 1.0;
+      if (eff > best + 1e-3) {
+        best = eff;
+        R = (int32_t)(reff < 1 ? 1 : reff);
+        ms = m;
+      }
+    }
+    a.plan[0] = (int32_t)E;
+    a.plan[1] = (int32_t)cp;
+    a.plan[2] = R;
+    a.plan[3] = (int32_t)ms;
+    a.plan[4] = (int32_t)U;
+    a.plan[5] = (int32_t)Q;
+    a.plan[6] = (int32_t)(S < 0 ? -1 : S);
+  }
+}
+
+// The gather over the pair plan's list: workgroup item = (row, Q slot),
+// row-major, each wave 16 list entries.  Waves whose first entry is paired
+// run the four-product chunk (a single among them gets its out[g] only);
+// waves of singles run the three-product chunk of MfmaGather4.  The chunk
+// staging and loop shape are MfmaGather4's.
+template <int BC>
+struct MfmaPairGather4 {
+  static constexpr int T = 8;
+  using Base = MfmaGather4<T, BC, kTrigHw, false>;
+  static constexpr int V = Base::V, C = Base::C, NW = Base::NW, QF = Base::QF, HK = Base::HK, NH = Base::NH;
+
+  // fr (u = 0) and fi (u = 1) slices 2 u + h of block q: bv[u T + t], t in half h
+  __device__ static __forceinline__ void load_pair_half(const float* __restrict__ wb, int q, int lane, int h,
+                                                        float (&bv)[2 * T]) {
+    const float* pp = wb + q * QF;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sl = 2 * u + h;
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  template <int H>
+  __device__ static __forceinline__ void mfmas_pair_half(float c, float s, const float (&bv)[2 * T],
+                                                         f32x4 (&acc)[3][T], f32x4 (&accx)[T]) {
+#pragma unroll
+    for (int u = 0; u < T / 2; ++u) {
+      const int t = H * (T / 2) + u;
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv[t], acc[0][t], 0, 0, 0);
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv[T + t], acc[1][t], 0, 0, 0);
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s, bv[t], acc[2][t], 0, 0, 0);
+      accx[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s, bv[T + t], accx[t], 0, 0, 0);
+    }
+  }
+
+  // One chunk of the four-product form, pipelined as the three-product HW chunk.
+  __device__ static __forceinline__ void pair_chunk(const float* __restrict__ hb, const float* __restrict__ wb,
+                                                    int lane, float rx, float ry, float rz, f32x4 (&acc)[3][T],
+                                                    f32x4 (&accx)[T]) {
+    constexpr int NQ = C / 4;
+    float hc[HK], bv[2 * T];
+    Base::load_header(hb, 0, lane, hc);
+    load_pair_half(wb, 0, lane, 0, bv);
+    load_pair_half(wb, 0, lane, 1, bv);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float hn[HK];
+      if (q + 1 < NQ) Base::load_header(hb, q + 1, lane, hn);
+      sched_fence();
+      float c, s;
+      phase_sincos<kTrigHw>(hc, rx, ry, rz, c, s);
+      mfmas_pair_half<0>(c, s, bv, acc, accx);
+      sched_fence();
+      if (q + 1 < NQ) load_pair_half(wb, q + 1, lane, 0, bv);
+      sched_fence();
+      mfmas_pair_half<1>(c, s, bv, acc, accx);
+      sched_fence();
+      if (q + 1 < NQ) {
+        load_pair_half(wb, q + 1, lane, 1, bv);
+#pragma unroll
+        for (int i = 0; i < HK; ++i) hc[i] = hn[i];
+      }
+      sched_fence();
+    }
+  }
+
+  __device__ static __forceinline__ int2 entry(const int2* list, int64_t e, int64_t E, int64_t Cp, int64_t gcap) {
+    if (e >= E) return make_int2(-1, -1);
+    return list[e < Cp ? e : gcap - 1 - (e - Cp)];
+  }
+
+  // The chunk loop and write-out of one wave: PAIRED takes the four-product
+  // chunk, else the three-product one (skipped by waves past the list).  Both
+  // forms stage and wait in the same sequence, so the waves of a workgroup
+  // may take different forms.
+  template <bool PAIRED>
+  __device__ static __forceinline__ void loop(const MfmaArgs& a, int64_t lo, int32_t nch, int wig, int lane,
+                                              bool live, float rx, float ry, float rz, float4* sb0,
+                                              float4* sb1, float4* sh0, float4* sh1, float2* dst,
+                                              const int2* list, int64_t e0, int64_t E, int64_t Cp) {
+    f32x4 acc[3][T], accx[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
+      if constexpr (PAIRED) accx[t] = f32x4{};
+    }
+    auto chunk = [&](const float4* sh, const float4* sb) {
+      const float* hb = reinterpret_cast<const float*>(sh);
+      const float* wb = reinterpret_cast<const float*>(sb);
+      if constexpr (PAIRED)
+        pair_chunk(hb, wb, lane, rx, ry, rz, acc, accx);
+      else if (live)
+        Base::regular_chunk(hb, wb, lane, rx, ry, rz, acc);
+    };
+    if (nch > 0) Base::stage(a, lo, wig, lane, sb0, sh0);
+    Base::publish();
+    int32_t ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      Base::stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      chunk(sh0, sb0);
+      Base::publish();
+      if (ch + 2 < nch) Base::stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+      chunk(sh1, sb1);
+      Base::publish();
+    }
+    if (ch < nch) {
+      chunk(sh0, sb0);
+      Base::publish();
+    }
+    if (!live) return;
+    const int c = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * (lane >> 4) + r;
+      const int2 en = entry(list, e0 + i, E, Cp, a.gcap);
+      if (en.x < 0) continue;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int cc = 16 * t + c;
+        const int b = cc / V, j = cc % V;
+        const int64_t n = (int64_t)en.x * V + j;
+        if constexpr (PAIRED) {
+          if (n < a.N) dst[(int64_t)b * a.N + n] = make_float2(acc[0][t][r] - accx[t][r], acc[1][t][r] + acc[2][t][r]);
+          if (en.y >= 0)
+            dst[(int64_t)b * a.N + (int64_t)en.y * V + j] =
+                make_float2(acc[0][t][r] + accx[t][r], acc[1][t][r] - acc[2][t][r]);
+        } else if (n < a.N) {
+          dst[(int64_t)b * a.N + n] = make_float2(acc[0][t][r] - acc[2][t][r], acc[1][t][r] + acc[2][t][r]);
+        }
+      }
+    }
+  }
+
+  __device__ static void run(const MfmaArgs& a) {
+    __shared__ float4 sb0[C / 4 * QF / 4], sb1[C / 4 * QF / 4];
+    __shared__ float4 sh0[NH], sh1[NH];
+    const int32_t* P = a.pairs;
+    const int64_t E = P[0], Cp = P[1], U = P[4], Q = P[5];
+    const int32_t R = P[2];
+    const int64_t m_split = P[3];
+    const int64_t item = blockIdx.x;
+    if (item >= Q * R) return;   // the whole workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int32_t row = (int32_t)(item / Q);
+    const int64_t slot = (item - (int64_t)row * Q) * NW + wig;
+    const bool live = slot < U;
+    const bool paired = live && slot * 16 < Cp;
+    const int2* list = reinterpret_cast<const int2*>(P + kPairHeader);
+    const int2 me = entry(list, slot * 16 + (lane & 15), E, Cp, a.gcap);
+    float rx = 0.0f, ry = 0.0f, rz = 0.0f;
+    if (me.x >= 0) {
+      const int64_t r = (int64_t)me.x * V + a.jref;
+      rx = a.x[r]; ry = a.y[r]; rz = a.z[r];
+    }
+    int64_t lo, hi;
+    row_range(m_split, a.mpad, row, lo, hi);
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+    if (paired)
+      loop<true>(a, lo, nch, wig, lane, live, rx, ry, rz, sb0, sb1, sh0, sh1, dst, list, slot * 16, E, Cp);
+    else
+      loop<false>(a, lo, nch, wig, lane, live, rx, ry, rz, sb0, sb1, sh0, sh1, dst, list, slot * 16, E, Cp);
+  }
+};
+
+// Adds the pair plan's launch rows of partial sums in row order.
+__global__ void __launch_bounds__(kWorkgroup)
+reduce_dev_rows_kernel(const float2* __restrict__ partial, float2* __restrict__ out, int64_t count,
+                       const int32_t* __restrict__ plan) {
+  const int64_t i = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  if (i >= count) return;
+  const int32_t rows = plan[2];
+  float re = 0.0f, im = 0.0f;
+  for (int32_t p = 0; p < rows; ++p) {
+    const float2 v = partial[(int64_t)p * count + i];
+    re += v.x;
+    im += v.y;
+  }
+  out[i] = make_float2(re, im);
+}
 
 // Resident waves per SIMD the gather is compiled for: 4 with one tile of 32
 // complex columns (48 accumulators + 32 running totals, <= 128 VGPRs; 25 KB
@@ -873,6 +1236,36 @@ mfma4_gather_kernel(MfmaArgs a) {
 template <int T, int BC, int TRIG>
 __global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a) {
   MfmaDirect4<T, BC, TRIG>::run(a);
+}
+
+// Mirror-pair gather: 128 accumulators, 2 waves per SIMD (two 4-wave
+// workgroups per CU, kPairResidentWgs in all).
+template <int BC>
+__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
+mfma4_pair_kernel(MfmaArgs a) {
+  MfmaPairGather4<BC>::run(a);
+}
+
+struct PairFns {
+  void (*flags)(PairPlanArgs);
+  void (*gather)(MfmaArgs);
+  void (*direct)(MfmaArgs);
+};
+
+template <int BC>
+PairFns pair_fns() {
+  return {pair_flags_kernel<128 / BC>, mfma4_pair_kernel<BC>, mfma4_direct_kernel<8, BC, kTrigHw>};
+}
+
+PairFns select_pair(int BC) {
+  switch (BC) {
+    case 1: return pair_fns<1>();
+    case 2: return pair_fns<2>();
+    case 4: return pair_fns<4>();
+    case 8: return pair_fns<8>();
+    case 16: return pair_fns<16>();
+    default: return {nullptr, nullptr, nullptr};
+  }
 }
 
 using MfmaFn = void (*)(MfmaArgs);
@@ -936,6 +1329,41 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
   const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
   hipLaunchKernelGGL(mfma_records_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, is_q,
                      trig, T, BC);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_pair_gather(int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s) {
+  const PairFns fn = select_pair(BC);
+  if (!fn.gather || !a.pairs || a.pairs != pa.plan || !a.flags || a.flags != pa.flags || pa.V != 128 / BC ||
+      pa.rows_lo < 1 || pa.rows_hi < pa.rows_lo || (pa.rows_hi > 1 && !a.partial) || pa.jref < 0 ||
+      pa.jref >= pa.V || (pa.N > 0 && pa.jref >= pa.N) || a.jref != pa.jref || a.gcap != pa.G ||
+      pa.G != (pa.N + pa.V - 1) / pa.V || a.N != pa.N || a.mpad != pa.mpad || a.mpad % kMfmaChunk != 0)
+    return hipErrorInvalidValue;
+  if (a.N <= 0) return hipSuccess;
+  const int64_t waves = mfma_gather_waves(a.N, 8, BC);
+  const int64_t fblocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  hipLaunchKernelGGL(fn.flags, dim3((unsigned)fblocks), dim3(kWorkgroup), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_list_kernel, dim3(1), dim3(kListThreads), 0, s, pa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // workgroup items: at most every wave alone (Q <= waves / 4) on the most rows
+  const int64_t qmax = (waves + kMfma4Waves - 1) / kMfma4Waves;
+  hipLaunchKernelGGL(fn.gather, dim3((unsigned)(qmax * pa.rows_hi)), dim3(64 * kMfma4Waves), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn.direct, dim3((unsigned)fblocks, (unsigned)pa.rows_hi), dim3(kWorkgroup), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_dev_rows(int BC, const int32_t* plan, const GatherArgs& a, hipStream_t s) {
+  if (!a.partial || a.N <= 0) return hipSuccess;
+  if (!plan) return hipErrorInvalidValue;
+  const int64_t count = (int64_t)BC * a.N;
+  const int64_t rblocks = (count + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(reduce_dev_rows_kernel, dim3((unsigned)rblocks), dim3(kWorkgroup), 0, s, a.partial, a.out,
+                     count, plan);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ _STAGES = {"all": _lib.FHD_STAGE_ALL, "mu": _lib.FHD_STAGE_MU, "gather": _lib.FH
 
 
 def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages="all",
-              workspace: torch.Tensor | None = None, sample_splits=0, engine="auto") -> _lib.FhdOpts:
+              workspace: torch.Tensor | None = None, sample_splits=0, engine="auto",
+              mirror_pairs=True) -> _lib.FhdOpts:
     o = _lib.FhdOpts()
     _lib.load().fhd_default_opts(ctypes.byref(o))
     o.trig = _TRIG[trig] if isinstance(trig, str) else int(trig)
@@ -34,6 +35,7 @@ def make_opts(trig="accurate", sum="blocked", voxels_per_lane=0, tile=0, stages=
     o.stages = _STAGES[stages] if isinstance(stages, str) else int(stages)
     o.sample_splits = int(sample_splits)
     o.engine = _ENGINE[engine] if isinstance(engine, str) else int(engine)
+    o.flags = 0 if mirror_pairs else _lib.FHD_FLAG_NO_MIRROR_PAIRS
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -92,7 +94,7 @@ def _stream_ptr(stream) -> int:
 
 def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
                 voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
-                stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
+                stream=None, sample_splits=0, engine="auto", mirror_pairs=True) -> torch.Tensor:
     """F^H D on the GPU.  D is complex64 [M] or [B, M]; returns complex64 [N] or [B, N].
 
     The work is enqueued on `stream` (default: torch's current stream).
@@ -118,9 +120,10 @@ def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
     if workspace is None:
         nbytes = fhd_workspace_bytes(M, N, B, False, trig=trig, sum=sum,
                                      voxels_per_lane=voxels_per_lane, tile=tile,
-                                     sample_splits=sample_splits, engine=engine)
+                                     sample_splits=sample_splits, engine=engine,
+                                     mirror_pairs=mirror_pairs)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine, mirror_pairs)
     st = _lib.load().fhd_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                  y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
                                  out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
@@ -130,7 +133,7 @@ def fhd_compute(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
 
 def fhd_compute_noalloc(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="blocked",
                         voxels_per_lane=0, tile=0, out=None, stream=None, sample_splits=0,
-                        engine="auto") -> torch.Tensor:
+                        engine="auto", mirror_pairs=True) -> torch.Tensor:
     """F^H D through the allocation-free entry point: the library's fixed device
     array is the workspace (no device allocation by the library).  Same
     arguments as fhd_compute without workspace and stages; pass `out` to keep
@@ -153,7 +156,7 @@ def fhd_compute_noalloc(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="bl
         _dev_c64(out, "out")
         if out.numel() != B * N:
             raise ValueError("out must hold B*N complex values")
-    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine)
+    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine, mirror_pairs)
     st = _lib.load().fhd_compute_noalloc(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                          y.data_ptr(), z.data_ptr(), phi.data_ptr(), D2.data_ptr(),
                                          out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))
@@ -163,7 +166,7 @@ def fhd_compute_noalloc(kx, ky, kz, x, y, z, phi, D, *, trig="accurate", sum="bl
 
 def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
               voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
-              stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
+              stream=None, sample_splits=0, engine="auto", mirror_pairs=True) -> torch.Tensor:
     """Q on the GPU: complex64 [N]."""
     for n, t in (("kx", kx), ("ky", ky), ("kz", kz), ("x", x), ("y", y), ("z", z)):
         _dev_f32(t, n)
@@ -180,9 +183,10 @@ def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
     if workspace is None:
         nbytes = fhd_workspace_bytes(M, N, 1, True, trig=trig, sum=sum,
                                      voxels_per_lane=voxels_per_lane, tile=tile,
-                                     sample_splits=sample_splits, engine=engine)
+                                     sample_splits=sample_splits, engine=engine,
+                                     mirror_pairs=mirror_pairs)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine, mirror_pairs)
     st = _lib.load().q_compute(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                y.data_ptr(), z.data_ptr(), phi.data_ptr(), out.data_ptr(),
                                M, N, ctypes.byref(o), _stream_ptr(stream))
@@ -255,7 +259,7 @@ def toeplitz_lengths(shape) -> tuple[int, int, int]:
 
 def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked",
                         voxels_per_lane=0, tile=0, sample_splits=0, engine="auto",
-                        out=None, stream=None) -> torch.Tensor:
+                        out=None, stream=None, mirror_pairs=True) -> torch.Tensor:
     """Qhat for an image grid of `shape` = (nz, ny, nx): pz * py * px float32 values,
     returned as a [pz, py, px] tensor whose storage order is the library's
     (blocks of min(32, px py) consecutive (ky, kx) columns, kz-major within a
@@ -281,7 +285,7 @@ def fhd_toeplitz_kernel(kx, ky, kz, phi, shape, *, trig="accurate", sum="blocked
             raise TypeError("out must be a contiguous float32 CUDA tensor")
         if out.numel() != plen[0] * plen[1] * plen[2]:
             raise ValueError("out must hold pz * py * px floats")
-    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine)
+    o = make_opts(trig, sum, voxels_per_lane, tile, "all", None, sample_splits, engine, mirror_pairs)
     st = _lib.load().fhd_toeplitz_kernel(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), phi.data_ptr(),
                                          M, nx, ny, nz, out.data_ptr(), ctypes.byref(o),
                                          _stream_ptr(stream))

@@ -52,9 +52,9 @@ def test_opts_struct_layout(lib):
     o.engine = 5
     lib.fhd_default_opts(ctypes.byref(o))
     assert (o.trig, o.sum, o.voxels_per_lane, o.tile, o.stages, o.sample_splits) == (0, 0, 0, 0, 7, 0)
-    assert (o.engine, o.reserved) == (_lib.FHD_ENGINE_AUTO, 0)
+    assert (o.engine, o.flags) == (_lib.FHD_ENGINE_AUTO, 0)
     assert o.workspace is None and o.workspace_bytes == 0
-    assert ctypes.sizeof(_lib.FhdPlanInfo) == 40
+    assert ctypes.sizeof(_lib.FhdPlanInfo) == 48
 
 
 def test_status_strings_and_version(lib):
@@ -120,7 +120,7 @@ def test_stage_combinations(lib):
     ("trig", 2), ("trig", -1), ("sum", 3), ("voxels_per_lane", 3), ("voxels_per_lane", 48),
     ("voxels_per_lane", 256),
     ("tile", -4), ("stages", 8), ("sample_splits", -1), ("sample_splits", 1025),
-    ("engine", 4), ("engine", -1), ("reserved", 1),
+    ("engine", 4), ("engine", -1), ("flags", 2), ("flags", -1),
 ])
 def test_bad_options(lib, field, value):
     assert _fhd(lib, opts=_opts(**{field: value})) == _lib.FHD_ERR_INVALID_ARGUMENT
@@ -344,8 +344,17 @@ def test_describe_plan_mfma(lib):
     assert acc["tile"] == 512
     # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
-    # headers, factors, 16 rows of partial sums, 1024 per-wave flags
-    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8 + 1024 * 4
+    # the HW path pairs mirror groups and picks its rows on the device, at most
+    # twice the automatic count: headers, factors, 32 rows of partial sums, 1024
+    # per-wave flags, the pair plan (16 int32 header, one int2 per group)
+    assert hw["mirror_pairs"] == 1 and hw["max_sample_splits"] == 32
+    assert acc["mirror_pairs"] == 0 and acc["max_sample_splits"] == acc["sample_splits"] == 16
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 32 * 128 ** 3 * 8 + 1024 * 4 + (64 + 16384 * 8 + 255) // 256 * 256
+    off = fhd_describe_plan(262144, 128 ** 3, trig="hw", mirror_pairs=False)
+    assert off["mirror_pairs"] == 0 and off["max_sample_splits"] == 16
+    assert off["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8 + 1024 * 4
+    fixed = fhd_describe_plan(262144, 128 ** 3, trig="hw", sample_splits=12)
+    assert fixed["mirror_pairs"] == 1 and fixed["max_sample_splits"] == fixed["sample_splits"] == 12
     # groups of 64 (T = 4) or 32 (T = 2) on request, two-sample engine
     four = fhd_describe_plan(262144, 128 ** 3, trig="hw", voxels_per_lane=64)
     assert four["voxels_per_lane"] == 64 and four["record_dwords"] == 4 + 192
