@@ -55,7 +55,7 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # the kernel source it was taken on, like TRAFFIC below)
 MFMA_BUSY = {
     ("fhd_128cube_262144_spirals", "hw", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0", "busy": 0.925,
+        "source": "fhd_mfma.hip", "kernel_sha256": "34dee8804c3af7cd", "busy": 0.928,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", 128): {
         "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0", "busy": 0.851,
@@ -80,8 +80,8 @@ def method_roofline(kind: str, B: int) -> dict:
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0",
-        "fetch_bytes": 1801995.4 * 1024 * 2.0, "write_bytes": 262153.1 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "34dee8804c3af7cd",
+        "fetch_bytes": 2556809.1 * 1024 * 2.0, "write_bytes": 497756.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
         "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0",
@@ -488,19 +488,19 @@ def traffic_for(config: str, trig: str, summ: str, engine: str, group: int, gath
 
 def mirror_pair_work(ws, ws_bytes: int, p, plan: dict) -> dict:
     """The pair plan the device wrote for the last gather pass (at the end of
-    the workspace: 16 int32 of header, then one int2 per voxel group), and the
-    matrix work it implies: per block of four samples a wave of paired groups
-    issues 4 MFMAs per tile of 16 columns (8 tiles), a wave of groups alone 3;
-    each v_mfma_f32_16x16x4_f32 is 16 x 16 x 4 multiply-adds."""
+    the workspace: 16 int32 of header, one int2 per voxel group, then each
+    group's reference voxel as a float4), and the
+    matrix work it implies: per block of four samples every wave of 16 list
+    entries (a group with its partner, or a group alone) issues 4 MFMAs per
+    tile of 16 columns (8 tiles); the unpaired kernel's waves of 16 groups
+    issue 3.  Each v_mfma_f32_16x16x4_f32 is 16 x 16 x 4 multiply-adds."""
     V = plan["voxels_per_lane"]
     G = -(-p.N // V)
-    pair_bytes = (64 + 8 * G + 255) // 256 * 256
+    pair_bytes = ((64 + 8 * G + 15) // 16 * 16 + 16 * G + 255) // 256 * 256
     head = ws[ws_bytes - pair_bytes:ws_bytes - pair_bytes + 64].view(torch_int32()).cpu().numpy()
     E, Cp, R, U = int(head[0]), int(head[1]), int(head[2]), int(head[4])
-    slots_p = -(-Cp // 16)
-    slots_s = U - slots_p
     mpad = plan["padded_samples"]
-    mfmas = (slots_p * 32 + slots_s * 24) * (mpad // 4) * plan["passes"]
+    mfmas = U * 32 * (mpad // 4) * plan["passes"]
     flop = mfmas * 16 * 16 * 4 * 2
     alone_mfmas = -(-G // 16) * 24 * (mpad // 4) * plan["passes"]
     return {"paired_groups": Cp, "groups_alone": E - Cp, "groups": G, "launch_rows": R,

@@ -84,11 +84,6 @@ struct Plan {
   size_t ws_bytes;
 };
 
-// Reference column of a mirror-pair pass: the middle of the group, so that
-// on a grid with coordinates i - L/2 the reference sits at x = 0 (or, for a
-// group of several per row, its partner group's middle mirrors it); column
-// 0 when the voxels do not reach it.
-int32_t pair_jref(int64_t N, int V) { return N > V / 2 ? V / 2 : 0; }
 
 // Launch-shape choices when the caller leaves them to the library; all
 // measured on MI355X (256 CUs x 4 SIMDs).  Waves of one gather launch all do
@@ -136,6 +131,22 @@ int64_t cube_edge(int64_t N) {
   for (int64_t c = L > 1 ? L - 1 : 1; c <= L + 1; ++c)
     if (c * c * c == N) return c;
   return 0;
+}
+
+// Reference column of a mirror-pair pass.  On an L^3 grid with coordinates
+// (i - L/2) step, x fastest: a group of V <= L voxels is a segment of a row
+// and its middle column V / 2 mirrors the middle of the opposite segment of
+// the mirror row (segment q of L / V onto L / V - 1 - q); a group of V = k L
+// voxels is k whole rows, and the voxel x = 0 of its row k / 2, column
+// V / 2 + L / 2, mirrors that of the group whose rows are mirrored in reverse
+// order.  Either way every group whose rows have a mirror row is paired.
+// Other voxel sets take the middle column.  Column 0 when the voxels do not
+// reach the choice.
+int32_t pair_jref(int64_t N, int V) {
+  const int64_t L = cube_edge(N);
+  int64_t j = V / 2;
+  if (L > 0 && V > L && V % L == 0) j = V / 2 + L / 2;
+  return N > j ? (int32_t)j : 0;
 }
 
 // Whether groups of V consecutive voxels (x fastest) of an L^3 grid all sit
@@ -326,7 +337,13 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
            !(o->flags & FHD_FLAG_NO_MIRROR_PAIRS);
   p.rows_lo = p.rows_hi = p.splits;
   if (p.pair && o->sample_splits == 0 && o->sum != FHD_SUM_PLAIN && p.mpad > 0) {
+    // at most twice the rows, or enough for every SIMD's 3 waves when about
+    // half the waves remain after pairing (plus a quarter for the device to
+    // round to whole rounds)
     int64_t hi = 2 * (int64_t)p.splits;
+    const int64_t half = (ncmri::mfma_gather_waves(N, p.tiles, p.bc[0]) + 1) / 2;
+    const int64_t fill = (3 * kSimds + half - 1) / half;
+    if (fill + fill / 4 > hi) hi = fill + fill / 4;
     const int64_t cap = max_splits(p.mpad, kMinSplitSamplesMfma);
     const int64_t row_bytes = (int64_t)p.bc[0] * N * (int64_t)sizeof(fhd_c32);
     if (hi > cap) hi = cap;
@@ -781,7 +798,8 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
         what = "gather";
         if (p.pair) {
           const int64_t G = (N + Vp - 1) / Vp;
-          ncmri::PairPlanArgs pa{x, y, z, N, Vp, jref, G, flags, pairplan, 1, p.rows_lo, p.rows_hi, p.mpad};
+          float4* refs = (float4*)((char*)pairplan + ncmri::pair_list_bytes(G));
+          ncmri::PairPlanArgs pa{x, y, z, N, Vp, jref, G, flags, pairplan, refs, 1, p.rows_lo, p.rows_hi, p.mpad};
           ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
                              p.rows_hi > 1 ? partial : nullptr, flags, nullptr, nullptr, pairplan, jref, G};
           e = ncmri::launch_mfma_pair_gather(bc, pa, ma, s);

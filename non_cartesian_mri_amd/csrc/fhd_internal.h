@@ -148,10 +148,12 @@ struct MfmaArgs {
 //   [3] samples per row, [4] wave slots U = ceil(E / 16), [5] workgroup slots
 //   Q = ceil(U / kMfma4Waves) per row, [6] the index sum S of a pair (-1: none),
 //   then int2 entries (g, partner or -1): paired entries e < Cp at slot e,
-//   the others at slot gcap - 1 - (e - Cp).
+//   the others at slot gcap - 1 - (e - Cp); then (16-byte aligned) each
+//   group's reference voxel as a float4 (x, y, z, 0).
 constexpr int kPairHeader = 16;
-constexpr int kPairResidentWgs = 2 * 256;  // resident 4-wave workgroups of the pair gather (2 per CU)
-inline size_t pair_plan_bytes(int64_t groups) { return (size_t)kPairHeader * 4 + (size_t)groups * 8; }
+constexpr int kPairResidentWgs = 3 * 256;  // resident 4-wave workgroups of the pair gather (3 per CU)
+inline size_t pair_list_bytes(int64_t groups) { return ((size_t)kPairHeader * 4 + (size_t)groups * 8 + 15) / 16 * 16; }
+inline size_t pair_plan_bytes(int64_t groups) { return pair_list_bytes(groups) + (size_t)groups * 16; }
 
 struct PairPlanArgs {
   const float* x; const float* y; const float* z;
@@ -160,6 +162,7 @@ struct PairPlanArgs {
   int64_t G;             // groups ceil(N / V): the list's slots
   int32_t* flags;        // [ceil(G / 16)] regular waves
   int32_t* plan;         // pair plan
+  float4* refs;          // [G] reference voxels (inside the pair plan buffer)
   int32_t pair;          // 0: every group alone (no partner search)
   int32_t rows_lo, rows_hi;  // the device picks the launch rows in this range
   int64_t mpad;

@@ -871,8 +871,15 @@ __global__ void __launch_bounds__(kWorkgroup) pair_flags_kernel(PairPlanArgs a) 
   const bool gin = n0 < a.N;
   const float gx = gin ? a.x[n0] : 0.0f, gy = gin ? a.y[n0] : 0.0f, gz = gin ? a.z[n0] : 0.0f;
   bool reg = wave_regular<V, 16>(a.x, a.y, a.z, a.N, n0, lane, gx, gy, gz);
-  reg = __all(reg && (!gin || n0 + a.jref < a.N));
+  const bool has_ref = gin && n0 + a.jref < a.N;
+  reg = __all(reg && (!gin || has_ref));
   if (lane == 0) a.flags[wave] = reg ? 1 : 0;
+  // each group's reference voxel, packed for the list kernel's reads
+  const int64_t g = wave * 16 + lane;
+  if (lane < 16 && g < a.G) {
+    const int64_t r = n0 + a.jref;
+    a.refs[g] = has_ref ? make_float4(a.x[r], a.y[r], a.z[r], 0.0f) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
 }
 
 constexpr int kListThreads = 1024;
@@ -939,16 +946,17 @@ __global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a)
   }
   last = block_reduce64(last, true, red);
   int64_t S = -1;
+  const float4* refs = a.refs;
   if (a.pair && last >= 0) {
-    const int64_t rb = last * V + a.jref;
-    const float tx = -a.x[rb], ty = -a.y[rb], tz = -a.z[rb];
+    const float4 rl = refs[last];
+    const float tx = -rl.x, ty = -rl.y, tz = -rl.z;
     for (int64_t base = 0; base < Gfull; base += (int64_t)kListThreads * kListPer) {
       int64_t mine = INT64_MAX;
       for (int i = 0; i < kListPer; ++i) {
         const int64_t g = base + (int64_t)i * kListThreads + tid;
         if (g < Gfull && a.flags[g >> 4]) {
-          const int64_t r = g * V + a.jref;
-          if (a.x[r] == tx && a.y[r] == ty && a.z[r] == tz && g < mine) mine = g;
+          const float4 r = refs[g];
+          if (r.x == tx && r.y == ty && r.z == tz && g < mine) mine = g;
         }
       }
       const int64_t found = block_reduce64(mine, false, red);
@@ -972,8 +980,8 @@ __global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a)
       part[i] = -1;
       const int64_t h = S - g;
       if (S >= 0 && g < Gfull && h >= 0 && h < Gfull && h != g && a.flags[h >> 4]) {
-        const int64_t rg = g * V + a.jref, rh = h * V + a.jref;
-        if (a.x[rh] == -a.x[rg] && a.y[rh] == -a.y[rg] && a.z[rh] == -a.z[rg]) part[i] = h > g ? (int)h : -2;
+        const float4 rg = refs[g], rh = refs[h];
+        if (rh.x == -rg.x && rh.y == -rg.y && rh.z == -rg.z) part[i] = h > g ? (int)h : -2;
       }
       np += part[i] >= 0;
       ns += part[i] == -1;
@@ -1019,10 +1027,17 @@ __global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a)
 }
 
 // The gather over the pair plan's list: workgroup item = (row, Q slot),
-// row-major, each wave 16 list entries.  Waves whose first entry is paired
-// run the four-product chunk (a single among them gets its out[g] only);
-// waves of singles run the three-product chunk of MfmaGather4.  The chunk
-// staging and loop shape are MfmaGather4's.
+// row-major, each wave 16 list entries, all summed in the four-product form
+// (a group without a partner gets its own sums only: on the grids the
+// pairing is made for these are the few rows without a mirror row, and one
+// form keeps the kernel at 3 waves per SIMD).  The chunk staging and loop
+// shape are MfmaGather4's.
+// Summation block of the pair gather: 1024 chunks of 16 samples.  (A
+// coherent sum -- Q at x = 0, the reference of the self-mirrored group, where
+// every product is |phi|^2 -- over one 131,072-sample block misses by 2e-5 in
+// fp32; in blocks of 16,384 by a few 1e-6.)
+constexpr int32_t kPairBlockChunks = 1024;
+
 template <int BC>
 struct MfmaPairGather4 {
   static constexpr int T = 8;
@@ -1090,28 +1105,83 @@ struct MfmaPairGather4 {
     return list[e < Cp ? e : gcap - 1 - (e - Cp)];
   }
 
-  // The chunk loop and write-out of one wave: PAIRED takes the four-product
-  // chunk, else the three-product one (skipped by waves past the list).  Both
-  // forms stage and wait in the same sequence, so the waves of a workgroup
-  // may take different forms.
-  template <bool PAIRED>
-  __device__ static __forceinline__ void loop(const MfmaArgs& a, int64_t lo, int32_t nch, int wig, int lane,
-                                              bool live, float rx, float ry, float rz, float4* sb0,
-                                              float4* sb1, float4* sh0, float4* sh1, float2* dst,
-                                              const int2* list, int64_t e0, int64_t E, int64_t Cp) {
+  __device__ static void run(const MfmaArgs& a) {
+    __shared__ float4 sb0[C / 4 * QF / 4], sb1[C / 4 * QF / 4];
+    __shared__ float4 sh0[NH], sh1[NH];
+    const int32_t* P = a.pairs;
+    const int64_t E = P[0], Cp = P[1], U = P[4], Q = P[5];
+    const int32_t R = P[2];
+    const int64_t m_split = P[3];
+    const int64_t item = blockIdx.x;
+    if (item >= Q * R) return;   // the whole workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int32_t row = (int32_t)(item / Q);
+    const int64_t slot = (item - (int64_t)row * Q) * NW + wig;
+    const bool live = slot < U;   // waves past the list only help stage the chunks
+    const int2* list = reinterpret_cast<const int2*>(P + kPairHeader);
+    const int2 me = entry(list, slot * 16 + (lane & 15), E, Cp, a.gcap);
+    float rx = 0.0f, ry = 0.0f, rz = 0.0f;
+    if (me.x >= 0) {
+      const int64_t r = (int64_t)me.x * V + a.jref;
+      rx = a.x[r]; ry = a.y[r]; rz = a.z[r];
+    }
+    int64_t lo, hi;
+    row_range(m_split, a.mpad, row, lo, hi);
+    const int32_t nch = (int32_t)((hi - lo) / C);
     f32x4 acc[3][T], accx[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{};
-      if constexpr (PAIRED) accx[t] = f32x4{};
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{}; accx[t] = f32x4{};
     }
+    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
+    const int c = lane & 15;
+    // out[g] = (Pcr - Psi, Pci + Psr); out[h] = (Pcr + Psi, Pci - Psr) for a partner h.
+    // ADD: the block's sums are added to what earlier blocks of the row wrote.
+    auto write = [&](bool add) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * (lane >> 4) + r;
+        const int2 en = entry(list, slot * 16 + i, E, Cp, a.gcap);
+        if (en.x < 0) continue;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int cc = 16 * t + c;
+          const int b = cc / V, j = cc % V;
+          const int64_t n = (int64_t)en.x * V + j;
+          float2 vg = make_float2(acc[0][t][r] - accx[t][r], acc[1][t][r] + acc[2][t][r]);
+          if (n < a.N) {
+            float2* o = dst + (int64_t)b * a.N + n;
+            if (add) { const float2 w = *o; vg.x += w.x; vg.y += w.y; }
+            *o = vg;
+          }
+          if (en.y >= 0) {
+            float2 vh = make_float2(acc[0][t][r] + accx[t][r], acc[1][t][r] - acc[2][t][r]);
+            float2* o = dst + (int64_t)b * a.N + (int64_t)en.y * V + j;
+            if (add) { const float2 w = *o; vh.x += w.x; vh.y += w.y; }
+            *o = vh;
+          }
+        }
+      }
+    };
+    // a row longer than kPairBlockChunks chunks is summed in blocks of that
+    // many: each block's sums are added into the row's outputs (this wave owns
+    // them in this row) and the accumulators restart
+    int32_t done = 0;
+    bool written = false;
     auto chunk = [&](const float4* sh, const float4* sb) {
-      const float* hb = reinterpret_cast<const float*>(sh);
-      const float* wb = reinterpret_cast<const float*>(sb);
-      if constexpr (PAIRED)
-        pair_chunk(hb, wb, lane, rx, ry, rz, acc, accx);
-      else if (live)
-        Base::regular_chunk(hb, wb, lane, rx, ry, rz, acc);
+      if (live)
+        pair_chunk(reinterpret_cast<const float*>(sh), reinterpret_cast<const float*>(sb), lane, rx, ry, rz,
+                   acc, accx);
+      ++done;
+      if (done % kPairBlockChunks == 0 && done < nch && live) {
+        write(written);
+        written = true;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{}; accx[t] = f32x4{};
+        }
+      }
     };
     if (nch > 0) Base::stage(a, lo, wig, lane, sb0, sh0);
     Base::publish();
@@ -1129,59 +1199,7 @@ struct MfmaPairGather4 {
       Base::publish();
     }
     if (!live) return;
-    const int c = lane & 15;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * (lane >> 4) + r;
-      const int2 en = entry(list, e0 + i, E, Cp, a.gcap);
-      if (en.x < 0) continue;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int cc = 16 * t + c;
-        const int b = cc / V, j = cc % V;
-        const int64_t n = (int64_t)en.x * V + j;
-        if constexpr (PAIRED) {
-          if (n < a.N) dst[(int64_t)b * a.N + n] = make_float2(acc[0][t][r] - accx[t][r], acc[1][t][r] + acc[2][t][r]);
-          if (en.y >= 0)
-            dst[(int64_t)b * a.N + (int64_t)en.y * V + j] =
-                make_float2(acc[0][t][r] + accx[t][r], acc[1][t][r] - acc[2][t][r]);
-        } else if (n < a.N) {
-          dst[(int64_t)b * a.N + n] = make_float2(acc[0][t][r] - acc[2][t][r], acc[1][t][r] + acc[2][t][r]);
-        }
-      }
-    }
-  }
-
-  __device__ static void run(const MfmaArgs& a) {
-    __shared__ float4 sb0[C / 4 * QF / 4], sb1[C / 4 * QF / 4];
-    __shared__ float4 sh0[NH], sh1[NH];
-    const int32_t* P = a.pairs;
-    const int64_t E = P[0], Cp = P[1], U = P[4], Q = P[5];
-    const int32_t R = P[2];
-    const int64_t m_split = P[3];
-    const int64_t item = blockIdx.x;
-    if (item >= Q * R) return;   // the whole workgroup
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int32_t row = (int32_t)(item / Q);
-    const int64_t slot = (item - (int64_t)row * Q) * NW + wig;
-    const bool live = slot < U;
-    const bool paired = live && slot * 16 < Cp;
-    const int2* list = reinterpret_cast<const int2*>(P + kPairHeader);
-    const int2 me = entry(list, slot * 16 + (lane & 15), E, Cp, a.gcap);
-    float rx = 0.0f, ry = 0.0f, rz = 0.0f;
-    if (me.x >= 0) {
-      const int64_t r = (int64_t)me.x * V + a.jref;
-      rx = a.x[r]; ry = a.y[r]; rz = a.z[r];
-    }
-    int64_t lo, hi;
-    row_range(m_split, a.mpad, row, lo, hi);
-    const int32_t nch = (int32_t)((hi - lo) / C);
-    float2* dst = a.partial ? a.partial + (int64_t)row * BC * a.N : a.out;
-    if (paired)
-      loop<true>(a, lo, nch, wig, lane, live, rx, ry, rz, sb0, sb1, sh0, sh1, dst, list, slot * 16, E, Cp);
-    else
-      loop<false>(a, lo, nch, wig, lane, live, rx, ry, rz, sb0, sb1, sh0, sh1, dst, list, slot * 16, E, Cp);
+    write(written);
   }
 };
 
@@ -1238,10 +1256,10 @@ __global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a) {
   MfmaDirect4<T, BC, TRIG>::run(a);
 }
 
-// Mirror-pair gather: 128 accumulators, 2 waves per SIMD (two 4-wave
-// workgroups per CU, kPairResidentWgs in all).
+// Mirror-pair gather: 128 accumulators, 3 waves per SIMD (three 4-wave
+// workgroups of ~49 KB of LDS per CU, kPairResidentWgs in all).
 template <int BC>
-__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(3)))
 mfma4_pair_kernel(MfmaArgs a) {
   MfmaPairGather4<BC>::run(a);
 }
@@ -1335,6 +1353,7 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
 hipError_t launch_mfma_pair_gather(int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s) {
   const PairFns fn = select_pair(BC);
   if (!fn.gather || !a.pairs || a.pairs != pa.plan || !a.flags || a.flags != pa.flags || pa.V != 128 / BC ||
+      pa.refs != reinterpret_cast<const float4*>(reinterpret_cast<const char*>(pa.plan) + pair_list_bytes(pa.G)) ||
       pa.rows_lo < 1 || pa.rows_hi < pa.rows_lo || (pa.rows_hi > 1 && !a.partial) || pa.jref < 0 ||
       pa.jref >= pa.V || (pa.N > 0 && pa.jref >= pa.N) || a.jref != pa.jref || a.gcap != pa.G ||
       pa.G != (pa.N + pa.V - 1) / pa.V || a.N != pa.N || a.mpad != pa.mpad || a.mpad % kMfmaChunk != 0)

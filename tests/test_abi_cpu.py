@@ -349,7 +349,7 @@ def test_describe_plan_mfma(lib):
     # per-wave flags, the pair plan (16 int32 header, one int2 per group)
     assert hw["mirror_pairs"] == 1 and hw["max_sample_splits"] == 32
     assert acc["mirror_pairs"] == 0 and acc["max_sample_splits"] == acc["sample_splits"] == 16
-    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 32 * 128 ** 3 * 8 + 1024 * 4 + (64 + 16384 * 8 + 255) // 256 * 256
+    assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 32 * 128 ** 3 * 8 + 1024 * 4 + ((64 + 16384 * 8 + 15) // 16 * 16 + 16384 * 16 + 255) // 256 * 256
     off = fhd_describe_plan(262144, 128 ** 3, trig="hw", mirror_pairs=False)
     assert off["mirror_pairs"] == 0 and off["max_sample_splits"] == 16
     assert off["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 16 * 128 ** 3 * 8 + 1024 * 4

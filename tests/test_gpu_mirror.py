@@ -75,7 +75,7 @@ def _plan_header(p, d, **opts):
     nbytes = fhd_workspace_bytes(p.kx.size, p.x.size, B, p.kind == "q", **o)
     V = info["voxels_per_lane"]
     G = -(-p.x.size // V)
-    pair_bytes = (64 + 8 * G + 255) // 256 * 256
+    pair_bytes = ((64 + 8 * G + 15) // 16 * 16 + 16 * G + 255) // 256 * 256
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
     out = _run(p, d, ws, **opts)
     head = ws[nbytes - pair_bytes:nbytes - pair_bytes + 64].view(torch.int32).cpu().numpy()
