@@ -149,6 +149,19 @@ int32_t pair_jref(int64_t N, int V) {
   return N > j ? (int32_t)j : 0;
 }
 
+// Summation block of the mirror-pair gather in samples: the plan's tile,
+// at most kPairBlockSamples unless the sum is plain (one running sum per row
+// by definition).  A coherent sum -- Q at x = 0, the reference voxel of the
+// self-mirrored group, where every product is |phi|^2 -- misses by 2e-5 in
+// fp32 over one 131,072-sample block, by a few 1e-6 in blocks of 16,384.
+constexpr int64_t kPairBlockSamples = 16384;
+constexpr int64_t kPairAccurateTile = 2048;
+
+int64_t pair_block(const Plan& p) {
+  if (p.sum == FHD_SUM_PLAIN) return p.mpad > 0 ? p.mpad : ncmri::kMfmaChunk;
+  return p.tile < kPairBlockSamples ? p.tile : kPairBlockSamples;
+}
+
 // Whether groups of V consecutive voxels (x fastest) of an L^3 grid all sit
 // at the first group's offsets: V divides a row, or V is whole rows of a plane.
 bool groups_regular(int64_t L, int64_t V) { return L % V == 0 || (V % L == 0 && (L * L) % V == 0); }
@@ -330,11 +343,16 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
   // the four-sample engine's does; its accurate path folds tiles of ~sqrt(M)
   if (half && o->trig == FHD_TRIG_HW && o->tile == 0) p.tile = p.m_split;
   if (half && p.tile > p.m_split && p.m_split > 0) p.tile = p.m_split;
-  // mirror pairs: the four-sample engine summing each launch row as one block
-  // on the HW path; with automatic rows the device picks between half and
-  // twice the count above
-  p.pair = engine == FHD_ENGINE_MFMA && p.tiles == 8 && o->trig == FHD_TRIG_HW && p.tile >= p.m_split &&
-           !(o->flags & FHD_FLAG_NO_MIRROR_PAIRS);
+  // mirror pairs: the four-sample engine on either trig path; with automatic
+  // rows the device picks between half and twice the count above (or what
+  // fills every SIMD when pairing halves the waves)
+  p.pair = engine == FHD_ENGINE_MFMA && p.tiles == 8 && !(o->flags & FHD_FLAG_NO_MIRROR_PAIRS);
+  // the pair gather adds each block's sums into the row's outputs in memory
+  // (64 KB per wave and block): the accurate path's automatic tile is
+  // kPairAccurateTile there (128^3 x 262,144: 18.4 ms with blocks of 512, the
+  // old ~sqrt(M) tile, 16.6 ms with blocks of 16,384; rel-L2 ~1e-6 at 2048)
+  if (p.pair && o->tile == 0 && o->sum != FHD_SUM_PLAIN && o->trig == FHD_TRIG_ACCURATE && p.tile < kPairAccurateTile)
+    p.tile = kPairAccurateTile;
   p.rows_lo = p.rows_hi = p.splits;
   if (p.pair && o->sample_splits == 0 && o->sum != FHD_SUM_PLAIN && p.mpad > 0) {
     // at most twice the rows, or enough for every SIMD's 3 waves when about
@@ -342,7 +360,8 @@ fhd_status make_plan(Plan& p, int is_q, int64_t M, int64_t N, int32_t batch, con
     // round to whole rounds)
     int64_t hi = 2 * (int64_t)p.splits;
     const int64_t half = (ncmri::mfma_gather_waves(N, p.tiles, p.bc[0]) + 1) / 2;
-    const int64_t fill = (3 * kSimds + half - 1) / half;
+    const int64_t fill = (ncmri::pair_resident_wgs(o->trig == FHD_TRIG_HW ? ncmri::kTrigHw : ncmri::kTrigAccurate) *
+                              ncmri::kMfma4Waves + half - 1) / half;
     if (fill + fill / 4 > hi) hi = fill + fill / 4;
     const int64_t cap = max_splits(p.mpad, kMinSplitSamplesMfma);
     const int64_t row_bytes = (int64_t)p.bc[0] * N * (int64_t)sizeof(fhd_c32);
@@ -799,10 +818,12 @@ fhd_status run(int is_q, const float* kx, const float* ky, const float* kz, cons
         if (p.pair) {
           const int64_t G = (N + Vp - 1) / Vp;
           float4* refs = (float4*)((char*)pairplan + ncmri::pair_list_bytes(G));
-          ncmri::PairPlanArgs pa{x, y, z, N, Vp, jref, G, flags, pairplan, refs, 1, p.rows_lo, p.rows_hi, p.mpad};
-          ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
+          ncmri::PairPlanArgs pa{x, y, z, N, Vp, jref, G, flags, pairplan, refs, 1, p.rows_lo, p.rows_hi, p.mpad,
+                                 ncmri::pair_resident_wgs(p.trig == FHD_TRIG_HW ? ncmri::kTrigHw : ncmri::kTrigAccurate)};
+          ncmri::MfmaArgs ma{hdr, wb, p.mpad, pair_block(p), x, y, z, N, outp, p.m_split,
                              p.rows_hi > 1 ? partial : nullptr, flags, nullptr, nullptr, pairplan, jref, G};
-          e = ncmri::launch_mfma_pair_gather(bc, pa, ma, s);
+          e = ncmri::launch_mfma_pair_gather(p.trig == FHD_TRIG_HW ? ncmri::kTrigHw : ncmri::kTrigAccurate, bc, pa,
+                                             ma, s);
         } else {
           ncmri::MfmaArgs ma{hdr, wb, p.mpad, p.tile, x, y, z, N, outp, p.m_split,
                              p.splits > 1 ? partial : nullptr, flags};

@@ -142,8 +142,8 @@ struct MfmaArgs {
   int64_t gcap;          // list slots (groups of the pass)
 };
 
-// Mirror pairs (four-sample engine, HW trig, each launch row one summation
-// block).  The pair plan, written on the device before the gather:
+// Mirror pairs (four-sample engine).  The pair plan, written on the device
+// before the gather:
 //   [0] E list entries, [1] Cp of them paired (the first Cp), [2] launch rows R,
 //   [3] samples per row, [4] wave slots U = ceil(E / 16), [5] workgroup slots
 //   Q = ceil(U / kMfma4Waves) per row, [6] the index sum S of a pair (-1: none),
@@ -151,7 +151,8 @@ struct MfmaArgs {
 //   the others at slot gcap - 1 - (e - Cp); then (16-byte aligned) each
 //   group's reference voxel as a float4 (x, y, z, 0).
 constexpr int kPairHeader = 16;
-constexpr int kPairResidentWgs = 3 * 256;  // resident 4-wave workgroups of the pair gather (3 per CU)
+// resident 4-wave workgroups of the pair gather: 2 per CU on either trig path
+inline constexpr int pair_resident_wgs(int) { return 2 * 256; }
 inline size_t pair_list_bytes(int64_t groups) { return ((size_t)kPairHeader * 4 + (size_t)groups * 8 + 15) / 16 * 16; }
 inline size_t pair_plan_bytes(int64_t groups) { return pair_list_bytes(groups) + (size_t)groups * 16; }
 
@@ -166,6 +167,7 @@ struct PairPlanArgs {
   int32_t pair;          // 0: every group alone (no partner search)
   int32_t rows_lo, rows_hi;  // the device picks the launch rows in this range
   int64_t mpad;
+  int32_t resident;      // resident workgroups of the gather (pair_resident_wgs)
 };
 
 // ---------------------------------------------------------------------------
@@ -231,11 +233,11 @@ hipError_t launch_fwd_direct(int trig, int T, int BC, const FwdArgs& a, hipStrea
 // complex columns); BC: vectors of the pass.
 hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaRecordArgs& a,
                                hipStream_t s);
-// Mirror-pair gather of the four-sample engine (HW trig, rows one summation
-// block): pair plan kernels, the gather over the plan's list and the direct
+// Mirror-pair gather of the four-sample engine (a.tile: the summation block
+// in samples): pair plan kernels, the gather over the plan's list and the direct
 // kernel for irregular waves, with the device's launch rows (at most
 // pa.rows_hi; a.partial holds that many rows when pa.rows_hi > 1).
-hipError_t launch_mfma_pair_gather(int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s);
+hipError_t launch_mfma_pair_gather(int trig, int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s);
 // Adds the device-chosen rows' partial sums (rows from the pair plan).
 hipError_t launch_reduce_dev_rows(int BC, const int32_t* plan, const GatherArgs& a, hipStream_t s);
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,

@@ -846,8 +846,7 @@ struct MfmaDirect4 {
 };
 
 // ---------------------------------------------------------------------------
-// Mirror pairs of the four-sample engine (HW trig, each launch row summed as
-// one block).  Take each group's reference at column jref, x_g = x[g V + jref],
+// Mirror pairs of the four-sample engine.  Take each group's reference at column jref, x_g = x[g V + jref],
 // with factors f_j = Mu exp(i 2 pi k.(x_j - x_jref)).  A group h whose
 // reference is exactly -x_g holds at column j the voxel -x_g + (x_j - x_jref)
 // (both groups on the common offsets), so with (c, s) = (cos, sin)(2 pi k.x_g)
@@ -1008,8 +1007,8 @@ __global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a)
       m = (m + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
       const int64_t reff = m > 0 ? (a.mpad + m - 1) / m : 1;
       if (reff != r && r != a.rows_lo) continue;  // a count that leaves empty rows
-      const int64_t items = Q * reff, rounds = (items + kPairResidentWgs - 1) / kPairResidentWgs;
-      const double eff = rounds > 0 ? (double)items / (double)(rounds * kPairResidentWgs) : 1.0;
+      const int64_t items = Q * reff, rounds = (items + a.resident - 1) / a.resident;
+      const double eff = rounds > 0 ? (double)items / (double)(rounds * a.resident) : 1.0;
       if (eff > best + 1e-3) {
         best = eff;
         R = (int32_t)(reff < 1 ? 1 : reff);
@@ -1032,16 +1031,14 @@ __global__ void __launch_bounds__(kListThreads) pair_list_kernel(PairPlanArgs a)
 // pairing is made for these are the few rows without a mirror row, and one
 // form keeps the kernel at 3 waves per SIMD).  The chunk staging and loop
 // shape are MfmaGather4's.
-// Summation block of the pair gather: 1024 chunks of 16 samples.  (A
-// coherent sum -- Q at x = 0, the reference of the self-mirrored group, where
-// every product is |phi|^2 -- over one 131,072-sample block misses by 2e-5 in
-// fp32; in blocks of 16,384 by a few 1e-6.)
-constexpr int32_t kPairBlockChunks = 1024;
-
-template <int BC>
+// The pair gather sums each launch row in blocks of a.tile samples (a
+// multiple of the 16-sample chunk): each block's sums are added into the
+// row's outputs in memory, which the wave owns in that row -- blocked
+// summation with the running totals in memory instead of registers.
+template <int BC, int TRIG>
 struct MfmaPairGather4 {
   static constexpr int T = 8;
-  using Base = MfmaGather4<T, BC, kTrigHw, false>;
+  using Base = MfmaGather4<T, BC, TRIG, false>;
   static constexpr int V = Base::V, C = Base::C, NW = Base::NW, QF = Base::QF, HK = Base::HK, NH = Base::NH;
 
   // fr (u = 0) and fi (u = 1) slices 2 u + h of block q: bv[u T + t], t in half h
@@ -1069,7 +1066,8 @@ struct MfmaPairGather4 {
     }
   }
 
-  // One chunk of the four-product form, pipelined as the three-product HW chunk.
+  // One chunk of the four-product form, pipelined as the three-product HW
+  // chunk (B entries half a block ahead, the phase right before its MFMAs).
   __device__ static __forceinline__ void pair_chunk(const float* __restrict__ hb, const float* __restrict__ wb,
                                                     int lane, float rx, float ry, float rz, f32x4 (&acc)[3][T],
                                                     f32x4 (&accx)[T]) {
@@ -1084,7 +1082,7 @@ struct MfmaPairGather4 {
       if (q + 1 < NQ) Base::load_header(hb, q + 1, lane, hn);
       sched_fence();
       float c, s;
-      phase_sincos<kTrigHw>(hc, rx, ry, rz, c, s);
+      phase_sincos<TRIG>(hc, rx, ry, rz, c, s);
       mfmas_pair_half<0>(c, s, bv, acc, accx);
       sched_fence();
       if (q + 1 < NQ) load_pair_half(wb, q + 1, lane, 0, bv);
@@ -1139,10 +1137,12 @@ struct MfmaPairGather4 {
     // out[g] = (Pcr - Psi, Pci + Psr); out[h] = (Pcr + Psi, Pci - Psr) for a partner h.
     // ADD: the block's sums are added to what earlier blocks of the row wrote.
     auto write = [&](bool add) {
+      const int64_t e0 = slot * 16;
+      float2* out = dst;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (lane >> 4) + r;
-        const int2 en = entry(list, slot * 16 + i, E, Cp, a.gcap);
+        const int2 en = entry(list, e0 + i, E, Cp, a.gcap);
         if (en.x < 0) continue;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -1151,30 +1151,51 @@ struct MfmaPairGather4 {
           const int64_t n = (int64_t)en.x * V + j;
           float2 vg = make_float2(acc[0][t][r] - accx[t][r], acc[1][t][r] + acc[2][t][r]);
           if (n < a.N) {
-            float2* o = dst + (int64_t)b * a.N + n;
+            float2* o = out + (int64_t)b * a.N + n;
             if (add) { const float2 w = *o; vg.x += w.x; vg.y += w.y; }
             *o = vg;
           }
           if (en.y >= 0) {
             float2 vh = make_float2(acc[0][t][r] + accx[t][r], acc[1][t][r] - acc[2][t][r]);
-            float2* o = dst + (int64_t)b * a.N + (int64_t)en.y * V + j;
+            float2* o = out + (int64_t)b * a.N + (int64_t)en.y * V + j;
             if (add) { const float2 w = *o; vh.x += w.x; vh.y += w.y; }
             *o = vh;
           }
         }
       }
     };
-    // a row longer than kPairBlockChunks chunks is summed in blocks of that
-    // many: each block's sums are added into the row's outputs (this wave owns
-    // them in this row) and the accumulators restart
-    int32_t done = 0;
+    // blocks of a.tile samples (an even number of chunks): each block's sums
+    // are added into the row's outputs (this wave owns them in this row) and
+    // the accumulators restart.  The block loop is outside the double-buffered
+    // chunk loop, which keeps its pipeline across block ends (the last pair
+    // of a block stages the next block's first chunk); a per-chunk block test
+    // inside it measured 11 % slower.
+    const int32_t block = (int32_t)(a.tile / C);
     bool written = false;
     auto chunk = [&](const float4* sh, const float4* sb) {
       if (live)
         pair_chunk(reinterpret_cast<const float*>(sh), reinterpret_cast<const float*>(sb), lane, rx, ry, rz,
                    acc, accx);
-      ++done;
-      if (done % kPairBlockChunks == 0 && done < nch && live) {
+    };
+    if (nch > 0) Base::stage(a, lo, wig, lane, sb0, sh0);
+    Base::publish();
+    int32_t ch = 0;
+    while (ch < nch) {
+      const int32_t end = nch - ch > block ? ch + block : nch;
+      for (; ch + 1 < end; ch += 2) {
+        Base::stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+        chunk(sh0, sb0);
+        Base::publish();
+        if (ch + 2 < nch) Base::stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+        chunk(sh1, sb1);
+        Base::publish();
+      }
+      if (ch < end) {  // an odd last chunk of the row (blocks hold an even number)
+        chunk(sh0, sb0);
+        Base::publish();
+        ++ch;
+      }
+      if (ch < nch && live) {
         write(written);
         written = true;
 #pragma unroll
@@ -1182,21 +1203,6 @@ struct MfmaPairGather4 {
           acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{}; accx[t] = f32x4{};
         }
       }
-    };
-    if (nch > 0) Base::stage(a, lo, wig, lane, sb0, sh0);
-    Base::publish();
-    int32_t ch = 0;
-    for (; ch + 1 < nch; ch += 2) {
-      Base::stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
-      chunk(sh0, sb0);
-      Base::publish();
-      if (ch + 2 < nch) Base::stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
-      chunk(sh1, sb1);
-      Base::publish();
-    }
-    if (ch < nch) {
-      chunk(sh0, sb0);
-      Base::publish();
     }
     if (!live) return;
     write(written);
@@ -1256,12 +1262,16 @@ __global__ void __launch_bounds__(kWorkgroup) mfma4_direct_kernel(MfmaArgs a) {
   MfmaDirect4<T, BC, TRIG>::run(a);
 }
 
-// Mirror-pair gather: 128 accumulators, 3 waves per SIMD (three 4-wave
-// workgroups of ~49 KB of LDS per CU, kPairResidentWgs in all).
-template <int BC>
-__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(3)))
+// Mirror-pair gather: 128 accumulators, 2 waves per SIMD (two 4-wave
+// workgroups of ~49 KB of LDS per CU, pair_resident_wgs in all).  (At 3 waves
+// per SIMD the HW kernel fits 168 VGPRs only by spilling the block write's
+// addresses into the chunk loop, 2 % slower; without the block write it
+// fitted, but measured no faster than at 2 waves: the matrix pipe is busy
+// 0.93 of the time either way.)
+template <int BC, int TRIG>
+__global__ void __launch_bounds__(64 * kMfma4Waves) __attribute__((amdgpu_waves_per_eu(2)))
 mfma4_pair_kernel(MfmaArgs a) {
-  MfmaPairGather4<BC>::run(a);
+  MfmaPairGather4<BC, TRIG>::run(a);
 }
 
 struct PairFns {
@@ -1271,17 +1281,20 @@ struct PairFns {
 };
 
 template <int BC>
-PairFns pair_fns() {
-  return {pair_flags_kernel<128 / BC>, mfma4_pair_kernel<BC>, mfma4_direct_kernel<8, BC, kTrigHw>};
+PairFns pair_fns(int trig) {
+  if (trig == kTrigHw)
+    return {pair_flags_kernel<128 / BC>, mfma4_pair_kernel<BC, kTrigHw>, mfma4_direct_kernel<8, BC, kTrigHw>};
+  return {pair_flags_kernel<128 / BC>, mfma4_pair_kernel<BC, kTrigAccurate>,
+          mfma4_direct_kernel<8, BC, kTrigAccurate>};
 }
 
-PairFns select_pair(int BC) {
+PairFns select_pair(int BC, int trig) {
   switch (BC) {
-    case 1: return pair_fns<1>();
-    case 2: return pair_fns<2>();
-    case 4: return pair_fns<4>();
-    case 8: return pair_fns<8>();
-    case 16: return pair_fns<16>();
+    case 1: return pair_fns<1>(trig);
+    case 2: return pair_fns<2>(trig);
+    case 4: return pair_fns<4>(trig);
+    case 8: return pair_fns<8>(trig);
+    case 16: return pair_fns<16>(trig);
     default: return {nullptr, nullptr, nullptr};
   }
 }
@@ -1350,13 +1363,14 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_pair_gather(int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s) {
-  const PairFns fn = select_pair(BC);
+hipError_t launch_mfma_pair_gather(int trig, int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s) {
+  const PairFns fn = select_pair(BC, trig);
   if (!fn.gather || !a.pairs || a.pairs != pa.plan || !a.flags || a.flags != pa.flags || pa.V != 128 / BC ||
       pa.refs != reinterpret_cast<const float4*>(reinterpret_cast<const char*>(pa.plan) + pair_list_bytes(pa.G)) ||
       pa.rows_lo < 1 || pa.rows_hi < pa.rows_lo || (pa.rows_hi > 1 && !a.partial) || pa.jref < 0 ||
       pa.jref >= pa.V || (pa.N > 0 && pa.jref >= pa.N) || a.jref != pa.jref || a.gcap != pa.G ||
-      pa.G != (pa.N + pa.V - 1) / pa.V || a.N != pa.N || a.mpad != pa.mpad || a.mpad % kMfmaChunk != 0)
+      pa.G != (pa.N + pa.V - 1) / pa.V || a.N != pa.N || a.mpad != pa.mpad || a.mpad % kMfmaChunk != 0 ||
+      a.tile <= 0 || a.tile % (2 * kMfma4Chunk) != 0 || pa.resident != pair_resident_wgs(trig))
     return hipErrorInvalidValue;
   if (a.N <= 0) return hipSuccess;
   const int64_t waves = mfma_gather_waves(a.N, 8, BC);

@@ -341,14 +341,17 @@ def test_describe_plan_mfma(lib):
     # tile ~sqrt(M) for the accurate path; the four-sample engine's HW path
     # sums a whole launch row (16,384 samples) as one block
     assert hw["padded_samples"] == 262144 and hw["passes"] == 1 and hw["tile"] == 16384
-    assert acc["tile"] == 512
+    # (the accurate path's ~sqrt(M) tile, raised to 2048 samples where the
+    # mirror-pair gather writes each block's sums to memory)
+    assert acc["tile"] == 2048
+    assert fhd_describe_plan(262144, 128 ** 3, trig="accurate", mirror_pairs=False)["tile"] == 512
     # 1024 waves of 16 groups; 16 rows of 16384 samples
     assert hw["sample_splits"] == 16
     # the HW path pairs mirror groups and picks its rows on the device, at most
     # twice the automatic count: headers, factors, 32 rows of partial sums, 1024
     # per-wave flags, the pair plan (16 int32 header, one int2 per group)
     assert hw["mirror_pairs"] == 1 and hw["max_sample_splits"] == 32
-    assert acc["mirror_pairs"] == 0 and acc["max_sample_splits"] == acc["sample_splits"] == 16
+    assert acc["mirror_pairs"] == 1 and acc["sample_splits"] == 16 and acc["max_sample_splits"] == 32
     assert hw["workspace_bytes"] == 262144 * 16 + 262144 * 1536 + 32 * 128 ** 3 * 8 + 1024 * 4 + ((64 + 16384 * 8 + 15) // 16 * 16 + 16384 * 16 + 255) // 256 * 256
     off = fhd_describe_plan(262144, 128 ** 3, trig="hw", mirror_pairs=False)
     assert off["mirror_pairs"] == 0 and off["max_sample_splits"] == 16

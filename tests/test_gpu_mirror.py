@@ -1,5 +1,6 @@
-"""GPU parity of the mirror-pair gather (four-sample matrix-core engine, HW
-trig, launch rows summed as one block) against the double-precision oracle.
+"""GPU parity of the mirror-pair gather (four-sample matrix-core engine, both
+trig paths; launch rows summed in blocks of the plan's tile, at most 16,384
+samples on the HW path) against the double-precision oracle.
 
 The pairing rests on e^{-i2 pi k.x} = conj e^{i2 pi k.x} for real k and x (the
 phase of PMPP ch. 17 Eq. 17.1): a voxel group whose reference voxel (column
@@ -102,34 +103,36 @@ def _expected_pairs(ys, zs, segs=1):
     return pairs, len(rows) * segs - 2 * pairs
 
 
+@pytest.mark.parametrize("trig", ["hw", "accurate"])
 @pytest.mark.parametrize("kind", ["fhd", "q"])
-def test_pairs_on_an_asymmetric_box(oracle_mod, kind):
+def test_pairs_on_an_asymmetric_box(oracle_mod, kind, trig):
     """y from -5 to 4, z from -3 to 3: 31 mirror pairs, the 7 rows at y = -5 and
     the row y = z = 0 alone; 70 groups in 5 waves (the last one partial)."""
     ys, zs = np.arange(-5, 5), np.arange(-3, 4)
     p = _problem(901, 1500, XS, ys, zs, kind=kind)
     d = dev_problem(p)
     ref = _oracle(oracle_mod, p)
-    got, head = _plan_header(p, d)
+    got, head = _plan_header(p, d, trig=trig)
     pairs, alone = _expected_pairs(ys, zs)
     assert (pairs, alone) == (31, 8)
     assert head[1] == pairs and head[0] == pairs + alone, head[:8]
-    assert_close(got, ref, TOL["hw"], f"mirror pairs {kind}")
-    off = _run(p, d, mirror_pairs=False)
-    assert_close(off, ref, TOL["hw"], f"pairing off {kind}")
+    assert_close(got, ref, TOL[trig], f"mirror pairs {kind} {trig}")
+    off = _run(p, d, mirror_pairs=False, trig=trig)
+    assert_close(off, ref, TOL[trig], f"pairing off {kind} {trig}")
     # same phases up to the conjugation: the two paths agree far below the HW bar
     assert np.linalg.norm(got - off) <= 1e-5 * np.linalg.norm(off)
 
 
+@pytest.mark.parametrize("trig", ["hw", "accurate"])
 @pytest.mark.parametrize("B", [2, 4, 16, 19])
-def test_pairs_in_batched_passes(oracle_mod, B):
+def test_pairs_in_batched_passes(oracle_mod, B, trig):
     """Passes of 16/4/2/1 vectors: groups of 8, 32, 64 and 128 voxels, 16 to 1
     groups per row, each mirrored onto the mirror row's opposite segment."""
     ys, zs = np.arange(-3, 3), np.arange(-2, 3)
     p = _problem(902 + B, 700, XS, ys, zs, B=B)
     d = dev_problem(p)
     ref = _oracle(oracle_mod, p)
-    assert_close(_run(p, d), ref, TOL["hw"], f"mirror pairs batched B={B}")
+    assert_close(_run(p, d, trig=trig), ref, TOL[trig], f"mirror pairs batched B={B} {trig}")
 
 
 def test_pair_counts_with_several_groups_per_row(oracle_mod):
@@ -144,13 +147,14 @@ def test_pair_counts_with_several_groups_per_row(oracle_mod):
     assert_close(got, _oracle(oracle_mod, p), TOL["hw"], "mirror pairs, two groups per row")
 
 
+@pytest.mark.parametrize("trig", ["hw", "accurate"])
 @pytest.mark.parametrize("N", [70 * 128 - 50, 70 * 128 - 70, 69 * 128 + 1])
-def test_ragged_voxel_counts(oracle_mod, N):
+def test_ragged_voxel_counts(oracle_mod, N, trig):
     """A partial last group that holds its reference voxel (summed alone), and
     last groups without it (their wave goes to the direct kernel)."""
     p = _problem(904, 900, XS, np.arange(-5, 5), np.arange(-3, 4), N=N)
     d = dev_problem(p)
-    assert_close(_run(p, d), _oracle(oracle_mod, p), TOL["hw"], f"mirror pairs N={N}")
+    assert_close(_run(p, d, trig=trig), _oracle(oracle_mod, p), TOL[trig], f"mirror pairs N={N} {trig}")
 
 
 def test_displaced_voxel_and_no_mirrors(oracle_mod):
@@ -170,11 +174,16 @@ def test_displaced_voxel_and_no_mirrors(oracle_mod):
 
 
 @pytest.mark.parametrize("opts", [dict(sum="plain"), dict(sample_splits=3), dict(sample_splits=1),
-                                  dict(sample_splits=7)])
+                                  dict(sample_splits=7), dict(tile=96), dict(tile=96, sample_splits=2),
+                                  dict(trig="accurate", sum="plain"), dict(trig="accurate", tile=2048),
+                                  dict(trig="accurate", sample_splits=3)])
 def test_row_choices(oracle_mod, opts):
+    """Plain sums (one block per row), fixed and device-chosen rows, blocks
+    shorter than a row (tile) on both trig paths."""
     p = _problem(907, 2100, XS, np.arange(-3, 4), np.arange(-3, 3))
     d = dev_problem(p)
-    assert_close(_run(p, d, **opts), _oracle(oracle_mod, p), TOL["hw"], f"mirror pairs {opts}")
+    trig = opts.get("trig", "hw")
+    assert_close(_run(p, d, **opts), _oracle(oracle_mod, p), TOL[trig], f"mirror pairs {opts}")
 
 
 @pytest.mark.parametrize("M", [0, 1, 3, 33, 4099])
