@@ -535,10 +535,45 @@ fhd_status make_fwd_plan(Plan& p, int64_t M, int64_t N, int32_t batch, const fhd
     const int64_t row_bytes = gs * ncmri::mfma_factor_floats(p.tiles) * (int64_t)sizeof(float);
     if (row_bytes <= kRowBlockBytes && gs > p.tile) p.tile = gs;
   }
+  // mirror pairs (the fp32 four-group engine): the K dimension runs over the
+  // pair plan's entries; each launch row is one summation block of at most
+  // kPairBlockSamples entries (HW) or kPairAccurateTile (accurate), or the
+  // caller's tile, through the rows' partial sums (the pair gather keeps no
+  // running totals); sample_splits, if given, is the row count
+  p.pair = !half && p.tiles == 8 && !(o->flags & FHD_FLAG_NO_MIRROR_PAIRS);
+  if (p.pair && gmax > 0 && M > 0 && o->sum != FHD_SUM_PLAIN && o->sample_splits == 0) {
+    const int64_t block = o->tile > 0 ? p.tile : (o->trig == FHD_TRIG_HW ? kPairBlockSamples : kPairAccurateTile);
+    int64_t G = 0;
+    for (int i = 0; i < p.npass; ++i) {
+      const int64_t Vi = 16 * p.tiles / p.bc[i], gi = (N + Vi - 1) / Vi;
+      G = gi > G ? gi : G;
+    }
+    int64_t rows = (G + block - 1) / block;
+    if (rows < p.splits) rows = p.splits;
+    const int64_t row_bytes = (int64_t)p.bc[0] * M * (int64_t)sizeof(fhd_c32);
+    if (row_bytes > 0 && rows > kMaxPartialBytes / row_bytes) rows = kMaxPartialBytes / row_bytes;
+    if (rows > kMaxSplits) rows = kMaxSplits;
+    if (rows < 1) rows = 1;
+    p.splits = (int32_t)rows;
+    p.tile = block;
+  }
+  p.rows_lo = p.rows_hi = p.splits;
+  p.pair_bytes = 0;
   p.m_split = 0;
   p.hdr_bytes = 0;
   p.ws_bytes = 0;
   for (int i = 0; i < p.npass; ++i) {
+    if (p.pair && p.gpad[i] > 0) {
+      // entry headers [gpad][4], entries [gpad][64 T] (ur, ui, wi, wr), list of
+      // groups of irregular waves [1 + gpad], wave flags, the pair plan
+      const int64_t Vi = 16 * p.tiles / p.bc[i], Gi = (N + Vi - 1) / Vi;
+      p.pass_bytes[i] = align256((size_t)p.gpad[i] * 4 * sizeof(float)) +
+                        align256((size_t)p.gpad[i] * 64 * p.tiles * sizeof(float)) +
+                        align256((size_t)(p.gpad[i] + 1) * sizeof(int32_t)) +
+                        align256((size_t)((Gi + 15) / 16) * sizeof(int32_t)) + ncmri::pair_plan_bytes(Gi);
+      p.ws_bytes += align256(p.pass_bytes[i]);
+      continue;
+    }
     // header [gpad][4], image [gpad][48 T], list of flagged groups [1 + gpad] int32
     p.pass_bytes[i] = p.gpad[i] == 0 ? 0
                       : align256((size_t)p.gpad[i] * 4 * sizeof(float)) +
@@ -655,14 +690,41 @@ fhd_status run_forward(const float* kx, const float* ky, const float* kz, const 
     }
     hipError_t e = hipSuccess;
     const char* what = "pack";
+    ncmri::PairPlanArgs pa{};
+    if (p.pair && p.gpad[i] > 0) {
+      const int Vp = 16 * p.tiles / bc;
+      const int64_t Gi = (N + Vp - 1) / Vp;
+      const size_t hb2 = align256((size_t)p.gpad[i] * 4 * sizeof(float));
+      const size_t ib2 = align256((size_t)p.gpad[i] * 64 * p.tiles * sizeof(float));
+      const size_t lb2 = align256((size_t)(p.gpad[i] + 1) * sizeof(int32_t));
+      int32_t* wflags = (int32_t*)(base + hb2 + ib2 + lb2);
+      int32_t* plan = (int32_t*)((char*)wflags + align256((size_t)((Gi + 15) / 16) * sizeof(int32_t)));
+      const int32_t jref = pair_jref(N, Vp);
+      pa = ncmri::PairPlanArgs{x, y, z, N, Vp, jref, Gi, wflags, plan,
+                               (float4*)((char*)plan + ncmri::pair_list_bytes(Gi)), 1, 1, 1, 0,
+                               ncmri::pair_resident_wgs(ncmri::kTrigHw)};
+      fa.gwb = (float*)(base + hb2);
+      fa.glist = (int32_t*)(base + hb2 + ib2);
+      fa.pairs = plan;
+      fa.refs = pa.refs;
+      fa.wflags = wflags;
+      fa.jref = jref;
+      fa.gcap = Gi;
+    }
     if (p.stages & FHD_STAGE_MU) {
-      e = ncmri::launch_fwd_pack(p.tiles, bc, fa, s);
+      if (p.pair && p.gpad[i] > 0) {
+        e = ncmri::launch_pair_plan(bc, pa, s);
+        if (e == hipSuccess) e = ncmri::launch_fwd_pair_pack(bc, fa, s);
+      } else {
+        e = ncmri::launch_fwd_pack(p.tiles, bc, fa, s);
+      }
       if (e == hipSuccess && half && p.gpad[i] > 0) e = ncmri::launch_fwd_half_pack(bc, ha, s);
     }
     if (e == hipSuccess && (p.stages & FHD_STAGE_GATHER)) {
       what = "gather";
-      e = half && p.gpad[i] > 0 ? ncmri::launch_fwd_half_gather(p.trig, bc, p.splits, ha, s)
-                                : ncmri::launch_fwd_gather(p.trig, p.tiles, bc, p.splits, fa, s);
+      e = half && p.gpad[i] > 0  ? ncmri::launch_fwd_half_gather(p.trig, bc, p.splits, ha, s)
+          : p.pair && p.gpad[i] > 0 ? ncmri::launch_fwd_pair_gather(p.trig, bc, p.splits, fa, s)
+                                    : ncmri::launch_fwd_gather(p.trig, p.tiles, bc, p.splits, fa, s);
     }
     if (e == hipSuccess && (p.stages & FHD_STAGE_REDUCE)) {
       what = "reduce";

@@ -116,8 +116,10 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_list_kernel(FwdArgs a, int V) 
   const int64_t per = (G + kWorkgroup - 1) / kWorkgroup;
   const int64_t g0 = tid * per < G ? tid * per : G;
   const int64_t g1 = g0 + per < G ? g0 + per : G;
+  // flagged: off the common offsets, or (mirror pairs) in an irregular wave
+  auto flagged = [&](int64_t g) { return a.wflags ? a.wflags[g >> 4] == 0 : a.ghdr[g * 4 + 3] != 0.0f; };
   int32_t c = 0;
-  for (int64_t g = g0; g < g1; ++g) c += a.ghdr[g * 4 + 3] != 0.0f ? 1 : 0;
+  for (int64_t g = g0; g < g1; ++g) c += flagged(g) ? 1 : 0;
   cnt[tid] = c;
   __syncthreads();
   // exclusive prefix sum (Hillis-Steele on the inclusive sums, then shift)
@@ -130,7 +132,7 @@ __global__ void __launch_bounds__(kWorkgroup) fwd_list_kernel(FwdArgs a, int V) 
   int32_t pos = cnt[tid] - c;
   if (tid == kWorkgroup - 1) a.glist[0] = cnt[tid];
   for (int64_t g = g0; g < g1; ++g)
-    if (a.ghdr[g * 4 + 3] != 0.0f) a.glist[1 + pos++] = (int32_t)g;
+    if (flagged(g)) a.glist[1 + pos++] = (int32_t)g;
 }
 
 // ---------------------------------------------------------------------------
@@ -570,6 +572,208 @@ struct FwdGather4 {
 };
 
 // ---------------------------------------------------------------------------
+// Mirror pairs (four-group engine).  With each group's reference at column
+// jref (x_g = x[g V + jref], offsets d_j = x_j - x_jref) a group h whose
+// reference is exactly -x_g holds at column j the voxel -x_g + d_j, so its
+// phase is the conjugate of g's at every sample, and
+//   e^{-i 2 pi k.x_g} rho_g[j] + e^{+i 2 pi k.x_g} rho_h[j]
+//     = c u - i s w,  u = rho_g + rho_h, w = rho_g - rho_h,
+// (c, s) = (cos, sin)(2 pi k.x_g): Re = c ur + s wi, Im = c ui - s wr, four
+// real products for two groups where the three-product form takes six.  The
+// K dimension of the product runs over the pair plan's entries (a group with
+// its partner, or a group alone: w = u).
+//
+// Packing of the entries: one lane per (entry slot e, complex column cc);
+// slots past the list (to the next multiple of the chunk) are zero.  Layout
+// per block of four entries: value q (ur, ui, wi, wr) of tile t = cc / 16 at
+// e' = q T + t, lane p = 16 (e % 4) + cc % 16: [e / 4][e' / 4][p][e' % 4]
+// (256 T floats per block); the entry's header is its group's reference.
+__global__ void __launch_bounds__(kWorkgroup) fwd_pair_pack_kernel(FwdArgs a, int BC) {
+  constexpr int T = 8;
+  const int64_t idx = (int64_t)blockIdx.x * kWorkgroup + threadIdx.x;
+  const int64_t e = idx >> 7;
+  const int cc = (int)(idx & 127);
+  const int64_t E = a.pairs[0], Cp = a.pairs[1];
+  const int64_t Epad = (E + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
+  if (e >= Epad || e >= a.gpad) return;
+  const int2* list = reinterpret_cast<const int2*>(a.pairs + kPairHeader);
+  const int2 en = e < E ? list[e < Cp ? e : a.gcap - 1 - (e - Cp)] : make_int2(-1, -1);
+  if (cc == 0) {
+    const float4 r = en.x >= 0 ? a.refs[en.x] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    reinterpret_cast<float4*>(a.ghdr)[e] = make_float4(r.x, r.y, r.z, 0.0f);
+  }
+  const int V = 128 / BC;
+  const int b = cc / V, j = cc % V;
+  float2 rg = make_float2(0.0f, 0.0f), rh = make_float2(0.0f, 0.0f);
+  if (en.x >= 0) {
+    const int64_t n = (int64_t)en.x * V + j;
+    if (n < a.N) rg = a.rho[(int64_t)b * a.N + n];
+  }
+  if (en.y >= 0) rh = a.rho[(int64_t)b * a.N + (int64_t)en.y * V + j];
+  const float v[4] = {rg.x + rh.x, rg.y + rh.y, rg.y - rh.y, rg.x - rh.x};   // ur, ui, wi, wr
+  const int t = cc / 16, lp = 16 * (int)(e & 3) + cc % 16;
+  float* blk = a.gwb + (e >> 2) * (256 * T);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ep = q * T + t;
+    blk[((ep >> 2) * 64 + lp) * 4 + (ep & 3)] = v[q];
+  }
+}
+
+// The four-group engine over the pair plan's entries: FwdGather4's staging,
+// pipelining and finish with four products per tile.  The launch rows split
+// the padded entries evenly (chunks of 32), and each row is one summation
+// block: the plan bounds a row's entries (blocked summation through the rows'
+// partial sums), so the kernel keeps no running totals (with them, 128
+// accumulators, 64 totals and 32 B entries spill past 256 VGPRs).
+template <int BC, int TRIG>
+struct FwdPairGather4 {
+  static constexpr int T = 8;
+  static constexpr int V = 16 * T / BC;
+  static constexpr int C = kMfma4Chunk;             // entries per chunk
+  static constexpr int NW = kWorkgroup / 64;
+  static constexpr int QF = 256 * T;                // image floats per block of four entries
+  static constexpr int NB = C / 4 * QF * 4 / 1024;  // 1 KiB image blocks per chunk
+  static constexpr int NH = C;
+  static constexpr int SB = C / 4 * QF / 4;
+  static constexpr int HC = 8 * T;
+  static constexpr int GH = 16 * HC * 2 / 4;
+  static constexpr int LDS4 = 2 * SB > NW * GH ? 2 * SB : NW * GH;
+  static_assert(NB % NW == 0 && NH <= 64, "chunk staging");
+
+  __device__ static __forceinline__ void stage(const FwdArgs& a, int64_t g, int wig, int lane, float4* lb,
+                                               float4* lh) {
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_rsrc(reinterpret_cast<const float4*>(a.gwb) + (g / 4) * (QF / 4), NB * 64 * 16);
+#pragma unroll
+    for (int i = 0; i < NB / NW; ++i) {
+      const int blk = i * NW + wig;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)(lb + blk * 64), 16, lane * 16, blk * 1024, 0, 0);
+    }
+    if (wig == 0 && lane < NH)
+      lds_dma16(buffer_rsrc(reinterpret_cast<const float4*>(a.ghdr) + g, NH * 16), lane * 16, lh);
+  }
+
+  __device__ static __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  __device__ static __forceinline__ void load_header(const float* __restrict__ hb, int q, int lane, float (&hs)[3]) {
+    const float* hp = hb + (4 * q + (lane >> 4)) * 4;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) hs[i] = hp[i];
+  }
+
+  // slices 2 q + h of block qb (values q = ur, ui, wi, wr of tiles 4h .. 4h + 3): bv[q T + t]
+  __device__ static __forceinline__ void load_half(const float* __restrict__ wb, int qb, int lane, int h,
+                                                   float (&bv)[4 * T]) {
+    const float* pp = wb + qb * QF;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sl = 2 * q + h;
+      const float4 v = *reinterpret_cast<const float4*>(pp + (sl * 64 + lane) * 4);
+      bv[4 * sl] = v.x; bv[4 * sl + 1] = v.y; bv[4 * sl + 2] = v.z; bv[4 * sl + 3] = v.w;
+    }
+  }
+
+  template <int H>
+  __device__ static __forceinline__ void mfmas_half(float c, float s, const float (&bv)[4 * T], f32x4 (&acc)[4][T]) {
+#pragma unroll
+    for (int u = 0; u < T / 2; ++u) {
+      const int t = H * (T / 2) + u;
+      acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv[t], acc[0][t], 0, 0, 0);           // c ur
+      acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv[T + t], acc[1][t], 0, 0, 0);       // c ui
+      acc[2][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s, bv[2 * T + t], acc[2][t], 0, 0, 0);   // s wi
+      acc[3][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(s, bv[3 * T + t], acc[3][t], 0, 0, 0);   // s wr
+    }
+  }
+
+  // One chunk of 16 entries (4 blocks): B slices half a block ahead, the
+  // phase right before its MFMAs (the HW-path pipeline of FwdGather4).
+  __device__ static __forceinline__ void chunk(const float* __restrict__ hb, const float* __restrict__ wb, int lane,
+                                               const SampleK<TRIG>& k, f32x4 (&acc)[4][T]) {
+    constexpr int NQ = C / 4;
+    float hc[3], bv[4 * T];
+    load_header(hb, 0, lane, hc);
+    load_half(wb, 0, lane, 0, bv);
+    load_half(wb, 0, lane, 1, bv);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float hn[3];
+      if (q + 1 < NQ) load_header(hb, q + 1, lane, hn);
+      sched_fence();
+      float c, s;
+      k.sincos_phase(hc[0], hc[1], hc[2], c, s);
+      mfmas_half<0>(c, s, bv, acc);
+      sched_fence();
+      if (q + 1 < NQ) load_half(wb, q + 1, lane, 0, bv);
+      sched_fence();
+      mfmas_half<1>(c, s, bv, acc);
+      sched_fence();
+      if (q + 1 < NQ) {
+        load_half(wb, q + 1, lane, 1, bv);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) hc[i] = hn[i];
+      }
+      sched_fence();
+    }
+  }
+
+  __device__ static void run(const FwdArgs& a) {
+    __shared__ float4 lds[LDS4];
+    __shared__ float4 sh0[NH], sh1[NH];
+    float4* sb0 = lds;
+    float4* sb1 = lds + SB;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wig = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * NW + wig;
+    const int64_t m = wave * 16 + (lane & 15);
+    const bool valid = m < a.M;
+    SampleK<TRIG> k;
+    k.load(a, m, valid);
+    // this launch row's entries: the padded list split evenly over the rows
+    const int64_t E = a.pairs[0];
+    const int64_t Epad = (E + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
+    const int32_t rows = (int32_t)gridDim.y, row = (int32_t)blockIdx.y;
+    int64_t gs = (Epad + rows - 1) / rows;
+    gs = (gs + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
+    const int64_t lo64 = (int64_t)row * gs;
+    const int64_t lo = lo64 < Epad ? lo64 : Epad;
+    const int64_t hi = lo64 + gs < Epad ? lo64 + gs : Epad;
+    const int32_t nch = (int32_t)((hi - lo) / C);
+    if (nch > 0) stage(a, lo, wig, lane, sb0, sh0);
+    publish();
+    f32x4 acc[4][T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[0][t] = f32x4{}; acc[1][t] = f32x4{}; acc[2][t] = f32x4{}; acc[3][t] = f32x4{};
+    }
+    int32_t ch = 0;
+    for (; ch + 1 < nch; ch += 2) {
+      stage(a, lo + (int64_t)(ch + 1) * C, wig, lane, sb1, sh1);
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
+      publish();
+      if (ch + 2 < nch) stage(a, lo + (int64_t)(ch + 2) * C, wig, lane, sb0, sh0);
+      chunk(reinterpret_cast<const float*>(sh1), reinterpret_cast<const float*>(sb1), lane, k, acc);
+      publish();
+    }
+    if (ch < nch) {
+      chunk(reinterpret_cast<const float*>(sh0), reinterpret_cast<const float*>(sb0), lane, k, acc);
+      publish();
+    }
+    // G = sum over entries of (c ur + s wi) + i (c ui - s wr)
+    f32x4 ore[T], oim[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      ore[t] = acc[0][t] + acc[2][t];
+      oim[t] = acc[1][t] - acc[3][t];
+    }
+    fwd_finish<T, BC, TRIG>(a, lds, wig, lane, valid, m, row, k, ore, oim);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Direct evaluation of the listed groups: one lane per sample, the groups in
 // increasing order (indices and voxels read as wave-uniform scalars); the sum
 // is blocked by `tile` listed groups and added into the (already reduced)
@@ -637,6 +841,29 @@ fwd4_gather_kernel(FwdArgs a) {
 
 using FwdFn = void (*)(FwdArgs);
 
+// Mirror-pair forward gather: 128 accumulators, 2 waves per SIMD.
+template <int BC, int TRIG>
+__global__ void __launch_bounds__(kWorkgroup) __attribute__((amdgpu_waves_per_eu(2)))
+fwd4_pair_gather_kernel(FwdArgs a) {
+  FwdPairGather4<BC, TRIG>::run(a);
+}
+
+template <int BC>
+void pick_pair(int trig, FwdFn& f) {
+  f = trig == kTrigHw ? fwd4_pair_gather_kernel<BC, kTrigHw> : fwd4_pair_gather_kernel<BC, kTrigAccurate>;
+}
+
+bool select_pair_fwd(int trig, int BC, FwdFn& f) {
+  switch (BC) {
+    case 1: pick_pair<1>(trig, f); return true;
+    case 2: pick_pair<2>(trig, f); return true;
+    case 4: pick_pair<4>(trig, f); return true;
+    case 8: pick_pair<8>(trig, f); return true;
+    case 16: pick_pair<16>(trig, f); return true;
+    default: return false;
+  }
+}
+
 // gather: the kernel for tiles shorter than a launch row; gather_row (four-
 // group engine only) the one for a tile that spans the row.
 struct FwdKernels { FwdFn gather; FwdFn direct; FwdFn gather_row; };
@@ -701,6 +928,34 @@ hipError_t launch_fwd_gather(int trig, int T, int BC, int32_t splits, const FwdA
   const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
   const FwdFn g = (fn.gather_row && a.tile >= a.g_split) ? fn.gather_row : fn.gather;
   hipLaunchKernelGGL(g, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_pair_pack(int BC, const FwdArgs& a, hipStream_t s) {
+  FwdFn f;
+  if (!select_pair_fwd(kTrigHw, BC, f) || a.gpad % kMfmaChunk != 0 || !a.pairs || !a.refs || !a.wflags ||
+      a.gcap != (a.N + 128 / BC - 1) / (128 / BC) || a.gpad < a.gcap)
+    return hipErrorInvalidValue;
+  if (a.gpad <= 0) return hipSuccess;
+  if (!a.glist) return hipErrorInvalidValue;
+  const int64_t lanes = a.gpad * 128;
+  const int64_t blocks = (lanes + kWorkgroup - 1) / kWorkgroup;
+  hipLaunchKernelGGL(fwd_pair_pack_kernel, dim3((unsigned)blocks), dim3(kWorkgroup), 0, s, a, BC);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_list_kernel, dim3(1), dim3(kWorkgroup), 0, s, a, 128 / BC);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_pair_gather(int trig, int BC, int32_t splits, const FwdArgs& a, hipStream_t s) {
+  FwdFn f;
+  if (!select_pair_fwd(trig, BC, f) || splits < 1 || (splits > 1) != (a.partial != nullptr) || !a.pairs)
+    return hipErrorInvalidValue;
+  if (a.gpad % kMfmaChunk != 0) return hipErrorInvalidValue;
+  if (a.M <= 0) return hipSuccess;
+  const int64_t waves = (a.M + 15) / 16;
+  const int64_t blocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  hipLaunchKernelGGL(f, dim3((unsigned)blocks, (unsigned)splits), dim3(kWorkgroup), 0, s, a);
   return hipGetLastError();
 }
 

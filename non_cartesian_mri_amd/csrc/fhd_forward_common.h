@@ -76,8 +76,10 @@ __device__ __forceinline__ void fwd_finish(const FwdArgs& a, float4* lds, int wi
   float dre[BC], dim[BC];
 #pragma unroll
   for (int b = 0; b < BC; ++b) { dre[b] = 0.0f; dim[b] = 0.0f; }
+  // offsets relative to the reference column (0, or jref < N with mirror pairs)
   const bool any_voxel = a.N > 0;
-  const float x0 = any_voxel ? a.x[0] : 0.0f, y0 = any_voxel ? a.y[0] : 0.0f, z0 = any_voxel ? a.z[0] : 0.0f;
+  const float x0 = any_voxel ? a.x[a.jref] : 0.0f, y0 = any_voxel ? a.y[a.jref] : 0.0f,
+              z0 = any_voxel ? a.z[a.jref] : 0.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (h > 0) __syncthreads();   // the first half's reads are done
@@ -101,7 +103,7 @@ __device__ __forceinline__ void fwd_finish(const FwdArgs& a, float4* lds, int wi
       for (int jj = lane >> 4; jj < JN && j0 + jj < a.N; jj += 4) {
         const int j = j0 + jj;
         float cj = 1.0f, sj = 0.0f;
-        if (j > 0) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
+        if (j != a.jref) k.sincos_phase(a.x[j] - x0, a.y[j] - y0, a.z[j] - z0, cj, sj);
 #pragma unroll
         for (int bb = 0; bb < (BC == 1 ? 1 : BC / 2); ++bb) {
           const int b = BC == 1 ? 0 : h * (BC / 2) + bb;

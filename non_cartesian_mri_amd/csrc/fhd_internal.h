@@ -220,6 +220,14 @@ struct FwdArgs {
                          // indices in increasing order
   float2* out;           // first output vector of this pass ([BC][M])
   float2* partial;       // [rows][BC][M] when rows > 1, else nullptr
+  // mirror pairs (four-group engine; nullptr / 0 otherwise): the K dimension
+  // runs over the pair plan's entries instead of groups; ghdr then holds each
+  // entry's reference voxel and gwb its packed (rho_g + rho_h, rho_g - rho_h)
+  const int32_t* pairs;  // pair plan (kPairHeader int32, int2 list, group references)
+  const float4* refs;    // the plan's group references
+  const int32_t* wflags; // regular waves of 16 groups (groups of the others go to glist)
+  int32_t jref;          // reference column (0 without pairs)
+  int64_t gcap;          // list slots (groups of the pass)
 };
 
 // Packs the image (and lists the groups off the common offsets).
@@ -238,6 +246,12 @@ hipError_t launch_mfma_records(int is_q, int trig, int T, int BC, const MfmaReco
 // kernel for irregular waves, with the device's launch rows (at most
 // pa.rows_hi; a.partial holds that many rows when pa.rows_hi > 1).
 hipError_t launch_mfma_pair_gather(int trig, int BC, const PairPlanArgs& pa, const MfmaArgs& a, hipStream_t s);
+// The pair plan alone (flags, references, list), for the forward operator.
+hipError_t launch_pair_plan(int BC, const PairPlanArgs& pa, hipStream_t s);
+// Forward operator with mirror pairs: packs the plan's entries (and lists the
+// groups of irregular waves), then the gather over the entries.
+hipError_t launch_fwd_pair_pack(int BC, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_pair_gather(int trig, int BC, int32_t splits, const FwdArgs& a, hipStream_t s);
 // Adds the device-chosen rows' partial sums (rows from the pair plan).
 hipError_t launch_reduce_dev_rows(int BC, const int32_t* plan, const GatherArgs& a, hipStream_t s);
 hipError_t launch_mfma_gather(int trig, int T, int BC, int32_t splits, const MfmaArgs& a,

@@ -1390,6 +1390,22 @@ hipError_t launch_mfma_pair_gather(int trig, int BC, const PairPlanArgs& pa, con
   return hipGetLastError();
 }
 
+hipError_t launch_pair_plan(int BC, const PairPlanArgs& pa, hipStream_t s) {
+  const PairFns fn = select_pair(BC, kTrigHw);
+  if (!fn.flags || !pa.plan || !pa.flags || pa.V != 128 / BC || pa.jref < 0 || pa.jref >= pa.V ||
+      (pa.N > 0 && pa.jref >= pa.N) || pa.G != (pa.N + pa.V - 1) / pa.V || pa.rows_lo < 1 || pa.rows_hi < pa.rows_lo ||
+      pa.refs != reinterpret_cast<const float4*>(reinterpret_cast<const char*>(pa.plan) + pair_list_bytes(pa.G)))
+    return hipErrorInvalidValue;
+  if (pa.N <= 0) return hipSuccess;
+  const int64_t waves = (pa.G + 15) / 16;
+  const int64_t fblocks = (waves + kWorkgroup / 64 - 1) / (kWorkgroup / 64);
+  hipLaunchKernelGGL(fn.flags, dim3((unsigned)fblocks), dim3(kWorkgroup), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_list_kernel, dim3(1), dim3(kListThreads), 0, s, pa);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_dev_rows(int BC, const int32_t* plan, const GatherArgs& a, hipStream_t s) {
   if (!a.partial || a.N <= 0) return hipSuccess;
   if (!plan) return hipErrorInvalidValue;

@@ -196,7 +196,7 @@ def q_compute(kx, ky, kz, x, y, z, phi, *, trig="accurate", sum="blocked",
 
 def fhd_forward(kx, ky, kz, x, y, z, phi, rho, *, trig="accurate", sum="blocked",
                 voxels_per_lane=0, tile=0, stages="all", out=None, workspace=None,
-                stream=None, sample_splits=0, engine="auto") -> torch.Tensor:
+                stream=None, sample_splits=0, engine="auto", mirror_pairs=True) -> torch.Tensor:
     """F rho on the GPU: rho complex64 [N] or [B, N]; returns complex64 [M] or [B, M].
 
     D[b][m] = phi[m] sum_n rho[b][n] exp(-i 2 pi k_m . x_n), the adjoint of
@@ -223,9 +223,10 @@ def fhd_forward(kx, ky, kz, x, y, z, phi, rho, *, trig="accurate", sum="blocked"
     if workspace is None:
         nbytes = fhd_workspace_bytes(M, N, B, op="forward", trig=trig, sum=sum,
                                      voxels_per_lane=voxels_per_lane, tile=tile,
-                                     sample_splits=sample_splits, engine=engine)
+                                     sample_splits=sample_splits, engine=engine,
+                                     mirror_pairs=mirror_pairs)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=kx.device)
-    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine)
+    o = make_opts(trig, sum, voxels_per_lane, tile, stages, workspace, sample_splits, engine, mirror_pairs)
     st = _lib.load().fhd_forward(kx.data_ptr(), ky.data_ptr(), kz.data_ptr(), x.data_ptr(),
                                  y.data_ptr(), z.data_ptr(), phi.data_ptr(), R2.data_ptr(),
                                  out.data_ptr(), M, N, B, ctypes.byref(o), _stream_ptr(stream))

@@ -314,7 +314,7 @@ def test_describe_plan_half_split(lib):
     # packed image (gpad x 1536 bytes), the gather's headers (gpad x 16) and the
     # scale beside the fp32 workspace
     f = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma16", trig="hw")
-    f32 = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma", trig="hw")
+    f32 = fhd_describe_plan(262144, 128 ** 3, op="forward", engine="mfma", trig="hw", mirror_pairs=False)
     assert f["engine"] == _lib.FHD_ENGINE_MFMA16 and f["voxels_per_lane"] == 128
     assert f["workspace_bytes"] - f32["workspace_bytes"] == 16384 * 1536 + 16384 * 16 + 1280
     # one launch row of all 16,384 groups: HW sums it as one block, accurate folds ~sqrt(G)
@@ -442,32 +442,48 @@ def test_forward_plan(lib):
     from non_cartesian_mri_amd.fhd import fhd_describe_plan, fhd_workspace_bytes
     a256 = lambda b: (b + 255) // 256 * 256
     # 128^3: T = 8, groups of 128 voxels -> 16,384 groups; 16,384 waves of 16 samples fill the GPU
-    p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
+    p = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw", mirror_pairs=False)
     assert p["engine"] == _lib.FHD_ENGINE_MFMA and p["voxels_per_lane"] == 128
     assert p["record_dwords"] == 4 + 384 and p["padded_samples"] == 262144
     # HW trig: the launch row (all 16,384 groups) is one summation block
     assert p["sample_splits"] == 1 and p["tile"] == 16384
     # accurate trig keeps ~sqrt(groups) per tile; so does HW with rows of more
     # than 256 MiB of packed groups (512^3: 1.6 GB per row, ~4 sqrt(G))
-    assert fhd_describe_plan(262144, 512 ** 3, op="forward", trig="hw")["tile"] == 4096
+    assert fhd_describe_plan(262144, 512 ** 3, op="forward", trig="hw", mirror_pairs=False)["tile"] == 4096
     # the 16-image pass on 96^3 (groups of 8 voxels: 110,592 groups, 170 MB per
     # row) is one block per row
-    b16 = fhd_describe_plan(500001, 96 ** 3, batch=16, op="forward", trig="hw")
+    b16 = fhd_describe_plan(500001, 96 ** 3, batch=16, op="forward", trig="hw", mirror_pairs=False)
     assert b16["sample_splits"] == 1 and b16["tile"] == 110592 and b16["voxels_per_lane"] == 8
-    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate")["tile"] == 128
+    assert fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate", mirror_pairs=False)["tile"] == 128
     pas = lambda g, T: a256(a256(g * 16) + a256(g * 192 * T) + 4 * (g + 1))
     assert p["workspace_bytes"] == pas(16384, 8)
     # groups of 64 on request: the pair engine, 32,768 groups
     p64 = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw", voxels_per_lane=64)
     assert p64["record_dwords"] == 4 + 192 and p64["tile"] == 1024 and p64["workspace_bytes"] == pas(32768, 4)
-    assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw") == p["workspace_bytes"]
+    assert fhd_workspace_bytes(262144, 128 ** 3, op="forward", trig="hw", mirror_pairs=False) == p["workspace_bytes"]
+    # mirror pairs (the default with T = 8): entry headers, entries of 64 T floats
+    # (rho_g + rho_h, rho_g - rho_h), the list of groups of irregular waves, the
+    # wave flags and the pair plan; each launch row one block of at most 16,384
+    # (HW) or 2,048 (accurate) entries over the partial sums
+    plan_b = lambda g: ((64 + 8 * g + 15) // 16 * 16) + 16 * g
+    pp = lambda g, gpad: a256(a256(gpad * 16) + a256(gpad * 64 * 8 * 4) + a256(4 * (gpad + 1)) +
+                              a256(4 * ((g + 15) // 16)) + plan_b(g))
+    q = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="hw")
+    assert q["sample_splits"] == 1 and q["tile"] == 16384 and q["workspace_bytes"] == pp(16384, 16384)
+    qa = fhd_describe_plan(262144, 128 ** 3, op="forward", trig="accurate")
+    assert qa["sample_splits"] == 8 and qa["tile"] == 2048
+    assert qa["workspace_bytes"] == pp(16384, 16384) + a256(8 * 262144 * 8)
+    q512 = fhd_describe_plan(262144, 512 ** 3, op="forward", trig="hw")
+    assert q512["sample_splits"] == 64 and q512["tile"] == 16384
+    q16 = fhd_describe_plan(500001, 96 ** 3, batch=16, op="forward", trig="hw")
+    assert q16["sample_splits"] == 7 and q16["tile"] == 16384
     # 32^3 x 2048 samples: 64 waves; rows over the 1024 groups (at least 64 groups each)
     s = fhd_describe_plan(2048, 32 ** 3, op="forward", trig="hw")
     assert s["voxels_per_lane"] == 32 and s["sample_splits"] == 16 and s["tile"] == 128
     assert s["workspace_bytes"] == pas(1024, 2) + a256(16 * 2048 * 8)
     # batch 3 on 64^3: passes of 2 and 1 images, T = 8: groups of 64 and 128 voxels
     # (128 = two rows of a plane)
-    b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1)
+    b = fhd_describe_plan(5000, 64 ** 3, batch=3, op="forward", trig="hw", sample_splits=1, mirror_pairs=False)
     assert b["passes"] == 2 and b["voxels_per_lane"] == 64 and b["tile"] == 4096
     assert b["workspace_bytes"] == pas(4096, 8) + pas(2048, 8)
     # with groups of 32 per image on request (T = 2): groups of 16 and 32

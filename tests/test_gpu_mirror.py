@@ -227,3 +227,86 @@ def test_stages_and_repeats_are_bitwise_equal():
                     workspace=ws1, out=out1, **o)
     torch.cuda.synchronize()
     assert np.array_equal(out1.cpu().numpy(), whole)
+
+
+# ------------------------- forward operator F rho ---------------------------
+def _fwd(p, rho, **opts):
+    from non_cartesian_mri_amd import fhd_forward
+    d = dev_problem(p)
+    opts.setdefault("engine", "mfma")
+    opts.setdefault("voxels_per_lane", 128)
+    r = torch.from_numpy(np.ascontiguousarray(rho)).to("cuda:0")
+    out = fhd_forward(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], r, **opts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(rho.shape[0], -1)
+
+
+def _rho(seed, B, N):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([inputs.complex_normal(rng, N) for _ in range(B)])
+
+
+@pytest.mark.parametrize("trig", ["hw", "accurate"])
+@pytest.mark.parametrize("B", [1, 2, 16, 19])
+def test_forward_pairs(oracle_mod, trig, B):
+    """F rho with the sum over voxel groups run over mirror pairs (one phase
+    and four products per pair: c (rho_g + rho_h) - i s (rho_g - rho_h)),
+    against the oracle, on the asymmetric box (pairs, a self-mirrored row and
+    rows alone) and against the same call with pairing off."""
+    p = _problem(910 + B, 900, XS, np.arange(-5, 5), np.arange(-3, 4), B=B)
+    rho = _rho(911 + B, B, p.x.size)
+    ref = oracle_mod.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho)
+    got = _fwd(p, rho, trig=trig)
+    assert_close(got, ref, TOL[trig], f"forward pairs B={B} {trig}")
+    off = _fwd(p, rho, trig=trig, mirror_pairs=False)
+    assert_close(off, ref, TOL[trig], f"forward pairing off B={B} {trig}")
+
+
+@pytest.mark.parametrize("trig", ["hw", "accurate"])
+@pytest.mark.parametrize("case", ["ragged", "short", "displaced", "no_mirrors", "rows3", "plain", "tile64"])
+def test_forward_pair_cases(oracle_mod, trig, case):
+    """A partial last group with its reference, a last wave without (direct
+    path), a displaced voxel (its wave direct), a grid without mirrors (every
+    group alone), explicit rows, a plain sum and short blocks."""
+    ys, zs, opts, N = np.arange(-5, 5), np.arange(-3, 4), {}, None
+    xs = XS
+    if case == "ragged":
+        N = 70 * 128 - 50
+    elif case == "short":
+        N = 69 * 128 + 1
+    elif case == "no_mirrors":
+        xs, ys, zs = XS + 0.5, np.arange(-4, 4) + 0.5, np.arange(-2, 2) + 0.5
+    elif case == "rows3":
+        opts = dict(sample_splits=3)
+    elif case == "plain":
+        opts = dict(sum="plain")
+    elif case == "tile64":
+        opts = dict(tile=64)
+    p = _problem(920, 700, xs, ys, zs, N=N)
+    if case == "displaced":
+        x = p.x.copy()
+        x[3 * 128 + 5] += 0.25
+        p = dataclasses.replace(p, x=x)
+    rho = _rho(921, 1, p.x.size)
+    ref = oracle_mod.forward(p.kx, p.ky, p.kz, p.x, p.y, p.z, p.phi, rho)
+    assert_close(_fwd(p, rho, trig=trig, **opts), ref, TOL[trig], f"forward pairs {case} {trig}")
+
+
+def test_forward_pairs_adjoint_and_repeat():
+    """<F rho, d> = <rho, F^H d> between the paired forward and the paired
+    adjoint, and two forward runs agree bit for bit."""
+    from non_cartesian_mri_amd import fhd_compute
+    p = _problem(930, 1100, XS, np.arange(-4, 4), np.arange(-3, 3))
+    rho = _rho(931, 1, p.x.size)
+    d = dev_problem(p)
+    a1 = _fwd(p, rho, trig="accurate")
+    a2 = _fwd(p, rho, trig="accurate")
+    assert np.array_equal(a1, a2)
+    fh = fhd_compute(d["kx"], d["ky"], d["kz"], d["x"], d["y"], d["z"], d["phi"], d["D"], trig="accurate",
+                     engine="mfma", voxels_per_lane=128)
+    torch.cuda.synchronize()
+    fh = fh.cpu().numpy().ravel().astype(np.complex128)
+    # the adjoint pairs phi against D: F^H D = sum_m conj(phi) D e^{+}, F rho = phi sum rho e^{-}
+    lhs = np.vdot(a1.ravel().astype(np.complex128), p.D[0].astype(np.complex128))
+    rhs = np.vdot(rho.ravel().astype(np.complex128), fh)
+    assert abs(lhs - rhs) <= 1e-5 * abs(lhs)
