@@ -55,10 +55,10 @@ MFMA_FLOP_PER_PAIR = {"gather": 6, "forward": 6}
 # the kernel source it was taken on, like TRAFFIC below)
 MFMA_BUSY = {
     ("fhd_128cube_262144_spirals", "hw", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "34dee8804c3af7cd", "busy": 0.928,
+        "source": "fhd_mfma.hip", "kernel_sha256": "beb77294902e5603", "busy": 0.926,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0", "busy": 0.851,
+        "source": "fhd_mfma.hip", "kernel_sha256": "beb77294902e5603", "busy": 0.854,
         "profile": "profiles/mfma_gather_128cubed_x_262144_issue_counters.md"},
 }
 
@@ -80,40 +80,40 @@ def method_roofline(kind: str, B: int) -> dict:
 # same launch configuration; otherwise the benchmark reports null.
 TRAFFIC = {
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "34dee8804c3af7cd",
-        "fetch_bytes": 2556809.1 * 1024 * 2.0, "write_bytes": 497756.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "beb77294902e5603",
+        "fetch_bytes": 2438538.5 * 1024 * 2.0, "write_bytes": 507904.0 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_mfma.hip", "kernel_sha256": "f05f272ba27b24b0",
-        "fetch_bytes": 1785493.0 * 1024 * 2.0, "write_bytes": 262152.0 * 1024 * 1.0,
+        "source": "fhd_mfma.hip", "kernel_sha256": "beb77294902e5603",
+        "fetch_bytes": 3529561.1 * 1024 * 2.0, "write_bytes": 2517529.6 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "52d901a194293be4",
-        "fetch_bytes": 1577175.4 * 1024 * 2.0, "write_bytes": 31086.9 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "4e60ce8e9dcf22de",
+        "fetch_bytes": 1057504.1 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma", 128): {
-        "source": "fhd_forward.hip", "kernel_sha256": "52d901a194293be4",
-        "fetch_bytes": 1520017.6 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward.hip", "kernel_sha256": "4e60ce8e9dcf22de",
+        "fetch_bytes": 88648.3 * 1024 * 2.0, "write_bytes": 16384.0 * 1024 * 1.0,
         "profile": "profiles/forward_gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals/forward", "hw", "blocked", "mfma16", 128): {
-        "source": "fhd_forward_half.hip", "kernel_sha256": "f4aa14a7d648053b",
-        "fetch_bytes": 797316.1 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
+        "source": "fhd_forward_half.hip", "kernel_sha256": "1de86f640c4e14c3",
+        "fetch_bytes": 797316.6 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_half_gather_128cubed_x_262144_kernel_stats.md"},
     ("fhd_128cube_262144_spirals/forward", "accurate", "blocked", "mfma16", 128): {
-        "source": "fhd_forward_half.hip", "kernel_sha256": "f4aa14a7d648053b",
+        "source": "fhd_forward_half.hip", "kernel_sha256": "1de86f640c4e14c3",
         "fetch_bytes": 797340.6 * 1024 * 2.0, "write_bytes": 2048.0 * 1024 * 1.0,
         "profile": "profiles/forward_half_gather_128cubed_x_262144_kernel_stats.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "22004205ff484185",
-        "fetch_bytes": 984574.4 * 1024 * 2.0, "write_bytes": 262145.7 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "09b302823e68cacf",
+        "fetch_bytes": 982777.8 * 1024 * 2.0, "write_bytes": 262148.1 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "accurate", "blocked", "valu", 16): {
-        "source": "fhd_kernels.hip", "kernel_sha256": "22004205ff484185",
-        "fetch_bytes": 1047842.2 * 1024 * 2.0, "write_bytes": 262145.6 * 1024 * 1.0,
+        "source": "fhd_kernels.hip", "kernel_sha256": "09b302823e68cacf",
+        "fetch_bytes": 1047734.7 * 1024 * 2.0, "write_bytes": 262147.2 * 1024 * 1.0,
         "profile": "profiles/gather_128cubed_x_262144_hbm_counters.md"},
     ("fhd_128cube_262144_spirals", "hw", "blocked", "mfma16", 128): {
-        "source": "fhd_half.hip", "kernel_sha256": "cb9b5c05d5ca9c9b",
-        "fetch_bytes": 6491823.3 * 1024 * 2.0, "write_bytes": 262148.3 * 1024 * 1.0,
+        "source": "fhd_half.hip", "kernel_sha256": "8d3129522d42899d",
+        "fetch_bytes": 2318758.5 * 1024 * 2.0, "write_bytes": 262148.0 * 1024 * 1.0,
         "profile": "profiles/half_gather_128cubed_x_262144_kernel_stats.md"},
     # the whole gridding reconstruction (sort, deposit + x transform, y and z passes)
     ("fhd_128cube_262144_spirals/gridding", "-", "-", "-", 0): {
@@ -508,6 +508,27 @@ def mirror_pair_work(ws, ws_bytes: int, p, plan: dict) -> dict:
             "mfma_ratio_to_unpaired": round(mfmas / alone_mfmas, 4)}
 
 
+def forward_pair_work(ws, p, plan: dict) -> dict:
+    """The forward operator's pair plan (first pass; one pass for every
+    workload here) and its matrix work: per wave of 16 samples and block of
+    four list entries, 4 MFMAs per tile of 16 columns (8 tiles), over the
+    entries padded to 32.  Pass layout: entry headers, entries (64 T floats
+    each), the list of groups of irregular waves, the wave flags, the plan."""
+    a256 = lambda b: (b + 255) // 256 * 256
+    V = plan["voxels_per_lane"]
+    G = -(-p.N // V)
+    gpad = -(-G // 32) * 32
+    off = a256(gpad * 16) + a256(gpad * 64 * 8 * 4) + a256(4 * (gpad + 1)) + a256(4 * -(-G // 16))
+    head = ws[off:off + 64].view(torch_int32()).cpu().numpy()
+    E, Cp = int(head[0]), int(head[1])
+    epad = -(-E // 32) * 32
+    mfmas = -(-p.M // 16) * (epad // 4) * 32 * plan["passes"]
+    alone = -(-p.M // 16) * (gpad // 4) * 24 * plan["passes"]
+    return {"paired_groups": Cp, "groups_alone": E - Cp, "groups": G, "launch_rows": plan["sample_splits"],
+            "executed_flop_per_pair": mfmas * 16 * 16 * 4 * 2 / (p.N * p.M * p.B),
+            "mfma_ratio_to_unpaired": round(mfmas / alone, 4)}
+
+
 def torch_int32():
     import torch
     return torch.int32
@@ -752,8 +773,8 @@ def main():
     elif forward or engine == "mfma":
         flop_per_pair = MFMA_FLOP_PER_PAIR["forward" if forward else "gather"]
         pairing = None
-        if not forward and plan.get("mirror_pairs"):
-            pairing = mirror_pair_work(ws, ws_bytes, p, plan)
+        if plan.get("mirror_pairs"):
+            pairing = forward_pair_work(ws, p, plan) if forward else mirror_pair_work(ws, ws_bytes, p, plan)
             flop_per_pair = pairing["executed_flop_per_pair"]
         ex = flop_per_pair * pairs / (g_avg * 1e-3) / 1e12
         busy = MFMA_BUSY.get((args.config, args.trig, plan["voxels_per_lane"])) if not forward else None
