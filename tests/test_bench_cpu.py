@@ -53,3 +53,43 @@ def test_traffic_only_for_current_sources():
         else:
             assert rate is None and detail is None
     assert bench.traffic_for("no such workload", "hw", "blocked", "mfma", 128, 10.0) == (None, None)
+
+
+def _plan_workspace(nbytes, offset, header):
+    import torch
+    ws = torch.zeros(nbytes, dtype=torch.uint8)
+    ws[offset:offset + 4 * len(header)] = torch.tensor(header, dtype=torch.int32).view(torch.uint8)
+    return ws
+
+
+def test_mirror_pair_work_reads_the_plan():
+    """The adjoint's pair plan sits at the end of the workspace; 128^3 with
+    8,064 pairs and 256 groups alone: 520 wave slots of 32 MFMAs per block of
+    four samples against 1,024 waves of 24 -> 4.0625 executed FLOP per pair."""
+    from types import SimpleNamespace
+    G = 16384
+    pair_bytes = ((64 + 8 * G + 15) // 16 * 16 + 16 * G + 255) // 256 * 256
+    nbytes = 10 * pair_bytes
+    ws = _plan_workspace(nbytes, nbytes - pair_bytes, [8320, 8064, 31, 8464, 520, 130, 16512])
+    p = SimpleNamespace(N=128 ** 3, M=262144, B=1)
+    plan = {"voxels_per_lane": 128, "padded_samples": 262144, "passes": 1}
+    w = bench.mirror_pair_work(ws, nbytes, p, plan)
+    assert (w["paired_groups"], w["groups_alone"], w["launch_rows"], w["wave_slots"]) == (8064, 256, 31, 520)
+    assert w["executed_flop_per_pair"] == pytest.approx(4.0625)
+    assert w["mfma_ratio_to_unpaired"] == pytest.approx(520 * 32 / (1024 * 24), abs=1e-4)
+
+
+def test_forward_pair_work_reads_the_plan():
+    """The forward's pair plan follows the entry headers, entries, list and
+    wave flags of the pass; 8,320 entries over 16,384 groups -> 4.0625."""
+    from types import SimpleNamespace
+    G, gpad = 16384, 16384
+    a256 = lambda b: (b + 255) // 256 * 256
+    off = a256(gpad * 16) + a256(gpad * 64 * 8 * 4) + a256(4 * (gpad + 1)) + a256(4 * (G // 16))
+    ws = _plan_workspace(off + 4096, off, [8320, 8064, 1, 0, 520, 130, 16512])
+    p = SimpleNamespace(N=128 ** 3, M=262144, B=1)
+    plan = {"voxels_per_lane": 128, "passes": 1, "sample_splits": 1}
+    w = bench.forward_pair_work(ws, p, plan)
+    assert (w["paired_groups"], w["groups_alone"]) == (8064, 256)
+    assert w["executed_flop_per_pair"] == pytest.approx(4.0625)
+    assert w["mfma_ratio_to_unpaired"] == pytest.approx(8320 * 32 / (16384 * 24), abs=1e-4)
